@@ -1,0 +1,168 @@
+/*
+ * sgmv.h - C ABI of libsgmv: Segmented Gather Matrix-Vector multiplication
+ * (SGMV) for multi-LoRA batches on AMD Instinct MI355X (gfx950).
+ *
+ * What is computed.  The Punica README (page "Punica：多 LoRA 模型统一服务框架",
+ * LoRA paragraph) gives a LoRA pair as A [H1, r] and B [r, H2] beside a
+ * pretrained weight W [H1, H2]; a row vector x run through the finetuned layer
+ * gives x@(W + A@B) = x@W + x@A@B.  The multi-LoRA paragraph of the same page
+ * batches rows X = (x_1..x_n) where every row carries its own LoRA model, so
+ * the layer output is X@W plus, row by row, x_i @ A_{id(i)} @ B_{id(i)}; its
+ * SGMV paragraph names the kernel that computes that second term.  This
+ * library computes only that LoRA term and adds it onto a Y that already holds
+ * the caller's X@W:
+ *
+ *     for every segment s, k = lora_idx[s], rows i in [seg_indptr[s], seg_indptr[s+1]):
+ *         V[i, :]  = X[i, :] @ A_k                 (shrink, fp32 result)
+ *         Y[i, :] += V[i, :] @ B_k                 (expand)
+ *
+ * Rows are grouped into segments: contiguous row ranges that share one LoRA
+ * ("Segmented"), whose weights are fetched through per-LoRA pointer tables
+ * ("Gather").  No LoRA scale factor appears in the pages' formula; the scale
+ * is 1 and a caller folds any alpha/r into B.
+ *
+ * Layouts (all row-major, contiguous, the logical shapes of the LoRA
+ * paragraph with row-vector inputs):
+ *   X   [n_rows, h_in]    dtype            (read)
+ *   A_k [h_in,  rank]     dtype            (read; A_ptrs[k] points to it)
+ *   B_k [rank,  h_out]    dtype            (read; B_ptrs[k] points to it)
+ *   V   [n_rows, rank]    float32          (written by sgmv_shrink, read by sgmv_expand)
+ *   Y   [n_rows, h_out]   dtype            (read-modify-write)
+ *   seg_indptr [num_segs+1], lora_idx [num_segs]   int32
+ *   A_ptrs, B_ptrs [num_loras]  arrays of device pointers (uint64)
+ *
+ * Memory: every pointer passed to a device entry point (X, V, Y, A_ptrs,
+ * B_ptrs, the matrices they point to, seg_indptr, lora_idx, workspace) is
+ * DEVICE memory on the current HIP device, owned by the caller; it must stay
+ * alive until the stream work finishes.  X, V and Y must not alias each
+ * other.  The library allocates nothing and keeps no per-call state.
+ *
+ * Precision: inputs are fp16 or bf16; products and sums are fp32; Y is
+ * rounded once (round-to-nearest-even) from fp32 (Y + addend) on store.
+ *
+ * Segment metadata preconditions (device-resident, so not checked by the
+ * device entry points; sgmv_check_segments checks a host copy):
+ *   seg_indptr[0] = 0, seg_indptr non-decreasing, seg_indptr[num_segs] <= n_rows,
+ *   every segment length <= max_seg_len, 0 <= lora_idx[s] < num_loras.
+ * Segments may come in any LoRA order and a LoRA id may appear in several
+ * segments; empty segments are no-ops; rows at or past seg_indptr[num_segs]
+ * are left untouched.  A violated precondition gives unspecified values in
+ * Y / V but no out-of-bounds access beyond what the pointer tables allow.
+ *
+ * Errors: every entry point returns sgmv_status_t and never throws.  Argument
+ * checks run on the host before any HIP call; a launch failure returns
+ * SGMV_ERR_HIP.  Device entry points are asynchronous on `stream` (a
+ * hipStream_t; NULL = the default stream) and never synchronise.
+ */
+#ifndef SGMV_H
+#define SGMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sgmv_status {
+  SGMV_OK = 0,
+  SGMV_ERR_INVALID_ARG = 1,  /* null pointer, negative size, bad metadata (host checks) */
+  SGMV_ERR_UNSUPPORTED = 2,  /* rank, dtype, alignment or size outside what the kernels take */
+  SGMV_ERR_WORKSPACE = 3,    /* workspace missing or smaller than sgmv_workspace_bytes */
+  SGMV_ERR_HIP = 4           /* a HIP runtime call or kernel launch failed */
+} sgmv_status_t;
+
+typedef enum sgmv_dtype {
+  SGMV_F16 = 0,   /* IEEE binary16 */
+  SGMV_BF16 = 1   /* bfloat16 (upper half of binary32) */
+} sgmv_dtype_t;
+
+/* Kernel family.  AUTO picks per call from max_seg_len and rank; the others
+ * force one family (tests use them to pin every variant to the oracle). */
+typedef enum sgmv_variant {
+  SGMV_VARIANT_AUTO = 0,
+  SGMV_VARIANT_VECTOR = 1,  /* split-K vector kernels, one launch per stage */
+  SGMV_VARIANT_FUSED = 2,   /* sgmv_lora_apply only: one persistent launch, shrink->expand handoff on chip */
+  SGMV_VARIANT_MFMA = 3     /* matrix-core kernels for long (prefill) segments */
+} sgmv_variant_t;
+
+/* Host-side shape summary; the host never reads device memory to plan. */
+typedef struct sgmv_problem {
+  int32_t dtype;        /* sgmv_dtype_t */
+  int32_t n_rows;       /* rows of X, V and Y (>= 0) */
+  int32_t h_in;         /* H1: columns of X, rows of A_k; multiple of 8 */
+  int32_t h_out;        /* H2: columns of Y and B_k; multiple of 8 */
+  int32_t rank;         /* r: one of 8, 16, 32, 64 */
+  int32_t num_loras;    /* entries of A_ptrs / B_ptrs (>= 1 when num_segs > 0) */
+  int32_t num_segs;     /* S (>= 0); 0 makes every device call a no-op */
+  int32_t max_seg_len;  /* upper bound on every segment's length, 0..n_rows */
+  int32_t variant;      /* sgmv_variant_t */
+  int32_t reserved;     /* must be 0 */
+} sgmv_problem_t;
+
+/* Size of the leading area of every workspace that holds the kernels'
+ * arrival counters.  It must be zero-filled before the workspace's first use;
+ * every call that completes leaves it zero again. */
+#define SGMV_WS_COUNTER_BYTES ((size_t)1 << 20)
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* sgmv_status_str(sgmv_status_t status);
+
+/* Host-only segment builder (no device access).  Groups the n requests of a
+ * batch by LoRA id, as the multi-LoRA paragraph of the Punica README
+ * requires (every input row bound to its own LoRA), into the segments of the
+ * SGMV paragraph.  Order: ascending LoRA id, ties by request index (a stable
+ * sort), only non-empty segments.
+ *   req_lora   [n]      in:  LoRA id of request i, each in [0, num_loras)
+ *   perm       [n]      out: perm[j] = request index placed at sorted row j
+ *   seg_indptr [n+1]    out: capacity n+1; first *num_segs+1 entries written
+ *   lora_idx   [n]      out: capacity n;   first *num_segs entries written
+ *   num_segs, max_seg_len  out scalars
+ * n = 0 gives num_segs = 0, seg_indptr[0] = 0, max_seg_len = 0.
+ * Returns SGMV_ERR_INVALID_ARG for null pointers (other than arrays of an
+ * n = 0 call), n < 0, num_loras < 1, or an id outside [0, num_loras); outputs
+ * are then unspecified.  Runs in O(n + num_loras) time. */
+sgmv_status_t sgmv_build_segments(const int32_t* req_lora, int32_t n, int32_t num_loras,
+                                  int32_t* perm, int32_t* seg_indptr, int32_t* lora_idx,
+                                  int32_t* num_segs, int32_t* max_seg_len);
+
+/* Host-only check of a problem description: sizes, rank, dtype, variant. */
+sgmv_status_t sgmv_check_problem(const sgmv_problem_t* problem);
+
+/* Host-only check of a HOST copy of the segment metadata against the
+ * preconditions listed above (num_segs, n_rows, max_seg_len and num_loras
+ * taken from *problem). */
+sgmv_status_t sgmv_check_segments(const sgmv_problem_t* problem, const int32_t* seg_indptr_host,
+                                  const int32_t* lora_idx_host);
+
+/* Workspace bytes that sgmv_shrink / sgmv_lora_apply need for *problem
+ * (always >= SGMV_WS_COUNTER_BYTES). */
+sgmv_status_t sgmv_workspace_bytes(const sgmv_problem_t* problem, size_t* bytes);
+
+/* Shrink: V[i, :] = X[i, :] @ A_{lora_idx[s]} for every covered row i
+ * (Punica README, LoRA paragraph: the x@A factor of x@A@B).  V rows not
+ * covered by a segment are left untouched.  ws: device workspace of at least
+ * sgmv_workspace_bytes bytes whose counter area is zero (see above). */
+sgmv_status_t sgmv_shrink(const sgmv_problem_t* problem, const void* X, const void* const* A_ptrs,
+                          float* V, const int32_t* seg_indptr, const int32_t* lora_idx, void* ws,
+                          size_t ws_bytes, void* stream);
+
+/* Expand: Y[i, :] += V[i, :] @ B_{lora_idx[s]} for every covered row i
+ * (the trailing @B factor), V in fp32, one rounding of Y on store. */
+sgmv_status_t sgmv_expand(const sgmv_problem_t* problem, const float* V, const void* const* B_ptrs,
+                          void* Y, const int32_t* seg_indptr, const int32_t* lora_idx,
+                          void* stream);
+
+/* Fused apply: Y[i, :] += (X[i, :] @ A_k) @ B_k, the whole LoRA term of the
+ * multi-LoRA paragraph, with the fp32 intermediate kept in the workspace or
+ * on chip.  Same workspace contract as sgmv_shrink. */
+sgmv_status_t sgmv_lora_apply(const sgmv_problem_t* problem, const void* X,
+                              const void* const* A_ptrs, const void* const* B_ptrs, void* Y,
+                              const int32_t* seg_indptr, const int32_t* lora_idx, void* ws,
+                              size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SGMV_H */
