@@ -97,7 +97,8 @@ typedef struct sgmv_problem {
   int32_t num_segs;     /* S (>= 0); 0 makes every device call a no-op */
   int32_t max_seg_len;  /* upper bound on every segment's length, 0..n_rows */
   int32_t variant;      /* sgmv_variant_t */
-  int32_t reserved;     /* must be 0 */
+  int32_t splits;       /* workgroups sharing one row block of a segment (split-K
+                           factor of the vector kernels); 0 picks it automatically */
 } sgmv_problem_t;
 
 /* Size of the leading area of every workspace that holds the kernels'

@@ -1,0 +1,228 @@
+"""Python binding of libsgmv (SGMV LoRA kernels for MI355X / gfx950).
+
+A thin ctypes layer over the C ABI in ``include/sgmv.h``: each function here
+has the name of the C entry point it calls and only marshals arguments
+(torch tensors -> device pointers, the current HIP stream, status codes ->
+exceptions).  Every step of the computation runs in the library's HIP
+kernels; there is no fallback path.  PyTorch is used for device memory and
+streams only.
+
+What is computed is the LoRA term of the Punica README (page "Punica：多 LoRA
+模型统一服务框架", LoRA and multi-LoRA paragraphs): for rows grouped into
+segments that share a LoRA pair (A_k [H1, r], B_k [r, H2]),
+``Y[i] += (X[i] @ A_k) @ B_k`` on top of the base output already in Y.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsgmv.so")
+
+SGMV_OK, SGMV_ERR_INVALID_ARG, SGMV_ERR_UNSUPPORTED, SGMV_ERR_WORKSPACE, SGMV_ERR_HIP = range(5)
+SGMV_F16, SGMV_BF16 = 0, 1
+SGMV_VARIANT_AUTO, SGMV_VARIANT_VECTOR, SGMV_VARIANT_FUSED, SGMV_VARIANT_MFMA = range(4)
+SGMV_WS_COUNTER_BYTES = 1 << 20
+
+ENTRY_POINTS = ("sgmv_status_str", "sgmv_build_segments", "sgmv_check_problem",
+                "sgmv_check_segments", "sgmv_workspace_bytes", "sgmv_shrink", "sgmv_expand",
+                "sgmv_lora_apply")
+
+
+class SgmvError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {sgmv_status_str(status)}")
+
+
+class sgmv_problem_t(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32), ("n_rows", ctypes.c_int32), ("h_in", ctypes.c_int32),
+                ("h_out", ctypes.c_int32), ("rank", ctypes.c_int32), ("num_loras", ctypes.c_int32),
+                ("num_segs", ctypes.c_int32), ("max_seg_len", ctypes.c_int32),
+                ("variant", ctypes.c_int32), ("splits", ctypes.c_int32)]
+
+    def __repr__(self):
+        return "sgmv_problem_t(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libsgmv.so (built in-tree by ``python -m segmented_gather_matvec_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"libsgmv is not built ({path} missing); run "
+                          "`python -m segmented_gather_matvec_amd.build` with ROCm's hipcc")
+    lib = ctypes.CDLL(path)
+    P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    prob = ctypes.POINTER(sgmv_problem_t)
+    lib.sgmv_status_str.argtypes = [ctypes.c_int]
+    lib.sgmv_status_str.restype = ctypes.c_char_p
+    lib.sgmv_build_segments.argtypes = [P, I32, I32, P, P, P, P, P]
+    lib.sgmv_check_problem.argtypes = [prob]
+    lib.sgmv_check_segments.argtypes = [prob, P, P]
+    lib.sgmv_workspace_bytes.argtypes = [prob, ctypes.POINTER(SZ)]
+    lib.sgmv_shrink.argtypes = [prob, P, P, P, P, P, P, SZ, P]
+    lib.sgmv_expand.argtypes = [prob, P, P, P, P, P, P]
+    lib.sgmv_lora_apply.argtypes = [prob, P, P, P, P, P, P, P, SZ, P]
+    for name in ENTRY_POINTS[1:]:
+        getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def sgmv_status_str(status: int) -> str:
+    return load_library().sgmv_status_str(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != SGMV_OK:
+        raise SgmvError(status, where)
+
+
+def make_problem(dtype, n_rows, h_in, h_out, rank, num_loras, num_segs, max_seg_len,
+                 variant=SGMV_VARIANT_AUTO, splits=0) -> sgmv_problem_t:
+    """Fill an sgmv_problem_t; ``dtype`` is 'f16' / 'bf16', a torch dtype, or an SGMV_* code."""
+    return sgmv_problem_t(_dtype_code(dtype), int(n_rows), int(h_in), int(h_out), int(rank),
+                          int(num_loras), int(num_segs), int(max_seg_len), int(variant), int(splits))
+
+
+def _dtype_code(dtype) -> int:
+    if isinstance(dtype, int):
+        return dtype
+    if isinstance(dtype, str):
+        return {"f16": SGMV_F16, "bf16": SGMV_BF16}[dtype]
+    import torch
+    return {torch.float16: SGMV_F16, torch.bfloat16: SGMV_BF16}[dtype]
+
+
+# ----------------------------------------------------------------- host-only
+
+def sgmv_build_segments(req_lora, num_loras: int):
+    """Host segment builder.  Returns numpy int32 ``(perm, seg_indptr, lora_idx)`` and the
+    int ``max_seg_len``; ``perm[j]`` is the request placed at sorted row j."""
+    ids = np.ascontiguousarray(np.asarray(req_lora, dtype=np.int32).reshape(-1))
+    n = ids.size
+    perm = np.empty(max(n, 1), np.int32)
+    seg = np.empty(n + 1, np.int32)
+    lidx = np.empty(max(n, 1), np.int32)
+    S, mx = ctypes.c_int32(0), ctypes.c_int32(0)
+    st = load_library().sgmv_build_segments(ids.ctypes.data, n, int(num_loras), perm.ctypes.data,
+                                            seg.ctypes.data, lidx.ctypes.data,
+                                            ctypes.byref(S), ctypes.byref(mx))
+    _check(st, "sgmv_build_segments")
+    return perm[:n], seg[: S.value + 1], lidx[: S.value], int(mx.value)
+
+
+def sgmv_check_problem(problem: sgmv_problem_t) -> int:
+    return load_library().sgmv_check_problem(ctypes.byref(problem))
+
+
+def sgmv_check_segments(problem: sgmv_problem_t, seg_indptr, lora_idx) -> int:
+    sp = np.ascontiguousarray(np.asarray(seg_indptr, dtype=np.int32))
+    li = np.ascontiguousarray(np.asarray(lora_idx, dtype=np.int32))
+    return load_library().sgmv_check_segments(ctypes.byref(problem), sp.ctypes.data,
+                                              li.ctypes.data if li.size else None)
+
+
+def sgmv_workspace_bytes(problem: sgmv_problem_t) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load_library().sgmv_workspace_bytes(ctypes.byref(problem), ctypes.byref(out)),
+           "sgmv_workspace_bytes")
+    return int(out.value)
+
+
+# ----------------------------------------------------------------- device calls
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _need(t, name, dtype=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _torch_dtype(problem):
+    import torch
+    return torch.bfloat16 if problem.dtype == SGMV_BF16 else torch.float16
+
+
+def sgmv_shrink(problem, X, A_ptrs, V, seg_indptr, lora_idx, ws, stream=None):
+    """V[i] = X[i] @ A_{lora_idx[s]} (fp32 V) on the device; asynchronous."""
+    import torch
+    _need(X, "X", _torch_dtype(problem)); _need(V, "V", torch.float32)
+    _need(A_ptrs, "A_ptrs", torch.int64); _need(seg_indptr, "seg_indptr", torch.int32)
+    _need(lora_idx, "lora_idx", torch.int32); _need(ws, "ws")
+    st = load_library().sgmv_shrink(ctypes.byref(problem), _ptr(X), _ptr(A_ptrs), _ptr(V),
+                                    _ptr(seg_indptr), _ptr(lora_idx), _ptr(ws),
+                                    ws.numel() * ws.element_size() if ws is not None else 0,
+                                    _stream(stream))
+    _check(st, "sgmv_shrink")
+
+
+def sgmv_expand(problem, V, B_ptrs, Y, seg_indptr, lora_idx, stream=None):
+    """Y[i] += V[i] @ B_{lora_idx[s]} on the device; asynchronous."""
+    import torch
+    _need(V, "V", torch.float32); _need(Y, "Y", _torch_dtype(problem))
+    _need(B_ptrs, "B_ptrs", torch.int64); _need(seg_indptr, "seg_indptr", torch.int32)
+    _need(lora_idx, "lora_idx", torch.int32)
+    st = load_library().sgmv_expand(ctypes.byref(problem), _ptr(V), _ptr(B_ptrs), _ptr(Y),
+                                    _ptr(seg_indptr), _ptr(lora_idx), _stream(stream))
+    _check(st, "sgmv_expand")
+
+
+def sgmv_lora_apply(problem, X, A_ptrs, B_ptrs, Y, seg_indptr, lora_idx, ws, stream=None):
+    """Y[i] += (X[i] @ A_k) @ B_k on the device; asynchronous."""
+    import torch
+    dt = _torch_dtype(problem)
+    _need(X, "X", dt); _need(Y, "Y", dt)
+    _need(A_ptrs, "A_ptrs", torch.int64); _need(B_ptrs, "B_ptrs", torch.int64)
+    _need(seg_indptr, "seg_indptr", torch.int32); _need(lora_idx, "lora_idx", torch.int32)
+    _need(ws, "ws")
+    st = load_library().sgmv_lora_apply(ctypes.byref(problem), _ptr(X), _ptr(A_ptrs), _ptr(B_ptrs),
+                                        _ptr(Y), _ptr(seg_indptr), _ptr(lora_idx), _ptr(ws),
+                                        ws.numel() * ws.element_size() if ws is not None else 0,
+                                        _stream(stream))
+    _check(st, "sgmv_lora_apply")
+
+
+# ----------------------------------------------------------------- helpers
+
+def pointer_table(stacked) -> "torch.Tensor":
+    """Device int64 table of per-LoRA pointers into a stacked [P, ...] tensor."""
+    import torch
+    _need(stacked, "stacked weights")
+    P = stacked.shape[0]
+    stride = stacked[0].numel() * stacked.element_size() if P else 0
+    return (torch.arange(P, device=stacked.device, dtype=torch.int64) * stride
+            + stacked.data_ptr()).contiguous()
+
+
+def new_workspace(problem: sgmv_problem_t, device="cuda"):
+    """Zero-filled device workspace of sgmv_workspace_bytes(problem) bytes."""
+    import torch
+    nbytes = sgmv_workspace_bytes(problem)
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device)

@@ -1,0 +1,303 @@
+// sgmv_api.cpp - host side of libsgmv: argument checks, the segment builder,
+// problem planning (kernel family, row blocks, splits) and launches.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstdlib>
+#include <mutex>
+#include <utility>
+#include <vector>
+
+#include "../../include/sgmv.h"
+#include "sgmv_plan.h"
+
+namespace {
+
+using sgmv::VecParams;
+
+constexpr int kMaxDevices = 64;
+constexpr int64_t kCounterSlots = (int64_t)(SGMV_WS_COUNTER_BYTES / sizeof(uint32_t));
+// Aim for this many workgroups per launch of the vector kernels: two per CU of
+// a 256-CU MI355X keeps enough 128-bit loads in flight to cover HBM latency.
+constexpr int kTargetWorkgroups = 512;
+constexpr int kMaxSplits = 1024;
+
+bool rank_supported(int r) { return r == 8 || r == 16 || r == 32 || r == 64; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t round_up(int64_t a, int64_t m) { return ceil_div(a, m) * m; }
+
+// Plan of one vector-kernel launch.
+struct VecPlan {
+  int rb = 1;
+  int direct = 1;
+  int64_t num_units = 0;
+  int splits = 1;
+  int kc = 8;
+  int cw = 8;
+  size_t partial_bytes() const {
+    return (size_t)num_units * (size_t)splits * (size_t)rb * sizeof(float);  // times rank
+  }
+};
+
+int pick_rb(int max_seg_len) { return max_seg_len <= 1 ? 1 : (max_seg_len <= 4 ? 4 : 16); }
+
+VecPlan plan_vec(const sgmv_problem_t& p, int64_t target_wgs) {
+  VecPlan v;
+  v.rb = pick_rb(p.max_seg_len);
+  if (p.max_seg_len <= v.rb) {
+    v.direct = 1;
+    v.num_units = p.num_segs;
+  } else {
+    v.direct = 0;
+    const int64_t per_seg = ceil_div(p.max_seg_len, v.rb);
+    v.num_units = std::min<int64_t>((int64_t)p.num_segs * per_seg, ceil_div(p.n_rows, v.rb) + p.num_segs);
+  }
+  const int64_t max_split = std::min<int64_t>(
+      {ceil_div(p.h_in, 8), ceil_div(p.h_out, 8), (int64_t)kMaxSplits});
+  int64_t g = p.splits > 0 ? p.splits : ceil_div(target_wgs, std::max<int64_t>(v.num_units, 1));
+  g = std::max<int64_t>(1, std::min(g, max_split));
+  v.splits = (int)g;
+  v.kc = (int)round_up(ceil_div(p.h_in, g), 8);
+  v.cw = (int)round_up(ceil_div(p.h_out, g), 8);
+  return v;
+}
+
+size_t vec_ws_bytes(const VecPlan& v, int rank) {
+  return SGMV_WS_COUNTER_BYTES + v.partial_bytes() * (size_t)rank;
+}
+
+// fp32 intermediate V [n_rows, rank] of the two-launch route of sgmv_lora_apply.
+size_t v_area_bytes(const sgmv_problem_t& p) {
+  return (size_t)round_up((int64_t)p.n_rows * p.rank * (int64_t)sizeof(float), 256);
+}
+
+int device_capacity(int dtype, int rank, int rb) {
+  static std::mutex mu;
+  static int cache[kMaxDevices][2][4][3];
+  static bool init[kMaxDevices][2][4][3];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  const int ri = rank == 8 ? 0 : rank == 16 ? 1 : rank == 32 ? 2 : 3;
+  const int bi = rb == 1 ? 0 : rb == 4 ? 1 : 2;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!init[dev][dtype][ri][bi]) {
+    cache[dev][dtype][ri][bi] = sgmv::fused_resident_capacity(dtype, rank, rb);
+    init[dev][dtype][ri][bi] = true;
+  }
+  return cache[dev][dtype][ri][bi];
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned8(const void* p) { return ((uintptr_t)p & 7u) == 0; }
+
+bool nothing_to_do(const sgmv_problem_t& p) {
+  return p.num_segs == 0 || p.n_rows == 0 || p.max_seg_len == 0;
+}
+
+VecParams base_params(const sgmv_problem_t& p, const VecPlan& v, const int32_t* seg_indptr,
+                      const int32_t* lora_idx, void* ws) {
+  VecParams q{};
+  q.seg_indptr = seg_indptr;
+  q.lora_idx = lora_idx;
+  q.counters = static_cast<uint32_t*>(ws);
+  q.partials = reinterpret_cast<float*>(static_cast<char*>(ws) + SGMV_WS_COUNTER_BYTES);
+  q.n_rows = p.n_rows;
+  q.h_in = p.h_in;
+  q.h_out = p.h_out;
+  q.num_segs = p.num_segs;
+  q.num_loras = p.num_loras;
+  q.num_units = (int32_t)v.num_units;
+  q.splits = v.splits;
+  q.kc = v.kc;
+  q.cw = v.cw;
+  q.direct_units = v.direct;
+  return q;
+}
+
+sgmv_status_t hip_status(hipError_t e) { return e == hipSuccess ? SGMV_OK : SGMV_ERR_HIP; }
+
+// Which kernels a fused apply runs.
+enum class ApplyRoute { kFused, kTwoLaunch };
+
+ApplyRoute route_apply(const sgmv_problem_t& p, const VecPlan& fused) {
+  if (p.variant == SGMV_VARIANT_VECTOR) return ApplyRoute::kTwoLaunch;
+  const int64_t grid = fused.num_units * fused.splits;
+  const int cap = device_capacity(p.dtype, p.rank, fused.rb);
+  const bool fits = cap > 0 && grid <= cap && 2 * fused.num_units <= kCounterSlots;
+  if (p.variant == SGMV_VARIANT_FUSED) return fits ? ApplyRoute::kFused : ApplyRoute::kTwoLaunch;
+  // AUTO: the fused kernel serves decode-shaped calls whose grid fits on chip.
+  return fits ? ApplyRoute::kFused : ApplyRoute::kTwoLaunch;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sgmv_status_str(sgmv_status_t status) {
+  switch (status) {
+    case SGMV_OK: return "SGMV_OK";
+    case SGMV_ERR_INVALID_ARG: return "SGMV_ERR_INVALID_ARG: invalid argument";
+    case SGMV_ERR_UNSUPPORTED: return "SGMV_ERR_UNSUPPORTED: shape, rank, dtype or alignment not supported";
+    case SGMV_ERR_WORKSPACE: return "SGMV_ERR_WORKSPACE: workspace missing or too small";
+    case SGMV_ERR_HIP: return "SGMV_ERR_HIP: HIP runtime or launch failure";
+  }
+  return "SGMV_ERR_UNKNOWN";
+}
+
+sgmv_status_t sgmv_build_segments(const int32_t* req_lora, int32_t n, int32_t num_loras,
+                                  int32_t* perm, int32_t* seg_indptr, int32_t* lora_idx,
+                                  int32_t* num_segs, int32_t* max_seg_len) {
+  if (n < 0 || num_loras < 1 || !seg_indptr || !num_segs || !max_seg_len) return SGMV_ERR_INVALID_ARG;
+  if (n > 0 && (!req_lora || !perm || !lora_idx)) return SGMV_ERR_INVALID_ARG;
+  for (int32_t i = 0; i < n; ++i)
+    if (req_lora[i] < 0 || req_lora[i] >= num_loras) return SGMV_ERR_INVALID_ARG;
+  seg_indptr[0] = 0;
+  int32_t S = 0, longest = 0;
+  if ((int64_t)num_loras <= 4 * (int64_t)n + 1024) {
+    // Counting sort: O(n + num_loras), stable.
+    std::vector<int32_t> start((size_t)num_loras + 1, 0);
+    for (int32_t i = 0; i < n; ++i) ++start[(size_t)req_lora[i] + 1];
+    for (int32_t k = 0; k < num_loras; ++k) {
+      const int32_t c = start[(size_t)k + 1];
+      if (c > 0) {
+        lora_idx[S] = k;
+        seg_indptr[S + 1] = seg_indptr[S] + c;
+        longest = std::max(longest, c);
+        ++S;
+      }
+      start[(size_t)k + 1] += start[(size_t)k];
+    }
+    for (int32_t i = 0; i < n; ++i) perm[start[(size_t)req_lora[i]]++] = i;
+  } else {
+    // Sparse ids: stable comparison sort, O(n log n).
+    std::vector<std::pair<int32_t, int32_t>> key((size_t)n);
+    for (int32_t i = 0; i < n; ++i) key[(size_t)i] = {req_lora[i], i};
+    std::sort(key.begin(), key.end());
+    for (int32_t j = 0; j < n; ++j) {
+      perm[j] = key[(size_t)j].second;
+      if (j == 0 || key[(size_t)j].first != key[(size_t)j - 1].first) {
+        if (j > 0) seg_indptr[S] = j;
+        lora_idx[S++] = key[(size_t)j].first;
+      }
+    }
+    if (n > 0) seg_indptr[S] = n;
+    for (int32_t s = 0; s < S; ++s) longest = std::max(longest, seg_indptr[s + 1] - seg_indptr[s]);
+  }
+  *num_segs = S;
+  *max_seg_len = longest;
+  return SGMV_OK;
+}
+
+sgmv_status_t sgmv_check_problem(const sgmv_problem_t* p) {
+  if (!p) return SGMV_ERR_INVALID_ARG;
+  if (p->n_rows < 0 || p->h_in <= 0 || p->h_out <= 0 || p->num_segs < 0 || p->num_loras < 0 ||
+      p->max_seg_len < 0 || p->max_seg_len > p->n_rows || p->splits < 0)
+    return SGMV_ERR_INVALID_ARG;
+  if (p->num_segs > 0 && p->num_loras < 1) return SGMV_ERR_INVALID_ARG;
+  if (p->variant < SGMV_VARIANT_AUTO || p->variant > SGMV_VARIANT_MFMA) return SGMV_ERR_INVALID_ARG;
+  if (p->dtype != SGMV_F16 && p->dtype != SGMV_BF16) return SGMV_ERR_UNSUPPORTED;
+  if (!rank_supported(p->rank)) return SGMV_ERR_UNSUPPORTED;
+  if (p->h_in % 8 != 0 || p->h_out % 8 != 0) return SGMV_ERR_UNSUPPORTED;
+  if (p->variant == SGMV_VARIANT_MFMA) return SGMV_ERR_UNSUPPORTED;  // not built yet
+  const VecPlan v = plan_vec(*p, kTargetWorkgroups);
+  if (2 * v.num_units > kCounterSlots) return SGMV_ERR_UNSUPPORTED;
+  return SGMV_OK;
+}
+
+sgmv_status_t sgmv_check_segments(const sgmv_problem_t* p, const int32_t* seg_indptr_host,
+                                  const int32_t* lora_idx_host) {
+  if (!p) return SGMV_ERR_INVALID_ARG;
+  if (p->num_segs < 0) return SGMV_ERR_INVALID_ARG;
+  if (!seg_indptr_host || (p->num_segs > 0 && !lora_idx_host)) return SGMV_ERR_INVALID_ARG;
+  if (seg_indptr_host[0] != 0) return SGMV_ERR_INVALID_ARG;
+  for (int32_t s = 0; s < p->num_segs; ++s) {
+    const int32_t len = seg_indptr_host[s + 1] - seg_indptr_host[s];
+    if (len < 0 || len > p->max_seg_len) return SGMV_ERR_INVALID_ARG;
+    if (lora_idx_host[s] < 0 || lora_idx_host[s] >= p->num_loras) return SGMV_ERR_INVALID_ARG;
+  }
+  if (seg_indptr_host[p->num_segs] > p->n_rows) return SGMV_ERR_INVALID_ARG;
+  return SGMV_OK;
+}
+
+sgmv_status_t sgmv_workspace_bytes(const sgmv_problem_t* p, size_t* bytes) {
+  if (!bytes) return SGMV_ERR_INVALID_ARG;
+  const sgmv_status_t st = sgmv_check_problem(p);
+  if (st != SGMV_OK) return st;
+  const VecPlan v = plan_vec(*p, kTargetWorkgroups);
+  *bytes = vec_ws_bytes(v, p->rank) + v_area_bytes(*p);
+  return SGMV_OK;
+}
+
+sgmv_status_t sgmv_shrink(const sgmv_problem_t* p, const void* X, const void* const* A_ptrs,
+                          float* V, const int32_t* seg_indptr, const int32_t* lora_idx, void* ws,
+                          size_t ws_bytes, void* stream) {
+  sgmv_status_t st = sgmv_check_problem(p);
+  if (st != SGMV_OK) return st;
+  if (nothing_to_do(*p)) return SGMV_OK;
+  if (!X || !A_ptrs || !V || !seg_indptr || !lora_idx) return SGMV_ERR_INVALID_ARG;
+  if (!aligned16(X) || !aligned16(V) || !aligned8(A_ptrs)) return SGMV_ERR_UNSUPPORTED;
+  const VecPlan v = plan_vec(*p, kTargetWorkgroups);
+  if (!ws || ws_bytes < vec_ws_bytes(v, p->rank)) return SGMV_ERR_WORKSPACE;
+  if (!aligned16(ws)) return SGMV_ERR_UNSUPPORTED;
+  VecParams q = base_params(*p, v, seg_indptr, lora_idx, ws);
+  q.X = static_cast<const uint16_t*>(X);
+  q.A_ptrs = reinterpret_cast<const uint64_t*>(A_ptrs);
+  q.V = V;
+  return hip_status(sgmv::launch_vec(p->dtype, p->rank, v.rb, sgmv::kModeShrink, q,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+sgmv_status_t sgmv_expand(const sgmv_problem_t* p, const float* V, const void* const* B_ptrs,
+                          void* Y, const int32_t* seg_indptr, const int32_t* lora_idx,
+                          void* stream) {
+  sgmv_status_t st = sgmv_check_problem(p);
+  if (st != SGMV_OK) return st;
+  if (nothing_to_do(*p)) return SGMV_OK;
+  if (!V || !B_ptrs || !Y || !seg_indptr || !lora_idx) return SGMV_ERR_INVALID_ARG;
+  if (!aligned16(V) || !aligned16(Y) || !aligned8(B_ptrs)) return SGMV_ERR_UNSUPPORTED;
+  const VecPlan v = plan_vec(*p, kTargetWorkgroups);
+  VecParams q = base_params(*p, v, seg_indptr, lora_idx, nullptr);
+  q.counters = nullptr;
+  q.partials = nullptr;
+  q.V = const_cast<float*>(V);
+  q.B_ptrs = reinterpret_cast<const uint64_t*>(B_ptrs);
+  q.Y = static_cast<uint16_t*>(Y);
+  return hip_status(sgmv::launch_vec(p->dtype, p->rank, v.rb, sgmv::kModeExpand, q,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+sgmv_status_t sgmv_lora_apply(const sgmv_problem_t* p, const void* X, const void* const* A_ptrs,
+                              const void* const* B_ptrs, void* Y, const int32_t* seg_indptr,
+                              const int32_t* lora_idx, void* ws, size_t ws_bytes, void* stream) {
+  sgmv_status_t st = sgmv_check_problem(p);
+  if (st != SGMV_OK) return st;
+  if (nothing_to_do(*p)) return SGMV_OK;
+  if (!X || !A_ptrs || !B_ptrs || !Y || !seg_indptr || !lora_idx) return SGMV_ERR_INVALID_ARG;
+  if (!aligned16(X) || !aligned16(Y) || !aligned8(A_ptrs) || !aligned8(B_ptrs))
+    return SGMV_ERR_UNSUPPORTED;
+  const VecPlan v = plan_vec(*p, kTargetWorkgroups);
+  const size_t need_fused = vec_ws_bytes(v, p->rank);
+  // The two-launch route keeps the fp32 intermediate V [n_rows, rank] after the
+  // shrink's own split partials.
+  const size_t v_bytes = v_area_bytes(*p);
+  if (!ws || ws_bytes < need_fused) return SGMV_ERR_WORKSPACE;
+  if (!aligned16(ws)) return SGMV_ERR_UNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  VecParams q = base_params(*p, v, seg_indptr, lora_idx, ws);
+  q.X = static_cast<const uint16_t*>(X);
+  q.A_ptrs = reinterpret_cast<const uint64_t*>(A_ptrs);
+  q.B_ptrs = reinterpret_cast<const uint64_t*>(B_ptrs);
+  q.Y = static_cast<uint16_t*>(Y);
+  if (route_apply(*p, v) == ApplyRoute::kFused)
+    return hip_status(sgmv::launch_vec(p->dtype, p->rank, v.rb, sgmv::kModeFused, q, s));
+  // Two launches: shrink into V (held at the end of the workspace), then expand.
+  if (ws_bytes < need_fused + v_bytes) return SGMV_ERR_WORKSPACE;
+  q.V = reinterpret_cast<float*>(static_cast<char*>(ws) + need_fused);
+  hipError_t e = sgmv::launch_vec(p->dtype, p->rank, v.rb, sgmv::kModeShrink, q, s);
+  if (e != hipSuccess) return SGMV_ERR_HIP;
+  return hip_status(sgmv::launch_vec(p->dtype, p->rank, v.rb, sgmv::kModeExpand, q, s));
+}
+
+}  // extern "C"

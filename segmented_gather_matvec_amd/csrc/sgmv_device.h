@@ -1,0 +1,82 @@
+// sgmv_device.h - device-side helpers shared by the libsgmv kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sgmv {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;  // every kernel runs 4 wave64s per workgroup
+constexpr int kWaves = kThreads / 64;
+
+// Element formats.  Values travel as raw 16-bit patterns and are widened to
+// fp32 for arithmetic.
+struct F16 {
+  __device__ static inline float lo(uint32_t w) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+  }
+  __device__ static inline float hi(uint32_t w) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+  }
+  __device__ static inline float one(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+  // round to nearest even (v_cvt_f16_f32 under the default rounding mode)
+  __device__ static inline uint16_t round(float f) {
+    return __builtin_bit_cast(uint16_t, (_Float16)f);
+  }
+};
+
+struct BF16 {
+  __device__ static inline float lo(uint32_t w) { return __uint_as_float(w << 16); }
+  __device__ static inline float hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+  __device__ static inline float one(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+  // round to nearest even (v_cvt_pk_bf16_f32)
+  __device__ static inline uint16_t round(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+};
+
+// Eight 16-bit values of a 128-bit vector, widened to fp32.
+template <class T>
+__device__ inline void unpack8(const u32x4& v, float (&f)[8]) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    f[2 * w] = T::lo(v[w]);
+    f[2 * w + 1] = T::hi(v[w]);
+  }
+}
+
+template <class T>
+__device__ inline u32x4 pack8(const float (&f)[8]) {
+  u32x4 v;
+#pragma unroll
+  for (int w = 0; w < 4; ++w)
+    v[w] = (uint32_t)T::round(f[2 * w]) | ((uint32_t)T::round(f[2 * w + 1]) << 16);
+  return v;
+}
+
+// 128-bit loads of data that is read exactly once per call (LoRA weights,
+// X, Y): the non-temporal hint keeps them from displacing reusable lines.
+__device__ inline u32x4 load_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ inline u32x4 load_vec(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ inline void store_vec(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+__device__ inline float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }
+
+// Cross-workgroup hand-off through global counters (device scope).  The
+// release publishes this workgroup's earlier global writes; the acquire makes
+// other workgroups' published writes visible to this one.
+__device__ inline uint32_t counter_add_release(uint32_t* c, uint32_t v) {
+  return __hip_atomic_fetch_add(c, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline uint32_t counter_load_acquire(const uint32_t* c) {
+  return __hip_atomic_load(c, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void counter_store_relaxed(uint32_t* c, uint32_t v) {
+  __hip_atomic_store(c, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void fence_acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+__device__ inline void fence_release_agent() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
+
+}  // namespace sgmv

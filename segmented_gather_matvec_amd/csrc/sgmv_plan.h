@@ -1,0 +1,48 @@
+// sgmv_plan.h - host-side interface between the C ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sgmv {
+
+// Vector (split-K) kernels: one template, three modes.
+enum VecMode : int {
+  kModeShrink = 0,  // V = X @ A_k (partials reduced by the last-arriving workgroup)
+  kModeExpand = 1,  // Y += V @ B_k
+  kModeFused = 2    // both, partial V handed over on chip; grid must be co-resident
+};
+
+// A "unit" is one row block (<= RB rows) of one segment; each unit is worked by
+// `splits` workgroups, split g covering input rows [g*kc, (g+1)*kc) of A_k in
+// the shrink and output columns [g*cw, (g+1)*cw) of B_k in the expand.
+struct VecParams {
+  const uint16_t* X;
+  const uint64_t* A_ptrs;
+  const uint64_t* B_ptrs;
+  uint16_t* Y;
+  float* V;
+  const int32_t* seg_indptr;
+  const int32_t* lora_idx;
+  float* partials;     // [num_units][splits][RB][rank] fp32
+  uint32_t* counters;  // [2 * num_units]: arrivals, departures
+  int32_t n_rows, h_in, h_out, num_segs, num_loras;
+  int32_t num_units;     // units in the grid (an upper bound when not direct)
+  int32_t splits;        // workgroups per unit
+  int32_t kc;            // shrink input-row chunk per split, multiple of 8
+  int32_t cw;            // expand column chunk per split, multiple of 8
+  int32_t direct_units;  // 1: unit u is segment u (every segment fits one row block)
+};
+
+// Rows of A_k covered by one pass of the shrink loop and columns of B_k covered
+// by one pass of the expand loop (two 128-bit loads per thread per pass).
+constexpr int vec_rows_per_pass(int rank) { return 256 * 2 * 8 / rank; }
+constexpr int vec_cols_per_pass(int rank) { return 256 * 2 * 8 / rank; }
+
+// Launch one vector kernel; returns the HIP error of the launch.
+hipError_t launch_vec(int dtype, int rank, int rb, int mode, const VecParams& p, hipStream_t stream);
+
+// Workgroups of the fused kernel that fit on the device at once (0 if unknown).
+int fused_resident_capacity(int dtype, int rank, int rb);
+
+}  // namespace sgmv

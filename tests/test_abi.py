@@ -1,0 +1,185 @@
+"""Host-side tests of libsgmv's C ABI: no GPU needed, no kernel launched.
+
+Covers: the shared library loads and exports every entry point declared in
+include/sgmv.h; the host segment builder matches the oracle's stable-sort
+builder bit for bit; argument checks return their status codes before any
+HIP call.
+"""
+import ctypes
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import segmented_gather_matvec_amd as sg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sgmv.h")
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(sgmv_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_entry_point():
+    lib = sg.load_library()
+    names = declared_functions()
+    assert len(names) >= 8
+    for name in names:
+        assert hasattr(lib, name), f"{name} declared in sgmv.h but not exported"
+    assert set(names) == set(sg.ENTRY_POINTS)
+
+
+def test_problem_struct_layout_matches_header():
+    src = open(HEADER).read()
+    body = re.search(r"typedef struct sgmv_problem \{(.*?)\} sgmv_problem_t;", src, re.S).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    fields = re.findall(r"int32_t\s+(\w+);", body)
+    assert fields == [n for n, _ in sg.sgmv_problem_t._fields_]
+    assert ctypes.sizeof(sg.sgmv_problem_t) == 4 * len(fields)
+    assert f"SGMV_WS_COUNTER_BYTES ((size_t)1 << 20)" in src and sg.SGMV_WS_COUNTER_BYTES == 1 << 20
+
+
+def test_status_strings():
+    for st in range(5):
+        assert sg.sgmv_status_str(st).startswith("SGMV_")
+    assert "UNKNOWN" in sg.sgmv_status_str(99)
+
+
+# ------------------------------------------------------------------ builder
+
+def test_builder_golden_examples():
+    with open(os.path.join(GOLDEN, "builder_examples.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        perm, seg, lidx, mx = sg.sgmv_build_segments(c["req_lora"], c["num_loras"])
+        assert perm.tolist() == c["perm"]
+        assert seg.tolist() == c["seg_indptr"]
+        assert lidx.tolist() == c["lora_idx"]
+        assert mx == c["max_seg_len"]
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_builder_matches_oracle_bit_exact(seed):
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(0, 400))
+    # dense pools take the counting sort, sparse pools the comparison sort
+    P = int(rng.choice([1, 3, 50, 4096, 10_000_000]))
+    ids = rng.integers(0, P, size=n)
+    perm, seg, lidx, mx = sg.sgmv_build_segments(ids, P)
+    operm, oseg, olidx, omx = oracle.build_segments(ids, P)
+    assert perm.tolist() == operm and seg.tolist() == oseg and lidx.tolist() == olidx and mx == omx
+
+
+@pytest.mark.parametrize("kind,n", [("identical", 32), ("uniform", 64), ("skewed", 64), ("skewed", 32)])
+def test_builder_on_popularity_workloads(kind, n):
+    import workloads
+    w = workloads.popularity(kind, n)
+    perm, seg, lidx, mx = sg.sgmv_build_segments(w.req_lora, w.num_loras)
+    operm, oseg, olidx, omx = oracle.build_segments(w.req_lora, w.num_loras)
+    assert perm.tolist() == operm and seg.tolist() == oseg and lidx.tolist() == olidx and mx == omx
+
+
+@pytest.mark.parametrize("ids,P", [([0, 3], 3), ([-1], 3), ([0], 0)])
+def test_builder_rejects_bad_ids(ids, P):
+    with pytest.raises(sg.SgmvError) as e:
+        sg.sgmv_build_segments(ids, P)
+    assert e.value.status == sg.SGMV_ERR_INVALID_ARG
+
+
+# ------------------------------------------------------------------ problem checks
+
+def good(**kw):
+    base = dict(dtype="f16", n_rows=32, h_in=4096, h_out=4096, rank=16, num_loras=32,
+                num_segs=32, max_seg_len=1)
+    base.update(kw)
+    return sg.make_problem(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({}, sg.SGMV_OK),
+    ({"dtype": "bf16", "rank": 64}, sg.SGMV_OK),
+    ({"rank": 8}, sg.SGMV_OK),
+    ({"rank": 32}, sg.SGMV_OK),
+    ({"rank": 12}, sg.SGMV_ERR_UNSUPPORTED),
+    ({"rank": 128}, sg.SGMV_ERR_UNSUPPORTED),
+    ({"dtype": 7}, sg.SGMV_ERR_UNSUPPORTED),
+    ({"h_in": 4100}, sg.SGMV_ERR_UNSUPPORTED),
+    ({"h_out": 12}, sg.SGMV_ERR_UNSUPPORTED),
+    ({"h_in": 0}, sg.SGMV_ERR_INVALID_ARG),
+    ({"n_rows": -1}, sg.SGMV_ERR_INVALID_ARG),
+    ({"num_segs": -1}, sg.SGMV_ERR_INVALID_ARG),
+    ({"max_seg_len": 33}, sg.SGMV_ERR_INVALID_ARG),
+    ({"num_loras": 0}, sg.SGMV_ERR_INVALID_ARG),
+    ({"variant": 9}, sg.SGMV_ERR_INVALID_ARG),
+    ({"splits": -2}, sg.SGMV_ERR_INVALID_ARG),
+    ({"num_segs": 0, "num_loras": 0, "max_seg_len": 0}, sg.SGMV_OK),
+    ({"n_rows": 0, "num_segs": 0, "max_seg_len": 0}, sg.SGMV_OK),
+])
+def test_check_problem(kw, status):
+    assert sg.sgmv_check_problem(good(**kw)) == status
+
+
+def test_check_problem_null():
+    assert sg.load_library().sgmv_check_problem(None) == sg.SGMV_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("seg,lidx,status", [
+    ([0, 1, 2, 4], [0, 1, 2], sg.SGMV_OK),
+    ([0, 0, 2, 4], [0, 1, 2], sg.SGMV_OK),           # empty segment
+    ([1, 1, 2, 4], [0, 1, 2], sg.SGMV_ERR_INVALID_ARG),  # seg_indptr[0] != 0
+    ([0, 2, 1, 4], [0, 1, 2], sg.SGMV_ERR_INVALID_ARG),  # decreasing
+    ([0, 1, 2, 9], [0, 1, 2], sg.SGMV_ERR_INVALID_ARG),  # past n_rows
+    ([0, 1, 2, 4], [0, 1, 5], sg.SGMV_ERR_INVALID_ARG),  # id out of range
+    ([0, 1, 2, 4], [0, -1, 2], sg.SGMV_ERR_INVALID_ARG),
+    ([0, 1, 4, 4], [0, 1, 2], sg.SGMV_ERR_INVALID_ARG),  # longer than max_seg_len
+])
+def test_check_segments(seg, lidx, status):
+    p = sg.make_problem("f16", 8, 64, 64, 8, 4, 3, 2)
+    assert sg.sgmv_check_segments(p, seg, lidx) == status
+
+
+def test_workspace_bytes():
+    p = good()
+    nbytes = sg.sgmv_workspace_bytes(p)
+    assert nbytes >= sg.SGMV_WS_COUNTER_BYTES + 32 * 16 * 4
+    with pytest.raises(sg.SgmvError):
+        sg.sgmv_workspace_bytes(good(rank=7))
+
+
+def test_device_entry_points_fail_fast_on_bad_arguments():
+    """Every status below is returned by host checks before any HIP call."""
+    lib = sg.load_library()
+    p = good()
+    fake = ctypes.c_void_p(0x10000)    # aligned, never dereferenced on these paths
+    odd = ctypes.c_void_p(0x10002)
+    ws_need = sg.sgmv_workspace_bytes(p)
+    # null pointers
+    assert lib.sgmv_lora_apply(ctypes.byref(p), None, fake, fake, fake, fake, fake, fake, ws_need,
+                               None) == sg.SGMV_ERR_INVALID_ARG
+    assert lib.sgmv_shrink(ctypes.byref(p), fake, None, fake, fake, fake, fake, ws_need,
+                           None) == sg.SGMV_ERR_INVALID_ARG
+    assert lib.sgmv_expand(ctypes.byref(p), fake, fake, None, fake, fake, None) == sg.SGMV_ERR_INVALID_ARG
+    # misaligned X / Y
+    assert lib.sgmv_lora_apply(ctypes.byref(p), odd, fake, fake, fake, fake, fake, fake, ws_need,
+                               None) == sg.SGMV_ERR_UNSUPPORTED
+    assert lib.sgmv_expand(ctypes.byref(p), fake, fake, odd, fake, fake, None) == sg.SGMV_ERR_UNSUPPORTED
+    # workspace missing / too small
+    assert lib.sgmv_lora_apply(ctypes.byref(p), fake, fake, fake, fake, fake, fake, None, 0,
+                               None) == sg.SGMV_ERR_WORKSPACE
+    assert lib.sgmv_shrink(ctypes.byref(p), fake, fake, fake, fake, fake, fake, sg.SGMV_WS_COUNTER_BYTES,
+                           None) == sg.SGMV_ERR_WORKSPACE
+    # unsupported rank
+    bad = good(rank=24)
+    assert lib.sgmv_lora_apply(ctypes.byref(bad), fake, fake, fake, fake, fake, fake, fake, ws_need,
+                               None) == sg.SGMV_ERR_UNSUPPORTED
+    # nothing to do: OK without touching any pointer
+    empty = good(num_segs=0, max_seg_len=0)
+    assert lib.sgmv_lora_apply(ctypes.byref(empty), None, None, None, None, None, None, None, 0,
+                               None) == sg.SGMV_OK

@@ -1,0 +1,267 @@
+"""GPU parity of libsgmv against the fp64 oracle, through the C ABI.
+
+Bar: every element within |gpu - ref| <= 1e-3 + 1e-2*|ref| of the unrounded
+fp64 oracle; integer-exact inputs (every partial sum an exact fp32 integer,
+every output exact in fp16/bf16) must match bit for bit in every variant;
+segment metadata from the library's builder must equal the oracle's builder.
+Workloads follow the Punica README's popularity cases (page "Punica：多 LoRA
+模型统一服务框架", throughput paragraph) and the shapes listed per test.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import segmented_gather_matvec_amd as sg
+import workloads
+from tests.gpu_cases import DeviceCall, assert_close, assert_close_f32, to_bits, to_device
+
+pytestmark = pytest.mark.gpu
+
+APPLY_VARIANTS = [sg.SGMV_VARIANT_AUTO, sg.SGMV_VARIANT_VECTOR, sg.SGMV_VARIANT_FUSED]
+
+
+def run_workload(w, variant=sg.SGMV_VARIANT_AUTO, splits=0):
+    """Run a Workload (builder applied when it carries per-request ids)."""
+    X, Y0 = w.X, w.Y0
+    if w.req_lora is not None:
+        perm, seg, lidx, _ = sg.sgmv_build_segments(w.req_lora, w.num_loras)
+        operm, oseg, olidx, _ = oracle.build_segments(w.req_lora, w.num_loras)
+        assert perm.tolist() == operm and seg.tolist() == oseg and lidx.tolist() == olidx
+        X, Y0 = X[perm], Y0[perm]
+    else:
+        seg, lidx = w.seg_indptr, w.lora_idx
+    call = DeviceCall(w.dtype, X, w.A, w.B, Y0, seg, lidx, variant=variant, splits=splits)
+    return call
+
+
+# ------------------------------------------------------------ workloads of the pages' study
+
+@pytest.mark.parametrize("variant", APPLY_VARIANTS)
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_tiny(variant, dtype):
+    w = workloads.tiny()
+    if dtype == "bf16":
+        w.dtype = "bf16"
+        w.X, w.A, w.B = (workloads.to_bits(oracle.decode(t, "f16").astype(np.float32), "bf16")
+                         for t in (w.X, w.A, w.B))
+    call = run_workload(w, variant)
+    assert_close(to_bits(call.apply()), call.oracle_apply(), dtype)
+    assert call.counters_clear()
+
+
+@pytest.mark.parametrize("variant", APPLY_VARIANTS)
+def test_decode_distinct_h4096_r16_b32(variant):
+    call = run_workload(workloads.decode_distinct(), variant)
+    assert_close(to_bits(call.apply()), call.oracle_apply(), "f16")
+    assert call.counters_clear()
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 7, 16, 64, 512])
+@pytest.mark.parametrize("variant", [sg.SGMV_VARIANT_VECTOR, sg.SGMV_VARIANT_FUSED])
+def test_decode_distinct_any_split(splits, variant):
+    call = run_workload(workloads.decode_distinct(), variant, splits)
+    assert_close(to_bits(call.apply()), call.oracle_apply(), "f16")
+    assert call.counters_clear()
+
+
+@pytest.mark.parametrize("variant", APPLY_VARIANTS)
+@pytest.mark.parametrize("kind,n", [("identical", 32), ("identical", 64), ("uniform", 32),
+                                    ("uniform", 64), ("skewed", 32), ("skewed", 64)])
+def test_popularity_sweep(kind, n, variant):
+    call = run_workload(workloads.popularity(kind, n), variant)
+    assert_close(to_bits(call.apply()), call.oracle_apply(), "f16")
+    assert call.counters_clear()
+
+
+@pytest.mark.parametrize("rank", [16, 64])
+def test_mixed_prefill_decode_reduced(rank):
+    """Config-4 layout (8 prefill + 24 one-row segments, 16 LoRAs, bf16) with prefill
+    lengths 16..100 and hidden sizes 512/1376, small enough for a full comparison."""
+    for w in workloads.mixed(rank, seed=400 + rank, pairs=((512, 1376), (1376, 512)), lo=16, hi=100):
+        call = run_workload(w)
+        assert_close(to_bits(call.apply()), call.oracle_apply(), "bf16", what=w.name)
+
+
+@pytest.mark.parametrize("rank", [16, 64])
+def test_mixed_prefill_decode_full_size_sampled(rank):
+    """Config 4 at full size (Llama-7B MLP shapes, ~4.6k rows), oracle on sampled rows."""
+    for w in workloads.mixed(rank):
+        call = run_workload(w)
+        got = to_bits(call.apply())
+        rng = np.random.default_rng(7)
+        seg = call.seg
+        rows = set(int(r) for r in rng.choice(call.Xh.shape[0], size=24, replace=False))
+        for s in range(len(seg) - 1):       # first and last row of every segment
+            if seg[s + 1] > seg[s]:
+                rows.update((int(seg[s]), int(seg[s + 1] - 1)))
+        rows = np.array(sorted(rows))
+        mask = np.zeros(call.Xh.shape[0], np.uint8)
+        mask[rows] = 1
+        ref = call.oracle_apply(row_mask=mask)
+        assert_close(got, ref, "bf16", rows=rows, what=w.name)
+
+
+# ------------------------------------------------------------ bit-exact pins
+
+INT_EXACT = {("f16", 8): (64, 512), ("f16", 16): (64, 512), ("f16", 32): (32, 512),
+             ("f16", 64): (16, 512), ("bf16", 8): (16, 64), ("bf16", 16): (8, 64),
+             ("bf16", 32): (4, 64), ("bf16", 64): (2, 64)}
+
+
+@pytest.mark.parametrize("variant", APPLY_VARIANTS)
+@pytest.mark.parametrize("dtype,rank", sorted(INT_EXACT))
+def test_integer_exact_inputs_bitwise(dtype, rank, variant):
+    m, c = INT_EXACT[(dtype, rank)]
+    rng = np.random.default_rng(1000 + rank)
+    X, A, B, Y0 = workloads.integer_exact(rng, 24, 256, 264, rank, 4, dtype, m, c)
+    seg, lidx = [0, 5, 5, 6, 9, 17, 24], [3, 1, 0, 3, 2, 1]
+    call = DeviceCall(dtype, X, A, B, Y0, seg, lidx, variant=variant)
+    got = oracle.decode(to_bits(call.apply()), dtype)
+    assert np.array_equal(got, call.oracle_apply())
+
+
+@pytest.mark.parametrize("variant", APPLY_VARIANTS)
+def test_integer_exact_full_decode_shape(variant):
+    rng = np.random.default_rng(2024)
+    X, A, B, Y0 = workloads.integer_exact(rng, 32, 4096, 4096, 16, 32, "f16", 64, 512)
+    call = DeviceCall("f16", X, A, B, Y0, np.arange(33), np.arange(32)[::-1].copy(), variant=variant)
+    assert np.array_equal(oracle.decode(to_bits(call.apply()), "f16"), call.oracle_apply())
+
+
+def test_integer_exact_shrink_bitwise():
+    rng = np.random.default_rng(77)
+    X, A, B, Y0 = workloads.integer_exact(rng, 40, 512, 64, 32, 3, "bf16", 4, 64)
+    seg, lidx = [0, 1, 21, 40], [2, 0, 1]
+    call = DeviceCall("bf16", X, A, B, Y0, seg, lidx)
+    V = call.shrink().cpu().numpy().astype(np.float64)
+    assert np.array_equal(V, oracle.sgmv_shrink("bf16", X, A, seg, lidx))
+
+
+# ------------------------------------------------------------ edge cases
+
+def rand_inputs(seed, n, h_in, h_out, rank, P, dtype="f16"):
+    rng = np.random.default_rng(seed)
+    X = workloads.to_bits(rng.standard_normal((n, h_in), dtype=np.float32), dtype)
+    A = workloads.to_bits(rng.standard_normal((P, h_in, rank), dtype=np.float32) / np.sqrt(h_in), dtype)
+    B = workloads.to_bits(rng.standard_normal((P, rank, h_out), dtype=np.float32) / np.sqrt(rank), dtype)
+    Y0 = workloads.to_bits(rng.standard_normal((n, h_out), dtype=np.float32), dtype)
+    return X, A, B, Y0
+
+
+@pytest.mark.parametrize("variant", APPLY_VARIANTS)
+def test_empty_unsorted_repeated_segments_and_uncovered_rows(variant):
+    X, A, B, Y0 = rand_inputs(1, 20, 256, 128, 16, 5)
+    seg, lidx = [0, 0, 3, 3, 4, 9, 9, 15], [4, 2, 2, 0, 1, 3, 2]   # rows 15.. uncovered
+    call = DeviceCall("f16", X, A, B, Y0, seg, lidx, variant=variant)
+    got = to_bits(call.apply())
+    assert_close(got, call.oracle_apply(), "f16")
+    assert np.array_equal(got[15:], Y0[15:])
+    assert call.counters_clear()
+
+
+@pytest.mark.parametrize("variant", APPLY_VARIANTS)
+def test_no_segments_is_a_no_op(variant):
+    X, A, B, Y0 = rand_inputs(2, 8, 64, 64, 8, 2)
+    call = DeviceCall("f16", X, A, B, Y0, [0], [], variant=variant)
+    assert np.array_equal(to_bits(call.apply()), Y0)
+    call2 = DeviceCall("f16", X, A, B, Y0, [0, 0, 0], [1, 0], variant=variant)
+    assert np.array_equal(to_bits(call2.apply()), Y0)
+
+
+@pytest.mark.parametrize("variant", APPLY_VARIANTS)
+@pytest.mark.parametrize("h_in,h_out", [(8, 8), (24, 40), (4104, 1000), (11008, 8)])
+def test_ragged_hidden_sizes(h_in, h_out, variant):
+    X, A, B, Y0 = rand_inputs(3, 6, h_in, h_out, 16, 3, "bf16")
+    call = DeviceCall("bf16", X, A, B, Y0, [0, 2, 3, 6], [2, 0, 1], variant=variant)
+    assert_close(to_bits(call.apply()), call.oracle_apply(), "bf16")
+
+
+@pytest.mark.parametrize("variant", APPLY_VARIANTS)
+@pytest.mark.parametrize("rank", [8, 32, 64])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_ranks(rank, dtype, variant):
+    X, A, B, Y0 = rand_inputs(4 + rank, 40, 1024, 768, rank, 6, dtype)
+    seg, lidx = [0, 1, 2, 6, 7, 23, 24, 40], [5, 0, 3, 3, 1, 2, 4]
+    call = DeviceCall(dtype, X, A, B, Y0, seg, lidx, variant=variant)
+    assert_close(to_bits(call.apply()), call.oracle_apply(), dtype)
+
+
+@pytest.mark.parametrize("variant", APPLY_VARIANTS)
+def test_one_long_segment(variant):
+    X, A, B, Y0 = rand_inputs(5, 300, 512, 256, 16, 2)
+    call = DeviceCall("f16", X, A, B, Y0, [0, 300], [1], variant=variant)
+    assert_close(to_bits(call.apply()), call.oracle_apply(), "f16")
+
+
+@pytest.mark.parametrize("variant", APPLY_VARIANTS)
+def test_many_segments_more_than_a_wave(variant):
+    # 150 segments mixing lengths 0..3 (unit lookup scans segments 64 at a time)
+    rng = np.random.default_rng(6)
+    lens = rng.integers(0, 4, size=150)
+    seg = np.concatenate([[0], np.cumsum(lens)])
+    n = int(seg[-1]) + 5
+    X, A, B, Y0 = rand_inputs(6, n, 128, 64, 8, 7)
+    call = DeviceCall("f16", X, A, B, Y0, seg, rng.integers(0, 7, size=150), variant=variant)
+    assert_close(to_bits(call.apply()), call.oracle_apply(), "f16")
+
+
+def test_max_seg_len_bound_above_actual():
+    """max_seg_len is an upper bound: a looser bound must not change the result."""
+    X, A, B, Y0 = rand_inputs(8, 12, 256, 256, 16, 3)
+    seg, lidx = [0, 2, 3, 12], [1, 0, 2]
+    ref = None
+    for bound in (9, 12):
+        call = DeviceCall("f16", X, A, B, Y0, seg, lidx, max_seg_len=bound)
+        got = to_bits(call.apply())
+        ref = call.oracle_apply() if ref is None else ref
+        assert_close(got, ref, "f16")
+
+
+# ------------------------------------------------------------ the separate stages
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("rank", [8, 16, 64])
+def test_shrink_matches_oracle(dtype, rank):
+    X, A, B, Y0 = rand_inputs(9, 30, 2048, 64, rank, 4, dtype)
+    seg, lidx = [0, 1, 9, 9, 25], [3, 0, 1, 2]           # rows 25..29 uncovered
+    call = DeviceCall(dtype, X, A, B, Y0, seg, lidx)
+    V = call.shrink().cpu().numpy()
+    ref = oracle.sgmv_shrink(dtype, X, A, seg, lidx)
+    assert_close_f32(V[:25].astype(np.float64), ref[:25])
+    assert np.isnan(V[25:]).all()
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_expand_matches_oracle(dtype):
+    import torch
+    X, A, B, Y0 = rand_inputs(10, 30, 64, 3000, 32, 4, dtype)
+    seg, lidx = [0, 7, 8, 20], [1, 3, 0]
+    rng = np.random.default_rng(11)
+    Vh = rng.standard_normal((30, 32)).astype(np.float32)
+    call = DeviceCall(dtype, X, A, B, Y0, seg, lidx)
+    got = to_bits(call.expand(torch.from_numpy(Vh).cuda()))
+    ref = oracle.sgmv_expand(dtype, Vh.astype(np.float64), B, seg, lidx, Y0)
+    assert_close(got, ref, dtype)
+    assert np.array_equal(got[20:], Y0[20:])
+
+
+def test_results_are_deterministic():
+    call = run_workload(workloads.popularity("skewed", 64), sg.SGMV_VARIANT_AUTO)
+    first = to_bits(call.apply())
+    for _ in range(3):
+        call.reset_y()
+        assert np.array_equal(to_bits(call.apply()), first)
+
+
+def test_back_to_back_calls_share_workspace():
+    """Calls of different shapes on one workspace (counters must come back to zero)."""
+    import torch
+    calls = [run_workload(workloads.decode_distinct(seed=30 + i, n=8 + 8 * i, h=1024)) for i in range(3)]
+    nbytes = max(sg.sgmv_workspace_bytes(c.problem) for c in calls)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    for rep in range(2):
+        for c in calls:
+            c.ws = ws
+            c.reset_y()
+            assert_close(to_bits(c.apply()), c.oracle_apply(), "f16")
+    assert bool((ws[: sg.SGMV_WS_COUNTER_BYTES] == 0).all().item())
