@@ -73,7 +73,53 @@ size_t v_area_bytes(const sgmv_problem_t& p) {
   return (size_t)round_up((int64_t)p.n_rows * p.rank * (int64_t)sizeof(float), 256);
 }
 
-int device_capacity(int dtype, int rank, int rb) {
+// Plan of one decode-kernel launch (sgmv_lora_apply on short segments).
+struct DecodePlan {
+  bool supported = false;  // shapes the decode kernel takes
+  int rb = 1;
+  int direct = 1;
+  int64_t num_units = 0;
+  int splits = 1;
+  int kc = 8;
+  int cw = 8;
+  int64_t grid = 0;
+  size_t slot_bytes = 0;
+};
+
+// Aim for one workgroup per CU: each decode workgroup keeps 32+ KiB of loads
+// in flight, so 256 of them cover the HBM latency-bandwidth product.
+constexpr int kDecodeTargetWorkgroups = 256;
+
+DecodePlan plan_decode(const sgmv_problem_t& p) {
+  DecodePlan d;
+  d.rb = pick_rb(p.max_seg_len);
+  if (!sgmv::decode_supported(p.rank, d.rb)) return d;
+  if (p.max_seg_len <= d.rb) {
+    d.direct = 1;
+    d.num_units = p.num_segs;
+  } else {
+    d.direct = 0;
+    const int64_t per_seg = ceil_div(p.max_seg_len, d.rb);
+    d.num_units = std::min<int64_t>((int64_t)p.num_segs * per_seg, ceil_div(p.n_rows, d.rb) + p.num_segs);
+  }
+  const int64_t gmin = std::max(ceil_div(p.h_in, sgmv::decode_max_kc(p.rank)),
+                                ceil_div(p.h_out, sgmv::decode_max_cw()));
+  const int64_t gmax = std::min<int64_t>({ceil_div(p.h_in, 8), ceil_div(p.h_out, 8), (int64_t)kMaxSplits});
+  if (gmin > gmax) return d;
+  int64_t g = p.splits > 0 ? p.splits
+                           : ceil_div(kDecodeTargetWorkgroups, std::max<int64_t>(d.num_units, 1));
+  g = std::max(gmin, std::min(g, gmax));
+  d.splits = (int)g;
+  d.kc = (int)round_up(ceil_div(p.h_in, g), 8);
+  d.cw = (int)round_up(ceil_div(p.h_out, g), 8);
+  d.grid = 8 * ceil_div(d.num_units, 8) * g;
+  const int parts = d.rb == 1 ? 4 : 1;  // partials published per workgroup
+  d.slot_bytes = (size_t)d.num_units * (size_t)g * parts * d.rb * p.rank * sizeof(uint64_t);
+  d.supported = d.grid > 0 && d.grid <= (int64_t)INT32_MAX;
+  return d;
+}
+
+int decode_capacity(int dtype, int rank, int rb) {
   static std::mutex mu;
   static int cache[kMaxDevices][2][4][3];
   static bool init[kMaxDevices][2][4][3];
@@ -83,7 +129,7 @@ int device_capacity(int dtype, int rank, int rb) {
   const int bi = rb == 1 ? 0 : rb == 4 ? 1 : 2;
   std::lock_guard<std::mutex> lock(mu);
   if (!init[dev][dtype][ri][bi]) {
-    cache[dev][dtype][ri][bi] = sgmv::fused_resident_capacity(dtype, rank, rb);
+    cache[dev][dtype][ri][bi] = sgmv::decode_resident_capacity(dtype, rank, rb);
     init[dev][dtype][ri][bi] = true;
   }
   return cache[dev][dtype][ri][bi];
@@ -118,17 +164,21 @@ VecParams base_params(const sgmv_problem_t& p, const VecPlan& v, const int32_t* 
 
 sgmv_status_t hip_status(hipError_t e) { return e == hipSuccess ? SGMV_OK : SGMV_ERR_HIP; }
 
-// Which kernels a fused apply runs.
-enum class ApplyRoute { kFused, kTwoLaunch };
+// sgmv_lora_apply runs the one-launch decode kernel when its plan fits on the
+// device at once (the kernel's workgroups wait for each other), else the
+// shrink and expand vector kernels as two launches.
+bool use_decode(const sgmv_problem_t& p, const DecodePlan& d) {
+  if (p.variant == SGMV_VARIANT_VECTOR || !d.supported) return false;
+  const int cap = decode_capacity(p.dtype, p.rank, d.rb);
+  return cap > 0 && d.grid <= cap;
+}
 
-ApplyRoute route_apply(const sgmv_problem_t& p, const VecPlan& fused) {
-  if (p.variant == SGMV_VARIANT_VECTOR) return ApplyRoute::kTwoLaunch;
-  const int64_t grid = fused.num_units * fused.splits;
-  const int cap = device_capacity(p.dtype, p.rank, fused.rb);
-  const bool fits = cap > 0 && grid <= cap && 2 * fused.num_units <= kCounterSlots;
-  if (p.variant == SGMV_VARIANT_FUSED) return fits ? ApplyRoute::kFused : ApplyRoute::kTwoLaunch;
-  // AUTO: the fused kernel serves decode-shaped calls whose grid fits on chip.
-  return fits ? ApplyRoute::kFused : ApplyRoute::kTwoLaunch;
+size_t apply_ws_bytes(const sgmv_problem_t& p) {
+  const VecPlan v = plan_vec(p, kTargetWorkgroups);
+  const DecodePlan d = plan_decode(p);
+  const size_t two_launch = vec_ws_bytes(v, p.rank) + v_area_bytes(p);
+  const size_t one_launch = SGMV_WS_COUNTER_BYTES + (d.supported ? d.slot_bytes : 0);
+  return std::max(two_launch, one_launch);
 }
 
 }  // namespace
@@ -225,8 +275,7 @@ sgmv_status_t sgmv_workspace_bytes(const sgmv_problem_t* p, size_t* bytes) {
   if (!bytes) return SGMV_ERR_INVALID_ARG;
   const sgmv_status_t st = sgmv_check_problem(p);
   if (st != SGMV_OK) return st;
-  const VecPlan v = plan_vec(*p, kTargetWorkgroups);
-  *bytes = vec_ws_bytes(v, p->rank) + v_area_bytes(*p);
+  *bytes = apply_ws_bytes(*p);
   return SGMV_OK;
 }
 
@@ -277,24 +326,42 @@ sgmv_status_t sgmv_lora_apply(const sgmv_problem_t* p, const void* X, const void
   if (!X || !A_ptrs || !B_ptrs || !Y || !seg_indptr || !lora_idx) return SGMV_ERR_INVALID_ARG;
   if (!aligned16(X) || !aligned16(Y) || !aligned8(A_ptrs) || !aligned8(B_ptrs))
     return SGMV_ERR_UNSUPPORTED;
-  const VecPlan v = plan_vec(*p, kTargetWorkgroups);
-  const size_t need_fused = vec_ws_bytes(v, p->rank);
-  // The two-launch route keeps the fp32 intermediate V [n_rows, rank] after the
-  // shrink's own split partials.
-  const size_t v_bytes = v_area_bytes(*p);
-  if (!ws || ws_bytes < need_fused) return SGMV_ERR_WORKSPACE;
+  if (!ws) return SGMV_ERR_WORKSPACE;
   if (!aligned16(ws)) return SGMV_ERR_UNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const DecodePlan d = plan_decode(*p);
+  if (use_decode(*p, d)) {
+    if (ws_bytes < SGMV_WS_COUNTER_BYTES + d.slot_bytes) return SGMV_ERR_WORKSPACE;
+    sgmv::DecodeParams q{};
+    q.X = static_cast<const uint16_t*>(X);
+    q.A_ptrs = reinterpret_cast<const uint64_t*>(A_ptrs);
+    q.B_ptrs = reinterpret_cast<const uint64_t*>(B_ptrs);
+    q.Y = static_cast<uint16_t*>(Y);
+    q.seg_indptr = seg_indptr;
+    q.lora_idx = lora_idx;
+    q.slots = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + SGMV_WS_COUNTER_BYTES);
+    q.n_rows = p->n_rows;
+    q.h_in = p->h_in;
+    q.h_out = p->h_out;
+    q.num_segs = p->num_segs;
+    q.num_loras = p->num_loras;
+    q.num_units = (int32_t)d.num_units;
+    q.splits = d.splits;
+    q.kc = d.kc;
+    q.cw = d.cw;
+    q.direct_units = d.direct;
+    return hip_status(sgmv::launch_decode(p->dtype, p->rank, d.rb, q, s));
+  }
+  // Two launches: shrink into V (held after the shrink's split partials), then expand.
+  const VecPlan v = plan_vec(*p, kTargetWorkgroups);
+  const size_t need = vec_ws_bytes(v, p->rank);
+  if (ws_bytes < need + v_area_bytes(*p)) return SGMV_ERR_WORKSPACE;
   VecParams q = base_params(*p, v, seg_indptr, lora_idx, ws);
   q.X = static_cast<const uint16_t*>(X);
   q.A_ptrs = reinterpret_cast<const uint64_t*>(A_ptrs);
   q.B_ptrs = reinterpret_cast<const uint64_t*>(B_ptrs);
   q.Y = static_cast<uint16_t*>(Y);
-  if (route_apply(*p, v) == ApplyRoute::kFused)
-    return hip_status(sgmv::launch_vec(p->dtype, p->rank, v.rb, sgmv::kModeFused, q, s));
-  // Two launches: shrink into V (held at the end of the workspace), then expand.
-  if (ws_bytes < need_fused + v_bytes) return SGMV_ERR_WORKSPACE;
-  q.V = reinterpret_cast<float*>(static_cast<char*>(ws) + need_fused);
+  q.V = reinterpret_cast<float*>(static_cast<char*>(ws) + need);
   hipError_t e = sgmv::launch_vec(p->dtype, p->rank, v.rb, sgmv::kModeShrink, q, s);
   if (e != hipSuccess) return SGMV_ERR_HIP;
   return hip_status(sgmv::launch_vec(p->dtype, p->rank, v.rb, sgmv::kModeExpand, q, s));

@@ -1,0 +1,398 @@
+// sgmv_decode.hip - one-launch SGMV for decode-shaped segments (gfx950).
+//
+// Computes the LoRA term of the Punica README (page "Punica：多 LoRA 模型统一服务框架",
+// LoRA and multi-LoRA paragraphs), Y[i] += (X[i] @ A_k) @ B_k, for segments of
+// at most RB rows per unit, in a single launch:
+//
+//   * `splits` workgroups share a unit; split g owns input rows
+//     [g*kc, (g+1)*kc) of A_k and output columns [g*cw, (g+1)*cw) of B_k.
+//   * Every workgroup issues all of its HBM loads (its A_k chunk, X values,
+//     its B_k chunk and Y values) up front in straight-line code, so the whole
+//     call is in flight at once.
+//   * Shrink partial sums are reduced inside each wave, then published as
+//     64-bit words {fp32 value, launch tag}: one device-coherent atomic store
+//     carries both the datum and its validity, so no counter, fence or cache
+//     flush is needed.  Each workgroup polls the partials of its unit until
+//     every tag matches, sums them in a fixed order (bitwise reproducible),
+//     and expands its column chunk with the B_k values it already holds in
+//     registers (each thread consumes exactly the B_k vectors it loaded).
+//   * The launch tag mixes the dispatch packet id with the queue address, so it
+//     changes on every launch, including replays of a captured graph; it is
+//     always odd, so a zero-filled workspace never matches.
+//   * The workgroups of one unit are placed on one XCD (workgroups are
+//     dispatched round-robin over the 8 XCDs), which keeps the exchange local.
+//   * The grid is sized by the host to be co-resident, so every wait ends.
+#include "sgmv_device.h"
+#include "sgmv_plan.h"
+#include "sgmv_units.h"
+
+// The packet id of the current kernel dispatch (LLVM intrinsic; it makes the
+// runtime pass the id in user SGPRs).
+extern "C" __device__ unsigned long long sgmv_llvm_dispatch_id() __asm("llvm.amdgcn.dispatch.id");
+
+namespace sgmv {
+namespace {
+
+constexpr int kXcds = 8;
+constexpr int kPollPerThread = 8;
+constexpr int kStage = kThreads * kPollPerThread;
+
+__device__ inline uint32_t launch_tag() {
+  const uint64_t did = sgmv_llvm_dispatch_id();
+  const uint64_t q = reinterpret_cast<uint64_t>(__builtin_amdgcn_queue_ptr());
+  const uint32_t qh = (uint32_t)(q >> 12) * 0x9E3779B1u;
+  return (((uint32_t)did ^ qh) << 1) | 1u;
+}
+
+__device__ inline void publish_tagged(uint64_t* slot, float v, uint32_t tag) {
+  const uint64_t w = ((uint64_t)tag << 32) | __float_as_uint(v);
+  __hip_atomic_store(slot, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline uint64_t fetch_tagged(const uint64_t* slot) {
+  return __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Value of a 64-bit lane variable in lane `l` (l uniform over the wave).
+__device__ inline uint64_t readlane_u64(uint64_t v, int l) {
+  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Lane exchanges inside a quad of lanes (DPP, no LDS traffic).
+__device__ inline float quad_xor1(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+__device__ inline float quad_xor2(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+}
+
+template <int H>
+__device__ inline void halve(float (&v)[8], int lane, int mask) {
+  const bool upper = (lane & mask) != 0;
+#pragma unroll
+  for (int q = 0; q < H; ++q) {
+    const float send = upper ? v[q] : v[q + H];
+    const float keep = upper ? v[q + H] : v[q];
+    v[q] = keep + shfl_xor(send, mask);
+  }
+}
+
+template <int R>
+constexpr int log2_groups() {
+  return R == 8 ? 0 : R == 16 ? 1 : R == 32 ? 2 : 3;
+}
+
+// SMALL: at most 64 LoRAs (pointer tables fetched one entry per lane).
+template <class T, int R, int RB, bool SMALL>
+__global__ __launch_bounds__(kThreads) void sgmv_decode_kernel(DecodeParams p) {
+  constexpr int JG = R / 8;                  // 128-bit vectors per row of A_k
+  constexpr int B0 = log2_groups<R>();
+  constexpr int HS = kThreads / JG;          // A_k rows covered by one sweep of the workgroup
+  constexpr int NA = kDecodeRowsPerThread;   // A_k rows per thread
+  constexpr int KCMAX = NA * HS;             // = decode_max_kc(R)
+  constexpr int JQ = kDecodeLanesPerColumn;  // lanes sharing one 8-column vector of B_k
+  constexpr int NB = R / JQ;                 // B_k vectors per thread
+  constexpr int NY = (RB + JQ - 1) / JQ;     // Y vectors per thread
+  constexpr int PW = RB == 1 ? kWaves : 1;   // published partials per workgroup
+  constexpr int NXV = RB == 1 ? 1 : (RB * KCMAX / 8 + kThreads - 1) / kThreads;
+  static_assert(RB * R <= kThreads, "one output of V per thread");
+
+  __shared__ __attribute__((aligned(16))) uint16_t lds_x[RB == 1 ? 8 : RB * KCMAX];
+  __shared__ float lds_red[RB == 1 ? 1 : kWaves * RB * R];
+  __shared__ float lds_stage[kStage];
+  __shared__ float lds_v[RB * R];
+
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int G = p.splits;
+  // Workgroups go round-robin over the XCDs: keep the splits of a unit on one.
+  const int xcd = blockIdx.x % kXcds;
+  const int slot = blockIdx.x / kXcds;
+  const int unit = (slot / G) * kXcds + xcd;
+  const int g = slot - (slot / G) * G;
+  if (unit >= p.num_units) return;
+  // With at most 64 LoRAs, fetch both pointer tables (one entry per lane) in
+  // parallel with the segment metadata instead of after it: the LoRA id then
+  // selects its pointers from registers, saving one dependent memory trip.
+  uint64_t a_lane = 0, b_lane = 0;
+  if (SMALL && lane < p.num_loras) {
+    a_lane = p.A_ptrs[lane];
+    b_lane = p.B_ptrs[lane];
+  }
+  const Unit un = resolve_unit<RB>(p.seg_indptr, p.lora_idx, p.num_segs, p.num_loras, p.n_rows,
+                                   p.direct_units, unit);
+  if (un.L <= 0) return;  // uniform over the workgroup (and over the unit)
+  const int L = un.L;
+  const int r0 = un.r0;
+  const uint32_t tag = launch_tag();
+
+  const uint16_t* Ak;
+  const uint16_t* Bk;
+  if constexpr (SMALL) {
+    Ak = reinterpret_cast<const uint16_t*>(readlane_u64(a_lane, un.k));
+    Bk = reinterpret_cast<const uint16_t*>(readlane_u64(b_lane, un.k));
+  } else {
+    Ak = reinterpret_cast<const uint16_t*>(p.A_ptrs[un.k]);
+    Bk = reinterpret_cast<const uint16_t*>(p.B_ptrs[un.k]);
+  }
+  const int h0 = g * p.kc;
+  const int h1 = p.h_in < h0 + p.kc ? p.h_in : h0 + p.kc;
+  const int c0 = g * p.cw;
+  const int c1 = p.h_out < c0 + p.cw ? p.h_out : c0 + p.cw;
+  const uint16_t* Xr = p.X + (int64_t)r0 * p.h_in;
+  uint16_t* Yr = p.Y + (int64_t)r0 * p.h_out;
+
+  // ---------------- all loads, issued up front ----------------
+  // Shrink: thread t owns ranks (t % JG)*8..+7 of rows h0 + t/JG + q*HS.
+  const int jg = t % JG;
+  u32x4 av[NA];
+#pragma unroll
+  for (int q = 0; q < NA; ++q) {
+    const int h = h0 + t / JG + q * HS;
+    av[q] = load_stream(Ak + (h < h1 ? (int64_t)h * R + jg * 8 : 0));
+  }
+  uint16_t xs[RB == 1 ? NA : 1];
+  u32x4 xv[NXV];
+  if constexpr (RB == 1) {
+#pragma unroll
+    for (int q = 0; q < NA; ++q) {
+      const int h = h0 + t / JG + q * HS;
+      xs[q] = load_stream_u16(Xr + (h < h1 ? h : 0));
+    }
+  } else {
+    const int xvr = (h1 - h0) / 8;  // 128-bit vectors per row of the chunk
+#pragma unroll
+    for (int q = 0; q < NXV; ++q) {
+      const int x = t + kThreads * q;
+      const int i = xvr > 0 ? x / xvr : 0, c = x - i * xvr;
+      xv[q] = load_stream(Xr + (x < L * xvr ? (int64_t)i * p.h_in + h0 + c * 8 : 0));
+    }
+  }
+  // Expand: thread t owns the 8 columns c0 + (t / JQ)*8 .. +7 and ranks
+  // jq, jq + JQ, ... of B_k; lane jq also carries the Y rows i = jq + n*JQ.
+  const int jq = t % JQ;
+  const int col = c0 + (t / JQ) * 8;
+  const bool col_ok = col < c1;
+  u32x4 bv[NB];
+#pragma unroll
+  for (int m = 0; m < NB; ++m)
+    bv[m] = load_stream(Bk + (col_ok ? (int64_t)(jq + JQ * m) * p.h_out + col : 0));
+  u32x4 yv[NY];
+#pragma unroll
+  for (int n = 0; n < NY; ++n) {
+    const int i = jq + JQ * n;
+    yv[n] = load_stream(Yr + (col_ok && i < L ? (int64_t)i * p.h_out + col : 0));
+  }
+
+  // ---------------- shrink ----------------
+  float acc[RB][8];
+#pragma unroll
+  for (int i = 0; i < RB; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[i][e] = 0.f;
+  if constexpr (RB > 1) {
+    const int xvr = (h1 - h0) / 8;
+#pragma unroll
+    for (int q = 0; q < NXV; ++q) {
+      const int x = t + kThreads * q;
+      if (x < L * xvr) {
+        const int i = x / xvr, c = x - i * xvr;
+        store_vec(&lds_x[i * KCMAX + c * 8], xv[q]);
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int q = 0; q < NA; ++q) {
+    const int hl = t / JG + q * HS;  // row inside the chunk
+    if (h0 + hl < h1) {
+      float af[8];
+      unpack8<T>(av[q], af);
+#pragma unroll
+      for (int i = 0; i < RB; ++i) {
+        if (i < L) {
+          const float xf = RB == 1 ? T::one(xs[q]) : T::one(lds_x[i * KCMAX + hl]);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[i][e] = __builtin_fmaf(xf, af[e], acc[i][e]);
+        }
+      }
+    }
+  }
+  // Reduce each row's partial ranks over the lanes that share them (lane bits
+  // B0..5); afterwards lane l < R of every wave holds rank
+  // (l % JG)*8 + e(l) of the wave's partial.
+  const int j_of_lane = (lane & (JG - 1)) * 8 + ((lane >> B0) & 1) * 4 + ((lane >> (B0 + 1)) & 1) * 2 +
+                        ((lane >> (B0 + 2)) & 1);
+  const bool rank_lane = (lane >> (B0 + 3)) == 0;
+#pragma unroll
+  for (int i = 0; i < RB; ++i) {
+    if (i < L) {
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = acc[i][e];
+      halve<4>(v, lane, 1 << B0);
+      halve<2>(v, lane, 1 << (B0 + 1));
+      halve<1>(v, lane, 1 << (B0 + 2));
+#pragma unroll
+      for (int b = B0 + 3; b < 6; ++b) v[0] += shfl_xor(v[0], 1 << b);
+      acc[i][0] = v[0];
+    }
+  }
+
+  // ---------------- publish ----------------
+  // Per-unit slot layout: [G][PW][RB*R] tagged words.
+  uint64_t* unit_slots = p.slots + (int64_t)unit * G * PW * (RB * R);
+  if constexpr (RB == 1) {
+    if (rank_lane) publish_tagged(unit_slots + ((int64_t)g * PW + wave) * R + j_of_lane, acc[0][0], tag);
+  } else {
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+      if (i < L && rank_lane) lds_red[(wave * RB + i) * R + j_of_lane] = acc[i][0];
+    __syncthreads();
+    if (t < L * R) {
+      float s = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) s += lds_red[w * RB * R + t];
+      publish_tagged(unit_slots + (int64_t)g * (RB * R) + t, s, tag);
+    }
+  }
+
+  // ---------------- gather: wait for every split of the unit ----------------
+  const int n_out = L * R;                    // outputs of V for this unit
+  const int parts = G * PW;                   // partials per output
+  const int per_round = kStage / n_out;       // partials staged per round (>= 1)
+  float vsum = 0.f;
+  for (int p0 = 0; p0 < parts; p0 += per_round) {
+    const int pn = parts - p0 < per_round ? parts - p0 : per_round;
+    const int items = pn * n_out;
+    uint64_t w[kPollPerThread];
+    const uint64_t* src[kPollPerThread];
+#pragma unroll
+    for (int m = 0; m < kPollPerThread; ++m) {
+      const int it = t + kThreads * m;
+      const int pp = it / n_out, o = it - pp * n_out;
+      src[m] = unit_slots + (it < items ? (int64_t)(p0 + pp) * (RB * R) + o : 0);
+      w[m] = fetch_tagged(src[m]);
+    }
+    for (;;) {
+      bool done = true;
+#pragma unroll
+      for (int m = 0; m < kPollPerThread; ++m)
+        if (t + kThreads * m < items && (uint32_t)(w[m] >> 32) != tag) done = false;
+      if (done) break;
+      __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+      for (int m = 0; m < kPollPerThread; ++m)
+        if (t + kThreads * m < items && (uint32_t)(w[m] >> 32) != tag) w[m] = fetch_tagged(src[m]);
+    }
+#pragma unroll
+    for (int m = 0; m < kPollPerThread; ++m) {
+      const int it = t + kThreads * m;
+      if (it < items) lds_stage[it] = __uint_as_float((uint32_t)w[m]);
+    }
+    __syncthreads();
+    if (t < n_out)
+      for (int pp = 0; pp < pn; ++pp) vsum += lds_stage[pp * n_out + t];
+    __syncthreads();
+  }
+  if (t < n_out) lds_v[t] = vsum;
+  __syncthreads();
+
+  // ---------------- expand ----------------
+  float bf[NB][8];
+#pragma unroll
+  for (int m = 0; m < NB; ++m) unpack8<T>(bv[m], bf[m]);
+#pragma unroll
+  for (int i = 0; i < RB; ++i) {
+    if (i < L) {
+      float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = 0; m < NB; ++m) {
+        const float vj = lds_v[i * R + jq + JQ * m];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s[e] = __builtin_fmaf(vj, bf[m][e], s[e]);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        s[e] += quad_xor1(s[e]);
+        s[e] += quad_xor2(s[e]);
+      }
+      if (col_ok && jq == i % JQ) {
+        float yf[8];
+        unpack8<T>(yv[i / JQ], yf);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) yf[e] += s[e];
+        store_vec(Yr + (int64_t)i * p.h_out + col, pack8<T>(yf));
+      }
+    }
+  }
+}
+
+template <class T, int R, int RB>
+hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
+  const unsigned grid = (unsigned)kXcds * (unsigned)((p.num_units + kXcds - 1) / kXcds) * (unsigned)p.splits;
+  if (grid == 0) return hipSuccess;
+  if (p.num_loras <= 64)
+    hipLaunchKernelGGL((sgmv_decode_kernel<T, R, RB, true>), dim3(grid), dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((sgmv_decode_kernel<T, R, RB, false>), dim3(grid), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+// Both pool variants use the same registers and LDS within a few VGPRs; the
+// smaller of the two occupancies is reported.
+template <class T, int R, int RB>
+int capacity_t() {
+  int per_cu = 0, per_cu2 = 0, dev = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &per_cu, reinterpret_cast<const void*>(&sgmv_decode_kernel<T, R, RB, true>), kThreads, 0) != hipSuccess)
+    return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &per_cu2, reinterpret_cast<const void*>(&sgmv_decode_kernel<T, R, RB, false>), kThreads, 0) != hipSuccess)
+    return 0;
+  per_cu = per_cu < per_cu2 ? per_cu : per_cu2;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return per_cu * cus;
+}
+
+// Instantiated (rank, rows per unit) pairs: rank * RB <= 256.
+template <class T>
+hipError_t dispatch(int rank, int rb, const DecodeParams& p, hipStream_t s, int* cap) {
+#define SGMV_DECODE_CASE(R_, RB_)                          \
+  if (rank == R_ && rb == RB_) {                           \
+    if (cap) {                                             \
+      *cap = capacity_t<T, R_, RB_>();                     \
+      return hipSuccess;                                   \
+    }                                                      \
+    return launch_t<T, R_, RB_>(p, s);                     \
+  }
+  SGMV_DECODE_CASE(8, 1) SGMV_DECODE_CASE(8, 4) SGMV_DECODE_CASE(8, 16)
+  SGMV_DECODE_CASE(16, 1) SGMV_DECODE_CASE(16, 4) SGMV_DECODE_CASE(16, 16)
+  SGMV_DECODE_CASE(32, 1) SGMV_DECODE_CASE(32, 4)
+  SGMV_DECODE_CASE(64, 1) SGMV_DECODE_CASE(64, 4)
+#undef SGMV_DECODE_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool decode_supported(int rank, int rb) { return rank * rb <= kThreads && (rb == 1 || rb == 4 || rb == 16); }
+
+hipError_t launch_decode(int dtype, int rank, int rb, const DecodeParams& p, hipStream_t stream) {
+  return dtype == 1 ? dispatch<BF16>(rank, rb, p, stream, nullptr)
+                    : dispatch<F16>(rank, rb, p, stream, nullptr);
+}
+
+int decode_resident_capacity(int dtype, int rank, int rb) {
+  int cap = 0;
+  if (dtype == 1)
+    (void)dispatch<BF16>(rank, rb, DecodeParams{}, nullptr, &cap);
+  else
+    (void)dispatch<F16>(rank, rb, DecodeParams{}, nullptr, &cap);
+  return cap;
+}
+
+}  // namespace sgmv

@@ -56,27 +56,48 @@ __device__ inline u32x4 pack8(const float (&f)[8]) {
 
 // 128-bit loads of data that is read exactly once per call (LoRA weights,
 // X, Y): the non-temporal hint keeps them from displacing reusable lines.
+// (Pointers read from the LoRA tables are generic; the cast lets the compiler
+// use global instead of flat loads.)
+typedef const __attribute__((address_space(1))) u32x4* global_u32x4_ptr;
+typedef const __attribute__((address_space(1))) uint16_t* global_u16_ptr;
 __device__ inline u32x4 load_stream(const void* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return __builtin_nontemporal_load((global_u32x4_ptr)p);
+}
+__device__ inline uint16_t load_stream_u16(const uint16_t* p) {
+  return __builtin_nontemporal_load((global_u16_ptr)p);
 }
 __device__ inline u32x4 load_vec(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ inline void store_vec(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
 
 __device__ inline float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }
 
-// Cross-workgroup hand-off through global counters (device scope).  The
-// release publishes this workgroup's earlier global writes; the acquire makes
-// other workgroups' published writes visible to this one.
-__device__ inline uint32_t counter_add_release(uint32_t* c, uint32_t v) {
-  return __hip_atomic_fetch_add(c, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+// Cross-workgroup hand-off (device scope) without whole-cache maintenance.
+// Agent-scope release/acquire fences lower to a write-back / invalidate of the
+// entire L2 of the XCD on gfx950, which costs far more than the few hundred
+// bytes handed over here.  Instead, every datum that crosses workgroups is
+// itself a relaxed device-scope atomic access (sc1: written through to, and
+// read from, the device-coherent level), and ordering comes from waiting for
+// the stores to complete before the counter update that announces them.
+__device__ inline void publish_f32(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ inline uint32_t counter_load_acquire(const uint32_t* c) {
-  return __hip_atomic_load(c, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+__device__ inline float fetch_published_f32(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ inline void counter_store_relaxed(uint32_t* c, uint32_t v) {
+// Wait until every memory operation this thread issued has completed.
+__device__ inline void wait_memory_ops() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+__device__ inline uint32_t counter_add(uint32_t* c, uint32_t v) {
+  return __hip_atomic_fetch_add(c, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline uint32_t counter_load(const uint32_t* c) {
+  return __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void counter_store(uint32_t* c, uint32_t v) {
   __hip_atomic_store(c, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ inline void fence_acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
-__device__ inline void fence_release_agent() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
 
 }  // namespace sgmv

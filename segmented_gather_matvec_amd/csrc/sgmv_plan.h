@@ -6,11 +6,10 @@
 
 namespace sgmv {
 
-// Vector (split-K) kernels: one template, three modes.
+// Vector (split-K) kernels: one template, two modes.
 enum VecMode : int {
   kModeShrink = 0,  // V = X @ A_k (partials reduced by the last-arriving workgroup)
-  kModeExpand = 1,  // Y += V @ B_k
-  kModeFused = 2    // both, partial V handed over on chip; grid must be co-resident
+  kModeExpand = 1   // Y += V @ B_k
 };
 
 // A "unit" is one row block (<= RB rows) of one segment; each unit is worked by
@@ -42,7 +41,27 @@ constexpr int vec_cols_per_pass(int rank) { return 256 * 2 * 8 / rank; }
 // Launch one vector kernel; returns the HIP error of the launch.
 hipError_t launch_vec(int dtype, int rank, int rb, int mode, const VecParams& p, hipStream_t stream);
 
-// Workgroups of the fused kernel that fit on the device at once (0 if unknown).
-int fused_resident_capacity(int dtype, int rank, int rb);
+// One-launch decode kernel (shrink, on-chip hand-off, expand).
+constexpr int kDecodeRowsPerThread = 4;   // A_k rows (128-bit vectors) per thread
+constexpr int kDecodeLanesPerColumn = 4;  // lanes sharing one 8-column vector of B_k
+constexpr int decode_max_kc(int rank) { return kDecodeRowsPerThread * 256 / (rank / 8); }
+constexpr int decode_max_cw() { return 256 / kDecodeLanesPerColumn * 8; }
+
+struct DecodeParams {
+  const uint16_t* X;
+  const uint64_t* A_ptrs;
+  const uint64_t* B_ptrs;
+  uint16_t* Y;
+  const int32_t* seg_indptr;
+  const int32_t* lora_idx;
+  uint64_t* slots;  // [num_units][splits][parts][RB*rank] tagged partials
+  int32_t n_rows, h_in, h_out, num_segs, num_loras;
+  int32_t num_units, splits, kc, cw, direct_units;
+};
+
+bool decode_supported(int rank, int rb);
+hipError_t launch_decode(int dtype, int rank, int rb, const DecodeParams& p, hipStream_t stream);
+// Workgroups of the decode kernel that fit on the device at once (0 if unknown).
+int decode_resident_capacity(int dtype, int rank, int rb);
 
 }  // namespace sgmv
