@@ -11,9 +11,13 @@ Infinity Cache, the 32 LoRAs of call c are drawn from a pool of 4096
 
 Prints one JSON line: value = whole-job algorithmic GB/s over the timed steps
 (K back-to-back launches, wall time between two device synchronisations);
-roofline.achieved = algorithmic bytes per launch / mean kernel duration from
-HIP events around each launch (a second, separate pass); cpu_baseline = the
-fp64 oracle timed on the host cores on a bounded sample of the same workload.
+roofline.achieved = algorithmic bytes per launch / mean launch duration from
+HIP events recorded on the launch stream around the same timed region;
+roofline.traffic = HBM bytes per launch from the committed counter runs
+(FETCH_SIZE + WRITE_SIZE scaled by a copy kernel of known size), reported only
+while the kernel sources still match the ones the counters were taken on;
+cpu_baseline = the fp64 oracle timed on the host cores on a bounded sample of
+the same workload.
 """
 from __future__ import annotations
 
@@ -30,10 +34,13 @@ sys.path.insert(0, ROOT)
 
 METRIC = "SGMV shrink+expand achieved HBM GB/s (% peak) and tokens/s, H=4096 r=16 batch 32"
 HBM_PEAK_GBS = 8000.0
-KERNEL_SOURCES = ("segmented_gather_matvec_amd/csrc/sgmv_vector.hip",
+KERNEL_SOURCES = ("segmented_gather_matvec_amd/csrc/sgmv_decode.hip",
                   "segmented_gather_matvec_amd/csrc/sgmv_device.h",
+                  "segmented_gather_matvec_amd/csrc/sgmv_units.h",
+                  "segmented_gather_matvec_amd/csrc/sgmv_plan.h",
                   "segmented_gather_matvec_amd/csrc/sgmv_api.cpp")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sgmv_fused_decode_distinct_h4096_r16_b32_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sgmv_decode_kernel_decode_distinct_h4096_r16_b32_traffic.json")
+COPY_CALIBRATION_BYTES = 512 << 20
 
 
 def kernel_source_hash() -> str:
@@ -174,6 +181,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run 8 plain device copies of 512 MiB (reference for HBM counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -183,6 +192,15 @@ def main():
 
     import torch
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        src = torch.empty(COPY_CALIBRATION_BYTES // 4, dtype=torch.float32, device="cuda").normal_()
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(8):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        torch.cuda.empty_cache()
     variant = {"auto": 0, "vector": 1, "fused": 2}[args.variant]
     bench = DecodeBench(variant=variant, splits=args.splits)
     worst = None if args.no_check else bench.check_sample()
@@ -203,31 +221,24 @@ def main():
         graph.replay()
         torch.cuda.synchronize()
 
-    # Timed region: K steps between two device synchronisations.
-    sid = torch.cuda.current_stream().cuda_stream
+    # Timed region: K steps between two device synchronisations, with HIP
+    # events recorded on the launch stream at both ends.
+    stream = torch.cuda.current_stream()
+    sid = stream.cuda_stream
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    e0.record(stream)
     if graph is not None:
         graph.replay()
     else:
         for c in range(K):
             bench.step(c, sid)
+    e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall / K * 1e3
-
-    # Separate pass: HIP events around each launch on the launch stream.
-    stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(min(K, 1000))]
-    for c, (e0, e1) in enumerate(ev):
-        e0.record(stream)
-        bench.step(c, sid)
-        e1.record(stream)
-    torch.cuda.synchronize()
-    durs = sorted(e0.elapsed_time(e1) * 1e-3 for e0, e1 in ev)
-    mean_kernel_s = sum(durs) / len(durs)
-    median_kernel_s = durs[len(durs) // 2]
+    mean_kernel_s = e0.elapsed_time(e1) * 1e-3 / K
 
     value = bench.bytes * K / wall / 1e9
     achieved = bench.bytes / mean_kernel_s / 1e9
@@ -254,8 +265,7 @@ def main():
         "pct_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(bench.n * K / wall, 1),
         "us_per_call": round(ms_per_step * 1e3, 3),
-        "kernel_us_mean": round(mean_kernel_s * 1e6, 3),
-        "kernel_us_median": round(median_kernel_s * 1e6, 3),
+        "launch_us_mean_events": round(mean_kernel_s * 1e6, 3),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic},
