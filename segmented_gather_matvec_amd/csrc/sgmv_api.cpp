@@ -135,6 +135,66 @@ int decode_capacity(int dtype, int rank, int rb) {
   return cache[dev][dtype][ri][bi];
 }
 
+// Plan of the matrix-core kernels (long segments).
+struct MfmaPlan {
+  int direct = 1;
+  int64_t num_units = 0;
+  int ksplit = 1;
+  int kc = 0;
+  size_t partial_bytes = 0;  // split partials of V, fp32 [ksplit][n_rows][rank]
+};
+
+// Split H1 so that shrink workgroups (row tiles x splits) reach about two per CU.
+constexpr int kMfmaTargetWorkgroups = 512;
+
+MfmaPlan plan_mfma(const sgmv_problem_t& p, bool allow_split) {
+  MfmaPlan m;
+  const int mt = sgmv::kMfmaRowsPerTile;
+  if (p.max_seg_len <= mt) {
+    m.direct = 1;
+    m.num_units = p.num_segs;
+  } else {
+    m.direct = 0;
+    m.num_units = std::min<int64_t>((int64_t)p.num_segs * ceil_div(p.max_seg_len, mt),
+                                    ceil_div(p.n_rows, mt) + p.num_segs);
+  }
+  int64_t ks = 1;
+  if (allow_split)
+    ks = std::max<int64_t>(1, std::min<int64_t>(ceil_div(kMfmaTargetWorkgroups, std::max<int64_t>(m.num_units, 1)),
+                                                ceil_div(p.h_in, sgmv::kMfmaKChunk)));
+  m.kc = (int)round_up(ceil_div(p.h_in, ks), sgmv::kMfmaKChunk);
+  m.ksplit = (int)ceil_div(p.h_in, m.kc);
+  m.partial_bytes = (size_t)m.ksplit * (size_t)p.n_rows * p.rank * sizeof(float);
+  return m;
+}
+
+sgmv::MfmaParams mfma_params(const sgmv_problem_t& p, const MfmaPlan& m, const int32_t* seg_indptr,
+                             const int32_t* lora_idx) {
+  sgmv::MfmaParams q{};
+  q.seg_indptr = seg_indptr;
+  q.lora_idx = lora_idx;
+  q.partial_stride = (int64_t)p.n_rows * p.rank;
+  q.n_rows = p.n_rows;
+  q.h_in = p.h_in;
+  q.h_out = p.h_out;
+  q.num_segs = p.num_segs;
+  q.num_loras = p.num_loras;
+  q.num_units = (int32_t)m.num_units;
+  q.ksplit = m.ksplit;
+  q.kc = m.kc;
+  q.direct_units = m.direct;
+  return q;
+}
+
+// The matrix-core kernels take over segments longer than the decode kernel's
+// row blocks (at ranks 16..64); AUTO picks them when the decode kernel cannot
+// run the call.
+bool stage_uses_mfma(const sgmv_problem_t& p) {
+  if (!sgmv::mfma_supported(p.rank)) return false;
+  if (p.variant == SGMV_VARIANT_MFMA) return true;
+  return p.variant == SGMV_VARIANT_AUTO && p.max_seg_len > 16;
+}
+
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 bool aligned8(const void* p) { return ((uintptr_t)p & 7u) == 0; }
 
@@ -178,7 +238,10 @@ size_t apply_ws_bytes(const sgmv_problem_t& p) {
   const DecodePlan d = plan_decode(p);
   const size_t two_launch = vec_ws_bytes(v, p.rank) + v_area_bytes(p);
   const size_t one_launch = SGMV_WS_COUNTER_BYTES + (d.supported ? d.slot_bytes : 0);
-  return std::max(two_launch, one_launch);
+  const size_t matrix = sgmv::mfma_supported(p.rank)
+                            ? SGMV_WS_COUNTER_BYTES + plan_mfma(p, true).partial_bytes
+                            : 0;
+  return std::max({two_launch, one_launch, matrix});
 }
 
 }  // namespace
@@ -250,7 +313,7 @@ sgmv_status_t sgmv_check_problem(const sgmv_problem_t* p) {
   if (p->dtype != SGMV_F16 && p->dtype != SGMV_BF16) return SGMV_ERR_UNSUPPORTED;
   if (!rank_supported(p->rank)) return SGMV_ERR_UNSUPPORTED;
   if (p->h_in % 8 != 0 || p->h_out % 8 != 0) return SGMV_ERR_UNSUPPORTED;
-  if (p->variant == SGMV_VARIANT_MFMA) return SGMV_ERR_UNSUPPORTED;  // not built yet
+  if (p->variant == SGMV_VARIANT_MFMA && !sgmv::mfma_supported(p->rank)) return SGMV_ERR_UNSUPPORTED;
   const VecPlan v = plan_vec(*p, kTargetWorkgroups);
   if (2 * v.num_units > kCounterSlots) return SGMV_ERR_UNSUPPORTED;
   return SGMV_OK;
@@ -287,6 +350,13 @@ sgmv_status_t sgmv_shrink(const sgmv_problem_t* p, const void* X, const void* co
   if (nothing_to_do(*p)) return SGMV_OK;
   if (!X || !A_ptrs || !V || !seg_indptr || !lora_idx) return SGMV_ERR_INVALID_ARG;
   if (!aligned16(X) || !aligned16(V) || !aligned8(A_ptrs)) return SGMV_ERR_UNSUPPORTED;
+  if (stage_uses_mfma(*p)) {
+    sgmv::MfmaParams q = mfma_params(*p, plan_mfma(*p, false), seg_indptr, lora_idx);
+    q.X = static_cast<const uint16_t*>(X);
+    q.A_ptrs = reinterpret_cast<const uint64_t*>(A_ptrs);
+    q.V = V;
+    return hip_status(sgmv::launch_mfma_shrink(p->dtype, p->rank, q, static_cast<hipStream_t>(stream)));
+  }
   const VecPlan v = plan_vec(*p, kTargetWorkgroups);
   if (!ws || ws_bytes < vec_ws_bytes(v, p->rank)) return SGMV_ERR_WORKSPACE;
   if (!aligned16(ws)) return SGMV_ERR_UNSUPPORTED;
@@ -306,6 +376,13 @@ sgmv_status_t sgmv_expand(const sgmv_problem_t* p, const float* V, const void* c
   if (nothing_to_do(*p)) return SGMV_OK;
   if (!V || !B_ptrs || !Y || !seg_indptr || !lora_idx) return SGMV_ERR_INVALID_ARG;
   if (!aligned16(V) || !aligned16(Y) || !aligned8(B_ptrs)) return SGMV_ERR_UNSUPPORTED;
+  if (stage_uses_mfma(*p)) {
+    sgmv::MfmaParams q = mfma_params(*p, plan_mfma(*p, false), seg_indptr, lora_idx);
+    q.V = const_cast<float*>(V);
+    q.B_ptrs = reinterpret_cast<const uint64_t*>(B_ptrs);
+    q.Y = static_cast<uint16_t*>(Y);
+    return hip_status(sgmv::launch_mfma_expand(p->dtype, p->rank, q, static_cast<hipStream_t>(stream)));
+  }
   const VecPlan v = plan_vec(*p, kTargetWorkgroups);
   VecParams q = base_params(*p, v, seg_indptr, lora_idx, nullptr);
   q.counters = nullptr;
@@ -351,6 +428,21 @@ sgmv_status_t sgmv_lora_apply(const sgmv_problem_t* p, const void* X, const void
     q.cw = d.cw;
     q.direct_units = d.direct;
     return hip_status(sgmv::launch_decode(p->dtype, p->rank, d.rb, q, s));
+  }
+  if (stage_uses_mfma(*p)) {
+    // Matrix-core route: the shrink writes one fp32 partial of V per H1 chunk,
+    // the expand sums them in chunk order.
+    const MfmaPlan m = plan_mfma(*p, true);
+    if (ws_bytes < SGMV_WS_COUNTER_BYTES + m.partial_bytes) return SGMV_ERR_WORKSPACE;
+    sgmv::MfmaParams q = mfma_params(*p, m, seg_indptr, lora_idx);
+    q.X = static_cast<const uint16_t*>(X);
+    q.A_ptrs = reinterpret_cast<const uint64_t*>(A_ptrs);
+    q.B_ptrs = reinterpret_cast<const uint64_t*>(B_ptrs);
+    q.Y = static_cast<uint16_t*>(Y);
+    q.V = reinterpret_cast<float*>(static_cast<char*>(ws) + SGMV_WS_COUNTER_BYTES);
+    hipError_t e = sgmv::launch_mfma_shrink(p->dtype, p->rank, q, s);
+    if (e != hipSuccess) return SGMV_ERR_HIP;
+    return hip_status(sgmv::launch_mfma_expand(p->dtype, p->rank, q, s));
   }
   // Two launches: shrink into V (held after the shrink's split partials), then expand.
   const VecPlan v = plan_vec(*p, kTargetWorkgroups);

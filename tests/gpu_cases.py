@@ -57,7 +57,12 @@ class DeviceCall:
         self.B_ptrs = sg.pointer_table(self.B)
         self.seg_d = i32(self.seg if self.seg.size else [0])
         self.lidx_d = i32(self.lidx if self.lidx.size else [0])
-        self.ws = sg.new_workspace(self.problem)
+        try:
+            self.ws = sg.new_workspace(self.problem)
+        except sg.SgmvError:
+            # an unsupported problem: the call itself must report the status
+            import torch
+            self.ws = torch.zeros(sg.SGMV_WS_COUNTER_BYTES, dtype=torch.uint8, device="cuda")
 
     def reset_y(self):
         self.Y.copy_(to_device(self.Y0h, self.dtype))

@@ -17,7 +17,19 @@ from tests.gpu_cases import DeviceCall, assert_close, assert_close_f32, to_bits,
 
 pytestmark = pytest.mark.gpu
 
-APPLY_VARIANTS = [sg.SGMV_VARIANT_AUTO, sg.SGMV_VARIANT_VECTOR, sg.SGMV_VARIANT_FUSED]
+APPLY_VARIANTS = [sg.SGMV_VARIANT_AUTO, sg.SGMV_VARIANT_VECTOR, sg.SGMV_VARIANT_FUSED,
+                  sg.SGMV_VARIANT_MFMA]
+
+
+def expect_unsupported(call):
+    """The matrix-core kernels take ranks 16, 32 and 64 only."""
+    with pytest.raises(sg.SgmvError) as e:
+        call.apply()
+    assert e.value.status == sg.SGMV_ERR_UNSUPPORTED
+
+
+def mfma_rank_ok(variant, rank):
+    return variant != sg.SGMV_VARIANT_MFMA or rank in (16, 32, 64)
 
 
 def run_workload(w, variant=sg.SGMV_VARIANT_AUTO, splits=0):
@@ -45,6 +57,8 @@ def test_tiny(variant, dtype):
         w.X, w.A, w.B = (workloads.to_bits(oracle.decode(t, "f16").astype(np.float32), "bf16")
                          for t in (w.X, w.A, w.B))
     call = run_workload(w, variant)
+    if not mfma_rank_ok(variant, 8):
+        return expect_unsupported(call)
     assert_close(to_bits(call.apply()), call.oracle_apply(), dtype)
     assert call.counters_clear()
 
@@ -73,12 +87,13 @@ def test_popularity_sweep(kind, n, variant):
     assert call.counters_clear()
 
 
+@pytest.mark.parametrize("variant", [sg.SGMV_VARIANT_AUTO, sg.SGMV_VARIANT_VECTOR, sg.SGMV_VARIANT_MFMA])
 @pytest.mark.parametrize("rank", [16, 64])
-def test_mixed_prefill_decode_reduced(rank):
+def test_mixed_prefill_decode_reduced(rank, variant):
     """Config-4 layout (8 prefill + 24 one-row segments, 16 LoRAs, bf16) with prefill
     lengths 16..100 and hidden sizes 512/1376, small enough for a full comparison."""
     for w in workloads.mixed(rank, seed=400 + rank, pairs=((512, 1376), (1376, 512)), lo=16, hi=100):
-        call = run_workload(w)
+        call = run_workload(w, variant)
         assert_close(to_bits(call.apply()), call.oracle_apply(), "bf16", what=w.name)
 
 
@@ -116,6 +131,8 @@ def test_integer_exact_inputs_bitwise(dtype, rank, variant):
     X, A, B, Y0 = workloads.integer_exact(rng, 24, 256, 264, rank, 4, dtype, m, c)
     seg, lidx = [0, 5, 5, 6, 9, 17, 24], [3, 1, 0, 3, 2, 1]
     call = DeviceCall(dtype, X, A, B, Y0, seg, lidx, variant=variant)
+    if not mfma_rank_ok(variant, rank):
+        return expect_unsupported(call)
     got = oracle.decode(to_bits(call.apply()), dtype)
     assert np.array_equal(got, call.oracle_apply())
 
@@ -128,11 +145,12 @@ def test_integer_exact_full_decode_shape(variant):
     assert np.array_equal(oracle.decode(to_bits(call.apply()), "f16"), call.oracle_apply())
 
 
-def test_integer_exact_shrink_bitwise():
+@pytest.mark.parametrize("variant", [sg.SGMV_VARIANT_AUTO, sg.SGMV_VARIANT_VECTOR, sg.SGMV_VARIANT_MFMA])
+def test_integer_exact_shrink_bitwise(variant):
     rng = np.random.default_rng(77)
     X, A, B, Y0 = workloads.integer_exact(rng, 40, 512, 64, 32, 3, "bf16", 4, 64)
     seg, lidx = [0, 1, 21, 40], [2, 0, 1]
-    call = DeviceCall("bf16", X, A, B, Y0, seg, lidx)
+    call = DeviceCall("bf16", X, A, B, Y0, seg, lidx, variant=variant)
     V = call.shrink().cpu().numpy().astype(np.float64)
     assert np.array_equal(V, oracle.sgmv_shrink("bf16", X, A, seg, lidx))
 
@@ -161,7 +179,7 @@ def test_empty_unsorted_repeated_segments_and_uncovered_rows(variant):
 
 @pytest.mark.parametrize("variant", APPLY_VARIANTS)
 def test_no_segments_is_a_no_op(variant):
-    X, A, B, Y0 = rand_inputs(2, 8, 64, 64, 8, 2)
+    X, A, B, Y0 = rand_inputs(2, 8, 64, 64, 16, 2)
     call = DeviceCall("f16", X, A, B, Y0, [0], [], variant=variant)
     assert np.array_equal(to_bits(call.apply()), Y0)
     call2 = DeviceCall("f16", X, A, B, Y0, [0, 0, 0], [1, 0], variant=variant)
@@ -183,6 +201,8 @@ def test_ranks(rank, dtype, variant):
     X, A, B, Y0 = rand_inputs(4 + rank, 40, 1024, 768, rank, 6, dtype)
     seg, lidx = [0, 1, 2, 6, 7, 23, 24, 40], [5, 0, 3, 3, 1, 2, 4]
     call = DeviceCall(dtype, X, A, B, Y0, seg, lidx, variant=variant)
+    if not mfma_rank_ok(variant, rank):
+        return expect_unsupported(call)
     assert_close(to_bits(call.apply()), call.oracle_apply(), dtype)
 
 
@@ -200,7 +220,7 @@ def test_many_segments_more_than_a_wave(variant):
     lens = rng.integers(0, 4, size=150)
     seg = np.concatenate([[0], np.cumsum(lens)])
     n = int(seg[-1]) + 5
-    X, A, B, Y0 = rand_inputs(6, n, 128, 64, 8, 7)
+    X, A, B, Y0 = rand_inputs(6, n, 128, 64, 16, 7)
     call = DeviceCall("f16", X, A, B, Y0, seg, rng.integers(0, 7, size=150), variant=variant)
     assert_close(to_bits(call.apply()), call.oracle_apply(), "f16")
 
@@ -219,26 +239,30 @@ def test_max_seg_len_bound_above_actual():
 
 # ------------------------------------------------------------ the separate stages
 
+@pytest.mark.parametrize("variant", [sg.SGMV_VARIANT_AUTO, sg.SGMV_VARIANT_MFMA])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("rank", [8, 16, 64])
-def test_shrink_matches_oracle(dtype, rank):
+def test_shrink_matches_oracle(dtype, rank, variant):
+    if not mfma_rank_ok(variant, rank):
+        pytest.skip("matrix-core kernels take ranks 16, 32, 64 (error path covered elsewhere)")
     X, A, B, Y0 = rand_inputs(9, 30, 2048, 64, rank, 4, dtype)
     seg, lidx = [0, 1, 9, 9, 25], [3, 0, 1, 2]           # rows 25..29 uncovered
-    call = DeviceCall(dtype, X, A, B, Y0, seg, lidx)
+    call = DeviceCall(dtype, X, A, B, Y0, seg, lidx, variant=variant)
     V = call.shrink().cpu().numpy()
     ref = oracle.sgmv_shrink(dtype, X, A, seg, lidx)
     assert_close_f32(V[:25].astype(np.float64), ref[:25])
     assert np.isnan(V[25:]).all()
 
 
+@pytest.mark.parametrize("variant", [sg.SGMV_VARIANT_AUTO, sg.SGMV_VARIANT_VECTOR, sg.SGMV_VARIANT_MFMA])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-def test_expand_matches_oracle(dtype):
+def test_expand_matches_oracle(dtype, variant):
     import torch
     X, A, B, Y0 = rand_inputs(10, 30, 64, 3000, 32, 4, dtype)
     seg, lidx = [0, 7, 8, 20], [1, 3, 0]
     rng = np.random.default_rng(11)
     Vh = rng.standard_normal((30, 32)).astype(np.float32)
-    call = DeviceCall(dtype, X, A, B, Y0, seg, lidx)
+    call = DeviceCall(dtype, X, A, B, Y0, seg, lidx, variant=variant)
     got = to_bits(call.expand(torch.from_numpy(Vh).cuda()))
     ref = oracle.sgmv_expand(dtype, Vh.astype(np.float64), B, seg, lidx, Y0)
     assert_close(got, ref, dtype)
