@@ -1,23 +1,31 @@
 #!/usr/bin/env python3
 """Benchmark of libsgmv's SGMV LoRA term on one MI355X.
 
-Default workload: decode batch, Distinct LoRA popularity (Punica README, page
-"Punica：多 LoRA 模型统一服务框架", throughput paragraph): H1 = H2 = 4096 (Llama-7B
-q_proj), r = 16, 32 fp16 rows, one row per segment, each on its own LoRA.
-One step is one sgmv_lora_apply call (shrink + expand of the whole batch)
-with the segment metadata already built.  To measure HBM and not the 256 MB
-Infinity Cache, the 32 LoRAs of call c are drawn from a pool of 4096
-(1 GiB of A and B) shifted by 32*c, and X / Y rotate over 64 copies.
+Default workload (the headline): decode batch, Distinct LoRA popularity
+(Punica README, page "Punica：多 LoRA 模型统一服务框架", throughput paragraph):
+H1 = H2 = 4096 (Llama-7B q_proj), r = 16, 32 fp16 rows, one row per segment,
+each on its own LoRA.  One step is one sgmv_lora_apply call (shrink + expand
+of the whole batch) with the segment metadata already built.  To measure HBM
+rather than the 256 MB Infinity Cache, each call's LoRAs come from a physical
+pool of >= 1 GiB (the logical ids are shifted by a multiple of the logical
+pool per call, which keeps the popularity structure) and X / Y rotate over
+several copies.
+
+Other workloads (--workload): the popularity sweep (Identical / Uniform /
+Skewed, batch 32 and 64, segments made by the library's builder), the mixed
+prefill+decode batch on Llama-7B MLP shapes (r = 16 or 64, bf16), and one
+forward of all 280 LoRA calls of a 13B model (r = 64, bf16, batch 256, Zipf
+LoRA assignment), where one step is the whole forward.
 
 Prints one JSON line: value = whole-job algorithmic GB/s over the timed steps
-(K back-to-back launches, wall time between two device synchronisations);
+(K back-to-back steps, wall time between two device synchronisations);
 roofline.achieved = algorithmic bytes per launch / mean launch duration from
 HIP events recorded on the launch stream around the same timed region;
 roofline.traffic = HBM bytes per launch from the committed counter runs
 (FETCH_SIZE + WRITE_SIZE scaled by a copy kernel of known size), reported only
 while the kernel sources still match the ones the counters were taken on;
 cpu_baseline = the fp64 oracle timed on the host cores on a bounded sample of
-the same workload.
+the same workload (default workload only).
 """
 from __future__ import annotations
 
@@ -25,6 +33,7 @@ import argparse
 import ctypes
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -41,6 +50,7 @@ KERNEL_SOURCES = ("segmented_gather_matvec_amd/csrc/sgmv_decode.hip",
                   "segmented_gather_matvec_amd/csrc/sgmv_api.cpp")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sgmv_decode_kernel_decode_distinct_h4096_r16_b32_traffic.json")
 COPY_CALIBRATION_BYTES = 512 << 20
+DEFAULT_WORKLOAD = "decode_distinct_h4096_r16_b32"
 
 
 def kernel_source_hash() -> str:
@@ -58,9 +68,11 @@ def algorithmic_bytes(elem, n_rows_covered, h_in, h_out, rank, distinct_loras):
                    + 2 * n_rows_covered * h_out)
 
 
-def recorded_traffic(src_hash):
+def recorded_traffic(src_hash, workload):
     """HBM bytes per launch measured by the committed counter runs, if they were
-    taken on the current kernel sources."""
+    taken on the current kernel sources and this workload."""
+    if workload != DEFAULT_WORKLOAD:
+        return None
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
@@ -71,35 +83,92 @@ def recorded_traffic(src_hash):
     return rec.get("bytes_per_launch")
 
 
-class DecodeBench:
-    """Config: H1 = H2 = h, rank r, n rows, one segment per row, LoRA pool rotation."""
+def _bits(t):
+    import numpy as np
+    import torch
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
-    def __init__(self, h=4096, rank=16, n=32, pool=4096, copies=64, variant=0, seed=2, splits=0):
+
+# --------------------------------------------------------------------------- layouts
+
+def workload_layout(name):
+    """(dtype, h_in, h_out, rank, n_rows, seg_indptr, lora_idx, logical_pool, seed) of a
+    single-call workload; segment metadata comes from the workload's definition or from
+    the library's segment builder."""
+    import numpy as np
+    import segmented_gather_matvec_amd as sg
+    import workloads as wl
+    parts = name.split("_")
+    if name.startswith("decode_distinct"):
+        # decode_distinct_h{H}_r{r}_b{n}
+        h, r, n = int(parts[2][1:]), int(parts[3][1:]), int(parts[4][1:])
+        return "f16", h, h, r, n, np.arange(n + 1, dtype=np.int32), np.arange(n, dtype=np.int32), n, 2
+    if parts[0] in ("identical", "uniform", "skewed"):
+        # {kind}_b{n}: H=4096, r=16, fp16
+        kind, n = parts[0], int(parts[1][1:])
+        seed = wl.POPULARITY_SEEDS[(kind, n)]
+        ids, pool = wl.draw_ids(np.random.default_rng(seed), kind, n)
+        _, seg, lidx, _ = sg.sgmv_build_segments(ids, pool)
+        return "f16", 4096, 4096, 16, n, seg, lidx, pool, seed
+    if parts[0] == "mixed":
+        # mixed_r{r}_{h_in}to{h_out}
+        r = int(parts[1][1:])
+        h_in, h_out = (int(x) for x in parts[2].split("to"))
+        seed = 41 if r == 16 else 42
+        seg, ids = wl.mixed_layout(np.random.default_rng(seed))
+        return "bf16", h_in, h_out, r, int(seg[-1]), seg, ids, 16, seed
+    raise SystemExit(f"unknown workload {name}")
+
+
+SINGLE_WORKLOADS = (["decode_distinct_h4096_r16_b32", "decode_distinct_h4096_r16_b64"]
+                    + [f"{k}_b{n}" for k in ("identical", "uniform", "skewed") for n in (32, 64)]
+                    + [f"mixed_r{r}_{a}" for r in (16, 64) for a in ("4096to11008", "11008to4096")])
+MODEL_WORKLOADS = ["llama13b_r64_b256_forward"]
+
+
+class SingleCallBench:
+    """One sgmv_lora_apply call per step, weights rotated through a >= 1 GiB pool."""
+
+    def __init__(self, name, variant=0, splits=0):
+        import numpy as np
         import torch
         import segmented_gather_matvec_amd as sg
-        import workloads
+        import workloads as wl
 
-        self.sg, self.torch = sg, torch
-        self.h, self.rank, self.n, self.pool, self.copies = h, rank, n, pool, copies
+        self.name, self.sg, self.torch = name, sg, torch
+        (self.dtype, self.h_in, self.h_out, self.rank, self.n, seg, lidx, self.lpool,
+         seed) = workload_layout(name)
+        seg, lidx = np.asarray(seg, np.int32), np.asarray(lidx, np.int32)
+        lens = np.diff(seg)
+        used = sorted(set(int(k) for k, L in zip(lidx, lens) if L > 0))
+        self.seg_h, self.lidx_h = seg, lidx
+        self.distinct = len(used)
+        self.rows_covered = int(seg[-1])
+        e = 2
+        lora_bytes = e * (self.h_in * self.rank + self.rank * self.h_out)
+        # Physical pool: >= 1 GiB of weights, a multiple of the logical pool.
+        self.tables = max(1, min(4096 // self.lpool, math.ceil((1 << 30) / (lora_bytes * self.lpool))))
+        self.ppool = self.tables * self.lpool
+        xy_bytes = e * self.n * (self.h_in + self.h_out)
+        self.copies = max(2, min(64, math.ceil((256 << 20) / xy_bytes)))
+        s0 = seed * 1000
+        self.A = wl.device_normal((self.ppool, self.h_in, self.rank), self.h_in ** -0.5, self.dtype, s0 + 1)
+        self.B = wl.device_normal((self.ppool, self.rank, self.h_out), self.rank ** -0.5, self.dtype, s0 + 2)
+        self.X = wl.device_normal((self.copies, self.n, self.h_in), 1.0, self.dtype, s0 + 3)
+        self.Y = wl.device_normal((self.copies, self.n, self.h_out), 1.0, self.dtype, s0 + 4)
         dev = "cuda"
-        # Weights: pool of `pool` LoRAs, drawn on the device (seeded), fp16.
-        self.A = workloads.device_normal((pool, h, rank), 1.0 / h ** 0.5, "f16", seed * 1000 + 1)
-        self.B = workloads.device_normal((pool, rank, h), 1.0 / rank ** 0.5, "f16", seed * 1000 + 2)
-        self.X = workloads.device_normal((copies, n, h), 1.0, "f16", seed * 1000 + 3)
-        self.Y = workloads.device_normal((copies, n, h), 1.0, "f16", seed * 1000 + 4)
-        self.tables = pool // n if pool >= n else 1
-        a0, b0 = self.A.data_ptr(), self.B.data_ptr()
-        sa, sb = h * rank * 2, rank * h * 2
-        ids = (torch.arange(self.tables, device=dev)[:, None] * n
-               + torch.arange(n, device=dev)[None, :]) % pool
-        self.A_tab = (a0 + ids.to(torch.int64) * sa).contiguous()
-        self.B_tab = (b0 + ids.to(torch.int64) * sb).contiguous()
-        self.seg = torch.arange(n + 1, dtype=torch.int32, device=dev)
-        self.lidx = torch.arange(n, dtype=torch.int32, device=dev)
-        self.problem = sg.make_problem("f16", n, h, h, rank, n, n, 1, variant, splits)
+        phys = (torch.arange(self.tables, device=dev)[:, None] * self.lpool
+                + torch.arange(self.lpool, device=dev)[None, :]).to(torch.int64)
+        self.A_tab = (self.A.data_ptr() + phys * (self.h_in * self.rank * e)).contiguous()
+        self.B_tab = (self.B.data_ptr() + phys * (self.rank * self.h_out * e)).contiguous()
+        self.seg = torch.from_numpy(seg).to(dev)
+        self.lidx = torch.from_numpy(lidx if lidx.size else np.zeros(1, np.int32)).to(dev)
+        self.problem = sg.make_problem(self.dtype, self.n, self.h_in, self.h_out, self.rank, self.lpool,
+                                       len(lidx), int(lens.max()) if lens.size else 0, variant, splits)
         self.ws = sg.new_workspace(self.problem)
-        self.bytes = algorithmic_bytes(2, n, h, h, rank, n)
-        # Raw C entry point and per-call argument tuples (marshalled once).
+        self.bytes = algorithmic_bytes(e, self.rows_covered, self.h_in, self.h_out, self.rank, self.distinct)
+        self.rows_per_step = self.rows_covered
+        self.calls_per_step = 1
         self.fn = sg.load_library().sgmv_lora_apply
         self.marshal()
         torch.cuda.synchronize()
@@ -110,45 +179,152 @@ class DecodeBench:
         self.args = []
         for c in range(max(self.tables, self.copies)):
             t, x = c % self.tables, c % self.copies
-            self.args.append((pb, self.X[x].data_ptr(), self.A_tab[t].data_ptr(),
-                              self.B_tab[t].data_ptr(), self.Y[x].data_ptr(), self.seg.data_ptr(),
-                              self.lidx.data_ptr(), self.ws.data_ptr(), wsn))
+            self.args.append((pb, self.X[x].data_ptr(), self.A_tab[t].data_ptr(), self.B_tab[t].data_ptr(),
+                              self.Y[x].data_ptr(), self.seg.data_ptr(), self.lidx.data_ptr(),
+                              self.ws.data_ptr(), wsn))
 
-    def step(self, c, stream=None):
-        """Launch call c on `stream` (a raw hipStream_t; None = torch's current stream)."""
-        if stream is None:
-            stream = self.torch.cuda.current_stream().cuda_stream
+    def step(self, c, stream):
         st = self.fn(*self.args[c % len(self.args)], stream)
         if st != 0:
             raise RuntimeError(self.sg.sgmv_status_str(st))
 
-    def check_sample(self, calls=2):
+    def check_sample(self, calls=2, max_rows=64):
         """Parity of the timed launch configuration on sampled calls (oracle, fp64)."""
         import numpy as np
         import oracle
         torch = self.torch
         worst = 0.0
+        sid = torch.cuda.current_stream().cuda_stream
         for c in range(calls):
             t, x = c % self.tables, c % self.copies
-            ids = [(t * self.n + i) % self.pool for i in range(self.n)]
-            Xh = self.X[x].view(torch.int16).cpu().numpy().view(np.uint16)
-            Y0 = self.Y[x].view(torch.int16).cpu().numpy().view(np.uint16).copy()
-            A = [self.A[k].view(torch.int16).cpu().numpy().view(np.uint16) for k in ids]
-            B = [self.B[k].view(torch.int16).cpu().numpy().view(np.uint16) for k in ids]
-            self.step(c)
+            Xh, Y0 = _bits(self.X[x]), _bits(self.Y[x]).copy()
+            A = [_bits(self.A[t * self.lpool + k]) for k in range(self.lpool)]
+            B = [_bits(self.B[t * self.lpool + k]) for k in range(self.lpool)]
+            mask = None
+            if self.n > max_rows:
+                rows = set(np.random.default_rng(c).choice(self.n, 16, replace=False).tolist())
+                for s in range(len(self.seg_h) - 1):
+                    if self.seg_h[s + 1] > self.seg_h[s]:
+                        rows.update((int(self.seg_h[s]), int(self.seg_h[s + 1]) - 1))
+                mask = np.zeros(self.n, np.uint8)
+                mask[sorted(rows)] = 1
+            self.step(c, sid)
             torch.cuda.synchronize()
-            got = oracle.decode(self.Y[x].view(torch.int16).cpu().numpy().view(np.uint16), "f16")
-            ref = oracle.sgmv_apply("f16", Xh, A, B, list(range(self.n + 1)), list(range(self.n)), Y0)
-            ratio = np.abs(got - ref) / (1e-3 + 1e-2 * np.abs(ref))
+            got = oracle.decode(_bits(self.Y[x]), self.dtype)
+            ref = oracle.sgmv_apply(self.dtype, Xh, A, B, self.seg_h, self.lidx_h, Y0, row_mask=mask)
+            sel = slice(None) if mask is None else mask.astype(bool)
+            ratio = np.abs(got[sel] - ref[sel]) / (1e-3 + 1e-2 * np.abs(ref[sel]))
             worst = max(worst, float(ratio.max()))
         if worst > 1.0:
             raise AssertionError(f"bench parity check failed: max err/bound {worst:.3f}")
         return worst
 
+    def config(self):
+        return {"workload": self.name, "h_in": self.h_in, "h_out": self.h_out, "rank": self.rank,
+                "batch_rows": self.n, "segments": int(len(self.lidx_h)), "distinct_loras": self.distinct,
+                "lora_pool": self.lpool, "physical_lora_pool": self.ppool, "xy_copies": self.copies,
+                "algorithmic_bytes_per_step": self.bytes}
+
+
+class ModelForwardBench:
+    """All 280 LoRA calls of one 13B forward (40 layers x q,k,v,o,gate,up,down), r=64,
+    bf16, 64 LoRAs per projection, batch 256 with Zipf(1.5) LoRA assignment."""
+
+    dtype = "bf16"
+
+    def __init__(self, name, variant=0, splits=0, layers=None):
+        import numpy as np
+        import torch
+        import segmented_gather_matvec_amd as sg
+        import workloads as wl
+
+        self.name, self.sg, self.torch = name, sg, torch
+        self.n, self.rank, self.P = 256, 64, 64
+        self.layers = layers or wl.LLAMA13B_LAYERS
+        ids = wl.full_model_ids(seed=5, n=self.n, pool=self.P)
+        _, seg, lidx, mx = sg.sgmv_build_segments(ids, self.P)
+        self.seg_h, self.lidx_h = seg, lidx
+        self.distinct = len(lidx)
+        self.seg = torch.from_numpy(seg).to("cuda")
+        self.lidx = torch.from_numpy(lidx).to("cuda")
+        self.fn = sg.load_library().sgmv_lora_apply
+        self.calls, self.keep, total = [], [], 0
+        probs = {}
+        for (_, h_in, h_out) in wl.LLAMA13B_PROJ:
+            if (h_in, h_out) not in probs:
+                probs[(h_in, h_out)] = sg.make_problem("bf16", self.n, h_in, h_out, self.rank, self.P,
+                                                        len(lidx), mx, variant, splits)
+        self.probs = probs
+        ws_bytes = max(sg.sgmv_workspace_bytes(p) for p in probs.values())
+        self.ws = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda")
+        for layer in range(self.layers):
+            xs = {"qkv": wl.device_normal((self.n, 5120), 1.0, "bf16", 900000 + 4 * layer),
+                  "o": wl.device_normal((self.n, 5120), 1.0, "bf16", 900001 + 4 * layer),
+                  "gu": wl.device_normal((self.n, 5120), 1.0, "bf16", 900002 + 4 * layer),
+                  "down": wl.device_normal((self.n, 13824), 1.0, "bf16", 900003 + 4 * layer)}
+            for proj, (pname, h_in, h_out) in enumerate(wl.LLAMA13B_PROJ):
+                seed = wl.full_model_weight_seed(layer, proj)
+                A = wl.device_normal((self.P, h_in, self.rank), h_in ** -0.5, "bf16", seed * 2)
+                B = wl.device_normal((self.P, self.rank, h_out), self.rank ** -0.5, "bf16", seed * 2 + 1)
+                Y = wl.device_normal((self.n, h_out), 1.0, "bf16", 950000 + 7 * layer + proj)
+                group = {"q": "qkv", "k": "qkv", "v": "qkv", "o": "o", "gate": "gu", "up": "gu",
+                         "down": "down"}[pname]
+                X = xs[group]
+                At, Bt = sg.pointer_table(A), sg.pointer_table(B)
+                self.keep.append((A, B, Y, X, At, Bt))
+                pb = probs[(h_in, h_out)]
+                self.calls.append((ctypes.byref(pb), X.data_ptr(), At.data_ptr(), Bt.data_ptr(), Y.data_ptr(),
+                                   self.seg.data_ptr(), self.lidx.data_ptr(), self.ws.data_ptr(),
+                                   self.ws.numel()))
+                total += algorithmic_bytes(2, self.n, h_in, h_out, self.rank, self.distinct)
+        self.bytes = total
+        self.rows_per_step = self.n
+        self.calls_per_step = len(self.calls)
+        torch.cuda.synchronize()
+
+    def step(self, c, stream):
+        for args in self.calls:
+            st = self.fn(*args, stream)
+            if st != 0:
+                raise RuntimeError(self.sg.sgmv_status_str(st))
+
+    def check_sample(self, rows=16):
+        """Two calls (first layer q, last layer down) against the oracle on sampled rows."""
+        import numpy as np
+        import oracle
+        torch = self.torch
+        sid = torch.cuda.current_stream().cuda_stream
+        used = set(int(k) for k in self.lidx_h)
+        worst = 0.0
+        for idx in (0, len(self.calls) - 1):
+            A, B, Y, X, _, _ = self.keep[idx]
+            Xh, Y0 = _bits(X), _bits(Y).copy()
+            Ah = [_bits(A[k]) if k in used else np.zeros((1, 1), np.uint16) for k in range(self.P)]
+            Bh = [_bits(B[k]) if k in used else np.zeros((1, 1), np.uint16) for k in range(self.P)]
+            st = self.fn(*self.calls[idx], sid)
+            if st != 0:
+                raise RuntimeError(self.sg.sgmv_status_str(st))
+            torch.cuda.synchronize()
+            mask = np.zeros(self.n, np.uint8)
+            mask[np.random.default_rng(idx).choice(self.n, rows, replace=False)] = 1
+            mask[[0, self.n - 1]] = 1
+            got = oracle.decode(_bits(Y), "bf16")
+            ref = oracle.sgmv_apply("bf16", Xh, Ah, Bh, self.seg_h, self.lidx_h, Y0, row_mask=mask)
+            sel = mask.astype(bool)
+            worst = max(worst, float((np.abs(got[sel] - ref[sel]) / (1e-3 + 1e-2 * np.abs(ref[sel]))).max()))
+        if worst > 1.0:
+            raise AssertionError(f"bench parity check failed: max err/bound {worst:.3f}")
+        return worst
+
+    def config(self):
+        return {"workload": self.name, "layers": self.layers, "projections": "q,k,v,o,gate,up,down",
+                "rank": self.rank, "batch_rows": self.n, "segments": self.distinct,
+                "distinct_loras": self.distinct, "lora_pool": self.P, "calls_per_step": len(self.calls),
+                "algorithmic_bytes_per_step": self.bytes}
+
 
 def cpu_baseline(seconds=10.0):
-    """The oracle as it stands, on a host copy of the same workload shape."""
-    import numpy as np
+    """The oracle as it stands, on a host copy of the headline workload's shape."""
     import oracle
     import workloads
     w = workloads.decode_distinct()
@@ -172,10 +348,11 @@ def cpu_baseline(seconds=10.0):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--variant", choices=["auto", "vector", "fused"], default="auto")
-    ap.add_argument("--splits", type=int, default=0, help="workgroups per segment (0 = automatic)")
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default 2000; 20 for a forward)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default 200; 3 for a forward)")
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=SINGLE_WORKLOADS + MODEL_WORKLOADS)
+    ap.add_argument("--variant", choices=["auto", "vector", "fused", "mfma"], default="auto")
+    ap.add_argument("--splits", type=int, default=0, help="workgroups per segment block (0 = automatic)")
     ap.add_argument("--graph", action="store_true",
                     help="replay the timed steps from a captured HIP graph instead of eager launches")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -201,13 +378,17 @@ def main():
         torch.cuda.synchronize()
         del src, dst
         torch.cuda.empty_cache()
-    variant = {"auto": 0, "vector": 1, "fused": 2}[args.variant]
-    bench = DecodeBench(variant=variant, splits=args.splits)
+    variant = {"auto": 0, "vector": 1, "fused": 2, "mfma": 3}[args.variant]
+    model = args.workload in MODEL_WORKLOADS
+    K = args.steps if args.steps is not None else (20 if model else 2000)
+    W = args.warmup if args.warmup is not None else (3 if model else 200)
+    bench = (ModelForwardBench if model else SingleCallBench)(args.workload, variant=variant, splits=args.splits)
     worst = None if args.no_check else bench.check_sample()
 
-    K, W = args.steps, args.warmup
+    stream = torch.cuda.current_stream()
+    sid = stream.cuda_stream
     for c in range(W):
-        bench.step(c)
+        bench.step(c, sid)
     torch.cuda.synchronize()
 
     graph = None
@@ -223,8 +404,6 @@ def main():
 
     # Timed region: K steps between two device synchronisations, with HIP
     # events recorded on the launch stream at both ends.
-    stream = torch.cuda.current_stream()
-    sid = stream.cuda_stream
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -237,13 +416,13 @@ def main():
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    ev_s = e0.elapsed_time(e1) * 1e-3
     ms_per_step = wall / K * 1e3
-    mean_kernel_s = e0.elapsed_time(e1) * 1e-3 / K
+    launch_s = ev_s / (K * bench.calls_per_step)
 
     value = bench.bytes * K / wall / 1e9
-    achieved = bench.bytes / mean_kernel_s / 1e9
+    achieved = bench.bytes / bench.calls_per_step / launch_s / 1e9
     src_hash = kernel_source_hash()
-    traffic = recorded_traffic(src_hash)
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -255,24 +434,21 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
+        "dtype": bench.dtype,
         "data": "synthetic",
-        "config": {"workload": "decode_distinct_h4096_r16_b32", "h_in": 4096, "h_out": 4096,
-                   "rank": 16, "batch_rows": 32, "segments": 32, "distinct_loras": 32,
-                   "lora_pool": bench.pool, "xy_copies": bench.copies, "variant": args.variant,
-                   "launch": "graph" if graph is not None else "eager",
-                   "algorithmic_bytes_per_step": bench.bytes},
+        "config": dict(bench.config(), variant=args.variant,
+                       launch="graph" if graph is not None else "eager"),
         "pct_peak": round(100 * value / HBM_PEAK_GBS, 2),
-        "tokens_per_s": round(bench.n * K / wall, 1),
-        "us_per_call": round(ms_per_step * 1e3, 3),
-        "launch_us_mean_events": round(mean_kernel_s * 1e6, 3),
+        "tokens_per_s": round(bench.rows_per_step * K / wall, 1),
+        "us_per_call": round(ms_per_step * 1e3 / bench.calls_per_step, 3),
+        "launch_us_mean_events": round(launch_s * 1e6, 3),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic},
+                     "traffic": recorded_traffic(src_hash, args.workload)},
         "kernel_source_hash": src_hash,
         "parity_max_err_over_bound": None if worst is None else round(worst, 4),
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.workload == DEFAULT_WORKLOAD:
         line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(line), flush=True)
 

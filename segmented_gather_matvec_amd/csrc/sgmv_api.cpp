@@ -106,14 +106,19 @@ DecodePlan plan_decode(const sgmv_problem_t& p) {
                                 ceil_div(p.h_out, sgmv::decode_max_cw()));
   const int64_t gmax = std::min<int64_t>({ceil_div(p.h_in, 8), ceil_div(p.h_out, 8), (int64_t)kMaxSplits});
   if (gmin > gmax) return d;
+  // Each workgroup gathers splits * parts * rows * rank partials; keep that to
+  // one staging round (2048 values) unless the caller asks for more splits.
+  const int parts = d.rb == 1 ? 4 : 1;
+  const int64_t rows = std::max(1, std::min(d.rb, p.max_seg_len));
+  const int64_t gather_cap = std::max<int64_t>(1, 2048 / ((int64_t)parts * rows * p.rank));
   int64_t g = p.splits > 0 ? p.splits
-                           : ceil_div(kDecodeTargetWorkgroups, std::max<int64_t>(d.num_units, 1));
+                           : std::min(ceil_div(kDecodeTargetWorkgroups, std::max<int64_t>(d.num_units, 1)),
+                                      gather_cap);
   g = std::max(gmin, std::min(g, gmax));
   d.splits = (int)g;
   d.kc = (int)round_up(ceil_div(p.h_in, g), 8);
   d.cw = (int)round_up(ceil_div(p.h_out, g), 8);
   d.grid = 8 * ceil_div(d.num_units, 8) * g;
-  const int parts = d.rb == 1 ? 4 : 1;  // partials published per workgroup
   d.slot_bytes = (size_t)d.num_units * (size_t)g * parts * d.rb * p.rank * sizeof(uint64_t);
   d.supported = d.grid > 0 && d.grid <= (int64_t)INT32_MAX;
   return d;
@@ -137,33 +142,39 @@ int decode_capacity(int dtype, int rank, int rb) {
 
 // Plan of the matrix-core kernels (long segments).
 struct MfmaPlan {
-  int direct = 1;
-  int64_t num_units = 0;
+  int64_t units = 0, units64 = 0;
+  int direct = 1, direct64 = 1;
   int ksplit = 1;
   int kc = 0;
+  int chunks_per_wg = 1;
   size_t partial_bytes = 0;  // split partials of V, fp32 [ksplit][n_rows][rank]
 };
 
-// Split H1 so that shrink workgroups (row tiles x splits) reach about two per CU.
-constexpr int kMfmaTargetWorkgroups = 512;
+// Split H1 so that shrink workgroups (row units x chunks) reach about two per
+// CU; group expand column chunks so that about four workgroups run per CU.
+constexpr int kMfmaShrinkTarget = 512;
+constexpr int kMfmaExpandTarget = 1024;
 
-MfmaPlan plan_mfma(const sgmv_problem_t& p, bool allow_split) {
-  MfmaPlan m;
-  const int mt = sgmv::kMfmaRowsPerTile;
-  if (p.max_seg_len <= mt) {
-    m.direct = 1;
-    m.num_units = p.num_segs;
-  } else {
-    m.direct = 0;
-    m.num_units = std::min<int64_t>((int64_t)p.num_segs * ceil_div(p.max_seg_len, mt),
-                                    ceil_div(p.n_rows, mt) + p.num_segs);
+int64_t units_for(const sgmv_problem_t& p, int rows, int* direct) {
+  if (p.max_seg_len <= rows) {
+    *direct = 1;
+    return p.num_segs;
   }
-  int64_t ks = 1;
-  if (allow_split)
-    ks = std::max<int64_t>(1, std::min<int64_t>(ceil_div(kMfmaTargetWorkgroups, std::max<int64_t>(m.num_units, 1)),
-                                                ceil_div(p.h_in, sgmv::kMfmaKChunk)));
+  *direct = 0;
+  return std::min<int64_t>((int64_t)p.num_segs * ceil_div(p.max_seg_len, rows), ceil_div(p.n_rows, rows) + p.num_segs);
+}
+
+MfmaPlan plan_mfma(const sgmv_problem_t& p) {
+  MfmaPlan m;
+  m.units = units_for(p, sgmv::kMfmaShrinkUnitRows, &m.direct);
+  m.units64 = units_for(p, sgmv::kMfmaRowsPerTile, &m.direct64);
+  const int64_t ks = std::max<int64_t>(1, std::min<int64_t>(ceil_div(kMfmaShrinkTarget, std::max<int64_t>(m.units, 1)),
+                                                            ceil_div(p.h_in, sgmv::kMfmaKChunk)));
   m.kc = (int)round_up(ceil_div(p.h_in, ks), sgmv::kMfmaKChunk);
   m.ksplit = (int)ceil_div(p.h_in, m.kc);
+  const int64_t nchunks = ceil_div(p.h_out, sgmv::kMfmaColsPerTile);
+  m.chunks_per_wg = (int)std::max<int64_t>(1, std::min<int64_t>(nchunks,
+      ceil_div(std::max<int64_t>(m.units64, 1) * nchunks, kMfmaExpandTarget)));
   m.partial_bytes = (size_t)m.ksplit * (size_t)p.n_rows * p.rank * sizeof(float);
   return m;
 }
@@ -179,10 +190,13 @@ sgmv::MfmaParams mfma_params(const sgmv_problem_t& p, const MfmaPlan& m, const i
   q.h_out = p.h_out;
   q.num_segs = p.num_segs;
   q.num_loras = p.num_loras;
-  q.num_units = (int32_t)m.num_units;
+  q.num_units = (int32_t)m.units;
+  q.direct_units = m.direct;
+  q.num_units64 = (int32_t)m.units64;
+  q.direct_units64 = m.direct64;
   q.ksplit = m.ksplit;
   q.kc = m.kc;
-  q.direct_units = m.direct;
+  q.chunks_per_wg = m.chunks_per_wg;
   return q;
 }
 
@@ -228,7 +242,7 @@ sgmv_status_t hip_status(hipError_t e) { return e == hipSuccess ? SGMV_OK : SGMV
 // device at once (the kernel's workgroups wait for each other), else the
 // shrink and expand vector kernels as two launches.
 bool use_decode(const sgmv_problem_t& p, const DecodePlan& d) {
-  if (p.variant == SGMV_VARIANT_VECTOR || !d.supported) return false;
+  if (p.variant == SGMV_VARIANT_VECTOR || p.variant == SGMV_VARIANT_MFMA || !d.supported) return false;
   const int cap = decode_capacity(p.dtype, p.rank, d.rb);
   return cap > 0 && d.grid <= cap;
 }
@@ -239,7 +253,7 @@ size_t apply_ws_bytes(const sgmv_problem_t& p) {
   const size_t two_launch = vec_ws_bytes(v, p.rank) + v_area_bytes(p);
   const size_t one_launch = SGMV_WS_COUNTER_BYTES + (d.supported ? d.slot_bytes : 0);
   const size_t matrix = sgmv::mfma_supported(p.rank)
-                            ? SGMV_WS_COUNTER_BYTES + plan_mfma(p, true).partial_bytes
+                            ? SGMV_WS_COUNTER_BYTES + plan_mfma(p).partial_bytes + v_area_bytes(p)
                             : 0;
   return std::max({two_launch, one_launch, matrix});
 }
@@ -351,9 +365,13 @@ sgmv_status_t sgmv_shrink(const sgmv_problem_t* p, const void* X, const void* co
   if (!X || !A_ptrs || !V || !seg_indptr || !lora_idx) return SGMV_ERR_INVALID_ARG;
   if (!aligned16(X) || !aligned16(V) || !aligned8(A_ptrs)) return SGMV_ERR_UNSUPPORTED;
   if (stage_uses_mfma(*p)) {
-    sgmv::MfmaParams q = mfma_params(*p, plan_mfma(*p, false), seg_indptr, lora_idx);
+    const MfmaPlan m = plan_mfma(*p);
+    if (!ws || ws_bytes < SGMV_WS_COUNTER_BYTES + m.partial_bytes) return SGMV_ERR_WORKSPACE;
+    if (!aligned16(ws)) return SGMV_ERR_UNSUPPORTED;
+    sgmv::MfmaParams q = mfma_params(*p, m, seg_indptr, lora_idx);
     q.X = static_cast<const uint16_t*>(X);
     q.A_ptrs = reinterpret_cast<const uint64_t*>(A_ptrs);
+    q.partials = reinterpret_cast<float*>(static_cast<char*>(ws) + SGMV_WS_COUNTER_BYTES);
     q.V = V;
     return hip_status(sgmv::launch_mfma_shrink(p->dtype, p->rank, q, static_cast<hipStream_t>(stream)));
   }
@@ -377,7 +395,7 @@ sgmv_status_t sgmv_expand(const sgmv_problem_t* p, const float* V, const void* c
   if (!V || !B_ptrs || !Y || !seg_indptr || !lora_idx) return SGMV_ERR_INVALID_ARG;
   if (!aligned16(V) || !aligned16(Y) || !aligned8(B_ptrs)) return SGMV_ERR_UNSUPPORTED;
   if (stage_uses_mfma(*p)) {
-    sgmv::MfmaParams q = mfma_params(*p, plan_mfma(*p, false), seg_indptr, lora_idx);
+    sgmv::MfmaParams q = mfma_params(*p, plan_mfma(*p), seg_indptr, lora_idx);
     q.V = const_cast<float*>(V);
     q.B_ptrs = reinterpret_cast<const uint64_t*>(B_ptrs);
     q.Y = static_cast<uint16_t*>(Y);
@@ -430,16 +448,17 @@ sgmv_status_t sgmv_lora_apply(const sgmv_problem_t* p, const void* X, const void
     return hip_status(sgmv::launch_decode(p->dtype, p->rank, d.rb, q, s));
   }
   if (stage_uses_mfma(*p)) {
-    // Matrix-core route: the shrink writes one fp32 partial of V per H1 chunk,
-    // the expand sums them in chunk order.
-    const MfmaPlan m = plan_mfma(*p, true);
-    if (ws_bytes < SGMV_WS_COUNTER_BYTES + m.partial_bytes) return SGMV_ERR_WORKSPACE;
+    // Matrix-core route: the shrink writes one fp32 partial plane of V per H1
+    // chunk, the reduce sums them (in chunk order) into V, the expand reads V.
+    const MfmaPlan m = plan_mfma(*p);
+    if (ws_bytes < SGMV_WS_COUNTER_BYTES + m.partial_bytes + v_area_bytes(*p)) return SGMV_ERR_WORKSPACE;
     sgmv::MfmaParams q = mfma_params(*p, m, seg_indptr, lora_idx);
     q.X = static_cast<const uint16_t*>(X);
     q.A_ptrs = reinterpret_cast<const uint64_t*>(A_ptrs);
     q.B_ptrs = reinterpret_cast<const uint64_t*>(B_ptrs);
     q.Y = static_cast<uint16_t*>(Y);
-    q.V = reinterpret_cast<float*>(static_cast<char*>(ws) + SGMV_WS_COUNTER_BYTES);
+    q.partials = reinterpret_cast<float*>(static_cast<char*>(ws) + SGMV_WS_COUNTER_BYTES);
+    q.V = reinterpret_cast<float*>(static_cast<char*>(ws) + SGMV_WS_COUNTER_BYTES + m.partial_bytes);
     hipError_t e = sgmv::launch_mfma_shrink(p->dtype, p->rank, q, s);
     if (e != hipSuccess) return SGMV_ERR_HIP;
     return hip_status(sgmv::launch_mfma_expand(p->dtype, p->rank, q, s));

@@ -8,18 +8,21 @@
 // sustain against HBM, so both run on v_mfma_f32_16x16x32_{f16,bf16}
 // (lane l holds A[l%16][8(l/16)+e], B[8(l/16)+e][l%16], D[4(l/16)+i][l%16]).
 //
-// Shrink: a workgroup (4 waves) takes a 64-row tile of one segment and a
-// chunk of H1.  A_k is staged through LDS transposed ([r][h], so a lane reads
-// its 8 consecutive h of one rank with one 128-bit LDS read); X fragments go
-// straight from HBM into registers.  With several H1 chunks, each writes its
-// own fp32 partial [n_rows, r]; the expand sums them in a fixed order.
-//
-// Expand: a workgroup takes a 64-row tile and 128 output columns.  V is split
-// into V_hi + V_lo (both in the input format), which the MFMA consumes as a
-// K dimension of 2r against [B_k; B_k], keeping ~2x the input format's
-// significand bits of V.  B_k is staged transposed in LDS ([c][j]); the
-// result tile goes through LDS so that Y is read and written with 128-bit
-// accesses (Y is prefetched before the MFMA work).
+// Three launches:
+//  1. shrink: a workgroup (4 waves) takes up to 256 rows of one segment (four
+//     64-row subtiles) and one chunk of H1.  Each 256-row sub-chunk of A_k is
+//     staged once in LDS, transposed to [r][h] so that a lane reads the 8
+//     consecutive h of one rank with one 128-bit LDS read, and reused by all
+//     subtiles; X fragments go straight from HBM into registers.  Each H1
+//     chunk writes its own fp32 partial plane of V.
+//  2. reduce: V = sum of the partial planes, in chunk order (reproducible).
+//  3. expand: a workgroup takes 64 rows and a group of 128-column chunks.  V is
+//     split into V_hi + V_lo (both in the input format), consumed as a K of 2r
+//     against [B_k; B_k], which keeps about twice the format's significand
+//     bits of V; its MFMA fragments stay in registers for all chunks.  Each
+//     chunk of B_k is staged transposed ([c][j]) in LDS while the next chunk's
+//     B_k and Y are in flight; the result tile goes through LDS so that Y is
+//     read and written with 128-bit accesses.
 #include "sgmv_device.h"
 #include "sgmv_plan.h"
 #include "sgmv_units.h"
@@ -31,9 +34,10 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kMT = kMfmaRowsPerTile;  // 64 rows per tile: 16 per wave
-constexpr int kKSub = 256;             // A_k rows staged per sub-chunk (shrink)
-constexpr int kCW = kMfmaColsPerTile;  // 128 output columns per expand workgroup
+constexpr int kMT = kMfmaRowsPerTile;        // 64 rows per subtile: 16 per wave
+constexpr int kUnitRows = kMfmaShrinkUnitRows;  // rows per shrink workgroup (4 subtiles)
+constexpr int kKSub = kMfmaKChunk;           // A_k rows staged per sub-chunk
+constexpr int kCW = kMfmaColsPerTile;        // 128 output columns per expand chunk
 
 template <class T>
 __device__ inline f32x4 mfma(const u32x4& a, const u32x4& b, f32x4 c);
@@ -48,9 +52,17 @@ __device__ inline f32x4 mfma<BF16>(const u32x4& a, const u32x4& b, f32x4 c) {
                                                  c, 0, 0, 0);
 }
 
-template <class T>
-__device__ inline float widen(uint16_t b) {
-  return T::one(b);
+// Write two 8-element rows (u, v) of a row-major tile transposed into LDS as
+// 32-bit pairs: dst[e*stride] = {u[e], v[e]} for e < 8 (dst in 16-bit units,
+// even offset).
+__device__ inline void store_pair_transposed(uint16_t* dst, int stride, const u32x4& u, const u32x4& v) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t lo = (u[w] & 0xffffu) | (v[w] << 16);
+    const uint32_t hi = (u[w] >> 16) | (v[w] & 0xffff0000u);
+    *reinterpret_cast<uint32_t*>(dst + (2 * w) * stride) = lo;
+    *reinterpret_cast<uint32_t*>(dst + (2 * w + 1) * stride) = hi;
+  }
 }
 
 // ---------------------------------------------------------------- shrink
@@ -58,9 +70,11 @@ template <class T, int R>
 __global__ __launch_bounds__(kThreads) void sgmv_mfma_shrink_kernel(MfmaParams p) {
   constexpr int NT = R / 16;                   // 16-wide rank tiles
   constexpr int JG = R / 8;                    // 128-bit vectors per row of A_k
-  constexpr int NAV = kKSub * JG / kThreads;   // A_k vectors per thread per sub-chunk
+  constexpr int NPAIR = kKSub / 2 * JG / kThreads;  // (h, h+1) vector pairs per thread
   constexpr int KSTEPS = kKSub / 32;           // MFMA k-steps per sub-chunk
+  constexpr int NSUB = kUnitRows / kMT;        // 64-row subtiles per workgroup
   constexpr int AST = kKSub + 8;               // LDS row stride (halves) of transposed A_k
+  static_assert(NPAIR >= 1, "tile shape");
   __shared__ __attribute__((aligned(16))) uint16_t lds_at[R * AST];
 
   const int t = threadIdx.x;
@@ -71,89 +85,129 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_shrink_kernel(MfmaParams p
   const int KS = p.ksplit;
   const int unit = blockIdx.x / KS;
   const int g = blockIdx.x - unit * KS;
-  const Unit un = resolve_unit<kMT>(p.seg_indptr, p.lora_idx, p.num_segs, p.num_loras, p.n_rows,
-                                    p.direct_units, unit);
+  const Unit un = resolve_unit<kUnitRows>(p.seg_indptr, p.lora_idx, p.num_segs, p.num_loras, p.n_rows,
+                                          p.direct_units, unit);
   if (un.L <= 0) return;
   const int L = un.L, r0 = un.r0;
   const uint16_t* Ak = reinterpret_cast<const uint16_t*>(p.A_ptrs[un.k]);
   const int k0 = g * p.kc;
   const int k1 = p.h_in < k0 + p.kc ? p.h_in : k0 + p.kc;
+  const int nsub = (L + kMT - 1) / kMT;
 
-  const int row = wave * 16 + ml;  // this lane's row of the tile (A operand)
-  const uint16_t* xrow = p.X + (int64_t)(r0 + (row < L ? row : L - 1)) * p.h_in;
-
-  f32x4 acc[NT];
+  // Row of the tile this lane feeds into the MFMA A operand, per subtile.
+  const uint16_t* xrow[NSUB];
 #pragma unroll
-  for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int st = 0; st < NSUB; ++st) {
+    const int row = st * kMT + wave * 16 + ml;
+    xrow[st] = p.X + (int64_t)(r0 + (row < L ? row : L - 1)) * p.h_in;
+  }
+
+  f32x4 acc[NSUB][NT];
+#pragma unroll
+  for (int st = 0; st < NSUB; ++st)
+#pragma unroll
+    for (int n = 0; n < NT; ++n) acc[st][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   for (int kk = k0; kk < k1; kk += kKSub) {
     const int nk = k1 - kk < kKSub ? k1 - kk : kKSub;  // multiple of 8
-    // Loads of this sub-chunk: A_k rows [kk, kk+nk) and this lane's X fragments.
-    u32x4 av[NAV];
+    u32x4 av[NPAIR][2];
 #pragma unroll
-    for (int m = 0; m < NAV; ++m) {
-      const int v = t + kThreads * m;
-      const int h = v / JG;
-      av[m] = load_stream(Ak + (h < nk ? (int64_t)(kk + h) * R + (v % JG) * 8 : 0));
+    for (int m = 0; m < NPAIR; ++m) {
+      const int pr = t + kThreads * m;
+      const int h = (pr / JG) * 2, jg = pr % JG;
+      av[m][0] = load_stream(Ak + (h < nk ? (int64_t)(kk + h) * R + jg * 8 : 0));
+      av[m][1] = load_stream(Ak + (h + 1 < nk ? (int64_t)(kk + h + 1) * R + jg * 8 : 0));
     }
     u32x4 xf[KSTEPS];
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
       const int h = kk + s * 32 + q * 8;
-      xf[s] = load_stream(xrow + (h < k1 ? h : 0));
+      xf[s] = load_stream(xrow[0] + (h < k1 ? h : 0));
     }
     __syncthreads();  // the previous sub-chunk is done with lds_at
 #pragma unroll
-    for (int m = 0; m < NAV; ++m) {
-      const int v = t + kThreads * m;
-      const int h = v / JG, jg = v % JG;
-      const bool ok = h < nk;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t word = ok ? av[m][w] : 0u;
-        lds_at[(jg * 8 + 2 * w) * AST + h] = (uint16_t)(word & 0xffffu);
-        lds_at[(jg * 8 + 2 * w + 1) * AST + h] = (uint16_t)(word >> 16);
-      }
+    for (int m = 0; m < NPAIR; ++m) {
+      const int pr = t + kThreads * m;
+      const int h = (pr / JG) * 2, jg = pr % JG;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      store_pair_transposed(&lds_at[(jg * 8) * AST + h], AST, h < nk ? av[m][0] : z, h + 1 < nk ? av[m][1] : z);
     }
     __syncthreads();
     const int steps = (nk + 31) / 32;
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
-      if (s < steps) {
-        u32x4 a = xf[s];
-        if (kk + s * 32 + q * 8 >= k1) a = u32x4{0u, 0u, 0u, 0u};  // ragged tail of H1
+    for (int st = 0; st < NSUB; ++st) {
+      if (st < nsub) {
+        // X fragments of the next subtile are fetched while this one computes.
+        u32x4 xn[KSTEPS];
+        if (st + 1 < nsub) {
 #pragma unroll
-        for (int n = 0; n < NT; ++n) {
-          const u32x4 b = load_vec(&lds_at[(n * 16 + ml) * AST + s * 32 + q * 8]);
-          acc[n] = mfma<T>(a, b, acc[n]);
+          for (int s = 0; s < KSTEPS; ++s) {
+            const int h = kk + s * 32 + q * 8;
+            xn[s] = load_stream(xrow[st + 1 < NSUB ? st + 1 : st] + (h < k1 ? h : 0));
+          }
+        }
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s) {
+          if (s < steps) {
+            u32x4 a = xf[s];
+            if (kk + s * 32 + q * 8 >= k1) a = u32x4{0u, 0u, 0u, 0u};  // ragged tail of H1
+#pragma unroll
+            for (int n = 0; n < NT; ++n) {
+              const u32x4 b = load_vec(&lds_at[(n * 16 + ml) * AST + s * 32 + q * 8]);
+              acc[st][n] = mfma<T>(a, b, acc[st][n]);
+            }
+          }
+        }
+        if (st + 1 < nsub) {
+#pragma unroll
+          for (int s = 0; s < KSTEPS; ++s) xf[s] = xn[s];
         }
       }
     }
   }
 
-  // D[4q+i][ml] of rank tile n: row wave*16 + 4q + i, rank n*16 + ml.
-  float* dst = p.V + (int64_t)g * p.partial_stride;
+  // D[4q+i][ml] of rank tile n: row st*64 + wave*16 + 4q + i, rank n*16 + ml.
+  float* dst = p.partials + (int64_t)g * p.partial_stride;
 #pragma unroll
-  for (int n = 0; n < NT; ++n)
+  for (int st = 0; st < NSUB; ++st)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rr = wave * 16 + q * 4 + i;
-      if (rr < L) dst[(int64_t)(r0 + rr) * R + n * 16 + ml] = acc[n][i];
-    }
+    for (int n = 0; n < NT; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rr = st * kMT + wave * 16 + q * 4 + i;
+        if (rr < L) dst[(int64_t)(r0 + rr) * R + n * 16 + ml] = acc[st][n][i];
+      }
+}
+
+// ---------------------------------------------------------------- reduce
+// V[row] = sum over the ksplit partial planes, in plane order, for the rows
+// of every segment (rows outside all segments are left untouched).
+template <int R>
+__global__ __launch_bounds__(kThreads) void sgmv_mfma_reduce_kernel(MfmaParams p) {
+  const Unit un = resolve_unit<kMT>(p.seg_indptr, p.lora_idx, p.num_segs, p.num_loras, p.n_rows,
+                                    p.direct_units64, blockIdx.x);
+  if (un.L <= 0) return;
+  for (int o = threadIdx.x; o < un.L * R / 4; o += kThreads) {
+    const int64_t off = (int64_t)un.r0 * R + o * 4;
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < p.ksplit; ++k)
+      s += *reinterpret_cast<const f32x4*>(p.partials + (int64_t)k * p.partial_stride + off);
+    *reinterpret_cast<f32x4*>(p.V + off) = s;
+  }
 }
 
 // ---------------------------------------------------------------- expand
 template <class T, int R>
 __global__ __launch_bounds__(kThreads) void sgmv_mfma_expand_kernel(MfmaParams p) {
-  constexpr int K2 = 2 * R;           // virtual K: [V_hi | V_lo] against [B_k; B_k]
+  constexpr int K2 = 2 * R;            // virtual K: [V_hi | V_lo] against [B_k; B_k]
   constexpr int KSTEPS = K2 / 32;
-  constexpr int NTC = kCW / 16;       // 16-wide column tiles per wave
-  constexpr int BST = R + 8;          // LDS stride (halves) of transposed B_k, per column
-  constexpr int VST = K2 + 8;         // LDS stride (halves) of [V_hi | V_lo], per row
-  constexpr int OST = kCW + 4;        // LDS stride (floats) of the result tile
-  constexpr int NBV = R * (kCW / 8) / kThreads;  // B_k vectors per thread
-  constexpr int NYV = 16 * (kCW / 8) / 64;       // Y vectors per lane (16 rows of the wave)
-  static_assert(NBV >= 1 && NYV >= 1, "tile shape");
+  constexpr int NTC = kCW / 16;        // 16-wide column tiles per chunk
+  constexpr int CV = kCW / 8;          // 128-bit column vectors per chunk row
+  constexpr int BST = R + 8;           // LDS stride (halves) of transposed B_k, per column
+  constexpr int VST = K2 + 8;          // LDS stride (halves) of [V_hi | V_lo], per row
+  constexpr int OST = kCW + 4;         // LDS stride (floats) of the result tile
+  constexpr int NBP = (R / 2 * CV + kThreads - 1) / kThreads;  // (j, j+1) B_k vector pairs per thread
+  constexpr int NYV = 16 * CV / 64;    // Y vectors per lane (16 rows of the wave)
   __shared__ __attribute__((aligned(16))) uint16_t lds_bt[kCW * BST];
   __shared__ __attribute__((aligned(16))) uint16_t lds_v[kMT * VST];
   __shared__ __attribute__((aligned(16))) float lds_o[kWaves * 16 * OST];
@@ -164,104 +218,122 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_expand_kernel(MfmaParams p
   const int q = lane >> 4;
   const int ml = lane & 15;
   const int nchunks = (p.h_out + kCW - 1) / kCW;
-  const int unit = blockIdx.x / nchunks;
-  const int cc = blockIdx.x - unit * nchunks;
+  const int ngroups = (nchunks + p.chunks_per_wg - 1) / p.chunks_per_wg;
+  const int unit = blockIdx.x / ngroups;
+  const int grp = blockIdx.x - unit * ngroups;
   const Unit un = resolve_unit<kMT>(p.seg_indptr, p.lora_idx, p.num_segs, p.num_loras, p.n_rows,
-                                    p.direct_units, unit);
+                                    p.direct_units64, unit);
   if (un.L <= 0) return;
   const int L = un.L, r0 = un.r0;
-  const int c0 = cc * kCW;
+  const int ch0 = grp * p.chunks_per_wg;
+  const int ch1 = nchunks < ch0 + p.chunks_per_wg ? nchunks : ch0 + p.chunks_per_wg;
   const uint16_t* Bk = reinterpret_cast<const uint16_t*>(p.B_ptrs[un.k]);
+  uint16_t* Yr = p.Y + (int64_t)r0 * p.h_out;
 
-  // Y of this wave's 16 rows: vector u -> (row, 8-column group), fetched first.
-  u32x4 yv[NYV];
+  // Loads of one chunk (all lanes issue the same loads; addresses of lanes
+  // without work are clamped to a valid element).
+  auto issue = [&](int ch, u32x4 (&bv)[NBP][2], u32x4 (&yv)[NYV]) {
+    const int c0 = ch * kCW;
 #pragma unroll
-  for (int u = 0; u < NYV; ++u) {
-    const int v = lane + 64 * u;
-    const int rr = wave * 16 + v / (kCW / 8);
-    const int c = c0 + (v % (kCW / 8)) * 8;
-    const bool ok = rr < L && c < p.h_out;
-    yv[u] = load_stream(p.Y + (int64_t)r0 * p.h_out + (ok ? (int64_t)rr * p.h_out + c : 0));
-  }
-  u32x4 bv[NBV];
+    for (int m = 0; m < NBP; ++m) {
+      const int pr = t + kThreads * m;
+      const int j = (pr / CV) * 2, c = c0 + (pr % CV) * 8;
+      const bool ok = pr < R / 2 * CV && ch < ch1 && c < p.h_out;
+      bv[m][0] = load_stream(Bk + (ok ? (int64_t)j * p.h_out + c : 0));
+      bv[m][1] = load_stream(Bk + (ok ? (int64_t)(j + 1) * p.h_out + c : 0));
+    }
 #pragma unroll
-  for (int m = 0; m < NBV; ++m) {
-    const int v = t + kThreads * m;
-    const int j = v / (kCW / 8);
-    const int c = c0 + (v % (kCW / 8)) * 8;
-    bv[m] = load_stream(Bk + (c < p.h_out ? (int64_t)j * p.h_out + c : 0));
-  }
-  // V of the tile rows (sum of the shrink's split partials, fixed order), split hi/lo.
+    for (int u = 0; u < NYV; ++u) {
+      const int v = lane + 64 * u;
+      const int rr = wave * 16 + v / CV;
+      const int c = c0 + (v % CV) * 8;
+      const bool ok = rr < L && ch < ch1 && c < p.h_out;
+      yv[u] = load_stream(Yr + (ok ? (int64_t)rr * p.h_out + c : 0));
+    }
+  };
+  u32x4 bvA[NBP][2], yvA[NYV], bvB[NBP][2], yvB[NYV];
+  issue(ch0, bvA, yvA);
+
+  // V of the tile rows, split hi/lo, then this wave's MFMA A fragments.
   for (int o = t; o < kMT * R; o += kThreads) {
     const int rr = o / R, j = o % R;
-    float v = 0.f;
-    if (rr < L)
-      for (int s = 0; s < p.ksplit; ++s) v += p.V[(int64_t)s * p.partial_stride + (int64_t)(r0 + rr) * R + j];
+    const float v = rr < L ? p.V[(int64_t)(r0 + rr) * R + j] : 0.f;
     const uint16_t hi = T::round(v);
-    const uint16_t lo = T::round(v - widen<T>(hi));
+    const uint16_t lo = T::round(v - T::one(hi));
     lds_v[rr * VST + j] = hi;
     lds_v[rr * VST + R + j] = lo;
   }
-#pragma unroll
-  for (int m = 0; m < NBV; ++m) {
-    const int v = t + kThreads * m;
-    const int j = v / (kCW / 8);
-    const int cl = (v % (kCW / 8)) * 8;
-    const bool ok = c0 + cl < p.h_out;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const uint32_t word = ok ? bv[m][w] : 0u;
-      lds_bt[(cl + 2 * w) * BST + j] = (uint16_t)(word & 0xffffu);
-      lds_bt[(cl + 2 * w + 1) * BST + j] = (uint16_t)(word >> 16);
-    }
-  }
   __syncthreads();
-
   u32x4 af[KSTEPS];
 #pragma unroll
   for (int s = 0; s < KSTEPS; ++s) af[s] = load_vec(&lds_v[(wave * 16 + ml) * VST + s * 32 + q * 8]);
   float* out = lds_o + wave * 16 * OST;
+
+  auto compute = [&](int ch, const u32x4 (&bv)[NBP][2], const u32x4 (&yv)[NYV]) {
+    const int c0 = ch * kCW;
+    __syncthreads();  // the previous chunk is done with lds_bt and lds_o
 #pragma unroll
-  for (int n = 0; n < NTC; ++n) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
-      const int kb = (s * 32 + q * 8) % R;  // rank of the B_k copy this k-group reads
-      const u32x4 b = load_vec(&lds_bt[(n * 16 + ml) * BST + kb]);
-      acc = mfma<T>(af[s], b, acc);
+    for (int m = 0; m < NBP; ++m) {
+      const int pr = t + kThreads * m;
+      if (pr < R / 2 * CV) {
+        const int j = (pr / CV) * 2, cl = (pr % CV) * 8;
+        store_pair_transposed(&lds_bt[cl * BST + j], BST, bv[m][0], bv[m][1]);
+      }
     }
+    __syncthreads();
 #pragma unroll
-    for (int i = 0; i < 4; ++i) out[(q * 4 + i) * OST + n * 16 + ml] = acc[i];
-  }
-  __syncthreads();
+    for (int n = 0; n < NTC; ++n) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int u = 0; u < NYV; ++u) {
-    const int v = lane + 64 * u;
-    const int rl = v / (kCW / 8);
-    const int cl = (v % (kCW / 8)) * 8;
-    const int rr = wave * 16 + rl;
-    if (rr < L && c0 + cl < p.h_out) {
-      float yf[8];
-      unpack8<T>(yv[u], yf);
+      for (int s = 0; s < KSTEPS; ++s) {
+        const int kb = (s * 32 + q * 8) % R;  // rank of the B_k copy this k-group reads
+        acc = mfma<T>(af[s], load_vec(&lds_bt[(n * 16 + ml) * BST + kb]), acc);
+      }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) yf[e] += out[rl * OST + cl + e];
-      store_vec(p.Y + (int64_t)(r0 + rr) * p.h_out + c0 + cl, pack8<T>(yf));
+      for (int i = 0; i < 4; ++i) out[(q * 4 + i) * OST + n * 16 + ml] = acc[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < NYV; ++u) {
+      const int v = lane + 64 * u;
+      const int rl = v / CV;
+      const int cl = (v % CV) * 8;
+      const int rr = wave * 16 + rl;
+      if (rr < L && c0 + cl < p.h_out) {
+        float yf[8];
+        unpack8<T>(yv[u], yf);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) yf[e] += out[rl * OST + cl + e];
+        store_vec(Yr + (int64_t)rr * p.h_out + c0 + cl, pack8<T>(yf));
+      }
+    }
+  };
+  // Ping-pong: chunk ch+1 is in flight while chunk ch is computed.
+  for (int ch = ch0; ch < ch1; ch += 2) {
+    issue(ch + 1, bvB, yvB);
+    compute(ch, bvA, yvA);
+    if (ch + 1 < ch1) {
+      issue(ch + 2, bvA, yvA);
+      compute(ch + 1, bvB, yvB);
     }
   }
 }
 
 template <class T, int R>
 hipError_t launch_t(int stage, const MfmaParams& p, hipStream_t s) {
+  unsigned grid = 0;
   if (stage == 0) {
-    const unsigned grid = (unsigned)p.num_units * (unsigned)p.ksplit;
-    if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL((sgmv_mfma_shrink_kernel<T, R>), dim3(grid), dim3(kThreads), 0, s, p);
+    grid = (unsigned)p.num_units * (unsigned)p.ksplit;
+    if (grid) hipLaunchKernelGGL((sgmv_mfma_shrink_kernel<T, R>), dim3(grid), dim3(kThreads), 0, s, p);
+  } else if (stage == 1) {
+    grid = (unsigned)p.num_units64;
+    if (grid) hipLaunchKernelGGL((sgmv_mfma_reduce_kernel<R>), dim3(grid), dim3(kThreads), 0, s, p);
   } else {
-    const unsigned grid = (unsigned)p.num_units * (unsigned)((p.h_out + kCW - 1) / kCW);
-    if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL((sgmv_mfma_expand_kernel<T, R>), dim3(grid), dim3(kThreads), 0, s, p);
+    const int nchunks = (p.h_out + kCW - 1) / kCW;
+    grid = (unsigned)p.num_units64 * (unsigned)((nchunks + p.chunks_per_wg - 1) / p.chunks_per_wg);
+    if (grid) hipLaunchKernelGGL((sgmv_mfma_expand_kernel<T, R>), dim3(grid), dim3(kThreads), 0, s, p);
   }
-  return hipGetLastError();
+  return grid ? hipGetLastError() : hipSuccess;
 }
 
 template <class T>
@@ -274,16 +346,22 @@ hipError_t launch_rank(int rank, int stage, const MfmaParams& p, hipStream_t s) 
   return hipErrorInvalidValue;
 }
 
+hipError_t launch_stage(int dtype, int rank, int stage, const MfmaParams& p, hipStream_t s) {
+  return dtype == 1 ? launch_rank<BF16>(rank, stage, p, s) : launch_rank<F16>(rank, stage, p, s);
+}
+
 }  // namespace
 
 bool mfma_supported(int rank) { return rank == 16 || rank == 32 || rank == 64; }
 
 hipError_t launch_mfma_shrink(int dtype, int rank, const MfmaParams& p, hipStream_t stream) {
-  return dtype == 1 ? launch_rank<BF16>(rank, 0, p, stream) : launch_rank<F16>(rank, 0, p, stream);
+  hipError_t e = launch_stage(dtype, rank, 0, p, stream);
+  if (e != hipSuccess) return e;
+  return launch_stage(dtype, rank, 1, p, stream);
 }
 
 hipError_t launch_mfma_expand(int dtype, int rank, const MfmaParams& p, hipStream_t stream) {
-  return dtype == 1 ? launch_rank<BF16>(rank, 1, p, stream) : launch_rank<F16>(rank, 1, p, stream);
+  return launch_stage(dtype, rank, 2, p, stream);
 }
 
 }  // namespace sgmv

@@ -64,25 +64,31 @@ hipError_t launch_decode(int dtype, int rank, int rb, const DecodeParams& p, hip
 // Workgroups of the decode kernel that fit on the device at once (0 if unknown).
 int decode_resident_capacity(int dtype, int rank, int rb);
 
-// Matrix-core kernels for long segments (two launches: shrink, expand).
-constexpr int kMfmaRowsPerTile = 64;   // rows of one segment per workgroup
-constexpr int kMfmaColsPerTile = 128;  // output columns per expand workgroup
-constexpr int kMfmaKChunk = 256;       // H1 granule of the shrink's split
+// Matrix-core kernels for long segments: shrink (+ reduce of the H1 split),
+// then expand.
+constexpr int kMfmaRowsPerTile = 64;      // rows per MFMA subtile / expand workgroup
+constexpr int kMfmaShrinkUnitRows = 256;  // rows of one segment per shrink workgroup
+constexpr int kMfmaColsPerTile = 128;     // output columns per expand chunk
+constexpr int kMfmaKChunk = 256;          // H1 granule of the shrink's split
 
 struct MfmaParams {
   const uint16_t* X;
   const uint64_t* A_ptrs;
   const uint64_t* B_ptrs;
   uint16_t* Y;
-  float* V;                // shrink: output (split s at V + s*partial_stride); expand: input
+  float* V;                // reduce: output; expand: input (fp32 [n_rows, rank])
+  float* partials;         // shrink: H1-chunk s writes partials + s*partial_stride
   const int32_t* seg_indptr;
   const int32_t* lora_idx;
-  int64_t partial_stride;  // floats between split partials (n_rows * rank)
+  int64_t partial_stride;  // floats between partial planes (n_rows * rank)
   int32_t n_rows, h_in, h_out, num_segs, num_loras;
-  int32_t num_units, ksplit, kc, direct_units;
+  int32_t num_units, direct_units;      // shrink units of <= 256 rows
+  int32_t num_units64, direct_units64;  // reduce / expand units of <= 64 rows
+  int32_t ksplit, kc, chunks_per_wg;
 };
 
 bool mfma_supported(int rank);
+// Shrink into the partial planes, then reduce them into V (two launches).
 hipError_t launch_mfma_shrink(int dtype, int rank, const MfmaParams& p, hipStream_t stream);
 hipError_t launch_mfma_expand(int dtype, int rank, const MfmaParams& p, hipStream_t stream);
 

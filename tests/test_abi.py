@@ -153,6 +153,25 @@ def test_workspace_bytes():
         sg.sgmv_workspace_bytes(good(rank=7))
 
 
+@pytest.mark.parametrize("kw", [
+    {"num_segs": 0, "max_seg_len": 0},
+    {"n_rows": 0, "num_segs": 0, "max_seg_len": 0, "num_loras": 0},
+    {"n_rows": 1, "num_segs": 1, "max_seg_len": 1, "num_loras": 1},
+    {"n_rows": 5000, "num_segs": 3, "max_seg_len": 4000, "rank": 64, "h_in": 11008, "h_out": 8},
+    {"n_rows": 4, "num_segs": 1, "max_seg_len": 4, "rank": 8, "h_in": 8, "h_out": 8},
+    {"n_rows": 300, "num_segs": 300, "max_seg_len": 1, "rank": 32, "variant": 3},
+])
+@pytest.mark.parametrize("rank", [8, 16, 32, 64])
+def test_workspace_bytes_degenerate_and_extreme_problems(kw, rank):
+    """Planning every route must not fail (or trap) for empty, tiny or huge problems."""
+    kw = dict(kw)
+    kw.setdefault("rank", rank)
+    if kw.get("variant") == 3 and kw["rank"] == 8:
+        kw["rank"] = 16
+    nbytes = sg.sgmv_workspace_bytes(good(**kw))
+    assert nbytes >= sg.SGMV_WS_COUNTER_BYTES
+
+
 def test_device_entry_points_fail_fast_on_bad_arguments():
     """Every status below is returned by host checks before any HIP call."""
     lib = sg.load_library()
