@@ -140,6 +140,35 @@ sgmv_status_t sgmv_check_segments(const sgmv_problem_t* problem, const int32_t* 
  * (always >= SGMV_WS_COUNTER_BYTES). */
 sgmv_status_t sgmv_workspace_bytes(const sgmv_problem_t* problem, size_t* bytes);
 
+/* Kernel route that sgmv_lora_apply takes for a problem on the current HIP
+ * device.  The SGMV paragraph of the Punica README describes one kernel for
+ * every batch shape; here the route is chosen from the segment lengths: the
+ * one-launch kernel while its grid fits on the device at once (decode-shaped
+ * batches), the matrix-core kernels when some segment is long (prefill), else
+ * the vector kernels. */
+typedef enum sgmv_route {
+  SGMV_ROUTE_NONE = 0,    /* nothing to do (no rows or segments) */
+  SGMV_ROUTE_DECODE = 1,  /* one launch: shrink, on-chip exchange, expand */
+  SGMV_ROUTE_MFMA = 2,    /* matrix-core shrink, split reduce, matrix-core expand */
+  SGMV_ROUTE_VECTOR = 3   /* split-K vector shrink, then vector expand */
+} sgmv_route_t;
+
+typedef struct sgmv_plan_info {
+  int32_t route;          /* sgmv_route_t */
+  int32_t launches;       /* kernel launches per sgmv_lora_apply call */
+  int32_t rows_per_unit;  /* rows of one segment block (decode and vector routes) or of
+                             one expand tile (matrix-core route) */
+  int32_t units;          /* segment blocks planned (an upper bound: empty ones exit at once) */
+  int32_t splits;         /* workgroups that share one block (decode, vector) or
+                             partial planes of the H1 split (matrix-core) */
+  int32_t grid;           /* workgroups of the first launch */
+} sgmv_plan_info_t;
+
+/* Host-only: the plan sgmv_lora_apply would run for *problem on the current
+ * device (the decode route depends on the device's occupancy; without a
+ * usable device it is never chosen).  No device memory is touched. */
+sgmv_status_t sgmv_query_plan(const sgmv_problem_t* problem, sgmv_plan_info_t* info);
+
 /* Shrink: V[i, :] = X[i, :] @ A_{lora_idx[s]} for every covered row i
  * (Punica README, LoRA paragraph: the x@A factor of x@A@B).  V rows not
  * covered by a segment are left untouched.  ws: device workspace of at least

@@ -26,11 +26,12 @@ LIB_PATH = os.path.join(_HERE, "libsgmv.so")
 SGMV_OK, SGMV_ERR_INVALID_ARG, SGMV_ERR_UNSUPPORTED, SGMV_ERR_WORKSPACE, SGMV_ERR_HIP = range(5)
 SGMV_F16, SGMV_BF16 = 0, 1
 SGMV_VARIANT_AUTO, SGMV_VARIANT_VECTOR, SGMV_VARIANT_FUSED, SGMV_VARIANT_MFMA = range(4)
+SGMV_ROUTE_NONE, SGMV_ROUTE_DECODE, SGMV_ROUTE_MFMA, SGMV_ROUTE_VECTOR = range(4)
 SGMV_WS_COUNTER_BYTES = 1 << 20
 
 ENTRY_POINTS = ("sgmv_status_str", "sgmv_build_segments", "sgmv_check_problem",
-                "sgmv_check_segments", "sgmv_workspace_bytes", "sgmv_shrink", "sgmv_expand",
-                "sgmv_lora_apply")
+                "sgmv_check_segments", "sgmv_workspace_bytes", "sgmv_query_plan", "sgmv_shrink",
+                "sgmv_expand", "sgmv_lora_apply")
 
 
 class SgmvError(RuntimeError):
@@ -47,6 +48,14 @@ class sgmv_problem_t(ctypes.Structure):
 
     def __repr__(self):
         return "sgmv_problem_t(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
+
+
+class sgmv_plan_info_t(ctypes.Structure):
+    _fields_ = [("route", ctypes.c_int32), ("launches", ctypes.c_int32), ("rows_per_unit", ctypes.c_int32),
+                ("units", ctypes.c_int32), ("splits", ctypes.c_int32), ("grid", ctypes.c_int32)]
+
+    def as_dict(self):
+        return {n: int(getattr(self, n)) for n, _ in self._fields_}
 
 
 _lib = None
@@ -69,6 +78,7 @@ def load_library(path: str = LIB_PATH):
     lib.sgmv_check_problem.argtypes = [prob]
     lib.sgmv_check_segments.argtypes = [prob, P, P]
     lib.sgmv_workspace_bytes.argtypes = [prob, ctypes.POINTER(SZ)]
+    lib.sgmv_query_plan.argtypes = [prob, ctypes.POINTER(sgmv_plan_info_t)]
     lib.sgmv_shrink.argtypes = [prob, P, P, P, P, P, P, SZ, P]
     lib.sgmv_expand.argtypes = [prob, P, P, P, P, P, P]
     lib.sgmv_lora_apply.argtypes = [prob, P, P, P, P, P, P, P, SZ, P]
@@ -137,6 +147,13 @@ def sgmv_workspace_bytes(problem: sgmv_problem_t) -> int:
     _check(load_library().sgmv_workspace_bytes(ctypes.byref(problem), ctypes.byref(out)),
            "sgmv_workspace_bytes")
     return int(out.value)
+
+
+def sgmv_query_plan(problem: sgmv_problem_t) -> sgmv_plan_info_t:
+    """Route, row block, split and grid that sgmv_lora_apply takes on the current device."""
+    info = sgmv_plan_info_t()
+    _check(load_library().sgmv_query_plan(ctypes.byref(problem), ctypes.byref(info)), "sgmv_query_plan")
+    return info
 
 
 # ----------------------------------------------------------------- device calls

@@ -84,15 +84,17 @@ struct DecodePlan {
   int cw = 8;
   int64_t grid = 0;
   size_t slot_bytes = 0;
+  int split_major = 0;
 };
 
 // Aim for one workgroup per CU: each decode workgroup keeps 32+ KiB of loads
 // in flight, so 256 of them cover the HBM latency-bandwidth product.
 constexpr int kDecodeTargetWorkgroups = 256;
 
-DecodePlan plan_decode(const sgmv_problem_t& p) {
+DecodePlan plan_decode_rb(const sgmv_problem_t& p, int rb, int split_major) {
   DecodePlan d;
-  d.rb = pick_rb(p.max_seg_len);
+  d.rb = rb;
+  d.split_major = split_major;
   if (!sgmv::decode_supported(p.rank, d.rb)) return d;
   if (p.max_seg_len <= d.rb) {
     d.direct = 1;
@@ -118,7 +120,7 @@ DecodePlan plan_decode(const sgmv_problem_t& p) {
   d.splits = (int)g;
   d.kc = (int)round_up(ceil_div(p.h_in, g), 8);
   d.cw = (int)round_up(ceil_div(p.h_out, g), 8);
-  d.grid = 8 * ceil_div(d.num_units, 8) * g;
+  d.grid = (split_major ? d.num_units : 8 * ceil_div(d.num_units, 8)) * g;
   d.slot_bytes = (size_t)d.num_units * (size_t)g * parts * d.rb * p.rank * sizeof(uint64_t);
   d.supported = d.grid > 0 && d.grid <= (int64_t)INT32_MAX;
   return d;
@@ -138,6 +140,47 @@ int decode_capacity(int dtype, int rank, int rb) {
     init[dev][dtype][ri][bi] = true;
   }
   return cache[dev][dtype][ri][bi];
+}
+
+// Largest decode grid of any plan: eight co-resident workgroups on each of 256
+// CUs. The workspace is sized over the candidate plans up to this bound, and
+// the device's occupancy picks among them at launch.
+constexpr int64_t kMaxDecodeGrid = 2048;
+
+// Candidate decode plans, smallest row block first. Blocks of one row keep
+// the most workgroups busy; when segments hold several rows (rows that share
+// a LoRA), the split-major mapping puts equal splits of neighbouring units on
+// one XCD, so a segment's rows re-read their A_k / B_k slice from that XCD's
+// L2 rather than from HBM. Segments of one row keep a unit on one XCD.
+int decode_candidates(const sgmv_problem_t& p, DecodePlan out[3]) {
+  const int split_major = p.max_seg_len > 1 ? 1 : 0;
+  int n = 0;
+  for (int rb : {1, 4, 16}) {
+    const DecodePlan d = plan_decode_rb(p, rb, split_major);
+    if (d.supported && d.grid <= kMaxDecodeGrid) out[n++] = d;
+    if (p.max_seg_len <= rb) break;  // a larger block only adds empty rows
+  }
+  return n;
+}
+
+// The first candidate whose grid is co-resident on the current device (the
+// kernel's workgroups wait for each other); unsupported if none is.
+DecodePlan plan_decode(const sgmv_problem_t& p) {
+  DecodePlan c[3];
+  const int n = decode_candidates(p, c);
+  for (int i = 0; i < n; ++i) {
+    const int cap = decode_capacity(p.dtype, p.rank, c[i].rb);
+    if (cap > 0 && c[i].grid <= cap) return c[i];
+  }
+  return DecodePlan{};
+}
+
+size_t decode_ws_bytes(const sgmv_problem_t& p) {
+  DecodePlan c[3];
+  const int n = decode_candidates(p, c);
+  size_t b = 0;
+  for (int i = 0; i < n; ++i) b = std::max(b, c[i].slot_bytes);
+  return b;
 }
 
 // Plan of the matrix-core kernels (long segments).
@@ -238,20 +281,22 @@ VecParams base_params(const sgmv_problem_t& p, const VecPlan& v, const int32_t* 
 
 sgmv_status_t hip_status(hipError_t e) { return e == hipSuccess ? SGMV_OK : SGMV_ERR_HIP; }
 
-// sgmv_lora_apply runs the one-launch decode kernel when its plan fits on the
-// device at once (the kernel's workgroups wait for each other), else the
-// shrink and expand vector kernels as two launches.
+// sgmv_lora_apply runs the one-launch decode kernel when one of its plans fits
+// on the device at once, else the matrix-core or vector kernels.
 bool use_decode(const sgmv_problem_t& p, const DecodePlan& d) {
-  if (p.variant == SGMV_VARIANT_VECTOR || p.variant == SGMV_VARIANT_MFMA || !d.supported) return false;
-  const int cap = decode_capacity(p.dtype, p.rank, d.rb);
-  return cap > 0 && d.grid <= cap;
+  return p.variant != SGMV_VARIANT_VECTOR && p.variant != SGMV_VARIANT_MFMA && d.supported;
+}
+
+sgmv_route_t apply_route(const sgmv_problem_t& p, const DecodePlan& d) {
+  if (nothing_to_do(p)) return SGMV_ROUTE_NONE;
+  if (use_decode(p, d)) return SGMV_ROUTE_DECODE;
+  return stage_uses_mfma(p) ? SGMV_ROUTE_MFMA : SGMV_ROUTE_VECTOR;
 }
 
 size_t apply_ws_bytes(const sgmv_problem_t& p) {
   const VecPlan v = plan_vec(p, kTargetWorkgroups);
-  const DecodePlan d = plan_decode(p);
   const size_t two_launch = vec_ws_bytes(v, p.rank) + v_area_bytes(p);
-  const size_t one_launch = SGMV_WS_COUNTER_BYTES + (d.supported ? d.slot_bytes : 0);
+  const size_t one_launch = SGMV_WS_COUNTER_BYTES + decode_ws_bytes(p);
   const size_t matrix = sgmv::mfma_supported(p.rank)
                             ? SGMV_WS_COUNTER_BYTES + plan_mfma(p).partial_bytes + v_area_bytes(p)
                             : 0;
@@ -412,6 +457,44 @@ sgmv_status_t sgmv_expand(const sgmv_problem_t* p, const float* V, const void* c
                                      static_cast<hipStream_t>(stream)));
 }
 
+sgmv_status_t sgmv_query_plan(const sgmv_problem_t* p, sgmv_plan_info_t* info) {
+  sgmv_status_t st = sgmv_check_problem(p);
+  if (st != SGMV_OK) return st;
+  if (!info) return SGMV_ERR_INVALID_ARG;
+  *info = sgmv_plan_info_t{};
+  const DecodePlan d = plan_decode(*p);
+  info->route = apply_route(*p, d);
+  switch (info->route) {
+    case SGMV_ROUTE_DECODE:
+      info->launches = 1;
+      info->rows_per_unit = d.rb;
+      info->units = (int32_t)d.num_units;
+      info->splits = d.splits;
+      info->grid = (int32_t)d.grid;
+      break;
+    case SGMV_ROUTE_MFMA: {
+      const MfmaPlan m = plan_mfma(*p);
+      info->launches = 3;
+      info->rows_per_unit = sgmv::kMfmaRowsPerTile;
+      info->units = (int32_t)m.units64;
+      info->splits = m.ksplit;
+      info->grid = (int32_t)(m.units * m.ksplit);
+      break;
+    }
+    case SGMV_ROUTE_VECTOR: {
+      const VecPlan v = plan_vec(*p, kTargetWorkgroups);
+      info->launches = 2;
+      info->rows_per_unit = v.rb;
+      info->units = (int32_t)v.num_units;
+      info->splits = v.splits;
+      info->grid = (int32_t)(v.num_units * v.splits);
+      break;
+    }
+    default: break;
+  }
+  return SGMV_OK;
+}
+
 sgmv_status_t sgmv_lora_apply(const sgmv_problem_t* p, const void* X, const void* const* A_ptrs,
                               const void* const* B_ptrs, void* Y, const int32_t* seg_indptr,
                               const int32_t* lora_idx, void* ws, size_t ws_bytes, void* stream) {
@@ -425,7 +508,8 @@ sgmv_status_t sgmv_lora_apply(const sgmv_problem_t* p, const void* X, const void
   if (!aligned16(ws)) return SGMV_ERR_UNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const DecodePlan d = plan_decode(*p);
-  if (use_decode(*p, d)) {
+  const sgmv_route_t route = apply_route(*p, d);
+  if (route == SGMV_ROUTE_DECODE) {
     if (ws_bytes < SGMV_WS_COUNTER_BYTES + d.slot_bytes) return SGMV_ERR_WORKSPACE;
     sgmv::DecodeParams q{};
     q.X = static_cast<const uint16_t*>(X);
@@ -445,9 +529,10 @@ sgmv_status_t sgmv_lora_apply(const sgmv_problem_t* p, const void* X, const void
     q.kc = d.kc;
     q.cw = d.cw;
     q.direct_units = d.direct;
+    q.split_major = d.split_major;
     return hip_status(sgmv::launch_decode(p->dtype, p->rank, d.rb, q, s));
   }
-  if (stage_uses_mfma(*p)) {
+  if (route == SGMV_ROUTE_MFMA) {
     // Matrix-core route: the shrink writes one fp32 partial plane of V per H1
     // chunk, the reduce sums them (in chunk order) into V, the expand reads V.
     const MfmaPlan m = plan_mfma(*p);

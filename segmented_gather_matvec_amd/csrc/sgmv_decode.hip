@@ -19,8 +19,11 @@
 //   * The launch tag mixes the dispatch packet id with the queue address, so it
 //     changes on every launch, including replays of a captured graph; it is
 //     always odd, so a zero-filled workspace never matches.
-//   * The workgroups of one unit are placed on one XCD (workgroups are
-//     dispatched round-robin over the 8 XCDs), which keeps the exchange local.
+//   * Workgroups are dispatched round-robin over the 8 XCDs.  With one-row
+//     segments the splits of a unit are placed on one XCD; when segments
+//     hold several rows that share a LoRA, split-major order instead places
+//     equal splits of neighbouring units (the same A_k / B_k slice) on one
+//     XCD, so those slices are fetched from HBM once per XCD.
 //   * The grid is sized by the host to be co-resident, so every wait ends.
 #include "sgmv_device.h"
 #include "sgmv_plan.h"
@@ -107,11 +110,17 @@ __global__ __launch_bounds__(kThreads) void sgmv_decode_kernel(DecodeParams p) {
   const int lane = t & 63;
   const int wave = t >> 6;
   const int G = p.splits;
-  // Workgroups go round-robin over the XCDs: keep the splits of a unit on one.
-  const int xcd = blockIdx.x % kXcds;
-  const int slot = blockIdx.x / kXcds;
-  const int unit = (slot / G) * kXcds + xcd;
-  const int g = slot - (slot / G) * G;
+  // Workgroups go round-robin over the XCDs.
+  int unit, g;
+  if (p.split_major) {
+    unit = blockIdx.x / G;
+    g = blockIdx.x - unit * G;
+  } else {  // keep the splits of a unit on one XCD
+    const int xcd = blockIdx.x % kXcds;
+    const int slot = blockIdx.x / kXcds;
+    unit = (slot / G) * kXcds + xcd;
+    g = slot - (slot / G) * G;
+  }
   if (unit >= p.num_units) return;
   // With at most 64 LoRAs, fetch both pointer tables (one entry per lane) in
   // parallel with the segment metadata instead of after it: the LoRA id then
@@ -332,7 +341,9 @@ __global__ __launch_bounds__(kThreads) void sgmv_decode_kernel(DecodeParams p) {
 
 template <class T, int R, int RB>
 hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
-  const unsigned grid = (unsigned)kXcds * (unsigned)((p.num_units + kXcds - 1) / kXcds) * (unsigned)p.splits;
+  const unsigned units = p.split_major ? (unsigned)p.num_units
+                                       : (unsigned)kXcds * (unsigned)((p.num_units + kXcds - 1) / kXcds);
+  const unsigned grid = units * (unsigned)p.splits;
   if (grid == 0) return hipSuccess;
   if (p.num_loras <= 64)
     hipLaunchKernelGGL((sgmv_decode_kernel<T, R, RB, true>), dim3(grid), dim3(kThreads), 0, stream, p);

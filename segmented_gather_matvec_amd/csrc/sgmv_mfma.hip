@@ -187,11 +187,21 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_reduce_kernel(MfmaParams p
   const Unit un = resolve_unit<kMT>(p.seg_indptr, p.lora_idx, p.num_segs, p.num_loras, p.n_rows,
                                     p.direct_units64, blockIdx.x);
   if (un.L <= 0) return;
+  constexpr int kBatch = 8;  // partial planes fetched at once (independent loads)
   for (int o = threadIdx.x; o < un.L * R / 4; o += kThreads) {
     const int64_t off = (int64_t)un.r0 * R + o * 4;
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
-    for (int k = 0; k < p.ksplit; ++k)
-      s += *reinterpret_cast<const f32x4*>(p.partials + (int64_t)k * p.partial_stride + off);
+    for (int k0 = 0; k0 < p.ksplit; k0 += kBatch) {
+      f32x4 v[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int k = k0 + u < p.ksplit ? k0 + u : p.ksplit - 1;
+        v[u] = *reinterpret_cast<const f32x4*>(p.partials + (int64_t)k * p.partial_stride + off);
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+        if (k0 + u < p.ksplit) s += v[u];
+    }
     *reinterpret_cast<f32x4*>(p.V + off) = s;
   }
 }
@@ -254,14 +264,28 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_expand_kernel(MfmaParams p
   u32x4 bvA[NBP][2], yvA[NYV], bvB[NBP][2], yvB[NYV];
   issue(ch0, bvA, yvA);
 
-  // V of the tile rows, split hi/lo, then this wave's MFMA A fragments.
-  for (int o = t; o < kMT * R; o += kThreads) {
+  // V of the tile rows (all fetched at once), split hi/lo, then this wave's
+  // MFMA A fragments.
+  constexpr int NV4 = kMT * R / 4 / kThreads;  // float4 of V per thread
+  f32x4 vv[NV4];
+#pragma unroll
+  for (int m = 0; m < NV4; ++m) {
+    const int o = (t + kThreads * m) * 4;
+    const int rr = o / R;
+    vv[m] = *reinterpret_cast<const f32x4*>(p.V + (int64_t)(r0 + (rr < L ? rr : 0)) * R + o % R);
+  }
+#pragma unroll
+  for (int m = 0; m < NV4; ++m) {
+    const int o = (t + kThreads * m) * 4;
     const int rr = o / R, j = o % R;
-    const float v = rr < L ? p.V[(int64_t)(r0 + rr) * R + j] : 0.f;
-    const uint16_t hi = T::round(v);
-    const uint16_t lo = T::round(v - T::one(hi));
-    lds_v[rr * VST + j] = hi;
-    lds_v[rr * VST + R + j] = lo;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float v = rr < L ? vv[m][e] : 0.f;
+      const uint16_t hi = T::round(v);
+      const uint16_t lo = T::round(v - T::one(hi));
+      lds_v[rr * VST + j + e] = hi;
+      lds_v[rr * VST + R + j + e] = lo;
+    }
   }
   __syncthreads();
   u32x4 af[KSTEPS];
@@ -299,7 +323,7 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_expand_kernel(MfmaParams p
       const int rl = v / CV;
       const int cl = (v % CV) * 8;
       const int rr = wave * 16 + rl;
-      if (rr < L && c0 + cl < p.h_out) {
+      if (rr < L && ch < ch1 && c0 + cl < p.h_out) {
         float yf[8];
         unpack8<T>(yv[u], yf);
 #pragma unroll
@@ -308,14 +332,15 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_expand_kernel(MfmaParams p
       }
     }
   };
-  // Ping-pong: chunk ch+1 is in flight while chunk ch is computed.
+  // Ping-pong: chunk ch+1 is in flight while chunk ch is computed. The body
+  // has no branch, so the loads of one buffer are waited for only where that
+  // buffer is consumed; a chunk past ch1 loads clamped addresses and stores
+  // nothing.
   for (int ch = ch0; ch < ch1; ch += 2) {
     issue(ch + 1, bvB, yvB);
     compute(ch, bvA, yvA);
-    if (ch + 1 < ch1) {
-      issue(ch + 2, bvA, yvA);
-      compute(ch + 1, bvB, yvB);
-    }
+    issue(ch + 2, bvA, yvA);
+    compute(ch + 1, bvB, yvB);
   }
 }
 

@@ -57,6 +57,11 @@ struct DecodeParams {
   uint64_t* slots;  // [num_units][splits][parts][RB*rank] tagged partials
   int32_t n_rows, h_in, h_out, num_segs, num_loras;
   int32_t num_units, splits, kc, cw, direct_units;
+  // 1: workgroup b runs split b % splits of unit b / splits, so the splits of a
+  // unit go round-robin over the XCDs and equal splits of neighbouring units
+  // (which read the same A_k / B_k slice when they share a LoRA) meet on one
+  // XCD. 0: the splits of a unit share an XCD (grid padded to 8 units).
+  int32_t split_major;
 };
 
 bool decode_supported(int rank, int rb);

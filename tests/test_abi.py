@@ -46,6 +46,40 @@ def test_problem_struct_layout_matches_header():
     assert f"SGMV_WS_COUNTER_BYTES ((size_t)1 << 20)" in src and sg.SGMV_WS_COUNTER_BYTES == 1 << 20
 
 
+def test_plan_info_struct_layout_matches_header():
+    src = open(HEADER).read()
+    body = re.search(r"typedef struct sgmv_plan_info \{(.*?)\} sgmv_plan_info_t;", src, re.S).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    fields = re.findall(r"int32_t\s+(\w+);", body)
+    assert fields == [n for n, _ in sg.sgmv_plan_info_t._fields_]
+    assert ctypes.sizeof(sg.sgmv_plan_info_t) == 4 * len(fields)
+    for name, val in [("SGMV_ROUTE_NONE", 0), ("SGMV_ROUTE_DECODE", 1), ("SGMV_ROUTE_MFMA", 2),
+                      ("SGMV_ROUTE_VECTOR", 3)]:
+        assert re.search(rf"{name} = {val}\b", src) and getattr(sg, name) == val
+
+
+@pytest.mark.parametrize("kw,routes", [
+    ({"num_segs": 0, "max_seg_len": 0}, {sg.SGMV_ROUTE_NONE}),
+    ({"variant": sg.SGMV_VARIANT_VECTOR}, {sg.SGMV_ROUTE_VECTOR}),
+    ({"variant": sg.SGMV_VARIANT_MFMA, "rank": 16}, {sg.SGMV_ROUTE_MFMA}),
+    # the one-launch route needs the device's occupancy; without a GPU it is never taken
+    ({}, {sg.SGMV_ROUTE_DECODE, sg.SGMV_ROUTE_VECTOR, sg.SGMV_ROUTE_MFMA}),
+    ({"n_rows": 2048, "num_segs": 4, "max_seg_len": 1024, "rank": 64},
+     {sg.SGMV_ROUTE_MFMA}),
+])
+def test_query_plan_routes(kw, routes):
+    info = sg.sgmv_query_plan(good(**kw))
+    assert info.route in routes
+    if info.route == sg.SGMV_ROUTE_NONE:
+        assert info.launches == 0 and info.grid == 0
+    else:
+        assert info.launches == {1: 1, 2: 3, 3: 2}[info.route]
+        assert info.units >= 1 and info.splits >= 1 and info.grid >= 1
+    with pytest.raises(sg.SgmvError):
+        sg.sgmv_query_plan(good(rank=7))
+    assert sg.load_library().sgmv_query_plan(ctypes.byref(good()), None) == sg.SGMV_ERR_INVALID_ARG
+
+
 def test_status_strings():
     for st in range(5):
         assert sg.sgmv_status_str(st).startswith("SGMV_")

@@ -87,6 +87,29 @@ def test_popularity_sweep(kind, n, variant):
     assert call.counters_clear()
 
 
+@pytest.mark.parametrize("kind,n", [("identical", 32), ("uniform", 64), ("skewed", 64)])
+def test_popularity_auto_takes_one_launch_route(kind, n):
+    """Decode-shaped batches run the one-launch kernel with one-row blocks."""
+    call = run_workload(workloads.popularity(kind, n))
+    info = sg.sgmv_query_plan(call.problem)
+    assert (info.route, info.launches, info.rows_per_unit) == (sg.SGMV_ROUTE_DECODE, 1, 1), info.as_dict()
+
+
+@pytest.mark.parametrize("kind,n,splits,rows_per_unit", [
+    ("identical", 32, 64, 4), ("identical", 32, 256, 16), ("identical", 64, 128, 16),
+    ("skewed", 32, 64, None), ("uniform", 64, 32, None), ("skewed", 64, 48, None)])
+def test_popularity_larger_row_blocks(kind, n, splits, rows_per_unit):
+    """Forcing more splits pushes the one-launch kernel to 4- and 16-row blocks
+    (the plans that larger batches get), or off it when no plan fits on the
+    device at once; the result must not change."""
+    call = run_workload(workloads.popularity(kind, n), sg.SGMV_VARIANT_FUSED, splits)
+    info = sg.sgmv_query_plan(call.problem)
+    if rows_per_unit is not None:
+        assert (info.route, info.rows_per_unit) == (sg.SGMV_ROUTE_DECODE, rows_per_unit), info.as_dict()
+    assert_close(to_bits(call.apply()), call.oracle_apply(), "f16")
+    assert call.counters_clear()
+
+
 @pytest.mark.parametrize("variant", [sg.SGMV_VARIANT_AUTO, sg.SGMV_VARIANT_VECTOR, sg.SGMV_VARIANT_MFMA])
 @pytest.mark.parametrize("rank", [16, 64])
 def test_mixed_prefill_decode_reduced(rank, variant):
