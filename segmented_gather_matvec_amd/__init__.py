@@ -69,6 +69,14 @@ def load_library(path: str = LIB_PATH):
     if not os.path.exists(path):
         raise ImportError(f"libsgmv is not built ({path} missing); run "
                           "`python -m segmented_gather_matvec_amd.build` with ROCm's hipcc")
+    # PyTorch ships its own HIP runtime.  Load it first so that libsgmv binds to
+    # that same runtime (one process, one HIP runtime); loading libsgmv first
+    # would bring in the system runtime beside torch's, and launches on torch's
+    # memory and streams would then fail.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     prob = ctypes.POINTER(sgmv_problem_t)

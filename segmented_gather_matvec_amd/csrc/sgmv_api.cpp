@@ -185,17 +185,17 @@ size_t decode_ws_bytes(const sgmv_problem_t& p) {
 
 // Plan of the matrix-core kernels (long segments).
 struct MfmaPlan {
-  int64_t units = 0, units64 = 0;
-  int direct = 1, direct64 = 1;
+  int64_t units64 = 0;
+  int direct64 = 1;
   int ksplit = 1;
   int kc = 0;
   int chunks_per_wg = 1;
   size_t partial_bytes = 0;  // split partials of V, fp32 [ksplit][n_rows][rank]
 };
 
-// Split H1 so that shrink workgroups (row units x chunks) reach about two per
-// CU; group expand column chunks so that about four workgroups run per CU.
-constexpr int kMfmaShrinkTarget = 512;
+// Aim for about four shrink workgroups (row tile x H1 chunk) and four expand
+// workgroups per CU.
+constexpr int kMfmaShrinkTarget = 1024;
 constexpr int kMfmaExpandTarget = 1024;
 
 int64_t units_for(const sgmv_problem_t& p, int rows, int* direct) {
@@ -209,15 +209,21 @@ int64_t units_for(const sgmv_problem_t& p, int rows, int* direct) {
 
 MfmaPlan plan_mfma(const sgmv_problem_t& p) {
   MfmaPlan m;
-  m.units = units_for(p, sgmv::kMfmaShrinkUnitRows, &m.direct);
   m.units64 = units_for(p, sgmv::kMfmaRowsPerTile, &m.direct64);
-  const int64_t ks = std::max<int64_t>(1, std::min<int64_t>(ceil_div(kMfmaShrinkTarget, std::max<int64_t>(m.units, 1)),
-                                                            ceil_div(p.h_in, sgmv::kMfmaKChunk)));
+  // The H1 split multiplies the workgroups, but every split writes (and the
+  // reduce reads) one fp32 plane of V: keep that traffic within a quarter of
+  // what the shrink must read anyway (X, plus A_k once per segment).
+  const int64_t units = std::max<int64_t>(m.units64, 1);
+  const double must_read = 2.0 * (double)p.n_rows * p.h_in + 2.0 * (double)p.num_segs * p.h_in * p.rank;
+  const double per_split = 8.0 * (double)p.n_rows * p.rank;
+  const int64_t ks_traffic = std::max<int64_t>(1, (int64_t)(0.25 * must_read / std::max(per_split, 1.0)));
+  const int64_t ks = std::max<int64_t>(1, std::min<int64_t>({ceil_div(kMfmaShrinkTarget, units), ks_traffic,
+                                                             ceil_div(p.h_in, sgmv::kMfmaKChunk)}));
   m.kc = (int)round_up(ceil_div(p.h_in, ks), sgmv::kMfmaKChunk);
   m.ksplit = (int)ceil_div(p.h_in, m.kc);
   const int64_t nchunks = ceil_div(p.h_out, sgmv::kMfmaColsPerTile);
   m.chunks_per_wg = (int)std::max<int64_t>(1, std::min<int64_t>(nchunks,
-      ceil_div(std::max<int64_t>(m.units64, 1) * nchunks, kMfmaExpandTarget)));
+      ceil_div(units * nchunks, kMfmaExpandTarget)));
   m.partial_bytes = (size_t)m.ksplit * (size_t)p.n_rows * p.rank * sizeof(float);
   return m;
 }
@@ -233,8 +239,6 @@ sgmv::MfmaParams mfma_params(const sgmv_problem_t& p, const MfmaPlan& m, const i
   q.h_out = p.h_out;
   q.num_segs = p.num_segs;
   q.num_loras = p.num_loras;
-  q.num_units = (int32_t)m.units;
-  q.direct_units = m.direct;
   q.num_units64 = (int32_t)m.units64;
   q.direct_units64 = m.direct64;
   q.ksplit = m.ksplit;
@@ -478,7 +482,7 @@ sgmv_status_t sgmv_query_plan(const sgmv_problem_t* p, sgmv_plan_info_t* info) {
       info->rows_per_unit = sgmv::kMfmaRowsPerTile;
       info->units = (int32_t)m.units64;
       info->splits = m.ksplit;
-      info->grid = (int32_t)(m.units * m.ksplit);
+      info->grid = (int32_t)(m.units64 * m.ksplit);
       break;
     }
     case SGMV_ROUTE_VECTOR: {

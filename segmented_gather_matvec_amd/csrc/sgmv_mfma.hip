@@ -9,12 +9,14 @@
 // (lane l holds A[l%16][8(l/16)+e], B[8(l/16)+e][l%16], D[4(l/16)+i][l%16]).
 //
 // Three launches:
-//  1. shrink: a workgroup (4 waves) takes up to 256 rows of one segment (four
-//     64-row subtiles) and one chunk of H1.  Each 256-row sub-chunk of A_k is
-//     staged once in LDS, transposed to [r][h] so that a lane reads the 8
-//     consecutive h of one rank with one 128-bit LDS read, and reused by all
-//     subtiles; X fragments go straight from HBM into registers.  Each H1
-//     chunk writes its own fp32 partial plane of V.
+//  1. shrink: a workgroup (4 waves, 16 rows each) takes up to 64 rows of one
+//     segment and one chunk of H1, streamed in stages of 128 H1 rows that are
+//     pipelined two deep: the X fragments (registers, straight from HBM) and
+//     A_k rows of the next stage are in flight while the current one is
+//     multiplied.  Each stage of A_k is staged in LDS, transposed to [r][h] so
+//     that a lane reads the 8 consecutive h of one rank with one 128-bit LDS
+//     read.  Each H1 chunk writes its own fp32 partial plane of V; workgroups
+//     that read the same chunk of A_k run on one XCD.
 //  2. reduce: V = sum of the partial planes, in chunk order (reproducible).
 //  3. expand: a workgroup takes 64 rows and a group of 128-column chunks.  V is
 //     split into V_hi + V_lo (both in the input format), consumed as a K of 2r
@@ -35,9 +37,18 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMT = kMfmaRowsPerTile;        // 64 rows per subtile: 16 per wave
-constexpr int kUnitRows = kMfmaShrinkUnitRows;  // rows per shrink workgroup (4 subtiles)
-constexpr int kKSub = kMfmaKChunk;           // A_k rows staged per sub-chunk
 constexpr int kCW = kMfmaColsPerTile;        // 128 output columns per expand chunk
+
+constexpr int kXcds = 8;
+
+// Workgroups are dispatched round-robin over the 8 XCDs (workgroup b on XCD
+// b % 8), each with its own L2.  Give every XCD a contiguous run of the linear
+// work order (grid = 8 * per_xcd), so that items adjacent in that order, which
+// read the same weight slice, run on one XCD and share its L2.
+__device__ inline int xcd_linear_index() {
+  const int per_xcd = gridDim.x / kXcds;
+  return (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+}
 
 template <class T>
 __device__ inline f32x4 mfma(const u32x4& a, const u32x4& b, f32x4 c);
@@ -66,15 +77,19 @@ __device__ inline void store_pair_transposed(uint16_t* dst, int stride, const u3
 }
 
 // ---------------------------------------------------------------- shrink
+// H1 rows per pipeline stage: while one stage's X fragments and A_k rows are
+// multiplied, the next stage's loads are in flight.
+constexpr int kKStage = 128;
+
 template <class T, int R>
 __global__ __launch_bounds__(kThreads) void sgmv_mfma_shrink_kernel(MfmaParams p) {
-  constexpr int NT = R / 16;                   // 16-wide rank tiles
-  constexpr int JG = R / 8;                    // 128-bit vectors per row of A_k
-  constexpr int NPAIR = kKSub / 2 * JG / kThreads;  // (h, h+1) vector pairs per thread
-  constexpr int KSTEPS = kKSub / 32;           // MFMA k-steps per sub-chunk
-  constexpr int NSUB = kUnitRows / kMT;        // 64-row subtiles per workgroup
-  constexpr int AST = kKSub + 8;               // LDS row stride (halves) of transposed A_k
-  static_assert(NPAIR >= 1, "tile shape");
+  constexpr int NT = R / 16;                // 16-wide rank tiles
+  constexpr int JG = R / 8;                 // 128-bit vectors per row of A_k
+  constexpr int PAIRS = kKStage / 2 * JG;   // (h, h+1) vector pairs of A_k per stage
+  constexpr int NPAIR = (PAIRS + kThreads - 1) / kThreads;
+  constexpr int MS = kKStage / 32;          // MFMA k-steps per stage
+  constexpr int AST = kKStage + 8;          // LDS row stride (halves) of transposed A_k
+  static_assert(kMfmaKChunk % (2 * kKStage) == 0, "H1 chunks hold whole stage pairs");
   __shared__ __attribute__((aligned(16))) uint16_t lds_at[R * AST];
 
   const int t = threadIdx.x;
@@ -82,114 +97,118 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_shrink_kernel(MfmaParams p
   const int wave = t >> 6;
   const int q = lane >> 4;   // k-group of the lane (8 k each)
   const int ml = lane & 15;  // row (A operand) / rank column (B operand) of the lane
-  const int KS = p.ksplit;
-  const int unit = blockIdx.x / KS;
-  const int g = blockIdx.x - unit * KS;
-  const Unit un = resolve_unit<kUnitRows>(p.seg_indptr, p.lora_idx, p.num_segs, p.num_loras, p.n_rows,
-                                          p.direct_units, unit);
+  // Linear order: H1 chunk major, so the row units that read one chunk of A_k
+  // share an XCD.
+  const int idx = xcd_linear_index();
+  if (idx >= p.num_units64 * p.ksplit) return;
+  const int g = idx / p.num_units64;
+  const int unit = idx - g * p.num_units64;
+  const Unit un = resolve_unit<kMT>(p.seg_indptr, p.lora_idx, p.num_segs, p.num_loras, p.n_rows,
+                                    p.direct_units64, unit);
   if (un.L <= 0) return;
   const int L = un.L, r0 = un.r0;
   const uint16_t* Ak = reinterpret_cast<const uint16_t*>(p.A_ptrs[un.k]);
   const int k0 = g * p.kc;
   const int k1 = p.h_in < k0 + p.kc ? p.h_in : k0 + p.kc;
-  const int nsub = (L + kMT - 1) / kMT;
+  // Row this lane feeds into the MFMA A operand (rows past the segment re-read
+  // its last row and are never stored).
+  const int row = wave * 16 + ml;
+  const uint16_t* xrow = p.X + (int64_t)(r0 + (row < L ? row : L - 1)) * p.h_in;
 
-  // Row of the tile this lane feeds into the MFMA A operand, per subtile.
-  const uint16_t* xrow[NSUB];
-#pragma unroll
-  for (int st = 0; st < NSUB; ++st) {
-    const int row = st * kMT + wave * 16 + ml;
-    xrow[st] = p.X + (int64_t)(r0 + (row < L ? row : L - 1)) * p.h_in;
-  }
-
-  f32x4 acc[NSUB][NT];
-#pragma unroll
-  for (int st = 0; st < NSUB; ++st)
-#pragma unroll
-    for (int n = 0; n < NT; ++n) acc[st][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int kk = k0; kk < k1; kk += kKSub) {
-    const int nk = k1 - kk < kKSub ? k1 - kk : kKSub;  // multiple of 8
-    u32x4 av[NPAIR][2];
+  // All loads of one stage, at clamped (valid) addresses; values past k1 are
+  // zeroed where they are consumed.
+  auto issue = [&](int kk, u32x4 (&x)[MS], u32x4 (&a)[NPAIR][2]) {
 #pragma unroll
     for (int m = 0; m < NPAIR; ++m) {
       const int pr = t + kThreads * m;
-      const int h = (pr / JG) * 2, jg = pr % JG;
-      av[m][0] = load_stream(Ak + (h < nk ? (int64_t)(kk + h) * R + jg * 8 : 0));
-      av[m][1] = load_stream(Ak + (h + 1 < nk ? (int64_t)(kk + h + 1) * R + jg * 8 : 0));
+      const int h = kk + (pr / JG) * 2, jg = pr % JG;
+      const bool ok = pr < PAIRS;
+      a[m][0] = load_stream(Ak + (ok && h < k1 ? (int64_t)h * R + jg * 8 : 0));
+      a[m][1] = load_stream(Ak + (ok && h + 1 < k1 ? (int64_t)(h + 1) * R + jg * 8 : 0));
     }
-    u32x4 xf[KSTEPS];
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
+    for (int s = 0; s < MS; ++s) {
       const int h = kk + s * 32 + q * 8;
-      xf[s] = load_stream(xrow[0] + (h < k1 ? h : 0));
+      x[s] = load_stream(xrow + (h < k1 ? h : 0));
     }
-    __syncthreads();  // the previous sub-chunk is done with lds_at
+  };
+
+  f32x4 acc[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Stage the A_k rows transposed ([r][h]) so that a lane reads the 8
+  // consecutive h of one rank with one 128-bit LDS read, then multiply.
+  auto compute = [&](int kk, const u32x4 (&x)[MS], const u32x4 (&a)[NPAIR][2]) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    __syncthreads();  // the previous stage is done with lds_at
 #pragma unroll
     for (int m = 0; m < NPAIR; ++m) {
       const int pr = t + kThreads * m;
-      const int h = (pr / JG) * 2, jg = pr % JG;
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      store_pair_transposed(&lds_at[(jg * 8) * AST + h], AST, h < nk ? av[m][0] : z, h + 1 < nk ? av[m][1] : z);
+      if (pr < PAIRS) {
+        const int h = (pr / JG) * 2, jg = pr % JG;
+        store_pair_transposed(&lds_at[(jg * 8) * AST + h], AST, kk + h < k1 ? a[m][0] : z,
+                              kk + h + 1 < k1 ? a[m][1] : z);
+      }
     }
     __syncthreads();
-    const int steps = (nk + 31) / 32;
 #pragma unroll
-    for (int st = 0; st < NSUB; ++st) {
-      if (st < nsub) {
-        // X fragments of the next subtile are fetched while this one computes.
-        u32x4 xn[KSTEPS];
-        if (st + 1 < nsub) {
+    for (int s = 0; s < MS; ++s) {
+      const u32x4 xa = kk + s * 32 + q * 8 < k1 ? x[s] : z;  // ragged tail of H1
 #pragma unroll
-          for (int s = 0; s < KSTEPS; ++s) {
-            const int h = kk + s * 32 + q * 8;
-            xn[s] = load_stream(xrow[st + 1 < NSUB ? st + 1 : st] + (h < k1 ? h : 0));
-          }
-        }
-#pragma unroll
-        for (int s = 0; s < KSTEPS; ++s) {
-          if (s < steps) {
-            u32x4 a = xf[s];
-            if (kk + s * 32 + q * 8 >= k1) a = u32x4{0u, 0u, 0u, 0u};  // ragged tail of H1
-#pragma unroll
-            for (int n = 0; n < NT; ++n) {
-              const u32x4 b = load_vec(&lds_at[(n * 16 + ml) * AST + s * 32 + q * 8]);
-              acc[st][n] = mfma<T>(a, b, acc[st][n]);
-            }
-          }
-        }
-        if (st + 1 < nsub) {
-#pragma unroll
-          for (int s = 0; s < KSTEPS; ++s) xf[s] = xn[s];
-        }
-      }
+      for (int n = 0; n < NT; ++n)
+        acc[n] = mfma<T>(xa, load_vec(&lds_at[(n * 16 + ml) * AST + s * 32 + q * 8]), acc[n]);
     }
+  };
+
+  // Ping-pong over stage pairs: each buffer is waited for only where it is
+  // consumed.  A stage past k1 loads clamped addresses and contributes zeros;
+  // no loads are issued past the last stage pair (the stores below would
+  // wait for them).
+  u32x4 xA[MS], aA[NPAIR][2], xB[MS], aB[NPAIR][2];
+  issue(k0, xA, aA);
+  for (int kk = k0; kk < k1; kk += 2 * kKStage) {
+    issue(kk + kKStage, xB, aB);
+    compute(kk, xA, aA);
+    if (kk + 2 * kKStage < k1) issue(kk + 2 * kKStage, xA, aA);
+    compute(kk + kKStage, xB, aB);
   }
 
-  // D[4q+i][ml] of rank tile n: row st*64 + wave*16 + 4q + i, rank n*16 + ml.
+  // D[4q+i][ml] of rank tile n: row wave*16 + 4q + i, rank n*16 + ml.
   float* dst = p.partials + (int64_t)g * p.partial_stride;
 #pragma unroll
-  for (int st = 0; st < NSUB; ++st)
+  for (int n = 0; n < NT; ++n)
 #pragma unroll
-    for (int n = 0; n < NT; ++n)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int rr = st * kMT + wave * 16 + q * 4 + i;
-        if (rr < L) dst[(int64_t)(r0 + rr) * R + n * 16 + ml] = acc[st][n][i];
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int rr = wave * 16 + q * 4 + i;
+      if (rr < L) dst[(int64_t)(r0 + rr) * R + n * 16 + ml] = acc[n][i];
+    }
 }
 
 // ---------------------------------------------------------------- reduce
 // V[row] = sum over the ksplit partial planes, in plane order, for the rows
-// of every segment (rows outside all segments are left untouched).
+// of every segment (rows outside all segments are left untouched).  A
+// workgroup takes 16 rows of one 64-row unit; every thread fetches its float4
+// from up to 16 planes at once.
+constexpr int kReduceRows = 16;
+
 template <int R>
 __global__ __launch_bounds__(kThreads) void sgmv_mfma_reduce_kernel(MfmaParams p) {
+  constexpr int PER_ROWS = kMT / kReduceRows;
+  constexpr int NV = kReduceRows * R / 4;     // float4 of V per workgroup
+  constexpr int NO = (NV + kThreads - 1) / kThreads;
+  constexpr int kBatch = 16;
+  const int unit = blockIdx.x / PER_ROWS;
+  const int part = blockIdx.x - unit * PER_ROWS;
   const Unit un = resolve_unit<kMT>(p.seg_indptr, p.lora_idx, p.num_segs, p.num_loras, p.n_rows,
-                                    p.direct_units64, blockIdx.x);
-  if (un.L <= 0) return;
-  constexpr int kBatch = 8;  // partial planes fetched at once (independent loads)
-  for (int o = threadIdx.x; o < un.L * R / 4; o += kThreads) {
-    const int64_t off = (int64_t)un.r0 * R + o * 4;
+                                    p.direct_units64, unit);
+  const int rows = un.L - part * kReduceRows;
+  if (rows <= 0) return;
+#pragma unroll
+  for (int o = 0; o < NO; ++o) {
+    const int v4 = threadIdx.x + kThreads * o;
+    if (v4 >= NV || v4 * 4 >= rows * R) continue;
+    const int64_t off = (int64_t)(un.r0 + part * kReduceRows) * R + v4 * 4;
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
     for (int k0 = 0; k0 < p.ksplit; k0 += kBatch) {
       f32x4 v[kBatch];
@@ -229,8 +248,12 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_expand_kernel(MfmaParams p
   const int ml = lane & 15;
   const int nchunks = (p.h_out + kCW - 1) / kCW;
   const int ngroups = (nchunks + p.chunks_per_wg - 1) / p.chunks_per_wg;
-  const int unit = blockIdx.x / ngroups;
-  const int grp = blockIdx.x - unit * ngroups;
+  // Linear order: column group major, so the row units that read one slice of
+  // B_k share an XCD.
+  const int idx = xcd_linear_index();
+  if (idx >= p.num_units64 * ngroups) return;
+  const int grp = idx / p.num_units64;
+  const int unit = idx - grp * p.num_units64;
   const Unit un = resolve_unit<kMT>(p.seg_indptr, p.lora_idx, p.num_segs, p.num_loras, p.n_rows,
                                     p.direct_units64, unit);
   if (un.L <= 0) return;
@@ -344,18 +367,20 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_expand_kernel(MfmaParams p
   }
 }
 
+unsigned xcd_grid(unsigned items) { return kXcds * ((items + kXcds - 1) / kXcds); }
+
 template <class T, int R>
 hipError_t launch_t(int stage, const MfmaParams& p, hipStream_t s) {
   unsigned grid = 0;
   if (stage == 0) {
-    grid = (unsigned)p.num_units * (unsigned)p.ksplit;
+    grid = xcd_grid((unsigned)p.num_units64 * (unsigned)p.ksplit);
     if (grid) hipLaunchKernelGGL((sgmv_mfma_shrink_kernel<T, R>), dim3(grid), dim3(kThreads), 0, s, p);
   } else if (stage == 1) {
-    grid = (unsigned)p.num_units64;
+    grid = (unsigned)p.num_units64 * (unsigned)(kMT / kReduceRows);
     if (grid) hipLaunchKernelGGL((sgmv_mfma_reduce_kernel<R>), dim3(grid), dim3(kThreads), 0, s, p);
   } else {
     const int nchunks = (p.h_out + kCW - 1) / kCW;
-    grid = (unsigned)p.num_units64 * (unsigned)((nchunks + p.chunks_per_wg - 1) / p.chunks_per_wg);
+    grid = xcd_grid((unsigned)p.num_units64 * (unsigned)((nchunks + p.chunks_per_wg - 1) / p.chunks_per_wg));
     if (grid) hipLaunchKernelGGL((sgmv_mfma_expand_kernel<T, R>), dim3(grid), dim3(kThreads), 0, s, p);
   }
   return grid ? hipGetLastError() : hipSuccess;

@@ -71,8 +71,7 @@ int decode_resident_capacity(int dtype, int rank, int rb);
 
 // Matrix-core kernels for long segments: shrink (+ reduce of the H1 split),
 // then expand.
-constexpr int kMfmaRowsPerTile = 64;      // rows per MFMA subtile / expand workgroup
-constexpr int kMfmaShrinkUnitRows = 256;  // rows of one segment per shrink workgroup
+constexpr int kMfmaRowsPerTile = 64;      // rows of one segment per shrink / expand workgroup
 constexpr int kMfmaColsPerTile = 128;     // output columns per expand chunk
 constexpr int kMfmaKChunk = 256;          // H1 granule of the shrink's split
 
@@ -87,8 +86,7 @@ struct MfmaParams {
   const int32_t* lora_idx;
   int64_t partial_stride;  // floats between partial planes (n_rows * rank)
   int32_t n_rows, h_in, h_out, num_segs, num_loras;
-  int32_t num_units, direct_units;      // shrink units of <= 256 rows
-  int32_t num_units64, direct_units64;  // reduce / expand units of <= 64 rows
+  int32_t num_units64, direct_units64;  // units of <= 64 rows of one segment
   int32_t ksplit, kc, chunks_per_wg;
 };
 
