@@ -67,6 +67,19 @@ def counter_means(pmc_dir: str, counter: str) -> Dict[str, dict]:
     return {k: {"dispatches": len(v), "mean": st.mean(v), "median": st.median(v)} for k, v in vals.items()}
 
 
+def copy_reference(pmc_dir: str, counter: str, regex: str) -> dict:
+    """Counter of the calibration copies: among the dispatches whose kernel
+    matches `regex`, those with the largest grid (other, smaller copies made
+    by the program are left out)."""
+    rows = [r for r in _rows(pmc_dir, "counter_collection.csv")
+            if r.get("Counter_Name") == counter and re.search(regex, short_name(r["Kernel_Name"]))]
+    if not rows:
+        raise SystemExit(f"no copy dispatch matches {regex!r}")
+    grid = max(int(r["Grid_Size"]) for r in rows)
+    v = [float(r["Counter_Value"]) for r in rows if int(r["Grid_Size"]) == grid]
+    return {"dispatches": len(v), "mean": st.mean(v), "median": st.median(v), "grid": grid}
+
+
 def _match(table: Dict[str, dict], regex: str) -> dict:
     keys = [k for k in table if re.search(regex, k)]
     if not keys:
@@ -96,7 +109,7 @@ def cmd_traffic(a):
     fetch = counter_means(a.fetch, "FETCH_SIZE")
     write = counter_means(a.write, "WRITE_SIZE")
     kf, kw = _match(fetch, a.kernel), _match(write, a.kernel)
-    cf, cw = _match(fetch, a.copy), _match(write, a.copy)
+    cf, cw = copy_reference(a.fetch, "FETCH_SIZE", a.copy), copy_reference(a.write, "WRITE_SIZE", a.copy)
     # Scale: a copy of N bytes reads N and writes N bytes of HBM.
     f_scale = a.copy_bytes / (cf["mean"] * 1024.0)
     w_scale = a.copy_bytes / (cw["mean"] * 1024.0)
