@@ -110,7 +110,7 @@ DecodePlan plan_decode_rb(const sgmv_problem_t& p, int rb, int split_major) {
   if (gmin > gmax) return d;
   // Each workgroup gathers splits * parts * rows * rank partials; keep that to
   // one staging round (2048 values) unless the caller asks for more splits.
-  const int parts = d.rb == 1 ? 4 : 1;
+  const int parts = 1;  // one published partial per workgroup
   const int64_t rows = std::max(1, std::min(d.rb, p.max_seg_len));
   const int64_t gather_cap = std::max<int64_t>(1, 2048 / ((int64_t)parts * rows * p.rank));
   int64_t g = p.splits > 0 ? p.splits

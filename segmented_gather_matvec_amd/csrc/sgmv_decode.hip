@@ -97,12 +97,12 @@ __global__ __launch_bounds__(kThreads) void sgmv_decode_kernel(DecodeParams p) {
   constexpr int JQ = kDecodeLanesPerColumn;  // lanes sharing one 8-column vector of B_k
   constexpr int NB = R / JQ;                 // B_k vectors per thread
   constexpr int NY = (RB + JQ - 1) / JQ;     // Y vectors per thread
-  constexpr int PW = RB == 1 ? kWaves : 1;   // published partials per workgroup
+  constexpr int PW = 1;                      // published partials per workgroup
   constexpr int NXV = RB == 1 ? 1 : (RB * KCMAX / 8 + kThreads - 1) / kThreads;
   static_assert(RB * R <= kThreads, "one output of V per thread");
 
   __shared__ __attribute__((aligned(16))) uint16_t lds_x[RB == 1 ? 8 : RB * KCMAX];
-  __shared__ float lds_red[RB == 1 ? 1 : kWaves * RB * R];
+  __shared__ float lds_red[kWaves * RB * R];
   __shared__ float lds_stage[kStage];
   __shared__ float lds_v[RB * R];
 
@@ -253,9 +253,9 @@ __global__ __launch_bounds__(kThreads) void sgmv_decode_kernel(DecodeParams p) {
   // ---------------- publish ----------------
   // Per-unit slot layout: [G][PW][RB*R] tagged words.
   uint64_t* unit_slots = p.slots + (int64_t)unit * G * PW * (RB * R);
-  if constexpr (RB == 1) {
-    if (rank_lane) publish_tagged(unit_slots + ((int64_t)g * PW + wave) * R + j_of_lane, acc[0][0], tag);
-  } else {
+  // The waves' partials are summed in LDS first: one word per output leaves
+  // the workgroup, which keeps the device-scope exchange small.
+  {
 #pragma unroll
     for (int i = 0; i < RB; ++i)
       if (i < L && rank_lane) lds_red[(wave * RB + i) * R + j_of_lane] = acc[i][0];
@@ -283,7 +283,9 @@ __global__ __launch_bounds__(kThreads) void sgmv_decode_kernel(DecodeParams p) {
       const int it = t + kThreads * m;
       const int pp = it / n_out, o = it - pp * n_out;
       src[m] = unit_slots + (it < items ? (int64_t)(p0 + pp) * (RB * R) + o : 0);
-      w[m] = fetch_tagged(src[m]);
+      // Only lanes with an item load (device-scope loads are the exchange's
+      // cost); the others are never examined.
+      w[m] = it < items ? fetch_tagged(src[m]) : 0;
     }
     for (;;) {
       bool done = true;

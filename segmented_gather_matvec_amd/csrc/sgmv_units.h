@@ -67,7 +67,10 @@ __device__ inline Unit resolve_unit(const int32_t* seg_indptr, const int32_t* lo
   const int r0 = lo + rb * RB;
   int r1 = hi < r0 + RB ? hi : r0 + RB;
   r1 = r1 < n_rows ? r1 : n_rows;
-  if (r0 < 0 || r1 <= r0 || k < 0 || k >= num_loras) return out;
+  // One combined test (no short circuit), so that the three loads above are
+  // issued together rather than split around an early exit on r0.
+  const bool bad = (r0 < 0) | (r1 <= r0) | (k < 0) | (k >= num_loras);
+  if (bad) return out;
   out.r0 = r0;
   out.L = r1 - r0;
   out.k = k;
