@@ -193,10 +193,33 @@ struct MfmaPlan {
   size_t partial_bytes = 0;  // split partials of V, fp32 [ksplit][n_rows][rank]
 };
 
-// Aim for about four shrink workgroups (row tile x H1 chunk) and four expand
-// workgroups per CU.
+// Aim for about four shrink workgroups (row tile x H1 chunk) per CU.
+// Expand: when row tiles are mostly full, a chunk is bandwidth-bound and
+// about four workgroups per CU (dispatched as slots free up) hide latency
+// best.  When they are mostly short (decode-like rows of many LoRAs), a chunk
+// is latency-bound: the grid is then sized to be resident at once, so each
+// workgroup streams several chunks through its prefetch pipeline and pays its
+// start-up once.  Measured: on 256 rows in 34 segments this cut the expand by
+// a quarter; on 5.4k rows in 32 segments it cost a tenth.
 constexpr int kMfmaShrinkTarget = 1024;
 constexpr int kMfmaExpandTarget = 1024;
+constexpr int kMfmaShortTileRows = 32;   // mean rows per 64-row tile below which tiles count as short
+constexpr int kMfmaExpandFallbackCapacity = 512;
+
+int mfma_expand_capacity_cached(int dtype, int rank) {
+  static std::mutex mu;
+  static int cache[kMaxDevices][2][3];
+  static bool init[kMaxDevices][2][3];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  const int ri = rank == 16 ? 0 : rank == 32 ? 1 : 2;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!init[dev][dtype][ri]) {
+    cache[dev][dtype][ri] = sgmv::mfma_expand_capacity(dtype, rank);
+    init[dev][dtype][ri] = true;
+  }
+  return cache[dev][dtype][ri];
+}
 
 int64_t units_for(const sgmv_problem_t& p, int rows, int* direct) {
   if (p.max_seg_len <= rows) {
@@ -222,8 +245,13 @@ MfmaPlan plan_mfma(const sgmv_problem_t& p) {
   m.kc = (int)round_up(ceil_div(p.h_in, ks), sgmv::kMfmaKChunk);
   m.ksplit = (int)ceil_div(p.h_in, m.kc);
   const int64_t nchunks = ceil_div(p.h_out, sgmv::kMfmaColsPerTile);
-  m.chunks_per_wg = (int)std::max<int64_t>(1, std::min<int64_t>(nchunks,
-      ceil_div(units * nchunks, kMfmaExpandTarget)));
+  int64_t target = kMfmaExpandTarget;
+  if ((int64_t)p.n_rows < kMfmaShortTileRows * units) {
+    target = sgmv::mfma_supported(p.rank) ? mfma_expand_capacity_cached(p.dtype, p.rank) : 0;
+    if (target <= 0) target = kMfmaExpandFallbackCapacity;
+  }
+  const int64_t groups = std::max<int64_t>(1, std::min<int64_t>(nchunks, target / units));
+  m.chunks_per_wg = (int)ceil_div(nchunks, groups);
   m.partial_bytes = (size_t)m.ksplit * (size_t)p.n_rows * p.rank * sizeof(float);
   return m;
 }

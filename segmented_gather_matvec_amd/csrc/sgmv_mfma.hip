@@ -355,16 +355,19 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_expand_kernel(MfmaParams p
       }
     }
   };
-  // Ping-pong: chunk ch+1 is in flight while chunk ch is computed. The body
-  // has no branch, so the loads of one buffer are waited for only where that
-  // buffer is consumed; a chunk past ch1 loads clamped addresses and stores
-  // nothing.
-  for (int ch = ch0; ch < ch1; ch += 2) {
+  // Ping-pong over chunk pairs: chunk ch+1 is in flight while chunk ch is
+  // computed.  The body has no branch, so the loads of one buffer are waited
+  // for only where that buffer is consumed (a chunk past ch1 loads clamped
+  // addresses); an odd last chunk is computed once after the loop.
+  int ch = ch0;
+  for (; ch + 1 < ch1; ch += 2) {
     issue(ch + 1, bvB, yvB);
     compute(ch, bvA, yvA);
     issue(ch + 2, bvA, yvA);
     compute(ch + 1, bvB, yvB);
   }
+  // An odd last chunk, already in flight in buffer A.
+  if (ch < ch1) compute(ch, bvA, yvA);
 }
 
 unsigned xcd_grid(unsigned items) { return kXcds * ((items + kXcds - 1) / kXcds); }
@@ -403,6 +406,26 @@ hipError_t launch_stage(int dtype, int rank, int stage, const MfmaParams& p, hip
 }  // namespace
 
 bool mfma_supported(int rank) { return rank == 16 || rank == 32 || rank == 64; }
+
+template <class T, int R>
+int expand_capacity_t() {
+  int per_cu = 0, dev = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &per_cu, reinterpret_cast<const void*>(&sgmv_mfma_expand_kernel<T, R>), kThreads, 0) != hipSuccess)
+    return 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return per_cu * cus;
+}
+
+int mfma_expand_capacity(int dtype, int rank) {
+  switch (rank) {
+    case 16: return dtype == 1 ? expand_capacity_t<BF16, 16>() : expand_capacity_t<F16, 16>();
+    case 32: return dtype == 1 ? expand_capacity_t<BF16, 32>() : expand_capacity_t<F16, 32>();
+    case 64: return dtype == 1 ? expand_capacity_t<BF16, 64>() : expand_capacity_t<F16, 64>();
+  }
+  return 0;
+}
 
 hipError_t launch_mfma_shrink(int dtype, int rank, const MfmaParams& p, hipStream_t stream) {
   hipError_t e = launch_stage(dtype, rank, 0, p, stream);

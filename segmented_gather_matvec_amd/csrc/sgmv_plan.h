@@ -91,6 +91,8 @@ struct MfmaParams {
 };
 
 bool mfma_supported(int rank);
+// Expand workgroups that fit on the device at once (0 if unknown).
+int mfma_expand_capacity(int dtype, int rank);
 // Shrink into the partial planes, then reduce them into V (two launches).
 hipError_t launch_mfma_shrink(int dtype, int rank, const MfmaParams& p, hipStream_t stream);
 hipError_t launch_mfma_expand(int dtype, int rank, const MfmaParams& p, hipStream_t stream);
