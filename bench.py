@@ -232,7 +232,7 @@ class ModelForwardBench:
 
     dtype = "bf16"
 
-    def __init__(self, name, variant=0, splits=0, layers=None):
+    def __init__(self, name, variant=0, splits=0, layers=None, batch_projections=True):
         import numpy as np
         import torch
         import segmented_gather_matvec_amd as sg
@@ -247,15 +247,19 @@ class ModelForwardBench:
         self.distinct = len(lidx)
         self.seg = torch.from_numpy(seg).to("cuda")
         self.lidx = torch.from_numpy(lidx).to("cuda")
-        self.fn = sg.load_library().sgmv_lora_apply
+        lib = sg.load_library()
+        self.fn = lib.sgmv_lora_apply
+        self.fn_batched = lib.sgmv_lora_apply_batched
+        self.batch_projections = batch_projections
         self.calls, self.keep, total = [], [], 0
+        self.launch_groups = []  # per layer: lists of projection indices issued as one call
         probs = {}
         for (_, h_in, h_out) in wl.LLAMA13B_PROJ:
             if (h_in, h_out) not in probs:
                 probs[(h_in, h_out)] = sg.make_problem("bf16", self.n, h_in, h_out, self.rank, self.P,
                                                         len(lidx), mx, variant, splits)
         self.probs = probs
-        ws_bytes = max(sg.sgmv_workspace_bytes(p) for p in probs.values())
+        ws_bytes = max(sg.batched_workspace_bytes(p, 3) for p in probs.values())
         self.ws = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda")
         for layer in range(self.layers):
             xs = {"qkv": wl.device_normal((self.n, 5120), 1.0, "bf16", 900000 + 4 * layer),
@@ -277,41 +281,67 @@ class ModelForwardBench:
                                    self.seg.data_ptr(), self.lidx.data_ptr(), self.ws.data_ptr(),
                                    self.ws.numel()))
                 total += algorithmic_bytes(2, self.n, h_in, h_out, self.rank, self.distinct)
+        # Projections that read the same input (q, k, v; gate, up) run as one
+        # batched call unless asked otherwise.
+        names = [pn for (pn, _, _) in wl.LLAMA13B_PROJ]
+        groups = ([[names.index(g) for g in grp] for grp in (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))]
+                  if batch_projections else [[i] for i in range(len(names))])
+        self.batched, self.group_idx = [], []
+        self.group_names = ",".join("".join(names[j] for j in grp) for grp in groups)
+        for layer in range(self.layers):
+            for grp in groups:
+                idx = [layer * len(names) + j for j in grp]
+                self.group_idx.append(idx)
+                if len(idx) == 1:
+                    self.batched.append(("single", self.calls[idx[0]]))
+                else:
+                    first = self.calls[idx[0]]
+                    arr = (sg.sgmv_projection_t * len(idx))(
+                        *[sg.sgmv_projection_t(self.calls[c][2], self.calls[c][3], self.calls[c][4]) for c in idx])
+                    self.keep.append(arr)
+                    self.batched.append(("batched", (first[0], first[1], arr, len(idx), first[5], first[6], first[7],
+                                                     first[8])))
         self.bytes = total
         self.rows_per_step = self.n
-        self.calls_per_step = len(self.calls)
+        self.calls_per_step = len(self.batched)
         torch.cuda.synchronize()
 
     def step(self, c, stream):
-        for args in self.calls:
-            st = self.fn(*args, stream)
+        for kind, args in self.batched:
+            st = self.fn(*args, stream) if kind == "single" else self.fn_batched(*args, stream)
             if st != 0:
                 raise RuntimeError(self.sg.sgmv_status_str(st))
 
     def check_sample(self, rows=16):
-        """Two calls (first layer q, last layer down) against the oracle on sampled rows."""
+        """The first and the last call of a forward (layer 0's first projection group,
+        the last layer's down projection), every projection in them against the
+        oracle on sampled rows."""
         import numpy as np
         import oracle
         torch = self.torch
         sid = torch.cuda.current_stream().cuda_stream
         used = set(int(k) for k in self.lidx_h)
         worst = 0.0
-        for idx in (0, len(self.calls) - 1):
-            A, B, Y, X, _, _ = self.keep[idx]
-            Xh, Y0 = _bits(X), _bits(Y).copy()
-            Ah = [_bits(A[k]) if k in used else np.zeros((1, 1), np.uint16) for k in range(self.P)]
-            Bh = [_bits(B[k]) if k in used else np.zeros((1, 1), np.uint16) for k in range(self.P)]
-            st = self.fn(*self.calls[idx], sid)
+        for g in (0, len(self.batched) - 1):
+            snaps = []
+            for idx in self.group_idx[g]:
+                A, B, Y, X, _, _ = self.keep[idx]
+                snaps.append((Y, _bits(X), _bits(Y).copy(),
+                              [_bits(A[k]) if k in used else np.zeros((1, 1), np.uint16) for k in range(self.P)],
+                              [_bits(B[k]) if k in used else np.zeros((1, 1), np.uint16) for k in range(self.P)]))
+            kind, args = self.batched[g]
+            st = self.fn(*args, sid) if kind == "single" else self.fn_batched(*args, sid)
             if st != 0:
                 raise RuntimeError(self.sg.sgmv_status_str(st))
             torch.cuda.synchronize()
             mask = np.zeros(self.n, np.uint8)
-            mask[np.random.default_rng(idx).choice(self.n, rows, replace=False)] = 1
+            mask[np.random.default_rng(g).choice(self.n, rows, replace=False)] = 1
             mask[[0, self.n - 1]] = 1
-            got = oracle.decode(_bits(Y), "bf16")
-            ref = oracle.sgmv_apply("bf16", Xh, Ah, Bh, self.seg_h, self.lidx_h, Y0, row_mask=mask)
             sel = mask.astype(bool)
-            worst = max(worst, float((np.abs(got[sel] - ref[sel]) / (1e-3 + 1e-2 * np.abs(ref[sel]))).max()))
+            for Y, Xh, Y0, Ah, Bh in snaps:
+                got = oracle.decode(_bits(Y), "bf16")
+                ref = oracle.sgmv_apply("bf16", Xh, Ah, Bh, self.seg_h, self.lidx_h, Y0, row_mask=mask)
+                worst = max(worst, float((np.abs(got[sel] - ref[sel]) / (1e-3 + 1e-2 * np.abs(ref[sel]))).max()))
         if worst > 1.0:
             raise AssertionError(f"bench parity check failed: max err/bound {worst:.3f}")
         return worst
@@ -319,7 +349,8 @@ class ModelForwardBench:
     def config(self):
         return {"workload": self.name, "layers": self.layers, "projections": "q,k,v,o,gate,up,down",
                 "rank": self.rank, "batch_rows": self.n, "segments": self.distinct,
-                "distinct_loras": self.distinct, "lora_pool": self.P, "calls_per_step": len(self.calls),
+                "distinct_loras": self.distinct, "lora_pool": self.P, "projection_calls": len(self.calls),
+                "calls_per_step": len(self.batched), "calls_per_layer": self.group_names,
                 "algorithmic_bytes_per_step": self.bytes}
 
 
@@ -353,6 +384,9 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=SINGLE_WORKLOADS + MODEL_WORKLOADS)
     ap.add_argument("--variant", choices=["auto", "vector", "fused", "mfma"], default="auto")
     ap.add_argument("--splits", type=int, default=0, help="workgroups per segment block (0 = automatic)")
+    ap.add_argument("--no-batch", action="store_true",
+                    help="forward workload: one call per projection instead of batching the "
+                         "projections that share an input (q,k,v and gate,up)")
     ap.add_argument("--graph", action="store_true",
                     help="replay the timed steps from a captured HIP graph instead of eager launches")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -382,7 +416,11 @@ def main():
     model = args.workload in MODEL_WORKLOADS
     K = args.steps if args.steps is not None else (20 if model else 2000)
     W = args.warmup if args.warmup is not None else (3 if model else 200)
-    bench = (ModelForwardBench if model else SingleCallBench)(args.workload, variant=variant, splits=args.splits)
+    if model:
+        bench = ModelForwardBench(args.workload, variant=variant, splits=args.splits,
+                                  batch_projections=not args.no_batch)
+    else:
+        bench = SingleCallBench(args.workload, variant=variant, splits=args.splits)
     worst = None if args.no_check else bench.check_sample()
 
     stream = torch.cuda.current_stream()

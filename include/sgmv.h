@@ -191,6 +191,37 @@ sgmv_status_t sgmv_lora_apply(const sgmv_problem_t* problem, const void* X,
                               const int32_t* seg_indptr, const int32_t* lora_idx, void* ws,
                               size_t ws_bytes, void* stream);
 
+/* One projection of a batched apply: its own LoRA tables and output.  All
+ * three pointers are device pointers, as in sgmv_lora_apply. */
+typedef struct sgmv_projection {
+  const void* const* A_ptrs;  /* [num_loras] pointers to A_k [h_in, rank] */
+  const void* const* B_ptrs;  /* [num_loras] pointers to B_k [rank, h_out] */
+  void* Y;                    /* [n_rows, h_out], read-modify-write */
+} sgmv_projection_t;
+
+#define SGMV_MAX_PROJECTIONS 4
+
+/* Batched apply: Y_p[i, :] += (X[i, :] @ A_{p,k}) @ B_{p,k} for every
+ * projection p < num_projections and every covered row i.  The multi-LoRA
+ * paragraph of the Punica README applies a LoRA per row to a layer's input;
+ * the projections of one layer that read the same input (for instance the
+ * query, key and value projections of an attention layer, each with its own
+ * LoRA pair per model) share X, the shapes and the segments, and run here as
+ * one call (one launch per stage instead of one per projection).
+ *   projections  HOST array of num_projections (1..SGMV_MAX_PROJECTIONS)
+ *                descriptors; the Y buffers must not alias X or each other.
+ *   ws           device workspace of at least
+ *                (num_projections - 1) * round_up(W, 256) + W bytes, where W is
+ *                sgmv_workspace_bytes(problem): projection p uses the slice at
+ *                p * round_up(W, 256), whose counter area must be zero (zero
+ *                the whole workspace once).
+ * Same preconditions, precision and error conventions as sgmv_lora_apply,
+ * which is this call with one projection. */
+sgmv_status_t sgmv_lora_apply_batched(const sgmv_problem_t* problem, const void* X,
+                                      const sgmv_projection_t* projections, int32_t num_projections,
+                                      const int32_t* seg_indptr, const int32_t* lora_idx, void* ws,
+                                      size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

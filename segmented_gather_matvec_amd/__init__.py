@@ -28,10 +28,11 @@ SGMV_F16, SGMV_BF16 = 0, 1
 SGMV_VARIANT_AUTO, SGMV_VARIANT_VECTOR, SGMV_VARIANT_FUSED, SGMV_VARIANT_MFMA = range(4)
 SGMV_ROUTE_NONE, SGMV_ROUTE_DECODE, SGMV_ROUTE_MFMA, SGMV_ROUTE_VECTOR = range(4)
 SGMV_WS_COUNTER_BYTES = 1 << 20
+SGMV_MAX_PROJECTIONS = 4
 
 ENTRY_POINTS = ("sgmv_status_str", "sgmv_build_segments", "sgmv_check_problem",
                 "sgmv_check_segments", "sgmv_workspace_bytes", "sgmv_query_plan", "sgmv_shrink",
-                "sgmv_expand", "sgmv_lora_apply")
+                "sgmv_expand", "sgmv_lora_apply", "sgmv_lora_apply_batched")
 
 
 class SgmvError(RuntimeError):
@@ -56,6 +57,10 @@ class sgmv_plan_info_t(ctypes.Structure):
 
     def as_dict(self):
         return {n: int(getattr(self, n)) for n, _ in self._fields_}
+
+
+class sgmv_projection_t(ctypes.Structure):
+    _fields_ = [("A_ptrs", ctypes.c_void_p), ("B_ptrs", ctypes.c_void_p), ("Y", ctypes.c_void_p)]
 
 
 _lib = None
@@ -90,6 +95,7 @@ def load_library(path: str = LIB_PATH):
     lib.sgmv_shrink.argtypes = [prob, P, P, P, P, P, P, SZ, P]
     lib.sgmv_expand.argtypes = [prob, P, P, P, P, P, P]
     lib.sgmv_lora_apply.argtypes = [prob, P, P, P, P, P, P, P, SZ, P]
+    lib.sgmv_lora_apply_batched.argtypes = [prob, P, ctypes.POINTER(sgmv_projection_t), I32, P, P, P, SZ, P]
     for name in ENTRY_POINTS[1:]:
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -234,7 +240,34 @@ def sgmv_lora_apply(problem, X, A_ptrs, B_ptrs, Y, seg_indptr, lora_idx, ws, str
     _check(st, "sgmv_lora_apply")
 
 
+def sgmv_lora_apply_batched(problem, X, projections, seg_indptr, lora_idx, ws, stream=None):
+    """Y_p[i] += (X[i] @ A_{p,k}) @ B_{p,k} for each (A_ptrs, B_ptrs, Y) in `projections`
+    (up to SGMV_MAX_PROJECTIONS), one call; asynchronous.  `ws` must hold
+    batched_workspace_bytes(problem, len(projections)) bytes."""
+    import torch
+    dt = _torch_dtype(problem)
+    _need(X, "X", dt)
+    _need(seg_indptr, "seg_indptr", torch.int32); _need(lora_idx, "lora_idx", torch.int32)
+    _need(ws, "ws")
+    arr = (sgmv_projection_t * max(1, len(projections)))()
+    for i, (A_ptrs, B_ptrs, Y) in enumerate(projections):
+        _need(Y, f"Y[{i}]", dt)
+        _need(A_ptrs, f"A_ptrs[{i}]", torch.int64); _need(B_ptrs, f"B_ptrs[{i}]", torch.int64)
+        arr[i] = sgmv_projection_t(_ptr(A_ptrs), _ptr(B_ptrs), _ptr(Y))
+    st = load_library().sgmv_lora_apply_batched(ctypes.byref(problem), _ptr(X), arr, len(projections),
+                                                _ptr(seg_indptr), _ptr(lora_idx), _ptr(ws),
+                                                ws.numel() * ws.element_size() if ws is not None else 0,
+                                                _stream(stream))
+    _check(st, "sgmv_lora_apply_batched")
+
+
 # ----------------------------------------------------------------- helpers
+
+def batched_workspace_bytes(problem: sgmv_problem_t, num_projections: int) -> int:
+    """Workspace bytes of sgmv_lora_apply_batched: one 256-byte aligned slice per projection."""
+    w = sgmv_workspace_bytes(problem)
+    return (num_projections - 1) * ((w + 255) // 256 * 256) + w
+
 
 def pointer_table(stacked) -> "torch.Tensor":
     """Device int64 table of per-LoRA pointers into a stacked [P, ...] tensor."""

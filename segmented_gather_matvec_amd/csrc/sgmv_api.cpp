@@ -335,6 +335,85 @@ size_t apply_ws_bytes(const sgmv_problem_t& p) {
   return std::max({two_launch, one_launch, matrix});
 }
 
+// sgmv_lora_apply for num_proj projections that share X, the shapes and the
+// segments.  Projection i uses the workspace slice [i*stride, i*stride + need).
+sgmv_status_t apply(const sgmv_problem_t& p, const void* X, const sgmv_projection_t* pj, int np,
+                    const int32_t* seg_indptr, const int32_t* lora_idx, char* ws, size_t stride,
+                    hipStream_t s) {
+  const DecodePlan d = plan_decode(p);
+  const sgmv_route_t route = apply_route(p, d);
+  if (route == SGMV_ROUTE_DECODE) {
+    // The workgroups of one projection wait for each other; all projections
+    // run in one launch when all of them fit on the device at once.
+    if (np > 1 && d.grid * np > decode_capacity(p.dtype, p.rank, d.rb)) {
+      for (int i = 0; i < np; ++i) {
+        const sgmv_status_t st = apply(p, X, pj + i, 1, seg_indptr, lora_idx, ws + (size_t)i * stride, stride, s);
+        if (st != SGMV_OK) return st;
+      }
+      return SGMV_OK;
+    }
+    sgmv::DecodeParams q{};
+    q.X = static_cast<const uint16_t*>(X);
+    for (int i = 0; i < np; ++i) {
+      q.proj[i].A_ptrs = reinterpret_cast<const uint64_t*>(pj[i].A_ptrs);
+      q.proj[i].B_ptrs = reinterpret_cast<const uint64_t*>(pj[i].B_ptrs);
+      q.proj[i].Y = static_cast<uint16_t*>(pj[i].Y);
+    }
+    q.seg_indptr = seg_indptr;
+    q.lora_idx = lora_idx;
+    q.slots = reinterpret_cast<uint64_t*>(ws + SGMV_WS_COUNTER_BYTES);
+    q.slot_stride = (int64_t)(stride / sizeof(uint64_t));
+    q.n_rows = p.n_rows;
+    q.h_in = p.h_in;
+    q.h_out = p.h_out;
+    q.num_segs = p.num_segs;
+    q.num_loras = p.num_loras;
+    q.num_units = (int32_t)d.num_units;
+    q.splits = d.splits;
+    q.kc = d.kc;
+    q.cw = d.cw;
+    q.direct_units = d.direct;
+    q.split_major = d.split_major;
+    return hip_status(sgmv::launch_decode(p.dtype, p.rank, d.rb, q, np, s));
+  }
+  if (route == SGMV_ROUTE_MFMA) {
+    // Matrix-core route: the shrink writes one fp32 partial plane of V per H1
+    // chunk, the reduce sums them (in chunk order) into V, the expand reads V.
+    const MfmaPlan m = plan_mfma(p);
+    sgmv::MfmaParams q = mfma_params(p, m, seg_indptr, lora_idx);
+    q.X = static_cast<const uint16_t*>(X);
+    for (int i = 0; i < np; ++i) {
+      q.proj[i].A_ptrs = reinterpret_cast<const uint64_t*>(pj[i].A_ptrs);
+      q.proj[i].B_ptrs = reinterpret_cast<const uint64_t*>(pj[i].B_ptrs);
+      q.proj[i].Y = static_cast<uint16_t*>(pj[i].Y);
+    }
+    q.partials = reinterpret_cast<float*>(ws + SGMV_WS_COUNTER_BYTES);
+    q.V = reinterpret_cast<float*>(ws + SGMV_WS_COUNTER_BYTES + m.partial_bytes);
+    q.proj_stride = (int64_t)(stride / sizeof(float));
+    hipError_t e = sgmv::launch_mfma_shrink(p.dtype, p.rank, q, np, s);
+    if (e != hipSuccess) return SGMV_ERR_HIP;
+    return hip_status(sgmv::launch_mfma_expand(p.dtype, p.rank, q, np, s));
+  }
+  // Two launches per projection: shrink into V (held after the shrink's split
+  // partials), then expand.
+  const VecPlan v = plan_vec(p, kTargetWorkgroups);
+  const size_t need = vec_ws_bytes(v, p.rank);
+  for (int i = 0; i < np; ++i) {
+    char* wsi = ws + (size_t)i * stride;
+    VecParams q = base_params(p, v, seg_indptr, lora_idx, wsi);
+    q.X = static_cast<const uint16_t*>(X);
+    q.A_ptrs = reinterpret_cast<const uint64_t*>(pj[i].A_ptrs);
+    q.B_ptrs = reinterpret_cast<const uint64_t*>(pj[i].B_ptrs);
+    q.Y = static_cast<uint16_t*>(pj[i].Y);
+    q.V = reinterpret_cast<float*>(wsi + need);
+    hipError_t e = sgmv::launch_vec(p.dtype, p.rank, v.rb, sgmv::kModeShrink, q, s);
+    if (e != hipSuccess) return SGMV_ERR_HIP;
+    e = sgmv::launch_vec(p.dtype, p.rank, v.rb, sgmv::kModeExpand, q, s);
+    if (e != hipSuccess) return SGMV_ERR_HIP;
+  }
+  return SGMV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -447,10 +526,10 @@ sgmv_status_t sgmv_shrink(const sgmv_problem_t* p, const void* X, const void* co
     if (!aligned16(ws)) return SGMV_ERR_UNSUPPORTED;
     sgmv::MfmaParams q = mfma_params(*p, m, seg_indptr, lora_idx);
     q.X = static_cast<const uint16_t*>(X);
-    q.A_ptrs = reinterpret_cast<const uint64_t*>(A_ptrs);
+    q.proj[0].A_ptrs = reinterpret_cast<const uint64_t*>(A_ptrs);
     q.partials = reinterpret_cast<float*>(static_cast<char*>(ws) + SGMV_WS_COUNTER_BYTES);
     q.V = V;
-    return hip_status(sgmv::launch_mfma_shrink(p->dtype, p->rank, q, static_cast<hipStream_t>(stream)));
+    return hip_status(sgmv::launch_mfma_shrink(p->dtype, p->rank, q, 1, static_cast<hipStream_t>(stream)));
   }
   const VecPlan v = plan_vec(*p, kTargetWorkgroups);
   if (!ws || ws_bytes < vec_ws_bytes(v, p->rank)) return SGMV_ERR_WORKSPACE;
@@ -474,9 +553,9 @@ sgmv_status_t sgmv_expand(const sgmv_problem_t* p, const float* V, const void* c
   if (stage_uses_mfma(*p)) {
     sgmv::MfmaParams q = mfma_params(*p, plan_mfma(*p), seg_indptr, lora_idx);
     q.V = const_cast<float*>(V);
-    q.B_ptrs = reinterpret_cast<const uint64_t*>(B_ptrs);
-    q.Y = static_cast<uint16_t*>(Y);
-    return hip_status(sgmv::launch_mfma_expand(p->dtype, p->rank, q, static_cast<hipStream_t>(stream)));
+    q.proj[0].B_ptrs = reinterpret_cast<const uint64_t*>(B_ptrs);
+    q.proj[0].Y = static_cast<uint16_t*>(Y);
+    return hip_status(sgmv::launch_mfma_expand(p->dtype, p->rank, q, 1, static_cast<hipStream_t>(stream)));
   }
   const VecPlan v = plan_vec(*p, kTargetWorkgroups);
   VecParams q = base_params(*p, v, seg_indptr, lora_idx, nullptr);
@@ -530,69 +609,32 @@ sgmv_status_t sgmv_query_plan(const sgmv_problem_t* p, sgmv_plan_info_t* info) {
 sgmv_status_t sgmv_lora_apply(const sgmv_problem_t* p, const void* X, const void* const* A_ptrs,
                               const void* const* B_ptrs, void* Y, const int32_t* seg_indptr,
                               const int32_t* lora_idx, void* ws, size_t ws_bytes, void* stream) {
+  const sgmv_projection_t one{A_ptrs, B_ptrs, Y};
+  return sgmv_lora_apply_batched(p, X, &one, 1, seg_indptr, lora_idx, ws, ws_bytes, stream);
+}
+
+sgmv_status_t sgmv_lora_apply_batched(const sgmv_problem_t* p, const void* X,
+                                      const sgmv_projection_t* projections, int32_t num_projections,
+                                      const int32_t* seg_indptr, const int32_t* lora_idx, void* ws,
+                                      size_t ws_bytes, void* stream) {
   sgmv_status_t st = sgmv_check_problem(p);
   if (st != SGMV_OK) return st;
+  if (!projections || num_projections < 1 || num_projections > SGMV_MAX_PROJECTIONS) return SGMV_ERR_INVALID_ARG;
   if (nothing_to_do(*p)) return SGMV_OK;
-  if (!X || !A_ptrs || !B_ptrs || !Y || !seg_indptr || !lora_idx) return SGMV_ERR_INVALID_ARG;
-  if (!aligned16(X) || !aligned16(Y) || !aligned8(A_ptrs) || !aligned8(B_ptrs))
-    return SGMV_ERR_UNSUPPORTED;
+  if (!X || !seg_indptr || !lora_idx) return SGMV_ERR_INVALID_ARG;
+  if (!aligned16(X)) return SGMV_ERR_UNSUPPORTED;
+  for (int32_t i = 0; i < num_projections; ++i) {
+    const sgmv_projection_t& pj = projections[i];
+    if (!pj.A_ptrs || !pj.B_ptrs || !pj.Y) return SGMV_ERR_INVALID_ARG;
+    if (!aligned16(pj.Y) || !aligned8(pj.A_ptrs) || !aligned8(pj.B_ptrs)) return SGMV_ERR_UNSUPPORTED;
+  }
   if (!ws) return SGMV_ERR_WORKSPACE;
   if (!aligned16(ws)) return SGMV_ERR_UNSUPPORTED;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const DecodePlan d = plan_decode(*p);
-  const sgmv_route_t route = apply_route(*p, d);
-  if (route == SGMV_ROUTE_DECODE) {
-    if (ws_bytes < SGMV_WS_COUNTER_BYTES + d.slot_bytes) return SGMV_ERR_WORKSPACE;
-    sgmv::DecodeParams q{};
-    q.X = static_cast<const uint16_t*>(X);
-    q.A_ptrs = reinterpret_cast<const uint64_t*>(A_ptrs);
-    q.B_ptrs = reinterpret_cast<const uint64_t*>(B_ptrs);
-    q.Y = static_cast<uint16_t*>(Y);
-    q.seg_indptr = seg_indptr;
-    q.lora_idx = lora_idx;
-    q.slots = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + SGMV_WS_COUNTER_BYTES);
-    q.n_rows = p->n_rows;
-    q.h_in = p->h_in;
-    q.h_out = p->h_out;
-    q.num_segs = p->num_segs;
-    q.num_loras = p->num_loras;
-    q.num_units = (int32_t)d.num_units;
-    q.splits = d.splits;
-    q.kc = d.kc;
-    q.cw = d.cw;
-    q.direct_units = d.direct;
-    q.split_major = d.split_major;
-    return hip_status(sgmv::launch_decode(p->dtype, p->rank, d.rb, q, s));
-  }
-  if (route == SGMV_ROUTE_MFMA) {
-    // Matrix-core route: the shrink writes one fp32 partial plane of V per H1
-    // chunk, the reduce sums them (in chunk order) into V, the expand reads V.
-    const MfmaPlan m = plan_mfma(*p);
-    if (ws_bytes < SGMV_WS_COUNTER_BYTES + m.partial_bytes + v_area_bytes(*p)) return SGMV_ERR_WORKSPACE;
-    sgmv::MfmaParams q = mfma_params(*p, m, seg_indptr, lora_idx);
-    q.X = static_cast<const uint16_t*>(X);
-    q.A_ptrs = reinterpret_cast<const uint64_t*>(A_ptrs);
-    q.B_ptrs = reinterpret_cast<const uint64_t*>(B_ptrs);
-    q.Y = static_cast<uint16_t*>(Y);
-    q.partials = reinterpret_cast<float*>(static_cast<char*>(ws) + SGMV_WS_COUNTER_BYTES);
-    q.V = reinterpret_cast<float*>(static_cast<char*>(ws) + SGMV_WS_COUNTER_BYTES + m.partial_bytes);
-    hipError_t e = sgmv::launch_mfma_shrink(p->dtype, p->rank, q, s);
-    if (e != hipSuccess) return SGMV_ERR_HIP;
-    return hip_status(sgmv::launch_mfma_expand(p->dtype, p->rank, q, s));
-  }
-  // Two launches: shrink into V (held after the shrink's split partials), then expand.
-  const VecPlan v = plan_vec(*p, kTargetWorkgroups);
-  const size_t need = vec_ws_bytes(v, p->rank);
-  if (ws_bytes < need + v_area_bytes(*p)) return SGMV_ERR_WORKSPACE;
-  VecParams q = base_params(*p, v, seg_indptr, lora_idx, ws);
-  q.X = static_cast<const uint16_t*>(X);
-  q.A_ptrs = reinterpret_cast<const uint64_t*>(A_ptrs);
-  q.B_ptrs = reinterpret_cast<const uint64_t*>(B_ptrs);
-  q.Y = static_cast<uint16_t*>(Y);
-  q.V = reinterpret_cast<float*>(static_cast<char*>(ws) + need);
-  hipError_t e = sgmv::launch_vec(p->dtype, p->rank, v.rb, sgmv::kModeShrink, q, s);
-  if (e != hipSuccess) return SGMV_ERR_HIP;
-  return hip_status(sgmv::launch_vec(p->dtype, p->rank, v.rb, sgmv::kModeExpand, q, s));
+  const size_t need = apply_ws_bytes(*p);
+  const size_t stride = (size_t)round_up((int64_t)need, 256);
+  if (ws_bytes < stride * (size_t)(num_projections - 1) + need) return SGMV_ERR_WORKSPACE;
+  return apply(*p, X, projections, num_projections, seg_indptr, lora_idx, static_cast<char*>(ws), stride,
+               static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

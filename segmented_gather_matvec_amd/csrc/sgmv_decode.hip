@@ -110,6 +110,7 @@ __global__ __launch_bounds__(kThreads) void sgmv_decode_kernel(DecodeParams p) {
   const int lane = t & 63;
   const int wave = t >> 6;
   const int G = p.splits;
+  const Projection pr = p.proj[blockIdx.y];
   // Workgroups go round-robin over the XCDs.
   int unit, g;
   if (p.split_major) {
@@ -127,8 +128,8 @@ __global__ __launch_bounds__(kThreads) void sgmv_decode_kernel(DecodeParams p) {
   // selects its pointers from registers, saving one dependent memory trip.
   uint64_t a_lane = 0, b_lane = 0;
   if (SMALL && lane < p.num_loras) {
-    a_lane = p.A_ptrs[lane];
-    b_lane = p.B_ptrs[lane];
+    a_lane = pr.A_ptrs[lane];
+    b_lane = pr.B_ptrs[lane];
   }
   const Unit un = resolve_unit<RB>(p.seg_indptr, p.lora_idx, p.num_segs, p.num_loras, p.n_rows,
                                    p.direct_units, unit);
@@ -143,15 +144,15 @@ __global__ __launch_bounds__(kThreads) void sgmv_decode_kernel(DecodeParams p) {
     Ak = reinterpret_cast<const uint16_t*>(readlane_u64(a_lane, un.k));
     Bk = reinterpret_cast<const uint16_t*>(readlane_u64(b_lane, un.k));
   } else {
-    Ak = reinterpret_cast<const uint16_t*>(p.A_ptrs[un.k]);
-    Bk = reinterpret_cast<const uint16_t*>(p.B_ptrs[un.k]);
+    Ak = reinterpret_cast<const uint16_t*>(pr.A_ptrs[un.k]);
+    Bk = reinterpret_cast<const uint16_t*>(pr.B_ptrs[un.k]);
   }
   const int h0 = g * p.kc;
   const int h1 = p.h_in < h0 + p.kc ? p.h_in : h0 + p.kc;
   const int c0 = g * p.cw;
   const int c1 = p.h_out < c0 + p.cw ? p.h_out : c0 + p.cw;
   const uint16_t* Xr = p.X + (int64_t)r0 * p.h_in;
-  uint16_t* Yr = p.Y + (int64_t)r0 * p.h_out;
+  uint16_t* Yr = pr.Y + (int64_t)r0 * p.h_out;
 
   // ---------------- all loads, issued up front ----------------
   // Shrink: thread t owns ranks (t % JG)*8..+7 of rows h0 + t/JG + q*HS.
@@ -252,7 +253,7 @@ __global__ __launch_bounds__(kThreads) void sgmv_decode_kernel(DecodeParams p) {
 
   // ---------------- publish ----------------
   // Per-unit slot layout: [G][PW][RB*R] tagged words.
-  uint64_t* unit_slots = p.slots + (int64_t)unit * G * PW * (RB * R);
+  uint64_t* unit_slots = p.slots + (int64_t)blockIdx.y * p.slot_stride + (int64_t)unit * G * PW * (RB * R);
   // The waves' partials are summed in LDS first: one word per output leaves
   // the workgroup, which keeps the device-scope exchange small.
   {
@@ -342,15 +343,15 @@ __global__ __launch_bounds__(kThreads) void sgmv_decode_kernel(DecodeParams p) {
 }
 
 template <class T, int R, int RB>
-hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
+hipError_t launch_t(const DecodeParams& p, int num_proj, hipStream_t stream) {
   const unsigned units = p.split_major ? (unsigned)p.num_units
                                        : (unsigned)kXcds * (unsigned)((p.num_units + kXcds - 1) / kXcds);
   const unsigned grid = units * (unsigned)p.splits;
-  if (grid == 0) return hipSuccess;
+  if (grid == 0 || num_proj <= 0) return hipSuccess;
   if (p.num_loras <= 64)
-    hipLaunchKernelGGL((sgmv_decode_kernel<T, R, RB, true>), dim3(grid), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((sgmv_decode_kernel<T, R, RB, true>), dim3(grid, num_proj), dim3(kThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL((sgmv_decode_kernel<T, R, RB, false>), dim3(grid), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((sgmv_decode_kernel<T, R, RB, false>), dim3(grid, num_proj), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -373,14 +374,14 @@ int capacity_t() {
 
 // Instantiated (rank, rows per unit) pairs: rank * RB <= 256.
 template <class T>
-hipError_t dispatch(int rank, int rb, const DecodeParams& p, hipStream_t s, int* cap) {
+hipError_t dispatch(int rank, int rb, const DecodeParams& p, int num_proj, hipStream_t s, int* cap) {
 #define SGMV_DECODE_CASE(R_, RB_)                          \
   if (rank == R_ && rb == RB_) {                           \
     if (cap) {                                             \
       *cap = capacity_t<T, R_, RB_>();                     \
       return hipSuccess;                                   \
     }                                                      \
-    return launch_t<T, R_, RB_>(p, s);                     \
+    return launch_t<T, R_, RB_>(p, num_proj, s);           \
   }
   SGMV_DECODE_CASE(8, 1) SGMV_DECODE_CASE(8, 4) SGMV_DECODE_CASE(8, 16)
   SGMV_DECODE_CASE(16, 1) SGMV_DECODE_CASE(16, 4) SGMV_DECODE_CASE(16, 16)
@@ -394,17 +395,17 @@ hipError_t dispatch(int rank, int rb, const DecodeParams& p, hipStream_t s, int*
 
 bool decode_supported(int rank, int rb) { return rank * rb <= kThreads && (rb == 1 || rb == 4 || rb == 16); }
 
-hipError_t launch_decode(int dtype, int rank, int rb, const DecodeParams& p, hipStream_t stream) {
-  return dtype == 1 ? dispatch<BF16>(rank, rb, p, stream, nullptr)
-                    : dispatch<F16>(rank, rb, p, stream, nullptr);
+hipError_t launch_decode(int dtype, int rank, int rb, const DecodeParams& p, int num_proj, hipStream_t stream) {
+  return dtype == 1 ? dispatch<BF16>(rank, rb, p, num_proj, stream, nullptr)
+                    : dispatch<F16>(rank, rb, p, num_proj, stream, nullptr);
 }
 
 int decode_resident_capacity(int dtype, int rank, int rb) {
   int cap = 0;
   if (dtype == 1)
-    (void)dispatch<BF16>(rank, rb, DecodeParams{}, nullptr, &cap);
+    (void)dispatch<BF16>(rank, rb, DecodeParams{}, 0, nullptr, &cap);
   else
-    (void)dispatch<F16>(rank, rb, DecodeParams{}, nullptr, &cap);
+    (void)dispatch<F16>(rank, rb, DecodeParams{}, 0, nullptr, &cap);
   return cap;
 }
 

@@ -107,7 +107,7 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_shrink_kernel(MfmaParams p
                                     p.direct_units64, unit);
   if (un.L <= 0) return;
   const int L = un.L, r0 = un.r0;
-  const uint16_t* Ak = reinterpret_cast<const uint16_t*>(p.A_ptrs[un.k]);
+  const uint16_t* Ak = reinterpret_cast<const uint16_t*>(p.proj[blockIdx.y].A_ptrs[un.k]);
   const int k0 = g * p.kc;
   const int k1 = p.h_in < k0 + p.kc ? p.h_in : k0 + p.kc;
   // Row this lane feeds into the MFMA A operand (rows past the segment re-read
@@ -175,7 +175,7 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_shrink_kernel(MfmaParams p
   }
 
   // D[4q+i][ml] of rank tile n: row wave*16 + 4q + i, rank n*16 + ml.
-  float* dst = p.partials + (int64_t)g * p.partial_stride;
+  float* dst = p.partials + (int64_t)blockIdx.y * p.proj_stride + (int64_t)g * p.partial_stride;
 #pragma unroll
   for (int n = 0; n < NT; ++n)
 #pragma unroll
@@ -200,6 +200,8 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_reduce_kernel(MfmaParams p
   constexpr int kBatch = 16;
   const int unit = blockIdx.x / PER_ROWS;
   const int part = blockIdx.x - unit * PER_ROWS;
+  const float* partials = p.partials + (int64_t)blockIdx.y * p.proj_stride;
+  float* V = p.V + (int64_t)blockIdx.y * p.proj_stride;
   const Unit un = resolve_unit<kMT>(p.seg_indptr, p.lora_idx, p.num_segs, p.num_loras, p.n_rows,
                                     p.direct_units64, unit);
   const int rows = un.L - part * kReduceRows;
@@ -215,13 +217,13 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_reduce_kernel(MfmaParams p
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
         const int k = k0 + u < p.ksplit ? k0 + u : p.ksplit - 1;
-        v[u] = *reinterpret_cast<const f32x4*>(p.partials + (int64_t)k * p.partial_stride + off);
+        v[u] = *reinterpret_cast<const f32x4*>(partials + (int64_t)k * p.partial_stride + off);
       }
 #pragma unroll
       for (int u = 0; u < kBatch; ++u)
         if (k0 + u < p.ksplit) s += v[u];
     }
-    *reinterpret_cast<f32x4*>(p.V + off) = s;
+    *reinterpret_cast<f32x4*>(V + off) = s;
   }
 }
 
@@ -260,8 +262,9 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_expand_kernel(MfmaParams p
   const int L = un.L, r0 = un.r0;
   const int ch0 = grp * p.chunks_per_wg;
   const int ch1 = nchunks < ch0 + p.chunks_per_wg ? nchunks : ch0 + p.chunks_per_wg;
-  const uint16_t* Bk = reinterpret_cast<const uint16_t*>(p.B_ptrs[un.k]);
-  uint16_t* Yr = p.Y + (int64_t)r0 * p.h_out;
+  const uint16_t* Bk = reinterpret_cast<const uint16_t*>(p.proj[blockIdx.y].B_ptrs[un.k]);
+  uint16_t* Yr = p.proj[blockIdx.y].Y + (int64_t)r0 * p.h_out;
+  const float* Vp = p.V + (int64_t)blockIdx.y * p.proj_stride;
 
   // Loads of one chunk (all lanes issue the same loads; addresses of lanes
   // without work are clamped to a valid element).
@@ -295,7 +298,7 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_expand_kernel(MfmaParams p
   for (int m = 0; m < NV4; ++m) {
     const int o = (t + kThreads * m) * 4;
     const int rr = o / R;
-    vv[m] = *reinterpret_cast<const f32x4*>(p.V + (int64_t)(r0 + (rr < L ? rr : 0)) * R + o % R);
+    vv[m] = *reinterpret_cast<const f32x4*>(Vp + (int64_t)(r0 + (rr < L ? rr : 0)) * R + o % R);
   }
 #pragma unroll
   for (int m = 0; m < NV4; ++m) {
@@ -373,34 +376,34 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_expand_kernel(MfmaParams p
 unsigned xcd_grid(unsigned items) { return kXcds * ((items + kXcds - 1) / kXcds); }
 
 template <class T, int R>
-hipError_t launch_t(int stage, const MfmaParams& p, hipStream_t s) {
+hipError_t launch_t(int stage, const MfmaParams& p, int np, hipStream_t s) {
   unsigned grid = 0;
   if (stage == 0) {
     grid = xcd_grid((unsigned)p.num_units64 * (unsigned)p.ksplit);
-    if (grid) hipLaunchKernelGGL((sgmv_mfma_shrink_kernel<T, R>), dim3(grid), dim3(kThreads), 0, s, p);
+    if (grid && np > 0) hipLaunchKernelGGL((sgmv_mfma_shrink_kernel<T, R>), dim3(grid, np), dim3(kThreads), 0, s, p);
   } else if (stage == 1) {
     grid = (unsigned)p.num_units64 * (unsigned)(kMT / kReduceRows);
-    if (grid) hipLaunchKernelGGL((sgmv_mfma_reduce_kernel<R>), dim3(grid), dim3(kThreads), 0, s, p);
+    if (grid && np > 0) hipLaunchKernelGGL((sgmv_mfma_reduce_kernel<R>), dim3(grid, np), dim3(kThreads), 0, s, p);
   } else {
     const int nchunks = (p.h_out + kCW - 1) / kCW;
     grid = xcd_grid((unsigned)p.num_units64 * (unsigned)((nchunks + p.chunks_per_wg - 1) / p.chunks_per_wg));
-    if (grid) hipLaunchKernelGGL((sgmv_mfma_expand_kernel<T, R>), dim3(grid), dim3(kThreads), 0, s, p);
+    if (grid && np > 0) hipLaunchKernelGGL((sgmv_mfma_expand_kernel<T, R>), dim3(grid, np), dim3(kThreads), 0, s, p);
   }
-  return grid ? hipGetLastError() : hipSuccess;
+  return grid && np > 0 ? hipGetLastError() : hipSuccess;
 }
 
 template <class T>
-hipError_t launch_rank(int rank, int stage, const MfmaParams& p, hipStream_t s) {
+hipError_t launch_rank(int rank, int stage, const MfmaParams& p, int np, hipStream_t s) {
   switch (rank) {
-    case 16: return launch_t<T, 16>(stage, p, s);
-    case 32: return launch_t<T, 32>(stage, p, s);
-    case 64: return launch_t<T, 64>(stage, p, s);
+    case 16: return launch_t<T, 16>(stage, p, np, s);
+    case 32: return launch_t<T, 32>(stage, p, np, s);
+    case 64: return launch_t<T, 64>(stage, p, np, s);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_stage(int dtype, int rank, int stage, const MfmaParams& p, hipStream_t s) {
-  return dtype == 1 ? launch_rank<BF16>(rank, stage, p, s) : launch_rank<F16>(rank, stage, p, s);
+hipError_t launch_stage(int dtype, int rank, int stage, const MfmaParams& p, int np, hipStream_t s) {
+  return dtype == 1 ? launch_rank<BF16>(rank, stage, p, np, s) : launch_rank<F16>(rank, stage, p, np, s);
 }
 
 }  // namespace
@@ -427,14 +430,14 @@ int mfma_expand_capacity(int dtype, int rank) {
   return 0;
 }
 
-hipError_t launch_mfma_shrink(int dtype, int rank, const MfmaParams& p, hipStream_t stream) {
-  hipError_t e = launch_stage(dtype, rank, 0, p, stream);
+hipError_t launch_mfma_shrink(int dtype, int rank, const MfmaParams& p, int num_proj, hipStream_t stream) {
+  hipError_t e = launch_stage(dtype, rank, 0, p, num_proj, stream);
   if (e != hipSuccess) return e;
-  return launch_stage(dtype, rank, 1, p, stream);
+  return launch_stage(dtype, rank, 1, p, num_proj, stream);
 }
 
-hipError_t launch_mfma_expand(int dtype, int rank, const MfmaParams& p, hipStream_t stream) {
-  return launch_stage(dtype, rank, 2, p, stream);
+hipError_t launch_mfma_expand(int dtype, int rank, const MfmaParams& p, int num_proj, hipStream_t stream) {
+  return launch_stage(dtype, rank, 2, p, num_proj, stream);
 }
 
 }  // namespace sgmv

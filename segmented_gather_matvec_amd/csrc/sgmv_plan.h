@@ -47,14 +47,22 @@ constexpr int kDecodeLanesPerColumn = 4;  // lanes sharing one 8-column vector o
 constexpr int decode_max_kc(int rank) { return kDecodeRowsPerThread * 256 / (rank / 8); }
 constexpr int decode_max_cw() { return 256 / kDecodeLanesPerColumn * 8; }
 
-struct DecodeParams {
-  const uint16_t* X;
+// One projection of a batched call (its own LoRA tables and output); the
+// projection of a workgroup is blockIdx.y.
+constexpr int kMaxProjections = 4;
+struct Projection {
   const uint64_t* A_ptrs;
   const uint64_t* B_ptrs;
   uint16_t* Y;
+};
+
+struct DecodeParams {
+  const uint16_t* X;
+  Projection proj[kMaxProjections];
   const int32_t* seg_indptr;
   const int32_t* lora_idx;
-  uint64_t* slots;  // [num_units][splits][parts][RB*rank] tagged partials
+  uint64_t* slots;      // projection 0: [num_units][splits][parts][RB*rank] tagged partials
+  int64_t slot_stride;  // words between the slot areas of consecutive projections
   int32_t n_rows, h_in, h_out, num_segs, num_loras;
   int32_t num_units, splits, kc, cw, direct_units;
   // 1: workgroup b runs split b % splits of unit b / splits, so the splits of a
@@ -65,7 +73,8 @@ struct DecodeParams {
 };
 
 bool decode_supported(int rank, int rb);
-hipError_t launch_decode(int dtype, int rank, int rb, const DecodeParams& p, hipStream_t stream);
+// Launches num_proj projections (blockIdx.y).
+hipError_t launch_decode(int dtype, int rank, int rb, const DecodeParams& p, int num_proj, hipStream_t stream);
 // Workgroups of the decode kernel that fit on the device at once (0 if unknown).
 int decode_resident_capacity(int dtype, int rank, int rb);
 
@@ -77,14 +86,13 @@ constexpr int kMfmaKChunk = 256;          // H1 granule of the shrink's split
 
 struct MfmaParams {
   const uint16_t* X;
-  const uint64_t* A_ptrs;
-  const uint64_t* B_ptrs;
-  uint16_t* Y;
-  float* V;                // reduce: output; expand: input (fp32 [n_rows, rank])
-  float* partials;         // shrink: H1-chunk s writes partials + s*partial_stride
+  Projection proj[kMaxProjections];
+  float* V;                // projection 0; reduce: output; expand: input (fp32 [n_rows, rank])
+  float* partials;         // projection 0; shrink: H1-chunk s writes partials + s*partial_stride
   const int32_t* seg_indptr;
   const int32_t* lora_idx;
   int64_t partial_stride;  // floats between partial planes (n_rows * rank)
+  int64_t proj_stride;     // floats between the V / partial areas of consecutive projections
   int32_t n_rows, h_in, h_out, num_segs, num_loras;
   int32_t num_units64, direct_units64;  // units of <= 64 rows of one segment
   int32_t ksplit, kc, chunks_per_wg;
@@ -94,7 +102,7 @@ bool mfma_supported(int rank);
 // Expand workgroups that fit on the device at once (0 if unknown).
 int mfma_expand_capacity(int dtype, int rank);
 // Shrink into the partial planes, then reduce them into V (two launches).
-hipError_t launch_mfma_shrink(int dtype, int rank, const MfmaParams& p, hipStream_t stream);
-hipError_t launch_mfma_expand(int dtype, int rank, const MfmaParams& p, hipStream_t stream);
+hipError_t launch_mfma_shrink(int dtype, int rank, const MfmaParams& p, int num_proj, hipStream_t stream);
+hipError_t launch_mfma_expand(int dtype, int rank, const MfmaParams& p, int num_proj, hipStream_t stream);
 
 }  // namespace sgmv

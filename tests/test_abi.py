@@ -80,6 +80,41 @@ def test_query_plan_routes(kw, routes):
     assert sg.load_library().sgmv_query_plan(ctypes.byref(good()), None) == sg.SGMV_ERR_INVALID_ARG
 
 
+def test_projection_struct_layout_matches_header():
+    src = open(HEADER).read()
+    body = re.search(r"typedef struct sgmv_projection \{(.*?)\} sgmv_projection_t;", src, re.S).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    fields = re.findall(r"(\w+);", body)
+    assert fields == [n for n, _ in sg.sgmv_projection_t._fields_]
+    assert ctypes.sizeof(sg.sgmv_projection_t) == 8 * len(fields)
+    assert re.search(r"#define SGMV_MAX_PROJECTIONS 4\b", src) and sg.SGMV_MAX_PROJECTIONS == 4
+
+
+def test_batched_apply_fails_fast_on_bad_arguments():
+    """Host checks of sgmv_lora_apply_batched run before any HIP call."""
+    lib = sg.load_library()
+    p = good()
+    fake = ctypes.c_void_p(0x10000)
+    need = sg.sgmv_workspace_bytes(p)
+
+    def call(projs, n, ws_bytes, X=fake, problem=p):
+        arr = (sg.sgmv_projection_t * max(1, len(projs)))(*projs)
+        return lib.sgmv_lora_apply_batched(ctypes.byref(problem), X, arr if projs else None, n, fake, fake, fake,
+                                           ws_bytes, None)
+    ok = sg.sgmv_projection_t(0x10000, 0x10000, 0x10000)
+    assert call([], 0, need) == sg.SGMV_ERR_INVALID_ARG
+    assert call([ok] * 5, 5, 5 * need) == sg.SGMV_ERR_INVALID_ARG            # more than SGMV_MAX_PROJECTIONS
+    assert call([ok, sg.sgmv_projection_t(0x10000, None, 0x10000)], 2, 4 * need) == sg.SGMV_ERR_INVALID_ARG
+    assert call([ok, sg.sgmv_projection_t(0x10000, 0x10000, 0x10002)], 2, 4 * need) == sg.SGMV_ERR_UNSUPPORTED
+    assert call([ok, ok], 2, need) == sg.SGMV_ERR_WORKSPACE                    # one slice is not two
+    assert call([ok, ok], 2, sg.batched_workspace_bytes(p, 2) - 1) == sg.SGMV_ERR_WORKSPACE
+    assert call([ok], 1, need, X=None) == sg.SGMV_ERR_INVALID_ARG
+    empty = good(num_segs=0, max_seg_len=0)
+    assert call([ok, ok], 2, 0, problem=empty) == sg.SGMV_OK                  # nothing to do
+    assert sg.batched_workspace_bytes(p, 1) == need
+    assert sg.batched_workspace_bytes(p, 3) == 2 * ((need + 255) // 256 * 256) + need
+
+
 def test_status_strings():
     for st in range(5):
         assert sg.sgmv_status_str(st).startswith("SGMV_")

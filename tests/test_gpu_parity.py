@@ -110,6 +110,54 @@ def test_popularity_larger_row_blocks(kind, n, splits, rows_per_unit):
     assert call.counters_clear()
 
 
+def _batched_case(w, variant, nproj, seed):
+    """nproj projections of one workload's rows: projection 0 uses the workload's
+    weights and Y0; the others draw their own (seeded) weights and Y0."""
+    rng = np.random.default_rng(seed)
+    call = run_workload(w, variant)
+    projs = [(call.A, call.B, call.Y, call.A_ptrs, call.B_ptrs, call.Ah, call.Bh, call.Y0h)]
+    P, h_in, r = call.Ah.shape
+    h_out = call.Bh.shape[2]
+    for _ in range(nproj - 1):
+        Ah = workloads.to_bits((rng.standard_normal((P, h_in, r)) * h_in ** -0.5).astype(np.float32), w.dtype)
+        Bh = workloads.to_bits((rng.standard_normal((P, r, h_out)) * r ** -0.5).astype(np.float32), w.dtype)
+        Y0h = workloads.to_bits(rng.standard_normal(call.Y0h.shape).astype(np.float32), w.dtype)
+        A, B, Y = to_device(Ah, w.dtype), to_device(Bh, w.dtype), to_device(Y0h, w.dtype)
+        projs.append((A, B, Y, sg.pointer_table(A), sg.pointer_table(B), Ah, Bh, Y0h))
+    return call, projs
+
+
+@pytest.mark.parametrize("case", ["distinct3", "distinct_b64_4", "skewed3", "mixed2_mfma", "distinct3_vector"])
+def test_batched_projections_match_oracle_and_single_calls(case):
+    """sgmv_lora_apply_batched: every projection equals the oracle, and equals
+    (bitwise) a separate sgmv_lora_apply of that projection.  Distinct b64 with
+    4 projections does not fit on the device at once and runs the per-projection
+    fallback."""
+    import torch
+    w, variant, nproj = {
+        "distinct3": (workloads.decode_distinct(), sg.SGMV_VARIANT_AUTO, 3),
+        "distinct_b64_4": (workloads.decode_distinct(n=64), sg.SGMV_VARIANT_AUTO, 4),
+        "skewed3": (workloads.popularity("skewed", 32), sg.SGMV_VARIANT_AUTO, 3),
+        "mixed2_mfma": (workloads.mixed(64, seed=464, pairs=((512, 1376),), lo=16, hi=100)[0],
+                        sg.SGMV_VARIANT_MFMA, 2),
+        "distinct3_vector": (workloads.decode_distinct(), sg.SGMV_VARIANT_VECTOR, 3),
+    }[case]
+    call, projs = _batched_case(w, variant, nproj, seed=77)
+    ws = torch.zeros(sg.batched_workspace_bytes(call.problem, nproj), dtype=torch.uint8, device="cuda")
+    sg.sgmv_lora_apply_batched(call.problem, call.X, [(a, b, y) for (_, _, y, a, b, *_rest) in projs],
+                               call.seg_d, call.lidx_d, ws)
+    torch.cuda.synchronize()
+    got = [to_bits(pj[2]).copy() for pj in projs]
+    for i, (_, _, Y, A_ptrs, B_ptrs, Ah, Bh, Y0h) in enumerate(projs):
+        ref = oracle.sgmv_apply(w.dtype, call.Xh, Ah, Bh, call.seg, call.lidx, Y0h)
+        assert_close(got[i], ref, w.dtype, what=f"projection {i}")
+        Y.copy_(to_device(Y0h, w.dtype))
+        ws1 = sg.new_workspace(call.problem)
+        sg.sgmv_lora_apply(call.problem, call.X, A_ptrs, B_ptrs, Y, call.seg_d, call.lidx_d, ws1)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_bits(Y), got[i]), f"projection {i}: batched != single call"
+
+
 @pytest.mark.parametrize("variant", [sg.SGMV_VARIANT_AUTO, sg.SGMV_VARIANT_VECTOR, sg.SGMV_VARIANT_MFMA])
 @pytest.mark.parametrize("rank", [16, 64])
 def test_mixed_prefill_decode_reduced(rank, variant):
