@@ -129,13 +129,14 @@ MODEL_WORKLOADS = ["llama13b_r64_b256_forward"]
 class SingleCallBench:
     """One sgmv_lora_apply call per step, weights rotated through a >= 1 GiB pool."""
 
-    def __init__(self, name, variant=0, splits=0):
+    def __init__(self, name, variant=0, splits=0, row_map="none"):
         import numpy as np
         import torch
         import segmented_gather_matvec_amd as sg
         import workloads as wl
 
         self.name, self.sg, self.torch = name, sg, torch
+        self.row_map = row_map
         (self.dtype, self.h_in, self.h_out, self.rank, self.n, seg, lidx, self.lpool,
          seed) = workload_layout(name)
         seg, lidx = np.asarray(seg, np.int32), np.asarray(lidx, np.int32)
@@ -169,22 +170,59 @@ class SingleCallBench:
         self.bytes = algorithmic_bytes(e, self.rows_covered, self.h_in, self.h_out, self.rank, self.distinct)
         self.rows_per_step = self.rows_covered
         self.calls_per_step = 1
-        self.fn = sg.load_library().sgmv_lora_apply
+        # Row layout of X and Y.  "none": rows in segment order.  Otherwise rows
+        # are in request order, with request perm[j] at sorted row j (a seeded
+        # shuffle), and either the kernels gather / scatter them through the row
+        # map ("kernel") or the caller permutes around the call ("torch").
+        self.perm_h = (np.random.default_rng(seed + 7).permutation(self.n).astype(np.int32)
+                       if row_map != "none" else np.arange(self.n, dtype=np.int32))
+        self.perm = torch.from_numpy(self.perm_h).to(dev)
+        self.perm64 = self.perm.to(torch.int64)
+        lib = sg.load_library()
+        self.fn, self.fn_batched = lib.sgmv_lora_apply, lib.sgmv_lora_apply_batched
+        if row_map == "torch":
+            self.Xs = torch.empty_like(self.X[0])
+            self.Ys = torch.empty_like(self.Y[0])
         self.marshal()
         torch.cuda.synchronize()
 
     def marshal(self):
         pb = ctypes.byref(self.problem)
         wsn = self.ws.numel()
-        self.args = []
+        self.args, self.keep = [], []
         for c in range(max(self.tables, self.copies)):
             t, x = c % self.tables, c % self.copies
-            self.args.append((pb, self.X[x].data_ptr(), self.A_tab[t].data_ptr(), self.B_tab[t].data_ptr(),
-                              self.Y[x].data_ptr(), self.seg.data_ptr(), self.lidx.data_ptr(),
-                              self.ws.data_ptr(), wsn))
+            if self.row_map == "kernel":
+                pj = (self.sg.sgmv_projection_t * 1)(
+                    self.sg.sgmv_projection_t(self.A_tab[t].data_ptr(), self.B_tab[t].data_ptr(),
+                                              self.Y[x].data_ptr()))
+                self.keep.append(pj)
+                self.args.append((pb, self.X[x].data_ptr(), pj, 1, self.seg.data_ptr(), self.lidx.data_ptr(),
+                                  self.perm.data_ptr(), self.ws.data_ptr(), wsn))
+            elif self.row_map == "torch":
+                self.args.append((pb, self.Xs.data_ptr(), self.A_tab[t].data_ptr(), self.B_tab[t].data_ptr(),
+                                  self.Ys.data_ptr(), self.seg.data_ptr(), self.lidx.data_ptr(),
+                                  self.ws.data_ptr(), wsn))
+            else:
+                self.args.append((pb, self.X[x].data_ptr(), self.A_tab[t].data_ptr(), self.B_tab[t].data_ptr(),
+                                  self.Y[x].data_ptr(), self.seg.data_ptr(), self.lidx.data_ptr(),
+                                  self.ws.data_ptr(), wsn))
 
     def step(self, c, stream):
-        st = self.fn(*self.args[c % len(self.args)], stream)
+        i = c % len(self.args)
+        if self.row_map == "kernel":
+            st = self.fn_batched(*self.args[i], stream)
+        elif self.row_map == "torch":
+            # The caller's alternative to the row map: gather X and Y into
+            # segment order, apply, scatter Y back (torch ops on the same stream).
+            x = i % self.copies
+            torch = self.torch
+            torch.index_select(self.X[x], 0, self.perm64, out=self.Xs)
+            torch.index_select(self.Y[x], 0, self.perm64, out=self.Ys)
+            st = self.fn(*self.args[i], stream)
+            self.Y[x].index_copy_(0, self.perm64, self.Ys)
+        else:
+            st = self.fn(*self.args[i], stream)
         if st != 0:
             raise RuntimeError(self.sg.sgmv_status_str(st))
 
@@ -197,7 +235,7 @@ class SingleCallBench:
         sid = torch.cuda.current_stream().cuda_stream
         for c in range(calls):
             t, x = c % self.tables, c % self.copies
-            Xh, Y0 = _bits(self.X[x]), _bits(self.Y[x]).copy()
+            Xh, Y0 = _bits(self.X[x])[self.perm_h], _bits(self.Y[x])[self.perm_h]
             A = [_bits(self.A[t * self.lpool + k]) for k in range(self.lpool)]
             B = [_bits(self.B[t * self.lpool + k]) for k in range(self.lpool)]
             mask = None
@@ -210,7 +248,7 @@ class SingleCallBench:
                 mask[sorted(rows)] = 1
             self.step(c, sid)
             torch.cuda.synchronize()
-            got = oracle.decode(_bits(self.Y[x]), self.dtype)
+            got = oracle.decode(_bits(self.Y[x])[self.perm_h], self.dtype)
             ref = oracle.sgmv_apply(self.dtype, Xh, A, B, self.seg_h, self.lidx_h, Y0, row_mask=mask)
             sel = slice(None) if mask is None else mask.astype(bool)
             ratio = np.abs(got[sel] - ref[sel]) / (1e-3 + 1e-2 * np.abs(ref[sel]))
@@ -223,6 +261,8 @@ class SingleCallBench:
         return {"workload": self.name, "h_in": self.h_in, "h_out": self.h_out, "rank": self.rank,
                 "batch_rows": self.n, "segments": int(len(self.lidx_h)), "distinct_loras": self.distinct,
                 "lora_pool": self.lpool, "physical_lora_pool": self.ppool, "xy_copies": self.copies,
+                "row_layout": {"none": "segment order", "kernel": "request order, kernel row map",
+                               "torch": "request order, torch gather/scatter"}[self.row_map],
                 "algorithmic_bytes_per_step": self.bytes}
 
 
@@ -232,7 +272,7 @@ class ModelForwardBench:
 
     dtype = "bf16"
 
-    def __init__(self, name, variant=0, splits=0, layers=None, batch_projections=True):
+    def __init__(self, name, variant=0, splits=0, layers=None, batch_projections=True, row_map="none"):
         import numpy as np
         import torch
         import segmented_gather_matvec_amd as sg
@@ -242,8 +282,15 @@ class ModelForwardBench:
         self.n, self.rank, self.P = 256, 64, 64
         self.layers = layers or wl.LLAMA13B_LAYERS
         ids = wl.full_model_ids(seed=5, n=self.n, pool=self.P)
-        _, seg, lidx, mx = sg.sgmv_build_segments(ids, self.P)
+        perm, seg, lidx, mx = sg.sgmv_build_segments(ids, self.P)
         self.seg_h, self.lidx_h = seg, lidx
+        # "none": activations in segment order.  "kernel" / "torch": in request
+        # order (request perm[j] at sorted row j, the builder's output), gathered
+        # and scattered by the kernels' row map or by torch around each call.
+        self.row_map = row_map
+        self.perm_h = perm if row_map != "none" else np.arange(self.n, dtype=np.int32)
+        self.perm = torch.from_numpy(np.ascontiguousarray(self.perm_h)).to("cuda")
+        self.perm64 = self.perm.to(torch.int64)
         self.distinct = len(lidx)
         self.seg = torch.from_numpy(seg).to("cuda")
         self.lidx = torch.from_numpy(lidx).to("cuda")
@@ -292,25 +339,62 @@ class ModelForwardBench:
             for grp in groups:
                 idx = [layer * len(names) + j for j in grp]
                 self.group_idx.append(idx)
-                if len(idx) == 1:
+                if len(idx) == 1 and row_map != "kernel":
                     self.batched.append(("single", self.calls[idx[0]]))
                 else:
                     first = self.calls[idx[0]]
                     arr = (sg.sgmv_projection_t * len(idx))(
                         *[sg.sgmv_projection_t(self.calls[c][2], self.calls[c][3], self.calls[c][4]) for c in idx])
                     self.keep.append(arr)
-                    self.batched.append(("batched", (first[0], first[1], arr, len(idx), first[5], first[6], first[7],
-                                                     first[8])))
+                    self.batched.append(("batched", (first[0], first[1], arr, len(idx), first[5], first[6],
+                                                     self.perm.data_ptr() if row_map == "kernel" else None,
+                                                     first[7], first[8])))
+        if row_map == "torch":
+            # Segment-order staging buffers: one X per input group and one Y
+            # per projection of the largest group, reused by every call.
+            self.stage_x = {w: torch.empty((self.n, w), dtype=torch.bfloat16, device="cuda")
+                            for w in (5120, 13824)}
+            maxh = max(h for (_, _, h) in wl.LLAMA13B_PROJ)
+            self.stage_y = [torch.empty(self.n * maxh, dtype=torch.bfloat16, device="cuda") for _ in range(3)]
+            self.torch_calls = []
+            for g, (kind, args) in enumerate(self.batched):
+                idx = self.group_idx[g]
+                X = self.keep[idx[0]][3]
+                xs = self.stage_x[X.shape[1]]
+                ys = [self.stage_y[j][: self.n * self.keep[c][2].shape[1]].view(self.n, -1)
+                      for j, c in enumerate(idx)]
+                pj = (sg.sgmv_projection_t * len(idx))(
+                    *[sg.sgmv_projection_t(self.calls[c][2], self.calls[c][3], ys[j].data_ptr())
+                      for j, c in enumerate(idx)])
+                self.keep.append(pj)
+                first = self.calls[idx[0]]
+                self.torch_calls.append((X, xs, [self.keep[c][2] for c in idx], ys,
+                                         (first[0], xs.data_ptr(), pj, len(idx), first[5], first[6], None,
+                                          first[7], first[8])))
         self.bytes = total
         self.rows_per_step = self.n
         self.calls_per_step = len(self.batched)
         torch.cuda.synchronize()
 
-    def step(self, c, stream):
-        for kind, args in self.batched:
+    def run_group(self, g, stream):
+        if self.row_map == "torch":
+            torch = self.torch
+            X, xs, Ys, ys, args = self.torch_calls[g]
+            torch.index_select(X, 0, self.perm64, out=xs)
+            for Y, y in zip(Ys, ys):
+                torch.index_select(Y, 0, self.perm64, out=y)
+            st = self.fn_batched(*args, stream)
+            for Y, y in zip(Ys, ys):
+                Y.index_copy_(0, self.perm64, y)
+        else:
+            kind, args = self.batched[g]
             st = self.fn(*args, stream) if kind == "single" else self.fn_batched(*args, stream)
-            if st != 0:
-                raise RuntimeError(self.sg.sgmv_status_str(st))
+        if st != 0:
+            raise RuntimeError(self.sg.sgmv_status_str(st))
+
+    def step(self, c, stream):
+        for g in range(len(self.batched)):
+            self.run_group(g, stream)
 
     def check_sample(self, rows=16):
         """The first and the last call of a forward (layer 0's first projection group,
@@ -326,20 +410,17 @@ class ModelForwardBench:
             snaps = []
             for idx in self.group_idx[g]:
                 A, B, Y, X, _, _ = self.keep[idx]
-                snaps.append((Y, _bits(X), _bits(Y).copy(),
+                snaps.append((Y, _bits(X)[self.perm_h], _bits(Y)[self.perm_h],
                               [_bits(A[k]) if k in used else np.zeros((1, 1), np.uint16) for k in range(self.P)],
                               [_bits(B[k]) if k in used else np.zeros((1, 1), np.uint16) for k in range(self.P)]))
-            kind, args = self.batched[g]
-            st = self.fn(*args, sid) if kind == "single" else self.fn_batched(*args, sid)
-            if st != 0:
-                raise RuntimeError(self.sg.sgmv_status_str(st))
+            self.run_group(g, sid)
             torch.cuda.synchronize()
             mask = np.zeros(self.n, np.uint8)
             mask[np.random.default_rng(g).choice(self.n, rows, replace=False)] = 1
             mask[[0, self.n - 1]] = 1
             sel = mask.astype(bool)
             for Y, Xh, Y0, Ah, Bh in snaps:
-                got = oracle.decode(_bits(Y), "bf16")
+                got = oracle.decode(_bits(Y)[self.perm_h], "bf16")
                 ref = oracle.sgmv_apply("bf16", Xh, Ah, Bh, self.seg_h, self.lidx_h, Y0, row_mask=mask)
                 worst = max(worst, float((np.abs(got[sel] - ref[sel]) / (1e-3 + 1e-2 * np.abs(ref[sel]))).max()))
         if worst > 1.0:
@@ -351,6 +432,8 @@ class ModelForwardBench:
                 "rank": self.rank, "batch_rows": self.n, "segments": self.distinct,
                 "distinct_loras": self.distinct, "lora_pool": self.P, "projection_calls": len(self.calls),
                 "calls_per_step": len(self.batched), "calls_per_layer": self.group_names,
+                "row_layout": {"none": "segment order", "kernel": "request order, kernel row map",
+                               "torch": "request order, torch gather/scatter"}[self.row_map],
                 "algorithmic_bytes_per_step": self.bytes}
 
 
@@ -387,6 +470,9 @@ def main():
     ap.add_argument("--no-batch", action="store_true",
                     help="forward workload: one call per projection instead of batching the "
                          "projections that share an input (q,k,v and gate,up)")
+    ap.add_argument("--row-map", choices=["none", "kernel", "torch"], default="none",
+                    help="rows of X and Y in segment order (none), or in request order gathered and "
+                         "scattered by the kernels' row map (kernel) or by torch around each call (torch)")
     ap.add_argument("--graph", action="store_true",
                     help="replay the timed steps from a captured HIP graph instead of eager launches")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -418,9 +504,9 @@ def main():
     W = args.warmup if args.warmup is not None else (3 if model else 200)
     if model:
         bench = ModelForwardBench(args.workload, variant=variant, splits=args.splits,
-                                  batch_projections=not args.no_batch)
+                                  batch_projections=not args.no_batch, row_map=args.row_map)
     else:
-        bench = SingleCallBench(args.workload, variant=variant, splits=args.splits)
+        bench = SingleCallBench(args.workload, variant=variant, splits=args.splits, row_map=args.row_map)
     worst = None if args.no_check else bench.check_sample()
 
     stream = torch.cuda.current_stream()

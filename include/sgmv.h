@@ -201,8 +201,8 @@ typedef struct sgmv_projection {
 
 #define SGMV_MAX_PROJECTIONS 4
 
-/* Batched apply: Y_p[i, :] += (X[i, :] @ A_{p,k}) @ B_{p,k} for every
- * projection p < num_projections and every covered row i.  The multi-LoRA
+/* Batched apply: Y_p[row(i), :] += (X[row(i), :] @ A_{p,k}) @ B_{p,k} for
+ * every projection p < num_projections and every covered (sorted) row i.  The multi-LoRA
  * paragraph of the Punica README applies a LoRA per row to a layer's input;
  * the projections of one layer that read the same input (for instance the
  * query, key and value projections of an attention layer, each with its own
@@ -210,17 +210,25 @@ typedef struct sgmv_projection {
  * one call (one launch per stage instead of one per projection).
  *   projections  HOST array of num_projections (1..SGMV_MAX_PROJECTIONS)
  *                descriptors; the Y buffers must not alias X or each other.
+ *   row_idx      NULL (row(i) = i: X and Y are in segment order), or a DEVICE
+ *                int32 [n_rows] row map, row(i) = row_idx[i]: the sorted row i
+ *                of the segments is row row_idx[i] of X and of every Y.  With the
+ *                builder's perm as row_idx the caller keeps X and Y in request
+ *                order and skips both permutes (the gather and scatter of rows
+ *                happen in the kernels).  Precondition (not checked on the
+ *                device): the entries of row_idx[0 .. seg_indptr[S]) are
+ *                distinct and in [0, n_rows).
  *   ws           device workspace of at least
  *                (num_projections - 1) * round_up(W, 256) + W bytes, where W is
  *                sgmv_workspace_bytes(problem): projection p uses the slice at
  *                p * round_up(W, 256), whose counter area must be zero (zero
  *                the whole workspace once).
  * Same preconditions, precision and error conventions as sgmv_lora_apply,
- * which is this call with one projection. */
+ * which is this call with one projection and no row map. */
 sgmv_status_t sgmv_lora_apply_batched(const sgmv_problem_t* problem, const void* X,
                                       const sgmv_projection_t* projections, int32_t num_projections,
-                                      const int32_t* seg_indptr, const int32_t* lora_idx, void* ws,
-                                      size_t ws_bytes, void* stream);
+                                      const int32_t* seg_indptr, const int32_t* lora_idx,
+                                      const int32_t* row_idx, void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -95,7 +95,7 @@ def load_library(path: str = LIB_PATH):
     lib.sgmv_shrink.argtypes = [prob, P, P, P, P, P, P, SZ, P]
     lib.sgmv_expand.argtypes = [prob, P, P, P, P, P, P]
     lib.sgmv_lora_apply.argtypes = [prob, P, P, P, P, P, P, P, SZ, P]
-    lib.sgmv_lora_apply_batched.argtypes = [prob, P, ctypes.POINTER(sgmv_projection_t), I32, P, P, P, SZ, P]
+    lib.sgmv_lora_apply_batched.argtypes = [prob, P, ctypes.POINTER(sgmv_projection_t), I32, P, P, P, P, SZ, P]
     for name in ENTRY_POINTS[1:]:
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -240,14 +240,17 @@ def sgmv_lora_apply(problem, X, A_ptrs, B_ptrs, Y, seg_indptr, lora_idx, ws, str
     _check(st, "sgmv_lora_apply")
 
 
-def sgmv_lora_apply_batched(problem, X, projections, seg_indptr, lora_idx, ws, stream=None):
-    """Y_p[i] += (X[i] @ A_{p,k}) @ B_{p,k} for each (A_ptrs, B_ptrs, Y) in `projections`
-    (up to SGMV_MAX_PROJECTIONS), one call; asynchronous.  `ws` must hold
-    batched_workspace_bytes(problem, len(projections)) bytes."""
+def sgmv_lora_apply_batched(problem, X, projections, seg_indptr, lora_idx, ws, row_idx=None, stream=None):
+    """Y_p[row(i)] += (X[row(i)] @ A_{p,k}) @ B_{p,k} for each (A_ptrs, B_ptrs, Y) in
+    `projections` (up to SGMV_MAX_PROJECTIONS), one call; asynchronous.  `row_idx`
+    (optional device int32 [n_rows], e.g. the builder's perm) maps sorted row i to
+    row row_idx[i] of X and Y.  `ws` must hold batched_workspace_bytes(problem,
+    len(projections)) bytes."""
     import torch
     dt = _torch_dtype(problem)
     _need(X, "X", dt)
     _need(seg_indptr, "seg_indptr", torch.int32); _need(lora_idx, "lora_idx", torch.int32)
+    _need(row_idx, "row_idx", torch.int32)
     _need(ws, "ws")
     arr = (sgmv_projection_t * max(1, len(projections)))()
     for i, (A_ptrs, B_ptrs, Y) in enumerate(projections):
@@ -255,7 +258,7 @@ def sgmv_lora_apply_batched(problem, X, projections, seg_indptr, lora_idx, ws, s
         _need(A_ptrs, f"A_ptrs[{i}]", torch.int64); _need(B_ptrs, f"B_ptrs[{i}]", torch.int64)
         arr[i] = sgmv_projection_t(_ptr(A_ptrs), _ptr(B_ptrs), _ptr(Y))
     st = load_library().sgmv_lora_apply_batched(ctypes.byref(problem), _ptr(X), arr, len(projections),
-                                                _ptr(seg_indptr), _ptr(lora_idx), _ptr(ws),
+                                                _ptr(seg_indptr), _ptr(lora_idx), _ptr(row_idx), _ptr(ws),
                                                 ws.numel() * ws.element_size() if ws is not None else 0,
                                                 _stream(stream))
     _check(st, "sgmv_lora_apply_batched")

@@ -338,8 +338,8 @@ size_t apply_ws_bytes(const sgmv_problem_t& p) {
 // sgmv_lora_apply for num_proj projections that share X, the shapes and the
 // segments.  Projection i uses the workspace slice [i*stride, i*stride + need).
 sgmv_status_t apply(const sgmv_problem_t& p, const void* X, const sgmv_projection_t* pj, int np,
-                    const int32_t* seg_indptr, const int32_t* lora_idx, char* ws, size_t stride,
-                    hipStream_t s) {
+                    const int32_t* seg_indptr, const int32_t* lora_idx, const int32_t* row_idx, char* ws,
+                    size_t stride, hipStream_t s) {
   const DecodePlan d = plan_decode(p);
   const sgmv_route_t route = apply_route(p, d);
   if (route == SGMV_ROUTE_DECODE) {
@@ -347,7 +347,8 @@ sgmv_status_t apply(const sgmv_problem_t& p, const void* X, const sgmv_projectio
     // run in one launch when all of them fit on the device at once.
     if (np > 1 && d.grid * np > decode_capacity(p.dtype, p.rank, d.rb)) {
       for (int i = 0; i < np; ++i) {
-        const sgmv_status_t st = apply(p, X, pj + i, 1, seg_indptr, lora_idx, ws + (size_t)i * stride, stride, s);
+        const sgmv_status_t st =
+            apply(p, X, pj + i, 1, seg_indptr, lora_idx, row_idx, ws + (size_t)i * stride, stride, s);
         if (st != SGMV_OK) return st;
       }
       return SGMV_OK;
@@ -361,6 +362,7 @@ sgmv_status_t apply(const sgmv_problem_t& p, const void* X, const sgmv_projectio
     }
     q.seg_indptr = seg_indptr;
     q.lora_idx = lora_idx;
+    q.row_idx = row_idx;
     q.slots = reinterpret_cast<uint64_t*>(ws + SGMV_WS_COUNTER_BYTES);
     q.slot_stride = (int64_t)(stride / sizeof(uint64_t));
     q.n_rows = p.n_rows;
@@ -381,6 +383,7 @@ sgmv_status_t apply(const sgmv_problem_t& p, const void* X, const sgmv_projectio
     // chunk, the reduce sums them (in chunk order) into V, the expand reads V.
     const MfmaPlan m = plan_mfma(p);
     sgmv::MfmaParams q = mfma_params(p, m, seg_indptr, lora_idx);
+    q.row_idx = row_idx;
     q.X = static_cast<const uint16_t*>(X);
     for (int i = 0; i < np; ++i) {
       q.proj[i].A_ptrs = reinterpret_cast<const uint64_t*>(pj[i].A_ptrs);
@@ -401,6 +404,7 @@ sgmv_status_t apply(const sgmv_problem_t& p, const void* X, const sgmv_projectio
   for (int i = 0; i < np; ++i) {
     char* wsi = ws + (size_t)i * stride;
     VecParams q = base_params(p, v, seg_indptr, lora_idx, wsi);
+    q.row_idx = row_idx;
     q.X = static_cast<const uint16_t*>(X);
     q.A_ptrs = reinterpret_cast<const uint64_t*>(pj[i].A_ptrs);
     q.B_ptrs = reinterpret_cast<const uint64_t*>(pj[i].B_ptrs);
@@ -610,13 +614,13 @@ sgmv_status_t sgmv_lora_apply(const sgmv_problem_t* p, const void* X, const void
                               const void* const* B_ptrs, void* Y, const int32_t* seg_indptr,
                               const int32_t* lora_idx, void* ws, size_t ws_bytes, void* stream) {
   const sgmv_projection_t one{A_ptrs, B_ptrs, Y};
-  return sgmv_lora_apply_batched(p, X, &one, 1, seg_indptr, lora_idx, ws, ws_bytes, stream);
+  return sgmv_lora_apply_batched(p, X, &one, 1, seg_indptr, lora_idx, nullptr, ws, ws_bytes, stream);
 }
 
 sgmv_status_t sgmv_lora_apply_batched(const sgmv_problem_t* p, const void* X,
                                       const sgmv_projection_t* projections, int32_t num_projections,
-                                      const int32_t* seg_indptr, const int32_t* lora_idx, void* ws,
-                                      size_t ws_bytes, void* stream) {
+                                      const int32_t* seg_indptr, const int32_t* lora_idx,
+                                      const int32_t* row_idx, void* ws, size_t ws_bytes, void* stream) {
   sgmv_status_t st = sgmv_check_problem(p);
   if (st != SGMV_OK) return st;
   if (!projections || num_projections < 1 || num_projections > SGMV_MAX_PROJECTIONS) return SGMV_ERR_INVALID_ARG;
@@ -633,8 +637,8 @@ sgmv_status_t sgmv_lora_apply_batched(const sgmv_problem_t* p, const void* X,
   const size_t need = apply_ws_bytes(*p);
   const size_t stride = (size_t)round_up((int64_t)need, 256);
   if (ws_bytes < stride * (size_t)(num_projections - 1) + need) return SGMV_ERR_WORKSPACE;
-  return apply(*p, X, projections, num_projections, seg_indptr, lora_idx, static_cast<char*>(ws), stride,
-               static_cast<hipStream_t>(stream));
+  return apply(*p, X, projections, num_projections, seg_indptr, lora_idx, row_idx, static_cast<char*>(ws),
+               stride, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -87,7 +87,8 @@ constexpr int log2_groups() {
 }
 
 // SMALL: at most 64 LoRAs (pointer tables fetched one entry per lane).
-template <class T, int R, int RB, bool SMALL>
+// MAP: rows of X / Y are looked up in a row map.
+template <class T, int R, int RB, bool SMALL, bool MAP>
 __global__ __launch_bounds__(kThreads) void sgmv_decode_kernel(DecodeParams p) {
   constexpr int JG = R / 8;                  // 128-bit vectors per row of A_k
   constexpr int B0 = log2_groups<R>();
@@ -111,6 +112,15 @@ __global__ __launch_bounds__(kThreads) void sgmv_decode_kernel(DecodeParams p) {
   const int wave = t >> 6;
   const int G = p.splits;
   const Projection pr = p.proj[blockIdx.y];
+  // A negative size or a null table is a malformed launch (the host rejects
+  // both).  Testing every uniform argument here also makes the compiler fetch
+  // them all in the first batch of loads instead of one round trip per
+  // argument where it is first used.
+  const bool bad_size = (p.num_units | p.splits | p.kc | p.cw | p.direct_units | p.split_major | p.n_rows |
+                         p.h_in | p.h_out | p.num_segs | p.num_loras | (int32_t)(p.slot_stride >> 32)) < 0;
+  const bool bad_ptr = (p.seg_indptr == nullptr) | (p.lora_idx == nullptr) | (p.X == nullptr) |
+                       (p.slots == nullptr) | (pr.A_ptrs == nullptr) | (pr.B_ptrs == nullptr) | (pr.Y == nullptr);
+  if (bad_size | bad_ptr) return;
   // Workgroups go round-robin over the XCDs.
   int unit, g;
   if (p.split_major) {
@@ -122,7 +132,10 @@ __global__ __launch_bounds__(kThreads) void sgmv_decode_kernel(DecodeParams p) {
     unit = (slot / G) * kXcds + xcd;
     g = slot - (slot / G) * G;
   }
-  if (unit >= p.num_units) return;
+  // Workgroups past the last unit (the grid is padded to whole XCD rounds)
+  // resolve a unit past every segment and exit after the metadata loads: an
+  // exit before them would split the kernel-argument loads into serial rounds.
+  if (unit >= p.num_units) unit = 0x3fffffff;
   // With at most 64 LoRAs, fetch both pointer tables (one entry per lane) in
   // parallel with the segment metadata instead of after it: the LoRA id then
   // selects its pointers from registers, saving one dependent memory trip.
@@ -151,8 +164,12 @@ __global__ __launch_bounds__(kThreads) void sgmv_decode_kernel(DecodeParams p) {
   const int h1 = p.h_in < h0 + p.kc ? p.h_in : h0 + p.kc;
   const int c0 = g * p.cw;
   const int c1 = p.h_out < c0 + p.cw ? p.h_out : c0 + p.cw;
-  const uint16_t* Xr = p.X + (int64_t)r0 * p.h_in;
-  uint16_t* Yr = pr.Y + (int64_t)r0 * p.h_out;
+  // Rows of X / Y.  With a row map, lane l looks up the row behind sorted row
+  // r0 + l once, ahead of the streaming loads (L <= RB <= 64 rows), and every
+  // other lane takes it from there.
+  int prow = r0 + lane;
+  if constexpr (MAP) prow = p.row_idx[r0 + (lane < L ? lane : L - 1)];
+  const uint16_t* Xr = p.X + (int64_t)(MAP ? __builtin_amdgcn_readfirstlane(prow) : r0) * p.h_in;
 
   // ---------------- all loads, issued up front ----------------
   // Shrink: thread t owns ranks (t % JG)*8..+7 of rows h0 + t/JG + q*HS.
@@ -177,7 +194,9 @@ __global__ __launch_bounds__(kThreads) void sgmv_decode_kernel(DecodeParams p) {
     for (int q = 0; q < NXV; ++q) {
       const int x = t + kThreads * q;
       const int i = xvr > 0 ? x / xvr : 0, c = x - i * xvr;
-      xv[q] = load_stream(Xr + (x < L * xvr ? (int64_t)i * p.h_in + h0 + c * 8 : 0));
+      const int xi = x < L * xvr ? i : 0;
+      const int64_t row = MAP ? __shfl(prow, xi) : r0 + xi;
+      xv[q] = load_stream(p.X + row * p.h_in + (x < L * xvr ? h0 + c * 8 : 0));
     }
   }
   // Expand: thread t owns the 8 columns c0 + (t / JQ)*8 .. +7 and ranks
@@ -190,10 +209,13 @@ __global__ __launch_bounds__(kThreads) void sgmv_decode_kernel(DecodeParams p) {
   for (int m = 0; m < NB; ++m)
     bv[m] = load_stream(Bk + (col_ok ? (int64_t)(jq + JQ * m) * p.h_out + col : 0));
   u32x4 yv[NY];
+  int yrow[NY];  // row of Y of the rows i = jq + n*JQ (kept for the stores)
 #pragma unroll
   for (int n = 0; n < NY; ++n) {
     const int i = jq + JQ * n;
-    yv[n] = load_stream(Yr + (col_ok && i < L ? (int64_t)i * p.h_out + col : 0));
+    const int yi = col_ok && i < L ? i : 0;
+    yrow[n] = MAP ? __shfl(prow, yi) : r0 + yi;
+    yv[n] = load_stream(pr.Y + (int64_t)yrow[n] * p.h_out + (col_ok && i < L ? col : 0));
   }
 
   // ---------------- shrink ----------------
@@ -336,7 +358,7 @@ __global__ __launch_bounds__(kThreads) void sgmv_decode_kernel(DecodeParams p) {
         unpack8<T>(yv[i / JQ], yf);
 #pragma unroll
         for (int e = 0; e < 8; ++e) yf[e] += s[e];
-        store_vec(Yr + (int64_t)i * p.h_out + col, pack8<T>(yf));
+        store_vec(pr.Y + (int64_t)yrow[i / JQ] * p.h_out + col, pack8<T>(yf));
       }
     }
   }
@@ -348,25 +370,32 @@ hipError_t launch_t(const DecodeParams& p, int num_proj, hipStream_t stream) {
                                        : (unsigned)kXcds * (unsigned)((p.num_units + kXcds - 1) / kXcds);
   const unsigned grid = units * (unsigned)p.splits;
   if (grid == 0 || num_proj <= 0) return hipSuccess;
-  if (p.num_loras <= 64)
-    hipLaunchKernelGGL((sgmv_decode_kernel<T, R, RB, true>), dim3(grid, num_proj), dim3(kThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL((sgmv_decode_kernel<T, R, RB, false>), dim3(grid, num_proj), dim3(kThreads), 0, stream, p);
+  const bool small = p.num_loras <= 64;
+  void (*kernel)(DecodeParams) =
+      p.row_idx ? (small ? sgmv_decode_kernel<T, R, RB, true, true> : sgmv_decode_kernel<T, R, RB, false, true>)
+                : (small ? sgmv_decode_kernel<T, R, RB, true, false> : sgmv_decode_kernel<T, R, RB, false, false>);
+  hipLaunchKernelGGL(kernel, dim3(grid, num_proj), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
-// Both pool variants use the same registers and LDS within a few VGPRs; the
-// smaller of the two occupancies is reported.
+template <class T, int R, int RB, bool SMALL, bool MAP>
+int per_cu_t() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &n, reinterpret_cast<const void*>(&sgmv_decode_kernel<T, R, RB, SMALL, MAP>), kThreads, 0) != hipSuccess)
+    return 0;
+  return n;
+}
+
+// The variants (pointer pool, row map) use the same registers and LDS within a
+// few VGPRs; the smallest of their occupancies is reported.
 template <class T, int R, int RB>
 int capacity_t() {
-  int per_cu = 0, per_cu2 = 0, dev = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &per_cu, reinterpret_cast<const void*>(&sgmv_decode_kernel<T, R, RB, true>), kThreads, 0) != hipSuccess)
-    return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &per_cu2, reinterpret_cast<const void*>(&sgmv_decode_kernel<T, R, RB, false>), kThreads, 0) != hipSuccess)
-    return 0;
-  per_cu = per_cu < per_cu2 ? per_cu : per_cu2;
+  int dev = 0, cus = 0;
+  int per_cu = per_cu_t<T, R, RB, true, false>();
+  for (int n : {per_cu_t<T, R, RB, false, false>(), per_cu_t<T, R, RB, true, true>(),
+                per_cu_t<T, R, RB, false, true>()})
+    per_cu = n < per_cu ? n : per_cu;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
   return per_cu * cus;

@@ -81,7 +81,7 @@ __device__ inline void store_pair_transposed(uint16_t* dst, int stride, const u3
 // multiplied, the next stage's loads are in flight.
 constexpr int kKStage = 128;
 
-template <class T, int R>
+template <class T, int R, bool MAP>
 __global__ __launch_bounds__(kThreads) void sgmv_mfma_shrink_kernel(MfmaParams p) {
   constexpr int NT = R / 16;                // 16-wide rank tiles
   constexpr int JG = R / 8;                 // 128-bit vectors per row of A_k
@@ -99,6 +99,15 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_shrink_kernel(MfmaParams p
   const int ml = lane & 15;  // row (A operand) / rank column (B operand) of the lane
   // Linear order: H1 chunk major, so the row units that read one chunk of A_k
   // share an XCD.
+  const Projection pj = p.proj[blockIdx.y];
+  // A negative size or a null table is a malformed launch (the host rejects
+  // both).  Testing every uniform argument here also makes the compiler fetch
+  // them all in the first batch of loads.
+  const bool bad_size = (p.n_rows | p.h_in | p.num_segs | p.num_loras | p.num_units64 | p.direct_units64 |
+                         p.ksplit | p.kc | (int32_t)(p.partial_stride >> 32) | (int32_t)(p.proj_stride >> 32)) < 0;
+  const bool bad_ptr = (p.seg_indptr == nullptr) | (p.lora_idx == nullptr) | (p.X == nullptr) |
+                       (p.partials == nullptr) | (pj.A_ptrs == nullptr);
+  if (bad_size | bad_ptr) return;
   const int idx = xcd_linear_index();
   if (idx >= p.num_units64 * p.ksplit) return;
   const int g = idx / p.num_units64;
@@ -107,13 +116,13 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_shrink_kernel(MfmaParams p
                                     p.direct_units64, unit);
   if (un.L <= 0) return;
   const int L = un.L, r0 = un.r0;
-  const uint16_t* Ak = reinterpret_cast<const uint16_t*>(p.proj[blockIdx.y].A_ptrs[un.k]);
+  const uint16_t* Ak = reinterpret_cast<const uint16_t*>(pj.A_ptrs[un.k]);
   const int k0 = g * p.kc;
   const int k1 = p.h_in < k0 + p.kc ? p.h_in : k0 + p.kc;
   // Row this lane feeds into the MFMA A operand (rows past the segment re-read
   // its last row and are never stored).
   const int row = wave * 16 + ml;
-  const uint16_t* xrow = p.X + (int64_t)(r0 + (row < L ? row : L - 1)) * p.h_in;
+  const uint16_t* xrow = p.X + phys_row<MAP>(p.row_idx, r0 + (row < L ? row : L - 1)) * p.h_in;
 
   // All loads of one stage, at clamped (valid) addresses; values past k1 are
   // zeroed where they are consumed.
@@ -228,7 +237,7 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_reduce_kernel(MfmaParams p
 }
 
 // ---------------------------------------------------------------- expand
-template <class T, int R>
+template <class T, int R, bool MAP>
 __global__ __launch_bounds__(kThreads) void sgmv_mfma_expand_kernel(MfmaParams p) {
   constexpr int K2 = 2 * R;            // virtual K: [V_hi | V_lo] against [B_k; B_k]
   constexpr int KSTEPS = K2 / 32;
@@ -248,6 +257,13 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_expand_kernel(MfmaParams p
   const int wave = t >> 6;
   const int q = lane >> 4;
   const int ml = lane & 15;
+  const Projection pj = p.proj[blockIdx.y];
+  // Malformed launch test; it also batches the argument loads (as in the shrink).
+  const bool bad_size = (p.n_rows | p.h_out | p.num_segs | p.num_loras | p.num_units64 | p.direct_units64 |
+                         (p.chunks_per_wg - 1) | (int32_t)(p.proj_stride >> 32)) < 0;
+  const bool bad_ptr = (p.seg_indptr == nullptr) | (p.lora_idx == nullptr) | (p.V == nullptr) |
+                       (pj.B_ptrs == nullptr) | (pj.Y == nullptr);
+  if (bad_size | bad_ptr) return;
   const int nchunks = (p.h_out + kCW - 1) / kCW;
   const int ngroups = (nchunks + p.chunks_per_wg - 1) / p.chunks_per_wg;
   // Linear order: column group major, so the row units that read one slice of
@@ -262,9 +278,17 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_expand_kernel(MfmaParams p
   const int L = un.L, r0 = un.r0;
   const int ch0 = grp * p.chunks_per_wg;
   const int ch1 = nchunks < ch0 + p.chunks_per_wg ? nchunks : ch0 + p.chunks_per_wg;
-  const uint16_t* Bk = reinterpret_cast<const uint16_t*>(p.proj[blockIdx.y].B_ptrs[un.k]);
-  uint16_t* Yr = p.proj[blockIdx.y].Y + (int64_t)r0 * p.h_out;
+  const uint16_t* Bk = reinterpret_cast<const uint16_t*>(pj.B_ptrs[un.k]);
+  uint16_t* Ybase = pj.Y;
   const float* Vp = p.V + (int64_t)blockIdx.y * p.proj_stride;
+  // Row of Y behind each tile row this lane loads and stores, looked up once
+  // (tile rows past the segment take the first row and are never stored).
+  int yrow[NYV];
+#pragma unroll
+  for (int u = 0; u < NYV; ++u) {
+    const int rr = wave * 16 + (lane + 64 * u) / CV;
+    yrow[u] = (int)phys_row<MAP>(p.row_idx, r0 + (rr < L ? rr : 0));
+  }
 
   // Loads of one chunk (all lanes issue the same loads; addresses of lanes
   // without work are clamped to a valid element).
@@ -272,9 +296,9 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_expand_kernel(MfmaParams p
     const int c0 = ch * kCW;
 #pragma unroll
     for (int m = 0; m < NBP; ++m) {
-      const int pr = t + kThreads * m;
-      const int j = (pr / CV) * 2, c = c0 + (pr % CV) * 8;
-      const bool ok = pr < R / 2 * CV && ch < ch1 && c < p.h_out;
+      const int pv = t + kThreads * m;
+      const int j = (pv / CV) * 2, c = c0 + (pv % CV) * 8;
+      const bool ok = pv < R / 2 * CV && ch < ch1 && c < p.h_out;
       bv[m][0] = load_stream(Bk + (ok ? (int64_t)j * p.h_out + c : 0));
       bv[m][1] = load_stream(Bk + (ok ? (int64_t)(j + 1) * p.h_out + c : 0));
     }
@@ -284,7 +308,7 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_expand_kernel(MfmaParams p
       const int rr = wave * 16 + v / CV;
       const int c = c0 + (v % CV) * 8;
       const bool ok = rr < L && ch < ch1 && c < p.h_out;
-      yv[u] = load_stream(Yr + (ok ? (int64_t)rr * p.h_out + c : 0));
+      yv[u] = load_stream(Ybase + (int64_t)yrow[u] * p.h_out + (ok ? c : 0));
     }
   };
   u32x4 bvA[NBP][2], yvA[NYV], bvB[NBP][2], yvB[NYV];
@@ -354,7 +378,7 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_expand_kernel(MfmaParams p
         unpack8<T>(yv[u], yf);
 #pragma unroll
         for (int e = 0; e < 8; ++e) yf[e] += out[rl * OST + cl + e];
-        store_vec(Yr + (int64_t)rr * p.h_out + c0 + cl, pack8<T>(yf));
+        store_vec(Ybase + (int64_t)yrow[u] * p.h_out + c0 + cl, pack8<T>(yf));
       }
     }
   };
@@ -380,14 +404,24 @@ hipError_t launch_t(int stage, const MfmaParams& p, int np, hipStream_t s) {
   unsigned grid = 0;
   if (stage == 0) {
     grid = xcd_grid((unsigned)p.num_units64 * (unsigned)p.ksplit);
-    if (grid && np > 0) hipLaunchKernelGGL((sgmv_mfma_shrink_kernel<T, R>), dim3(grid, np), dim3(kThreads), 0, s, p);
+    if (grid && np > 0) {
+      if (p.row_idx)
+        hipLaunchKernelGGL((sgmv_mfma_shrink_kernel<T, R, true>), dim3(grid, np), dim3(kThreads), 0, s, p);
+      else
+        hipLaunchKernelGGL((sgmv_mfma_shrink_kernel<T, R, false>), dim3(grid, np), dim3(kThreads), 0, s, p);
+    }
   } else if (stage == 1) {
     grid = (unsigned)p.num_units64 * (unsigned)(kMT / kReduceRows);
     if (grid && np > 0) hipLaunchKernelGGL((sgmv_mfma_reduce_kernel<R>), dim3(grid, np), dim3(kThreads), 0, s, p);
   } else {
     const int nchunks = (p.h_out + kCW - 1) / kCW;
     grid = xcd_grid((unsigned)p.num_units64 * (unsigned)((nchunks + p.chunks_per_wg - 1) / p.chunks_per_wg));
-    if (grid && np > 0) hipLaunchKernelGGL((sgmv_mfma_expand_kernel<T, R>), dim3(grid, np), dim3(kThreads), 0, s, p);
+    if (grid && np > 0) {
+      if (p.row_idx)
+        hipLaunchKernelGGL((sgmv_mfma_expand_kernel<T, R, true>), dim3(grid, np), dim3(kThreads), 0, s, p);
+      else
+        hipLaunchKernelGGL((sgmv_mfma_expand_kernel<T, R, false>), dim3(grid, np), dim3(kThreads), 0, s, p);
+    }
   }
   return grid && np > 0 ? hipGetLastError() : hipSuccess;
 }
@@ -410,12 +444,17 @@ hipError_t launch_stage(int dtype, int rank, int stage, const MfmaParams& p, int
 
 bool mfma_supported(int rank) { return rank == 16 || rank == 32 || rank == 64; }
 
+// The smaller occupancy of the two row-layout variants.
 template <class T, int R>
 int expand_capacity_t() {
-  int per_cu = 0, dev = 0, cus = 0;
+  int per_cu = 0, per_cu2 = 0, dev = 0, cus = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &per_cu, reinterpret_cast<const void*>(&sgmv_mfma_expand_kernel<T, R>), kThreads, 0) != hipSuccess)
+          &per_cu, reinterpret_cast<const void*>(&sgmv_mfma_expand_kernel<T, R, false>), kThreads, 0) != hipSuccess)
     return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &per_cu2, reinterpret_cast<const void*>(&sgmv_mfma_expand_kernel<T, R, true>), kThreads, 0) != hipSuccess)
+    return 0;
+  per_cu = per_cu < per_cu2 ? per_cu : per_cu2;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
   return per_cu * cus;

@@ -23,6 +23,7 @@ struct VecParams {
   float* V;
   const int32_t* seg_indptr;
   const int32_t* lora_idx;
+  const int32_t* row_idx;  // null, or row of X / Y of each sorted row
   float* partials;     // [num_units][splits][RB][rank] fp32
   uint32_t* counters;  // [2 * num_units]: arrivals, departures
   int32_t n_rows, h_in, h_out, num_segs, num_loras;
@@ -56,20 +57,25 @@ struct Projection {
   uint16_t* Y;
 };
 
+
 struct DecodeParams {
-  const uint16_t* X;
-  Projection proj[kMaxProjections];
-  const int32_t* seg_indptr;
-  const int32_t* lora_idx;
-  uint64_t* slots;      // projection 0: [num_units][splits][parts][RB*rank] tagged partials
-  int64_t slot_stride;  // words between the slot areas of consecutive projections
-  int32_t n_rows, h_in, h_out, num_segs, num_loras;
+  // Scalars first and the pointers after them, so that the kernel fetches its
+  // arguments in a few wide loads before its first metadata load.
   int32_t num_units, splits, kc, cw, direct_units;
   // 1: workgroup b runs split b % splits of unit b / splits, so the splits of a
   // unit go round-robin over the XCDs and equal splits of neighbouring units
   // (which read the same A_k / B_k slice when they share a LoRA) meet on one
   // XCD. 0: the splits of a unit share an XCD (grid padded to 8 units).
   int32_t split_major;
+  int32_t n_rows, h_in, h_out, num_segs, num_loras;
+  int32_t pad_;
+  const int32_t* seg_indptr;
+  const int32_t* lora_idx;
+  const int32_t* row_idx;  // null, or row of X / Y of each sorted row
+  uint64_t* slots;      // projection 0: [num_units][splits][parts][RB*rank] tagged partials
+  int64_t slot_stride;  // words between the slot areas of consecutive projections
+  const uint16_t* X;
+  Projection proj[kMaxProjections];
 };
 
 bool decode_supported(int rank, int rb);
@@ -85,17 +91,18 @@ constexpr int kMfmaColsPerTile = 128;     // output columns per expand chunk
 constexpr int kMfmaKChunk = 256;          // H1 granule of the shrink's split
 
 struct MfmaParams {
-  const uint16_t* X;
-  Projection proj[kMaxProjections];
-  float* V;                // projection 0; reduce: output; expand: input (fp32 [n_rows, rank])
-  float* partials;         // projection 0; shrink: H1-chunk s writes partials + s*partial_stride
-  const int32_t* seg_indptr;
-  const int32_t* lora_idx;
-  int64_t partial_stride;  // floats between partial planes (n_rows * rank)
-  int64_t proj_stride;     // floats between the V / partial areas of consecutive projections
   int32_t n_rows, h_in, h_out, num_segs, num_loras;
   int32_t num_units64, direct_units64;  // units of <= 64 rows of one segment
   int32_t ksplit, kc, chunks_per_wg;
+  const int32_t* seg_indptr;
+  const int32_t* lora_idx;
+  const int32_t* row_idx;  // null, or row of X / Y of each sorted row
+  int64_t partial_stride;  // floats between partial planes (n_rows * rank)
+  int64_t proj_stride;     // floats between the V / partial areas of consecutive projections
+  const uint16_t* X;
+  float* V;                // projection 0; reduce: output; expand: input (fp32 [n_rows, rank])
+  float* partials;         // projection 0; shrink: H1-chunk s writes partials + s*partial_stride
+  Projection proj[kMaxProjections];
 };
 
 bool mfma_supported(int rank);

@@ -82,7 +82,7 @@ __device__ inline void gather_partials(const float* base, int G, int n, float* s
   if (t < n) dst[t] = acc;
 }
 
-template <class T, int R, int RB, int MODE>
+template <class T, int R, int RB, int MODE, bool MAP>
 __global__ __launch_bounds__(kThreads) void sgmv_vec_kernel(VecParams p) {
   constexpr int JG = R / 8;                 // 128-bit vectors per row of A_k
   constexpr int B0 = log2_groups<R>();
@@ -141,7 +141,7 @@ __global__ __launch_bounds__(kThreads) void sgmv_vec_kernel(VecParams p) {
       const int y = t + kThreads * q;
       const int i = cvr ? y / cvr : 0, cv = y - i * cvr;
       const bool ok = y < L * cvr;
-      yv[q] = load_stream(p.Y + (int64_t)r0 * p.h_out + (ok ? (int64_t)i * p.h_out + cp0 + cv * 8 : 0));
+      yv[q] = load_stream(p.Y + phys_row<MAP>(p.row_idx, r0 + (ok ? i : 0)) * p.h_out + (ok ? cp0 + cv * 8 : 0));
     }
   };
   auto compute_expand = [&](int cp0, const u32x4 (&bv)[kNB], const u32x4 (&yv)[NYV]) {
@@ -186,7 +186,7 @@ __global__ __launch_bounds__(kThreads) void sgmv_vec_kernel(VecParams p) {
         unpack8<T>(yv[0], yf);
 #pragma unroll
         for (int e = 0; e < 8; ++e) yf[e] += acc[e];
-        store_vec(p.Y + (int64_t)(r0 + i) * p.h_out + cp0 + cv * 8, pack8<T>(yf));
+        store_vec(p.Y + phys_row<MAP>(p.row_idx, r0 + i) * p.h_out + cp0 + cv * 8, pack8<T>(yf));
       }
     } else {
 #pragma unroll
@@ -207,7 +207,7 @@ __global__ __launch_bounds__(kThreads) void sgmv_vec_kernel(VecParams p) {
           unpack8<T>(yv[q], yf);
 #pragma unroll
           for (int e = 0; e < 8; ++e) yf[e] += acc[e];
-          store_vec(p.Y + (int64_t)(r0 + i) * p.h_out + cp0 + cv * 8, pack8<T>(yf));
+          store_vec(p.Y + phys_row<MAP>(p.row_idx, r0 + i) * p.h_out + cp0 + cv * 8, pack8<T>(yf));
         }
       }
     }
@@ -232,7 +232,7 @@ __global__ __launch_bounds__(kThreads) void sgmv_vec_kernel(VecParams p) {
         const int x = t + kThreads * q;
         const int i = xvr ? x / xvr : 0, c = x - i * xvr;
         const bool ok = x < L * xvr;
-        xv[q] = load_stream(p.X + (int64_t)r0 * p.h_in + (ok ? (int64_t)i * p.h_in + hp0 + c * 8 : 0));
+        xv[q] = load_stream(p.X + phys_row<MAP>(p.row_idx, r0 + (ok ? i : 0)) * p.h_in + (ok ? hp0 + c * 8 : 0));
       }
     };
     float acc[RB][8];
@@ -356,7 +356,10 @@ template <class T, int R, int RB, int MODE>
 hipError_t launch_one(const VecParams& p, hipStream_t stream) {
   const unsigned grid = (unsigned)p.num_units * (unsigned)p.splits;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((sgmv_vec_kernel<T, R, RB, MODE>), dim3(grid), dim3(kThreads), 0, stream, p);
+  if (p.row_idx)
+    hipLaunchKernelGGL((sgmv_vec_kernel<T, R, RB, MODE, true>), dim3(grid), dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((sgmv_vec_kernel<T, R, RB, MODE, false>), dim3(grid), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

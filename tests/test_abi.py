@@ -99,8 +99,8 @@ def test_batched_apply_fails_fast_on_bad_arguments():
 
     def call(projs, n, ws_bytes, X=fake, problem=p):
         arr = (sg.sgmv_projection_t * max(1, len(projs)))(*projs)
-        return lib.sgmv_lora_apply_batched(ctypes.byref(problem), X, arr if projs else None, n, fake, fake, fake,
-                                           ws_bytes, None)
+        return lib.sgmv_lora_apply_batched(ctypes.byref(problem), X, arr if projs else None, n, fake, fake, None,
+                                           fake, ws_bytes, None)
     ok = sg.sgmv_projection_t(0x10000, 0x10000, 0x10000)
     assert call([], 0, need) == sg.SGMV_ERR_INVALID_ARG
     assert call([ok] * 5, 5, 5 * need) == sg.SGMV_ERR_INVALID_ARG            # more than SGMV_MAX_PROJECTIONS

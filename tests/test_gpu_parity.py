@@ -158,6 +158,44 @@ def test_batched_projections_match_oracle_and_single_calls(case):
         assert np.array_equal(to_bits(Y), got[i]), f"projection {i}: batched != single call"
 
 
+@pytest.mark.parametrize("case", ["distinct", "skewed", "identical_rb4", "identical_rb16", "skewed_vector",
+                                  "mixed_mfma_random_map"])
+def test_row_map_gathers_and_scatters_rows(case):
+    """With row_idx the kernels read X and update Y in request order: the result
+    equals the oracle on the sorted rows, scattered back through the map, and
+    rows outside the map keep their values."""
+    import torch
+    if case == "mixed_mfma_random_map":
+        w = workloads.mixed(16, seed=416, pairs=((512, 1376),), lo=16, hi=100)[0]
+        seg, lidx = np.asarray(w.seg_indptr, np.int32), np.asarray(w.lora_idx, np.int32)
+        n = w.X.shape[0]
+        perm = np.random.default_rng(3).permutation(n + 7)[: n].astype(np.int32)  # rows among n + 7
+        X = np.zeros((n + 7, w.X.shape[1]), np.uint16); X[perm] = w.X
+        Y0 = workloads.to_bits(np.random.default_rng(4).standard_normal((n + 7, w.Y0.shape[1])).astype(np.float32),
+                               w.dtype)
+        variant, splits = sg.SGMV_VARIANT_MFMA, 0
+    else:
+        kind, n, variant, splits = {"distinct": ("distinct", 32, sg.SGMV_VARIANT_AUTO, 0),
+                                    "skewed": ("skewed", 64, sg.SGMV_VARIANT_AUTO, 0),
+                                    "identical_rb4": ("identical", 32, sg.SGMV_VARIANT_FUSED, 64),
+                                    "identical_rb16": ("identical", 64, sg.SGMV_VARIANT_FUSED, 128),
+                                    "skewed_vector": ("skewed", 32, sg.SGMV_VARIANT_VECTOR, 0)}[case]
+        w = workloads.popularity(kind, n) if kind != "distinct" else workloads.decode_distinct()
+        if w.req_lora is None:  # Distinct: requests in a shuffled order
+            w.req_lora = np.random.default_rng(5).permutation(w.num_loras)[: w.X.shape[0]].astype(np.int32)
+        perm, seg, lidx, _ = sg.sgmv_build_segments(w.req_lora, w.num_loras)
+        X, Y0 = w.X, w.Y0                    # request order
+    call = DeviceCall(w.dtype, X, w.A, w.B, Y0, seg, lidx, variant=variant, splits=splits)
+    ws = sg.new_workspace(call.problem)
+    sg.sgmv_lora_apply_batched(call.problem, call.X, [(call.A_ptrs, call.B_ptrs, call.Y)], call.seg_d,
+                               call.lidx_d, ws, row_idx=torch.from_numpy(np.ascontiguousarray(perm)).cuda())
+    torch.cuda.synchronize()
+    ref_sorted = oracle.sgmv_apply(w.dtype, X[perm], w.A, w.B, seg, lidx, Y0[perm])
+    ref = oracle.decode(Y0, w.dtype)
+    ref[perm] = ref_sorted
+    assert_close(to_bits(call.Y), ref, w.dtype, what=case)
+
+
 @pytest.mark.parametrize("variant", [sg.SGMV_VARIANT_AUTO, sg.SGMV_VARIANT_VECTOR, sg.SGMV_VARIANT_MFMA])
 @pytest.mark.parametrize("rank", [16, 64])
 def test_mixed_prefill_decode_reduced(rank, variant):
