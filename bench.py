@@ -121,6 +121,9 @@ def workload_layout(name):
 
 
 SINGLE_WORKLOADS = (["decode_distinct_h4096_r16_b32", "decode_distinct_h4096_r16_b64"]
+                    + [f"decode_distinct_h4096_r16_b{n}" for n in (1, 8, 16)]
+                    + ["decode_distinct_h4096_r32_b32", "decode_distinct_h4096_r64_b8",
+                       "decode_distinct_h4096_r64_b32", "decode_distinct_h11008_r16_b32"]
                     + [f"{k}_b{n}" for k in ("identical", "uniform", "skewed") for n in (32, 64)]
                     + [f"mixed_r{r}_{a}" for r in (16, 64) for a in ("4096to11008", "11008to4096")])
 MODEL_WORKLOADS = ["llama13b_r64_b256_forward"]
@@ -437,6 +440,128 @@ class ModelForwardBench:
                 "algorithmic_bytes_per_step": self.bytes}
 
 
+def latency_curve(batches=(1, 2, 4, 8, 16, 32, 64), steps=200, warmup=20):
+    """Latency of the LoRA addend against batch size, the micro-benchmark of the
+    Punica README (page "Punica：多 LoRA 模型统一服务框架", micro-benchmark
+    paragraph): the base projection X@W keeps its batching effect, a naive LoRA
+    implementation does not, SGMV does.  Shape of the headline workload
+    (H1 = H2 = 4096, r = 16, fp16, Distinct: every row its own LoRA).
+
+    Per batch size n, one call of each:
+      base_gemm   torch.matmul(X, W), W [4096, 4096] (context: the base layer)
+      sgmv        sgmv_lora_apply (this library)
+      loop        naive LoRA, one (x_i @ A_k) @ B_k pair of torch matmuls per segment
+      gather_bmm  naive LoRA, A_k / B_k gathered per row, then two torch.bmm
+    Each is timed eagerly (<name>_us: wall time per call, host launch costs
+    included) and as 16 calls replayed from a captured HIP graph
+    (<name>_graph_us: device time per call).
+    Weights come from a 1 GiB pool (W from 16 copies) rotated per call, as in
+    the other workloads.  Every method's output is checked against the fp64
+    oracle on the first call (max |err| / (1e-3 + 1e-2 |ref|), reported; the
+    torch baselines round V to fp16 and may exceed 1)."""
+    import numpy as np
+    import torch
+    import oracle
+    import segmented_gather_matvec_amd as sg
+    import workloads as wl
+
+    H, r, P, dt = 4096, 16, 4096, torch.float16
+    A = wl.device_normal((P, H, r), H ** -0.5, "f16", 7001)
+    B = wl.device_normal((P, r, H), r ** -0.5, "f16", 7002)
+    Ws = wl.device_normal((16, H, H), H ** -0.5, "f16", 7003)
+    lib = sg.load_library()
+    curve = []
+    for n in batches:
+        X = wl.device_normal((16, n, H), 1.0, "f16", 7100 + n)
+        Y = wl.device_normal((16, n, H), 1.0, "f16", 7200 + n)
+        out = torch.empty((n, H), dtype=dt, device="cuda")
+        tables = P // n
+        phys = torch.arange(tables * n, device="cuda", dtype=torch.int64).view(tables, n)
+        A_tab = (A.data_ptr() + phys * (H * r * 2)).contiguous()
+        B_tab = (B.data_ptr() + phys * (r * H * 2)).contiguous()
+        seg = torch.arange(n + 1, dtype=torch.int32, device="cuda")
+        lidx = torch.arange(n, dtype=torch.int32, device="cuda")
+        prob = sg.make_problem("f16", n, H, H, r, n, n, 1)
+        ws = sg.new_workspace(prob)
+        pb = ctypes.byref(prob)
+
+        def base_gemm(c):
+            torch.matmul(X[c % 16], Ws[c % 16], out=out)
+
+        sgmv_args = [(pb, X[c % 16].data_ptr(), A_tab[c % tables].data_ptr(), B_tab[c % tables].data_ptr(),
+                      Y[c % 16].data_ptr(), seg.data_ptr(), lidx.data_ptr(), ws.data_ptr(), ws.numel())
+                     for c in range(max(tables, 16))]
+
+        def sgmv(c):
+            st = lib.sgmv_lora_apply(*sgmv_args[c % len(sgmv_args)], torch.cuda.current_stream().cuda_stream)
+            if st != 0:
+                raise RuntimeError(sg.sgmv_status_str(st))
+
+        def loop(c):
+            t, x, y = c % tables, X[c % 16], Y[c % 16]
+            for i in range(n):
+                k = t * n + i
+                y[i:i + 1].addmm_(torch.mm(x[i:i + 1], A[k]), B[k])
+
+        def gather_bmm(c):
+            t, x, y = c % tables, X[c % 16], Y[c % 16]
+            idx = phys[t]
+            v = torch.bmm(x[:, None, :], A.index_select(0, idx))
+            y += torch.bmm(v, B.index_select(0, idx))[:, 0, :]
+
+        methods = {"base_gemm": base_gemm, "sgmv": sgmv, "loop": loop, "gather_bmm": gather_bmm}
+        row = {"batch": n}
+        # Parity of each LoRA method on call 0 against the oracle (host copies
+        # taken before the call; Y restored afterwards).
+        Xh = _bits(X[0])
+        Ah = [_bits(A[k]) for k in range(n)]
+        Bh = [_bits(B[k]) for k in range(n)]
+        for name in ("sgmv", "loop", "gather_bmm"):
+            y0 = Y[0].clone()
+            ref = oracle.sgmv_apply("f16", Xh, Ah, Bh, np.arange(n + 1, dtype=np.int32),
+                                    np.arange(n, dtype=np.int32), _bits(y0))
+            methods[name](0)
+            torch.cuda.synchronize()
+            got = oracle.decode(_bits(Y[0]), "f16")
+            row[name + "_err_over_bound"] = round(float((np.abs(got - ref) / (1e-3 + 1e-2 * np.abs(ref))).max()), 4)
+            Y[0].copy_(y0)
+        if row["sgmv_err_over_bound"] > 1.0:
+            raise AssertionError(f"sgmv parity failed at batch {n}: {row['sgmv_err_over_bound']}")
+        for name, fn in methods.items():
+            # Eager: what a Python caller sees, host launch costs included.
+            for c in range(warmup):
+                fn(c)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for c in range(steps):
+                fn(c)
+            torch.cuda.synchronize()
+            row[name + "_us"] = round((time.perf_counter() - t0) / steps * 1e6, 3)
+            # Device time: 16 calls (distinct weights) captured in a HIP graph
+            # and replayed, which takes the host out.
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for c in range(16):
+                    fn(c)
+            g.replay()
+            torch.cuda.synchronize()
+            reps = max(1, steps // 16)
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                g.replay()
+            torch.cuda.synchronize()
+            row[name + "_graph_us"] = round((time.perf_counter() - t0) / (reps * 16) * 1e6, 3)
+            del g
+        curve.append(row)
+        print(json.dumps(row), file=sys.stderr, flush=True)
+        del X, Y, out, A_tab, B_tab, ws
+    return {"metric": "LoRA addend latency vs batch size: SGMV against naive LoRA (base X@W for context)",
+            "unit": "us", "higher_is_better": False, "dtype": "f16", "data": "synthetic",
+            "config": {"workload": "latency_curve_h4096_r16_distinct", "h_in": H, "h_out": H, "rank": r,
+                       "lora_pool": P, "steps": steps, "warmup": warmup},
+            "curve": curve}
+
+
 def cpu_baseline(seconds=10.0):
     """The oracle as it stands, on a host copy of the headline workload's shape."""
     import oracle
@@ -473,6 +598,9 @@ def main():
     ap.add_argument("--row-map", choices=["none", "kernel", "torch"], default="none",
                     help="rows of X and Y in segment order (none), or in request order gathered and "
                          "scattered by the kernels' row map (kernel) or by torch around each call (torch)")
+    ap.add_argument("--curve", action="store_true",
+                    help="instead of one workload: the LoRA addend's latency against batch size for "
+                         "SGMV and two naive LoRA implementations (one JSON line)")
     ap.add_argument("--graph", action="store_true",
                     help="replay the timed steps from a captured HIP graph instead of eager launches")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -498,6 +626,9 @@ def main():
         torch.cuda.synchronize()
         del src, dst
         torch.cuda.empty_cache()
+    if args.curve:
+        print(json.dumps(latency_curve()), flush=True)
+        return
     variant = {"auto": 0, "vector": 1, "fused": 2, "mfma": 3}[args.variant]
     model = args.workload in MODEL_WORKLOADS
     K = args.steps if args.steps is not None else (20 if model else 2000)

@@ -87,10 +87,6 @@ struct DecodePlan {
   int split_major = 0;
 };
 
-// Aim for one workgroup per CU: each decode workgroup keeps 32+ KiB of loads
-// in flight, so 256 of them cover the HBM latency-bandwidth product.
-constexpr int kDecodeTargetWorkgroups = 256;
-
 DecodePlan plan_decode_rb(const sgmv_problem_t& p, int rb, int split_major) {
   DecodePlan d;
   d.rb = rb;
@@ -108,14 +104,12 @@ DecodePlan plan_decode_rb(const sgmv_problem_t& p, int rb, int split_major) {
                                 ceil_div(p.h_out, sgmv::decode_max_cw()));
   const int64_t gmax = std::min<int64_t>({ceil_div(p.h_in, 8), ceil_div(p.h_out, 8), (int64_t)kMaxSplits});
   if (gmin > gmax) return d;
-  // Each workgroup gathers splits * parts * rows * rank partials; keep that to
-  // one staging round (2048 values) unless the caller asks for more splits.
+  // The fewest splits whose chunks fit one workgroup: every extra split adds a
+  // partial to each unit's exchange, and measured over batches of 1 to 64 rows
+  // the exchange fan-in costs more than the bandwidth of the extra workgroups
+  // gains (one row: 8.8 us at 128 splits, 4.0 us at 8).
   const int parts = 1;  // one published partial per workgroup
-  const int64_t rows = std::max(1, std::min(d.rb, p.max_seg_len));
-  const int64_t gather_cap = std::max<int64_t>(1, 2048 / ((int64_t)parts * rows * p.rank));
-  int64_t g = p.splits > 0 ? p.splits
-                           : std::min(ceil_div(kDecodeTargetWorkgroups, std::max<int64_t>(d.num_units, 1)),
-                                      gather_cap);
+  int64_t g = p.splits > 0 ? p.splits : gmin;
   g = std::max(gmin, std::min(g, gmax));
   d.splits = (int)g;
   d.kc = (int)round_up(ceil_div(p.h_in, g), 8);

@@ -93,7 +93,7 @@ __global__ __launch_bounds__(kThreads) void sgmv_decode_kernel(DecodeParams p) {
   constexpr int JG = R / 8;                  // 128-bit vectors per row of A_k
   constexpr int B0 = log2_groups<R>();
   constexpr int HS = kThreads / JG;          // A_k rows covered by one sweep of the workgroup
-  constexpr int NA = kDecodeRowsPerThread;   // A_k rows per thread
+  constexpr int NA = decode_rows_per_thread(R);  // A_k rows per thread
   constexpr int KCMAX = NA * HS;             // = decode_max_kc(R)
   constexpr int JQ = kDecodeLanesPerColumn;  // lanes sharing one 8-column vector of B_k
   constexpr int NB = R / JQ;                 // B_k vectors per thread

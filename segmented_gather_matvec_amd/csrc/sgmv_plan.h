@@ -43,9 +43,13 @@ constexpr int vec_cols_per_pass(int rank) { return 256 * 2 * 8 / rank; }
 hipError_t launch_vec(int dtype, int rank, int rb, int mode, const VecParams& p, hipStream_t stream);
 
 // One-launch decode kernel (shrink, on-chip hand-off, expand).
-constexpr int kDecodeRowsPerThread = 4;   // A_k rows (128-bit vectors) per thread
+// A_k rows (one 128-bit vector each) per thread.  Ranks 32 and 64 take 8, so
+// that H1 = 4096 needs 16 splits instead of 32 (a rank-64 batch of 32 rows
+// then fits on the device at once: 9.9 us instead of 23.6 us on the two-launch
+// route); rank 16 is fastest at 4 (8 was 0.1-0.8 us slower on every batch).
+constexpr int decode_rows_per_thread(int rank) { return rank >= 32 ? 8 : 4; }
 constexpr int kDecodeLanesPerColumn = 4;  // lanes sharing one 8-column vector of B_k
-constexpr int decode_max_kc(int rank) { return kDecodeRowsPerThread * 256 / (rank / 8); }
+constexpr int decode_max_kc(int rank) { return decode_rows_per_thread(rank) * 256 / (rank / 8); }
 constexpr int decode_max_cw() { return 256 / kDecodeLanesPerColumn * 8; }
 
 // One projection of a batched call (its own LoRA tables and output); the
