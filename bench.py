@@ -127,6 +127,10 @@ SINGLE_WORKLOADS = (["decode_distinct_h4096_r16_b32", "decode_distinct_h4096_r16
                     + [f"{k}_b{n}" for k in ("identical", "uniform", "skewed") for n in (32, 64)]
                     + [f"mixed_r{r}_{a}" for r in (16, 64) for a in ("4096to11008", "11008to4096")])
 MODEL_WORKLOADS = ["llama13b_r64_b256_forward"]
+# Mixed ranks: Distinct decode batch whose LoRAs have ranks 8..64 (compact
+# storage, per-LoRA rank table and scales), against the same batch padded to
+# rank 64 (decode_distinct_h4096_r64_b32).
+HET_WORKLOADS = ["decode_mixedrank_h4096_r64_b32"]
 
 
 class SingleCallBench:
@@ -266,6 +270,109 @@ class SingleCallBench:
                 "lora_pool": self.lpool, "physical_lora_pool": self.ppool, "xy_copies": self.copies,
                 "row_layout": {"none": "segment order", "kernel": "request order, kernel row map",
                                "torch": "request order, torch gather/scatter"}[self.row_map],
+                "algorithmic_bytes_per_step": self.bytes}
+
+
+class MixedRankBench:
+    """One sgmv_lora_apply_batched call per step over a Distinct decode batch
+    (H1 = H2 = 4096, 32 fp16 rows, 32 LoRAs) whose LoRAs keep their own ranks,
+    drawn from {8, 16, 32, 64} (compact storage: A_k [4096, r_k], B_k [r_k, 4096]),
+    each with its own scale.  The largest rank (64) sets the compiled tile; the
+    kernels read only r_k ranks of each LoRA.  Weights rotate through a >= 1 GiB
+    pool and X / Y through copies, as in the other workloads."""
+
+    def __init__(self, name, variant=0, splits=0):
+        import numpy as np
+        import torch
+        import segmented_gather_matvec_amd as sg
+        import workloads as wl
+
+        self.name, self.sg, self.torch = name, sg, torch
+        self.dtype, self.h_in, self.h_out, self.R, self.n = "f16", 4096, 4096, 64, 32
+        rng = np.random.default_rng(61)
+        self.ranks_h = rng.choice([8, 16, 32, 64], self.n).astype(np.int32)
+        self.scales_h = rng.uniform(0.5, 2.0, self.n).astype(np.float32)
+        e = 2
+        lora_elems = (self.h_in + self.h_out) * self.ranks_h.astype(np.int64)
+        per_table = int(lora_elems.sum()) * e
+        self.tables = max(1, math.ceil((1 << 30) / per_table))
+        self.copies = 64
+        # one flat buffer per table: LoRA k's A_k then B_k, compact
+        offs = np.concatenate([[0], np.cumsum(lora_elems)])[:-1]
+        self.W = wl.device_normal((self.tables, int(lora_elems.sum())), 1.0, self.dtype, 6100)
+        # scale each LoRA's values to a unit-variance term: A by h_in^-1/2, B by r^-1/2
+        for k in range(self.n):
+            r, o = int(self.ranks_h[k]), int(offs[k])
+            self.W[:, o: o + self.h_in * r].mul_(self.h_in ** -0.5)
+            self.W[:, o + self.h_in * r: o + (self.h_in + self.h_out) * r].mul_(r ** -0.5)
+        base = self.W.data_ptr() + torch.arange(self.tables, dtype=torch.int64, device="cuda")[:, None] \
+            * (int(lora_elems.sum()) * e)
+        a_off = torch.from_numpy(offs * e).cuda()
+        b_off = torch.from_numpy((offs + self.h_in * self.ranks_h.astype(np.int64)) * e).cuda()
+        self.A_tab = (base + a_off[None, :]).contiguous()
+        self.B_tab = (base + b_off[None, :]).contiguous()
+        self.offs = offs
+        self.X = wl.device_normal((self.copies, self.n, self.h_in), 1.0, self.dtype, 6101)
+        self.Y = wl.device_normal((self.copies, self.n, self.h_out), 1.0, self.dtype, 6102)
+        self.seg_h = np.arange(self.n + 1, dtype=np.int32)
+        self.lidx_h = np.arange(self.n, dtype=np.int32)
+        self.seg = torch.from_numpy(self.seg_h).cuda()
+        self.lidx = torch.from_numpy(self.lidx_h).cuda()
+        self.ranks = torch.from_numpy(self.ranks_h).cuda()
+        self.scales = torch.from_numpy(self.scales_h).cuda()
+        self.problem = sg.make_problem(self.dtype, self.n, self.h_in, self.h_out, self.R, self.n, self.n, 1,
+                                       variant, splits)
+        self.ws = sg.new_workspace(self.problem)
+        self.bytes = e * (int(lora_elems.sum()) + self.n * self.h_in + 2 * self.n * self.h_out)
+        self.rows_per_step = self.n
+        self.calls_per_step = 1
+        self.fn = sg.load_library().sgmv_lora_apply_batched
+        pb = ctypes.byref(self.problem)
+        self.args, self.keep = [], []
+        for c in range(max(self.tables, self.copies)):
+            t, x = c % self.tables, c % self.copies
+            pj = (sg.sgmv_projection_t * 1)(sg.sgmv_projection_t(
+                self.A_tab[t].data_ptr(), self.B_tab[t].data_ptr(), self.Y[x].data_ptr(),
+                self.ranks.data_ptr(), self.scales.data_ptr()))
+            self.keep.append(pj)
+            self.args.append((pb, self.X[x].data_ptr(), pj, 1, self.seg.data_ptr(), self.lidx.data_ptr(), None,
+                              self.ws.data_ptr(), self.ws.numel()))
+        torch.cuda.synchronize()
+
+    def step(self, c, stream):
+        st = self.fn(*self.args[c % len(self.args)], stream)
+        if st != 0:
+            raise RuntimeError(self.sg.sgmv_status_str(st))
+
+    def check_sample(self, calls=2):
+        import numpy as np
+        import oracle
+        torch = self.torch
+        worst = 0.0
+        sid = torch.cuda.current_stream().cuda_stream
+        for c in range(calls):
+            t, x = c % self.tables, c % self.copies
+            Xh, Y0 = _bits(self.X[x]), _bits(self.Y[x])
+            Wt = _bits(self.W[t])
+            A, B = [], []
+            for k in range(self.n):
+                r, o = int(self.ranks_h[k]), int(self.offs[k])
+                A.append(Wt[o: o + self.h_in * r].reshape(self.h_in, r))
+                B.append(Wt[o + self.h_in * r: o + (self.h_in + self.h_out) * r].reshape(r, self.h_out))
+            self.step(c, sid)
+            torch.cuda.synchronize()
+            got = oracle.decode(_bits(self.Y[x]), self.dtype)
+            ref = oracle.sgmv_apply(self.dtype, Xh, A, B, self.seg_h, self.lidx_h, Y0, scales=self.scales_h,
+                                    rank=self.R)
+            worst = max(worst, float((np.abs(got - ref) / (1e-3 + 1e-2 * np.abs(ref))).max()))
+        if worst > 1.0:
+            raise AssertionError(f"bench parity check failed: max err/bound {worst:.3f}")
+        return worst
+
+    def config(self):
+        return {"workload": self.name, "h_in": self.h_in, "h_out": self.h_out, "max_rank": self.R,
+                "ranks": self.ranks_h.tolist(), "scaled": True, "batch_rows": self.n, "segments": self.n,
+                "distinct_loras": self.n, "physical_tables": self.tables, "xy_copies": self.copies,
                 "algorithmic_bytes_per_step": self.bytes}
 
 
@@ -589,7 +696,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None, help="timed steps (default 2000; 20 for a forward)")
     ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default 200; 3 for a forward)")
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=SINGLE_WORKLOADS + MODEL_WORKLOADS)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=SINGLE_WORKLOADS + MODEL_WORKLOADS + HET_WORKLOADS)
     ap.add_argument("--variant", choices=["auto", "vector", "fused", "mfma"], default="auto")
     ap.add_argument("--splits", type=int, default=0, help="workgroups per segment block (0 = automatic)")
     ap.add_argument("--no-batch", action="store_true",
@@ -633,7 +740,9 @@ def main():
     model = args.workload in MODEL_WORKLOADS
     K = args.steps if args.steps is not None else (20 if model else 2000)
     W = args.warmup if args.warmup is not None else (3 if model else 200)
-    if model:
+    if args.workload in HET_WORKLOADS:
+        bench = MixedRankBench(args.workload, variant=variant, splits=args.splits)
+    elif model:
         bench = ModelForwardBench(args.workload, variant=variant, splits=args.splits,
                                   batch_projections=not args.no_batch, row_map=args.row_map)
     else:

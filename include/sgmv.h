@@ -192,11 +192,30 @@ sgmv_status_t sgmv_lora_apply(const sgmv_problem_t* problem, const void* X,
                               size_t ws_bytes, void* stream);
 
 /* One projection of a batched apply: its own LoRA tables and output.  All
- * three pointers are device pointers, as in sgmv_lora_apply. */
+ * pointers are device pointers, as in sgmv_lora_apply.
+ *
+ * Heterogeneous ranks (ranks != NULL).  The Punica discussion page
+ * ("Punica: Serving multiple LoRA finetuned LLM as one", the question on LoRAs
+ * with different ranks) answers that padding every LoRA to one rank costs
+ * little because the kernels are not compute bound.  Here the padding is
+ * virtual: LoRA k keeps its own rank r_k = ranks[k] (a multiple of 8 in
+ * [0, problem->rank]; 0 means the LoRA adds nothing) and its compact storage,
+ * A_k [h_in, r_k] and B_k [r_k, h_out] row-major, and the kernels treat ranks
+ * r_k .. problem->rank - 1 as zero without reading them.  problem->rank is the
+ * largest rank (the compiled tile width).  A LoRA of rank 0 may have null
+ * table entries; rank values outside [0, problem->rank] are clamped and rounded
+ * down to a multiple of 8 (not an error: the values live on the device).
+ *
+ * Per-LoRA scale (scales != NULL): the term becomes
+ * scales[k] * (x @ A_k) @ B_k, the usual alpha / r factor of LoRA, which is
+ * otherwise folded into B_k by the caller.  It multiplies the fp32
+ * intermediate x @ A_k before the expand. */
 typedef struct sgmv_projection {
-  const void* const* A_ptrs;  /* [num_loras] pointers to A_k [h_in, rank] */
-  const void* const* B_ptrs;  /* [num_loras] pointers to B_k [rank, h_out] */
+  const void* const* A_ptrs;  /* [num_loras] pointers to A_k [h_in, r_k] */
+  const void* const* B_ptrs;  /* [num_loras] pointers to B_k [r_k, h_out] */
   void* Y;                    /* [n_rows, h_out], read-modify-write */
+  const int32_t* ranks;       /* NULL (every r_k = problem->rank) or [num_loras] int32 */
+  const float* scales;        /* NULL (every scale 1) or [num_loras] fp32 */
 } sgmv_projection_t;
 
 #define SGMV_MAX_PROJECTIONS 4

@@ -66,7 +66,7 @@ def _bind(path: str):
     lib.oracle_sgmv_expand.argtypes = [ctypes.c_int, i32, i32, i32, p, p, i32, p, p, i32, p, p,
                                        p, ctypes.c_int]
     lib.oracle_sgmv_expand.restype = ctypes.c_int
-    lib.oracle_sgmv_apply.argtypes = [ctypes.c_int, i32, i32, i32, i32, p, p, p, i32, p, p, i32,
+    lib.oracle_sgmv_apply.argtypes = [ctypes.c_int, i32, i32, i32, i32, p, p, p, p, p, i32, p, p, i32,
                                       p, p, p, p, ctypes.c_int]
     lib.oracle_sgmv_apply.restype = ctypes.c_int
     return lib
@@ -173,13 +173,33 @@ def sgmv_expand(dtype, V, B, seg_indptr, lora_idx, Y0, *, row_mask=None, nthread
     return Y
 
 
-def sgmv_apply(dtype, X, A, B, seg_indptr, lora_idx, Y0, *, row_mask=None, nthreads=0,
-               want_v=False):
-    """fp64 Y = Y0 + per-row (x_i @ A_k) @ B_k.  Returns Y, or (Y, V) with ``want_v``."""
+def sgmv_apply(dtype, X, A, B, seg_indptr, lora_idx, Y0, *, scales=None, rank=None, row_mask=None,
+               nthreads=0, want_v=False):
+    """fp64 Y = Y0 + per-row s_k * (x_i @ A_k) @ B_k.  Returns Y, or (Y, V) with ``want_v``.
+
+    Each A[k] is [h_in, r_k] and B[k] is [r_k, h_out]; the ranks may differ
+    (rank 0: the LoRA adds nothing).  ``rank`` is the width of V (default: the
+    largest r_k); ``scales`` (default all 1) gives s_k per LoRA."""
     X, Y0 = _u16(X), _u16(Y0)
     n, h_in = X.shape
     h_out = Y0.shape[1]
-    rank = _u16(A[0]).shape[1]
+    # Ranks of the LoRAs that a non-empty segment uses (the others are never
+    # read and may be placeholders).
+    sp0, li0 = _i32(seg_indptr), _i32(lora_idx)
+    # (Ids out of range and malformed segments are left for the C side to reject.)
+    used = sorted({int(li0[s]) for s in range(min(len(li0), len(sp0) - 1))
+                   if sp0[s + 1] > sp0[s] and 0 <= li0[s] < len(A)})
+    rk = np.zeros(len(A), dtype=np.int32)
+    for k in used:
+        a, b = _u16(A[k]), _u16(B[k])
+        if a.ndim != 2 or b.ndim != 2 or a.shape[0] != h_in or b.shape[1] != h_out or a.shape[1] != b.shape[0]:
+            raise ValueError(f"LoRA {k}: A {a.shape} and B {b.shape} are not [{h_in}, r] and [r, {h_out}]")
+        rk[k] = a.shape[1]
+    rank = int(rank if rank is not None else max(int(rk.max(initial=0)), 1))
+    uniform = all(rk[k] == rank for k in used)
+    sc = None if scales is None else np.ascontiguousarray(scales, dtype=np.float64)
+    if sc is not None and sc.shape != (len(A),):
+        raise ValueError("scales must hold one value per LoRA")
     sp, li = _i32(seg_indptr), _i32(lora_idx)
     ta, ka = _table(A)
     tb, kb = _table(B)
@@ -188,7 +208,8 @@ def sgmv_apply(dtype, X, A, B, seg_indptr, lora_idx, Y0, *, row_mask=None, nthre
     Y = np.full((n, h_out), np.nan)
     V = np.full((n, rank), np.nan) if want_v else None
     m, mp = _mask(row_mask, n)
-    rc = _load().oracle_sgmv_apply(DTYPES[dtype], n, h_in, h_out, rank, _ptr(X),
+    rc = _load().oracle_sgmv_apply(DTYPES[dtype], n, h_in, h_out, rank, 0 if uniform else _ptr(rk),
+                                   0 if sc is None else _ptr(sc), _ptr(X),
                                    ctypes.addressof(ta), ctypes.addressof(tb), len(ka), _ptr(sp),
                                    _ptr(li), len(li), _ptr(Y0), mp, _ptr(Y),
                                    _ptr(V) if want_v else 0, nthreads)

@@ -106,13 +106,13 @@ static void row_shrink(int dtype, int32_t h_in, int32_t rank, const uint16_t* x_
   }
 }
 
-/* y[c] = y0[c] + sum_j v[j] * B[j, c], j ascending. */
+/* y[c] = y0[c] + scale * sum_j v[j] * B[j, c], j ascending. */
 static void row_expand(int dtype, int32_t rank, int32_t h_out, const double* v,
-                       const uint16_t* b, const uint16_t* y0_row, double* y) {
+                       const uint16_t* b, const uint16_t* y0_row, double scale, double* y) {
   for (int32_t c = 0; c < h_out; ++c) {
     double acc = 0.0;
     for (int32_t j = 0; j < rank; ++j) acc += v[j] * decode(dtype, b[(int64_t)j * h_out + c]);
-    y[c] = decode(dtype, y0_row[c]) + acc;
+    y[c] = decode(dtype, y0_row[c]) + scale * acc;
   }
 }
 
@@ -161,26 +161,39 @@ int oracle_sgmv_expand(int dtype, int32_t n_rows, int32_t h_out, int32_t rank, c
       for (int32_t c = 0; c < h_out; ++c) y[c] = decode(dtype, y0[c]);
       continue;
     }
-    row_expand(dtype, rank, h_out, V + (int64_t)i * rank, B[lora_idx[s]], y0, y);
+    row_expand(dtype, rank, h_out, V + (int64_t)i * rank, B[lora_idx[s]], y0, 1.0, y);
   }
   free(seg_of_row);
   return 0;
 }
 
 /*
- * Whole LoRA term: Y[i, :] = Y0[i, :] + (X[i, :] @ A_k) @ B_k, k the LoRA of
- * row i's segment, the intermediate kept in fp64.  V (nullable) receives the
- * fp64 intermediate of covered rows.  Uncovered rows get Y = Y0 exactly.
- * Returns 0, or -1 on invalid metadata or allocation failure.
+ * Whole LoRA term: Y[i, :] = Y0[i, :] + s_k * (X[i, :] @ A_k) @ B_k, k the
+ * LoRA of row i's segment, the intermediate kept in fp64.
+ *   ranks  (nullable) rank r_k of each LoRA: A_k is [h_in, r_k] and B_k is
+ *          [r_k, h_out]; NULL means every LoRA has rank `rank`.  A LoRA of
+ *          rank 0 adds nothing.  The Punica discussion page ("Punica: Serving
+ *          multiple LoRA finetuned LLM as one", the question on LoRAs with
+ *          different ranks) treats such LoRAs as padded to one rank: padding
+ *          with zero columns of A and zero rows of B leaves the term unchanged,
+ *          which is what a rank table expresses.
+ *   scales (nullable) s_k of each LoRA; NULL means 1.
+ * V (nullable, [n_rows, rank]) receives the unscaled fp64 intermediate of
+ * covered rows, zero past r_k.  Uncovered rows get Y = Y0 exactly.
+ * Returns 0, or -1 on invalid metadata, a rank outside [0, rank], or
+ * allocation failure.
  */
 int oracle_sgmv_apply(int dtype, int32_t n_rows, int32_t h_in, int32_t h_out, int32_t rank,
-                      const uint16_t* X, const uint16_t* const* A, const uint16_t* const* B,
-                      int32_t num_loras, const int32_t* seg_indptr, const int32_t* lora_idx,
-                      int32_t num_segs, const uint16_t* Y0, const uint8_t* row_mask, double* Y,
-                      double* V, int nthreads) {
+                      const int32_t* ranks, const double* scales, const uint16_t* X,
+                      const uint16_t* const* A, const uint16_t* const* B, int32_t num_loras,
+                      const int32_t* seg_indptr, const int32_t* lora_idx, int32_t num_segs,
+                      const uint16_t* Y0, const uint8_t* row_mask, double* Y, double* V,
+                      int nthreads) {
   int32_t* seg_of_row = row_segments(n_rows, seg_indptr, lora_idx, num_segs, num_loras);
   if (!seg_of_row) return -1;
-  if (rank <= 0 || rank > 4096) {
+  int bad = rank <= 0 || rank > 4096;
+  for (int32_t k = 0; ranks && k < num_loras; ++k) bad |= ranks[k] < 0 || ranks[k] > rank;
+  if (bad) {
     free(seg_of_row);
     return -1;
   }
@@ -197,10 +210,11 @@ int oracle_sgmv_apply(int dtype, int32_t n_rows, int32_t h_in, int32_t h_out, in
     }
     double v[4096];
     const int32_t k = lora_idx[s];
-    row_shrink(dtype, h_in, rank, X + (int64_t)i * h_in, A[k], v);
-    row_expand(dtype, rank, h_out, v, B[k], y0, y);
+    const int32_t rk = ranks ? ranks[k] : rank;
+    row_shrink(dtype, h_in, rk, X + (int64_t)i * h_in, A[k], v);
+    row_expand(dtype, rk, h_out, v, B[k], y0, scales ? scales[k] : 1.0, y);
     if (V)
-      for (int32_t j = 0; j < rank; ++j) V[(int64_t)i * rank + j] = v[j];
+      for (int32_t j = 0; j < rank; ++j) V[(int64_t)i * rank + j] = j < rk ? v[j] : 0.0;
   }
   free(seg_of_row);
   return 0;

@@ -60,7 +60,8 @@ class sgmv_plan_info_t(ctypes.Structure):
 
 
 class sgmv_projection_t(ctypes.Structure):
-    _fields_ = [("A_ptrs", ctypes.c_void_p), ("B_ptrs", ctypes.c_void_p), ("Y", ctypes.c_void_p)]
+    _fields_ = [("A_ptrs", ctypes.c_void_p), ("B_ptrs", ctypes.c_void_p), ("Y", ctypes.c_void_p),
+                ("ranks", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
 
 
 _lib = None
@@ -241,11 +242,14 @@ def sgmv_lora_apply(problem, X, A_ptrs, B_ptrs, Y, seg_indptr, lora_idx, ws, str
 
 
 def sgmv_lora_apply_batched(problem, X, projections, seg_indptr, lora_idx, ws, row_idx=None, stream=None):
-    """Y_p[row(i)] += (X[row(i)] @ A_{p,k}) @ B_{p,k} for each (A_ptrs, B_ptrs, Y) in
-    `projections` (up to SGMV_MAX_PROJECTIONS), one call; asynchronous.  `row_idx`
-    (optional device int32 [n_rows], e.g. the builder's perm) maps sorted row i to
-    row row_idx[i] of X and Y.  `ws` must hold batched_workspace_bytes(problem,
-    len(projections)) bytes."""
+    """Y_p[row(i)] += s_{p,k} * (X[row(i)] @ A_{p,k}) @ B_{p,k} for each projection in
+    `projections` (up to SGMV_MAX_PROJECTIONS), one call; asynchronous.  A projection
+    is (A_ptrs, B_ptrs, Y) or (A_ptrs, B_ptrs, Y, ranks, scales): `ranks` (device
+    int32 [num_loras] or None) gives each LoRA's own rank (compact A_k [h_in, r_k],
+    B_k [r_k, h_out]; problem.rank is the largest), `scales` (device float32
+    [num_loras] or None) the factor of each LoRA's term.  `row_idx` (optional device
+    int32 [n_rows], e.g. the builder's perm) maps sorted row i to row row_idx[i] of
+    X and Y.  `ws` must hold batched_workspace_bytes(problem, len(projections)) bytes."""
     import torch
     dt = _torch_dtype(problem)
     _need(X, "X", dt)
@@ -253,10 +257,13 @@ def sgmv_lora_apply_batched(problem, X, projections, seg_indptr, lora_idx, ws, r
     _need(row_idx, "row_idx", torch.int32)
     _need(ws, "ws")
     arr = (sgmv_projection_t * max(1, len(projections)))()
-    for i, (A_ptrs, B_ptrs, Y) in enumerate(projections):
+    for i, pj in enumerate(projections):
+        A_ptrs, B_ptrs, Y = pj[:3]
+        ranks, scales = (tuple(pj[3:]) + (None, None))[:2]
         _need(Y, f"Y[{i}]", dt)
         _need(A_ptrs, f"A_ptrs[{i}]", torch.int64); _need(B_ptrs, f"B_ptrs[{i}]", torch.int64)
-        arr[i] = sgmv_projection_t(_ptr(A_ptrs), _ptr(B_ptrs), _ptr(Y))
+        _need(ranks, f"ranks[{i}]", torch.int32); _need(scales, f"scales[{i}]", torch.float32)
+        arr[i] = sgmv_projection_t(_ptr(A_ptrs), _ptr(B_ptrs), _ptr(Y), _ptr(ranks), _ptr(scales))
     st = load_library().sgmv_lora_apply_batched(ctypes.byref(problem), _ptr(X), arr, len(projections),
                                                 _ptr(seg_indptr), _ptr(lora_idx), _ptr(row_idx), _ptr(ws),
                                                 ws.numel() * ws.element_size() if ws is not None else 0,
@@ -280,6 +287,13 @@ def pointer_table(stacked) -> "torch.Tensor":
     stride = stacked[0].numel() * stacked.element_size() if P else 0
     return (torch.arange(P, device=stacked.device, dtype=torch.int64) * stride
             + stacked.data_ptr()).contiguous()
+
+
+def pointer_list(tensors, device="cuda") -> "torch.Tensor":
+    """Device int64 table of the data pointers of separately allocated per-LoRA
+    tensors (None: a null entry, allowed for a LoRA of rank 0)."""
+    import torch
+    return torch.tensor([0 if t is None else t.data_ptr() for t in tensors], dtype=torch.int64, device=device)
 
 
 def new_workspace(problem: sgmv_problem_t, device="cuda"):

@@ -329,6 +329,16 @@ size_t apply_ws_bytes(const sgmv_problem_t& p) {
   return std::max({two_launch, one_launch, matrix});
 }
 
+sgmv::Projection kernel_projection(const sgmv_projection_t& pj) {
+  sgmv::Projection k{};
+  k.A_ptrs = reinterpret_cast<const uint64_t*>(pj.A_ptrs);
+  k.B_ptrs = reinterpret_cast<const uint64_t*>(pj.B_ptrs);
+  k.Y = static_cast<uint16_t*>(pj.Y);
+  k.ranks = pj.ranks;
+  k.scales = pj.scales;
+  return k;
+}
+
 // sgmv_lora_apply for num_proj projections that share X, the shapes and the
 // segments.  Projection i uses the workspace slice [i*stride, i*stride + need).
 sgmv_status_t apply(const sgmv_problem_t& p, const void* X, const sgmv_projection_t* pj, int np,
@@ -349,11 +359,7 @@ sgmv_status_t apply(const sgmv_problem_t& p, const void* X, const sgmv_projectio
     }
     sgmv::DecodeParams q{};
     q.X = static_cast<const uint16_t*>(X);
-    for (int i = 0; i < np; ++i) {
-      q.proj[i].A_ptrs = reinterpret_cast<const uint64_t*>(pj[i].A_ptrs);
-      q.proj[i].B_ptrs = reinterpret_cast<const uint64_t*>(pj[i].B_ptrs);
-      q.proj[i].Y = static_cast<uint16_t*>(pj[i].Y);
-    }
+    for (int i = 0; i < np; ++i) q.proj[i] = kernel_projection(pj[i]);
     q.seg_indptr = seg_indptr;
     q.lora_idx = lora_idx;
     q.row_idx = row_idx;
@@ -379,11 +385,7 @@ sgmv_status_t apply(const sgmv_problem_t& p, const void* X, const sgmv_projectio
     sgmv::MfmaParams q = mfma_params(p, m, seg_indptr, lora_idx);
     q.row_idx = row_idx;
     q.X = static_cast<const uint16_t*>(X);
-    for (int i = 0; i < np; ++i) {
-      q.proj[i].A_ptrs = reinterpret_cast<const uint64_t*>(pj[i].A_ptrs);
-      q.proj[i].B_ptrs = reinterpret_cast<const uint64_t*>(pj[i].B_ptrs);
-      q.proj[i].Y = static_cast<uint16_t*>(pj[i].Y);
-    }
+    for (int i = 0; i < np; ++i) q.proj[i] = kernel_projection(pj[i]);
     q.partials = reinterpret_cast<float*>(ws + SGMV_WS_COUNTER_BYTES);
     q.V = reinterpret_cast<float*>(ws + SGMV_WS_COUNTER_BYTES + m.partial_bytes);
     q.proj_stride = (int64_t)(stride / sizeof(float));
@@ -403,6 +405,8 @@ sgmv_status_t apply(const sgmv_problem_t& p, const void* X, const sgmv_projectio
     q.A_ptrs = reinterpret_cast<const uint64_t*>(pj[i].A_ptrs);
     q.B_ptrs = reinterpret_cast<const uint64_t*>(pj[i].B_ptrs);
     q.Y = static_cast<uint16_t*>(pj[i].Y);
+    q.ranks = pj[i].ranks;
+    q.scales = pj[i].scales;
     q.V = reinterpret_cast<float*>(wsi + need);
     hipError_t e = sgmv::launch_vec(p.dtype, p.rank, v.rb, sgmv::kModeShrink, q, s);
     if (e != hipSuccess) return SGMV_ERR_HIP;
@@ -607,7 +611,7 @@ sgmv_status_t sgmv_query_plan(const sgmv_problem_t* p, sgmv_plan_info_t* info) {
 sgmv_status_t sgmv_lora_apply(const sgmv_problem_t* p, const void* X, const void* const* A_ptrs,
                               const void* const* B_ptrs, void* Y, const int32_t* seg_indptr,
                               const int32_t* lora_idx, void* ws, size_t ws_bytes, void* stream) {
-  const sgmv_projection_t one{A_ptrs, B_ptrs, Y};
+  const sgmv_projection_t one{A_ptrs, B_ptrs, Y, nullptr, nullptr};
   return sgmv_lora_apply_batched(p, X, &one, 1, seg_indptr, lora_idx, nullptr, ws, ws_bytes, stream);
 }
 
@@ -625,6 +629,8 @@ sgmv_status_t sgmv_lora_apply_batched(const sgmv_problem_t* p, const void* X,
     const sgmv_projection_t& pj = projections[i];
     if (!pj.A_ptrs || !pj.B_ptrs || !pj.Y) return SGMV_ERR_INVALID_ARG;
     if (!aligned16(pj.Y) || !aligned8(pj.A_ptrs) || !aligned8(pj.B_ptrs)) return SGMV_ERR_UNSUPPORTED;
+    if ((reinterpret_cast<uintptr_t>(pj.ranks) | reinterpret_cast<uintptr_t>(pj.scales)) % 4 != 0)
+      return SGMV_ERR_UNSUPPORTED;
   }
   if (!ws) return SGMV_ERR_WORKSPACE;
   if (!aligned16(ws)) return SGMV_ERR_UNSUPPORTED;

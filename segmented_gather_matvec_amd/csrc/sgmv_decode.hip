@@ -87,8 +87,10 @@ constexpr int log2_groups() {
 }
 
 // SMALL: at most 64 LoRAs (pointer tables fetched one entry per lane).
-// MAP: rows of X / Y are looked up in a row map.
-template <class T, int R, int RB, bool SMALL, bool MAP>
+// EXT: the extended arguments may be set: a row map (rows of X / Y looked up),
+// per-LoRA ranks (compact A_k [h_in, r_k], B_k [r_k, h_out]; ranks r_k..R-1
+// are zero) and per-LoRA scales.  Without EXT the kernel carries none of it.
+template <class T, int R, int RB, bool SMALL, bool EXT>
 __global__ __launch_bounds__(kThreads) void sgmv_decode_kernel(DecodeParams p) {
   constexpr int JG = R / 8;                  // 128-bit vectors per row of A_k
   constexpr int B0 = log2_groups<R>();
@@ -140,9 +142,15 @@ __global__ __launch_bounds__(kThreads) void sgmv_decode_kernel(DecodeParams p) {
   // parallel with the segment metadata instead of after it: the LoRA id then
   // selects its pointers from registers, saving one dependent memory trip.
   uint64_t a_lane = 0, b_lane = 0;
+  int rk_lane = R;
+  float sk_lane = 1.f;
   if (SMALL && lane < p.num_loras) {
     a_lane = pr.A_ptrs[lane];
     b_lane = pr.B_ptrs[lane];
+    if constexpr (EXT) {
+      if (pr.ranks) rk_lane = pr.ranks[lane];
+      if (pr.scales) sk_lane = pr.scales[lane];
+    }
   }
   const Unit un = resolve_unit<RB>(p.seg_indptr, p.lora_idx, p.num_segs, p.num_loras, p.n_rows,
                                    p.direct_units, unit);
@@ -153,12 +161,26 @@ __global__ __launch_bounds__(kThreads) void sgmv_decode_kernel(DecodeParams p) {
 
   const uint16_t* Ak;
   const uint16_t* Bk;
+  int rk = R;      // rank of this unit's LoRA (row stride of A_k)
+  float sk = 1.f;  // scale of its term
   if constexpr (SMALL) {
     Ak = reinterpret_cast<const uint16_t*>(readlane_u64(a_lane, un.k));
     Bk = reinterpret_cast<const uint16_t*>(readlane_u64(b_lane, un.k));
+    if constexpr (EXT) {
+      rk = __builtin_amdgcn_readlane(rk_lane, un.k);
+      sk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sk_lane), un.k));
+    }
   } else {
     Ak = reinterpret_cast<const uint16_t*>(pr.A_ptrs[un.k]);
     Bk = reinterpret_cast<const uint16_t*>(pr.B_ptrs[un.k]);
+    if constexpr (EXT) {
+      if (pr.ranks) rk = pr.ranks[un.k];
+      if (pr.scales) sk = pr.scales[un.k];
+    }
+  }
+  if constexpr (EXT) {
+    rk = lora_rank<R>(rk);
+    if (rk == 0) return;  // the LoRA adds nothing (uniform over the unit)
   }
   const int h0 = g * p.kc;
   const int h1 = p.h_in < h0 + p.kc ? p.h_in : h0 + p.kc;
@@ -167,18 +189,23 @@ __global__ __launch_bounds__(kThreads) void sgmv_decode_kernel(DecodeParams p) {
   // Rows of X / Y.  With a row map, lane l looks up the row behind sorted row
   // r0 + l once, ahead of the streaming loads (L <= RB <= 64 rows), and every
   // other lane takes it from there.
+  const bool map = EXT && p.row_idx != nullptr;
   int prow = r0 + lane;
-  if constexpr (MAP) prow = p.row_idx[r0 + (lane < L ? lane : L - 1)];
-  const uint16_t* Xr = p.X + (int64_t)(MAP ? __builtin_amdgcn_readfirstlane(prow) : r0) * p.h_in;
+  if (map) prow = p.row_idx[r0 + (lane < L ? lane : L - 1)];
+  const uint16_t* Xr = p.X + (int64_t)(map ? __builtin_amdgcn_readfirstlane(prow) : r0) * p.h_in;
 
   // ---------------- all loads, issued up front ----------------
   // Shrink: thread t owns ranks (t % JG)*8..+7 of rows h0 + t/JG + q*HS.
+  // With a rank below R, A_k rows are rk wide and the lanes of ranks >= rk
+  // load nothing new (their address is clamped) and compute nothing.
   const int jg = t % JG;
+  const bool jg_ok = !EXT || jg * 8 < rk;
+  const int a_stride = EXT ? rk : R;
   u32x4 av[NA];
 #pragma unroll
   for (int q = 0; q < NA; ++q) {
     const int h = h0 + t / JG + q * HS;
-    av[q] = load_stream(Ak + (h < h1 ? (int64_t)h * R + jg * 8 : 0));
+    av[q] = load_stream(Ak + (h < h1 && jg_ok ? (int64_t)h * a_stride + jg * 8 : 0));
   }
   uint16_t xs[RB == 1 ? NA : 1];
   u32x4 xv[NXV];
@@ -195,7 +222,7 @@ __global__ __launch_bounds__(kThreads) void sgmv_decode_kernel(DecodeParams p) {
       const int x = t + kThreads * q;
       const int i = xvr > 0 ? x / xvr : 0, c = x - i * xvr;
       const int xi = x < L * xvr ? i : 0;
-      const int64_t row = MAP ? __shfl(prow, xi) : r0 + xi;
+      const int64_t row = map ? __shfl(prow, xi) : r0 + xi;
       xv[q] = load_stream(p.X + row * p.h_in + (x < L * xvr ? h0 + c * 8 : 0));
     }
   }
@@ -206,15 +233,17 @@ __global__ __launch_bounds__(kThreads) void sgmv_decode_kernel(DecodeParams p) {
   const bool col_ok = col < c1;
   u32x4 bv[NB];
 #pragma unroll
-  for (int m = 0; m < NB; ++m)
-    bv[m] = load_stream(Bk + (col_ok ? (int64_t)(jq + JQ * m) * p.h_out + col : 0));
+  for (int m = 0; m < NB; ++m) {
+    const bool ok = col_ok && (!EXT || jq + JQ * m < rk);  // rows of B_k past rk do not exist
+    bv[m] = load_stream(Bk + (ok ? (int64_t)(jq + JQ * m) * p.h_out + col : 0));
+  }
   u32x4 yv[NY];
   int yrow[NY];  // row of Y of the rows i = jq + n*JQ (kept for the stores)
 #pragma unroll
   for (int n = 0; n < NY; ++n) {
     const int i = jq + JQ * n;
     const int yi = col_ok && i < L ? i : 0;
-    yrow[n] = MAP ? __shfl(prow, yi) : r0 + yi;
+    yrow[n] = map ? __shfl(prow, yi) : r0 + yi;
     yv[n] = load_stream(pr.Y + (int64_t)yrow[n] * p.h_out + (col_ok && i < L ? col : 0));
   }
 
@@ -239,7 +268,7 @@ __global__ __launch_bounds__(kThreads) void sgmv_decode_kernel(DecodeParams p) {
 #pragma unroll
   for (int q = 0; q < NA; ++q) {
     const int hl = t / JG + q * HS;  // row inside the chunk
-    if (h0 + hl < h1) {
+    if (h0 + hl < h1 && jg_ok) {
       float af[8];
       unpack8<T>(av[q], af);
 #pragma unroll
@@ -331,13 +360,18 @@ __global__ __launch_bounds__(kThreads) void sgmv_decode_kernel(DecodeParams p) {
       for (int pp = 0; pp < pn; ++pp) vsum += lds_stage[pp * n_out + t];
     __syncthreads();
   }
-  if (t < n_out) lds_v[t] = vsum;
+  if (t < n_out) lds_v[t] = EXT ? vsum * sk : vsum;
   __syncthreads();
 
   // ---------------- expand ----------------
   float bf[NB][8];
 #pragma unroll
-  for (int m = 0; m < NB; ++m) unpack8<T>(bv[m], bf[m]);
+  for (int m = 0; m < NB; ++m) {
+    unpack8<T>(bv[m], bf[m]);
+    if (EXT && jq + JQ * m >= rk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) bf[m][e] = 0.f;
+  }
 #pragma unroll
   for (int i = 0; i < RB; ++i) {
     if (i < L) {
@@ -371,23 +405,25 @@ hipError_t launch_t(const DecodeParams& p, int num_proj, hipStream_t stream) {
   const unsigned grid = units * (unsigned)p.splits;
   if (grid == 0 || num_proj <= 0) return hipSuccess;
   const bool small = p.num_loras <= 64;
+  bool ext = p.row_idx != nullptr;
+  for (int i = 0; i < num_proj; ++i) ext = ext || p.proj[i].ranks || p.proj[i].scales;
   void (*kernel)(DecodeParams) =
-      p.row_idx ? (small ? sgmv_decode_kernel<T, R, RB, true, true> : sgmv_decode_kernel<T, R, RB, false, true>)
-                : (small ? sgmv_decode_kernel<T, R, RB, true, false> : sgmv_decode_kernel<T, R, RB, false, false>);
+      ext ? (small ? sgmv_decode_kernel<T, R, RB, true, true> : sgmv_decode_kernel<T, R, RB, false, true>)
+          : (small ? sgmv_decode_kernel<T, R, RB, true, false> : sgmv_decode_kernel<T, R, RB, false, false>);
   hipLaunchKernelGGL(kernel, dim3(grid, num_proj), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
-template <class T, int R, int RB, bool SMALL, bool MAP>
+template <class T, int R, int RB, bool SMALL, bool EXT>
 int per_cu_t() {
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &n, reinterpret_cast<const void*>(&sgmv_decode_kernel<T, R, RB, SMALL, MAP>), kThreads, 0) != hipSuccess)
+          &n, reinterpret_cast<const void*>(&sgmv_decode_kernel<T, R, RB, SMALL, EXT>), kThreads, 0) != hipSuccess)
     return 0;
   return n;
 }
 
-// The variants (pointer pool, row map) use the same registers and LDS within a
+// The variants (pointer pool, extended arguments) use the same registers and LDS within a
 // few VGPRs; the smallest of their occupancies is reported.
 template <class T, int R, int RB>
 int capacity_t() {

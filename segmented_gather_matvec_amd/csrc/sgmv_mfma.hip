@@ -81,7 +81,9 @@ __device__ inline void store_pair_transposed(uint16_t* dst, int stride, const u3
 // multiplied, the next stage's loads are in flight.
 constexpr int kKStage = 128;
 
-template <class T, int R, bool MAP>
+// EXT: the extended arguments may be set (row map, per-LoRA ranks and scales;
+// see the decode kernel).  Without EXT the kernel carries none of it.
+template <class T, int R, bool EXT>
 __global__ __launch_bounds__(kThreads) void sgmv_mfma_shrink_kernel(MfmaParams p) {
   constexpr int NT = R / 16;                // 16-wide rank tiles
   constexpr int JG = R / 8;                 // 128-bit vectors per row of A_k
@@ -117,12 +119,20 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_shrink_kernel(MfmaParams p
   if (un.L <= 0) return;
   const int L = un.L, r0 = un.r0;
   const uint16_t* Ak = reinterpret_cast<const uint16_t*>(pj.A_ptrs[un.k]);
+  // Rank of the LoRA: A_k rows are rk wide; ranks >= rk are zero.
+  int rk = R;
+  if constexpr (EXT) {
+    if (pj.ranks) rk = lora_rank<R>(pj.ranks[un.k]);
+    if (rk == 0) return;  // nothing to add (the expand skips the unit too)
+  }
+  const int a_stride = EXT ? rk : R;
   const int k0 = g * p.kc;
   const int k1 = p.h_in < k0 + p.kc ? p.h_in : k0 + p.kc;
   // Row this lane feeds into the MFMA A operand (rows past the segment re-read
   // its last row and are never stored).
   const int row = wave * 16 + ml;
-  const uint16_t* xrow = p.X + phys_row<MAP>(p.row_idx, r0 + (row < L ? row : L - 1)) * p.h_in;
+  const int srow = r0 + (row < L ? row : L - 1);
+  const uint16_t* xrow = p.X + (EXT && p.row_idx ? (int64_t)p.row_idx[srow] : (int64_t)srow) * p.h_in;
 
   // All loads of one stage, at clamped (valid) addresses; values past k1 are
   // zeroed where they are consumed.
@@ -131,9 +141,9 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_shrink_kernel(MfmaParams p
     for (int m = 0; m < NPAIR; ++m) {
       const int pr = t + kThreads * m;
       const int h = kk + (pr / JG) * 2, jg = pr % JG;
-      const bool ok = pr < PAIRS;
-      a[m][0] = load_stream(Ak + (ok && h < k1 ? (int64_t)h * R + jg * 8 : 0));
-      a[m][1] = load_stream(Ak + (ok && h + 1 < k1 ? (int64_t)(h + 1) * R + jg * 8 : 0));
+      const bool ok = pr < PAIRS && (!EXT || jg * 8 < rk);
+      a[m][0] = load_stream(Ak + (ok && h < k1 ? (int64_t)h * a_stride + jg * 8 : 0));
+      a[m][1] = load_stream(Ak + (ok && h + 1 < k1 ? (int64_t)(h + 1) * a_stride + jg * 8 : 0));
     }
 #pragma unroll
     for (int s = 0; s < MS; ++s) {
@@ -156,8 +166,9 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_shrink_kernel(MfmaParams p
       const int pr = t + kThreads * m;
       if (pr < PAIRS) {
         const int h = (pr / JG) * 2, jg = pr % JG;
-        store_pair_transposed(&lds_at[(jg * 8) * AST + h], AST, kk + h < k1 ? a[m][0] : z,
-                              kk + h + 1 < k1 ? a[m][1] : z);
+        const bool live = !EXT || jg * 8 < rk;
+        store_pair_transposed(&lds_at[(jg * 8) * AST + h], AST, live && kk + h < k1 ? a[m][0] : z,
+                              live && kk + h + 1 < k1 ? a[m][1] : z);
       }
     }
     __syncthreads();
@@ -215,6 +226,9 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_reduce_kernel(MfmaParams p
                                     p.direct_units64, unit);
   const int rows = un.L - part * kReduceRows;
   if (rows <= 0) return;
+  // Scale of the LoRA's term, applied to V (one multiply after the sum).
+  const float* scales = p.proj[blockIdx.y].scales;
+  const float sk = scales ? scales[un.k] : 1.f;
 #pragma unroll
   for (int o = 0; o < NO; ++o) {
     const int v4 = threadIdx.x + kThreads * o;
@@ -232,12 +246,12 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_reduce_kernel(MfmaParams p
       for (int u = 0; u < kBatch; ++u)
         if (k0 + u < p.ksplit) s += v[u];
     }
-    *reinterpret_cast<f32x4*>(V + off) = s;
+    *reinterpret_cast<f32x4*>(V + off) = s * sk;
   }
 }
 
 // ---------------------------------------------------------------- expand
-template <class T, int R, bool MAP>
+template <class T, int R, bool EXT>
 __global__ __launch_bounds__(kThreads) void sgmv_mfma_expand_kernel(MfmaParams p) {
   constexpr int K2 = 2 * R;            // virtual K: [V_hi | V_lo] against [B_k; B_k]
   constexpr int KSTEPS = K2 / 32;
@@ -279,6 +293,12 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_expand_kernel(MfmaParams p
   const int ch0 = grp * p.chunks_per_wg;
   const int ch1 = nchunks < ch0 + p.chunks_per_wg ? nchunks : ch0 + p.chunks_per_wg;
   const uint16_t* Bk = reinterpret_cast<const uint16_t*>(pj.B_ptrs[un.k]);
+  // Rank of the LoRA: B_k has rk rows; V's ranks >= rk are zero.
+  int rk = R;
+  if constexpr (EXT) {
+    if (pj.ranks) rk = lora_rank<R>(pj.ranks[un.k]);
+    if (rk == 0) return;  // Y keeps its value
+  }
   uint16_t* Ybase = pj.Y;
   const float* Vp = p.V + (int64_t)blockIdx.y * p.proj_stride;
   // Row of Y behind each tile row this lane loads and stores, looked up once
@@ -287,7 +307,8 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_expand_kernel(MfmaParams p
 #pragma unroll
   for (int u = 0; u < NYV; ++u) {
     const int rr = wave * 16 + (lane + 64 * u) / CV;
-    yrow[u] = (int)phys_row<MAP>(p.row_idx, r0 + (rr < L ? rr : 0));
+    const int srow = r0 + (rr < L ? rr : 0);
+    yrow[u] = EXT && p.row_idx ? p.row_idx[srow] : srow;
   }
 
   // Loads of one chunk (all lanes issue the same loads; addresses of lanes
@@ -298,7 +319,7 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_expand_kernel(MfmaParams p
     for (int m = 0; m < NBP; ++m) {
       const int pv = t + kThreads * m;
       const int j = (pv / CV) * 2, c = c0 + (pv % CV) * 8;
-      const bool ok = pv < R / 2 * CV && ch < ch1 && c < p.h_out;
+      const bool ok = pv < R / 2 * CV && ch < ch1 && c < p.h_out && (!EXT || j < rk);
       bv[m][0] = load_stream(Bk + (ok ? (int64_t)j * p.h_out + c : 0));
       bv[m][1] = load_stream(Bk + (ok ? (int64_t)(j + 1) * p.h_out + c : 0));
     }
@@ -351,7 +372,9 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_expand_kernel(MfmaParams p
       const int pr = t + kThreads * m;
       if (pr < R / 2 * CV) {
         const int j = (pr / CV) * 2, cl = (pr % CV) * 8;
-        store_pair_transposed(&lds_bt[cl * BST + j], BST, bv[m][0], bv[m][1]);
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        const bool live = !EXT || j < rk;  // rk is even, so j < rk covers row j + 1 too
+        store_pair_transposed(&lds_bt[cl * BST + j], BST, live ? bv[m][0] : z, live ? bv[m][1] : z);
       }
     }
     __syncthreads();
@@ -402,10 +425,12 @@ unsigned xcd_grid(unsigned items) { return kXcds * ((items + kXcds - 1) / kXcds)
 template <class T, int R>
 hipError_t launch_t(int stage, const MfmaParams& p, int np, hipStream_t s) {
   unsigned grid = 0;
+  bool ext = p.row_idx != nullptr;
+  for (int i = 0; i < np; ++i) ext = ext || p.proj[i].ranks || p.proj[i].scales;
   if (stage == 0) {
     grid = xcd_grid((unsigned)p.num_units64 * (unsigned)p.ksplit);
     if (grid && np > 0) {
-      if (p.row_idx)
+      if (ext)
         hipLaunchKernelGGL((sgmv_mfma_shrink_kernel<T, R, true>), dim3(grid, np), dim3(kThreads), 0, s, p);
       else
         hipLaunchKernelGGL((sgmv_mfma_shrink_kernel<T, R, false>), dim3(grid, np), dim3(kThreads), 0, s, p);
@@ -417,7 +442,7 @@ hipError_t launch_t(int stage, const MfmaParams& p, int np, hipStream_t s) {
     const int nchunks = (p.h_out + kCW - 1) / kCW;
     grid = xcd_grid((unsigned)p.num_units64 * (unsigned)((nchunks + p.chunks_per_wg - 1) / p.chunks_per_wg));
     if (grid && np > 0) {
-      if (p.row_idx)
+      if (ext)
         hipLaunchKernelGGL((sgmv_mfma_expand_kernel<T, R, true>), dim3(grid, np), dim3(kThreads), 0, s, p);
       else
         hipLaunchKernelGGL((sgmv_mfma_expand_kernel<T, R, false>), dim3(grid, np), dim3(kThreads), 0, s, p);
@@ -444,7 +469,7 @@ hipError_t launch_stage(int dtype, int rank, int stage, const MfmaParams& p, int
 
 bool mfma_supported(int rank) { return rank == 16 || rank == 32 || rank == 64; }
 
-// The smaller occupancy of the two row-layout variants.
+// The smaller occupancy of the plain and the extended variant.
 template <class T, int R>
 int expand_capacity_t() {
   int per_cu = 0, per_cu2 = 0, dev = 0, cus = 0;

@@ -24,6 +24,8 @@ struct VecParams {
   const int32_t* seg_indptr;
   const int32_t* lora_idx;
   const int32_t* row_idx;  // null, or row of X / Y of each sorted row
+  const int32_t* ranks;    // null, or rank of each LoRA (A_k [h_in, r_k], B_k [r_k, h_out])
+  const float* scales;     // null, or scale of each LoRA's term (applied to V by the shrink)
   float* partials;     // [num_units][splits][RB][rank] fp32
   uint32_t* counters;  // [2 * num_units]: arrivals, departures
   int32_t n_rows, h_in, h_out, num_segs, num_loras;
@@ -59,6 +61,8 @@ struct Projection {
   const uint64_t* A_ptrs;
   const uint64_t* B_ptrs;
   uint16_t* Y;
+  const int32_t* ranks;  // null: every LoRA has the compiled rank
+  const float* scales;   // null: scale 1
 };
 
 

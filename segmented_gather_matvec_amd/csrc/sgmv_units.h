@@ -77,15 +77,12 @@ __device__ inline Unit resolve_unit(const int32_t* seg_indptr, const int32_t* lo
   return out;
 }
 
-// Row of X / Y that holds sorted row j: row_idx[j] with a row map (the caller's
-// rows in request order), j without one.  Kernels take MAP as a template
-// argument so that the plain layout carries no lookup and no wait on one.
-template <bool MAP>
-__device__ inline int64_t phys_row(const int32_t* row_idx, int j) {
-  if constexpr (MAP)
-    return (int64_t)row_idx[j];
-  else
-    return (int64_t)j;
+// Rank of a LoRA as used by the kernels: the stored value clamped to [0, R]
+// and rounded down to a multiple of 8 (one 128-bit vector of A_k per 8 ranks).
+template <int R>
+__device__ inline int lora_rank(int r) {
+  return (r < 0 ? 0 : r > R ? R : r) & ~7;
 }
+
 
 }  // namespace sgmv

@@ -82,7 +82,9 @@ __device__ inline void gather_partials(const float* base, int G, int n, float* s
   if (t < n) dst[t] = acc;
 }
 
-template <class T, int R, int RB, int MODE, bool MAP>
+// EXT: the extended arguments may be set (row map, per-LoRA ranks and scales;
+// see the decode kernel).  Without EXT the kernel carries none of it.
+template <class T, int R, int RB, int MODE, bool EXT>
 __global__ __launch_bounds__(kThreads) void sgmv_vec_kernel(VecParams p) {
   constexpr int JG = R / 8;                 // 128-bit vectors per row of A_k
   constexpr int B0 = log2_groups<R>();
@@ -113,6 +115,16 @@ __global__ __launch_bounds__(kThreads) void sgmv_vec_kernel(VecParams p) {
   if (un.L <= 0) return;  // uniform over the workgroup
   const int L = un.L;
   const int r0 = un.r0;
+  // Rank of the LoRA (A_k rows and B_k's row count; ranks >= rk are zero) and
+  // the scale of its term.
+  int rk = R;
+  float sk = 1.f;
+  if constexpr (EXT) {
+    if (p.ranks) rk = lora_rank<R>(p.ranks[un.k]);
+    if (p.scales) sk = p.scales[un.k];
+    if (rk == 0) return;  // nothing to add: every split of the unit leaves here
+  }
+  auto row_of = [&](int j) -> int64_t { return EXT && p.row_idx ? (int64_t)p.row_idx[j] : (int64_t)j; };
 
   // ---- expand operands: B_k columns [c0, c1), Y rows [r0, r0+L) ----
   // Every thread issues the same number of loads in every pass (addresses of
@@ -133,7 +145,7 @@ __global__ __launch_bounds__(kThreads) void sgmv_vec_kernel(VecParams p) {
     for (int q = 0; q < kNB; ++q) {
       const int v = t + kThreads * q;
       const int j = cvr ? v / cvr : 0, cv = v - j * cvr;
-      const bool ok = v < R * cvr;
+      const bool ok = v < R * cvr && (!EXT || j < rk);
       bv[q] = load_stream(Bk + (ok ? (int64_t)j * p.h_out + cp0 + cv * 8 : 0));
     }
 #pragma unroll
@@ -141,7 +153,7 @@ __global__ __launch_bounds__(kThreads) void sgmv_vec_kernel(VecParams p) {
       const int y = t + kThreads * q;
       const int i = cvr ? y / cvr : 0, cv = y - i * cvr;
       const bool ok = y < L * cvr;
-      yv[q] = load_stream(p.Y + phys_row<MAP>(p.row_idx, r0 + (ok ? i : 0)) * p.h_out + (ok ? cp0 + cv * 8 : 0));
+      yv[q] = load_stream(p.Y + row_of(r0 + (ok ? i : 0)) * p.h_out + (ok ? cp0 + cv * 8 : 0));
     }
   };
   auto compute_expand = [&](int cp0, const u32x4 (&bv)[kNB], const u32x4 (&yv)[NYV]) {
@@ -152,7 +164,8 @@ __global__ __launch_bounds__(kThreads) void sgmv_vec_kernel(VecParams p) {
       const int v = t + kThreads * q;
       if (v < R * cvr) {
         const int j = v / cvr, cv = v - j * cvr;
-        store_vec(&lds_b[j * CP + cv * 8], bv[q]);
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        store_vec(&lds_b[j * CP + cv * 8], !EXT || j < rk ? bv[q] : z);
       }
     }
     __syncthreads();
@@ -186,7 +199,7 @@ __global__ __launch_bounds__(kThreads) void sgmv_vec_kernel(VecParams p) {
         unpack8<T>(yv[0], yf);
 #pragma unroll
         for (int e = 0; e < 8; ++e) yf[e] += acc[e];
-        store_vec(p.Y + phys_row<MAP>(p.row_idx, r0 + i) * p.h_out + cp0 + cv * 8, pack8<T>(yf));
+        store_vec(p.Y + row_of(r0 + i) * p.h_out + cp0 + cv * 8, pack8<T>(yf));
       }
     } else {
 #pragma unroll
@@ -207,7 +220,7 @@ __global__ __launch_bounds__(kThreads) void sgmv_vec_kernel(VecParams p) {
           unpack8<T>(yv[q], yf);
 #pragma unroll
           for (int e = 0; e < 8; ++e) yf[e] += acc[e];
-          store_vec(p.Y + phys_row<MAP>(p.row_idx, r0 + i) * p.h_out + cp0 + cv * 8, pack8<T>(yf));
+          store_vec(p.Y + row_of(r0 + i) * p.h_out + cp0 + cv * 8, pack8<T>(yf));
         }
       }
     }
@@ -225,14 +238,16 @@ __global__ __launch_bounds__(kThreads) void sgmv_vec_kernel(VecParams p) {
 #pragma unroll
       for (int q = 0; q < kNA; ++q) {
         const int v = t + kThreads * q;
-        av[q] = load_stream(Ak + (v < hpn * JG ? (int64_t)hp0 * R + v * 8 : 0));
+        // Vector v holds ranks (v % JG)*8 .. +7 of row hp0 + v / JG.
+        const bool ok = v < hpn * JG && (!EXT || (v % JG) * 8 < rk);
+        av[q] = load_stream(Ak + (ok ? (int64_t)(hp0 + v / JG) * (EXT ? rk : R) + (v % JG) * 8 : 0));
       }
 #pragma unroll
       for (int q = 0; q < NXV; ++q) {
         const int x = t + kThreads * q;
         const int i = xvr ? x / xvr : 0, c = x - i * xvr;
         const bool ok = x < L * xvr;
-        xv[q] = load_stream(p.X + phys_row<MAP>(p.row_idx, r0 + (ok ? i : 0)) * p.h_in + (ok ? hp0 + c * 8 : 0));
+        xv[q] = load_stream(p.X + row_of(r0 + (ok ? i : 0)) * p.h_in + (ok ? hp0 + c * 8 : 0));
       }
     };
     float acc[RB][8];
@@ -256,7 +271,7 @@ __global__ __launch_bounds__(kThreads) void sgmv_vec_kernel(VecParams p) {
 #pragma unroll
       for (int q = 0; q < kNA; ++q) {
         const int v = t + kThreads * q;
-        if (v < hpn * JG) {
+        if (v < hpn * JG && (!EXT || (v % JG) * 8 < rk)) {
           const int hl = v / JG;  // row of A_k inside the pass; ranks (t % JG)*8 .. +7
           float af[8];
           unpack8<T>(av[q], af);
@@ -309,7 +324,7 @@ __global__ __launch_bounds__(kThreads) void sgmv_vec_kernel(VecParams p) {
         float s = 0.f;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) s += lds_red[w * RB * R + o];
-        p.V[(int64_t)(r0 + o / R) * R + (o % R)] = s;
+        p.V[(int64_t)(r0 + o / R) * R + (o % R)] = EXT ? s * sk : s;
       }
       return;
     }
@@ -333,7 +348,7 @@ __global__ __launch_bounds__(kThreads) void sgmv_vec_kernel(VecParams p) {
       const int n = L * R - o0 < kThreads ? L * R - o0 : kThreads;
       gather_partials<RB, R>(base + o0, G, n, lds_out, kStage, lds_v);
       __syncthreads();
-      if (t < n) p.V[(int64_t)(r0 + (o0 + t) / R) * R + ((o0 + t) % R)] = lds_v[t];
+      if (t < n) p.V[(int64_t)(r0 + (o0 + t) / R) * R + ((o0 + t) % R)] = EXT ? lds_v[t] * sk : lds_v[t];
       __syncthreads();
     }
     if (t == 0) counter_store(arrive, 0u);
@@ -356,7 +371,7 @@ template <class T, int R, int RB, int MODE>
 hipError_t launch_one(const VecParams& p, hipStream_t stream) {
   const unsigned grid = (unsigned)p.num_units * (unsigned)p.splits;
   if (grid == 0) return hipSuccess;
-  if (p.row_idx)
+  if (p.row_idx || p.ranks || p.scales)
     hipLaunchKernelGGL((sgmv_vec_kernel<T, R, RB, MODE, true>), dim3(grid), dim3(kThreads), 0, stream, p);
   else
     hipLaunchKernelGGL((sgmv_vec_kernel<T, R, RB, MODE, false>), dim3(grid), dim3(kThreads), 0, stream, p);

@@ -106,6 +106,9 @@ def test_batched_apply_fails_fast_on_bad_arguments():
     assert call([ok] * 5, 5, 5 * need) == sg.SGMV_ERR_INVALID_ARG            # more than SGMV_MAX_PROJECTIONS
     assert call([ok, sg.sgmv_projection_t(0x10000, None, 0x10000)], 2, 4 * need) == sg.SGMV_ERR_INVALID_ARG
     assert call([ok, sg.sgmv_projection_t(0x10000, 0x10000, 0x10002)], 2, 4 * need) == sg.SGMV_ERR_UNSUPPORTED
+    # rank and scale tables must be 4-byte aligned
+    assert call([sg.sgmv_projection_t(0x10000, 0x10000, 0x10000, 0x10002, None)], 1, need) == sg.SGMV_ERR_UNSUPPORTED
+    assert call([sg.sgmv_projection_t(0x10000, 0x10000, 0x10000, None, 0x10001)], 1, need) == sg.SGMV_ERR_UNSUPPORTED
     assert call([ok, ok], 2, need) == sg.SGMV_ERR_WORKSPACE                    # one slice is not two
     assert call([ok, ok], 2, sg.batched_workspace_bytes(p, 2) - 1) == sg.SGMV_ERR_WORKSPACE
     assert call([ok], 1, need, X=None) == sg.SGMV_ERR_INVALID_ARG

@@ -252,6 +252,63 @@ def test_integer_exact_inputs_give_integer_results():
     assert np.array_equal(workloads.to_bits(Y.astype(np.float32), "f16").view(np.float16).astype(np.float64), Y)
 
 
+# ---------------------------------------------------------------- ranks and scales
+# The Punica discussion page ("Punica: Serving multiple LoRA finetuned LLM as
+# one", the question on LoRAs with different ranks) handles mixed ranks by
+# padding every LoRA to one rank.  Padding A_k with zero columns and B_k with
+# zero rows leaves x @ A_k @ B_k unchanged, so a LoRA of rank r_k must give what
+# the uniform-rank path (pinned above) gives on the zero-padded pair.
+
+def het_case(seed, dtype="f16", ranks=(8, 0, 16, 24), R=32, n=10, h_in=48, h_out=40):
+    rng = np.random.default_rng(seed)
+    X = workloads.to_bits(rng.standard_normal((n, h_in), dtype=np.float32), dtype)
+    Y0 = workloads.to_bits(rng.standard_normal((n, h_out), dtype=np.float32), dtype)
+    A = [workloads.to_bits(rng.standard_normal((h_in, r), dtype=np.float32) * 0.2, dtype) for r in ranks]
+    B = [workloads.to_bits(rng.standard_normal((r, h_out), dtype=np.float32) * 0.5, dtype) for r in ranks]
+    Ap = [np.zeros((h_in, R), np.uint16) for _ in ranks]
+    Bp = [np.zeros((R, h_out), np.uint16) for _ in ranks]
+    for k, r in enumerate(ranks):
+        Ap[k][:, :r] = A[k]
+        Bp[k][:r, :] = B[k]
+    seg, lidx = [0, 3, 5, 9, 10], [2, 1, 0, 3]
+    return X, A, B, Ap, Bp, Y0, seg, lidx
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_rank_table_equals_zero_padding(dtype):
+    X, A, B, Ap, Bp, Y0, seg, lidx = het_case(30, dtype)
+    het, V = oracle.sgmv_apply(dtype, X, A, B, seg, lidx, Y0, rank=32, want_v=True)
+    pad, Vp = oracle.sgmv_apply(dtype, X, Ap, Bp, seg, lidx, Y0, want_v=True)
+    assert np.array_equal(het, pad)
+    assert np.array_equal(V, Vp)  # V is zero past each LoRA's rank
+    # and both agree with the per-row definition evaluated by numpy
+    assert np.allclose(het, brute_force(dtype, X, Ap, Bp, seg, lidx, Y0), rtol=1e-12, atol=1e-12)
+
+
+def test_rank_zero_lora_adds_nothing():
+    X, A, B, Ap, Bp, Y0, seg, lidx = het_case(31)
+    Y = oracle.sgmv_apply("f16", X, A, B, seg, lidx, Y0, rank=32)
+    rows = range(seg[1], seg[2])  # segment 1 uses LoRA 1, of rank 0
+    assert np.array_equal(Y[list(rows)], np_decode(Y0, "f16")[list(rows)])
+
+
+def test_scale_multiplies_the_term_only():
+    # Integer-exact inputs and power-of-two scales: every value is exact, so
+    # Y(s) - Y0 equals s * (Y(1) - Y0) bit for bit, and the base output is not
+    # scaled.
+    rng = np.random.default_rng(32)
+    X, A, B, Y0 = workloads.integer_exact(rng, 6, 128, 64, 16, 3, "f16", nnz_per_col=8, y0_bound=64)
+    seg, lidx = [0, 2, 3, 6], [2, 0, 1]
+    scales = np.array([0.5, 4.0, -0.25])
+    one = oracle.sgmv_apply("f16", X, A, B, seg, lidx, Y0)
+    got = oracle.sgmv_apply("f16", X, A, B, seg, lidx, Y0, scales=scales)
+    y0 = np_decode(Y0, "f16")
+    for s in range(3):
+        rows = slice(seg[s], seg[s + 1])
+        assert np.array_equal(got[rows] - y0[rows], scales[lidx[s]] * (one[rows] - y0[rows]))
+    assert not np.array_equal(one, y0)  # the term is not zero
+
+
 # ---------------------------------------------------------------- builder
 
 def test_builder_golden_examples():

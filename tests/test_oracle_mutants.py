@@ -19,9 +19,15 @@ MUTANTS = {
                           "acc += decode(dtype, x_row[h]) * decode(dtype, a[(int64_t)j * h_in + h]);"),
     "B_read_transposed": ("acc += v[j] * decode(dtype, b[(int64_t)j * h_out + c]);",
                           "acc += v[j] * decode(dtype, b[(int64_t)c * rank + j]);"),
-    "base_output_dropped": ("y[c] = decode(dtype, y0_row[c]) + acc;", "y[c] = acc;"),
-    "term_sign_flipped": ("y[c] = decode(dtype, y0_row[c]) + acc;",
-                          "y[c] = decode(dtype, y0_row[c]) - acc;"),
+    "base_output_dropped": ("y[c] = decode(dtype, y0_row[c]) + scale * acc;", "y[c] = scale * acc;"),
+    "term_sign_flipped": ("y[c] = decode(dtype, y0_row[c]) + scale * acc;",
+                          "y[c] = decode(dtype, y0_row[c]) - scale * acc;"),
+    "scale_ignored": ("y[c] = decode(dtype, y0_row[c]) + scale * acc;",
+                      "y[c] = decode(dtype, y0_row[c]) + acc;"),
+    "scale_applied_to_base": ("y[c] = decode(dtype, y0_row[c]) + scale * acc;",
+                              "y[c] = scale * (decode(dtype, y0_row[c]) + acc);"),
+    "rank_table_short_by_one_vector": ("const int32_t rk = ranks ? ranks[k] : rank;",
+                                       "const int32_t rk = ranks ? (ranks[k] > 8 ? ranks[k] - 8 : 0) : rank;"),
     "segment_index_as_lora": ("const int32_t k = lora_idx[s];", "const int32_t k = s % num_loras;"),
     "last_row_of_segment_dropped": ("for (int32_t i = lo; i < hi; ++i) seg_of_row[i] = s;",
                                     "for (int32_t i = lo; i + 1 < hi; ++i) seg_of_row[i] = s;"),
@@ -50,6 +56,9 @@ PINS = [
     lambda: pins.test_tiny_workload_brute_force("bf16"),
     pins.test_uncovered_rows_keep_base_output,
     pins.test_segments_equal_per_row_definition,
+    lambda: pins.test_rank_table_equals_zero_padding("f16"),
+    pins.test_rank_zero_lora_adds_nothing,
+    pins.test_scale_multiplies_the_term_only,
 ]
 
 
