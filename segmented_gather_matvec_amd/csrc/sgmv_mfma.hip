@@ -172,6 +172,7 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_shrink_kernel(MfmaParams p
       }
     }
     __syncthreads();
+    if (wave * 16 >= L) return;  // this wave's rows are all past the segment
 #pragma unroll
     for (int s = 0; s < MS; ++s) {
       const u32x4 xa = kk + s * 32 + q * 8 < k1 ? x[s] : z;  // ragged tail of H1
@@ -332,11 +333,9 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_expand_kernel(MfmaParams p
       yv[u] = load_stream(Ybase + (int64_t)yrow[u] * p.h_out + (ok ? c : 0));
     }
   };
-  u32x4 bvA[NBP][2], yvA[NYV], bvB[NBP][2], yvB[NYV];
-  issue(ch0, bvA, yvA);
-
-  // V of the tile rows (all fetched at once), split hi/lo, then this wave's
-  // MFMA A fragments.
+  // V of the tile rows (all fetched at once, ahead of the first chunk's loads
+  // so that waiting for V does not wait for them), split hi/lo, then this
+  // wave's MFMA A fragments.
   constexpr int NV4 = kMT * R / 4 / kThreads;  // float4 of V per thread
   f32x4 vv[NV4];
 #pragma unroll
@@ -345,6 +344,8 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_expand_kernel(MfmaParams p
     const int rr = o / R;
     vv[m] = *reinterpret_cast<const f32x4*>(Vp + (int64_t)(r0 + (rr < L ? rr : 0)) * R + o % R);
   }
+  u32x4 bvA[NBP][2], yvA[NYV], bvB[NBP][2], yvB[NYV];
+  issue(ch0, bvA, yvA);
 #pragma unroll
   for (int m = 0; m < NV4; ++m) {
     const int o = (t + kThreads * m) * 4;
@@ -378,6 +379,10 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_expand_kernel(MfmaParams p
       }
     }
     __syncthreads();
+    // A wave whose 16 rows are all past the segment has nothing to compute or
+    // store; each wave's result tile is its own, so only the wave itself
+    // waits for it (LDS operations of one wave complete in order).
+    if (wave * 16 >= L) return;
 #pragma unroll
     for (int n = 0; n < NTC; ++n) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -389,7 +394,9 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_expand_kernel(MfmaParams p
 #pragma unroll
       for (int i = 0; i < 4; ++i) out[(q * 4 + i) * OST + n * 16 + ml] = acc[i];
     }
-    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
     for (int u = 0; u < NYV; ++u) {
       const int v = lane + 64 * u;
