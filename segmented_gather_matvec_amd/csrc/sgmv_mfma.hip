@@ -259,6 +259,13 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_expand_kernel(MfmaParams p
   constexpr int NTC = kCW / 16;        // 16-wide column tiles per chunk
   constexpr int CV = kCW / 8;          // 128-bit column vectors per chunk row
   constexpr int BST = R + 8;           // LDS stride (halves) of transposed B_k, per column
+  // Within a column, B_k's ranks sit in groups of 8 (one 128-bit MFMA operand
+  // read); group g of column c is stored at group g ^ swz(c).  The transposed
+  // stores of a wave then spread over the LDS banks (without the swizzle the
+  // 16 lanes that write one rank pair of 16 column groups hit 2 banks), and
+  // the operand reads stay conflict-free.
+  constexpr int GMASK = R / 8 - 1;
+  auto swz = [](int c) { return (c >> 4) & GMASK; };
   constexpr int VST = K2 + 8;          // LDS stride (halves) of [V_hi | V_lo], per row
   constexpr int OST = kCW + 4;         // LDS stride (floats) of the result tile
   constexpr int NBP = (R / 2 * CV + kThreads - 1) / kThreads;  // (j, j+1) B_k vector pairs per thread
@@ -375,7 +382,8 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_expand_kernel(MfmaParams p
         const int j = (pr / CV) * 2, cl = (pr % CV) * 8;
         const u32x4 z = {0u, 0u, 0u, 0u};
         const bool live = !EXT || j < rk;  // rk is even, so j < rk covers row j + 1 too
-        store_pair_transposed(&lds_bt[cl * BST + j], BST, live ? bv[m][0] : z, live ? bv[m][1] : z);
+        const int js = (((j >> 3) ^ swz(cl)) << 3) | (j & 7);  // columns cl..cl+7 share swz(cl)
+        store_pair_transposed(&lds_bt[cl * BST + js], BST, live ? bv[m][0] : z, live ? bv[m][1] : z);
       }
     }
     __syncthreads();
@@ -389,7 +397,7 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_expand_kernel(MfmaParams p
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) {
         const int kb = (s * 32 + q * 8) % R;  // rank of the B_k copy this k-group reads
-        acc = mfma<T>(af[s], load_vec(&lds_bt[(n * 16 + ml) * BST + kb]), acc);
+        acc = mfma<T>(af[s], load_vec(&lds_bt[(n * 16 + ml) * BST + (((kb >> 3) ^ swz(n * 16)) << 3)]), acc);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) out[(q * 4 + i) * OST + n * 16 + ml] = acc[i];
