@@ -91,6 +91,12 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_shrink_kernel(MfmaParams p
   constexpr int NPAIR = (PAIRS + kThreads - 1) / kThreads;
   constexpr int MS = kKStage / 32;          // MFMA k-steps per stage
   constexpr int AST = kKStage + 8;          // LDS row stride (halves) of transposed A_k
+  // Within a rank row, the stage's h sit in groups of 8 (one 128-bit MFMA
+  // operand read); group g of rank row r is stored at group g ^ swz(r), which
+  // spreads a wave's transposed stores over the LDS banks at ranks 32 and 64
+  // (rank 16 is conflict-free as is) while the operand reads stay
+  // conflict-free.
+  auto swz = [](int r) { return (r >> 4) << (R == 64 ? 1 : 2); };
   static_assert(kMfmaKChunk % (2 * kKStage) == 0, "H1 chunks hold whole stage pairs");
   __shared__ __attribute__((aligned(16))) uint16_t lds_at[R * AST];
 
@@ -167,7 +173,8 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_shrink_kernel(MfmaParams p
       if (pr < PAIRS) {
         const int h = (pr / JG) * 2, jg = pr % JG;
         const bool live = !EXT || jg * 8 < rk;
-        store_pair_transposed(&lds_at[(jg * 8) * AST + h], AST, live && kk + h < k1 ? a[m][0] : z,
+        const int hs = (((h >> 3) ^ swz(jg * 8)) << 3) | (h & 7);  // rows jg*8..+7 share swz
+        store_pair_transposed(&lds_at[(jg * 8) * AST + hs], AST, live && kk + h < k1 ? a[m][0] : z,
                               live && kk + h + 1 < k1 ? a[m][1] : z);
       }
     }
@@ -178,7 +185,7 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_shrink_kernel(MfmaParams p
       const u32x4 xa = kk + s * 32 + q * 8 < k1 ? x[s] : z;  // ragged tail of H1
 #pragma unroll
       for (int n = 0; n < NT; ++n)
-        acc[n] = mfma<T>(xa, load_vec(&lds_at[(n * 16 + ml) * AST + s * 32 + q * 8]), acc[n]);
+        acc[n] = mfma<T>(xa, load_vec(&lds_at[(n * 16 + ml) * AST + (((4 * s + q) ^ swz(n * 16)) << 3)]), acc[n]);
     }
   };
 
