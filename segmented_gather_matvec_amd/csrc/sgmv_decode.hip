@@ -87,10 +87,11 @@ constexpr int log2_groups() {
 }
 
 // SMALL: at most 64 LoRAs (pointer tables fetched one entry per lane).
-// EXT: the extended arguments may be set: a row map (rows of X / Y looked up),
-// per-LoRA ranks (compact A_k [h_in, r_k], B_k [r_k, h_out]; ranks r_k..R-1
-// are zero) and per-LoRA scales.  Without EXT the kernel carries none of it.
-template <class T, int R, int RB, bool SMALL, bool EXT>
+// MAP: rows of X / Y are looked up in a row map.
+// HET: per-LoRA ranks (compact A_k [h_in, r_k], B_k [r_k, h_out]; ranks
+// r_k..R-1 are zero) and / or per-LoRA scales may be given.
+// Each feature is a template flag, so a call pays only for what it uses.
+template <class T, int R, int RB, bool SMALL, bool MAP, bool HET>
 __global__ __launch_bounds__(kThreads) void sgmv_decode_kernel(DecodeParams p) {
   constexpr int JG = R / 8;                  // 128-bit vectors per row of A_k
   constexpr int B0 = log2_groups<R>();
@@ -120,8 +121,13 @@ __global__ __launch_bounds__(kThreads) void sgmv_decode_kernel(DecodeParams p) {
   // argument where it is first used.
   const bool bad_size = (p.num_units | p.splits | p.kc | p.cw | p.direct_units | p.split_major | p.n_rows |
                          p.h_in | p.h_out | p.num_segs | p.num_loras | (int32_t)(p.slot_stride >> 32)) < 0;
-  const bool bad_ptr = (p.seg_indptr == nullptr) | (p.lora_idx == nullptr) | (p.X == nullptr) |
-                       (p.slots == nullptr) | (pr.A_ptrs == nullptr) | (pr.B_ptrs == nullptr) | (pr.Y == nullptr);
+  bool bad_ptr = (p.seg_indptr == nullptr) | (p.lora_idx == nullptr) | (p.X == nullptr) |
+                 (p.slots == nullptr) | (pr.A_ptrs == nullptr) | (pr.B_ptrs == nullptr) | (pr.Y == nullptr);
+  // The optional int32 / fp32 tables are 4-byte aligned (the rank and scale
+  // tables are nullable).
+  if constexpr (MAP) bad_ptr |= (reinterpret_cast<uintptr_t>(p.row_idx) & 3) != 0 || p.row_idx == nullptr;
+  if constexpr (HET)
+    bad_ptr |= ((reinterpret_cast<uintptr_t>(pr.ranks) | reinterpret_cast<uintptr_t>(pr.scales)) & 3) != 0;
   if (bad_size | bad_ptr) return;
   // Workgroups go round-robin over the XCDs.
   int unit, g;
@@ -147,7 +153,7 @@ __global__ __launch_bounds__(kThreads) void sgmv_decode_kernel(DecodeParams p) {
   if (SMALL && lane < p.num_loras) {
     a_lane = pr.A_ptrs[lane];
     b_lane = pr.B_ptrs[lane];
-    if constexpr (EXT) {
+    if constexpr (HET) {
       if (pr.ranks) rk_lane = pr.ranks[lane];
       if (pr.scales) sk_lane = pr.scales[lane];
     }
@@ -166,19 +172,19 @@ __global__ __launch_bounds__(kThreads) void sgmv_decode_kernel(DecodeParams p) {
   if constexpr (SMALL) {
     Ak = reinterpret_cast<const uint16_t*>(readlane_u64(a_lane, un.k));
     Bk = reinterpret_cast<const uint16_t*>(readlane_u64(b_lane, un.k));
-    if constexpr (EXT) {
+    if constexpr (HET) {
       rk = __builtin_amdgcn_readlane(rk_lane, un.k);
       sk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sk_lane), un.k));
     }
   } else {
     Ak = reinterpret_cast<const uint16_t*>(pr.A_ptrs[un.k]);
     Bk = reinterpret_cast<const uint16_t*>(pr.B_ptrs[un.k]);
-    if constexpr (EXT) {
+    if constexpr (HET) {
       if (pr.ranks) rk = pr.ranks[un.k];
       if (pr.scales) sk = pr.scales[un.k];
     }
   }
-  if constexpr (EXT) {
+  if constexpr (HET) {
     rk = lora_rank<R>(rk);
     if (rk == 0) return;  // the LoRA adds nothing (uniform over the unit)
   }
@@ -189,18 +195,17 @@ __global__ __launch_bounds__(kThreads) void sgmv_decode_kernel(DecodeParams p) {
   // Rows of X / Y.  With a row map, lane l looks up the row behind sorted row
   // r0 + l once, ahead of the streaming loads (L <= RB <= 64 rows), and every
   // other lane takes it from there.
-  const bool map = EXT && p.row_idx != nullptr;
   int prow = r0 + lane;
-  if (map) prow = p.row_idx[r0 + (lane < L ? lane : L - 1)];
-  const uint16_t* Xr = p.X + (int64_t)(map ? __builtin_amdgcn_readfirstlane(prow) : r0) * p.h_in;
+  if constexpr (MAP) prow = p.row_idx[r0 + (lane < L ? lane : L - 1)];
+  const uint16_t* Xr = p.X + (int64_t)(MAP ? __builtin_amdgcn_readfirstlane(prow) : r0) * p.h_in;
 
   // ---------------- all loads, issued up front ----------------
   // Shrink: thread t owns ranks (t % JG)*8..+7 of rows h0 + t/JG + q*HS.
   // With a rank below R, A_k rows are rk wide and the lanes of ranks >= rk
   // load nothing new (their address is clamped) and compute nothing.
   const int jg = t % JG;
-  const bool jg_ok = !EXT || jg * 8 < rk;
-  const int a_stride = EXT ? rk : R;
+  const bool jg_ok = !HET || jg * 8 < rk;
+  const int a_stride = HET ? rk : R;
   u32x4 av[NA];
 #pragma unroll
   for (int q = 0; q < NA; ++q) {
@@ -222,7 +227,7 @@ __global__ __launch_bounds__(kThreads) void sgmv_decode_kernel(DecodeParams p) {
       const int x = t + kThreads * q;
       const int i = xvr > 0 ? x / xvr : 0, c = x - i * xvr;
       const int xi = x < L * xvr ? i : 0;
-      const int64_t row = map ? __shfl(prow, xi) : r0 + xi;
+      const int64_t row = MAP ? __shfl(prow, xi) : r0 + xi;
       xv[q] = load_stream(p.X + row * p.h_in + (x < L * xvr ? h0 + c * 8 : 0));
     }
   }
@@ -234,7 +239,7 @@ __global__ __launch_bounds__(kThreads) void sgmv_decode_kernel(DecodeParams p) {
   u32x4 bv[NB];
 #pragma unroll
   for (int m = 0; m < NB; ++m) {
-    const bool ok = col_ok && (!EXT || jq + JQ * m < rk);  // rows of B_k past rk do not exist
+    const bool ok = col_ok && (!HET || jq + JQ * m < rk);  // rows of B_k past rk do not exist
     bv[m] = load_stream(Bk + (ok ? (int64_t)(jq + JQ * m) * p.h_out + col : 0));
   }
   u32x4 yv[NY];
@@ -243,7 +248,7 @@ __global__ __launch_bounds__(kThreads) void sgmv_decode_kernel(DecodeParams p) {
   for (int n = 0; n < NY; ++n) {
     const int i = jq + JQ * n;
     const int yi = col_ok && i < L ? i : 0;
-    yrow[n] = map ? __shfl(prow, yi) : r0 + yi;
+    yrow[n] = MAP ? __shfl(prow, yi) : r0 + yi;
     yv[n] = load_stream(pr.Y + (int64_t)yrow[n] * p.h_out + (col_ok && i < L ? col : 0));
   }
 
@@ -360,7 +365,7 @@ __global__ __launch_bounds__(kThreads) void sgmv_decode_kernel(DecodeParams p) {
       for (int pp = 0; pp < pn; ++pp) vsum += lds_stage[pp * n_out + t];
     __syncthreads();
   }
-  if (t < n_out) lds_v[t] = EXT ? vsum * sk : vsum;
+  if (t < n_out) lds_v[t] = HET ? vsum * sk : vsum;
   __syncthreads();
 
   // ---------------- expand ----------------
@@ -368,7 +373,7 @@ __global__ __launch_bounds__(kThreads) void sgmv_decode_kernel(DecodeParams p) {
 #pragma unroll
   for (int m = 0; m < NB; ++m) {
     unpack8<T>(bv[m], bf[m]);
-    if (EXT && jq + JQ * m >= rk)
+    if (HET && jq + JQ * m >= rk)
 #pragma unroll
       for (int e = 0; e < 8; ++e) bf[m][e] = 0.f;
   }
@@ -405,32 +410,42 @@ hipError_t launch_t(const DecodeParams& p, int num_proj, hipStream_t stream) {
   const unsigned grid = units * (unsigned)p.splits;
   if (grid == 0 || num_proj <= 0) return hipSuccess;
   const bool small = p.num_loras <= 64;
-  bool ext = p.row_idx != nullptr;
-  for (int i = 0; i < num_proj; ++i) ext = ext || p.proj[i].ranks || p.proj[i].scales;
-  void (*kernel)(DecodeParams) =
-      ext ? (small ? sgmv_decode_kernel<T, R, RB, true, true> : sgmv_decode_kernel<T, R, RB, false, true>)
-          : (small ? sgmv_decode_kernel<T, R, RB, true, false> : sgmv_decode_kernel<T, R, RB, false, false>);
+  const bool map = p.row_idx != nullptr;
+  bool het = false;
+  for (int i = 0; i < num_proj; ++i) het = het || p.proj[i].ranks || p.proj[i].scales;
+  using K = void (*)(DecodeParams);
+  // [small][map][het]
+  static constexpr K kernels[2][2][2] = {
+      {{sgmv_decode_kernel<T, R, RB, false, false, false>, sgmv_decode_kernel<T, R, RB, false, false, true>},
+       {sgmv_decode_kernel<T, R, RB, false, true, false>, sgmv_decode_kernel<T, R, RB, false, true, true>}},
+      {{sgmv_decode_kernel<T, R, RB, true, false, false>, sgmv_decode_kernel<T, R, RB, true, false, true>},
+       {sgmv_decode_kernel<T, R, RB, true, true, false>, sgmv_decode_kernel<T, R, RB, true, true, true>}}};
+  const K kernel = kernels[small][map][het];
   hipLaunchKernelGGL(kernel, dim3(grid, num_proj), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
-template <class T, int R, int RB, bool SMALL, bool EXT>
+template <class T, int R, int RB, bool SMALL, bool MAP, bool HET>
 int per_cu_t() {
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &n, reinterpret_cast<const void*>(&sgmv_decode_kernel<T, R, RB, SMALL, EXT>), kThreads, 0) != hipSuccess)
+          &n, reinterpret_cast<const void*>(&sgmv_decode_kernel<T, R, RB, SMALL, MAP, HET>), kThreads, 0) !=
+      hipSuccess)
     return 0;
   return n;
 }
 
-// The variants (pointer pool, extended arguments) use the same registers and LDS within a
-// few VGPRs; the smallest of their occupancies is reported.
+// The variants (pointer pool, row map, ranks and scales) use the same
+// registers and LDS within a few VGPRs; the smallest of their occupancies is
+// reported.
 template <class T, int R, int RB>
 int capacity_t() {
   int dev = 0, cus = 0;
-  int per_cu = per_cu_t<T, R, RB, true, false>();
-  for (int n : {per_cu_t<T, R, RB, false, false>(), per_cu_t<T, R, RB, true, true>(),
-                per_cu_t<T, R, RB, false, true>()})
+  int per_cu = per_cu_t<T, R, RB, true, false, false>();
+  for (int n : {per_cu_t<T, R, RB, false, false, false>(), per_cu_t<T, R, RB, true, true, false>(),
+                per_cu_t<T, R, RB, false, true, false>(), per_cu_t<T, R, RB, true, false, true>(),
+                per_cu_t<T, R, RB, false, false, true>(), per_cu_t<T, R, RB, true, true, true>(),
+                per_cu_t<T, R, RB, false, true, true>()})
     per_cu = n < per_cu ? n : per_cu;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
