@@ -121,7 +121,7 @@ def workload_layout(name):
 
 
 SINGLE_WORKLOADS = (["decode_distinct_h4096_r16_b32", "decode_distinct_h4096_r16_b64"]
-                    + [f"decode_distinct_h4096_r16_b{n}" for n in (1, 8, 16)]
+                    + [f"decode_distinct_h4096_r16_b{n}" for n in (1, 8, 16, 128, 256, 512)]
                     + ["decode_distinct_h4096_r32_b32", "decode_distinct_h4096_r64_b8",
                        "decode_distinct_h4096_r64_b32", "decode_distinct_h11008_r16_b32"]
                     + [f"{k}_b{n}" for k in ("identical", "uniform", "skewed") for n in (32, 64)]

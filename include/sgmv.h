@@ -166,7 +166,12 @@ typedef struct sgmv_plan_info {
 
 /* Host-only: the plan sgmv_lora_apply would run for *problem on the current
  * device (the decode route depends on the device's occupancy; without a
- * usable device it is never chosen).  No device memory is touched. */
+ * usable device it is never chosen).  A batched call with a row map or rank /
+ * scale tables launches a kernel variant whose occupancy may differ, so its
+ * plan may differ too.  When the decode route's units do not all fit on the
+ * device at once, it launches the largest co-resident grid (grid < units *
+ * splits) once per pass over them (launches > 1).
+ * No device memory is touched. */
 sgmv_status_t sgmv_query_plan(const sgmv_problem_t* problem, sgmv_plan_info_t* info);
 
 /* Shrink: V[i, :] = X[i, :] @ A_{lora_idx[s]} for every covered row i

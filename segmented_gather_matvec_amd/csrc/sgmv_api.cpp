@@ -82,7 +82,9 @@ struct DecodePlan {
   int splits = 1;
   int kc = 8;
   int cw = 8;
-  int64_t grid = 0;
+  int64_t grid = 0;         // workgroups of the launch: round_units * splits
+  int64_t round_units = 0;  // units covered by one pass of the grid
+  int64_t rounds = 1;       // passes: more than one when the units do not all fit at once
   size_t slot_bytes = 0;
   int split_major = 0;
 };
@@ -114,32 +116,43 @@ DecodePlan plan_decode_rb(const sgmv_problem_t& p, int rb, int split_major) {
   d.splits = (int)g;
   d.kc = (int)round_up(ceil_div(p.h_in, g), 8);
   d.cw = (int)round_up(ceil_div(p.h_out, g), 8);
-  d.grid = (split_major ? d.num_units : 8 * ceil_div(d.num_units, 8)) * g;
+  d.round_units = split_major ? d.num_units : 8 * ceil_div(d.num_units, 8);
+  d.grid = d.round_units * g;
   d.slot_bytes = (size_t)d.num_units * (size_t)g * parts * d.rb * p.rank * sizeof(uint64_t);
   d.supported = d.grid > 0 && d.grid <= (int64_t)INT32_MAX;
   return d;
 }
 
-int decode_capacity(int dtype, int rank, int rb) {
+// Variant of the decode kernel a call launches: bit 0 at most 64 LoRAs (the
+// pointer tables fetched one entry per lane), bit 1 a row map, bit 2 rank or
+// scale tables.  Their register use, hence their occupancy, differs.
+int decode_variant(const sgmv_problem_t& p, bool map, bool het) {
+  return (p.num_loras <= 64 ? 1 : 0) | (map ? 2 : 0) | (het ? 4 : 0);
+}
+
+int decode_capacity(int dtype, int rank, int rb, int variant) {
   static std::mutex mu;
-  static int cache[kMaxDevices][2][4][3];
-  static bool init[kMaxDevices][2][4][3];
+  static int cache[kMaxDevices][2][4][3][8];
+  static bool init[kMaxDevices][2][4][3][8];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  if (variant < 0 || variant > 7) return 0;
   const int ri = rank == 8 ? 0 : rank == 16 ? 1 : rank == 32 ? 2 : 3;
   const int bi = rb == 1 ? 0 : rb == 4 ? 1 : 2;
   std::lock_guard<std::mutex> lock(mu);
-  if (!init[dev][dtype][ri][bi]) {
-    cache[dev][dtype][ri][bi] = sgmv::decode_resident_capacity(dtype, rank, rb);
-    init[dev][dtype][ri][bi] = true;
+  if (!init[dev][dtype][ri][bi][variant]) {
+    cache[dev][dtype][ri][bi][variant] = sgmv::decode_resident_capacity(
+        dtype, rank, rb, (variant & 1) != 0, (variant & 2) != 0, (variant & 4) != 0);
+    init[dev][dtype][ri][bi][variant] = true;
   }
-  return cache[dev][dtype][ri][bi];
+  return cache[dev][dtype][ri][bi][variant];
 }
 
-// Largest decode grid of any plan: eight co-resident workgroups on each of 256
-// CUs. The workspace is sized over the candidate plans up to this bound, and
-// the device's occupancy picks among them at launch.
-constexpr int64_t kMaxDecodeGrid = 2048;
+// Passes (launches) of the decode kernel over the units beyond which the
+// two-launch route is taken instead (Distinct batches, H = 4096, r = 16: 256
+// rows in 2 passes 20.0 us against 27.4 us; 512 rows in 4 passes 40.2 against
+// 43.2 us).
+constexpr int64_t kMaxDecodeRounds = 4;
 
 // Candidate decode plans, smallest row block first. Blocks of one row keep
 // the most workgroups busy; when segments hold several rows (rows that share
@@ -151,20 +164,45 @@ int decode_candidates(const sgmv_problem_t& p, DecodePlan out[3]) {
   int n = 0;
   for (int rb : {1, 4, 16}) {
     const DecodePlan d = plan_decode_rb(p, rb, split_major);
-    if (d.supported && d.grid <= kMaxDecodeGrid) out[n++] = d;
+    if (d.supported) out[n++] = d;
     if (p.max_seg_len <= rb) break;  // a larger block only adds empty rows
   }
   return n;
 }
 
+// The matrix-core kernels take over segments longer than the decode kernel's
+// row blocks (at ranks 16..64); AUTO picks them when the decode kernel cannot
+// run the call.
+bool stage_uses_mfma(const sgmv_problem_t& p) {
+  if (!sgmv::mfma_supported(p.rank)) return false;
+  if (p.variant == SGMV_VARIANT_MFMA) return true;
+  return p.variant == SGMV_VARIANT_AUTO && p.max_seg_len > 16;
+}
+
 // The first candidate whose grid is co-resident on the current device (the
-// kernel's workgroups wait for each other); unsupported if none is.
-DecodePlan plan_decode(const sgmv_problem_t& p) {
+// kernel's workgroups wait for each other; the capacity is the launched
+// variant's, see decode_variant).  When none is, the smallest row block runs
+// in passes: launches of the largest co-resident grid, each over the next
+// round_units units, up to kMaxDecodeRounds; else unsupported.
+DecodePlan plan_decode(const sgmv_problem_t& p, int variant) {
   DecodePlan c[3];
   const int n = decode_candidates(p, c);
   for (int i = 0; i < n; ++i) {
-    const int cap = decode_capacity(p.dtype, p.rank, c[i].rb);
+    const int cap = decode_capacity(p.dtype, p.rank, c[i].rb, variant);
     if (cap > 0 && c[i].grid <= cap) return c[i];
+  }
+  // (Batches with long segments go to the matrix-core kernels instead.)
+  if (n > 0 && !stage_uses_mfma(p)) {
+    DecodePlan d = c[0];
+    const int64_t cap = decode_capacity(p.dtype, p.rank, d.rb, variant);
+    const int64_t step = d.split_major ? 1 : 8;  // the XCD mapping covers units 8 at a time
+    const int64_t ru = cap / d.splits / step * step;
+    if (ru >= step) {
+      d.round_units = ru;
+      d.grid = ru * d.splits;
+      d.rounds = ceil_div(d.num_units, ru);
+      if (d.rounds <= kMaxDecodeRounds) return d;
+    }
   }
   return DecodePlan{};
 }
@@ -269,14 +307,6 @@ sgmv::MfmaParams mfma_params(const sgmv_problem_t& p, const MfmaPlan& m, const i
   return q;
 }
 
-// The matrix-core kernels take over segments longer than the decode kernel's
-// row blocks (at ranks 16..64); AUTO picks them when the decode kernel cannot
-// run the call.
-bool stage_uses_mfma(const sgmv_problem_t& p) {
-  if (!sgmv::mfma_supported(p.rank)) return false;
-  if (p.variant == SGMV_VARIANT_MFMA) return true;
-  return p.variant == SGMV_VARIANT_AUTO && p.max_seg_len > 16;
-}
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 bool aligned8(const void* p) { return ((uintptr_t)p & 7u) == 0; }
@@ -344,12 +374,15 @@ sgmv::Projection kernel_projection(const sgmv_projection_t& pj) {
 sgmv_status_t apply(const sgmv_problem_t& p, const void* X, const sgmv_projection_t* pj, int np,
                     const int32_t* seg_indptr, const int32_t* lora_idx, const int32_t* row_idx, char* ws,
                     size_t stride, hipStream_t s) {
-  const DecodePlan d = plan_decode(p);
+  bool het = false;
+  for (int i = 0; i < np; ++i) het = het || pj[i].ranks || pj[i].scales;
+  const int variant = decode_variant(p, row_idx != nullptr, het);
+  const DecodePlan d = plan_decode(p, variant);
   const sgmv_route_t route = apply_route(p, d);
   if (route == SGMV_ROUTE_DECODE) {
     // The workgroups of one projection wait for each other; all projections
     // run in one launch when all of them fit on the device at once.
-    if (np > 1 && d.grid * np > decode_capacity(p.dtype, p.rank, d.rb)) {
+    if (np > 1 && d.grid * np > decode_capacity(p.dtype, p.rank, d.rb, variant)) {
       for (int i = 0; i < np; ++i) {
         const sgmv_status_t st =
             apply(p, X, pj + i, 1, seg_indptr, lora_idx, row_idx, ws + (size_t)i * stride, stride, s);
@@ -376,7 +409,15 @@ sgmv_status_t apply(const sgmv_problem_t& p, const void* X, const sgmv_projectio
     q.cw = d.cw;
     q.direct_units = d.direct;
     q.split_major = d.split_major;
-    return hip_status(sgmv::launch_decode(p.dtype, p.rank, d.rb, q, np, s));
+    q.round_units = (int32_t)d.round_units;
+    // One launch per pass of round_units units (a single one when they all
+    // fit on the device at once); each launch's workgroups are co-resident.
+    for (int64_t pass = 0; pass < d.rounds; ++pass) {
+      q.unit_base = (int32_t)(pass * d.round_units);
+      const hipError_t e = sgmv::launch_decode(p.dtype, p.rank, d.rb, q, np, s);
+      if (e != hipSuccess) return SGMV_ERR_HIP;
+    }
+    return SGMV_OK;
   }
   if (route == SGMV_ROUTE_MFMA) {
     // Matrix-core route: the shrink writes one fp32 partial plane of V per H1
@@ -575,11 +616,11 @@ sgmv_status_t sgmv_query_plan(const sgmv_problem_t* p, sgmv_plan_info_t* info) {
   if (st != SGMV_OK) return st;
   if (!info) return SGMV_ERR_INVALID_ARG;
   *info = sgmv_plan_info_t{};
-  const DecodePlan d = plan_decode(*p);
+  const DecodePlan d = plan_decode(*p, decode_variant(*p, false, false));
   info->route = apply_route(*p, d);
   switch (info->route) {
     case SGMV_ROUTE_DECODE:
-      info->launches = 1;
+      info->launches = (int32_t)d.rounds;
       info->rows_per_unit = d.rb;
       info->units = (int32_t)d.num_units;
       info->splits = d.splits;

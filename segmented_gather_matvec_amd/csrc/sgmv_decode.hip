@@ -120,7 +120,8 @@ __global__ __launch_bounds__(kThreads) void sgmv_decode_kernel(DecodeParams p) {
   // them all in the first batch of loads instead of one round trip per
   // argument where it is first used.
   const bool bad_size = (p.num_units | p.splits | p.kc | p.cw | p.direct_units | p.split_major | p.n_rows |
-                         p.h_in | p.h_out | p.num_segs | p.num_loras | (int32_t)(p.slot_stride >> 32)) < 0;
+                         p.h_in | p.h_out | p.num_segs | p.num_loras | p.unit_base | (p.round_units - 1) |
+                         (int32_t)(p.slot_stride >> 32)) < 0;
   bool bad_ptr = (p.seg_indptr == nullptr) | (p.lora_idx == nullptr) | (p.X == nullptr) |
                  (p.slots == nullptr) | (pr.A_ptrs == nullptr) | (pr.B_ptrs == nullptr) | (pr.Y == nullptr);
   // The optional int32 / fp32 tables are 4-byte aligned (the rank and scale
@@ -129,7 +130,9 @@ __global__ __launch_bounds__(kThreads) void sgmv_decode_kernel(DecodeParams p) {
   if constexpr (HET)
     bad_ptr |= ((reinterpret_cast<uintptr_t>(pr.ranks) | reinterpret_cast<uintptr_t>(pr.scales)) & 3) != 0;
   if (bad_size | bad_ptr) return;
-  // Workgroups go round-robin over the XCDs.
+  // Workgroups go round-robin over the XCDs.  This launch covers units
+  // unit_base .. unit_base + round_units - 1 (one launch unless the units do
+  // not all fit on the device at once; the host then launches passes).
   int unit, g;
   if (p.split_major) {
     unit = blockIdx.x / G;
@@ -140,6 +143,7 @@ __global__ __launch_bounds__(kThreads) void sgmv_decode_kernel(DecodeParams p) {
     unit = (slot / G) * kXcds + xcd;
     g = slot - (slot / G) * G;
   }
+  unit += p.unit_base;
   // Workgroups past the last unit (the grid is padded to whole XCD rounds)
   // resolve a unit past every segment and exit after the metadata loads: an
   // exit before them would split the kernel-argument loads into serial rounds.
@@ -405,9 +409,7 @@ __global__ __launch_bounds__(kThreads) void sgmv_decode_kernel(DecodeParams p) {
 
 template <class T, int R, int RB>
 hipError_t launch_t(const DecodeParams& p, int num_proj, hipStream_t stream) {
-  const unsigned units = p.split_major ? (unsigned)p.num_units
-                                       : (unsigned)kXcds * (unsigned)((p.num_units + kXcds - 1) / kXcds);
-  const unsigned grid = units * (unsigned)p.splits;
+  const unsigned grid = (unsigned)p.round_units * (unsigned)p.splits;
   if (grid == 0 || num_proj <= 0) return hipSuccess;
   const bool small = p.num_loras <= 64;
   const bool map = p.row_idx != nullptr;
@@ -435,30 +437,31 @@ int per_cu_t() {
   return n;
 }
 
-// The variants (pointer pool, row map, ranks and scales) use the same
-// registers and LDS within a few VGPRs; the smallest of their occupancies is
-// reported.
+// Workgroups of one variant that fit on the device at once.  `variant` holds
+// the pointer-pool, row-map and rank/scale flags as bits 0, 1, 2.
 template <class T, int R, int RB>
-int capacity_t() {
+int capacity_t(int variant) {
+  using F = int (*)();
+  static constexpr F per_cu[8] = {
+      per_cu_t<T, R, RB, false, false, false>, per_cu_t<T, R, RB, true, false, false>,
+      per_cu_t<T, R, RB, false, true, false>,  per_cu_t<T, R, RB, true, true, false>,
+      per_cu_t<T, R, RB, false, false, true>,  per_cu_t<T, R, RB, true, false, true>,
+      per_cu_t<T, R, RB, false, true, true>,   per_cu_t<T, R, RB, true, true, true>};
   int dev = 0, cus = 0;
-  int per_cu = per_cu_t<T, R, RB, true, false, false>();
-  for (int n : {per_cu_t<T, R, RB, false, false, false>(), per_cu_t<T, R, RB, true, true, false>(),
-                per_cu_t<T, R, RB, false, true, false>(), per_cu_t<T, R, RB, true, false, true>(),
-                per_cu_t<T, R, RB, false, false, true>(), per_cu_t<T, R, RB, true, true, true>(),
-                per_cu_t<T, R, RB, false, true, true>()})
-    per_cu = n < per_cu ? n : per_cu;
+  if (variant < 0 || variant > 7) return 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  return per_cu * cus;
+  return per_cu[variant]() * cus;
 }
 
 // Instantiated (rank, rows per unit) pairs: rank * RB <= 256.
 template <class T>
-hipError_t dispatch(int rank, int rb, const DecodeParams& p, int num_proj, hipStream_t s, int* cap) {
+hipError_t dispatch(int rank, int rb, const DecodeParams& p, int num_proj, hipStream_t s, int* cap,
+                    int variant) {
 #define SGMV_DECODE_CASE(R_, RB_)                          \
   if (rank == R_ && rb == RB_) {                           \
     if (cap) {                                             \
-      *cap = capacity_t<T, R_, RB_>();                     \
+      *cap = capacity_t<T, R_, RB_>(variant);              \
       return hipSuccess;                                   \
     }                                                      \
     return launch_t<T, R_, RB_>(p, num_proj, s);           \
@@ -476,16 +479,17 @@ hipError_t dispatch(int rank, int rb, const DecodeParams& p, int num_proj, hipSt
 bool decode_supported(int rank, int rb) { return rank * rb <= kThreads && (rb == 1 || rb == 4 || rb == 16); }
 
 hipError_t launch_decode(int dtype, int rank, int rb, const DecodeParams& p, int num_proj, hipStream_t stream) {
-  return dtype == 1 ? dispatch<BF16>(rank, rb, p, num_proj, stream, nullptr)
-                    : dispatch<F16>(rank, rb, p, num_proj, stream, nullptr);
+  return dtype == 1 ? dispatch<BF16>(rank, rb, p, num_proj, stream, nullptr, 0)
+                    : dispatch<F16>(rank, rb, p, num_proj, stream, nullptr, 0);
 }
 
-int decode_resident_capacity(int dtype, int rank, int rb) {
+int decode_resident_capacity(int dtype, int rank, int rb, bool small, bool map, bool het) {
+  const int variant = (small ? 1 : 0) | (map ? 2 : 0) | (het ? 4 : 0);
   int cap = 0;
   if (dtype == 1)
-    (void)dispatch<BF16>(rank, rb, DecodeParams{}, 0, nullptr, &cap);
+    (void)dispatch<BF16>(rank, rb, DecodeParams{}, 0, nullptr, &cap, variant);
   else
-    (void)dispatch<F16>(rank, rb, DecodeParams{}, 0, nullptr, &cap);
+    (void)dispatch<F16>(rank, rb, DecodeParams{}, 0, nullptr, &cap, variant);
   return cap;
 }
 

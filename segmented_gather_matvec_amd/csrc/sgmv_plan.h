@@ -76,6 +76,11 @@ struct DecodeParams {
   // XCD. 0: the splits of a unit share an XCD (grid padded to 8 units).
   int32_t split_major;
   int32_t n_rows, h_in, h_out, num_segs, num_loras;
+  // This launch covers units unit_base .. unit_base + round_units - 1 (grid =
+  // round_units * splits; round_units a multiple of 8 unless split_major).  One
+  // launch covers all units when they fit on the device at once; otherwise the
+  // host launches passes of round_units units.
+  int32_t unit_base, round_units;
   int32_t pad_;
   const int32_t* seg_indptr;
   const int32_t* lora_idx;
@@ -89,8 +94,10 @@ struct DecodeParams {
 bool decode_supported(int rank, int rb);
 // Launches num_proj projections (blockIdx.y).
 hipError_t launch_decode(int dtype, int rank, int rb, const DecodeParams& p, int num_proj, hipStream_t stream);
-// Workgroups of the decode kernel that fit on the device at once (0 if unknown).
-int decode_resident_capacity(int dtype, int rank, int rb);
+// Workgroups of the decode kernel variant that fit on the device at once (0 if
+// unknown).
+// small: at most 64 LoRAs; map: a row map; het: rank or scale tables.
+int decode_resident_capacity(int dtype, int rank, int rb, bool small, bool map, bool het);
 
 // Matrix-core kernels for long segments: shrink (+ reduce of the H1 split),
 // then expand.

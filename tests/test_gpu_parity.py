@@ -110,6 +110,33 @@ def test_popularity_larger_row_blocks(kind, n, splits, rows_per_unit):
     assert call.counters_clear()
 
 
+@pytest.mark.parametrize("case", ["distinct_b256", "distinct_b100_h1024_splits32", "skewed_b64_splits64",
+                                  "uniform_b32_splits128"])
+def test_decode_passes_when_units_exceed_the_device(case):
+    """When the units of a decode-shaped batch do not all fit on the device at
+    once, the decode kernel is launched in passes, each over the next units with
+    the largest co-resident grid; the result must equal the oracle, and the plan
+    must be that multi-pass one."""
+    if case == "distinct_b256":
+        call = run_workload(workloads.decode_distinct(n=256), sg.SGMV_VARIANT_AUTO)
+    elif case == "distinct_b100_h1024_splits32":
+        call = run_workload(workloads.decode_distinct(n=100, h=1024), sg.SGMV_VARIANT_FUSED, 32)
+    elif case == "skewed_b64_splits64":
+        call = run_workload(workloads.popularity("skewed", 64), sg.SGMV_VARIANT_FUSED, 64)
+    else:
+        call = run_workload(workloads.popularity("uniform", 32), sg.SGMV_VARIANT_FUSED, 128)
+    info = sg.sgmv_query_plan(call.problem)
+    assert info.route == sg.SGMV_ROUTE_DECODE, info.as_dict()
+    assert info.launches > 1 and info.grid < info.units * info.splits, info.as_dict()
+    rows = None if call.Xh.shape[0] <= 128 else np.r_[0:8, 120:136, call.Xh.shape[0] - 8:call.Xh.shape[0]]
+    mask = None
+    if rows is not None:
+        mask = np.zeros(call.Xh.shape[0], np.uint8)
+        mask[rows] = 1
+    ref = call.oracle_apply(row_mask=mask)
+    assert_close(to_bits(call.apply()), ref, "f16", rows=rows)
+
+
 def _batched_case(w, variant, nproj, seed):
     """nproj projections of one workload's rows: projection 0 uses the workload's
     weights and Y0; the others draw their own (seeded) weights and Y0."""
