@@ -111,7 +111,7 @@ def test_popularity_larger_row_blocks(kind, n, splits, rows_per_unit):
 
 
 @pytest.mark.parametrize("case", ["distinct_b256", "distinct_b100_h1024_splits32", "skewed_b64_splits64",
-                                  "uniform_b32_splits128"])
+                                  "uniform_b32_splits64"])
 def test_decode_passes_when_units_exceed_the_device(case):
     """When the units of a decode-shaped batch do not all fit on the device at
     once, the decode kernel is launched in passes, each over the next units with
@@ -124,7 +124,7 @@ def test_decode_passes_when_units_exceed_the_device(case):
     elif case == "skewed_b64_splits64":
         call = run_workload(workloads.popularity("skewed", 64), sg.SGMV_VARIANT_FUSED, 64)
     else:
-        call = run_workload(workloads.popularity("uniform", 32), sg.SGMV_VARIANT_FUSED, 128)
+        call = run_workload(workloads.popularity("uniform", 32), sg.SGMV_VARIANT_FUSED, 64)
     info = sg.sgmv_query_plan(call.problem)
     assert info.route == sg.SGMV_ROUTE_DECODE, info.as_dict()
     assert info.launches > 1 and info.grid < info.units * info.splits, info.as_dict()
