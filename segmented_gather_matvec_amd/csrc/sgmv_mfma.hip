@@ -17,7 +17,8 @@
 //     that a lane reads the 8 consecutive h of one rank with one 128-bit LDS
 //     read.  Each H1 chunk writes its own fp32 partial plane of V; workgroups
 //     that read the same chunk of A_k run on one XCD.
-//  2. reduce: V = sum of the partial planes, in chunk order (reproducible).
+//  2. reduce: V = sum of the partial planes, in chunk order (reproducible);
+//     the LoRA's scale, if any, is applied to V by the expand.
 //  3. expand: a workgroup takes 64 rows and a group of 128-column chunks.  V is
 //     split into V_hi + V_lo (both in the input format), consumed as a K of 2r
 //     against [B_k; B_k], which keeps about twice the format's significand
@@ -214,48 +215,56 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_shrink_kernel(MfmaParams p
 }
 
 // ---------------------------------------------------------------- reduce
-// V[row] = sum over the ksplit partial planes, in plane order, for the rows
-// of every segment (rows outside all segments are left untouched).  A
-// workgroup takes 16 rows of one 64-row unit; every thread fetches its float4
-// from up to 16 planes at once.
-constexpr int kReduceRows = 16;
-
+// V[row] = sum over the ksplit partial planes, in plane order.  The segments
+// tile the rows [0, seg_indptr[num_segs]) in order, so the rows to reduce
+// are known without looking up any segment: a workgroup takes kThreads / (R/4)
+// rows, every thread one float4 of one row, and all of the thread's plane
+// loads are issued at once (together with the one load of the row bound).
+// Rows outside all segments are left untouched.
 template <int R>
-__global__ __launch_bounds__(kThreads) void sgmv_mfma_reduce_kernel(MfmaParams p) {
-  constexpr int PER_ROWS = kMT / kReduceRows;
-  constexpr int NV = kReduceRows * R / 4;     // float4 of V per workgroup
-  constexpr int NO = (NV + kThreads - 1) / kThreads;
-  constexpr int kBatch = 16;
-  const int unit = blockIdx.x / PER_ROWS;
-  const int part = blockIdx.x - unit * PER_ROWS;
+// Few waves per SIMD are needed (the kernel is one round of loads), so the
+// scheduler may use registers to keep every load of a batch in flight.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2)))
+void sgmv_mfma_reduce_kernel(MfmaParams p) {
+  constexpr int V4 = R / 4;                 // float4 per row of V
+  constexpr int ROWS = kThreads / V4;       // rows per workgroup
+  constexpr int kBatch = 32;                // plane loads in flight per thread
+  const bool bad = (p.n_rows | p.num_segs | (p.ksplit - 1) | (int32_t)(p.partial_stride >> 32) |
+                    (int32_t)(p.proj_stride >> 32)) < 0;
+  const bool bad_ptr = (p.seg_indptr == nullptr) | (p.partials == nullptr) | (p.V == nullptr);
+  if (bad | bad_ptr) return;
+  const int t = threadIdx.x;
+  const int row = blockIdx.x * ROWS + t / V4;
   const float* partials = p.partials + (int64_t)blockIdx.y * p.proj_stride;
   float* V = p.V + (int64_t)blockIdx.y * p.proj_stride;
-  const Unit un = resolve_unit<kMT>(p.seg_indptr, p.lora_idx, p.num_segs, p.num_loras, p.n_rows,
-                                    p.direct_units64, unit);
-  const int rows = un.L - part * kReduceRows;
-  if (rows <= 0) return;
-  // Scale of the LoRA's term, applied to V (one multiply after the sum).
-  const float* scales = p.proj[blockIdx.y].scales;
-  const float sk = scales ? scales[un.k] : 1.f;
-#pragma unroll
-  for (int o = 0; o < NO; ++o) {
-    const int v4 = threadIdx.x + kThreads * o;
-    if (v4 >= NV || v4 * 4 >= rows * R) continue;
-    const int64_t off = (int64_t)(un.r0 + part * kReduceRows) * R + v4 * 4;
-    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+  int end = p.seg_indptr[p.num_segs];
+  end = end < p.n_rows ? end : p.n_rows;
+  const int64_t off = (int64_t)(row < p.n_rows ? row : p.n_rows - 1) * R + (t % V4) * 4;
+  f32x4 s = {0.f, 0.f, 0.f, 0.f};
+  const int64_t span = (int64_t)p.ksplit * p.partial_stride * 4;  // bytes of all planes
+  if (span <= (int64_t)UINT32_MAX) {
+    // One uniform base address and a 32-bit offset per load: all of a
+    // batch's loads are issued before the first add waits.
+    const char* base = reinterpret_cast<const char*>(partials);
+    const uint32_t pstride = (uint32_t)(p.partial_stride * 4);
+    const uint32_t boff = (uint32_t)(off * 4);
     for (int k0 = 0; k0 < p.ksplit; k0 += kBatch) {
       f32x4 v[kBatch];
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
-        const int k = k0 + u < p.ksplit ? k0 + u : p.ksplit - 1;
-        v[u] = *reinterpret_cast<const f32x4*>(partials + (int64_t)k * p.partial_stride + off);
+        const uint32_t k = (uint32_t)(k0 + u < p.ksplit ? k0 + u : p.ksplit - 1);
+        v[u] = *reinterpret_cast<const f32x4*>(base + (k * pstride + boff));
       }
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u)
-        if (k0 + u < p.ksplit) s += v[u];
+      for (int u = 0; u < kBatch; ++u) {
+        const f32x4 a = s + v[u];
+        s = k0 + u < p.ksplit ? a : s;
+      }
     }
-    *reinterpret_cast<f32x4*>(V + off) = s * sk;
+  } else {
+    for (int k = 0; k < p.ksplit; ++k) s += *reinterpret_cast<const f32x4*>(partials + k * p.partial_stride + off);
   }
+  if (row < end) *reinterpret_cast<f32x4*>(V + off) = s;
 }
 
 // ---------------------------------------------------------------- expand
@@ -308,10 +317,13 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_expand_kernel(MfmaParams p
   const int ch0 = grp * p.chunks_per_wg;
   const int ch1 = nchunks < ch0 + p.chunks_per_wg ? nchunks : ch0 + p.chunks_per_wg;
   const uint16_t* Bk = reinterpret_cast<const uint16_t*>(pj.B_ptrs[un.k]);
-  // Rank of the LoRA: B_k has rk rows; V's ranks >= rk are zero.
+  // Rank of the LoRA: B_k has rk rows; V's ranks >= rk are zero.  The LoRA's
+  // scale multiplies V (fp32) before it is split.
   int rk = R;
+  float sk = 1.f;
   if constexpr (EXT) {
     if (pj.ranks) rk = lora_rank<R>(pj.ranks[un.k]);
+    if (pj.scales) sk = pj.scales[un.k];
     if (rk == 0) return;  // Y keeps its value
   }
   uint16_t* Ybase = pj.Y;
@@ -366,7 +378,7 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_expand_kernel(MfmaParams p
     const int rr = o / R, j = o % R;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float v = rr < L ? vv[m][e] : 0.f;
+      const float v = rr < L ? vv[m][e] * sk : 0.f;
       const uint16_t hi = T::round(v);
       const uint16_t lo = T::round(v - T::one(hi));
       lds_v[rr * VST + j + e] = hi;
@@ -458,7 +470,8 @@ hipError_t launch_t(int stage, const MfmaParams& p, int np, hipStream_t s) {
         hipLaunchKernelGGL((sgmv_mfma_shrink_kernel<T, R, false>), dim3(grid, np), dim3(kThreads), 0, s, p);
     }
   } else if (stage == 1) {
-    grid = (unsigned)p.num_units64 * (unsigned)(kMT / kReduceRows);
+    constexpr unsigned rows = kThreads / (R / 4);
+    grid = ((unsigned)p.n_rows + rows - 1) / rows;
     if (grid && np > 0) hipLaunchKernelGGL((sgmv_mfma_reduce_kernel<R>), dim3(grid, np), dim3(kThreads), 0, s, p);
   } else {
     const int nchunks = (p.h_out + kCW - 1) / kCW;
