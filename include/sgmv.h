@@ -157,7 +157,7 @@ typedef struct sgmv_plan_info {
   int32_t route;          /* sgmv_route_t */
   int32_t launches;       /* kernel launches per sgmv_lora_apply call */
   int32_t rows_per_unit;  /* rows of one segment block (decode and vector routes) or of
-                             one expand tile (matrix-core route) */
+                             one shrink tile (matrix-core route) */
   int32_t units;          /* segment blocks planned (an upper bound: empty ones exit at once) */
   int32_t splits;         /* workgroups that share one block (decode, vector) or
                              partial planes of the H1 split (matrix-core) */

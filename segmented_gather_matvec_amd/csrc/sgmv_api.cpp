@@ -222,6 +222,9 @@ struct MfmaPlan {
   int ksplit = 1;
   int kc = 0;
   int chunks_per_wg = 1;
+  int expand_rows = sgmv::kMfmaRowsPerTile;  // rows of one expand tile (16 for short tiles)
+  int64_t units_x = 0;                        // expand units of <= expand_rows rows
+  int direct_x = 1;
   size_t partial_bytes = 0;  // split partials of V, fp32 [ksplit][n_rows][rank]
 };
 
@@ -236,21 +239,23 @@ struct MfmaPlan {
 constexpr int kMfmaShrinkTarget = 1024;
 constexpr int kMfmaExpandTarget = 1024;
 constexpr int kMfmaShortTileRows = 32;   // mean rows per 64-row tile below which tiles count as short
+constexpr int kMfmaShortExpandRows = 16; // expand tile rows for short tiles
 constexpr int kMfmaExpandFallbackCapacity = 512;
 
-int mfma_expand_capacity_cached(int dtype, int rank) {
+int mfma_expand_capacity_cached(int dtype, int rank, int rows) {
   static std::mutex mu;
-  static int cache[kMaxDevices][2][3];
-  static bool init[kMaxDevices][2][3];
+  static int cache[kMaxDevices][2][3][2];
+  static bool init[kMaxDevices][2][3][2];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
   const int ri = rank == 16 ? 0 : rank == 32 ? 1 : 2;
+  const int si = rows == kMfmaShortExpandRows ? 1 : 0;
   std::lock_guard<std::mutex> lock(mu);
-  if (!init[dev][dtype][ri]) {
-    cache[dev][dtype][ri] = sgmv::mfma_expand_capacity(dtype, rank);
-    init[dev][dtype][ri] = true;
+  if (!init[dev][dtype][ri][si]) {
+    cache[dev][dtype][ri][si] = sgmv::mfma_expand_capacity(dtype, rank, rows);
+    init[dev][dtype][ri][si] = true;
   }
-  return cache[dev][dtype][ri];
+  return cache[dev][dtype][ri][si];
 }
 
 int64_t units_for(const sgmv_problem_t& p, int rows, int* direct) {
@@ -278,11 +283,18 @@ MfmaPlan plan_mfma(const sgmv_problem_t& p) {
   m.ksplit = (int)ceil_div(p.h_in, m.kc);
   const int64_t nchunks = ceil_div(p.h_out, sgmv::kMfmaColsPerTile);
   int64_t target = kMfmaExpandTarget;
+  m.units_x = m.units64;
+  m.direct_x = m.direct64;
   if ((int64_t)p.n_rows < kMfmaShortTileRows * units) {
-    target = sgmv::mfma_supported(p.rank) ? mfma_expand_capacity_cached(p.dtype, p.rank) : 0;
+    // Short tiles: 16-row expand tiles (all four waves compute) and a grid
+    // that is resident at once.
+    m.expand_rows = kMfmaShortExpandRows;
+    m.units_x = units_for(p, kMfmaShortExpandRows, &m.direct_x);
+    target = sgmv::mfma_supported(p.rank) ? mfma_expand_capacity_cached(p.dtype, p.rank, m.expand_rows) : 0;
     if (target <= 0) target = kMfmaExpandFallbackCapacity;
   }
-  const int64_t groups = std::max<int64_t>(1, std::min<int64_t>(nchunks, target / units));
+  const int64_t groups =
+      std::max<int64_t>(1, std::min<int64_t>(nchunks, target / std::max<int64_t>(m.units_x, 1)));
   m.chunks_per_wg = (int)ceil_div(nchunks, groups);
   m.partial_bytes = (size_t)m.ksplit * (size_t)p.n_rows * p.rank * sizeof(float);
   return m;
@@ -304,6 +316,9 @@ sgmv::MfmaParams mfma_params(const sgmv_problem_t& p, const MfmaPlan& m, const i
   q.ksplit = m.ksplit;
   q.kc = m.kc;
   q.chunks_per_wg = m.chunks_per_wg;
+  q.expand_rows = m.expand_rows;
+  q.num_units_x = (int32_t)m.units_x;
+  q.direct_units_x = m.direct_x;
   return q;
 }
 

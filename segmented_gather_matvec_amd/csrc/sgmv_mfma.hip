@@ -19,10 +19,11 @@
 //     that read the same chunk of A_k run on one XCD.
 //  2. reduce: V = sum of the partial planes, in chunk order (reproducible);
 //     the LoRA's scale, if any, is applied to V by the expand.
-//  3. expand: a workgroup takes 64 rows and a group of 128-column chunks.  V is
-//     split into V_hi + V_lo (both in the input format), consumed as a K of 2r
-//     against [B_k; B_k], which keeps about twice the format's significand
-//     bits of V; its MFMA fragments stay in registers for all chunks.  Each
+//  3. expand: a workgroup takes 64 rows (16 when the segments are short) and a
+//     group of 128-column chunks.  V is split into V_hi + V_lo (both in the
+//     input format), consumed as a K of 2r against [B_k; B_k], which keeps
+//     about twice the format's significand bits of V; its MFMA fragments stay
+//     in registers for all chunks.  Each
 //     chunk of B_k is staged transposed ([c][j]) in LDS while the next chunk's
 //     B_k and Y are in flight; the result tile goes through LDS so that Y is
 //     read and written with 128-bit accesses.
@@ -268,12 +269,22 @@ void sgmv_mfma_reduce_kernel(MfmaParams p) {
 }
 
 // ---------------------------------------------------------------- expand
-template <class T, int R, bool EXT>
+// MT rows per tile.  MT = 64: wave w computes rows 16w..16w+15 over the whole
+// chunk.  MT = 16 (short segments, e.g. decode batches with a few rows per
+// LoRA): the four waves share the 16 rows and each computes a quarter of the
+// chunk's columns, so no wave idles and the smaller LDS footprint lets more
+// workgroups stream B_k at once.
+template <class T, int R, bool EXT, int MT>
 __global__ __launch_bounds__(kThreads) void sgmv_mfma_expand_kernel(MfmaParams p) {
   constexpr int K2 = 2 * R;            // virtual K: [V_hi | V_lo] against [B_k; B_k]
   constexpr int KSTEPS = K2 / 32;
+  constexpr int WR = MT / 16;          // 16-row groups of the tile
+  constexpr int WC = kWaves / WR;      // waves that share a row group, each on its own columns
+  static_assert(WR * WC == kWaves, "tile rows are 16 or 64");
   constexpr int NTC = kCW / 16;        // 16-wide column tiles per chunk
+  constexpr int NTW = NTC / WC;        // column tiles per wave
   constexpr int CV = kCW / 8;          // 128-bit column vectors per chunk row
+  constexpr int CVW = CV / WC;         // ... of one wave's columns
   constexpr int BST = R + 8;           // LDS stride (halves) of transposed B_k, per column
   // Within a column, B_k's ranks sit in groups of 8 (one 128-bit MFMA operand
   // read); group g of column c is stored at group g ^ swz(c).  The transposed
@@ -283,11 +294,11 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_expand_kernel(MfmaParams p
   constexpr int GMASK = R / 8 - 1;
   auto swz = [](int c) { return (c >> 4) & GMASK; };
   constexpr int VST = K2 + 8;          // LDS stride (halves) of [V_hi | V_lo], per row
-  constexpr int OST = kCW + 4;         // LDS stride (floats) of the result tile
+  constexpr int OST = kCW / WC + 4;    // LDS stride (floats) of a wave's result tile
   constexpr int NBP = (R / 2 * CV + kThreads - 1) / kThreads;  // (j, j+1) B_k vector pairs per thread
-  constexpr int NYV = 16 * CV / 64;    // Y vectors per lane (16 rows of the wave)
+  constexpr int NYV = 16 * CVW / 64;   // Y vectors per lane (16 rows of the wave's columns)
   __shared__ __attribute__((aligned(16))) uint16_t lds_bt[kCW * BST];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_v[kMT * VST];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_v[MT * VST];
   __shared__ __attribute__((aligned(16))) float lds_o[kWaves * 16 * OST];
 
   const int t = threadIdx.x;
@@ -295,9 +306,11 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_expand_kernel(MfmaParams p
   const int wave = t >> 6;
   const int q = lane >> 4;
   const int ml = lane & 15;
+  const int wr = wave / WC;            // row group of the wave
+  const int colw = (wave % WC) * (kCW / WC);  // first chunk column of the wave
   const Projection pj = p.proj[blockIdx.y];
   // Malformed launch test; it also batches the argument loads (as in the shrink).
-  const bool bad_size = (p.n_rows | p.h_out | p.num_segs | p.num_loras | p.num_units64 | p.direct_units64 |
+  const bool bad_size = (p.n_rows | p.h_out | p.num_segs | p.num_loras | p.num_units_x | p.direct_units_x |
                          (p.chunks_per_wg - 1) | (int32_t)(p.proj_stride >> 32)) < 0;
   const bool bad_ptr = (p.seg_indptr == nullptr) | (p.lora_idx == nullptr) | (p.V == nullptr) |
                        (pj.B_ptrs == nullptr) | (pj.Y == nullptr);
@@ -307,11 +320,11 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_expand_kernel(MfmaParams p
   // Linear order: column group major, so the row units that read one slice of
   // B_k share an XCD.
   const int idx = xcd_linear_index();
-  if (idx >= p.num_units64 * ngroups) return;
-  const int grp = idx / p.num_units64;
-  const int unit = idx - grp * p.num_units64;
-  const Unit un = resolve_unit<kMT>(p.seg_indptr, p.lora_idx, p.num_segs, p.num_loras, p.n_rows,
-                                    p.direct_units64, unit);
+  if (idx >= p.num_units_x * ngroups) return;
+  const int grp = idx / p.num_units_x;
+  const int unit = idx - grp * p.num_units_x;
+  const Unit un = resolve_unit<MT>(p.seg_indptr, p.lora_idx, p.num_segs, p.num_loras, p.n_rows,
+                                   p.direct_units_x, unit);
   if (un.L <= 0) return;
   const int L = un.L, r0 = un.r0;
   const int ch0 = grp * p.chunks_per_wg;
@@ -333,7 +346,7 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_expand_kernel(MfmaParams p
   int yrow[NYV];
 #pragma unroll
   for (int u = 0; u < NYV; ++u) {
-    const int rr = wave * 16 + (lane + 64 * u) / CV;
+    const int rr = wr * 16 + (lane + 64 * u) / CVW;
     const int srow = r0 + (rr < L ? rr : 0);
     yrow[u] = EXT && p.row_idx ? p.row_idx[srow] : srow;
   }
@@ -353,8 +366,8 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_expand_kernel(MfmaParams p
 #pragma unroll
     for (int u = 0; u < NYV; ++u) {
       const int v = lane + 64 * u;
-      const int rr = wave * 16 + v / CV;
-      const int c = c0 + (v % CV) * 8;
+      const int rr = wr * 16 + v / CVW;
+      const int c = c0 + colw + (v % CVW) * 8;
       const bool ok = rr < L && ch < ch1 && c < p.h_out;
       yv[u] = load_stream(Ybase + (int64_t)yrow[u] * p.h_out + (ok ? c : 0));
     }
@@ -362,7 +375,8 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_expand_kernel(MfmaParams p
   // V of the tile rows (all fetched at once, ahead of the first chunk's loads
   // so that waiting for V does not wait for them), split hi/lo, then this
   // wave's MFMA A fragments.
-  constexpr int NV4 = kMT * R / 4 / kThreads;  // float4 of V per thread
+  constexpr int NVF = MT * R / 4;                       // float4 of V in the tile
+  constexpr int NV4 = (NVF + kThreads - 1) / kThreads;  // ... per thread
   f32x4 vv[NV4];
 #pragma unroll
   for (int m = 0; m < NV4; ++m) {
@@ -375,20 +389,22 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_expand_kernel(MfmaParams p
 #pragma unroll
   for (int m = 0; m < NV4; ++m) {
     const int o = (t + kThreads * m) * 4;
-    const int rr = o / R, j = o % R;
+    if (o < NVF * 4) {
+      const int rr = o / R, j = o % R;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float v = rr < L ? vv[m][e] * sk : 0.f;
-      const uint16_t hi = T::round(v);
-      const uint16_t lo = T::round(v - T::one(hi));
-      lds_v[rr * VST + j + e] = hi;
-      lds_v[rr * VST + R + j + e] = lo;
+      for (int e = 0; e < 4; ++e) {
+        const float v = rr < L ? vv[m][e] * sk : 0.f;
+        const uint16_t hi = T::round(v);
+        const uint16_t lo = T::round(v - T::one(hi));
+        lds_v[rr * VST + j + e] = hi;
+        lds_v[rr * VST + R + j + e] = lo;
+      }
     }
   }
   __syncthreads();
   u32x4 af[KSTEPS];
 #pragma unroll
-  for (int s = 0; s < KSTEPS; ++s) af[s] = load_vec(&lds_v[(wave * 16 + ml) * VST + s * 32 + q * 8]);
+  for (int s = 0; s < KSTEPS; ++s) af[s] = load_vec(&lds_v[(wr * 16 + ml) * VST + s * 32 + q * 8]);
   float* out = lds_o + wave * 16 * OST;
 
   auto compute = [&](int ch, const u32x4 (&bv)[NBP][2], const u32x4 (&yv)[NYV]) {
@@ -409,14 +425,15 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_expand_kernel(MfmaParams p
     // A wave whose 16 rows are all past the segment has nothing to compute or
     // store; each wave's result tile is its own, so only the wave itself
     // waits for it (LDS operations of one wave complete in order).
-    if (wave * 16 >= L) return;
+    if (wr * 16 >= L) return;
 #pragma unroll
-    for (int n = 0; n < NTC; ++n) {
+    for (int n = 0; n < NTW; ++n) {
+      const int cn = colw + n * 16;    // first chunk column of the tile
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) {
         const int kb = (s * 32 + q * 8) % R;  // rank of the B_k copy this k-group reads
-        acc = mfma<T>(af[s], load_vec(&lds_bt[(n * 16 + ml) * BST + (((kb >> 3) ^ swz(n * 16)) << 3)]), acc);
+        acc = mfma<T>(af[s], load_vec(&lds_bt[(cn + ml) * BST + (((kb >> 3) ^ swz(cn)) << 3)]), acc);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) out[(q * 4 + i) * OST + n * 16 + ml] = acc[i];
@@ -427,15 +444,16 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_expand_kernel(MfmaParams p
 #pragma unroll
     for (int u = 0; u < NYV; ++u) {
       const int v = lane + 64 * u;
-      const int rl = v / CV;
-      const int cl = (v % CV) * 8;
-      const int rr = wave * 16 + rl;
-      if (rr < L && ch < ch1 && c0 + cl < p.h_out) {
+      const int rl = v / CVW;
+      const int cl = (v % CVW) * 8;
+      const int rr = wr * 16 + rl;
+      const int c = c0 + colw + cl;
+      if (rr < L && ch < ch1 && c < p.h_out) {
         float yf[8];
         unpack8<T>(yv[u], yf);
 #pragma unroll
         for (int e = 0; e < 8; ++e) yf[e] += out[rl * OST + cl + e];
-        store_vec(Ybase + (int64_t)yrow[u] * p.h_out + c0 + cl, pack8<T>(yf));
+        store_vec(Ybase + (int64_t)yrow[u] * p.h_out + c, pack8<T>(yf));
       }
     }
   };
@@ -474,13 +492,16 @@ hipError_t launch_t(int stage, const MfmaParams& p, int np, hipStream_t s) {
     grid = ((unsigned)p.n_rows + rows - 1) / rows;
     if (grid && np > 0) hipLaunchKernelGGL((sgmv_mfma_reduce_kernel<R>), dim3(grid, np), dim3(kThreads), 0, s, p);
   } else {
+    if (p.expand_rows != 16 && p.expand_rows != kMT) return hipErrorInvalidValue;
     const int nchunks = (p.h_out + kCW - 1) / kCW;
-    grid = xcd_grid((unsigned)p.num_units64 * (unsigned)((nchunks + p.chunks_per_wg - 1) / p.chunks_per_wg));
+    grid = xcd_grid((unsigned)p.num_units_x * (unsigned)((nchunks + p.chunks_per_wg - 1) / p.chunks_per_wg));
     if (grid && np > 0) {
-      if (ext)
-        hipLaunchKernelGGL((sgmv_mfma_expand_kernel<T, R, true>), dim3(grid, np), dim3(kThreads), 0, s, p);
-      else
-        hipLaunchKernelGGL((sgmv_mfma_expand_kernel<T, R, false>), dim3(grid, np), dim3(kThreads), 0, s, p);
+      using K = void (*)(MfmaParams);
+      // [short tiles][ext]
+      static constexpr K kernels[2][2] = {
+          {sgmv_mfma_expand_kernel<T, R, false, kMT>, sgmv_mfma_expand_kernel<T, R, true, kMT>},
+          {sgmv_mfma_expand_kernel<T, R, false, 16>, sgmv_mfma_expand_kernel<T, R, true, 16>}};
+      hipLaunchKernelGGL(kernels[p.expand_rows == 16][ext], dim3(grid, np), dim3(kThreads), 0, s, p);
     }
   }
   return grid && np > 0 ? hipGetLastError() : hipSuccess;
@@ -505,14 +526,16 @@ hipError_t launch_stage(int dtype, int rank, int stage, const MfmaParams& p, int
 bool mfma_supported(int rank) { return rank == 16 || rank == 32 || rank == 64; }
 
 // The smaller occupancy of the plain and the extended variant.
-template <class T, int R>
+template <class T, int R, int MT>
 int expand_capacity_t() {
   int per_cu = 0, per_cu2 = 0, dev = 0, cus = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &per_cu, reinterpret_cast<const void*>(&sgmv_mfma_expand_kernel<T, R, false>), kThreads, 0) != hipSuccess)
+          &per_cu, reinterpret_cast<const void*>(&sgmv_mfma_expand_kernel<T, R, false, MT>), kThreads, 0) !=
+      hipSuccess)
     return 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &per_cu2, reinterpret_cast<const void*>(&sgmv_mfma_expand_kernel<T, R, true>), kThreads, 0) != hipSuccess)
+          &per_cu2, reinterpret_cast<const void*>(&sgmv_mfma_expand_kernel<T, R, true, MT>), kThreads, 0) !=
+      hipSuccess)
     return 0;
   per_cu = per_cu < per_cu2 ? per_cu : per_cu2;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
@@ -520,11 +543,16 @@ int expand_capacity_t() {
   return per_cu * cus;
 }
 
-int mfma_expand_capacity(int dtype, int rank) {
+template <class T, int R>
+int expand_capacity_rows(int rows) {
+  return rows == 16 ? expand_capacity_t<T, R, 16>() : expand_capacity_t<T, R, kMT>();
+}
+
+int mfma_expand_capacity(int dtype, int rank, int rows) {
   switch (rank) {
-    case 16: return dtype == 1 ? expand_capacity_t<BF16, 16>() : expand_capacity_t<F16, 16>();
-    case 32: return dtype == 1 ? expand_capacity_t<BF16, 32>() : expand_capacity_t<F16, 32>();
-    case 64: return dtype == 1 ? expand_capacity_t<BF16, 64>() : expand_capacity_t<F16, 64>();
+    case 16: return dtype == 1 ? expand_capacity_rows<BF16, 16>(rows) : expand_capacity_rows<F16, 16>(rows);
+    case 32: return dtype == 1 ? expand_capacity_rows<BF16, 32>(rows) : expand_capacity_rows<F16, 32>(rows);
+    case 64: return dtype == 1 ? expand_capacity_rows<BF16, 64>(rows) : expand_capacity_rows<F16, 64>(rows);
   }
   return 0;
 }

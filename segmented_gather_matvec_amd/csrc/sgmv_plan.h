@@ -109,6 +109,8 @@ struct MfmaParams {
   int32_t n_rows, h_in, h_out, num_segs, num_loras;
   int32_t num_units64, direct_units64;  // units of <= 64 rows of one segment
   int32_t ksplit, kc, chunks_per_wg;
+  // Expand tiles of expand_rows (16 or 64) rows of one segment: num_units_x of them.
+  int32_t expand_rows, num_units_x, direct_units_x, pad_;
   const int32_t* seg_indptr;
   const int32_t* lora_idx;
   const int32_t* row_idx;  // null, or row of X / Y of each sorted row
@@ -121,8 +123,8 @@ struct MfmaParams {
 };
 
 bool mfma_supported(int rank);
-// Expand workgroups that fit on the device at once (0 if unknown).
-int mfma_expand_capacity(int dtype, int rank);
+// Expand workgroups with `rows`-row tiles that fit on the device at once (0 if unknown).
+int mfma_expand_capacity(int dtype, int rank, int rows);
 // Shrink into the partial planes, then reduce them into V (two launches).
 hipError_t launch_mfma_shrink(int dtype, int rank, const MfmaParams& p, int num_proj, hipStream_t stream);
 hipError_t launch_mfma_expand(int dtype, int rank, const MfmaParams& p, int num_proj, hipStream_t stream);
