@@ -11,6 +11,9 @@ Contents
   loops over rows that decode fp16/bf16 inputs exactly and evaluate
   ``Y0[i] + (x_i @ A_k) @ B_k`` as the Punica README states it (page
   "Punica：多 LoRA 模型统一服务框架", LoRA and multi-LoRA paragraphs).
+* ``sgmv_base_apply``: the base projection with the LoRA term,
+  ``x_i @ W + (x_i @ A_k) @ B_k`` (same page, LoRA paragraph), for rows with
+  and without a segment.
 * ``build_segments``: the segment builder written as a plain stable sort in
   Python (same page, multi-LoRA and SGMV paragraphs: every request is bound
   to its LoRA, and requests sharing a LoRA form one segment).
@@ -69,6 +72,9 @@ def _bind(path: str):
     lib.oracle_sgmv_apply.argtypes = [ctypes.c_int, i32, i32, i32, i32, p, p, p, p, p, i32, p, p, i32,
                                       p, p, p, p, ctypes.c_int]
     lib.oracle_sgmv_apply.restype = ctypes.c_int
+    lib.oracle_sgmv_base_apply.argtypes = [ctypes.c_int, i32, i32, i32, i32, p, p, p, p, i32, p, p, i32, p,
+                                           p, ctypes.c_int]
+    lib.oracle_sgmv_base_apply.restype = ctypes.c_int
     return lib
 
 
@@ -216,6 +222,37 @@ def sgmv_apply(dtype, X, A, B, seg_indptr, lora_idx, Y0, *, scales=None, rank=No
     if rc != 0:
         raise ValueError("oracle: invalid segment metadata")
     return (Y, V) if want_v else Y
+
+
+def sgmv_base_apply(dtype, X, W, A, B, seg_indptr, lora_idx, *, row_mask=None, nthreads=0):
+    """fp64 Y = X @ W + per-row (x_i @ A_k) @ B_k (rows no segment covers: X @ W only).
+
+    W is [h_in, h_out]; every A[k] is [h_in, r] and B[k] is [r, h_out] with one r.
+    Rows outside ``row_mask`` (when given) are left NaN."""
+    X, W = _u16(X), _u16(W)
+    n, h_in = X.shape
+    if W.ndim != 2 or W.shape[0] != h_in:
+        raise ValueError(f"W {W.shape} is not [{h_in}, h_out]")
+    h_out = W.shape[1]
+    ta, ka = _table(A)
+    tb, kb = _table(B)
+    if len(ka) != len(kb):
+        raise ValueError("A and B must list the same number of LoRAs")
+    a0 = _u16(A[0])
+    rank = int(a0.shape[1])
+    for k in range(len(ka)):
+        a, b = _u16(A[k]), _u16(B[k])
+        if a.shape != (h_in, rank) or b.shape != (rank, h_out):
+            raise ValueError(f"LoRA {k}: A {a.shape} and B {b.shape} are not [{h_in}, {rank}] and [{rank}, {h_out}]")
+    sp, li = _i32(seg_indptr), _i32(lora_idx)
+    Y = np.full((n, h_out), np.nan)
+    m, mp = _mask(row_mask, n)
+    rc = _load().oracle_sgmv_base_apply(DTYPES[dtype], n, h_in, h_out, rank, _ptr(X), _ptr(W),
+                                        ctypes.addressof(ta), ctypes.addressof(tb), len(ka), _ptr(sp),
+                                        _ptr(li), len(li), mp, _ptr(Y), nthreads)
+    if rc != 0:
+        raise ValueError("oracle: invalid segment metadata")
+    return Y
 
 
 def build_segments(req_lora: Sequence[int], num_loras: int):

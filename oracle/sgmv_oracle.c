@@ -219,3 +219,55 @@ int oracle_sgmv_apply(int dtype, int32_t n_rows, int32_t h_in, int32_t h_out, in
   free(seg_of_row);
   return 0;
 }
+
+/*
+ * Base projection plus the LoRA term.  The LoRA paragraph gives a row vector x
+ * the output x@W + x@A@B; the multi-LoRA paragraph computes X@W for the whole
+ * batch and adds each row's own LoRA term:
+ *   Y[i, c] = sum_h X[i, h] * W[h, c]  (h ascending)
+ *             + [row i covered] sum_j v[j] * B_k[j, c]  (j ascending),
+ *   v[j] = sum_h X[i, h] * A_k[h, j],  k the LoRA of row i's segment.
+ * W is [h_in, h_out] row-major.  A row no segment covers gets the base term
+ * only.  Every output's base sum runs over h in ascending order (the loop
+ * below walks W row by row and keeps h_out running sums).  row_mask
+ * (nullable) limits the work to rows with a non-zero mask byte; masked-out
+ * rows are not written.  Returns 0, or -1 on invalid metadata.
+ */
+int oracle_sgmv_base_apply(int dtype, int32_t n_rows, int32_t h_in, int32_t h_out, int32_t rank,
+                           const uint16_t* X, const uint16_t* W, const uint16_t* const* A,
+                           const uint16_t* const* B, int32_t num_loras, const int32_t* seg_indptr,
+                           const int32_t* lora_idx, int32_t num_segs, const uint8_t* row_mask,
+                           double* Y, int nthreads) {
+  int32_t* seg_of_row = row_segments(n_rows, seg_indptr, lora_idx, num_segs, num_loras);
+  if (!seg_of_row) return -1;
+  if (rank <= 0 || rank > 4096) {
+    free(seg_of_row);
+    return -1;
+  }
+  set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int32_t i = 0; i < n_rows; ++i) {
+    if (row_mask && !row_mask[i]) continue;
+    double* y = Y + (int64_t)i * h_out;
+    const uint16_t* x_row = X + (int64_t)i * h_in;
+    for (int32_t c = 0; c < h_out; ++c) y[c] = 0.0;
+    for (int32_t h = 0; h < h_in; ++h) {  /* base: running sums over h */
+      const double xh = decode(dtype, x_row[h]);
+      const uint16_t* w_row = W + (int64_t)h * h_out;
+      for (int32_t c = 0; c < h_out; ++c) y[c] += xh * decode(dtype, w_row[c]);
+    }
+    const int32_t s = seg_of_row[i];
+    if (s < 0) continue;
+    double v[4096];
+    const int32_t k = lora_idx[s];  /* LoRA of the row's segment */
+    row_shrink(dtype, h_in, rank, x_row, A[k], v);
+    for (int32_t c = 0; c < h_out; ++c) {
+      double acc = 0.0;
+      for (int32_t j = 0; j < rank; ++j)  /* LoRA term: v @ B_k */
+        acc += v[j] * decode(dtype, B[k][(int64_t)j * h_out + c]);
+      y[c] += acc;
+    }
+  }
+  free(seg_of_row);
+  return 0;
+}

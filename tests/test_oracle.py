@@ -309,6 +309,75 @@ def test_scale_multiplies_the_term_only():
     assert not np.array_equal(one, y0)  # the term is not zero
 
 
+# ---------------------------------------------------------------- base projection + LoRA term
+
+def base_case(seed, n=8, h_in=32, h_out=24, rank=4, P=3, dtype="f16"):
+    rng, X, A, B, _ = rand_case(seed, n, h_in, h_out, rank, P, dtype)
+    W = workloads.to_bits(rng.standard_normal((h_in, h_out), dtype=np.float32) * 0.2, dtype)
+    return X, W, A, B
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_base_apply_with_zero_weight_is_the_lora_term(dtype):
+    """W = 0: the base term vanishes and Y is sgmv_apply's result on Y0 = 0, bit for bit."""
+    X, W, A, B = base_case(40, dtype=dtype)
+    seg, lidx = [0, 3, 4, 8], [2, 0, 2]
+    got = oracle.sgmv_base_apply(dtype, X, np.zeros_like(W), A, B, seg, lidx)
+    ref = oracle.sgmv_apply(dtype, X, A, B, seg, lidx, np.zeros((8, 24), np.uint16))
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_base_apply_without_segments_is_a_matmul(dtype):
+    """No segment: Y = X @ W, against numpy's fp64 product of the decoded operands."""
+    X, W, A, B = base_case(41, h_in=40, h_out=24, dtype=dtype)
+    got = oracle.sgmv_base_apply(dtype, X, W, A, B, [0], [])
+    np.testing.assert_allclose(got, np_decode(X, dtype) @ np_decode(W, dtype), rtol=1e-12, atol=1e-12)
+
+
+def test_base_apply_identity_weight_adds_the_input():
+    """W = I (h_in = h_out): Y = X + the LoRA term, i.e. sgmv_apply with Y0 = X, bit for bit."""
+    X, W, A, B = base_case(42, h_in=24, h_out=24)
+    eye = workloads.to_bits(np.eye(24, dtype=np.float32), "f16")
+    seg, lidx = [0, 5, 8], [1, 0]
+    assert np.array_equal(oracle.sgmv_base_apply("f16", X, eye, A, B, seg, lidx),
+                          oracle.sgmv_apply("f16", X, A, B, seg, lidx, X))
+
+
+def test_base_apply_uncovered_rows_get_the_base_term_only():
+    X, W, A, B = base_case(43)
+    got = oracle.sgmv_base_apply("f16", X, W, A, B, [0, 2, 5], [1, 0])
+    base = oracle.sgmv_base_apply("f16", X, W, A, B, [0], [])
+    assert np.array_equal(got[5:], base[5:])
+    assert not np.allclose(got[:5], base[:5])
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_base_apply_brute_force(dtype):
+    """Per-row numpy evaluation of x @ W + (x @ A_k) @ B_k (h_in != h_out, LoRAs reused)."""
+    X, W, A, B = base_case(44, h_in=40, h_out=24, dtype=dtype)
+    seg, lidx = [0, 1, 4, 6], [2, 2, 0]
+    got = oracle.sgmv_base_apply(dtype, X, W, A, B, seg, lidx)
+    Xd = np_decode(X, dtype)
+    ref = Xd @ np_decode(W, dtype)
+    for s in range(len(lidx)):
+        Ak, Bk = np_decode(A[lidx[s]], dtype), np_decode(B[lidx[s]], dtype)
+        for i in range(seg[s], seg[s + 1]):
+            ref[i] += (Xd[i] @ Ak) @ Bk
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_base_apply_row_mask_computes_only_listed_rows():
+    X, W, A, B = base_case(45)
+    seg, lidx = [0, 4, 8], [1, 2]
+    full = oracle.sgmv_base_apply("f16", X, W, A, B, seg, lidx)
+    mask = np.zeros(8, np.uint8)
+    mask[[2, 7]] = 1
+    part = oracle.sgmv_base_apply("f16", X, W, A, B, seg, lidx, row_mask=mask)
+    assert np.array_equal(part[[2, 7]], full[[2, 7]])
+    assert np.isnan(part[[0, 1, 3, 4, 5, 6]]).all()
+
+
 # ---------------------------------------------------------------- builder
 
 def test_builder_golden_examples():

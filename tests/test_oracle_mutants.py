@@ -28,11 +28,23 @@ MUTANTS = {
                               "y[c] = scale * (decode(dtype, y0_row[c]) + acc);"),
     "rank_table_short_by_one_vector": ("const int32_t rk = ranks ? ranks[k] : rank;",
                                        "const int32_t rk = ranks ? (ranks[k] > 8 ? ranks[k] - 8 : 0) : rank;"),
-    "segment_index_as_lora": ("const int32_t k = lora_idx[s];", "const int32_t k = s % num_loras;"),
+    "segment_index_as_lora": ("const int32_t k = lora_idx[s];\n", "const int32_t k = s % num_loras;\n"),
+    "base_segment_index_as_lora": ("const int32_t k = lora_idx[s];  /* LoRA",
+                                   "const int32_t k = s % num_loras;  /* LoRA"),
     "last_row_of_segment_dropped": ("for (int32_t i = lo; i < hi; ++i) seg_of_row[i] = s;",
                                     "for (int32_t i = lo; i + 1 < hi; ++i) seg_of_row[i] = s;"),
-    "first_input_column_dropped": ("for (int32_t h = 0; h < h_in; ++h)",
-                                   "for (int32_t h = 1; h < h_in; ++h)"),
+    "first_input_column_dropped": ("for (int32_t h = 0; h < h_in; ++h)\n      acc +=",
+                                   "for (int32_t h = 1; h < h_in; ++h)\n      acc +="),
+    "base_weight_transposed": ("y[c] += xh * decode(dtype, w_row[c]);",
+                               "y[c] += xh * decode(dtype, W[(int64_t)c * h_in + h]);"),
+    "base_term_dropped": ("y[c] += xh * decode(dtype, w_row[c]);", "y[c] += 0.0 * xh * decode(dtype, w_row[c]);"),
+    "base_first_input_row_dropped": ("for (int32_t h = 0; h < h_in; ++h) {  /* base",
+                                     "for (int32_t h = 1; h < h_in; ++h) {  /* base"),
+    "base_lora_term_subtracted": ("      y[c] += acc;", "      y[c] -= acc;"),
+    "base_last_rank_dropped": ("for (int32_t j = 0; j < rank; ++j)  /* LoRA term",
+                               "for (int32_t j = 0; j + 1 < rank; ++j)  /* LoRA term"),
+    "base_lora_from_first_row": ("row_shrink(dtype, h_in, rank, x_row, A[k], v);",
+                                 "row_shrink(dtype, h_in, rank, X, A[k], v);"),
     "last_rank_dropped": ("for (int32_t j = 0; j < rank; ++j) acc += v[j]",
                           "for (int32_t j = 0; j + 1 < rank; ++j) acc += v[j]"),
     "f16_subnormal_scale": ("mag = ldexp((double)frac, -24);", "mag = ldexp((double)frac, -25);"),
@@ -59,6 +71,11 @@ PINS = [
     lambda: pins.test_rank_table_equals_zero_padding("f16"),
     pins.test_rank_zero_lora_adds_nothing,
     pins.test_scale_multiplies_the_term_only,
+    lambda: pins.test_base_apply_with_zero_weight_is_the_lora_term("f16"),
+    lambda: pins.test_base_apply_without_segments_is_a_matmul("bf16"),
+    pins.test_base_apply_identity_weight_adds_the_input,
+    pins.test_base_apply_uncovered_rows_get_the_base_term_only,
+    lambda: pins.test_base_apply_brute_force("f16"),
 ]
 
 
