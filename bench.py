@@ -131,6 +131,10 @@ MODEL_WORKLOADS = ["llama13b_r64_b256_forward"]
 # storage, per-LoRA rank table and scales), against the same batch padded to
 # rank 64 (decode_distinct_h4096_r64_b32).
 HET_WORKLOADS = ["decode_mixedrank_h4096_r64_b32"]
+# Base projection with the LoRA term (sgmv_base_lora_apply): Y = X @ W + the
+# per-row LoRA term, Distinct decode batches.
+BASE_WORKLOADS = ["base_decode_distinct_h4096_r16_b32", "base_decode_distinct_h4096_r16_b8",
+                  "base_decode_distinct_h4096_r16_b64", "base_decode_distinct_h11008to4096_r16_b32"]
 
 
 class SingleCallBench:
@@ -691,12 +695,136 @@ def cpu_baseline(seconds=10.0):
                        f"{per_call * 1e3:.2f} ms/call, {w.n_rows / per_call:.0f} rows/s")}
 
 
+class BaseBench:
+    """One sgmv_base_lora_apply call per step: Y = X @ W + (X @ A_k) @ B_k for a
+    Distinct decode batch (row i -> LoRA i), fp16.  W rotates through >= 1 GiB of
+    copies, the LoRAs through a >= 1 GiB pool and X / Y through 64 copies, so no
+    step finds its weights in the 256 MB Infinity Cache.  For context the config
+    also carries the unfused composition on the same buffers: torch's X @ W
+    (written to Y), then sgmv_lora_apply adding the LoRA term (two roundings)."""
+
+    def __init__(self, name):
+        import re
+        import torch
+        import numpy as np
+        import segmented_gather_matvec_amd as sg
+        import workloads as wl
+
+        m = re.fullmatch(r"base_decode_distinct_h(\d+)(?:to(\d+))?_r(\d+)_b(\d+)", name)
+        if not m:
+            raise SystemExit(f"unknown workload {name}")
+        self.name, self.sg, self.torch = name, sg, torch
+        self.dtype = "f16"
+        self.h_in = int(m.group(1))
+        self.h_out = int(m.group(2) or m.group(1))
+        self.rank, self.n = int(m.group(3)), int(m.group(4))
+        e = 2
+        w_bytes = e * self.h_in * self.h_out
+        self.wcopies = max(2, math.ceil((1 << 30) / w_bytes))
+        lora_bytes = e * (self.h_in + self.h_out) * self.rank
+        self.tables = max(2, math.ceil((1 << 30) / (lora_bytes * self.n)))
+        self.copies = 64
+        s0 = 7000 + self.n
+        self.W = wl.device_normal((self.wcopies, self.h_in, self.h_out), self.h_in ** -0.5, self.dtype, s0)
+        self.A = wl.device_normal((self.tables * self.n, self.h_in, self.rank), self.h_in ** -0.5, self.dtype,
+                                  s0 + 1)
+        self.B = wl.device_normal((self.tables * self.n, self.rank, self.h_out), self.rank ** -0.5, self.dtype,
+                                  s0 + 2)
+        self.X = wl.device_normal((self.copies, self.n, self.h_in), 1.0, self.dtype, s0 + 3)
+        self.Y = torch.zeros((self.copies, self.n, self.h_out), dtype=self.X.dtype, device="cuda")
+        idx = torch.arange(self.tables * self.n, dtype=torch.int64, device="cuda").view(self.tables, self.n)
+        self.A_tab = (self.A.data_ptr() + idx * (self.h_in * self.rank * e)).contiguous()
+        self.B_tab = (self.B.data_ptr() + idx * (self.rank * self.h_out * e)).contiguous()
+        self.seg_h = np.arange(self.n + 1, dtype=np.int32)
+        self.lidx_h = np.arange(self.n, dtype=np.int32)
+        self.seg = torch.from_numpy(self.seg_h).cuda()
+        self.lidx = torch.from_numpy(self.lidx_h).cuda()
+        self.problem = sg.make_problem(self.dtype, self.n, self.h_in, self.h_out, self.rank, self.n, self.n, 1)
+        self.ws = sg.new_base_workspace(self.problem)
+        self.bytes = e * (self.h_in * self.h_out + self.n * (self.h_in + self.h_out) * self.rank
+                          + self.n * self.h_in + self.n * self.h_out)
+        self.rows_per_step = self.n
+        self.calls_per_step = 1
+        self.fn = sg.load_library().sgmv_base_lora_apply
+        pb = ctypes.byref(self.problem)
+        self.args = []
+        for c in range(max(self.wcopies, self.tables, self.copies)):
+            w, t, x = c % self.wcopies, c % self.tables, c % self.copies
+            self.args.append((pb, self.X[x].data_ptr(), self.W[w].data_ptr(), self.A_tab[t].data_ptr(),
+                              self.B_tab[t].data_ptr(), self.Y[x].data_ptr(), self.seg.data_ptr(),
+                              self.lidx.data_ptr(), self.ws.data_ptr(), self.ws.numel()))
+        self.unfused = self.time_unfused()
+        torch.cuda.synchronize()
+
+    def step(self, c, stream):
+        st = self.fn(*self.args[c % len(self.args)], stream)
+        if st != 0:
+            raise RuntimeError(self.sg.sgmv_status_str(st))
+
+    def time_unfused(self, iters=200):
+        """Per-call time of torch's X @ W followed by sgmv_lora_apply (same rotation)."""
+        torch, sg = self.torch, self.sg
+        prob = sg.make_problem(self.dtype, self.n, self.h_in, self.h_out, self.rank, self.n, self.n, 1)
+        ws = sg.new_workspace(prob)
+        fn = sg.load_library().sgmv_lora_apply
+        sid = torch.cuda.current_stream().cuda_stream
+
+        def one(c):
+            w, t, x = c % self.wcopies, c % self.tables, c % self.copies
+            torch.matmul(self.X[x], self.W[w], out=self.Y[x])
+            st = fn(ctypes.byref(prob), self.X[x].data_ptr(), self.A_tab[t].data_ptr(), self.B_tab[t].data_ptr(),
+                    self.Y[x].data_ptr(), self.seg.data_ptr(), self.lidx.data_ptr(), ws.data_ptr(), ws.numel(),
+                    sid)
+            if st != 0:
+                raise RuntimeError(sg.sgmv_status_str(st))
+
+        for c in range(20):
+            one(c)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for c in range(iters):
+            one(c)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / iters
+
+    def check_sample(self, calls=2):
+        import numpy as np
+        import oracle
+        torch = self.torch
+        worst = 0.0
+        sid = torch.cuda.current_stream().cuda_stream
+        for c in range(calls):
+            w, t, x = c % self.wcopies, c % self.tables, c % self.copies
+            A = [_bits(self.A[t * self.n + k]) for k in range(self.n)]
+            B = [_bits(self.B[t * self.n + k]) for k in range(self.n)]
+            self.Y[x].fill_(float("nan"))
+            self.step(c, sid)
+            torch.cuda.synchronize()
+            got = oracle.decode(_bits(self.Y[x]), self.dtype)
+            ref = oracle.sgmv_base_apply(self.dtype, _bits(self.X[x]), _bits(self.W[w]), A, B, self.seg_h,
+                                         self.lidx_h)
+            worst = max(worst, float((np.abs(got - ref) / (1e-3 + 1e-2 * np.abs(ref))).max()))
+        if not worst <= 1.0:
+            raise AssertionError(f"bench parity check failed: max err/bound {worst:.3f}")
+        return worst
+
+    def config(self):
+        return {"workload": self.name, "h_in": self.h_in, "h_out": self.h_out, "rank": self.rank,
+                "batch_rows": self.n, "segments": self.n, "distinct_loras": self.n, "w_copies": self.wcopies,
+                "lora_tables": self.tables, "xy_copies": self.copies, "algorithmic_bytes_per_step": self.bytes,
+                "output": "Y = X @ W + LoRA term (written, one rounding)",
+                "unfused_torch_matmul_plus_sgmv_us_per_call": round(self.unfused, 3)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None, help="timed steps (default 2000; 20 for a forward)")
     ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default 200; 3 for a forward)")
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=SINGLE_WORKLOADS + MODEL_WORKLOADS + HET_WORKLOADS)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
+                    choices=SINGLE_WORKLOADS + MODEL_WORKLOADS + HET_WORKLOADS + BASE_WORKLOADS)
     ap.add_argument("--variant", choices=["auto", "vector", "fused", "mfma"], default="auto")
     ap.add_argument("--splits", type=int, default=0, help="workgroups per segment block (0 = automatic)")
     ap.add_argument("--no-batch", action="store_true",
@@ -742,6 +870,8 @@ def main():
     W = args.warmup if args.warmup is not None else (3 if model else 200)
     if args.workload in HET_WORKLOADS:
         bench = MixedRankBench(args.workload, variant=variant, splits=args.splits)
+    elif args.workload in BASE_WORKLOADS:
+        bench = BaseBench(args.workload)
     elif model:
         bench = ModelForwardBench(args.workload, variant=variant, splits=args.splits,
                                   batch_projections=not args.no_batch, row_map=args.row_map)

@@ -254,6 +254,35 @@ sgmv_status_t sgmv_lora_apply_batched(const sgmv_problem_t* problem, const void*
                                       const int32_t* seg_indptr, const int32_t* lora_idx,
                                       const int32_t* row_idx, void* ws, size_t ws_bytes, void* stream);
 
+/* ---- Base projection with the LoRA term (decode-sized batches) ----
+ *
+ * Punica README, LoRA paragraph: a row vector x gets the output x@W + x@A@B;
+ * multi-LoRA paragraph: X@W is one product for the whole batch and every row
+ * adds its own LoRA term.  sgmv_base_lora_apply computes, for every row
+ * i < n_rows,
+ *     Y[i, :] = X[i, :] @ W + (X[i, :] @ A_k) @ B_k     (k = lora_idx[s], i in segment s)
+ *     Y[i, :] = X[i, :] @ W                            (i covered by no segment)
+ * with the sum kept in fp32 and rounded once to the input format.  Y is
+ * written, not accumulated.
+ *   W       device [h_in, h_out] row-major, same format as X, 16-byte aligned.
+ *   X, Y    device [n_rows, h_in] and [n_rows, h_out]; Y must not alias X or W.
+ *   A_ptrs, B_ptrs, seg_indptr, lora_idx  as for sgmv_lora_apply (may be NULL
+ *           when num_segs == 0 or max_seg_len == 0: then Y = X @ W).
+ *   ws      device workspace of sgmv_base_workspace_bytes bytes (any contents;
+ *           it holds the fp32 partial planes of V and of X @ W).
+ * Supported: n_rows <= 64 (SGMV_ERR_UNSUPPORTED above; a prefill-sized base
+ * projection is a dense GEMM for a GEMM library, followed by sgmv_lora_apply);
+ * ranks, formats and alignment as for sgmv_lora_apply.  Two launches (split-K
+ * partial products of X @ W on the matrix cores together with the partial
+ * planes of V = X @ A_k; an epilogue that sums them, adds V @ B_k and rounds);
+ * asynchronous on `stream`.  Same metadata preconditions and error
+ * conventions as sgmv_lora_apply. */
+sgmv_status_t sgmv_base_workspace_bytes(const sgmv_problem_t* problem, size_t* bytes);
+sgmv_status_t sgmv_base_lora_apply(const sgmv_problem_t* problem, const void* X, const void* W,
+                                   const void* const* A_ptrs, const void* const* B_ptrs, void* Y,
+                                   const int32_t* seg_indptr, const int32_t* lora_idx, void* ws,
+                                   size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

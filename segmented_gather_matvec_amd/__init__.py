@@ -32,7 +32,8 @@ SGMV_MAX_PROJECTIONS = 4
 
 ENTRY_POINTS = ("sgmv_status_str", "sgmv_build_segments", "sgmv_check_problem",
                 "sgmv_check_segments", "sgmv_workspace_bytes", "sgmv_query_plan", "sgmv_shrink",
-                "sgmv_expand", "sgmv_lora_apply", "sgmv_lora_apply_batched")
+                "sgmv_expand", "sgmv_lora_apply", "sgmv_lora_apply_batched", "sgmv_base_workspace_bytes",
+                "sgmv_base_lora_apply")
 
 
 class SgmvError(RuntimeError):
@@ -97,6 +98,8 @@ def load_library(path: str = LIB_PATH):
     lib.sgmv_expand.argtypes = [prob, P, P, P, P, P, P]
     lib.sgmv_lora_apply.argtypes = [prob, P, P, P, P, P, P, P, SZ, P]
     lib.sgmv_lora_apply_batched.argtypes = [prob, P, ctypes.POINTER(sgmv_projection_t), I32, P, P, P, P, SZ, P]
+    lib.sgmv_base_workspace_bytes.argtypes = [prob, ctypes.POINTER(SZ)]
+    lib.sgmv_base_lora_apply.argtypes = [prob, P, P, P, P, P, P, P, P, SZ, P]
     for name in ENTRY_POINTS[1:]:
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -272,6 +275,36 @@ def sgmv_lora_apply_batched(problem, X, projections, seg_indptr, lora_idx, ws, r
 
 
 # ----------------------------------------------------------------- helpers
+
+def sgmv_base_workspace_bytes(problem: sgmv_problem_t) -> int:
+    """Workspace bytes of sgmv_base_lora_apply (n_rows <= 64)."""
+    out = ctypes.c_size_t(0)
+    _check(load_library().sgmv_base_workspace_bytes(ctypes.byref(problem), ctypes.byref(out)),
+           "sgmv_base_workspace_bytes")
+    return int(out.value)
+
+
+def new_base_workspace(problem: sgmv_problem_t, device="cuda"):
+    """Zero-filled device workspace of sgmv_base_workspace_bytes(problem) bytes."""
+    import torch
+    return torch.zeros(sgmv_base_workspace_bytes(problem), dtype=torch.uint8, device=device)
+
+
+def sgmv_base_lora_apply(problem, X, W, A_ptrs, B_ptrs, Y, seg_indptr, lora_idx, ws, stream=None):
+    """Y[i] = X[i] @ W + (X[i] @ A_k) @ B_k on the device (Y written, rounded once); asynchronous.
+    Rows no segment covers get X[i] @ W.  At most 64 rows."""
+    import torch
+    dt = _torch_dtype(problem)
+    _need(X, "X", dt); _need(W, "W", dt); _need(Y, "Y", dt)
+    _need(A_ptrs, "A_ptrs", torch.int64); _need(B_ptrs, "B_ptrs", torch.int64)
+    _need(seg_indptr, "seg_indptr", torch.int32); _need(lora_idx, "lora_idx", torch.int32)
+    _need(ws, "ws")
+    st = load_library().sgmv_base_lora_apply(ctypes.byref(problem), _ptr(X), _ptr(W), _ptr(A_ptrs),
+                                             _ptr(B_ptrs), _ptr(Y), _ptr(seg_indptr), _ptr(lora_idx),
+                                             _ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0,
+                                             _stream(stream))
+    _check(st, "sgmv_base_lora_apply")
+
 
 def batched_workspace_bytes(problem: sgmv_problem_t, num_projections: int) -> int:
     """Workspace bytes of sgmv_lora_apply_batched: one 256-byte aligned slice per projection."""

@@ -474,6 +474,38 @@ sgmv_status_t apply(const sgmv_problem_t& p, const void* X, const sgmv_projectio
 
 }  // namespace
 
+// Base projection with the LoRA term: W strips of kBaseStripCols columns,
+// split over K into fp32 partial planes so that about kBaseTarget workgroups
+// stream W at once.  A sweep of strips (64, 128, 256 columns) against targets
+// (128 to 1024) on 32-row batches (H = 4096 and 11008 -> 4096) found 128 x 256
+// best: more splits write (and the epilogue reads) more partial planes.
+constexpr int kBaseStripCols = 128;
+constexpr int kBaseTarget = 256;
+
+struct BasePlan {
+  int strip_cols = kBaseStripCols;
+  int strips = 0;
+  int ksplit = 1;
+  int kc = 0;
+  int base_grid = 0;
+  size_t v_off = 0, p_off = 0, total = 0;  // workspace layout
+};
+
+BasePlan plan_base(const sgmv_problem_t& p) {
+  BasePlan b;
+  b.strips = (int)ceil_div(p.h_out, b.strip_cols);
+  const int64_t max_split = ceil_div(p.h_in, sgmv::kBaseStageRows);
+  const int64_t ks = std::max<int64_t>(1, std::min<int64_t>(ceil_div(kBaseTarget, b.strips), max_split));
+  b.kc = (int)round_up(ceil_div(p.h_in, ks), sgmv::kBaseStageRows);
+  b.ksplit = (int)ceil_div(p.h_in, b.kc);
+  b.base_grid = (int)round_up((int64_t)b.strips * b.ksplit, 8);
+  // [partial planes of V][partial planes of Y]
+  b.v_off = 0;
+  b.p_off = (size_t)round_up((int64_t)b.ksplit * p.n_rows * p.rank * (int64_t)sizeof(float), 256);
+  b.total = b.p_off + (size_t)b.ksplit * (size_t)p.n_rows * (size_t)p.h_out * sizeof(float);
+  return b;
+}
+
 extern "C" {
 
 const char* sgmv_status_str(sgmv_status_t status) {
@@ -695,6 +727,58 @@ sgmv_status_t sgmv_lora_apply_batched(const sgmv_problem_t* p, const void* X,
   if (ws_bytes < stride * (size_t)(num_projections - 1) + need) return SGMV_ERR_WORKSPACE;
   return apply(*p, X, projections, num_projections, seg_indptr, lora_idx, row_idx, static_cast<char*>(ws),
                stride, static_cast<hipStream_t>(stream));
+}
+
+sgmv_status_t sgmv_base_workspace_bytes(const sgmv_problem_t* p, size_t* bytes) {
+  if (!bytes) return SGMV_ERR_INVALID_ARG;
+  const sgmv_status_t st = sgmv_check_problem(p);
+  if (st != SGMV_OK) return st;
+  if (p->n_rows > sgmv::kBaseMaxRows) return SGMV_ERR_UNSUPPORTED;
+  *bytes = plan_base(*p).total;
+  return SGMV_OK;
+}
+
+sgmv_status_t sgmv_base_lora_apply(const sgmv_problem_t* p, const void* X, const void* W,
+                                   const void* const* A_ptrs, const void* const* B_ptrs, void* Y,
+                                   const int32_t* seg_indptr, const int32_t* lora_idx, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  sgmv_status_t st = sgmv_check_problem(p);
+  if (st != SGMV_OK) return st;
+  if (p->n_rows > sgmv::kBaseMaxRows) return SGMV_ERR_UNSUPPORTED;
+  if (p->n_rows == 0) return SGMV_OK;
+  if (!X || !W || !Y) return SGMV_ERR_INVALID_ARG;
+  const bool lora = !nothing_to_do(*p);
+  if (lora && (!A_ptrs || !B_ptrs || !seg_indptr || !lora_idx)) return SGMV_ERR_INVALID_ARG;
+  if (!aligned16(X) || !aligned16(W) || !aligned16(Y)) return SGMV_ERR_UNSUPPORTED;
+  if (lora && (!aligned8(A_ptrs) || !aligned8(B_ptrs))) return SGMV_ERR_UNSUPPORTED;
+  const BasePlan b = plan_base(*p);
+  if (!ws || ws_bytes < b.total) return SGMV_ERR_WORKSPACE;
+  if (!aligned16(ws)) return SGMV_ERR_UNSUPPORTED;
+  char* w = static_cast<char*>(ws);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  sgmv::BaseParams q{};
+  q.n_rows = p->n_rows;
+  q.h_in = p->h_in;
+  q.h_out = p->h_out;
+  q.num_segs = lora ? p->num_segs : 0;
+  q.num_loras = p->num_loras;
+  q.strip_cols = b.strip_cols;
+  q.strips = b.strips;
+  q.ksplit = b.ksplit;
+  q.kc = b.kc;
+  q.base_grid = b.base_grid;
+  q.shrink_grid = lora ? (int32_t)round_up((int64_t)p->n_rows * b.ksplit, 8) : 0;
+  q.plane_stride = (int64_t)p->n_rows * p->h_out;
+  q.seg_indptr = lora ? seg_indptr : nullptr;
+  q.lora_idx = lora ? lora_idx : nullptr;
+  q.X = static_cast<const uint16_t*>(X);
+  q.W = static_cast<const uint16_t*>(W);
+  q.A_ptrs = lora ? reinterpret_cast<const uint64_t*>(A_ptrs) : nullptr;
+  q.B_ptrs = lora ? reinterpret_cast<const uint64_t*>(B_ptrs) : nullptr;
+  q.vpartials = lora ? reinterpret_cast<float*>(w + b.v_off) : nullptr;
+  q.partials = reinterpret_cast<float*>(w + b.p_off);
+  q.Y = static_cast<uint16_t*>(Y);
+  return hip_status(sgmv::launch_base(p->dtype, p->rank, q, s));
 }
 
 }  // extern "C"

@@ -1,0 +1,437 @@
+// sgmv_base.hip - base projection with the LoRA term added before its one
+// rounding (gfx950), for decode-sized batches.
+//
+// The LoRA paragraph of the Punica README (page "Punica：多 LoRA 模型统一服务框架")
+// gives a row vector x the output x@W + x@A@B; the multi-LoRA paragraph runs
+// X@W once for the whole batch and adds every row's own LoRA term.  For at
+// most 64 rows this file computes
+//     Y[i, :] = X[i, :] @ W + V[i, :] @ B_k      (k: LoRA of row i's segment)
+// with V = X @ A_k, the sum kept in fp32 and rounded once.  Rows no segment covers get X @ W.
+//
+// Two launches:
+//  1. partials: workgroup (g, s) multiplies X[:, K_g] by W[K_g, strip s] (SC
+//     columns) on the matrix cores and writes its tile of fp32 partial plane
+//     g.  W (the bulk of the bytes) streams from HBM exactly once; X (n x h_in,
+//     a few hundred KiB) is re-read from L2 by every strip.  Each stage of W
+//     rows is staged in LDS transposed to [column][k], so that a lane reads 8
+//     consecutive k of one column with one 128-bit read; the X stage is kept
+//     row-major ([row][k]), which is already the MFMA operand layout.  Further
+//     workgroups of the same launch compute the LoRA shrink, one fp32 partial
+//     plane of V per K chunk (nothing in the launch waits for anything).
+//  2. epilogue: one wave per (row, 512 columns) sums the partial planes of Y
+//     and of V in plane order, adds V[i] @ B_k over its columns and stores Y.
+#include "sgmv_device.h"
+#include "sgmv_plan.h"
+
+namespace sgmv {
+namespace {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kXcds = 8;
+
+
+template <class T>
+__device__ inline f32x4 mfma(const u32x4& a, const u32x4& b, f32x4 c);
+template <>
+__device__ inline f32x4 mfma<F16>(const u32x4& a, const u32x4& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                0, 0, 0);
+}
+template <>
+__device__ inline f32x4 mfma<BF16>(const u32x4& a, const u32x4& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                 c, 0, 0, 0);
+}
+
+// Two 8-element rows (u, v) of a row-major tile, written transposed into LDS
+// as 32-bit pairs: dst[e*stride] = {u[e], v[e]} for e < 8 (dst in 16-bit
+// units, even offset).
+__device__ inline void store_pair_transposed(uint16_t* dst, int stride, const u32x4& u, const u32x4& v) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t lo = (u[w] & 0xffffu) | (v[w] << 16);
+    const uint32_t hi = (u[w] >> 16) | (v[w] & 0xffff0000u);
+    *reinterpret_cast<uint32_t*>(dst + (2 * w) * stride) = lo;
+    *reinterpret_cast<uint32_t*>(dst + (2 * w + 1) * stride) = hi;
+  }
+}
+
+// ---------------------------------------------------------------- LoRA shrink
+// Segment of row i among segments first.. (64 at a time; -1: none covers it).
+__device__ inline int segment_of_row(const BaseParams& p, int i, int first = 0) {
+  const int lane = threadIdx.x & 63;
+  int seg = -1;
+  if (p.num_segs > 0 && p.seg_indptr != nullptr && p.lora_idx != nullptr) {
+    for (int s0 = first; s0 < p.num_segs; s0 += 64) {
+      const int s = s0 + lane;
+      bool hit = false;
+      if (s < p.num_segs) hit = p.seg_indptr[s] <= i && i < p.seg_indptr[s + 1];
+      const unsigned long long m = __ballot(hit);
+      if (m) {
+        seg = s0 + __builtin_ctzll(m);
+        break;
+      }
+    }
+  }
+  return __builtin_amdgcn_readfirstlane(seg);
+}
+
+// Workgroup (i, g) of the shrink role: partial V plane g of row i,
+//   vpart[g][i][j] = sum_{h in K_g} X[i, h] * A_k[h, j],
+// in fp32 with vector FMA (each row may use its own LoRA, so this is not a
+// shared-operand product).  Thread t owns 8 ranks (group t % JG) of the rows h
+// = t / JG + (256 / JG) m; the groups are summed in LDS in thread order.
+template <class T, int R>
+__device__ inline void shrink_role(const BaseParams& p, int item, float* lds) {
+  constexpr int JG = R / 8;               // 128-bit vectors per row of A_k
+  constexpr int HPT = kThreads / JG;      // rows of A_k per pass of the workgroup
+  const int t = threadIdx.x;
+  const int i = item / p.ksplit;
+  const int g = item - i * p.ksplit;
+  if (i >= p.n_rows) return;  // padding of the shrink grid to a multiple of 8
+  const int seg = segment_of_row(p, i);
+  if (seg < 0) return;
+  const int k = p.lora_idx[seg];
+  if (k < 0 || k >= p.num_loras || p.A_ptrs == nullptr) return;
+  const uint16_t* Ak = reinterpret_cast<const uint16_t*>(p.A_ptrs[k]);
+  const uint16_t* xrow = p.X + (int64_t)i * p.h_in;
+  const int k0 = g * p.kc;
+  const int k1 = p.h_in < k0 + p.kc ? p.h_in : k0 + p.kc;
+  const int jg = t % JG, h0 = t / JG;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  constexpr int kUnroll = 4;
+  for (int hb = k0 + h0; hb < k1; hb += HPT * kUnroll) {
+    u32x4 a[kUnroll];
+    float x[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int h = hb + u * HPT;
+      const bool ok = h < k1;
+      a[u] = load_stream(Ak + (ok ? (int64_t)h * R + jg * 8 : 0));
+      x[u] = ok ? T::one(load_stream_u16(xrow + h)) : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      float af[8];
+      unpack8<T>(a[u], af);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(x[u], af[e], acc[e]);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) lds[t * 8 + e] = acc[e];
+  __syncthreads();
+  if (t < R) {
+    const int jj = t / 8, e = t % 8;
+    float v = 0.f;
+    for (int hh = 0; hh < HPT; ++hh) v += lds[(hh * JG + jj) * 8 + e];
+    p.vpartials[((int64_t)g * p.n_rows + i) * R + t] = v;
+  }
+}
+
+// ---------------------------------------------------------------- partials
+// Workgroup (g, s): rows of X and W [K_g] x strip s of SC columns, on the
+// matrix cores; writes its tile of fp32 partial plane g.
+template <class T, int R, int SC, int NRT>
+__global__ __launch_bounds__(kThreads) void sgmv_base_partial_kernel(BaseParams p) {
+  constexpr int KS = kBaseStageRows;    // W rows per stage
+  constexpr int WST = KS + 8;           // LDS stride (halves) of transposed W, per column
+  constexpr int XST = KS + 8;           // LDS stride (halves) of the X stage, per row
+  constexpr int CV = SC / 8;            // 128-bit vectors per W row of the strip
+  constexpr int NWP = KS / 2 * CV / kThreads;        // (k, k+1) W vector pairs per thread
+  constexpr int XV = KS / 8;            // 128-bit vectors per X row of a stage
+  constexpr int NXV = (NRT * 16 * XV + kThreads - 1) / kThreads;  // X vectors per thread
+  constexpr int KSTEPS = KS / 32;       // MFMA k-steps per stage
+  constexpr int NTW = SC / 16 / kWaves; // 16-column tiles per wave
+  static_assert(NWP * kThreads == KS / 2 * CV, "W stage splits evenly over the threads");
+  static_assert(NTW * 16 * kWaves == SC, "strip splits evenly over the waves");
+  // Within a column, the stage's k sit in groups of 8 (one 128-bit operand
+  // read); group g of column c is stored at group g ^ swz(c), which spreads a
+  // wave's transposed stores over the LDS banks.
+  auto swz = [](int c) { return (c >> 4) & (KS / 8 - 1); };
+  __shared__ __attribute__((aligned(16))) uint16_t lds_wt[SC * WST];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_x[NRT * 16 * XST];
+
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int q = lane >> 4;
+  const int ml = lane & 15;
+  // A malformed launch returns at once (the host rejects all of these).
+  const bool bad = ((p.n_rows - 1) | p.h_in | p.h_out | (p.kc - 1) | (p.strips - 1) | (p.ksplit - 1) |
+                    (NRT * 16 - p.n_rows) | (int32_t)(p.plane_stride >> 32)) < 0;
+  const bool bad_ptr = (p.X == nullptr) | (p.W == nullptr) | (p.partials == nullptr);
+  if (bad | bad_ptr) return;
+  // The first shrink_grid workgroups compute the LoRA shrink (dispatched
+  // first, they finish while W streams).
+  if ((int)blockIdx.x < p.shrink_grid) {
+    if (p.vpartials != nullptr) shrink_role<T, R>(p, (int)blockIdx.x, reinterpret_cast<float*>(lds_wt));
+    return;
+  }
+  // Linear order of the base product: K split major; each XCD (workgroup b
+  // runs on XCD b % 8; shrink_grid is a multiple of 8) takes a contiguous run
+  // of it, so the strips that read one chunk of X share an L2.
+  const int b = (int)blockIdx.x - p.shrink_grid;
+  const int per_xcd = p.base_grid / kXcds;
+  const int idx = (b % kXcds) * per_xcd + b / kXcds;
+  if (idx >= p.strips * p.ksplit) return;
+  const int g = idx / p.strips;
+  const int c0 = (idx - g * p.strips) * SC;
+  const int n = p.n_rows;
+  const int k0 = g * p.kc;
+  const int k1 = p.h_in < k0 + p.kc ? p.h_in : k0 + p.kc;
+  const uint16_t* W = p.W;
+  const uint16_t* X = p.X;
+
+  // All loads of one stage, at clamped (valid) addresses; what lies past the
+  // matrix is zeroed where it is staged.
+  auto issue = [&](int kk, u32x4 (&w)[NWP][2], u32x4 (&x)[NXV]) {
+#pragma unroll
+    for (int m = 0; m < NWP; ++m) {
+      const int pv = t + kThreads * m;
+      const int k = kk + (pv / CV) * 2, c = c0 + (pv % CV) * 8;
+      const bool ok = c < p.h_out;
+      w[m][0] = load_stream(W + (ok && k < k1 ? (int64_t)k * p.h_out + c : 0));
+      w[m][1] = load_stream(W + (ok && k + 1 < k1 ? (int64_t)(k + 1) * p.h_out + c : 0));
+    }
+#pragma unroll
+    for (int m = 0; m < NXV; ++m) {
+      const int xv = t + kThreads * m;
+      const int r = xv / XV, k = kk + (xv % XV) * 8;
+      x[m] = load_vec(X + (r < n && k < k1 ? (int64_t)r * p.h_in + k : 0));
+    }
+  };
+
+  f32x4 acc[NRT][NTW];
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) acc[rt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int kk, const u32x4 (&w)[NWP][2], const u32x4 (&x)[NXV]) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    __syncthreads();  // the previous stage is done with the LDS tiles
+#pragma unroll
+    for (int m = 0; m < NWP; ++m) {
+      const int pv = t + kThreads * m;
+      const int kr = (pv / CV) * 2, cl = (pv % CV) * 8;
+      const bool ok = c0 + cl < p.h_out;
+      const int ks = (((kr >> 3) ^ swz(cl)) << 3) | (kr & 7);  // columns cl..cl+7 share swz(cl)
+      store_pair_transposed(&lds_wt[cl * WST + ks], WST, ok && kk + kr < k1 ? w[m][0] : z,
+                            ok && kk + kr + 1 < k1 ? w[m][1] : z);
+    }
+#pragma unroll
+    for (int m = 0; m < NXV; ++m) {
+      const int xv = t + kThreads * m;
+      const int r = xv / XV, kx = (xv % XV) * 8;
+      if (r < NRT * 16) store_vec(&lds_x[r * XST + kx], r < n && kk + kx < k1 ? x[m] : z);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+      u32x4 bf[NTW];
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) {
+        const int cn = (wave * NTW + j) * 16;  // first column of the tile
+        bf[j] = load_vec(&lds_wt[(cn + ml) * WST + (((4 * s + q) ^ swz(cn)) << 3)]);
+      }
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt) {
+        const u32x4 af = load_vec(&lds_x[(rt * 16 + ml) * XST + s * 32 + q * 8]);
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) acc[rt][j] = mfma<T>(af, bf[j], acc[rt][j]);
+      }
+    }
+  };
+
+  // Ping-pong over stage pairs; a stage past k1 loads clamped addresses and
+  // contributes zeros.
+  u32x4 wA[NWP][2], xA[NXV], wB[NWP][2], xB[NXV];
+  issue(k0, wA, xA);
+  for (int kk = k0; kk < k1; kk += 2 * KS) {
+    issue(kk + KS, wB, xB);
+    compute(kk, wA, xA);
+    if (kk + 2 * KS < k1) issue(kk + 2 * KS, wA, xA);
+    compute(kk + KS, wB, xB);
+  }
+
+  // D[4q+i][ml] of tile (rt, j): row rt*16 + 4q + i, column c0 + (wave*NTW + j)*16 + ml.
+  float* dst = p.partials + (int64_t)g * p.plane_stride;
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+    for (int j = 0; j < NTW; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = rt * 16 + q * 4 + i;
+        const int c = c0 + (wave * NTW + j) * 16 + ml;
+        if (r < n && c < p.h_out) dst[(int64_t)r * p.h_out + c] = acc[rt][j][i];
+      }
+}
+
+// ---------------------------------------------------------------- epilogue
+// One wave per (row i, 512 columns): lane l owns columns c .. c+7,
+// c = 512 * blockIdx.x + 8 * l.  Y[i, c..] = sum of the partial planes (plane
+// order) + V[i] @ B_k (ranks in ascending order), rounded once.
+template <class T, int R>
+__global__ __launch_bounds__(64) void sgmv_base_epilogue_kernel(BaseParams p) {
+  constexpr int kBatch = 16;  // plane loads in flight per lane
+  const int lane = threadIdx.x;
+  const int i = blockIdx.y;
+  const bool bad = (p.n_rows | p.h_out | p.num_segs | p.num_loras | (p.ksplit - 1) |
+                    (int32_t)(p.plane_stride >> 32)) < 0;
+  const bool bad_ptr = (p.partials == nullptr) | (p.Y == nullptr);
+  if (bad | bad_ptr || i >= p.n_rows) return;
+  const int c = blockIdx.x * 512 + lane * 8;
+  const bool col_ok = c < p.h_out;
+  const int cc = col_ok ? c : 0;
+
+  // Bounds of the first 64 segments, then the partial planes of Y (up to
+  // kBatch planes), all issued before anything waits: the wait for the
+  // bounds then does not wait for the planes (loads complete in order).
+  const bool have = p.seg_indptr != nullptr && p.lora_idx != nullptr && lane < p.num_segs;
+  int lo0 = 0, hi0 = 0;
+  if (have) {
+    lo0 = p.seg_indptr[lane];
+    hi0 = p.seg_indptr[lane + 1];
+  }
+  const float* row = p.partials + (int64_t)i * p.h_out + cc;
+  f32x4 a[kBatch], b[kBatch];
+#pragma unroll
+  for (int u = 0; u < kBatch; ++u) {
+    const int g = u < p.ksplit ? u : p.ksplit - 1;
+    a[u] = *reinterpret_cast<const f32x4*>(row + (int64_t)g * p.plane_stride);
+    b[u] = *reinterpret_cast<const f32x4*>(row + (int64_t)g * p.plane_stride + 4);
+  }
+
+  const unsigned long long m0 = __ballot(have && lo0 <= i && i < hi0);
+  int seg = m0 ? __builtin_ctzll(m0) : (p.num_segs > 64 ? segment_of_row(p, i, 64) : -1);
+  seg = __builtin_amdgcn_readfirstlane(seg);
+  int k = seg >= 0 ? p.lora_idx[seg] : -1;
+  k = __builtin_amdgcn_readfirstlane(k);
+  const bool lora = k >= 0 && k < p.num_loras && p.B_ptrs != nullptr && p.vpartials != nullptr;
+
+  constexpr int JB = R < 16 ? R : 16;  // B_k rows per batch of loads
+  const uint16_t* Bk = lora ? reinterpret_cast<const uint16_t*>(p.B_ptrs[k]) : nullptr;
+  u32x4 bv[JB];
+  if (lora) {
+#pragma unroll
+    for (int j = 0; j < JB; ++j) bv[j] = load_stream(Bk + (int64_t)j * p.h_out + cc);
+  }
+  // V[i] = sum of its partial planes in plane order (lane j < R owns rank j),
+  // shared through LDS.
+  __shared__ float lds_v[R];
+  if (lora && lane < R) {
+    // All of a batch's plane loads are issued before the first add.
+    float v = 0.f;
+    const float* vp = p.vpartials + (int64_t)i * R + lane;
+    for (int g0 = 0; g0 < p.ksplit; g0 += kBatch) {
+      float pv[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int g = g0 + u < p.ksplit ? g0 + u : p.ksplit - 1;
+        pv[u] = vp[(int64_t)g * p.n_rows * R];
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) v = g0 + u < p.ksplit ? v + pv[u] : v;
+    }
+    lds_v[lane] = v;
+  }
+  __syncthreads();
+
+  // Base: sum of the partial planes in plane order.
+  float y[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int g0 = 0; g0 < p.ksplit; g0 += kBatch) {
+    if (g0 > 0) {
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int g = g0 + u < p.ksplit ? g0 + u : p.ksplit - 1;
+        a[u] = *reinterpret_cast<const f32x4*>(row + (int64_t)g * p.plane_stride);
+        b[u] = *reinterpret_cast<const f32x4*>(row + (int64_t)g * p.plane_stride + 4);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const bool live = g0 + u < p.ksplit;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        y[e] = live ? y[e] + a[u][e] : y[e];
+        y[4 + e] = live ? y[4 + e] + b[u][e] : y[4 + e];
+      }
+    }
+  }
+  if (lora) {
+    float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j0 = 0; j0 < R; j0 += JB) {
+      if (j0 > 0) {
+#pragma unroll
+        for (int j = 0; j < JB; ++j) bv[j] = load_stream(Bk + (int64_t)(j0 + j) * p.h_out + cc);
+      }
+#pragma unroll
+      for (int j = 0; j < JB; ++j) {
+        float bf[8];
+        unpack8<T>(bv[j], bf);
+        const float vj = lds_v[j0 + j];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s[e] = __builtin_fmaf(vj, bf[e], s[e]);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] += s[e];
+  }
+  if (col_ok) store_vec(p.Y + (int64_t)i * p.h_out + c, pack8<T>(y));
+}
+
+// Grid: shrink_grid shrink workgroups (n_rows * ksplit rounded up to a
+// multiple of 8; none without a LoRA term), then the base product's
+// workgroups (a multiple of 8, for the XCD mapping).
+template <class T, int R, int SC>
+hipError_t launch_partial(const BaseParams& p, hipStream_t s) {
+  const dim3 grid((unsigned)p.shrink_grid + (unsigned)p.base_grid);
+  if (p.n_rows <= 16)
+    hipLaunchKernelGGL((sgmv_base_partial_kernel<T, R, SC, 1>), grid, dim3(kThreads), 0, s, p);
+  else if (p.n_rows <= 32)
+    hipLaunchKernelGGL((sgmv_base_partial_kernel<T, R, SC, 2>), grid, dim3(kThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL((sgmv_base_partial_kernel<T, R, SC, 4>), grid, dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+template <class T, int R>
+hipError_t launch_r(const BaseParams& p, hipStream_t s) {
+  hipError_t e = hipErrorInvalidValue;
+  switch (p.strip_cols) {
+    case 64: e = launch_partial<T, R, 64>(p, s); break;
+    case 128: e = launch_partial<T, R, 128>(p, s); break;
+    case 256: e = launch_partial<T, R, 256>(p, s); break;
+  }
+  if (e != hipSuccess) return e;
+  const dim3 egrid((unsigned)((p.h_out + 511) / 512), (unsigned)p.n_rows);
+  hipLaunchKernelGGL((sgmv_base_epilogue_kernel<T, R>), egrid, dim3(64), 0, s, p);
+  return hipGetLastError();
+}
+
+template <class T>
+hipError_t launch_t(int rank, const BaseParams& p, hipStream_t s) {
+  switch (rank) {
+    case 8: return launch_r<T, 8>(p, s);
+    case 16: return launch_r<T, 16>(p, s);
+    case 32: return launch_r<T, 32>(p, s);
+    case 64: return launch_r<T, 64>(p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_base(int dtype, int rank, const BaseParams& p, hipStream_t stream) {
+  if (p.n_rows <= 0 || p.strips <= 0) return hipSuccess;
+  if (p.n_rows > kBaseMaxRows) return hipErrorInvalidValue;
+  return dtype == 1 ? launch_t<BF16>(rank, p, stream) : launch_t<F16>(rank, p, stream);
+}
+
+}  // namespace sgmv

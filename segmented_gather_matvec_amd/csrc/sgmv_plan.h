@@ -129,4 +129,34 @@ int mfma_expand_capacity(int dtype, int rank, int rows);
 hipError_t launch_mfma_shrink(int dtype, int rank, const MfmaParams& p, int num_proj, hipStream_t stream);
 hipError_t launch_mfma_expand(int dtype, int rank, const MfmaParams& p, int num_proj, hipStream_t stream);
 
+// Base projection with the LoRA term (batches of at most kBaseMaxRows rows):
+// split-K partial planes of X @ W on the matrix cores (strips of strip_cols
+// columns) and of V = X @ A_k in one launch, then an epilogue that sums them,
+// adds V @ B_k and rounds once.
+constexpr int kBaseMaxRows = 64;
+constexpr int kBaseStageRows = 128;  // W rows per pipeline stage (kc is a multiple)
+
+struct BaseParams {
+  int32_t n_rows, h_in, h_out, num_segs, num_loras;
+  int32_t strip_cols;      // 64, 128 or 256
+  int32_t strips;          // ceil(h_out / strip_cols)
+  int32_t ksplit, kc;      // K split: plane g covers rows [g*kc, (g+1)*kc) of W and A_k
+  int32_t base_grid;       // workgroups of the base product (a multiple of 8)
+  int32_t shrink_grid;     // LoRA shrink workgroups before them (n_rows * ksplit, rounded up to 8; 0: none)
+  int32_t pad_;
+  int64_t plane_stride;    // floats between partial planes of Y (n_rows * h_out)
+  const int32_t* seg_indptr;
+  const int32_t* lora_idx;
+  const uint16_t* X;       // [n_rows, h_in]
+  const uint16_t* W;       // [h_in, h_out]
+  const uint64_t* A_ptrs;  // [num_loras] -> A_k [h_in, rank]
+  const uint64_t* B_ptrs;  // [num_loras] -> B_k [rank, h_out]
+  float* vpartials;        // [ksplit][n_rows][rank] (null: no LoRA term)
+  float* partials;         // [ksplit][n_rows][h_out]
+  uint16_t* Y;             // [n_rows, h_out], written
+};
+
+// Partials then epilogue (two launches).
+hipError_t launch_base(int dtype, int rank, const BaseParams& p, hipStream_t stream);
+
 }  // namespace sgmv

@@ -274,3 +274,41 @@ def test_device_entry_points_fail_fast_on_bad_arguments():
     empty = good(num_segs=0, max_seg_len=0)
     assert lib.sgmv_lora_apply(ctypes.byref(empty), None, None, None, None, None, None, None, 0,
                                None) == sg.SGMV_OK
+
+
+def test_base_apply_fails_fast_on_bad_arguments():
+    """sgmv_base_lora_apply: every status below comes from host checks before any HIP call."""
+    lib = sg.load_library()
+    p = good()
+    fake = ctypes.c_void_p(0x10000)
+    odd = ctypes.c_void_p(0x10002)
+    need = sg.sgmv_base_workspace_bytes(p)
+    call = lambda prob, X, W, Y, ws, nbytes, A=fake, B=fake: lib.sgmv_base_lora_apply(
+        ctypes.byref(prob), X, W, A, B, Y, fake, fake, ws, nbytes, None)
+    assert call(p, None, fake, fake, fake, need) == sg.SGMV_ERR_INVALID_ARG
+    assert call(p, fake, None, fake, fake, need) == sg.SGMV_ERR_INVALID_ARG
+    assert call(p, fake, fake, None, fake, need) == sg.SGMV_ERR_INVALID_ARG
+    assert call(p, fake, fake, fake, fake, need, A=None) == sg.SGMV_ERR_INVALID_ARG
+    assert call(p, fake, odd, fake, fake, need) == sg.SGMV_ERR_UNSUPPORTED
+    assert call(p, fake, fake, fake, None, 0) == sg.SGMV_ERR_WORKSPACE
+    assert call(p, fake, fake, fake, fake, need - 1) == sg.SGMV_ERR_WORKSPACE
+    # more than 64 rows: a dense GEMM, not this entry point
+    big = good(n_rows=65, num_segs=65)
+    assert call(big, fake, fake, fake, fake, need) == sg.SGMV_ERR_UNSUPPORTED
+    with pytest.raises(sg.SgmvError) as e:
+        sg.sgmv_base_workspace_bytes(big)
+    assert e.value.status == sg.SGMV_ERR_UNSUPPORTED
+    # no rows: nothing to do
+    none = good(n_rows=0, num_segs=0, max_seg_len=0)
+    assert call(none, None, None, None, None, 0) == sg.SGMV_OK
+
+
+@pytest.mark.parametrize("kw", [{}, {"h_out": 11008}, {"h_in": 13824, "h_out": 5120, "rank": 64},
+                                {"n_rows": 1, "num_segs": 1}, {"n_rows": 64, "num_segs": 64}])
+def test_base_workspace_covers_its_parts(kw):
+    """The base workspace holds one fp32 partial plane of V and of Y per K split."""
+    p = good(**kw)
+    need = sg.sgmv_base_workspace_bytes(p)
+    planes = need // (p.n_rows * (p.h_out + p.rank) * 4)
+    assert planes >= 1
+    assert need < (p.n_rows * p.h_out * 4) * (p.h_in // 128 + 1) + (64 << 20)

@@ -1,0 +1,115 @@
+"""Parity of sgmv_base_lora_apply (Y = X @ W + per-row LoRA term, rounded once)
+against the fp64 oracle, through the C ABI.
+
+Cases cover: one row per LoRA (the decode batch of the headline shape, full
+size), repeated LoRAs, rows no segment covers, no segments at all (Y = X @ W),
+a single row, 64 rows, ragged K (h_in not a multiple of the 128-row stage) and
+ragged column strips (h_out not a multiple of 128), both formats, every rank,
+and integer-valued inputs whose result is exact (compared bit for bit)."""
+import numpy as np
+import pytest
+
+import oracle
+import segmented_gather_matvec_amd as sg
+import workloads
+from tests.gpu_cases import assert_close, i32, to_bits, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def run_base(dtype, X, W, A, B, seg, lidx, Y_fill=None):
+    import torch
+    n, h_in = X.shape
+    P, _, rank = A.shape
+    h_out = W.shape[1]
+    seg = np.asarray(seg, np.int32)
+    lidx = np.asarray(lidx, np.int32)
+    mx = int(np.diff(seg).max()) if len(seg) > 1 else 0
+    prob = sg.make_problem(dtype, n, h_in, h_out, rank, P, len(lidx), mx)
+    Xd, Wd, Ad, Bd = (to_device(a, dtype) for a in (X, W, A, B))
+    Y = torch.full((n, h_out), float("nan") if Y_fill is None else Y_fill, dtype=Xd.dtype, device="cuda")
+    ws = torch.full((sg.sgmv_base_workspace_bytes(prob),), 0xA5, dtype=torch.uint8, device="cuda")  # any contents
+    sg.sgmv_base_lora_apply(prob, Xd, Wd, sg.pointer_table(Ad), sg.pointer_table(Bd), Y,
+                            i32(seg if seg.size else [0]), i32(lidx if lidx.size else [0]), ws)
+    torch.cuda.synchronize()
+    return to_bits(Y), prob, (Xd, Wd, Ad, Bd, Y, ws, seg, lidx)
+
+
+def make_case(seed, dtype, n, h_in, h_out, rank, P, layout):
+    rng = np.random.default_rng(seed)
+    X, A, B, _ = workloads._values(rng, n, h_in, h_out, rank, P, dtype)
+    W = workloads.base_weight(rng, h_in, h_out, dtype)
+    if layout == "distinct":                  # row i -> LoRA i
+        seg, lidx = list(range(n + 1)), list(range(n))
+    elif layout == "skewed":                  # builder-sorted Zipf ids
+        ids = np.minimum(rng.zipf(1.5, size=n) - 1, P - 1).astype(np.int32)
+        perm, seg, lidx, _ = sg.sgmv_build_segments(ids, P)
+        X = X[perm]
+        seg, lidx = seg.tolist(), lidx.tolist()
+    elif layout == "tail_uncovered":          # rows past 2n/3 have no LoRA
+        cut = 2 * n // 3
+        seg, lidx = [0, cut // 2, cut], [P - 1, 0]
+    elif layout == "none":
+        seg, lidx = [0], []
+    else:
+        raise ValueError(layout)
+    return X, W, A, B, seg, lidx
+
+
+CASES = {
+    # name: (seed, dtype, n, h_in, h_out, rank, P, layout)
+    "distinct_b32_h4096_r16": (2, "f16", 32, 4096, 4096, 16, 32, "distinct"),
+    "skewed_b64_bf16_r64": (3, "bf16", 64, 1024, 1376, 64, 16, "skewed"),
+    "tail_uncovered_ragged": (4, "f16", 20, 520, 264, 8, 4, "tail_uncovered"),
+    "no_segments_bf16": (5, "bf16", 7, 384, 512, 32, 2, "none"),
+    "one_row_r32": (6, "bf16", 1, 2048, 1024, 32, 3, "distinct"),
+    "distinct_b64_f16_r8": (7, "f16", 64, 256, 2056, 8, 64, "distinct"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_base_apply_matches_oracle(name):
+    seed, dtype, n, h_in, h_out, rank, P, layout = CASES[name]
+    X, W, A, B, seg, lidx = make_case(seed, dtype, n, h_in, h_out, rank, P, layout)
+    got, _, _ = run_base(dtype, X, W, A, B, seg, lidx)
+    ref = oracle.sgmv_base_apply(dtype, X, W, A, B, seg, lidx)
+    assert_close(got, ref, dtype, what=name)
+
+
+def test_base_apply_integer_inputs_bit_exact():
+    """X, W, B in {-1, 0, 1}, A with 8 entries of +-1 per column: every partial sum is
+    an integer far inside fp32's exact range and the result is exact in fp16, so
+    the device result equals the oracle's bit for bit."""
+    rng = np.random.default_rng(11)
+    n, h_in, h_out, rank, P = 24, 384, 392, 16, 5
+    X, A, B, _ = workloads.integer_exact(rng, n, h_in, h_out, rank, P, "f16", nnz_per_col=8, y0_bound=0)
+    Wf = np.zeros((h_in, h_out), np.float32)
+    for c in range(h_out):
+        rows = rng.choice(h_in, size=12, replace=False)
+        Wf[rows, c] = rng.choice([-1.0, 1.0], size=12)
+    W = workloads.to_bits(Wf, "f16")
+    seg, lidx = [0, 5, 6, 14, 20], [4, 0, 4, 2]   # rows 20.. uncovered
+    got, _, _ = run_base("f16", X, W, A, B, seg, lidx)
+    ref = oracle.sgmv_base_apply("f16", X, W, A, B, seg, lidx)
+    assert np.array_equal(oracle.decode(got, "f16"), ref)
+
+
+def test_base_apply_repeated_calls_and_shared_workspace():
+    """Two calls in a row on one workspace (the second with fewer rows and other
+    weights) each match the oracle: nothing stale leaks between calls."""
+    import torch
+    dtype = "bf16"
+    X, W, A, B, seg, lidx = make_case(21, dtype, 48, 768, 640, 16, 8, "skewed")
+    got1, prob1, dev1 = run_base(dtype, X, W, A, B, seg, lidx)
+    assert_close(got1, oracle.sgmv_base_apply(dtype, X, W, A, B, seg, lidx), dtype, what="first")
+    X2, W2, A2, B2, seg2, lidx2 = make_case(22, dtype, 9, 768, 640, 16, 12, "distinct")
+    ws = dev1[5]
+    seg2a, lidx2a = np.asarray(seg2, np.int32), np.asarray(lidx2, np.int32)
+    prob2 = sg.make_problem(dtype, 9, 768, 640, 16, 12, len(lidx2a), 1)
+    assert sg.sgmv_base_workspace_bytes(prob2) <= ws.numel()
+    Xd, Wd, Ad, Bd = (to_device(a, dtype) for a in (X2, W2, A2, B2))
+    Y = torch.full((9, 640), float("nan"), dtype=Xd.dtype, device="cuda")
+    sg.sgmv_base_lora_apply(prob2, Xd, Wd, sg.pointer_table(Ad), sg.pointer_table(Bd), Y, i32(seg2a),
+                            i32(lidx2a), ws)
+    torch.cuda.synchronize()
+    assert_close(to_bits(Y), oracle.sgmv_base_apply(dtype, X2, W2, A2, B2, seg2, lidx2), dtype, what="second")

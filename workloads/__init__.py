@@ -165,6 +165,11 @@ def mixed(rank: int, seed: Optional[int] = None, pairs=((4096, 11008), (11008, 4
     return out
 
 
+def base_weight(rng, h_in: int, h_out: int, dtype: str) -> np.ndarray:
+    """Base projection weight W [h_in, h_out] ~ N(0, 1/h_in), so that X @ W ~ N(0, 1)."""
+    return _normal_bits(rng, (h_in, h_out), 1.0 / np.sqrt(h_in), dtype)
+
+
 def integer_exact(rng, n, h_in, h_out, rank, num_loras, dtype, nnz_per_col, y0_bound):
     """Inputs whose every product and partial sum is an integer well inside fp32's exact
     range and whose final Y is exact in fp16 / bf16: X, B in {-1, 0, 1}; each column of
