@@ -846,8 +846,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build measures one GPU only; the SGMV path runs on a single "
-              "MI355X and has no multi-GPU mode (run with --gpus 1).", file=sys.stderr)
+        print("bench.py measures one GPU only: the SGMV path runs on a single MI355X and has no "
+              "multi-GPU mode (run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
 
     import torch

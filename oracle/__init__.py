@@ -18,12 +18,13 @@ Contents
   Python (same page, multi-LoRA and SGMV paragraphs: every request is bound
   to its LoRA, and requests sharing a LoRA form one segment).
 
-Readings taken where the pages are silent (each also listed in the design doc):
-segment metadata is CSR (``seg_indptr`` [S+1], ``lora_idx`` [S]); segments
-may come in any order and repeat ids; empty segments are no-ops; rows past
-``seg_indptr[S]`` keep ``Y0``; the LoRA scale is 1; the builder sorts by
-ascending LoRA id with ties kept in request order and emits only non-empty
-segments.
+Readings taken where the pages are silent: segment metadata is CSR
+(``seg_indptr`` [S+1], ``lora_idx`` [S]); segments may come in any order and
+repeat ids; empty segments are no-ops; rows past ``seg_indptr[S]`` keep
+``Y0`` (and get ``X @ W`` alone in the base projection); the LoRA scale is 1
+unless a per-LoRA scale is given, which multiplies the LoRA term only; a
+LoRA of smaller rank is its pair zero-padded; the builder sorts by ascending
+LoRA id with ties kept in request order and emits only non-empty segments.
 """
 from __future__ import annotations
 
