@@ -231,32 +231,15 @@ struct MfmaPlan {
 // Aim for about four shrink workgroups (row tile x H1 chunk) per CU.
 // Expand: when row tiles are mostly full, a chunk is bandwidth-bound and
 // about four workgroups per CU (dispatched as slots free up) hide latency
-// best.  When they are mostly short (decode-like rows of many LoRAs), a chunk
-// is latency-bound: the grid is then sized to be resident at once, so each
-// workgroup streams several chunks through its prefetch pipeline and pays its
-// start-up once.  Measured: on 256 rows in 34 segments this cut the expand by
-// a quarter; on 5.4k rows in 32 segments it cost a tenth.
+// best.  When they are mostly short (decode-like rows of many LoRAs), the
+// expand takes 16-row tiles and three 128-column chunks per workgroup: a sweep
+// of 1 to 10 chunks on 256 rows in 34 segments (r = 64, H = 5120 and 13824)
+// found 3 best, about 1.5% ahead of a grid sized to be resident at once.
 constexpr int kMfmaShrinkTarget = 1024;
 constexpr int kMfmaExpandTarget = 1024;
 constexpr int kMfmaShortTileRows = 32;   // mean rows per 64-row tile below which tiles count as short
 constexpr int kMfmaShortExpandRows = 16; // expand tile rows for short tiles
-constexpr int kMfmaExpandFallbackCapacity = 512;
-
-int mfma_expand_capacity_cached(int dtype, int rank, int rows) {
-  static std::mutex mu;
-  static int cache[kMaxDevices][2][3][2];
-  static bool init[kMaxDevices][2][3][2];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
-  const int ri = rank == 16 ? 0 : rank == 32 ? 1 : 2;
-  const int si = rows == kMfmaShortExpandRows ? 1 : 0;
-  std::lock_guard<std::mutex> lock(mu);
-  if (!init[dev][dtype][ri][si]) {
-    cache[dev][dtype][ri][si] = sgmv::mfma_expand_capacity(dtype, rank, rows);
-    init[dev][dtype][ri][si] = true;
-  }
-  return cache[dev][dtype][ri][si];
-}
+constexpr int kMfmaShortChunksPerWg = 3;
 
 int64_t units_for(const sgmv_problem_t& p, int rows, int* direct) {
   if (p.max_seg_len <= rows) {
@@ -282,20 +265,18 @@ MfmaPlan plan_mfma(const sgmv_problem_t& p) {
   m.kc = (int)round_up(ceil_div(p.h_in, ks), sgmv::kMfmaKChunk);
   m.ksplit = (int)ceil_div(p.h_in, m.kc);
   const int64_t nchunks = ceil_div(p.h_out, sgmv::kMfmaColsPerTile);
-  int64_t target = kMfmaExpandTarget;
   m.units_x = m.units64;
   m.direct_x = m.direct64;
   if ((int64_t)p.n_rows < kMfmaShortTileRows * units) {
-    // Short tiles: 16-row expand tiles (all four waves compute) and a grid
-    // that is resident at once.
+    // Short tiles: 16-row expand tiles (all four waves compute), a few chunks
+    // per workgroup.
     m.expand_rows = kMfmaShortExpandRows;
     m.units_x = units_for(p, kMfmaShortExpandRows, &m.direct_x);
-    target = sgmv::mfma_supported(p.rank) ? mfma_expand_capacity_cached(p.dtype, p.rank, m.expand_rows) : 0;
-    if (target <= 0) target = kMfmaExpandFallbackCapacity;
+    m.chunks_per_wg = (int)std::min<int64_t>(nchunks, kMfmaShortChunksPerWg);
+  } else {
+    const int64_t groups = std::max<int64_t>(1, std::min<int64_t>(nchunks, kMfmaExpandTarget / units));
+    m.chunks_per_wg = (int)ceil_div(nchunks, groups);
   }
-  const int64_t groups =
-      std::max<int64_t>(1, std::min<int64_t>(nchunks, target / std::max<int64_t>(m.units_x, 1)));
-  m.chunks_per_wg = (int)ceil_div(nchunks, groups);
   m.partial_bytes = (size_t)m.ksplit * (size_t)p.n_rows * p.rank * sizeof(float);
   return m;
 }

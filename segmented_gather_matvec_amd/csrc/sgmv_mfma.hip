@@ -525,38 +525,6 @@ hipError_t launch_stage(int dtype, int rank, int stage, const MfmaParams& p, int
 
 bool mfma_supported(int rank) { return rank == 16 || rank == 32 || rank == 64; }
 
-// The smaller occupancy of the plain and the extended variant.
-template <class T, int R, int MT>
-int expand_capacity_t() {
-  int per_cu = 0, per_cu2 = 0, dev = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &per_cu, reinterpret_cast<const void*>(&sgmv_mfma_expand_kernel<T, R, false, MT>), kThreads, 0) !=
-      hipSuccess)
-    return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &per_cu2, reinterpret_cast<const void*>(&sgmv_mfma_expand_kernel<T, R, true, MT>), kThreads, 0) !=
-      hipSuccess)
-    return 0;
-  per_cu = per_cu < per_cu2 ? per_cu : per_cu2;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  return per_cu * cus;
-}
-
-template <class T, int R>
-int expand_capacity_rows(int rows) {
-  return rows == 16 ? expand_capacity_t<T, R, 16>() : expand_capacity_t<T, R, kMT>();
-}
-
-int mfma_expand_capacity(int dtype, int rank, int rows) {
-  switch (rank) {
-    case 16: return dtype == 1 ? expand_capacity_rows<BF16, 16>(rows) : expand_capacity_rows<F16, 16>(rows);
-    case 32: return dtype == 1 ? expand_capacity_rows<BF16, 32>(rows) : expand_capacity_rows<F16, 32>(rows);
-    case 64: return dtype == 1 ? expand_capacity_rows<BF16, 64>(rows) : expand_capacity_rows<F16, 64>(rows);
-  }
-  return 0;
-}
-
 hipError_t launch_mfma_shrink(int dtype, int rank, const MfmaParams& p, int num_proj, hipStream_t stream) {
   hipError_t e = launch_stage(dtype, rank, 0, p, num_proj, stream);
   if (e != hipSuccess) return e;

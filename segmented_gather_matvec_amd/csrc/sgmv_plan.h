@@ -123,8 +123,6 @@ struct MfmaParams {
 };
 
 bool mfma_supported(int rank);
-// Expand workgroups with `rows`-row tiles that fit on the device at once (0 if unknown).
-int mfma_expand_capacity(int dtype, int rank, int rows);
 // Shrink into the partial planes, then reduce them into V (two launches).
 hipError_t launch_mfma_shrink(int dtype, int rank, const MfmaParams& p, int num_proj, hipStream_t stream);
 hipError_t launch_mfma_expand(int dtype, int rank, const MfmaParams& p, int num_proj, hipStream_t stream);
