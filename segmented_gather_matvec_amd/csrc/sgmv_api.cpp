@@ -469,7 +469,7 @@ struct BasePlan {
   int ksplit = 1;
   int kc = 0;
   int base_grid = 0;
-  size_t v_off = 0, p_off = 0, total = 0;  // workspace layout
+  size_t b_off = 0, v_off = 0, p_off = 0, total = 0;  // workspace layout
 };
 
 BasePlan plan_base(const sgmv_problem_t& p) {
@@ -480,9 +480,10 @@ BasePlan plan_base(const sgmv_problem_t& p) {
   b.kc = (int)round_up(ceil_div(p.h_in, ks), sgmv::kBaseStageRows);
   b.ksplit = (int)ceil_div(p.h_in, b.kc);
   b.base_grid = (int)round_up((int64_t)b.strips * b.ksplit, 8);
-  // [partial planes of V][partial planes of Y]
-  b.v_off = 0;
-  b.p_off = (size_t)round_up((int64_t)b.ksplit * p.n_rows * p.rank * (int64_t)sizeof(float), 256);
+  // [B_k of each row][partial planes of V][partial planes of Y]
+  b.b_off = 0;
+  b.v_off = (size_t)round_up((int64_t)p.n_rows * (int64_t)sizeof(uint64_t), 256);
+  b.p_off = b.v_off + (size_t)round_up((int64_t)b.ksplit * p.n_rows * p.rank * (int64_t)sizeof(float), 256);
   b.total = b.p_off + (size_t)b.ksplit * (size_t)p.n_rows * (size_t)p.h_out * sizeof(float);
   return b;
 }
@@ -757,6 +758,7 @@ sgmv_status_t sgmv_base_lora_apply(const sgmv_problem_t* p, const void* X, const
   q.A_ptrs = lora ? reinterpret_cast<const uint64_t*>(A_ptrs) : nullptr;
   q.B_ptrs = lora ? reinterpret_cast<const uint64_t*>(B_ptrs) : nullptr;
   q.vpartials = lora ? reinterpret_cast<float*>(w + b.v_off) : nullptr;
+  q.row_b = lora ? reinterpret_cast<uint64_t*>(w + b.b_off) : nullptr;
   q.partials = reinterpret_cast<float*>(w + b.p_off);
   q.Y = static_cast<uint16_t*>(Y);
   return hip_status(sgmv::launch_base(p->dtype, p->rank, q, s));

@@ -93,9 +93,11 @@ __device__ inline void shrink_role(const BaseParams& p, int item, float* lds) {
   const int g = item - i * p.ksplit;
   if (i >= p.n_rows) return;  // padding of the shrink grid to a multiple of 8
   const int seg = segment_of_row(p, i);
-  if (seg < 0) return;
-  const int k = p.lora_idx[seg];
-  if (k < 0 || k >= p.num_loras || p.A_ptrs == nullptr) return;
+  const int k = seg >= 0 ? p.lora_idx[seg] : -1;
+  const bool lora = k >= 0 && k < p.num_loras && p.A_ptrs != nullptr && p.B_ptrs != nullptr;
+  // Workgroup (i, 0) records row i's B_k (0: no LoRA term) for the epilogue.
+  if (g == 0 && t == 0) p.row_b[i] = lora ? p.B_ptrs[k] : 0ull;
+  if (!lora) return;
   const uint16_t* Ak = reinterpret_cast<const uint16_t*>(p.A_ptrs[k]);
   const uint16_t* xrow = p.X + (int64_t)i * p.h_in;
   const int k0 = g * p.kc;
@@ -289,14 +291,19 @@ __global__ __launch_bounds__(64) void sgmv_base_epilogue_kernel(BaseParams p) {
   const bool col_ok = c < p.h_out;
   const int cc = col_ok ? c : 0;
 
-  // Bounds of the first 64 segments, then the partial planes of Y (up to
-  // kBatch planes), all issued before anything waits: the wait for the
-  // bounds then does not wait for the planes (loads complete in order).
-  const bool have = p.seg_indptr != nullptr && p.lora_idx != nullptr && lane < p.num_segs;
-  int lo0 = 0, hi0 = 0;
-  if (have) {
-    lo0 = p.seg_indptr[lane];
-    hi0 = p.seg_indptr[lane + 1];
+  // Everything this wave needs that depends only on the row is fetched in one
+  // round: row i's B_k (recorded by the shrink), the partial planes of V
+  // (lane j < R: rank j) and the partial planes of Y (up to kBatch planes).
+  const bool lora_planes = p.vpartials != nullptr && p.row_b != nullptr;
+  const uint64_t bptr = lora_planes ? p.row_b[i] : 0ull;
+  float pv[kBatch];
+  const float* vp = lora_planes ? p.vpartials + (int64_t)i * R + (lane < R ? lane : 0) : nullptr;
+  if (lora_planes) {
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int g = u < p.ksplit ? u : p.ksplit - 1;
+      pv[u] = vp[(int64_t)g * p.n_rows * R];
+    }
   }
   const float* row = p.partials + (int64_t)i * p.h_out + cc;
   f32x4 a[kBatch], b[kBatch];
@@ -306,16 +313,10 @@ __global__ __launch_bounds__(64) void sgmv_base_epilogue_kernel(BaseParams p) {
     a[u] = *reinterpret_cast<const f32x4*>(row + (int64_t)g * p.plane_stride);
     b[u] = *reinterpret_cast<const f32x4*>(row + (int64_t)g * p.plane_stride + 4);
   }
-
-  const unsigned long long m0 = __ballot(have && lo0 <= i && i < hi0);
-  int seg = m0 ? __builtin_ctzll(m0) : (p.num_segs > 64 ? segment_of_row(p, i, 64) : -1);
-  seg = __builtin_amdgcn_readfirstlane(seg);
-  int k = seg >= 0 ? p.lora_idx[seg] : -1;
-  k = __builtin_amdgcn_readfirstlane(k);
-  const bool lora = k >= 0 && k < p.num_loras && p.B_ptrs != nullptr && p.vpartials != nullptr;
+  const bool lora = bptr != 0ull;
 
   constexpr int JB = R < 16 ? R : 16;  // B_k rows per batch of loads
-  const uint16_t* Bk = lora ? reinterpret_cast<const uint16_t*>(p.B_ptrs[k]) : nullptr;
+  const uint16_t* Bk = reinterpret_cast<const uint16_t*>(bptr);
   u32x4 bv[JB];
   if (lora) {
 #pragma unroll
@@ -325,15 +326,14 @@ __global__ __launch_bounds__(64) void sgmv_base_epilogue_kernel(BaseParams p) {
   // shared through LDS.
   __shared__ float lds_v[R];
   if (lora && lane < R) {
-    // All of a batch's plane loads are issued before the first add.
     float v = 0.f;
-    const float* vp = p.vpartials + (int64_t)i * R + lane;
     for (int g0 = 0; g0 < p.ksplit; g0 += kBatch) {
-      float pv[kBatch];
+      if (g0 > 0) {
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const int g = g0 + u < p.ksplit ? g0 + u : p.ksplit - 1;
-        pv[u] = vp[(int64_t)g * p.n_rows * R];
+        for (int u = 0; u < kBatch; ++u) {
+          const int g = g0 + u < p.ksplit ? g0 + u : p.ksplit - 1;
+          pv[u] = vp[(int64_t)g * p.n_rows * R];
+        }
       }
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) v = g0 + u < p.ksplit ? v + pv[u] : v;

@@ -150,6 +150,7 @@ struct BaseParams {
   const uint64_t* A_ptrs;  // [num_loras] -> A_k [h_in, rank]
   const uint64_t* B_ptrs;  // [num_loras] -> B_k [rank, h_out]
   float* vpartials;        // [ksplit][n_rows][rank] (null: no LoRA term)
+  uint64_t* row_b;         // [n_rows] B_k of each row, 0 without a LoRA term (written by the shrink)
   float* partials;         // [ksplit][n_rows][h_out]
   uint16_t* Y;             // [n_rows, h_out], written
 };
