@@ -32,7 +32,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kXcds = 8;
 
-
 template <class T>
 __device__ inline f32x4 mfma(const u32x4& a, const u32x4& b, f32x4 c);
 template <>
@@ -60,12 +59,12 @@ __device__ inline void store_pair_transposed(uint16_t* dst, int stride, const u3
 }
 
 // ---------------------------------------------------------------- LoRA shrink
-// Segment of row i among segments first.. (64 at a time; -1: none covers it).
-__device__ inline int segment_of_row(const BaseParams& p, int i, int first = 0) {
+// Segment of row i (64 segments at a time; -1: none covers it).
+__device__ inline int segment_of_row(const BaseParams& p, int i) {
   const int lane = threadIdx.x & 63;
   int seg = -1;
   if (p.num_segs > 0 && p.seg_indptr != nullptr && p.lora_idx != nullptr) {
-    for (int s0 = first; s0 < p.num_segs; s0 += 64) {
+    for (int s0 = 0; s0 < p.num_segs; s0 += 64) {
       const int s = s0 + lane;
       bool hit = false;
       if (s < p.num_segs) hit = p.seg_indptr[s] <= i && i < p.seg_indptr[s + 1];
@@ -96,7 +95,7 @@ __device__ inline void shrink_role(const BaseParams& p, int item, float* lds) {
   const int k = seg >= 0 ? p.lora_idx[seg] : -1;
   const bool lora = k >= 0 && k < p.num_loras && p.A_ptrs != nullptr && p.B_ptrs != nullptr;
   // Workgroup (i, 0) records row i's B_k (0: no LoRA term) for the epilogue.
-  if (g == 0 && t == 0) p.row_b[i] = lora ? p.B_ptrs[k] : 0ull;
+  if (g == 0 && t == 0 && p.row_b != nullptr) p.row_b[i] = lora ? p.B_ptrs[k] : 0ull;
   if (!lora) return;
   const uint16_t* Ak = reinterpret_cast<const uint16_t*>(p.A_ptrs[k]);
   const uint16_t* xrow = p.X + (int64_t)i * p.h_in;
