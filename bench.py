@@ -673,12 +673,13 @@ def latency_curve(batches=(1, 2, 4, 8, 16, 32, 64), steps=200, warmup=20):
             "curve": curve}
 
 
-def cpu_baseline(seconds=10.0):
-    """The oracle as it stands, on a host copy of the headline workload's shape."""
+def cpu_baseline(seconds=10.0, threads=0):
+    """The oracle as it stands, on a host copy of the headline workload's shape
+    (threads: 0 = every host core OpenMP offers)."""
     import oracle
     import workloads
     w = workloads.decode_distinct()
-    threads = oracle.max_threads()
+    threads = threads if threads > 0 else oracle.max_threads()
     calls, t0 = 0, time.perf_counter()
     while True:
         oracle.sgmv_apply("f16", w.X, w.A, w.B, w.seg_indptr, w.lora_idx, w.Y0, nthreads=threads)
@@ -840,6 +841,8 @@ def main():
                     help="replay the timed steps from a captured HIP graph instead of eager launches")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-threads", type=int, default=0,
+                    help="host threads of the oracle baseline (0 = all cores)")
     ap.add_argument("--no-check", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run 8 plain device copies of 512 MiB (reference for HBM counters)")
@@ -943,7 +946,7 @@ def main():
         "parity_max_err_over_bound": None if worst is None else round(worst, 4),
     }
     if not args.no_cpu_baseline and args.workload == DEFAULT_WORKLOAD:
-        line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(args.cpu_seconds, args.cpu_threads)
     print(json.dumps(line), flush=True)
 
 
