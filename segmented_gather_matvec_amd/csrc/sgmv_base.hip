@@ -52,13 +52,18 @@ __device__ inline int segment_of_row(const BaseParams& p, int i) {
 // Workgroup (i, g) of the shrink role: partial V plane g of row i,
 //   vpart[g][i][j] = sum_{h in K_g} X[i, h] * A_k[h, j],
 // in fp32 with vector FMA (each row may use its own LoRA, so this is not a
-// shared-operand product).  Thread t owns 8 ranks (group t % JG) of the rows h
-// = t / JG + (256 / JG) m; the groups are summed in LDS in thread order.
+// shared-operand product).  Thread t owns 8 ranks (group t % JG) of the rows
+// h = t / JG + HPT m; one round of loads covers HPT * kUnroll = 512 rows.  The
+// threads of one rank group are summed by a butterfly within each wave, then
+// the four waves in wave order through LDS (a fixed order).
 template <class T, int R>
 __device__ inline void shrink_role(const BaseParams& p, int item, float* lds) {
   constexpr int JG = R / 8;               // 128-bit vectors per row of A_k
-  constexpr int HPT = kThreads / JG;      // rows of A_k per pass of the workgroup
+  constexpr int HPT = kThreads / JG;      // rows of A_k per load of the workgroup
+  constexpr int kUnroll = 512 / HPT;      // loads per thread per round
   const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
   const int i = item / p.ksplit;
   const int g = item - i * p.ksplit;
   if (i >= p.n_rows) return;  // padding of the shrink grid to a multiple of 8
@@ -74,32 +79,38 @@ __device__ inline void shrink_role(const BaseParams& p, int item, float* lds) {
   const int k1 = p.h_in < k0 + p.kc ? p.h_in : k0 + p.kc;
   const int jg = t % JG, h0 = t / JG;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  constexpr int kUnroll = 4;
   for (int hb = k0 + h0; hb < k1; hb += HPT * kUnroll) {
     u32x4 a[kUnroll];
-    float x[kUnroll];
+    uint16_t xb[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int h = hb + u * HPT;
       const bool ok = h < k1;
       a[u] = load_stream(Ak + (ok ? (int64_t)h * R + jg * 8 : 0));
-      x[u] = ok ? T::one(load_stream_u16(xrow + h)) : 0.f;
+      xb[u] = load_stream_u16(xrow + (ok ? h : 0));
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
+      const float x = hb + u * HPT < k1 ? T::one(xb[u]) : 0.f;
       float af[8];
       unpack8<T>(a[u], af);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(x[u], af[e], acc[e]);
+      for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(x, af[e], acc[e]);
     }
   }
+  // Butterfly over the lanes of one rank group (lanes jg + JG m of the wave).
 #pragma unroll
-  for (int e = 0; e < 8; ++e) lds[t * 8 + e] = acc[e];
+  for (int mask = JG; mask < 64; mask <<= 1)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += shfl_xor(acc[e], mask);
+  if (lane < JG)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) lds[(wave * JG + lane) * 8 + e] = acc[e];
   __syncthreads();
   if (t < R) {
-    const int jj = t / 8, e = t % 8;
     float v = 0.f;
-    for (int hh = 0; hh < HPT; ++hh) v += lds[(hh * JG + jj) * 8 + e];
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) v += lds[w * R + t];
     p.vpartials[((int64_t)g * p.n_rows + i) * R + t] = v;
   }
 }
