@@ -133,8 +133,11 @@ MODEL_WORKLOADS = ["llama13b_r64_b256_forward"]
 HET_WORKLOADS = ["decode_mixedrank_h4096_r64_b32"]
 # Base projection with the LoRA term (sgmv_base_lora_apply): Y = X @ W + the
 # per-row LoRA term, Distinct decode batches.
+# The base_packed_ lines run sgmv_base_lora_apply_packed on W packed once
+# beforehand (the packing is not timed: a server packs its weights at load).
 BASE_WORKLOADS = ["base_decode_distinct_h4096_r16_b32", "base_decode_distinct_h4096_r16_b8",
                   "base_decode_distinct_h4096_r16_b64", "base_decode_distinct_h11008to4096_r16_b32"]
+BASE_WORKLOADS += [w.replace("base_", "base_packed_", 1) for w in BASE_WORKLOADS]
 
 
 class SingleCallBench:
@@ -711,14 +714,15 @@ class BaseBench:
         import segmented_gather_matvec_amd as sg
         import workloads as wl
 
-        m = re.fullmatch(r"base_decode_distinct_h(\d+)(?:to(\d+))?_r(\d+)_b(\d+)", name)
+        m = re.fullmatch(r"base_(packed_)?decode_distinct_h(\d+)(?:to(\d+))?_r(\d+)_b(\d+)", name)
         if not m:
             raise SystemExit(f"unknown workload {name}")
+        self.packed = m.group(1) is not None
         self.name, self.sg, self.torch = name, sg, torch
         self.dtype = "f16"
-        self.h_in = int(m.group(1))
-        self.h_out = int(m.group(2) or m.group(1))
-        self.rank, self.n = int(m.group(3)), int(m.group(4))
+        self.h_in = int(m.group(2))
+        self.h_out = int(m.group(3) or m.group(2))
+        self.rank, self.n = int(m.group(4)), int(m.group(5))
         e = 2
         w_bytes = e * self.h_in * self.h_out
         self.wcopies = max(2, math.ceil((1 << 30) / w_bytes))
@@ -747,11 +751,16 @@ class BaseBench:
         self.rows_per_step = self.n
         self.calls_per_step = 1
         self.fn = sg.load_library().sgmv_base_lora_apply
+        Wsrc = self.W
+        if self.packed:
+            self.fn = sg.load_library().sgmv_base_lora_apply_packed
+            Wsrc = torch.stack([sg.pack_base_weight(self.W[w]) for w in range(self.wcopies)])
+            self.Wp = Wsrc
         pb = ctypes.byref(self.problem)
         self.args = []
         for c in range(max(self.wcopies, self.tables, self.copies)):
             w, t, x = c % self.wcopies, c % self.tables, c % self.copies
-            self.args.append((pb, self.X[x].data_ptr(), self.W[w].data_ptr(), self.A_tab[t].data_ptr(),
+            self.args.append((pb, self.X[x].data_ptr(), Wsrc[w].data_ptr(), self.A_tab[t].data_ptr(),
                               self.B_tab[t].data_ptr(), self.Y[x].data_ptr(), self.seg.data_ptr(),
                               self.lidx.data_ptr(), self.ws.data_ptr(), self.ws.numel()))
         self.unfused = self.time_unfused()
@@ -816,6 +825,7 @@ class BaseBench:
                 "batch_rows": self.n, "segments": self.n, "distinct_loras": self.n, "w_copies": self.wcopies,
                 "lora_tables": self.tables, "xy_copies": self.copies, "algorithmic_bytes_per_step": self.bytes,
                 "output": "Y = X @ W + LoRA term (written, one rounding)",
+                "weight_layout": "packed once before timing" if self.packed else "row-major",
                 "unfused_torch_matmul_plus_sgmv_us_per_call": round(self.unfused, 3)}
 
 

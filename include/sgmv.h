@@ -283,6 +283,36 @@ sgmv_status_t sgmv_base_lora_apply(const sgmv_problem_t* problem, const void* X,
                                    const int32_t* seg_indptr, const int32_t* lora_idx, void* ws,
                                    size_t ws_bytes, void* stream);
 
+/* Base projection from a packed copy of W.  The base weight of a layer does
+ * not change while a server runs, so it can be rearranged once into the
+ * operand order of the matrix cores; sgmv_base_lora_apply_packed then streams
+ * it with fully coalesced loads straight into the MFMA operands (no LDS
+ * staging).  It computes exactly what sgmv_base_lora_apply computes (the same
+ * sums in the same order, so the two outputs are bitwise equal).
+ *
+ * Packed layout (16-bit elements, either format): kst = ceil(h_in / 128) * 4
+ * k-steps of 32 rows; ceil(h_out / 16) rounded up to an even count of
+ * 16-column blocks.  Block (nb, ks) is 512 elements at offset
+ * (nb * kst + ks) * 512; its elements 8 L + e (L = 16 q + m, e = 0..7) hold
+ * W[32 ks + 8 q + e][16 nb + m], or 0 past the matrix.
+ *
+ * sgmv_base_packed_weight_bytes: size of the packed copy for h_in, h_out > 0
+ *   (SGMV_ERR_INVALID_ARG otherwise).
+ * sgmv_base_pack_weight: W device [h_in, h_out] row-major, 2-byte aligned ->
+ *   Wp device, 16-byte aligned, wp_bytes >= sgmv_base_packed_weight_bytes
+ *   (SGMV_ERR_WORKSPACE below it).  One launch, asynchronous on `stream`; W is
+ *   not modified and the caller owns both buffers.
+ * sgmv_base_lora_apply_packed: the arguments of sgmv_base_lora_apply with Wp,
+ *   the packed copy of W for problem->h_in and problem->h_out, in place of W
+ *   (16-byte aligned); same workspace size, limits and errors. */
+sgmv_status_t sgmv_base_packed_weight_bytes(int32_t h_in, int32_t h_out, size_t* bytes);
+sgmv_status_t sgmv_base_pack_weight(const void* W, int32_t h_in, int32_t h_out, void* Wp, size_t wp_bytes,
+                                    void* stream);
+sgmv_status_t sgmv_base_lora_apply_packed(const sgmv_problem_t* problem, const void* X, const void* Wp,
+                                          const void* const* A_ptrs, const void* const* B_ptrs, void* Y,
+                                          const int32_t* seg_indptr, const int32_t* lora_idx, void* ws,
+                                          size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

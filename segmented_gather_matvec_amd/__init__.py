@@ -33,7 +33,8 @@ SGMV_MAX_PROJECTIONS = 4
 ENTRY_POINTS = ("sgmv_status_str", "sgmv_build_segments", "sgmv_check_problem",
                 "sgmv_check_segments", "sgmv_workspace_bytes", "sgmv_query_plan", "sgmv_shrink",
                 "sgmv_expand", "sgmv_lora_apply", "sgmv_lora_apply_batched", "sgmv_base_workspace_bytes",
-                "sgmv_base_lora_apply")
+                "sgmv_base_lora_apply", "sgmv_base_packed_weight_bytes", "sgmv_base_pack_weight",
+                "sgmv_base_lora_apply_packed")
 
 
 class SgmvError(RuntimeError):
@@ -100,6 +101,9 @@ def load_library(path: str = LIB_PATH):
     lib.sgmv_lora_apply_batched.argtypes = [prob, P, ctypes.POINTER(sgmv_projection_t), I32, P, P, P, P, SZ, P]
     lib.sgmv_base_workspace_bytes.argtypes = [prob, ctypes.POINTER(SZ)]
     lib.sgmv_base_lora_apply.argtypes = [prob, P, P, P, P, P, P, P, P, SZ, P]
+    lib.sgmv_base_packed_weight_bytes.argtypes = [I32, I32, ctypes.POINTER(SZ)]
+    lib.sgmv_base_pack_weight.argtypes = [P, I32, I32, P, SZ, P]
+    lib.sgmv_base_lora_apply_packed.argtypes = [prob, P, P, P, P, P, P, P, P, SZ, P]
     for name in ENTRY_POINTS[1:]:
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -290,20 +294,58 @@ def new_base_workspace(problem: sgmv_problem_t, device="cuda"):
     return torch.zeros(sgmv_base_workspace_bytes(problem), dtype=torch.uint8, device=device)
 
 
-def sgmv_base_lora_apply(problem, X, W, A_ptrs, B_ptrs, Y, seg_indptr, lora_idx, ws, stream=None):
-    """Y[i] = X[i] @ W + (X[i] @ A_k) @ B_k on the device (Y written, rounded once); asynchronous.
-    Rows no segment covers get X[i] @ W.  At most 64 rows."""
+def _base_apply(name, problem, X, W, A_ptrs, B_ptrs, Y, seg_indptr, lora_idx, ws, stream):
     import torch
     dt = _torch_dtype(problem)
     _need(X, "X", dt); _need(W, "W", dt); _need(Y, "Y", dt)
     _need(A_ptrs, "A_ptrs", torch.int64); _need(B_ptrs, "B_ptrs", torch.int64)
     _need(seg_indptr, "seg_indptr", torch.int32); _need(lora_idx, "lora_idx", torch.int32)
     _need(ws, "ws")
-    st = load_library().sgmv_base_lora_apply(ctypes.byref(problem), _ptr(X), _ptr(W), _ptr(A_ptrs),
-                                             _ptr(B_ptrs), _ptr(Y), _ptr(seg_indptr), _ptr(lora_idx),
-                                             _ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0,
-                                             _stream(stream))
-    _check(st, "sgmv_base_lora_apply")
+    st = getattr(load_library(), name)(ctypes.byref(problem), _ptr(X), _ptr(W), _ptr(A_ptrs),
+                                       _ptr(B_ptrs), _ptr(Y), _ptr(seg_indptr), _ptr(lora_idx),
+                                       _ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0,
+                                       _stream(stream))
+    _check(st, name)
+
+
+def sgmv_base_lora_apply(problem, X, W, A_ptrs, B_ptrs, Y, seg_indptr, lora_idx, ws, stream=None):
+    """Y[i] = X[i] @ W + (X[i] @ A_k) @ B_k on the device (Y written, rounded once); asynchronous.
+    Rows no segment covers get X[i] @ W.  At most 64 rows."""
+    _base_apply("sgmv_base_lora_apply", problem, X, W, A_ptrs, B_ptrs, Y, seg_indptr, lora_idx, ws, stream)
+
+
+def sgmv_base_packed_weight_bytes(h_in: int, h_out: int) -> int:
+    """Bytes of the packed copy of a [h_in, h_out] base weight."""
+    out = ctypes.c_size_t(0)
+    _check(load_library().sgmv_base_packed_weight_bytes(int(h_in), int(h_out), ctypes.byref(out)),
+           "sgmv_base_packed_weight_bytes")
+    return int(out.value)
+
+
+def sgmv_base_pack_weight(W, Wp, stream=None):
+    """Write the packed copy of the 2-D device weight W into Wp (asynchronous)."""
+    _need(W, "W"); _need(Wp, "Wp")
+    if W.dim() != 2 or W.element_size() != 2:
+        raise ValueError("W must be a 2-D tensor of a 16-bit format")
+    h_in, h_out = W.shape
+    st = load_library().sgmv_base_pack_weight(_ptr(W), int(h_in), int(h_out), _ptr(Wp),
+                                              Wp.numel() * Wp.element_size(), _stream(stream))
+    _check(st, "sgmv_base_pack_weight")
+
+
+def pack_base_weight(W, stream=None):
+    """New device tensor (same format as W, flat) holding the packed copy of W."""
+    import torch
+    n = sgmv_base_packed_weight_bytes(*W.shape) // W.element_size()
+    Wp = torch.empty(n, dtype=W.dtype, device=W.device)
+    sgmv_base_pack_weight(W, Wp, stream)
+    return Wp
+
+
+def sgmv_base_lora_apply_packed(problem, X, Wp, A_ptrs, B_ptrs, Y, seg_indptr, lora_idx, ws, stream=None):
+    """sgmv_base_lora_apply with Wp, the packed copy of W, in place of W."""
+    _base_apply("sgmv_base_lora_apply_packed", problem, X, Wp, A_ptrs, B_ptrs, Y, seg_indptr, lora_idx, ws,
+                stream)
 
 
 def batched_workspace_bytes(problem: sgmv_problem_t, num_projections: int) -> int:

@@ -306,6 +306,7 @@ sgmv::MfmaParams mfma_params(const sgmv_problem_t& p, const MfmaPlan& m, const i
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 bool aligned8(const void* p) { return ((uintptr_t)p & 7u) == 0; }
+bool aligned2(const void* p) { return ((uintptr_t)p & 1u) == 0; }
 
 bool nothing_to_do(const sgmv_problem_t& p) {
   return p.num_segs == 0 || p.n_rows == 0 || p.max_seg_len == 0;
@@ -720,10 +721,21 @@ sgmv_status_t sgmv_base_workspace_bytes(const sgmv_problem_t* p, size_t* bytes) 
   return SGMV_OK;
 }
 
-sgmv_status_t sgmv_base_lora_apply(const sgmv_problem_t* p, const void* X, const void* W,
-                                   const void* const* A_ptrs, const void* const* B_ptrs, void* Y,
-                                   const int32_t* seg_indptr, const int32_t* lora_idx, void* ws,
-                                   size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Bytes of the packed layout of W [h_in, h_out]: 16-column blocks (an even
+// count) of ceil(h_in / 128) * 4 k-steps of 1 KiB each.
+int64_t packed_ksteps(int64_t h_in) { return ceil_div(h_in, 128) * 4; }
+int64_t packed_bytes(int64_t h_in, int64_t h_out) {
+  return round_up(ceil_div(h_out, 16), 2) * packed_ksteps(h_in) * 1024;
+}
+
+sgmv_status_t base_apply(const sgmv_problem_t* p, const void* X, const void* W, bool packed,
+                         const void* const* A_ptrs, const void* const* B_ptrs, void* Y,
+                         const int32_t* seg_indptr, const int32_t* lora_idx, void* ws, size_t ws_bytes,
+                         void* stream) {
   sgmv_status_t st = sgmv_check_problem(p);
   if (st != SGMV_OK) return st;
   if (p->n_rows > sgmv::kBaseMaxRows) return SGMV_ERR_UNSUPPORTED;
@@ -750,6 +762,7 @@ sgmv_status_t sgmv_base_lora_apply(const sgmv_problem_t* p, const void* X, const
   q.kc = b.kc;
   q.base_grid = b.base_grid;
   q.shrink_grid = lora ? (int32_t)round_up((int64_t)p->n_rows * b.ksplit, 8) : 0;
+  q.packed_ksteps = packed ? (int32_t)packed_ksteps(p->h_in) : 0;
   q.plane_stride = (int64_t)p->n_rows * p->h_out;
   q.seg_indptr = lora ? seg_indptr : nullptr;
   q.lora_idx = lora ? lora_idx : nullptr;
@@ -762,6 +775,39 @@ sgmv_status_t sgmv_base_lora_apply(const sgmv_problem_t* p, const void* X, const
   q.partials = reinterpret_cast<float*>(w + b.p_off);
   q.Y = static_cast<uint16_t*>(Y);
   return hip_status(sgmv::launch_base(p->dtype, p->rank, q, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+sgmv_status_t sgmv_base_lora_apply(const sgmv_problem_t* p, const void* X, const void* W,
+                                   const void* const* A_ptrs, const void* const* B_ptrs, void* Y,
+                                   const int32_t* seg_indptr, const int32_t* lora_idx, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  return base_apply(p, X, W, false, A_ptrs, B_ptrs, Y, seg_indptr, lora_idx, ws, ws_bytes, stream);
+}
+
+sgmv_status_t sgmv_base_packed_weight_bytes(int32_t h_in, int32_t h_out, size_t* bytes) {
+  if (!bytes || h_in <= 0 || h_out <= 0) return SGMV_ERR_INVALID_ARG;
+  *bytes = (size_t)packed_bytes(h_in, h_out);
+  return SGMV_OK;
+}
+
+sgmv_status_t sgmv_base_pack_weight(const void* W, int32_t h_in, int32_t h_out, void* Wp, size_t wp_bytes,
+                                    void* stream) {
+  if (!W || !Wp || h_in <= 0 || h_out <= 0) return SGMV_ERR_INVALID_ARG;
+  if (wp_bytes < (size_t)packed_bytes(h_in, h_out)) return SGMV_ERR_WORKSPACE;
+  if (!aligned2(W) || !aligned16(Wp)) return SGMV_ERR_UNSUPPORTED;
+  return hip_status(sgmv::launch_base_pack(static_cast<const uint16_t*>(W), h_in, h_out,
+                                           static_cast<uint16_t*>(Wp), static_cast<hipStream_t>(stream)));
+}
+
+sgmv_status_t sgmv_base_lora_apply_packed(const sgmv_problem_t* p, const void* X, const void* Wp,
+                                          const void* const* A_ptrs, const void* const* B_ptrs, void* Y,
+                                          const int32_t* seg_indptr, const int32_t* lora_idx, void* ws,
+                                          size_t ws_bytes, void* stream) {
+  return base_apply(p, X, Wp, true, A_ptrs, B_ptrs, Y, seg_indptr, lora_idx, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

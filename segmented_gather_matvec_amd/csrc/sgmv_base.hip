@@ -255,6 +255,139 @@ __global__ __launch_bounds__(kThreads) void sgmv_base_partial_kernel(BaseParams 
       }
 }
 
+// ---------------------------------------------------------------- packed W
+// The packed layout of W [h_in, h_out] holds, for 16-column block nb and
+// 32-row k-step ks, one 1 KiB block at element (nb * kst + ks) * 512, with
+// kst = ceil(h_in / 128) * 4 k-steps per column block.  Inside the block, the
+// 8 elements at lane L = 16 q + m are W[32 ks + 8 q + e][16 nb + m], e = 0..7:
+// the B operand of one 16x16x32 MFMA, so a wave reads it with one fully
+// coalesced 128-bit load per lane.  Column blocks run to an even count;
+// entries past the matrix are zero.
+__global__ __launch_bounds__(64) void sgmv_base_pack_kernel(const uint16_t* __restrict__ W, int h_in,
+                                                            int h_out, int kst, uint16_t* __restrict__ Wp) {
+  const int ks = blockIdx.x, nb = blockIdx.y, lane = threadIdx.x;
+  const int q = lane >> 4, m = lane & 15;
+  const int c = nb * 16 + m;
+  uint16_t v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int k = ks * 32 + q * 8 + e;
+    v[e] = c < h_out && k < h_in ? W[(int64_t)k * h_out + c] : (uint16_t)0;
+  }
+  u32x4 o;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) o[w] = (uint32_t)v[2 * w] | ((uint32_t)v[2 * w + 1] << 16);
+  store_vec(Wp + ((int64_t)nb * kst + ks) * 512 + lane * 8, o);
+}
+
+// Workgroup (g, s) as in sgmv_base_partial_kernel, from the packed W: wave w
+// owns column blocks 8 s + 2 w and 8 s + 2 w + 1 over K chunk g and feeds the
+// matrix cores straight from its loads (W from HBM, X from L2): no LDS and no
+// barrier.  A ring of S register sets of D k-steps each: S - 1 sets are in
+// flight while one is multiplied.
+template <class T, int R, int NRT>
+__global__ __launch_bounds__(kThreads) void sgmv_base_packed_kernel(BaseParams p) {
+  constexpr int D = 4;                 // k-steps per register set (kst and the chunk are multiples of 4)
+  constexpr int S = 2;                 // register sets (three measured slower)
+  __shared__ float lds_s[kWaves * 64];
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int q = lane >> 4;
+  const int ml = lane & 15;
+  const int kst = p.packed_ksteps;
+  const bool bad = ((p.n_rows - 1) | p.h_in | p.h_out | (p.kc - 1) | (p.strips - 1) | (p.ksplit - 1) |
+                    (kst - 1) | (NRT * 16 - p.n_rows) | (int32_t)(p.plane_stride >> 32)) < 0;
+  const bool bad_ptr = (p.X == nullptr) | (p.W == nullptr) | (p.partials == nullptr);
+  if (bad | bad_ptr) return;
+  if ((int)blockIdx.x < p.shrink_grid) {
+    if (p.vpartials != nullptr) shrink_role<T, R>(p, (int)blockIdx.x, lds_s);
+    return;
+  }
+  const int b = (int)blockIdx.x - p.shrink_grid;
+  const int per_xcd = p.base_grid / kXcds;
+  const int idx = (b % kXcds) * per_xcd + b / kXcds;
+  if (idx >= p.strips * p.ksplit) return;
+  const int g = idx / p.strips;
+  const int nb0 = __builtin_amdgcn_readfirstlane((idx - g * p.strips) * 8 + wave * 2);
+  if (nb0 * 16 >= p.h_out) return;  // the whole wave: nothing below waits for other waves
+  const int ks0 = g * (p.kc / 32);
+  const int ks1 = kst < ks0 + p.kc / 32 ? kst : ks0 + p.kc / 32;
+  const int n = p.n_rows;
+  // Uniform bases and 32-bit per-lane offsets.
+  const uint16_t* Wb = p.W + (int64_t)nb0 * kst * 512;
+  const uint32_t wlane = (uint32_t)lane * 8, wnext = (uint32_t)kst * 512;
+  const uint16_t* X = p.X;
+  uint32_t xoff[NRT];
+  bool xrow[NRT];
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt) {
+    const int r = rt * 16 + ml;
+    xrow[rt] = r < n;
+    xoff[rt] = (uint32_t)((r < n ? r : 0) * p.h_in + q * 8);
+  }
+
+  auto issue = [&](int ks, u32x4 (&w)[D][2], u32x4 (&x)[D][NRT]) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const uint32_t o = (uint32_t)(ks + d) * 512 + wlane;
+      w[d][0] = load_stream(Wb + o);
+      w[d][1] = load_stream(Wb + o + wnext);
+    }
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt) {
+        const int k = (ks + d) * 32 + q * 8;
+        const bool ok = xrow[rt] && k < p.h_in;
+        x[d][rt] = load_vec(X + (ok ? xoff[rt] + (uint32_t)(ks + d) * 32 : 0u));
+        if (!ok) x[d][rt] = u32x4{0u, 0u, 0u, 0u};
+      }
+  };
+
+  f32x4 acc[NRT][2];
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[rt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto mma = [&](const u32x4 (&w)[D][2], const u32x4 (&x)[D][NRT]) {
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[rt][j] = mfma<T>(x[d][rt], w[d][j], acc[rt][j]);
+  };
+
+  u32x4 w[S][D][2], x[S][D][NRT];
+#pragma unroll
+  for (int i = 0; i < S - 1; ++i)
+    if (ks0 + i * D < ks1) issue(ks0 + i * D, w[i], x[i]);
+  for (int ks = ks0; ks < ks1; ks += S * D) {
+#pragma unroll
+    for (int i = 0; i < S; ++i) {
+      // Set (i + S - 1) % S was multiplied in the previous turn: refill it
+      // with the step S - 1 sets ahead, then multiply set i.
+      const int cur = ks + i * D, nxt = cur + (S - 1) * D;
+      if (nxt < ks1) issue(nxt, w[(i + S - 1) % S], x[(i + S - 1) % S]);
+      if (cur < ks1) mma(w[i], x[i]);
+    }
+  }
+
+  // D[4q+i][ml] of tile (rt, j): row rt*16 + 4q + i, column 16 (nb0 + j) + ml.
+  float* dst = p.partials + (int64_t)g * p.plane_stride;
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = rt * 16 + q * 4 + i;
+        const int c = (nb0 + j) * 16 + ml;
+        if (r < n && c < p.h_out) dst[(int64_t)r * p.h_out + c] = acc[rt][j][i];
+      }
+}
+
 // ---------------------------------------------------------------- epilogue
 // One wave per (row i, 512 columns): lane l owns columns c .. c+7,
 // c = 512 * blockIdx.x + 8 * l.  Y[i, c..] = sum of the partial planes (plane
@@ -383,12 +516,28 @@ hipError_t launch_partial(const BaseParams& p, hipStream_t s) {
 }
 
 template <class T, int R>
+hipError_t launch_packed(const BaseParams& p, hipStream_t s) {
+  const dim3 grid((unsigned)p.shrink_grid + (unsigned)p.base_grid);
+  if (p.n_rows <= 16)
+    hipLaunchKernelGGL((sgmv_base_packed_kernel<T, R, 1>), grid, dim3(kThreads), 0, s, p);
+  else if (p.n_rows <= 32)
+    hipLaunchKernelGGL((sgmv_base_packed_kernel<T, R, 2>), grid, dim3(kThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL((sgmv_base_packed_kernel<T, R, 4>), grid, dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+template <class T, int R>
 hipError_t launch_r(const BaseParams& p, hipStream_t s) {
   hipError_t e = hipErrorInvalidValue;
-  switch (p.strip_cols) {
-    case 64: e = launch_partial<T, R, 64>(p, s); break;
-    case 128: e = launch_partial<T, R, 128>(p, s); break;
-    case 256: e = launch_partial<T, R, 256>(p, s); break;
+  if (p.packed_ksteps > 0) {
+    if (p.strip_cols == 128) e = launch_packed<T, R>(p, s);
+  } else {
+    switch (p.strip_cols) {
+      case 64: e = launch_partial<T, R, 64>(p, s); break;
+      case 128: e = launch_partial<T, R, 128>(p, s); break;
+      case 256: e = launch_partial<T, R, 256>(p, s); break;
+    }
   }
   if (e != hipSuccess) return e;
   const dim3 egrid((unsigned)((p.h_out + 511) / 512), (unsigned)p.n_rows);
@@ -408,6 +557,15 @@ hipError_t launch_t(int rank, const BaseParams& p, hipStream_t s) {
 }
 
 }  // namespace
+
+hipError_t launch_base_pack(const uint16_t* W, int h_in, int h_out, uint16_t* Wp, hipStream_t stream) {
+  if (h_in <= 0 || h_out <= 0) return hipErrorInvalidValue;
+  const int kst = (h_in + 127) / 128 * 4;
+  const int nbp = ((h_out + 15) / 16 + 1) / 2 * 2;
+  hipLaunchKernelGGL(sgmv_base_pack_kernel, dim3((unsigned)kst, (unsigned)nbp), dim3(64), 0, stream, W, h_in,
+                     h_out, kst, Wp);
+  return hipGetLastError();
+}
 
 hipError_t launch_base(int dtype, int rank, const BaseParams& p, hipStream_t stream) {
   if (p.n_rows <= 0 || p.strips <= 0) return hipSuccess;

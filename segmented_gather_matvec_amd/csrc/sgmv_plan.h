@@ -141,12 +141,12 @@ struct BaseParams {
   int32_t ksplit, kc;      // K split: plane g covers rows [g*kc, (g+1)*kc) of W and A_k
   int32_t base_grid;       // workgroups of the base product (a multiple of 8)
   int32_t shrink_grid;     // LoRA shrink workgroups before them (n_rows * ksplit, rounded up to 8; 0: none)
-  int32_t pad_;
+  int32_t packed_ksteps;   // 0: W row-major; else W in the packed layout with this many 32-row k-steps
   int64_t plane_stride;    // floats between partial planes of Y (n_rows * h_out)
   const int32_t* seg_indptr;
   const int32_t* lora_idx;
   const uint16_t* X;       // [n_rows, h_in]
-  const uint16_t* W;       // [h_in, h_out]
+  const uint16_t* W;       // [h_in, h_out] row-major, or packed (packed_ksteps > 0)
   const uint64_t* A_ptrs;  // [num_loras] -> A_k [h_in, rank]
   const uint64_t* B_ptrs;  // [num_loras] -> B_k [rank, h_out]
   float* vpartials;        // [ksplit][n_rows][rank] (null: no LoRA term)
@@ -157,5 +157,7 @@ struct BaseParams {
 
 // Partials then epilogue (two launches).
 hipError_t launch_base(int dtype, int rank, const BaseParams& p, hipStream_t stream);
+// W [h_in, h_out] row-major -> the packed layout (one launch).
+hipError_t launch_base_pack(const uint16_t* W, int h_in, int h_out, uint16_t* Wp, hipStream_t stream);
 
 }  // namespace sgmv

@@ -303,6 +303,39 @@ def test_base_apply_fails_fast_on_bad_arguments():
     assert call(none, None, None, None, None, 0) == sg.SGMV_OK
 
 
+def test_packed_base_entry_points_fail_fast():
+    """sgmv_base_pack_weight / sgmv_base_lora_apply_packed: host checks before any HIP call."""
+    lib = sg.load_library()
+    fake = ctypes.c_void_p(0x10000)
+    odd = ctypes.c_void_p(0x10001)
+    need = sg.sgmv_base_packed_weight_bytes(520, 264)
+    pack = lambda W, h_in, h_out, Wp, nbytes: lib.sgmv_base_pack_weight(W, h_in, h_out, Wp, nbytes, None)
+    assert pack(None, 520, 264, fake, need) == sg.SGMV_ERR_INVALID_ARG
+    assert pack(fake, 520, 264, None, need) == sg.SGMV_ERR_INVALID_ARG
+    assert pack(fake, 0, 264, fake, need) == sg.SGMV_ERR_INVALID_ARG
+    assert pack(fake, 520, -8, fake, need) == sg.SGMV_ERR_INVALID_ARG
+    assert pack(fake, 520, 264, fake, need - 1) == sg.SGMV_ERR_WORKSPACE
+    assert pack(odd, 520, 264, fake, need) == sg.SGMV_ERR_UNSUPPORTED
+    assert pack(fake, 520, 264, ctypes.c_void_p(0x10008), need) == sg.SGMV_ERR_UNSUPPORTED
+    out = ctypes.c_size_t(0)
+    assert lib.sgmv_base_packed_weight_bytes(0, 8, ctypes.byref(out)) == sg.SGMV_ERR_INVALID_ARG
+    p = good()
+    ws = sg.sgmv_base_workspace_bytes(p)
+    call = lambda prob, X, Wp, Y, nbytes: lib.sgmv_base_lora_apply_packed(
+        ctypes.byref(prob), X, Wp, fake, fake, Y, fake, fake, fake, nbytes, None)
+    assert call(p, fake, None, fake, ws) == sg.SGMV_ERR_INVALID_ARG
+    assert call(p, fake, ctypes.c_void_p(0x10008), fake, ws) == sg.SGMV_ERR_UNSUPPORTED
+    assert call(p, fake, fake, fake, ws - 1) == sg.SGMV_ERR_WORKSPACE
+    assert call(good(n_rows=65, num_segs=65), fake, fake, fake, ws) == sg.SGMV_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("h_in,h_out,blocks,ksteps", [(4096, 4096, 256, 128), (520, 264, 18, 20),
+                                                      (8, 8, 2, 4), (11008, 4096, 256, 344)])
+def test_packed_weight_size(h_in, h_out, blocks, ksteps):
+    """1 KiB per (16-column block, 32-row k-step); blocks to an even count, k-steps to a multiple of 4."""
+    assert sg.sgmv_base_packed_weight_bytes(h_in, h_out) == blocks * ksteps * 1024
+
+
 @pytest.mark.parametrize("kw", [{}, {"h_out": 11008}, {"h_in": 13824, "h_out": 5120, "rank": 64},
                                 {"n_rows": 1, "num_segs": 1}, {"n_rows": 64, "num_segs": 64}])
 def test_base_workspace_covers_its_parts(kw):

@@ -17,7 +17,19 @@ from tests.gpu_cases import assert_close, i32, to_bits, to_device
 pytestmark = pytest.mark.gpu
 
 
-def run_base(dtype, X, W, A, B, seg, lidx, Y_fill=None):
+def packed_layout(W):
+    """The packed layout, built with numpy from its definition: block (nb, ks) holds
+    W[32 ks + 8 q + e][16 nb + m] at element 8 (16 q + m) + e; zero past the matrix."""
+    h_in, h_out = W.shape
+    kst = -(-h_in // 128) * 4
+    nbp = -(-(-(-h_out // 16)) // 2) * 2
+    Wpad = np.zeros((kst * 32, nbp * 16), np.uint16)
+    Wpad[:h_in, :h_out] = W
+    t = Wpad.reshape(kst, 4, 8, nbp, 16)           # [ks][q][e][nb][m]
+    return t.transpose(3, 0, 1, 4, 2).reshape(-1)  # [nb][ks][q][m][e]
+
+
+def run_base(dtype, X, W, A, B, seg, lidx, Y_fill=None, packed=False):
     import torch
     n, h_in = X.shape
     P, _, rank = A.shape
@@ -29,8 +41,12 @@ def run_base(dtype, X, W, A, B, seg, lidx, Y_fill=None):
     Xd, Wd, Ad, Bd = (to_device(a, dtype) for a in (X, W, A, B))
     Y = torch.full((n, h_out), float("nan") if Y_fill is None else Y_fill, dtype=Xd.dtype, device="cuda")
     ws = torch.full((sg.sgmv_base_workspace_bytes(prob),), 0xA5, dtype=torch.uint8, device="cuda")  # any contents
-    sg.sgmv_base_lora_apply(prob, Xd, Wd, sg.pointer_table(Ad), sg.pointer_table(Bd), Y,
-                            i32(seg if seg.size else [0]), i32(lidx if lidx.size else [0]), ws)
+    fn = sg.sgmv_base_lora_apply
+    if packed:
+        Wd = sg.pack_base_weight(Wd)
+        fn = sg.sgmv_base_lora_apply_packed
+    fn(prob, Xd, Wd, sg.pointer_table(Ad), sg.pointer_table(Bd), Y,
+       i32(seg if seg.size else [0]), i32(lidx if lidx.size else [0]), ws)
     torch.cuda.synchronize()
     return to_bits(Y), prob, (Xd, Wd, Ad, Bd, Y, ws, seg, lidx)
 
@@ -76,6 +92,32 @@ def test_base_apply_matches_oracle(name):
     assert_close(got, ref, dtype, what=name)
 
 
+@pytest.mark.parametrize("shape", [(520, 264), (1024, 1376), (4096, 4096), (8, 24)])
+def test_packed_weight_layout_bit_exact(shape):
+    """sgmv_base_pack_weight writes exactly the documented layout (bit for bit)."""
+    import torch
+    rng = np.random.default_rng(sum(shape))
+    W = workloads.base_weight(rng, shape[0], shape[1], "bf16")
+    Wd = to_device(W, "bf16")
+    Wp = torch.full((sg.sgmv_base_packed_weight_bytes(*shape) // 2,), 12345, dtype=torch.int16,
+                    device="cuda").view(torch.bfloat16)  # every element must be written
+    sg.sgmv_base_pack_weight(Wd, Wp)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_bits(Wp), packed_layout(W))
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_packed_base_apply_matches_oracle_and_row_major_call(name):
+    """The packed entry point meets the oracle bound and equals the row-major call bit for bit
+    (the same MFMA operands in the same order)."""
+    seed, dtype, n, h_in, h_out, rank, P, layout = CASES[name]
+    X, W, A, B, seg, lidx = make_case(seed, dtype, n, h_in, h_out, rank, P, layout)
+    got, _, _ = run_base(dtype, X, W, A, B, seg, lidx, packed=True)
+    assert_close(got, oracle.sgmv_base_apply(dtype, X, W, A, B, seg, lidx), dtype, what=name)
+    row_major, _, _ = run_base(dtype, X, W, A, B, seg, lidx)
+    assert np.array_equal(got, row_major)
+
+
 def test_base_apply_integer_inputs_bit_exact():
     """X, W, B in {-1, 0, 1}, A with 8 entries of +-1 per column: every partial sum is
     an integer far inside fp32's exact range and the result is exact in fp16, so
@@ -89,9 +131,10 @@ def test_base_apply_integer_inputs_bit_exact():
         Wf[rows, c] = rng.choice([-1.0, 1.0], size=12)
     W = workloads.to_bits(Wf, "f16")
     seg, lidx = [0, 5, 6, 14, 20], [4, 0, 4, 2]   # rows 20.. uncovered
-    got, _, _ = run_base("f16", X, W, A, B, seg, lidx)
     ref = oracle.sgmv_base_apply("f16", X, W, A, B, seg, lidx)
-    assert np.array_equal(oracle.decode(got, "f16"), ref)
+    for packed in (False, True):
+        got, _, _ = run_base("f16", X, W, A, B, seg, lidx, packed=packed)
+        assert np.array_equal(oracle.decode(got, "f16"), ref), packed
 
 
 def test_base_apply_repeated_calls_and_shared_workspace():
