@@ -287,8 +287,11 @@ sgmv_status_t sgmv_base_lora_apply(const sgmv_problem_t* problem, const void* X,
  * not change while a server runs, so it can be rearranged once into the
  * operand order of the matrix cores; sgmv_base_lora_apply_packed then streams
  * it with fully coalesced loads straight into the MFMA operands (no LDS
- * staging).  It computes exactly what sgmv_base_lora_apply computes (the same
- * sums in the same order, so the two outputs are bitwise equal).
+ * staging of W; over 32 rows, X is staged once per workgroup).  It computes
+ * what sgmv_base_lora_apply computes, to the same bound.  The outputs are
+ * bitwise equal whenever both calls split K alike.  That holds unless the call
+ * has over 32 rows and the row-major call's K chunk exceeds 512 rows of W.
+ * The packed call then takes a shorter chunk and more partial planes.
  *
  * Packed layout (16-bit elements, either format): kst = ceil(h_in / 128) * 4
  * k-steps of 32 rows; ceil(h_out / 16) rounded up to an even count of

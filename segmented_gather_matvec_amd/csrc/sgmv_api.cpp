@@ -473,12 +473,17 @@ struct BasePlan {
   size_t b_off = 0, v_off = 0, p_off = 0, total = 0;  // workspace layout
 };
 
-BasePlan plan_base(const sgmv_problem_t& p) {
+BasePlan plan_base(const sgmv_problem_t& p, bool packed) {
   BasePlan b;
   b.strips = (int)ceil_div(p.h_out, b.strip_cols);
   const int64_t max_split = ceil_div(p.h_in, sgmv::kBaseStageRows);
   const int64_t ks = std::max<int64_t>(1, std::min<int64_t>(ceil_div(kBaseTarget, b.strips), max_split));
   b.kc = (int)round_up(ceil_div(p.h_in, ks), sgmv::kBaseStageRows);
+  if (packed && p.n_rows > 32) {
+    // The packed-W kernel stages the X chunk of its four row tiles (64 x kc) in LDS.
+    const int64_t cap = sgmv::kBasePackedXElems / 64 / sgmv::kBaseStageRows * sgmv::kBaseStageRows;
+    b.kc = (int)std::min<int64_t>(b.kc, cap);
+  }
   b.ksplit = (int)ceil_div(p.h_in, b.kc);
   b.base_grid = (int)round_up((int64_t)b.strips * b.ksplit, 8);
   // [B_k of each row][partial planes of V][partial planes of Y]
@@ -717,7 +722,7 @@ sgmv_status_t sgmv_base_workspace_bytes(const sgmv_problem_t* p, size_t* bytes) 
   const sgmv_status_t st = sgmv_check_problem(p);
   if (st != SGMV_OK) return st;
   if (p->n_rows > sgmv::kBaseMaxRows) return SGMV_ERR_UNSUPPORTED;
-  *bytes = plan_base(*p).total;
+  *bytes = std::max(plan_base(*p, false).total, plan_base(*p, true).total);
   return SGMV_OK;
 }
 
@@ -745,7 +750,7 @@ sgmv_status_t base_apply(const sgmv_problem_t* p, const void* X, const void* W, 
   if (lora && (!A_ptrs || !B_ptrs || !seg_indptr || !lora_idx)) return SGMV_ERR_INVALID_ARG;
   if (!aligned16(X) || !aligned16(W) || !aligned16(Y)) return SGMV_ERR_UNSUPPORTED;
   if (lora && (!aligned8(A_ptrs) || !aligned8(B_ptrs))) return SGMV_ERR_UNSUPPORTED;
-  const BasePlan b = plan_base(*p);
+  const BasePlan b = plan_base(*p, packed);
   if (!ws || ws_bytes < b.total) return SGMV_ERR_WORKSPACE;
   if (!aligned16(ws)) return SGMV_ERR_UNSUPPORTED;
   char* w = static_cast<char*>(ws);

@@ -282,14 +282,22 @@ __global__ __launch_bounds__(64) void sgmv_base_pack_kernel(const uint16_t* __re
 
 // Workgroup (g, s) as in sgmv_base_partial_kernel, from the packed W: wave w
 // owns column blocks 8 s + 2 w and 8 s + 2 w + 1 over K chunk g and feeds the
-// matrix cores straight from its loads (W from HBM, X from L2): no LDS and no
-// barrier.  A ring of S register sets of D k-steps each: S - 1 sets are in
-// flight while one is multiplied.
+// matrix cores straight from its W loads.  A ring of S register sets of D
+// k-steps: S - 1 sets are in flight while one is multiplied.  X operands:
+//  - up to two row tiles: each wave loads them from L2 with its W (no LDS,
+//    no barrier);
+//  - four row tiles (XL): the workgroup's X chunk ([64 rows][kc], at most
+//    64 KiB) is staged in LDS once, behind one barrier, its 16-byte groups at
+//    group ^ (row & 7) within a row so that the 16 rows of one operand read
+//    fall on different banks.  Four operand loads per k-step from L2 would
+//    outnumber the two of W.
 template <class T, int R, int NRT>
 __global__ __launch_bounds__(kThreads) void sgmv_base_packed_kernel(BaseParams p) {
-  constexpr int D = 4;                 // k-steps per register set (kst and the chunk are multiples of 4)
-  constexpr int S = 2;                 // register sets (three measured slower)
-  __shared__ float lds_s[kWaves * 64];
+  constexpr int D = 4;  // k-steps per register set (kst and the chunk are multiples of 4)
+  constexpr int S = 2;  // register sets (three measured slower)
+  constexpr bool XL = NRT > 2;
+  constexpr int NX = XL ? 0 : NRT;  // X operands per k-step held in the ring
+  __shared__ __attribute__((aligned(16))) uint16_t lds_x[XL ? kBasePackedXElems : kWaves * 128];
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = t >> 6;
@@ -297,27 +305,28 @@ __global__ __launch_bounds__(kThreads) void sgmv_base_packed_kernel(BaseParams p
   const int ml = lane & 15;
   const int kst = p.packed_ksteps;
   const bool bad = ((p.n_rows - 1) | p.h_in | p.h_out | (p.kc - 1) | (p.strips - 1) | (p.ksplit - 1) |
-                    (kst - 1) | (NRT * 16 - p.n_rows) | (int32_t)(p.plane_stride >> 32)) < 0;
+                    (kst - 1) | (NRT * 16 - p.n_rows) | (XL ? kBasePackedXElems - NRT * 16 * p.kc : 0) |
+                    (int32_t)(p.plane_stride >> 32)) < 0;
   const bool bad_ptr = (p.X == nullptr) | (p.W == nullptr) | (p.partials == nullptr);
   if (bad | bad_ptr) return;
   if ((int)blockIdx.x < p.shrink_grid) {
-    if (p.vpartials != nullptr) shrink_role<T, R>(p, (int)blockIdx.x, lds_s);
+    if (p.vpartials != nullptr) shrink_role<T, R>(p, (int)blockIdx.x, reinterpret_cast<float*>(lds_x));
     return;
   }
   const int b = (int)blockIdx.x - p.shrink_grid;
   const int per_xcd = p.base_grid / kXcds;
   const int idx = (b % kXcds) * per_xcd + b / kXcds;
-  if (idx >= p.strips * p.ksplit) return;
+  if (idx >= p.strips * p.ksplit) return;  // the whole workgroup
   const int g = idx / p.strips;
   const int nb0 = __builtin_amdgcn_readfirstlane((idx - g * p.strips) * 8 + wave * 2);
-  if (nb0 * 16 >= p.h_out) return;  // the whole wave: nothing below waits for other waves
+  const bool active = nb0 * 16 < p.h_out;  // whole waves; inactive ones still stage X
   const int ks0 = g * (p.kc / 32);
   const int ks1 = kst < ks0 + p.kc / 32 ? kst : ks0 + p.kc / 32;
+  const int nk = (ks1 - ks0) * 32;  // k of this chunk (a multiple of 128)
   const int n = p.n_rows;
-  // Uniform bases and 32-bit per-lane offsets.
   const uint16_t* Wb = p.W + (int64_t)nb0 * kst * 512;
   const uint32_t wlane = (uint32_t)lane * 8, wnext = (uint32_t)kst * 512;
-  const uint16_t* X = p.X;
+
   uint32_t xoff[NRT];
   bool xrow[NRT];
 #pragma unroll
@@ -326,8 +335,7 @@ __global__ __launch_bounds__(kThreads) void sgmv_base_packed_kernel(BaseParams p
     xrow[rt] = r < n;
     xoff[rt] = (uint32_t)((r < n ? r : 0) * p.h_in + q * 8);
   }
-
-  auto issue = [&](int ks, u32x4 (&w)[D][2], u32x4 (&x)[D][NRT]) {
+  auto issue = [&](int ks, u32x4 (&w)[D][2], u32x4 (&x)[D][NX > 0 ? NX : 1]) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       const uint32_t o = (uint32_t)(ks + d) * 512 + wlane;
@@ -337,32 +345,69 @@ __global__ __launch_bounds__(kThreads) void sgmv_base_packed_kernel(BaseParams p
 #pragma unroll
     for (int d = 0; d < D; ++d)
 #pragma unroll
-      for (int rt = 0; rt < NRT; ++rt) {
-        const int k = (ks + d) * 32 + q * 8;
-        const bool ok = xrow[rt] && k < p.h_in;
-        x[d][rt] = load_vec(X + (ok ? xoff[rt] + (uint32_t)(ks + d) * 32 : 0u));
+      for (int rt = 0; rt < NX; ++rt) {
+        const bool ok = xrow[rt] && (ks + d) * 32 + q * 8 < p.h_in;
+        x[d][rt] = load_vec(p.X + (ok ? xoff[rt] + (uint32_t)(ks + d) * 32 : 0u));
         if (!ok) x[d][rt] = u32x4{0u, 0u, 0u, 0u};
       }
   };
+  u32x4 w[S][D][2], x[S][D][NX > 0 ? NX : 1];
+  if (active) {
+#pragma unroll
+    for (int i = 0; i < S - 1; ++i)
+      if (ks0 + i * D < ks1) issue(ks0 + i * D, w[i], x[i]);
+  }
+
+  // Stage X[0 .. NRT*16)[k0 .. k0 + nk) (zero past n rows or h_in), 8 vectors
+  // of 16 bytes per thread per round.
+  if constexpr (XL) {
+    const int k0 = ks0 * 32;
+    const int gpr = nk / 8;  // 16-byte groups per row
+    const int total = NRT * 16 * gpr;
+    for (int v0 = 0; v0 < total; v0 += kThreads * 8) {
+      u32x4 xv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int v = v0 + u * kThreads + t;
+        const int r = v / gpr, gi = v - r * gpr;
+        const bool ok = v < total && r < n && k0 + gi * 8 < p.h_in;
+        xv[u] = load_vec(p.X + (ok ? (int64_t)r * p.h_in + k0 + gi * 8 : 0));
+        if (!ok) xv[u] = u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int v = v0 + u * kThreads + t;
+        const int r = v / gpr, gi = v - r * gpr;
+        if (v < total) store_vec(&lds_x[r * nk + ((gi ^ (r & 7)) << 3)], xv[u]);
+      }
+    }
+  }
+  if constexpr (XL) __syncthreads();
+  if (!active) return;  // no barrier follows
 
   f32x4 acc[NRT][2];
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[rt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto mma = [&](const u32x4 (&w)[D][2], const u32x4 (&x)[D][NRT]) {
+  auto mma = [&](int ks, const u32x4 (&wv)[D][2], const u32x4 (&xv)[D][NX > 0 ? NX : 1]) {
 #pragma unroll
-    for (int d = 0; d < D; ++d)
+    for (int d = 0; d < D; ++d) {
+      const int gi = (ks - ks0 + d) * 4 + q;  // 16-byte group of this lane's 8 k
 #pragma unroll
-      for (int rt = 0; rt < NRT; ++rt)
+      for (int rt = 0; rt < NRT; ++rt) {
+        const int r = rt * 16 + ml;
+        u32x4 af;
+        if constexpr (XL)
+          af = load_vec(&lds_x[r * nk + ((gi ^ (r & 7)) << 3)]);
+        else
+          af = xv[d][rt < NX ? rt : 0];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[rt][j] = mfma<T>(x[d][rt], w[d][j], acc[rt][j]);
+        for (int j = 0; j < 2; ++j) acc[rt][j] = mfma<T>(af, wv[d][j], acc[rt][j]);
+      }
+    }
   };
 
-  u32x4 w[S][D][2], x[S][D][NRT];
-#pragma unroll
-  for (int i = 0; i < S - 1; ++i)
-    if (ks0 + i * D < ks1) issue(ks0 + i * D, w[i], x[i]);
   for (int ks = ks0; ks < ks1; ks += S * D) {
 #pragma unroll
     for (int i = 0; i < S; ++i) {
@@ -370,7 +415,7 @@ __global__ __launch_bounds__(kThreads) void sgmv_base_packed_kernel(BaseParams p
       // with the step S - 1 sets ahead, then multiply set i.
       const int cur = ks + i * D, nxt = cur + (S - 1) * D;
       if (nxt < ks1) issue(nxt, w[(i + S - 1) % S], x[(i + S - 1) % S]);
-      if (cur < ks1) mma(w[i], x[i]);
+      if (cur < ks1) mma(cur, w[i], x[i]);
     }
   }
 

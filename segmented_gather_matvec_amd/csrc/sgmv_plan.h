@@ -133,6 +133,9 @@ hipError_t launch_mfma_expand(int dtype, int rank, const MfmaParams& p, int num_
 // adds V @ B_k and rounds once.
 constexpr int kBaseMaxRows = 64;
 constexpr int kBaseStageRows = 128;  // W rows per pipeline stage (kc is a multiple)
+// LDS of the packed-W partial kernel's X chunk (16-bit elements, 64 KiB):
+// rows (16 per row tile) x K chunk may not exceed it.
+constexpr int kBasePackedXElems = 32768;
 
 struct BaseParams {
   int32_t n_rows, h_in, h_out, num_segs, num_loras;

@@ -80,6 +80,9 @@ CASES = {
     "no_segments_bf16": (5, "bf16", 7, 384, 512, 32, 2, "none"),
     "one_row_r32": (6, "bf16", 1, 2048, 1024, 32, 3, "distinct"),
     "distinct_b64_f16_r8": (7, "f16", 64, 256, 2056, 8, 64, "distinct"),
+    # 40 rows (four row tiles) over many strips: the packed kernel's LDS cap on
+    # the X chunk (512 k) cuts the K chunk below the row-major call's 640
+    "capped_chunk_b40_bf16_r32": (9, "bf16", 40, 2560, 8200, 32, 6, "skewed"),
 }
 
 
@@ -108,14 +111,16 @@ def test_packed_weight_layout_bit_exact(shape):
 
 @pytest.mark.parametrize("name", sorted(CASES))
 def test_packed_base_apply_matches_oracle_and_row_major_call(name):
-    """The packed entry point meets the oracle bound and equals the row-major call bit for bit
-    (the same MFMA operands in the same order)."""
+    """The packed entry point meets the oracle bound.  Where both calls split K alike (every
+    case but the capped one, whose packed call takes 5 planes against 4) it also equals the
+    row-major call bit for bit: the same MFMA operands in the same order."""
     seed, dtype, n, h_in, h_out, rank, P, layout = CASES[name]
     X, W, A, B, seg, lidx = make_case(seed, dtype, n, h_in, h_out, rank, P, layout)
     got, _, _ = run_base(dtype, X, W, A, B, seg, lidx, packed=True)
     assert_close(got, oracle.sgmv_base_apply(dtype, X, W, A, B, seg, lidx), dtype, what=name)
     row_major, _, _ = run_base(dtype, X, W, A, B, seg, lidx)
-    assert np.array_equal(got, row_major)
+    if not name.startswith("capped"):
+        assert np.array_equal(got, row_major)
 
 
 def test_base_apply_integer_inputs_bit_exact():
