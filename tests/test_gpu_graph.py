@@ -66,10 +66,11 @@ def test_graph_replays_match_eager(name):
         assert np.array_equal(to_bits(side.Y), eager), f"{name}: eager call after replay {rep} differs"
 
 
-def test_base_projection_graph_replays_match_eager():
-    """sgmv_base_lora_apply (no counters, no tags: two launches over plain
-    workspace planes) captured and replayed, with eager calls sharing the
-    workspace in between."""
+@pytest.mark.parametrize("packed", [False, True])
+def test_base_projection_graph_replays_match_eager(packed):
+    """sgmv_base_lora_apply, or its packed-W twin (no counters, no tags: two
+    launches over plain workspace planes), captured and replayed, with eager
+    calls sharing the workspace in between."""
     import torch
     from tests.test_gpu_base import make_case
     from tests.gpu_cases import i32
@@ -78,11 +79,15 @@ def test_base_projection_graph_replays_match_eager():
     seg, lidx = np.asarray(seg, np.int32), np.asarray(lidx, np.int32)
     prob = sg.make_problem(dtype, 24, 640, 392, 32, 6, len(lidx), int(np.diff(seg).max()))
     Xd, Wd, Ad, Bd = (to_device(a, dtype) for a in (X, W, A, B))
+    apply = sg.sgmv_base_lora_apply
+    if packed:
+        Wd, apply = sg.pack_base_weight(Wd), sg.sgmv_base_lora_apply_packed
+        torch.cuda.synchronize()
     At, Bt = sg.pointer_table(Ad), sg.pointer_table(Bd)
     seg_d, lidx_d = i32(seg), i32(lidx)
     ws = sg.new_base_workspace(prob)
     Y = torch.zeros((24, 392), dtype=Xd.dtype, device="cuda")
-    sg.sgmv_base_lora_apply(prob, Xd, Wd, At, Bt, Y, seg_d, lidx_d, ws)
+    apply(prob, Xd, Wd, At, Bt, Y, seg_d, lidx_d, ws)
     torch.cuda.synchronize()
     eager = to_bits(Y).copy()
     stream = torch.cuda.Stream()
@@ -91,7 +96,7 @@ def test_base_projection_graph_replays_match_eager():
     with torch.cuda.stream(stream):
         with torch.cuda.graph(g, stream=stream):
             Y.zero_()
-            sg.sgmv_base_lora_apply(prob, Xd, Wd, At, Bt, Y, seg_d, lidx_d, ws, stream=stream)
+            apply(prob, Xd, Wd, At, Bt, Y, seg_d, lidx_d, ws, stream=stream)
     torch.cuda.synchronize()
     Y2 = torch.zeros_like(Y)
     for rep in range(4):
@@ -99,6 +104,6 @@ def test_base_projection_graph_replays_match_eager():
         torch.cuda.synchronize()
         assert np.array_equal(to_bits(Y), eager), f"replay {rep} differs from the eager call"
         Y2.zero_()
-        sg.sgmv_base_lora_apply(prob, Xd, Wd, At, Bt, Y2, seg_d, lidx_d, ws)
+        apply(prob, Xd, Wd, At, Bt, Y2, seg_d, lidx_d, ws)
         torch.cuda.synchronize()
         assert np.array_equal(to_bits(Y2), eager), f"eager call after replay {rep} differs"
