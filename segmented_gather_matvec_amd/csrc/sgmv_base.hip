@@ -439,7 +439,7 @@ __global__ __launch_bounds__(kThreads) void sgmv_base_packed_kernel(BaseParams p
 // order) + V[i] @ B_k (ranks in ascending order), rounded once.
 template <class T, int R>
 __global__ __launch_bounds__(64) void sgmv_base_epilogue_kernel(BaseParams p) {
-  constexpr int kBatch = 16;  // plane loads in flight per lane
+  constexpr int kBatch = 8;   // plane loads in flight per lane
   const int lane = threadIdx.x;
   const int i = blockIdx.y;
   const bool bad = (p.n_rows | p.h_out | p.num_segs | p.num_loras | (p.ksplit - 1) |
