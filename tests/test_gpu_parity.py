@@ -96,12 +96,14 @@ def test_popularity_auto_takes_one_launch_route(kind, n):
 
 
 @pytest.mark.parametrize("kind,n,splits,rows_per_unit", [
-    ("identical", 32, 64, 4), ("identical", 32, 256, 16), ("identical", 64, 128, 16),
+    ("identical", 32, 128, 4), ("identical", 32, 256, 16), ("identical", 64, 128, 16),
     ("skewed", 32, 64, None), ("uniform", 64, 32, None), ("skewed", 64, 48, None)])
 def test_popularity_larger_row_blocks(kind, n, splits, rows_per_unit):
     """Forcing more splits pushes the one-launch kernel to 4- and 16-row blocks
     (the plans that larger batches get), or off it when no plan fits on the
-    device at once; the result must not change."""
+    device at once; the result must not change.  (32 one-row units of 128
+    splits exceed the 2048 workgroups a 256-CU device can ever hold at once;
+    the 16-row cases also exceed what the 4-row kernel's occupancy holds.)"""
     call = run_workload(workloads.popularity(kind, n), sg.SGMV_VARIANT_FUSED, splits)
     info = sg.sgmv_query_plan(call.problem)
     if rows_per_unit is not None:
@@ -110,21 +112,21 @@ def test_popularity_larger_row_blocks(kind, n, splits, rows_per_unit):
     assert call.counters_clear()
 
 
-@pytest.mark.parametrize("case", ["distinct_b256", "distinct_b100_h1024_splits32", "skewed_b64_splits64",
-                                  "uniform_b32_splits64"])
+@pytest.mark.parametrize("case", ["distinct_b512", "distinct_b100_h1024_splits32", "skewed_b64_splits64",
+                                  "uniform_b32_splits128"])
 def test_decode_passes_when_units_exceed_the_device(case):
     """When the units of a decode-shaped batch do not all fit on the device at
     once, the decode kernel is launched in passes, each over the next units with
     the largest co-resident grid; the result must equal the oracle, and the plan
     must be that multi-pass one."""
-    if case == "distinct_b256":
-        call = run_workload(workloads.decode_distinct(n=256), sg.SGMV_VARIANT_AUTO)
+    if case == "distinct_b512":
+        call = run_workload(workloads.decode_distinct(n=512), sg.SGMV_VARIANT_AUTO)
     elif case == "distinct_b100_h1024_splits32":
         call = run_workload(workloads.decode_distinct(n=100, h=1024), sg.SGMV_VARIANT_FUSED, 32)
     elif case == "skewed_b64_splits64":
         call = run_workload(workloads.popularity("skewed", 64), sg.SGMV_VARIANT_FUSED, 64)
     else:
-        call = run_workload(workloads.popularity("uniform", 32), sg.SGMV_VARIANT_FUSED, 64)
+        call = run_workload(workloads.popularity("uniform", 32), sg.SGMV_VARIANT_FUSED, 128)
     info = sg.sgmv_query_plan(call.problem)
     assert info.route == sg.SGMV_ROUTE_DECODE, info.as_dict()
     assert info.launches > 1 and info.grid < info.units * info.splits, info.as_dict()
@@ -154,16 +156,18 @@ def _batched_case(w, variant, nproj, seed):
     return call, projs
 
 
-@pytest.mark.parametrize("case", ["distinct3", "distinct_b64_4", "skewed3", "mixed2_mfma", "distinct3_vector"])
+@pytest.mark.parametrize("case", ["distinct3", "distinct_b64_4", "distinct_b128_4", "skewed3", "mixed2_mfma",
+                                  "distinct3_vector"])
 def test_batched_projections_match_oracle_and_single_calls(case):
     """sgmv_lora_apply_batched: every projection equals the oracle, and equals
-    (bitwise) a separate sgmv_lora_apply of that projection.  Distinct b64 with
-    4 projections does not fit on the device at once and runs the per-projection
-    fallback."""
+    (bitwise) a separate sgmv_lora_apply of that projection.  Distinct b128 with
+    4 projections (4096 workgroups) exceeds what the device holds at once and
+    runs the per-projection fallback."""
     import torch
     w, variant, nproj = {
         "distinct3": (workloads.decode_distinct(), sg.SGMV_VARIANT_AUTO, 3),
         "distinct_b64_4": (workloads.decode_distinct(n=64), sg.SGMV_VARIANT_AUTO, 4),
+        "distinct_b128_4": (workloads.decode_distinct(n=128), sg.SGMV_VARIANT_AUTO, 4),
         "skewed3": (workloads.popularity("skewed", 32), sg.SGMV_VARIANT_AUTO, 3),
         "mixed2_mfma": (workloads.mixed(64, seed=464, pairs=((512, 1376),), lo=16, hi=100)[0],
                         sg.SGMV_VARIANT_MFMA, 2),
@@ -425,3 +429,67 @@ def test_back_to_back_calls_share_workspace():
             c.reset_y()
             assert_close(to_bits(c.apply()), c.oracle_apply(), "f16")
     assert bool((ws[: sg.SGMV_WS_COUNTER_BYTES] == 0).all().item())
+
+
+# ------------------------------------------------------------ 13B full-model shapes
+
+@pytest.mark.parametrize("row_layout", ["segment_order", "row_map"])
+def test_llama13b_layer_sampled(row_layout):
+    """One layer of the 13B full-model sweep at its real shapes: q, k, v (5120 -> 5120)
+    batched in one call, o alone, gate and up (5120 -> 13824) batched, down
+    (13824 -> 5120) alone; r = 64, bf16, 64 LoRAs per projection, 256 decode rows
+    with truncated Zipf(1.5) LoRA ids (a request keeps its LoRA in every projection),
+    segments from the library's builder (checked against the oracle's).  Weights
+    and activations are drawn on the device from seeded generators; every
+    projection is compared element by element with the fp64 oracle on the first
+    and last row of every segment plus 24 random rows.  In "row_map" the
+    activations stay in request order and the kernels gather / scatter rows
+    through the builder's perm."""
+    import torch
+    n, rank, P = 256, 64, 64
+    ids = workloads.full_model_ids(seed=5, n=n, pool=P)
+    perm, seg, lidx, mx = sg.sgmv_build_segments(ids, P)
+    operm, oseg, olidx, omx = oracle.build_segments(ids, P)
+    assert (perm.tolist(), seg.tolist(), lidx.tolist(), mx) == (operm, oseg, olidx, omx)
+    used = sorted(set(int(k) for k in lidx))
+    seg_d = torch.from_numpy(seg).cuda()
+    lidx_d = torch.from_numpy(lidx).cuda()
+    perm_d = torch.from_numpy(np.ascontiguousarray(perm)).cuda() if row_layout == "row_map" else None
+    # sorted row j holds request perm[j]: with a row map, X / Y rows stay in request order
+    order = perm if row_layout == "row_map" else np.arange(n)
+    rng = np.random.default_rng(13)
+    sample = set(int(r) for r in rng.choice(n, 24, replace=False))
+    for s in range(len(seg) - 1):
+        sample.update((int(seg[s]), int(seg[s + 1]) - 1))
+    mask = np.zeros(n, np.uint8)
+    mask[sorted(sample)] = 1
+    groups = (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))
+    shapes = {name: (h_in, h_out) for (name, h_in, h_out) in workloads.LLAMA13B_PROJ}
+    names = [name for (name, _, _) in workloads.LLAMA13B_PROJ]
+    layer = 7
+    for gi, grp in enumerate(groups):
+        h_in, h_out = shapes[grp[0]]
+        X = workloads.device_normal((n, h_in), 1.0, "bf16", 880000 + 4 * layer + gi)
+        projs, host = [], []
+        for name in grp:
+            seed = workloads.full_model_weight_seed(layer, names.index(name))
+            A = workloads.device_normal((P, h_in, rank), h_in ** -0.5, "bf16", seed * 2)
+            B = workloads.device_normal((P, rank, h_out), rank ** -0.5, "bf16", seed * 2 + 1)
+            Y = workloads.device_normal((n, h_out), 1.0, "bf16", 890000 + 7 * layer + names.index(name))
+            host.append((Y, to_bits(Y), [to_bits(A[k]) if k in used else np.zeros((1, 1), np.uint16)
+                                         for k in range(P)],
+                         [to_bits(B[k]) if k in used else np.zeros((1, 1), np.uint16) for k in range(P)]))
+            projs.append((sg.pointer_table(A), sg.pointer_table(B), Y, A, B))
+        prob = sg.make_problem("bf16", n, h_in, h_out, rank, P, len(lidx), mx)
+        assert sg.sgmv_query_plan(prob).route == sg.SGMV_ROUTE_MFMA
+        ws = torch.zeros(sg.batched_workspace_bytes(prob, len(grp)), dtype=torch.uint8, device="cuda")
+        Xh = to_bits(X)
+        sg.sgmv_lora_apply_batched(prob, X, [(a, b, y) for (a, b, y, _, _) in projs], seg_d, lidx_d, ws,
+                                   row_idx=perm_d)
+        torch.cuda.synchronize()
+        for name, (Y, Y0h, Ah, Bh) in zip(grp, host):
+            # the oracle works on sorted rows: sorted row j is activation row order[j]
+            ref = oracle.sgmv_apply("bf16", Xh[order], Ah, Bh, seg, lidx, Y0h[order], row_mask=mask)
+            got = to_bits(Y)[order]
+            assert_close(got, ref, "bf16", rows=mask.astype(bool), what=f"{row_layout} {name}")
+            assert np.isfinite(oracle.decode(to_bits(Y), "bf16")).all()
