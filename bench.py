@@ -17,15 +17,19 @@ prefill+decode batch on Llama-7B MLP shapes (r = 16 or 64, bf16), and one
 forward of all 280 LoRA calls of a 13B model (r = 64, bf16, batch 256, Zipf
 LoRA assignment), where one step is the whole forward.
 
-Prints one JSON line: value = whole-job algorithmic GB/s over the timed steps
-(K back-to-back steps, wall time between two device synchronisations);
-roofline.achieved = algorithmic bytes per launch / mean launch duration from
-HIP events recorded on the launch stream around the same timed region;
-roofline.traffic = HBM bytes per launch from the committed counter runs
-(FETCH_SIZE + WRITE_SIZE scaled by a copy kernel of known size), reported only
-while the kernel sources still match the ones the counters were taken on;
-cpu_baseline = the fp64 oracle timed on the host cores on a bounded sample of
-the same workload (default workload only).
+Prints one JSON line.  The timed region is K back-to-back steps on one stream,
+with HIP events recorded on that stream at both ends and a device
+synchronisation before and after.  value = whole-job algorithmic GB/s over the
+device time between the two events (ms_per_step and tokens_per_s come from the
+same device time); the host wall clock around the region, which adds the fixed
+cost of the synchronisations and of the first launch, is reported beside it
+(wall_ms_per_step, wall_value).  roofline.achieved = algorithmic bytes per
+launch / mean launch duration from the same events; roofline.traffic = HBM
+bytes per launch from the committed counter runs (FETCH_SIZE + WRITE_SIZE
+scaled by a copy kernel of known size; roofline_traffic_from names the file),
+reported only while the kernel sources still match the ones the counters were
+taken on; cpu_baseline = the fp64 oracle timed on the host cores on a bounded
+sample of the same workload (default workload only).
 """
 from __future__ import annotations
 
@@ -100,7 +104,9 @@ def workload_layout(name):
     import workloads as wl
     parts = name.split("_")
     if name.startswith("decode_distinct"):
-        # decode_distinct_h{H}_r{r}_b{n}
+        # decode_distinct[_qkv]_h{H}_r{r}_b{n}
+        if parts[2] == "qkv":
+            parts = parts[:2] + parts[3:]
         h, r, n = int(parts[2][1:]), int(parts[3][1:]), int(parts[4][1:])
         return "f16", h, h, r, n, np.arange(n + 1, dtype=np.int32), np.arange(n, dtype=np.int32), n, 2
     if parts[0] in ("identical", "uniform", "skewed"):
@@ -124,6 +130,7 @@ SINGLE_WORKLOADS = (["decode_distinct_h4096_r16_b32", "decode_distinct_h4096_r16
                     + [f"decode_distinct_h4096_r16_b{n}" for n in (1, 8, 16, 128, 256, 512)]
                     + ["decode_distinct_h4096_r32_b32", "decode_distinct_h4096_r64_b8",
                        "decode_distinct_h4096_r64_b32", "decode_distinct_h11008_r16_b32"]
+                    + ["decode_distinct_qkv_h4096_r16_b32", "decode_distinct_qkv_h4096_r16_b64"]
                     + [f"{k}_b{n}" for k in ("identical", "uniform", "skewed") for n in (32, 64)]
                     + [f"mixed_r{r}_{a}" for r in (16, 64) for a in ("4096to11008", "11008to4096")])
 MODEL_WORKLOADS = ["llama13b_r64_b256_forward"]
@@ -141,7 +148,10 @@ BASE_WORKLOADS += [w.replace("base_", "base_packed_", 1) for w in BASE_WORKLOADS
 
 
 class SingleCallBench:
-    """One sgmv_lora_apply call per step, weights rotated through a >= 1 GiB pool."""
+    """One sgmv_lora_apply call per step, weights rotated through a >= 1 GiB pool.
+    A "_qkv" workload runs three projections that share X (a layer's query, key and
+    value projections, each with its own LoRA pool and output) as one
+    sgmv_lora_apply_batched call per step."""
 
     def __init__(self, name, variant=0, splits=0, row_map="none"):
         import numpy as np
@@ -151,6 +161,9 @@ class SingleCallBench:
 
         self.name, self.sg, self.torch = name, sg, torch
         self.row_map = row_map
+        self.nproj = 3 if "_qkv_" in name else 1
+        if self.nproj > 1 and row_map != "none":
+            raise SystemExit("the projection-batched workloads take rows in segment order only")
         (self.dtype, self.h_in, self.h_out, self.rank, self.n, seg, lidx, self.lpool,
          seed) = workload_layout(name)
         seg, lidx = np.asarray(seg, np.int32), np.asarray(lidx, np.int32)
@@ -167,21 +180,36 @@ class SingleCallBench:
         xy_bytes = e * self.n * (self.h_in + self.h_out)
         self.copies = max(2, min(64, math.ceil((256 << 20) / xy_bytes)))
         s0 = seed * 1000
-        self.A = wl.device_normal((self.ppool, self.h_in, self.rank), self.h_in ** -0.5, self.dtype, s0 + 1)
-        self.B = wl.device_normal((self.ppool, self.rank, self.h_out), self.rank ** -0.5, self.dtype, s0 + 2)
         self.X = wl.device_normal((self.copies, self.n, self.h_in), 1.0, self.dtype, s0 + 3)
-        self.Y = wl.device_normal((self.copies, self.n, self.h_out), 1.0, self.dtype, s0 + 4)
         dev = "cuda"
         phys = (torch.arange(self.tables, device=dev)[:, None] * self.lpool
                 + torch.arange(self.lpool, device=dev)[None, :]).to(torch.int64)
-        self.A_tab = (self.A.data_ptr() + phys * (self.h_in * self.rank * e)).contiguous()
-        self.B_tab = (self.B.data_ptr() + phys * (self.rank * self.h_out * e)).contiguous()
+        # one LoRA pool, pointer tables and output per projection
+        self.As, self.Bs, self.Ys, self.A_tabs, self.B_tabs = [], [], [], [], []
+        for j in range(self.nproj):
+            sj = s0 + 10 * j
+            A = wl.device_normal((self.ppool, self.h_in, self.rank), self.h_in ** -0.5, self.dtype, sj + 1)
+            B = wl.device_normal((self.ppool, self.rank, self.h_out), self.rank ** -0.5, self.dtype, sj + 2)
+            Y = wl.device_normal((self.copies, self.n, self.h_out), 1.0, self.dtype, sj + 4)
+            self.As.append(A)
+            self.Bs.append(B)
+            self.Ys.append(Y)
+            self.A_tabs.append((A.data_ptr() + phys * (self.h_in * self.rank * e)).contiguous())
+            self.B_tabs.append((B.data_ptr() + phys * (self.rank * self.h_out * e)).contiguous())
+        self.A, self.B, self.Y = self.As[0], self.Bs[0], self.Ys[0]
+        self.A_tab, self.B_tab = self.A_tabs[0], self.B_tabs[0]
         self.seg = torch.from_numpy(seg).to(dev)
         self.lidx = torch.from_numpy(lidx if lidx.size else np.zeros(1, np.int32)).to(dev)
         self.problem = sg.make_problem(self.dtype, self.n, self.h_in, self.h_out, self.rank, self.lpool,
                                        len(lidx), int(lens.max()) if lens.size else 0, variant, splits)
-        self.ws = sg.new_workspace(self.problem)
-        self.bytes = algorithmic_bytes(e, self.rows_covered, self.h_in, self.h_out, self.rank, self.distinct)
+        self.ws = torch.zeros(sg.batched_workspace_bytes(self.problem, self.nproj), dtype=torch.uint8,
+                              device=dev)
+        # X is read once for all projections; each projection streams its own
+        # LoRAs and reads and writes its own Y.
+        self.bytes = (algorithmic_bytes(e, self.rows_covered, self.h_in, self.h_out, self.rank, self.distinct)
+                      + (self.nproj - 1) * (algorithmic_bytes(e, self.rows_covered, self.h_in, self.h_out,
+                                                              self.rank, self.distinct)
+                                            - e * self.rows_covered * self.h_in))
         self.rows_per_step = self.rows_covered
         self.calls_per_step = 1
         # Row layout of X and Y.  "none": rows in segment order.  Otherwise rows
@@ -206,7 +234,14 @@ class SingleCallBench:
         self.args, self.keep = [], []
         for c in range(max(self.tables, self.copies)):
             t, x = c % self.tables, c % self.copies
-            if self.row_map == "kernel":
+            if self.nproj > 1:
+                pj = (self.sg.sgmv_projection_t * self.nproj)(
+                    *[self.sg.sgmv_projection_t(self.A_tabs[j][t].data_ptr(), self.B_tabs[j][t].data_ptr(),
+                                                self.Ys[j][x].data_ptr()) for j in range(self.nproj)])
+                self.keep.append(pj)
+                self.args.append((pb, self.X[x].data_ptr(), pj, self.nproj, self.seg.data_ptr(),
+                                  self.lidx.data_ptr(), None, self.ws.data_ptr(), wsn))
+            elif self.row_map == "kernel":
                 pj = (self.sg.sgmv_projection_t * 1)(
                     self.sg.sgmv_projection_t(self.A_tab[t].data_ptr(), self.B_tab[t].data_ptr(),
                                               self.Y[x].data_ptr()))
@@ -224,7 +259,7 @@ class SingleCallBench:
 
     def step(self, c, stream):
         i = c % len(self.args)
-        if self.row_map == "kernel":
+        if self.row_map == "kernel" or self.nproj > 1:
             st = self.fn_batched(*self.args[i], stream)
         elif self.row_map == "torch":
             # The caller's alternative to the row map: gather X and Y into
@@ -249,9 +284,10 @@ class SingleCallBench:
         sid = torch.cuda.current_stream().cuda_stream
         for c in range(calls):
             t, x = c % self.tables, c % self.copies
-            Xh, Y0 = _bits(self.X[x])[self.perm_h], _bits(self.Y[x])[self.perm_h]
-            A = [_bits(self.A[t * self.lpool + k]) for k in range(self.lpool)]
-            B = [_bits(self.B[t * self.lpool + k]) for k in range(self.lpool)]
+            Xh = _bits(self.X[x])[self.perm_h]
+            Y0 = [_bits(Y[x])[self.perm_h] for Y in self.Ys]
+            A = [[_bits(As[t * self.lpool + k]) for k in range(self.lpool)] for As in self.As]
+            B = [[_bits(Bs[t * self.lpool + k]) for k in range(self.lpool)] for Bs in self.Bs]
             mask = None
             if self.n > max_rows:
                 rows = set(np.random.default_rng(c).choice(self.n, 16, replace=False).tolist())
@@ -262,17 +298,20 @@ class SingleCallBench:
                 mask[sorted(rows)] = 1
             self.step(c, sid)
             torch.cuda.synchronize()
-            got = oracle.decode(_bits(self.Y[x])[self.perm_h], self.dtype)
-            ref = oracle.sgmv_apply(self.dtype, Xh, A, B, self.seg_h, self.lidx_h, Y0, row_mask=mask)
-            sel = slice(None) if mask is None else mask.astype(bool)
-            ratio = np.abs(got[sel] - ref[sel]) / (1e-3 + 1e-2 * np.abs(ref[sel]))
-            worst = max(worst, float(ratio.max()))
+            for j in range(self.nproj):
+                got = oracle.decode(_bits(self.Ys[j][x])[self.perm_h], self.dtype)
+                ref = oracle.sgmv_apply(self.dtype, Xh, A[j], B[j], self.seg_h, self.lidx_h, Y0[j],
+                                        row_mask=mask)
+                sel = slice(None) if mask is None else mask.astype(bool)
+                ratio = np.abs(got[sel] - ref[sel]) / (1e-3 + 1e-2 * np.abs(ref[sel]))
+                worst = max(worst, float(ratio.max()))
         if worst > 1.0:
             raise AssertionError(f"bench parity check failed: max err/bound {worst:.3f}")
         return worst
 
     def config(self):
         return {"workload": self.name, "h_in": self.h_in, "h_out": self.h_out, "rank": self.rank,
+                "projections": self.nproj,
                 "batch_rows": self.n, "segments": int(len(self.lidx_h)), "distinct_loras": self.distinct,
                 "lora_pool": self.lpool, "physical_lora_pool": self.ppool, "xy_copies": self.copies,
                 "row_layout": {"none": "segment order", "kernel": "request order, kernel row map",
@@ -924,12 +963,13 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ev_s = e0.elapsed_time(e1) * 1e-3
-    ms_per_step = wall / K * 1e3
+    ms_per_step = ev_s / K * 1e3
     launch_s = ev_s / (K * bench.calls_per_step)
 
-    value = bench.bytes * K / wall / 1e9
+    value = bench.bytes * K / ev_s / 1e9
     achieved = bench.bytes / bench.calls_per_step / launch_s / 1e9
     src_hash = kernel_source_hash()
+    traffic = recorded_traffic(src_hash, args.workload)
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -946,12 +986,18 @@ def main():
         "config": dict(bench.config(), variant=args.variant,
                        launch="graph" if graph is not None else "eager"),
         "pct_peak": round(100 * value / HBM_PEAK_GBS, 2),
-        "tokens_per_s": round(bench.rows_per_step * K / wall, 1),
+        "tokens_per_s": round(bench.rows_per_step * K / ev_s, 1),
         "us_per_call": round(ms_per_step * 1e3 / bench.calls_per_step, 3),
         "launch_us_mean_events": round(launch_s * 1e6, 3),
+        "wall_ms_per_step": round(wall / K * 1e3, 6),
+        "wall_value": round(bench.bytes * K / wall / 1e9, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": recorded_traffic(src_hash, args.workload)},
+                     "traffic": traffic},
+        "roofline_traffic_from": (None if traffic is None else
+                                  "committed counter run " + os.path.relpath(TRAFFIC_FILE, ROOT)
+                                  + " (FETCH_SIZE + WRITE_SIZE per launch, scaled by a 512 MiB copy; "
+                                  "kernel sources " + src_hash + ")"),
         "kernel_source_hash": src_hash,
         "parity_max_err_over_bound": None if worst is None else round(worst, 4),
     }
