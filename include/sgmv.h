@@ -86,12 +86,16 @@ typedef enum sgmv_variant {
   SGMV_VARIANT_MFMA = 3     /* matrix-core kernels for long (prefill) segments */
 } sgmv_variant_t;
 
+/* Largest hidden size (h_in, h_out) the kernels' plans take; larger sizes
+ * give SGMV_ERR_UNSUPPORTED. */
+#define SGMV_MAX_HIDDEN (1 << 20)
+
 /* Host-side shape summary; the host never reads device memory to plan. */
 typedef struct sgmv_problem {
   int32_t dtype;        /* sgmv_dtype_t */
   int32_t n_rows;       /* rows of X, V and Y (>= 0) */
-  int32_t h_in;         /* H1: columns of X, rows of A_k; multiple of 8 */
-  int32_t h_out;        /* H2: columns of Y and B_k; multiple of 8 */
+  int32_t h_in;         /* H1: columns of X, rows of A_k; multiple of 8, <= SGMV_MAX_HIDDEN */
+  int32_t h_out;        /* H2: columns of Y and B_k; multiple of 8, <= SGMV_MAX_HIDDEN */
   int32_t rank;         /* r: one of 8, 16, 32, 64 */
   int32_t num_loras;    /* entries of A_ptrs / B_ptrs (>= 1 when num_segs > 0) */
   int32_t num_segs;     /* S (>= 0); 0 makes every device call a no-op */
@@ -103,7 +107,23 @@ typedef struct sgmv_problem {
 
 /* Size of the leading area of every workspace that holds the kernels'
  * arrival counters.  It must be zero-filled before the workspace's first use;
- * every call that completes leaves it zero again. */
+ * every call that completes leaves it zero again.
+ *
+ * Workspace layout (one projection's slice; sizes from sgmv_workspace_bytes):
+ *   [0, SGMV_WS_COUNTER_BYTES)  arrival counters of the two-launch route
+ *   then                        that route's split partials and V, or the
+ *                               matrix-core route's partial planes and V
+ *   then                        the one-launch decode route's tagged partial
+ *                               slots: an area no other route writes, so a
+ *                               stale word there is always a tag of an
+ *                               earlier decode launch, never another route's
+ *                               data.
+ * Only the counter area must be zero before first use; the rest may hold
+ * anything.  A call that does not complete (a kernel killed part way, a
+ * device reset) can leave counters non-zero, after which two-launch calls on
+ * that workspace give unspecified results: zero the counter area again before
+ * reusing a workspace after such a failure.  The decode route needs no reset:
+ * its slots carry a per-launch tag. */
 #define SGMV_WS_COUNTER_BYTES ((size_t)1 << 20)
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -190,11 +210,40 @@ sgmv_status_t sgmv_expand(const sgmv_problem_t* problem, const float* V, const v
 
 /* Fused apply: Y[i, :] += (X[i, :] @ A_k) @ B_k, the whole LoRA term of the
  * multi-LoRA paragraph, with the fp32 intermediate kept in the workspace or
- * on chip.  Same workspace contract as sgmv_shrink. */
+ * on chip.  Same workspace contract as sgmv_shrink.
+ *
+ * Device sharing (decode route, SGMV_ROUTE_DECODE of sgmv_query_plan): the
+ * workgroups of one unit wait for each other's partial sums, and the grid is
+ * sized from the device's occupancy so that all of them are resident at once
+ * when the launch has the device to itself.  Precondition: no other
+ * decode-route launch runs concurrently on the same device (another stream,
+ * another process), and no other work holds the CUs that the launch needs.
+ * If that is broken, a waiting workgroup gives up after the wait limit
+ * (sgmv_set_wait_limit, default 1 s), leaves its part of Y untouched and sets
+ * SGMV_DEVICE_ERR_WAIT_TIMEOUT in the device error word
+ * (sgmv_take_device_errors): the kernel always ends, and the error is
+ * reported instead of a hang.  Calls on one workspace must not overlap. */
 sgmv_status_t sgmv_lora_apply(const sgmv_problem_t* problem, const void* X,
                               const void* const* A_ptrs, const void* const* B_ptrs, void* Y,
                               const int32_t* seg_indptr, const int32_t* lora_idx, void* ws,
                               size_t ws_bytes, void* stream);
+
+/* Bound on how long a workgroup of the one-launch decode route waits for the
+ * partial sums of the other workgroups of its unit, in microseconds (process
+ * wide, applies to later calls; default 1000000).  0 makes every such wait
+ * give up at once: the decode kernels then exit without updating Y and set
+ * SGMV_DEVICE_ERR_WAIT_TIMEOUT (a test hook for the give-up path).
+ * SGMV_ERR_INVALID_ARG for a negative value.  Host only. */
+sgmv_status_t sgmv_set_wait_limit(int64_t microseconds);
+
+/* Device error bits of the current HIP device. */
+#define SGMV_DEVICE_ERR_WAIT_TIMEOUT 1u  /* a decode-route wait gave up: Y of that call is unspecified */
+
+/* Synchronises the current device (hipDeviceSynchronize), then reads and
+ * clears its device error word: *flags gets the SGMV_DEVICE_ERR_* bits set by
+ * every kernel that ended since the last read (0: none).  SGMV_ERR_HIP when
+ * the device cannot be queried. */
+sgmv_status_t sgmv_take_device_errors(uint32_t* flags);
 
 /* One projection of a batched apply: its own LoRA tables and output.  All
  * pointers are device pointers, as in sgmv_lora_apply.
@@ -300,7 +349,7 @@ sgmv_status_t sgmv_base_lora_apply(const sgmv_problem_t* problem, const void* X,
  * W[32 ks + 8 q + e][16 nb + m], or 0 past the matrix.
  *
  * sgmv_base_packed_weight_bytes: size of the packed copy for h_in, h_out > 0
- *   (SGMV_ERR_INVALID_ARG otherwise).
+ *   (SGMV_ERR_INVALID_ARG otherwise; SGMV_ERR_UNSUPPORTED above SGMV_MAX_HIDDEN).
  * sgmv_base_pack_weight: W device [h_in, h_out] row-major, 2-byte aligned ->
  *   Wp device, 16-byte aligned, wp_bytes >= sgmv_base_packed_weight_bytes
  *   (SGMV_ERR_WORKSPACE below it).  One launch, asynchronous on `stream`; W is

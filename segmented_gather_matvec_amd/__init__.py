@@ -34,7 +34,8 @@ ENTRY_POINTS = ("sgmv_status_str", "sgmv_build_segments", "sgmv_check_problem",
                 "sgmv_check_segments", "sgmv_workspace_bytes", "sgmv_query_plan", "sgmv_shrink",
                 "sgmv_expand", "sgmv_lora_apply", "sgmv_lora_apply_batched", "sgmv_base_workspace_bytes",
                 "sgmv_base_lora_apply", "sgmv_base_packed_weight_bytes", "sgmv_base_pack_weight",
-                "sgmv_base_lora_apply_packed")
+                "sgmv_base_lora_apply_packed", "sgmv_set_wait_limit", "sgmv_take_device_errors")
+SGMV_DEVICE_ERR_WAIT_TIMEOUT = 1
 
 
 class SgmvError(RuntimeError):
@@ -104,6 +105,8 @@ def load_library(path: str = LIB_PATH):
     lib.sgmv_base_packed_weight_bytes.argtypes = [I32, I32, ctypes.POINTER(SZ)]
     lib.sgmv_base_pack_weight.argtypes = [P, I32, I32, P, SZ, P]
     lib.sgmv_base_lora_apply_packed.argtypes = [prob, P, P, P, P, P, P, P, P, SZ, P]
+    lib.sgmv_set_wait_limit.argtypes = [ctypes.c_int64]
+    lib.sgmv_take_device_errors.argtypes = [ctypes.POINTER(ctypes.c_uint32)]
     for name in ENTRY_POINTS[1:]:
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -176,6 +179,18 @@ def sgmv_query_plan(problem: sgmv_problem_t) -> sgmv_plan_info_t:
     info = sgmv_plan_info_t()
     _check(load_library().sgmv_query_plan(ctypes.byref(problem), ctypes.byref(info)), "sgmv_query_plan")
     return info
+
+
+def sgmv_set_wait_limit(microseconds: int):
+    """Bound (us) on a decode-route workgroup's wait for its unit's partials; 0 gives up at once."""
+    _check(load_library().sgmv_set_wait_limit(int(microseconds)), "sgmv_set_wait_limit")
+
+
+def sgmv_take_device_errors() -> int:
+    """Synchronise the current device, then read and clear its SGMV_DEVICE_ERR_* bits."""
+    out = ctypes.c_uint32(0)
+    _check(load_library().sgmv_take_device_errors(ctypes.byref(out)), "sgmv_take_device_errors")
+    return int(out.value)
 
 
 # ----------------------------------------------------------------- device calls

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdint>
 #include <cstdlib>
 #include <mutex>
@@ -10,117 +11,42 @@
 #include <vector>
 
 #include "../../include/sgmv.h"
+#include "sgmv_host.h"
 #include "sgmv_plan.h"
 
 namespace {
 
+using namespace sgmv_host;
 using sgmv::VecParams;
 
 constexpr int kMaxDevices = 64;
-constexpr int64_t kCounterSlots = (int64_t)(SGMV_WS_COUNTER_BYTES / sizeof(uint32_t));
-// Aim for this many workgroups per launch of the vector kernels: two per CU of
-// a 256-CU MI355X keeps enough 128-bit loads in flight to cover HBM latency.
-constexpr int kTargetWorkgroups = 512;
-constexpr int kMaxSplits = 1024;
 
-bool rank_supported(int r) { return r == 8 || r == 16 || r == 32 || r == 64; }
+static_assert(sgmv::kDecodeErrWaitTimeout == SGMV_DEVICE_ERR_WAIT_TIMEOUT, "error bits of the ABI");
 
-int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
-int64_t round_up(int64_t a, int64_t m) { return ceil_div(a, m) * m; }
+// Longest wait of a decode-route workgroup for its unit's other partials
+// (sgmv_set_wait_limit).  A legitimate wait lasts microseconds; the bound is
+// there for a launch that does not have the device to itself.
+std::atomic<int64_t> g_wait_limit_us{1000000};
 
-// Plan of one vector-kernel launch.
-struct VecPlan {
-  int rb = 1;
-  int direct = 1;
-  int64_t num_units = 0;
-  int splits = 1;
-  int kc = 8;
-  int cw = 8;
-  size_t partial_bytes() const {
-    return (size_t)num_units * (size_t)splits * (size_t)rb * sizeof(float);  // times rank
-  }
-};
-
-int pick_rb(int max_seg_len) { return max_seg_len <= 1 ? 1 : (max_seg_len <= 4 ? 4 : 16); }
-
-VecPlan plan_vec(const sgmv_problem_t& p, int64_t target_wgs) {
-  VecPlan v;
-  v.rb = pick_rb(p.max_seg_len);
-  if (p.max_seg_len <= v.rb) {
-    v.direct = 1;
-    v.num_units = p.num_segs;
+// The limit in ticks of the current device's real-time counter (0 only for a
+// limit of 0).
+uint32_t wait_ticks() {
+  static std::mutex mu;
+  static int khz[kMaxDevices];
+  const int64_t us = g_wait_limit_us.load(std::memory_order_relaxed);
+  if (us == 0) return 0;
+  int dev = 0, rate = 0;
+  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDevices) {
+    std::lock_guard<std::mutex> lock(mu);
+    if (khz[dev] == 0 &&
+        (hipDeviceGetAttribute(&khz[dev], hipDeviceAttributeWallClockRate, dev) != hipSuccess || khz[dev] <= 0))
+      khz[dev] = 100000;  // the 100 MHz counter of CDNA devices
+    rate = khz[dev];
   } else {
-    v.direct = 0;
-    const int64_t per_seg = ceil_div(p.max_seg_len, v.rb);
-    v.num_units = std::min<int64_t>((int64_t)p.num_segs * per_seg, ceil_div(p.n_rows, v.rb) + p.num_segs);
+    rate = 100000;
   }
-  const int64_t max_split = std::min<int64_t>(
-      {ceil_div(p.h_in, 8), ceil_div(p.h_out, 8), (int64_t)kMaxSplits});
-  int64_t g = p.splits > 0 ? p.splits : ceil_div(target_wgs, std::max<int64_t>(v.num_units, 1));
-  g = std::max<int64_t>(1, std::min(g, max_split));
-  v.splits = (int)g;
-  v.kc = (int)round_up(ceil_div(p.h_in, g), 8);
-  v.cw = (int)round_up(ceil_div(p.h_out, g), 8);
-  return v;
-}
-
-size_t vec_ws_bytes(const VecPlan& v, int rank) {
-  return SGMV_WS_COUNTER_BYTES + v.partial_bytes() * (size_t)rank;
-}
-
-// fp32 intermediate V [n_rows, rank] of the two-launch route of sgmv_lora_apply.
-size_t v_area_bytes(const sgmv_problem_t& p) {
-  return (size_t)round_up((int64_t)p.n_rows * p.rank * (int64_t)sizeof(float), 256);
-}
-
-// Plan of one decode-kernel launch (sgmv_lora_apply on short segments).
-struct DecodePlan {
-  bool supported = false;  // shapes the decode kernel takes
-  int rb = 1;
-  int direct = 1;
-  int64_t num_units = 0;
-  int splits = 1;
-  int kc = 8;
-  int cw = 8;
-  int64_t grid = 0;         // workgroups of the launch: round_units * splits
-  int64_t round_units = 0;  // units covered by one pass of the grid
-  int64_t rounds = 1;       // passes: more than one when the units do not all fit at once
-  size_t slot_bytes = 0;
-  int split_major = 0;
-};
-
-DecodePlan plan_decode_rb(const sgmv_problem_t& p, int rb, int split_major) {
-  DecodePlan d;
-  d.rb = rb;
-  d.split_major = split_major;
-  if (!sgmv::decode_supported(p.rank, d.rb)) return d;
-  if (p.max_seg_len <= d.rb) {
-    d.direct = 1;
-    d.num_units = p.num_segs;
-  } else {
-    d.direct = 0;
-    const int64_t per_seg = ceil_div(p.max_seg_len, d.rb);
-    d.num_units = std::min<int64_t>((int64_t)p.num_segs * per_seg, ceil_div(p.n_rows, d.rb) + p.num_segs);
-  }
-  const int64_t gmin = std::max(ceil_div(p.h_in, sgmv::decode_max_kc(p.rank)),
-                                ceil_div(p.h_out, sgmv::decode_max_cw()));
-  const int64_t gmax = std::min<int64_t>({ceil_div(p.h_in, 8), ceil_div(p.h_out, 8), (int64_t)kMaxSplits});
-  if (gmin > gmax) return d;
-  // The fewest splits whose chunks fit one workgroup: every extra split adds a
-  // partial to each unit's exchange, and measured over batches of 1 to 64 rows
-  // the exchange fan-in costs more than the bandwidth of the extra workgroups
-  // gains (one row: 8.8 us at 128 splits, 4.0 us at 8).
-  const int parts = 1;  // one published partial per workgroup
-  int64_t g = p.splits > 0 ? p.splits : gmin;
-  g = std::max(gmin, std::min(g, gmax));
-  d.splits = (int)g;
-  d.kc = (int)round_up(ceil_div(p.h_in, g), 8);
-  d.cw = (int)round_up(ceil_div(p.h_out, g), 8);
-  d.round_units = split_major ? d.num_units : 8 * ceil_div(d.num_units, 8);
-  d.grid = d.round_units * g;
-  d.slot_bytes = (size_t)d.num_units * (size_t)g * parts * d.rb * p.rank * sizeof(uint64_t);
-  d.supported = d.grid > 0 && d.grid <= (int64_t)INT32_MAX;
-  return d;
+  const double ticks = (double)us * rate / 1000.0;
+  return ticks >= 4294967295.0 ? 0xffffffffu : std::max<uint32_t>(1u, (uint32_t)ticks);
 }
 
 // Variant of the decode kernel a call launches: bit 0 at most 64 LoRAs (the
@@ -154,31 +80,6 @@ int decode_capacity(int dtype, int rank, int rb, int variant) {
 // 43.2 us).
 constexpr int64_t kMaxDecodeRounds = 4;
 
-// Candidate decode plans, smallest row block first. Blocks of one row keep
-// the most workgroups busy; when segments hold several rows (rows that share
-// a LoRA), the split-major mapping puts equal splits of neighbouring units on
-// one XCD, so a segment's rows re-read their A_k / B_k slice from that XCD's
-// L2 rather than from HBM. Segments of one row keep a unit on one XCD.
-int decode_candidates(const sgmv_problem_t& p, DecodePlan out[3]) {
-  const int split_major = p.max_seg_len > 1 ? 1 : 0;
-  int n = 0;
-  for (int rb : {1, 4, 16}) {
-    const DecodePlan d = plan_decode_rb(p, rb, split_major);
-    if (d.supported) out[n++] = d;
-    if (p.max_seg_len <= rb) break;  // a larger block only adds empty rows
-  }
-  return n;
-}
-
-// The matrix-core kernels take over segments longer than the decode kernel's
-// row blocks (at ranks 16..64); AUTO picks them when the decode kernel cannot
-// run the call.
-bool stage_uses_mfma(const sgmv_problem_t& p) {
-  if (!sgmv::mfma_supported(p.rank)) return false;
-  if (p.variant == SGMV_VARIANT_MFMA) return true;
-  return p.variant == SGMV_VARIANT_AUTO && p.max_seg_len > 16;
-}
-
 // The first candidate whose grid is co-resident on the current device (the
 // kernel's workgroups wait for each other; the capacity is the launched
 // variant's, see decode_variant).  When none is, the smallest row block runs
@@ -207,80 +108,6 @@ DecodePlan plan_decode(const sgmv_problem_t& p, int variant) {
   return DecodePlan{};
 }
 
-size_t decode_ws_bytes(const sgmv_problem_t& p) {
-  DecodePlan c[3];
-  const int n = decode_candidates(p, c);
-  size_t b = 0;
-  for (int i = 0; i < n; ++i) b = std::max(b, c[i].slot_bytes);
-  return b;
-}
-
-// Plan of the matrix-core kernels (long segments).
-struct MfmaPlan {
-  int64_t units64 = 0;
-  int direct64 = 1;
-  int ksplit = 1;
-  int kc = 0;
-  int chunks_per_wg = 1;
-  int expand_rows = sgmv::kMfmaRowsPerTile;  // rows of one expand tile (16 for short tiles)
-  int64_t units_x = 0;                        // expand units of <= expand_rows rows
-  int direct_x = 1;
-  size_t partial_bytes = 0;  // split partials of V, fp32 [ksplit][n_rows][rank]
-};
-
-// Aim for about four shrink workgroups (row tile x H1 chunk) per CU.
-// Expand: when row tiles are mostly full, a chunk is bandwidth-bound and
-// about four workgroups per CU (dispatched as slots free up) hide latency
-// best.  When they are mostly short (decode-like rows of many LoRAs), the
-// expand takes 16-row tiles and three 128-column chunks per workgroup: a sweep
-// of 1 to 10 chunks on 256 rows in 34 segments (r = 64, H = 5120 and 13824)
-// found 3 best, about 1.5% ahead of a grid sized to be resident at once.
-constexpr int kMfmaShrinkTarget = 1024;
-constexpr int kMfmaExpandTarget = 1024;
-constexpr int kMfmaShortTileRows = 32;   // mean rows per 64-row tile below which tiles count as short
-constexpr int kMfmaShortExpandRows = 16; // expand tile rows for short tiles
-constexpr int kMfmaShortChunksPerWg = 3;
-
-int64_t units_for(const sgmv_problem_t& p, int rows, int* direct) {
-  if (p.max_seg_len <= rows) {
-    *direct = 1;
-    return p.num_segs;
-  }
-  *direct = 0;
-  return std::min<int64_t>((int64_t)p.num_segs * ceil_div(p.max_seg_len, rows), ceil_div(p.n_rows, rows) + p.num_segs);
-}
-
-MfmaPlan plan_mfma(const sgmv_problem_t& p) {
-  MfmaPlan m;
-  m.units64 = units_for(p, sgmv::kMfmaRowsPerTile, &m.direct64);
-  // The H1 split multiplies the workgroups, but every split writes (and the
-  // reduce reads) one fp32 plane of V: keep that traffic within a quarter of
-  // what the shrink must read anyway (X, plus A_k once per segment).
-  const int64_t units = std::max<int64_t>(m.units64, 1);
-  const double must_read = 2.0 * (double)p.n_rows * p.h_in + 2.0 * (double)p.num_segs * p.h_in * p.rank;
-  const double per_split = 8.0 * (double)p.n_rows * p.rank;
-  const int64_t ks_traffic = std::max<int64_t>(1, (int64_t)(0.25 * must_read / std::max(per_split, 1.0)));
-  const int64_t ks = std::max<int64_t>(1, std::min<int64_t>({ceil_div(kMfmaShrinkTarget, units), ks_traffic,
-                                                             ceil_div(p.h_in, sgmv::kMfmaKChunk)}));
-  m.kc = (int)round_up(ceil_div(p.h_in, ks), sgmv::kMfmaKChunk);
-  m.ksplit = (int)ceil_div(p.h_in, m.kc);
-  const int64_t nchunks = ceil_div(p.h_out, sgmv::kMfmaColsPerTile);
-  m.units_x = m.units64;
-  m.direct_x = m.direct64;
-  if ((int64_t)p.n_rows < kMfmaShortTileRows * units) {
-    // Short tiles: 16-row expand tiles (all four waves compute), a few chunks
-    // per workgroup.
-    m.expand_rows = kMfmaShortExpandRows;
-    m.units_x = units_for(p, kMfmaShortExpandRows, &m.direct_x);
-    m.chunks_per_wg = (int)std::min<int64_t>(nchunks, kMfmaShortChunksPerWg);
-  } else {
-    const int64_t groups = std::max<int64_t>(1, std::min<int64_t>(nchunks, kMfmaExpandTarget / units));
-    m.chunks_per_wg = (int)ceil_div(nchunks, groups);
-  }
-  m.partial_bytes = (size_t)m.ksplit * (size_t)p.n_rows * p.rank * sizeof(float);
-  return m;
-}
-
 sgmv::MfmaParams mfma_params(const sgmv_problem_t& p, const MfmaPlan& m, const int32_t* seg_indptr,
                              const int32_t* lora_idx) {
   sgmv::MfmaParams q{};
@@ -307,10 +134,6 @@ sgmv::MfmaParams mfma_params(const sgmv_problem_t& p, const MfmaPlan& m, const i
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 bool aligned8(const void* p) { return ((uintptr_t)p & 7u) == 0; }
 bool aligned2(const void* p) { return ((uintptr_t)p & 1u) == 0; }
-
-bool nothing_to_do(const sgmv_problem_t& p) {
-  return p.num_segs == 0 || p.n_rows == 0 || p.max_seg_len == 0;
-}
 
 VecParams base_params(const sgmv_problem_t& p, const VecPlan& v, const int32_t* seg_indptr,
                       const int32_t* lora_idx, void* ws) {
@@ -346,16 +169,6 @@ sgmv_route_t apply_route(const sgmv_problem_t& p, const DecodePlan& d) {
   return stage_uses_mfma(p) ? SGMV_ROUTE_MFMA : SGMV_ROUTE_VECTOR;
 }
 
-size_t apply_ws_bytes(const sgmv_problem_t& p) {
-  const VecPlan v = plan_vec(p, kTargetWorkgroups);
-  const size_t two_launch = vec_ws_bytes(v, p.rank) + v_area_bytes(p);
-  const size_t one_launch = SGMV_WS_COUNTER_BYTES + decode_ws_bytes(p);
-  const size_t matrix = sgmv::mfma_supported(p.rank)
-                            ? SGMV_WS_COUNTER_BYTES + plan_mfma(p).partial_bytes + v_area_bytes(p)
-                            : 0;
-  return std::max({two_launch, one_launch, matrix});
-}
-
 sgmv::Projection kernel_projection(const sgmv_projection_t& pj) {
   sgmv::Projection k{};
   k.A_ptrs = reinterpret_cast<const uint64_t*>(pj.A_ptrs);
@@ -388,12 +201,14 @@ sgmv_status_t apply(const sgmv_problem_t& p, const void* X, const sgmv_projectio
       return SGMV_OK;
     }
     sgmv::DecodeParams q{};
+    if (sgmv::decode_error_word(&q.errors) != hipSuccess) return SGMV_ERR_HIP;
+    q.wait_ticks = wait_ticks();
     q.X = static_cast<const uint16_t*>(X);
     for (int i = 0; i < np; ++i) q.proj[i] = kernel_projection(pj[i]);
     q.seg_indptr = seg_indptr;
     q.lora_idx = lora_idx;
     q.row_idx = row_idx;
-    q.slots = reinterpret_cast<uint64_t*>(ws + SGMV_WS_COUNTER_BYTES);
+    q.slots = reinterpret_cast<uint64_t*>(ws + apply_ws_layout(p).decode_off);
     q.slot_stride = (int64_t)(stride / sizeof(uint64_t));
     q.n_rows = p.n_rows;
     q.h_in = p.h_in;
@@ -456,139 +271,7 @@ sgmv_status_t apply(const sgmv_problem_t& p, const void* X, const sgmv_projectio
 
 }  // namespace
 
-// Base projection with the LoRA term: W strips of kBaseStripCols columns,
-// split over K into fp32 partial planes so that about kBaseTarget workgroups
-// stream W at once.  A sweep of strips (64, 128, 256 columns) against targets
-// (128 to 1024) on 32-row batches (H = 4096 and 11008 -> 4096) found 128 x 256
-// best: more splits write (and the epilogue reads) more partial planes.
-constexpr int kBaseStripCols = 128;
-constexpr int kBaseTarget = 256;
-
-struct BasePlan {
-  int strip_cols = kBaseStripCols;
-  int strips = 0;
-  int ksplit = 1;
-  int kc = 0;
-  int base_grid = 0;
-  size_t b_off = 0, v_off = 0, p_off = 0, total = 0;  // workspace layout
-};
-
-BasePlan plan_base(const sgmv_problem_t& p, bool packed) {
-  BasePlan b;
-  b.strips = (int)ceil_div(p.h_out, b.strip_cols);
-  const int64_t max_split = ceil_div(p.h_in, sgmv::kBaseStageRows);
-  const int64_t ks = std::max<int64_t>(1, std::min<int64_t>(ceil_div(kBaseTarget, b.strips), max_split));
-  b.kc = (int)round_up(ceil_div(p.h_in, ks), sgmv::kBaseStageRows);
-  if (packed && p.n_rows > 32) {
-    // The packed-W kernel stages the X chunk of its four row tiles (64 x kc) in LDS.
-    const int64_t cap = sgmv::kBasePackedXElems / 64 / sgmv::kBaseStageRows * sgmv::kBaseStageRows;
-    b.kc = (int)std::min<int64_t>(b.kc, cap);
-  }
-  b.ksplit = (int)ceil_div(p.h_in, b.kc);
-  b.base_grid = (int)round_up((int64_t)b.strips * b.ksplit, 8);
-  // [B_k of each row][partial planes of V][partial planes of Y]
-  b.b_off = 0;
-  b.v_off = (size_t)round_up((int64_t)p.n_rows * (int64_t)sizeof(uint64_t), 256);
-  b.p_off = b.v_off + (size_t)round_up((int64_t)b.ksplit * p.n_rows * p.rank * (int64_t)sizeof(float), 256);
-  b.total = b.p_off + (size_t)b.ksplit * (size_t)p.n_rows * (size_t)p.h_out * sizeof(float);
-  return b;
-}
-
 extern "C" {
-
-const char* sgmv_status_str(sgmv_status_t status) {
-  switch (status) {
-    case SGMV_OK: return "SGMV_OK";
-    case SGMV_ERR_INVALID_ARG: return "SGMV_ERR_INVALID_ARG: invalid argument";
-    case SGMV_ERR_UNSUPPORTED: return "SGMV_ERR_UNSUPPORTED: shape, rank, dtype or alignment not supported";
-    case SGMV_ERR_WORKSPACE: return "SGMV_ERR_WORKSPACE: workspace missing or too small";
-    case SGMV_ERR_HIP: return "SGMV_ERR_HIP: HIP runtime or launch failure";
-  }
-  return "SGMV_ERR_UNKNOWN";
-}
-
-sgmv_status_t sgmv_build_segments(const int32_t* req_lora, int32_t n, int32_t num_loras,
-                                  int32_t* perm, int32_t* seg_indptr, int32_t* lora_idx,
-                                  int32_t* num_segs, int32_t* max_seg_len) {
-  if (n < 0 || num_loras < 1 || !seg_indptr || !num_segs || !max_seg_len) return SGMV_ERR_INVALID_ARG;
-  if (n > 0 && (!req_lora || !perm || !lora_idx)) return SGMV_ERR_INVALID_ARG;
-  for (int32_t i = 0; i < n; ++i)
-    if (req_lora[i] < 0 || req_lora[i] >= num_loras) return SGMV_ERR_INVALID_ARG;
-  seg_indptr[0] = 0;
-  int32_t S = 0, longest = 0;
-  if ((int64_t)num_loras <= 4 * (int64_t)n + 1024) {
-    // Counting sort: O(n + num_loras), stable.
-    std::vector<int32_t> start((size_t)num_loras + 1, 0);
-    for (int32_t i = 0; i < n; ++i) ++start[(size_t)req_lora[i] + 1];
-    for (int32_t k = 0; k < num_loras; ++k) {
-      const int32_t c = start[(size_t)k + 1];
-      if (c > 0) {
-        lora_idx[S] = k;
-        seg_indptr[S + 1] = seg_indptr[S] + c;
-        longest = std::max(longest, c);
-        ++S;
-      }
-      start[(size_t)k + 1] += start[(size_t)k];
-    }
-    for (int32_t i = 0; i < n; ++i) perm[start[(size_t)req_lora[i]]++] = i;
-  } else {
-    // Sparse ids: stable comparison sort, O(n log n).
-    std::vector<std::pair<int32_t, int32_t>> key((size_t)n);
-    for (int32_t i = 0; i < n; ++i) key[(size_t)i] = {req_lora[i], i};
-    std::sort(key.begin(), key.end());
-    for (int32_t j = 0; j < n; ++j) {
-      perm[j] = key[(size_t)j].second;
-      if (j == 0 || key[(size_t)j].first != key[(size_t)j - 1].first) {
-        if (j > 0) seg_indptr[S] = j;
-        lora_idx[S++] = key[(size_t)j].first;
-      }
-    }
-    if (n > 0) seg_indptr[S] = n;
-    for (int32_t s = 0; s < S; ++s) longest = std::max(longest, seg_indptr[s + 1] - seg_indptr[s]);
-  }
-  *num_segs = S;
-  *max_seg_len = longest;
-  return SGMV_OK;
-}
-
-sgmv_status_t sgmv_check_problem(const sgmv_problem_t* p) {
-  if (!p) return SGMV_ERR_INVALID_ARG;
-  if (p->n_rows < 0 || p->h_in <= 0 || p->h_out <= 0 || p->num_segs < 0 || p->num_loras < 0 ||
-      p->max_seg_len < 0 || p->max_seg_len > p->n_rows || p->splits < 0)
-    return SGMV_ERR_INVALID_ARG;
-  if (p->num_segs > 0 && p->num_loras < 1) return SGMV_ERR_INVALID_ARG;
-  if (p->variant < SGMV_VARIANT_AUTO || p->variant > SGMV_VARIANT_MFMA) return SGMV_ERR_INVALID_ARG;
-  if (p->dtype != SGMV_F16 && p->dtype != SGMV_BF16) return SGMV_ERR_UNSUPPORTED;
-  if (!rank_supported(p->rank)) return SGMV_ERR_UNSUPPORTED;
-  if (p->h_in % 8 != 0 || p->h_out % 8 != 0) return SGMV_ERR_UNSUPPORTED;
-  if (p->variant == SGMV_VARIANT_MFMA && !sgmv::mfma_supported(p->rank)) return SGMV_ERR_UNSUPPORTED;
-  const VecPlan v = plan_vec(*p, kTargetWorkgroups);
-  if (2 * v.num_units > kCounterSlots) return SGMV_ERR_UNSUPPORTED;
-  return SGMV_OK;
-}
-
-sgmv_status_t sgmv_check_segments(const sgmv_problem_t* p, const int32_t* seg_indptr_host,
-                                  const int32_t* lora_idx_host) {
-  if (!p) return SGMV_ERR_INVALID_ARG;
-  if (p->num_segs < 0) return SGMV_ERR_INVALID_ARG;
-  if (!seg_indptr_host || (p->num_segs > 0 && !lora_idx_host)) return SGMV_ERR_INVALID_ARG;
-  if (seg_indptr_host[0] != 0) return SGMV_ERR_INVALID_ARG;
-  for (int32_t s = 0; s < p->num_segs; ++s) {
-    const int32_t len = seg_indptr_host[s + 1] - seg_indptr_host[s];
-    if (len < 0 || len > p->max_seg_len) return SGMV_ERR_INVALID_ARG;
-    if (lora_idx_host[s] < 0 || lora_idx_host[s] >= p->num_loras) return SGMV_ERR_INVALID_ARG;
-  }
-  if (seg_indptr_host[p->num_segs] > p->n_rows) return SGMV_ERR_INVALID_ARG;
-  return SGMV_OK;
-}
-
-sgmv_status_t sgmv_workspace_bytes(const sgmv_problem_t* p, size_t* bytes) {
-  if (!bytes) return SGMV_ERR_INVALID_ARG;
-  const sgmv_status_t st = sgmv_check_problem(p);
-  if (st != SGMV_OK) return st;
-  *bytes = apply_ws_bytes(*p);
-  return SGMV_OK;
-}
 
 sgmv_status_t sgmv_shrink(const sgmv_problem_t* p, const void* X, const void* const* A_ptrs,
                           float* V, const int32_t* seg_indptr, const int32_t* lora_idx, void* ws,
@@ -684,6 +367,27 @@ sgmv_status_t sgmv_query_plan(const sgmv_problem_t* p, sgmv_plan_info_t* info) {
   return SGMV_OK;
 }
 
+sgmv_status_t sgmv_set_wait_limit(int64_t microseconds) {
+  if (microseconds < 0) return SGMV_ERR_INVALID_ARG;
+  g_wait_limit_us.store(microseconds, std::memory_order_relaxed);
+  return SGMV_OK;
+}
+
+sgmv_status_t sgmv_take_device_errors(uint32_t* flags) {
+  if (!flags) return SGMV_ERR_INVALID_ARG;
+  uint32_t* word = nullptr;
+  if (sgmv::decode_error_word(&word) != hipSuccess) return SGMV_ERR_HIP;
+  if (hipDeviceSynchronize() != hipSuccess) return SGMV_ERR_HIP;
+  uint32_t v = 0;
+  if (hipMemcpy(&v, word, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return SGMV_ERR_HIP;
+  if (v != 0) {
+    const uint32_t zero = 0;
+    if (hipMemcpy(word, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess) return SGMV_ERR_HIP;
+  }
+  *flags = v;
+  return SGMV_OK;
+}
+
 sgmv_status_t sgmv_lora_apply(const sgmv_problem_t* p, const void* X, const void* const* A_ptrs,
                               const void* const* B_ptrs, void* Y, const int32_t* seg_indptr,
                               const int32_t* lora_idx, void* ws, size_t ws_bytes, void* stream) {
@@ -710,32 +414,16 @@ sgmv_status_t sgmv_lora_apply_batched(const sgmv_problem_t* p, const void* X,
   }
   if (!ws) return SGMV_ERR_WORKSPACE;
   if (!aligned16(ws)) return SGMV_ERR_UNSUPPORTED;
-  const size_t need = apply_ws_bytes(*p);
+  const size_t need = apply_ws_layout(*p).total;
   const size_t stride = (size_t)round_up((int64_t)need, 256);
   if (ws_bytes < stride * (size_t)(num_projections - 1) + need) return SGMV_ERR_WORKSPACE;
   return apply(*p, X, projections, num_projections, seg_indptr, lora_idx, row_idx, static_cast<char*>(ws),
                stride, static_cast<hipStream_t>(stream));
 }
 
-sgmv_status_t sgmv_base_workspace_bytes(const sgmv_problem_t* p, size_t* bytes) {
-  if (!bytes) return SGMV_ERR_INVALID_ARG;
-  const sgmv_status_t st = sgmv_check_problem(p);
-  if (st != SGMV_OK) return st;
-  if (p->n_rows > sgmv::kBaseMaxRows) return SGMV_ERR_UNSUPPORTED;
-  *bytes = std::max(plan_base(*p, false).total, plan_base(*p, true).total);
-  return SGMV_OK;
-}
-
 }  // extern "C"
 
 namespace {
-
-// Bytes of the packed layout of W [h_in, h_out]: 16-column blocks (an even
-// count) of ceil(h_in / 128) * 4 k-steps of 1 KiB each.
-int64_t packed_ksteps(int64_t h_in) { return ceil_div(h_in, 128) * 4; }
-int64_t packed_bytes(int64_t h_in, int64_t h_out) {
-  return round_up(ceil_div(h_out, 16), 2) * packed_ksteps(h_in) * 1024;
-}
 
 sgmv_status_t base_apply(const sgmv_problem_t* p, const void* X, const void* W, bool packed,
                          const void* const* A_ptrs, const void* const* B_ptrs, void* Y,
@@ -791,12 +479,6 @@ sgmv_status_t sgmv_base_lora_apply(const sgmv_problem_t* p, const void* X, const
                                    const int32_t* seg_indptr, const int32_t* lora_idx, void* ws,
                                    size_t ws_bytes, void* stream) {
   return base_apply(p, X, W, false, A_ptrs, B_ptrs, Y, seg_indptr, lora_idx, ws, ws_bytes, stream);
-}
-
-sgmv_status_t sgmv_base_packed_weight_bytes(int32_t h_in, int32_t h_out, size_t* bytes) {
-  if (!bytes || h_in <= 0 || h_out <= 0) return SGMV_ERR_INVALID_ARG;
-  *bytes = (size_t)packed_bytes(h_in, h_out);
-  return SGMV_OK;
 }
 
 sgmv_status_t sgmv_base_pack_weight(const void* W, int32_t h_in, int32_t h_out, void* Wp, size_t wp_bytes,

@@ -24,7 +24,14 @@
 //     hold several rows that share a LoRA, split-major order instead places
 //     equal splits of neighbouring units (the same A_k / B_k slice) on one
 //     XCD, so those slices are fetched from HBM once per XCD.
-//   * The grid is sized by the host to be co-resident, so every wait ends.
+//   * The grid is sized by the host to be co-resident, so every wait ends when
+//     the launch has the device to itself.  Each wait is still bounded: past a
+//     deadline on the constant-rate real-time counter the workgroup gives up,
+//     sets a bit in the device error word and exits without touching Y (the
+//     case of another kernel holding the CUs that the unit's other workgroups
+//     need).
+#include <mutex>
+
 #include "sgmv_device.h"
 #include "sgmv_plan.h"
 #include "sgmv_units.h"
@@ -34,11 +41,21 @@
 extern "C" __device__ unsigned long long sgmv_llvm_dispatch_id() __asm("llvm.amdgcn.dispatch.id");
 
 namespace sgmv {
+
+// Sticky error bits of the decode route on this device (SGMV_DEVICE_ERR_*),
+// read and cleared by sgmv_take_device_errors.
+__device__ __align__(256) uint32_t decode_errors;
+
 namespace {
 
 constexpr int kXcds = 8;
-constexpr int kPollPerThread = 8;
-constexpr int kStage = kThreads * kPollPerThread;
+// Tagged words each thread polls per round: enough for the unit's outputs of
+// V times 16 splits (every plan of H1 up to 8192 at rank 16), at most 8; a
+// plan with more splits takes several rounds.  Fewer poll registers leave
+// more of the register budget to the streamed A_k and B_k.
+constexpr int poll_per_thread(int rb, int r) {
+  return rb * r * 16 / kThreads < 1 ? 1 : rb * r * 16 / kThreads > 4 ? 4 : rb * r * 16 / kThreads;
+}
 
 __device__ inline uint32_t launch_tag() {
   const uint64_t did = sgmv_llvm_dispatch_id();
@@ -103,12 +120,15 @@ __global__ __launch_bounds__(kThreads) void sgmv_decode_kernel(DecodeParams p) {
   constexpr int NY = (RB + JQ - 1) / JQ;     // Y vectors per thread
   constexpr int PW = 1;                      // published partials per workgroup
   constexpr int NXV = RB == 1 ? 1 : (RB * KCMAX / 8 + kThreads - 1) / kThreads;
+  constexpr int kPollPerThread = poll_per_thread(RB, R);
+  constexpr int kStage = kThreads * kPollPerThread;
   static_assert(RB * R <= kThreads, "one output of V per thread");
 
   __shared__ __attribute__((aligned(16))) uint16_t lds_x[RB == 1 ? 8 : RB * KCMAX];
   __shared__ float lds_red[kWaves * RB * R];
   __shared__ float lds_stage[kStage];
   __shared__ float lds_v[RB * R];
+  __shared__ int lds_gave_up;
 
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -123,7 +143,8 @@ __global__ __launch_bounds__(kThreads) void sgmv_decode_kernel(DecodeParams p) {
                          p.h_in | p.h_out | p.num_segs | p.num_loras | p.unit_base | (p.round_units - 1) |
                          (int32_t)(p.slot_stride >> 32)) < 0;
   bool bad_ptr = (p.seg_indptr == nullptr) | (p.lora_idx == nullptr) | (p.X == nullptr) |
-                 (p.slots == nullptr) | (pr.A_ptrs == nullptr) | (pr.B_ptrs == nullptr) | (pr.Y == nullptr);
+                 (p.slots == nullptr) | (pr.A_ptrs == nullptr) | (pr.B_ptrs == nullptr) | (pr.Y == nullptr) |
+                 (p.errors == nullptr);
   // The optional int32 / fp32 tables are 4-byte aligned (the rank and scale
   // tables are nullable).
   if constexpr (MAP) bad_ptr |= (reinterpret_cast<uintptr_t>(p.row_idx) & 3) != 0 || p.row_idx == nullptr;
@@ -320,6 +341,7 @@ __global__ __launch_bounds__(kThreads) void sgmv_decode_kernel(DecodeParams p) {
 #pragma unroll
     for (int i = 0; i < RB; ++i)
       if (i < L && rank_lane) lds_red[(wave * RB + i) * R + j_of_lane] = acc[i][0];
+    if (t == 0) lds_gave_up = 0;
     __syncthreads();
     if (t < L * R) {
       float s = 0.f;
@@ -334,6 +356,11 @@ __global__ __launch_bounds__(kThreads) void sgmv_decode_kernel(DecodeParams p) {
   const int parts = G * PW;                   // partials per output
   const int per_round = kStage / n_out;       // partials staged per round (>= 1)
   float vsum = 0.f;
+  // The wait ends at a deadline on the constant-rate real-time counter.  A
+  // limit of 0 (the host's test hook) waits for a tag no partial carries, so
+  // every workgroup gives up at its first check.
+  const uint64_t deadline = __builtin_amdgcn_s_memrealtime() + p.wait_ticks;
+  const uint32_t want = p.wait_ticks != 0 ? tag : ~tag;
   for (int p0 = 0; p0 < parts; p0 += per_round) {
     const int pn = parts - p0 < per_round ? parts - p0 : per_round;
     const int items = pn * n_out;
@@ -348,26 +375,34 @@ __global__ __launch_bounds__(kThreads) void sgmv_decode_kernel(DecodeParams p) {
       // cost); the others are never examined.
       w[m] = it < items ? fetch_tagged(src[m]) : 0;
     }
+    bool done;
     for (;;) {
-      bool done = true;
+      done = true;
 #pragma unroll
       for (int m = 0; m < kPollPerThread; ++m)
-        if (t + kThreads * m < items && (uint32_t)(w[m] >> 32) != tag) done = false;
-      if (done) break;
+        if (t + kThreads * m < items && (uint32_t)(w[m] >> 32) != want) done = false;
+      if (done || __builtin_amdgcn_s_memrealtime() > deadline) break;
       __builtin_amdgcn_s_sleep(1);
 #pragma unroll
       for (int m = 0; m < kPollPerThread; ++m)
-        if (t + kThreads * m < items && (uint32_t)(w[m] >> 32) != tag) w[m] = fetch_tagged(src[m]);
+        if (t + kThreads * m < items && (uint32_t)(w[m] >> 32) != want) w[m] = fetch_tagged(src[m]);
     }
 #pragma unroll
     for (int m = 0; m < kPollPerThread; ++m) {
       const int it = t + kThreads * m;
       if (it < items) lds_stage[it] = __uint_as_float((uint32_t)w[m]);
     }
+    if (!done) lds_gave_up = 1;
     __syncthreads();
     if (t < n_out)
       for (int pp = 0; pp < pn; ++pp) vsum += lds_stage[pp * n_out + t];
+    const bool quit = lds_gave_up != 0;  // read beside the partials, tested after the barrier
     __syncthreads();
+    // Every thread of the workgroup leaves together when any thread gave up.
+    if (quit) {
+      if (t == 0) __hip_atomic_fetch_or(p.errors, kDecodeErrWaitTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
   }
   if (t < n_out) lds_v[t] = HET ? vsum * sk : vsum;
   __syncthreads();
@@ -476,7 +511,24 @@ hipError_t dispatch(int rank, int rb, const DecodeParams& p, int num_proj, hipSt
 
 }  // namespace
 
-bool decode_supported(int rank, int rb) { return rank * rb <= kThreads && (rb == 1 || rb == 4 || rb == 16); }
+hipError_t decode_error_word(uint32_t** word) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static uint32_t* addr[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(decode_errors));
+    if (e != hipSuccess) return e;
+    addr[dev] = static_cast<uint32_t*>(ptr);
+  }
+  *word = addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_decode(int dtype, int rank, int rb, const DecodeParams& p, int num_proj, hipStream_t stream) {
   return dtype == 1 ? dispatch<BF16>(rank, rb, p, num_proj, stream, nullptr, 0)

@@ -495,7 +495,6 @@ hipError_t launch_stage(int dtype, int rank, int stage, const MfmaParams& p, int
 
 }  // namespace
 
-bool mfma_supported(int rank) { return rank == 16 || rank == 32 || rank == 64; }
 
 hipError_t launch_mfma_shrink(int dtype, int rank, const MfmaParams& p, int num_proj, hipStream_t stream) {
   hipError_t e = launch_stage(dtype, rank, 0, p, num_proj, stream);

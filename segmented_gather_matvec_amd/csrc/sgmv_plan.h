@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "sgmv_shapes.h"
+
 namespace sgmv {
 
 // Vector (split-K) kernels: one template, two modes.
@@ -36,27 +38,11 @@ struct VecParams {
   int32_t direct_units;  // 1: unit u is segment u (every segment fits one row block)
 };
 
-// Rows of A_k covered by one pass of the shrink loop and columns of B_k covered
-// by one pass of the expand loop (two 128-bit loads per thread per pass).
-constexpr int vec_rows_per_pass(int rank) { return 256 * 2 * 8 / rank; }
-constexpr int vec_cols_per_pass(int rank) { return 256 * 2 * 8 / rank; }
-
 // Launch one vector kernel; returns the HIP error of the launch.
 hipError_t launch_vec(int dtype, int rank, int rb, int mode, const VecParams& p, hipStream_t stream);
 
-// One-launch decode kernel (shrink, on-chip hand-off, expand).
-// A_k rows (one 128-bit vector each) per thread.  Ranks 32 and 64 take 8, so
-// that H1 = 4096 needs 16 splits instead of 32 (a rank-64 batch of 32 rows
-// then fits on the device at once: 9.9 us instead of 23.6 us on the two-launch
-// route); rank 16 is fastest at 4 (8 was 0.1-0.8 us slower on every batch).
-constexpr int decode_rows_per_thread(int rank) { return rank >= 32 ? 8 : 4; }
-constexpr int kDecodeLanesPerColumn = 4;  // lanes sharing one 8-column vector of B_k
-constexpr int decode_max_kc(int rank) { return decode_rows_per_thread(rank) * 256 / (rank / 8); }
-constexpr int decode_max_cw() { return 256 / kDecodeLanesPerColumn * 8; }
-
 // One projection of a batched call (its own LoRA tables and output); the
 // projection of a workgroup is blockIdx.y.
-constexpr int kMaxProjections = 4;
 struct Projection {
   const uint64_t* A_ptrs;
   const uint64_t* B_ptrs;
@@ -81,17 +67,25 @@ struct DecodeParams {
   // launch covers all units when they fit on the device at once; otherwise the
   // host launches passes of round_units units.
   int32_t unit_base, round_units;
-  int32_t pad_;
+  // Longest wait for the unit's other partials, in ticks of the real-time
+  // counter (0: give up at once, a test hook).
+  uint32_t wait_ticks;
   const int32_t* seg_indptr;
   const int32_t* lora_idx;
   const int32_t* row_idx;  // null, or row of X / Y of each sorted row
   uint64_t* slots;      // projection 0: [num_units][splits][parts][RB*rank] tagged partials
   int64_t slot_stride;  // words between the slot areas of consecutive projections
   const uint16_t* X;
+  uint32_t* errors;     // device error word: kDecodeErrWaitTimeout is set by a wait that gave up
   Projection proj[kMaxProjections];
 };
 
-bool decode_supported(int rank, int rb);
+// Error bit of the device error word: a workgroup gave up waiting for the
+// partial sums of its unit (equal to SGMV_DEVICE_ERR_WAIT_TIMEOUT).
+constexpr uint32_t kDecodeErrWaitTimeout = 1u;
+// Address of the device error word on the current device (looked up once per
+// device with hipGetSymbolAddress).
+hipError_t decode_error_word(uint32_t** word);
 // Launches num_proj projections (blockIdx.y).
 hipError_t launch_decode(int dtype, int rank, int rb, const DecodeParams& p, int num_proj, hipStream_t stream);
 // Workgroups of the decode kernel variant that fit on the device at once (0 if
@@ -101,9 +95,6 @@ int decode_resident_capacity(int dtype, int rank, int rb, bool small, bool map, 
 
 // Matrix-core kernels for long segments: shrink (+ reduce of the H1 split),
 // then expand.
-constexpr int kMfmaRowsPerTile = 64;      // rows of one segment per shrink / expand workgroup
-constexpr int kMfmaColsPerTile = 128;     // output columns per expand chunk
-constexpr int kMfmaKChunk = 256;          // H1 granule of the shrink's split
 
 struct MfmaParams {
   int32_t n_rows, h_in, h_out, num_segs, num_loras;
@@ -122,7 +113,6 @@ struct MfmaParams {
   Projection proj[kMaxProjections];
 };
 
-bool mfma_supported(int rank);
 // Shrink into the partial planes, then reduce them into V (two launches).
 hipError_t launch_mfma_shrink(int dtype, int rank, const MfmaParams& p, int num_proj, hipStream_t stream);
 hipError_t launch_mfma_expand(int dtype, int rank, const MfmaParams& p, int num_proj, hipStream_t stream);
@@ -131,11 +121,6 @@ hipError_t launch_mfma_expand(int dtype, int rank, const MfmaParams& p, int num_
 // split-K partial planes of X @ W on the matrix cores (strips of strip_cols
 // columns) and of V = X @ A_k in one launch, then an epilogue that sums them,
 // adds V @ B_k and rounds once.
-constexpr int kBaseMaxRows = 64;
-constexpr int kBaseStageRows = 128;  // W rows per pipeline stage (kc is a multiple)
-// LDS of the packed-W partial kernel's X chunk (16-bit elements, 64 KiB):
-// rows (16 per row tile) x K chunk may not exceed it.
-constexpr int kBasePackedXElems = 32768;
 
 struct BaseParams {
   int32_t n_rows, h_in, h_out, num_segs, num_loras;

@@ -345,3 +345,19 @@ def test_base_workspace_covers_its_parts(kw):
     planes = need // (p.n_rows * (p.h_out + p.rank) * 4)
     assert planes >= 1
     assert need < (p.n_rows * p.h_out * 4) * (p.h_in // 128 + 1) + (64 << 20)
+
+
+def test_wait_limit_and_device_error_entry_points_check_arguments():
+    """The wait bound of the decode route and the device error query reject bad
+    arguments on the host (no device touched)."""
+    lib = sg.load_library()
+    assert lib.sgmv_set_wait_limit(-1) == sg.SGMV_ERR_INVALID_ARG
+    assert lib.sgmv_take_device_errors(None) == sg.SGMV_ERR_INVALID_ARG
+    assert lib.sgmv_set_wait_limit(250000) == sg.SGMV_OK
+    assert lib.sgmv_set_wait_limit(1000000) == sg.SGMV_OK
+    with pytest.raises(sg.SgmvError) as e:
+        sg.sgmv_set_wait_limit(-5)
+    assert e.value.status == sg.SGMV_ERR_INVALID_ARG
+    src = open(HEADER).read()
+    assert re.search(r"#define SGMV_DEVICE_ERR_WAIT_TIMEOUT 1u", src)
+    assert sg.SGMV_DEVICE_ERR_WAIT_TIMEOUT == 1

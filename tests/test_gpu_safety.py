@@ -1,0 +1,109 @@
+"""GPU tests of the decode route's safety contract, through the C ABI.
+
+* The wait of a decode-route workgroup for its unit's other partial sums is
+  bounded; the host's test hook (a wait limit of 0) makes every wait give up
+  at once, so the give-up path runs with every kernel exiting normally: Y is
+  left untouched and the device error word reports the timeout.  A later call
+  with the default limit is correct again.
+* The decode route's tagged slots live in a workspace area that no other
+  route writes: calls of the matrix-core and two-launch routes on the same
+  workspace (their fp32 partials could otherwise pose as tagged words), and a
+  workspace holding arbitrary bytes outside its counter area, leave the
+  decode route's result equal to the oracle's.
+Workload: the decode batch of the Punica README's throughput paragraph
+(page "Punica：多 LoRA 模型统一服务框架"), Distinct popularity, H = 4096, r = 16.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import segmented_gather_matvec_amd as sg
+import workloads
+from tests.gpu_cases import DeviceCall, assert_close, to_bits
+
+pytestmark = pytest.mark.gpu
+
+DEFAULT_WAIT_US = 1000000
+
+
+def decode_call(seed=2, n=32, h=4096):
+    w = workloads.decode_distinct(seed=seed, n=n, h=h)
+    call = DeviceCall(w.dtype, w.X, w.A, w.B, w.Y0, w.seg_indptr, w.lora_idx)
+    assert sg.sgmv_query_plan(call.problem).route == sg.SGMV_ROUTE_DECODE
+    return call
+
+
+def test_decode_wait_gives_up_under_the_test_hook_and_recovers():
+    import torch
+    call = decode_call()
+    assert sg.sgmv_take_device_errors() == 0
+    try:
+        sg.sgmv_set_wait_limit(0)
+        call.apply()
+        torch.cuda.synchronize()
+        assert sg.sgmv_take_device_errors() == sg.SGMV_DEVICE_ERR_WAIT_TIMEOUT
+        # every workgroup gave up before its expand: Y is untouched
+        assert np.array_equal(to_bits(call.Y), call.Y0h)
+        assert sg.sgmv_take_device_errors() == 0  # the query clears the word
+    finally:
+        sg.sgmv_set_wait_limit(DEFAULT_WAIT_US)
+    call.reset_y()
+    assert_close(to_bits(call.apply()), call.oracle_apply(), "f16")
+    assert sg.sgmv_take_device_errors() == 0
+
+
+def test_multi_pass_decode_gives_up_in_every_pass():
+    """A batch whose units do not all fit on the device at once runs in passes;
+    every pass takes the give-up path."""
+    import torch
+    call = decode_call(seed=9, n=512)   # more units than the device holds at once: passes
+    info = sg.sgmv_query_plan(call.problem)
+    assert info.route == sg.SGMV_ROUTE_DECODE and info.launches > 1, info.as_dict()
+    try:
+        sg.sgmv_set_wait_limit(0)
+        call.apply()
+        torch.cuda.synchronize()
+        assert sg.sgmv_take_device_errors() == sg.SGMV_DEVICE_ERR_WAIT_TIMEOUT
+        assert np.array_equal(to_bits(call.Y), call.Y0h)
+    finally:
+        sg.sgmv_set_wait_limit(DEFAULT_WAIT_US)
+    call.reset_y()
+    rows = np.r_[0:4, 250:266, 508:512]
+    mask = np.zeros(512, np.uint8)
+    mask[rows] = 1
+    assert_close(to_bits(call.apply()), call.oracle_apply(row_mask=mask), "f16", rows=rows)
+    assert sg.sgmv_take_device_errors() == 0
+
+
+def test_decode_slots_untouched_by_other_routes():
+    """One workspace serves the matrix-core route, the two-launch route and the
+    decode route in turn; the decode route's result is the oracle's."""
+    import torch
+    call = decode_call(seed=11)
+    mfma = DeviceCall("f16", call.Xh, call.Ah, call.Bh, call.Y0h, call.seg, call.lidx,
+                      variant=sg.SGMV_VARIANT_MFMA)
+    vec = DeviceCall("f16", call.Xh, call.Ah, call.Bh, call.Y0h, call.seg, call.lidx,
+                     variant=sg.SGMV_VARIANT_VECTOR)
+    nbytes = max(sg.sgmv_workspace_bytes(c.problem) for c in (call, mfma, vec))
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    ref = call.oracle_apply()
+    for c in (mfma, vec, call, mfma, call):
+        c.ws = ws
+        c.reset_y()
+        assert_close(to_bits(c.apply()), ref, "f16")
+    assert sg.sgmv_take_device_errors() == 0
+
+
+def test_decode_route_accepts_any_bytes_outside_the_counter_area():
+    import torch
+    call = decode_call(seed=12)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    n = call.ws.numel()
+    call.ws[sg.SGMV_WS_COUNTER_BYTES:] = torch.randint(0, 256, (n - sg.SGMV_WS_COUNTER_BYTES,), generator=g,
+                                                       device="cuda", dtype=torch.int32).to(torch.uint8)
+    ref = call.oracle_apply()
+    for _ in range(2):
+        call.reset_y()
+        assert_close(to_bits(call.apply()), ref, "f16")
+    assert sg.sgmv_take_device_errors() == 0
