@@ -245,6 +245,27 @@ sgmv_status_t sgmv_set_wait_limit(int64_t microseconds);
  * the device cannot be queried. */
 sgmv_status_t sgmv_take_device_errors(uint32_t* flags);
 
+/* ---- For callers that cannot allocate ----
+ *
+ * sgmv_lora_apply without a workspace argument, for callers that cannot call
+ * hipMalloc or hand over device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.  The call allocates nothing
+ * (no hipMalloc, hipFree or allocating library routine); its workspace is a
+ * static device array of the library, SGMV_NOALLOC_MAX_WORKSPACE bytes on
+ * every GPU the library runs on, held until the process ends.  Same
+ * arguments, results, preconditions and errors as sgmv_lora_apply, plus
+ * SGMV_ERR_WORKSPACE when sgmv_workspace_bytes(problem) exceeds
+ * SGMV_NOALLOC_MAX_WORKSPACE.  Every call on a GPU shares that GPU's array:
+ * calls that overlap on one GPU (other streams, other host threads) race on it
+ * and give unspecified results (decode-route calls may also report
+ * SGMV_DEVICE_ERR_WAIT_TIMEOUT); serialise them.  The array keeps the last
+ * call's contents; the call itself clears what must start at zero (with a
+ * fill kernel on `stream`, on the two-launch route only). */
+#define SGMV_NOALLOC_MAX_WORKSPACE ((size_t)16 << 20)
+sgmv_status_t sgmv_lora_apply_noalloc(const sgmv_problem_t* problem, const void* X,
+                                      const void* const* A_ptrs, const void* const* B_ptrs, void* Y,
+                                      const int32_t* seg_indptr, const int32_t* lora_idx, void* stream);
+
 /* One projection of a batched apply: its own LoRA tables and output.  All
  * pointers are device pointers, as in sgmv_lora_apply.
  *

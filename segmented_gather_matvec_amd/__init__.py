@@ -34,8 +34,10 @@ ENTRY_POINTS = ("sgmv_status_str", "sgmv_build_segments", "sgmv_check_problem",
                 "sgmv_check_segments", "sgmv_workspace_bytes", "sgmv_query_plan", "sgmv_shrink",
                 "sgmv_expand", "sgmv_lora_apply", "sgmv_lora_apply_batched", "sgmv_base_workspace_bytes",
                 "sgmv_base_lora_apply", "sgmv_base_packed_weight_bytes", "sgmv_base_pack_weight",
-                "sgmv_base_lora_apply_packed", "sgmv_set_wait_limit", "sgmv_take_device_errors")
+                "sgmv_base_lora_apply_packed", "sgmv_set_wait_limit", "sgmv_take_device_errors",
+                "sgmv_lora_apply_noalloc")
 SGMV_DEVICE_ERR_WAIT_TIMEOUT = 1
+SGMV_NOALLOC_MAX_WORKSPACE = 16 << 20
 
 
 class SgmvError(RuntimeError):
@@ -107,6 +109,7 @@ def load_library(path: str = LIB_PATH):
     lib.sgmv_base_lora_apply_packed.argtypes = [prob, P, P, P, P, P, P, P, P, SZ, P]
     lib.sgmv_set_wait_limit.argtypes = [ctypes.c_int64]
     lib.sgmv_take_device_errors.argtypes = [ctypes.POINTER(ctypes.c_uint32)]
+    lib.sgmv_lora_apply_noalloc.argtypes = [prob, P, P, P, P, P, P, P]
     for name in ENTRY_POINTS[1:]:
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -261,6 +264,19 @@ def sgmv_lora_apply(problem, X, A_ptrs, B_ptrs, Y, seg_indptr, lora_idx, ws, str
                                         ws.numel() * ws.element_size() if ws is not None else 0,
                                         _stream(stream))
     _check(st, "sgmv_lora_apply")
+
+
+def sgmv_lora_apply_noalloc(problem, X, A_ptrs, B_ptrs, Y, seg_indptr, lora_idx, stream=None):
+    """sgmv_lora_apply on the library's static device scratch (no workspace argument,
+    nothing allocated); calls that overlap on one GPU race.  Asynchronous."""
+    import torch
+    dt = _torch_dtype(problem)
+    _need(X, "X", dt); _need(Y, "Y", dt)
+    _need(A_ptrs, "A_ptrs", torch.int64); _need(B_ptrs, "B_ptrs", torch.int64)
+    _need(seg_indptr, "seg_indptr", torch.int32); _need(lora_idx, "lora_idx", torch.int32)
+    st = load_library().sgmv_lora_apply_noalloc(ctypes.byref(problem), _ptr(X), _ptr(A_ptrs), _ptr(B_ptrs),
+                                                _ptr(Y), _ptr(seg_indptr), _ptr(lora_idx), _stream(stream))
+    _check(st, "sgmv_lora_apply_noalloc")
 
 
 def sgmv_lora_apply_batched(problem, X, projections, seg_indptr, lora_idx, ws, row_idx=None, stream=None):

@@ -181,9 +181,11 @@ sgmv::Projection kernel_projection(const sgmv_projection_t& pj) {
 
 // sgmv_lora_apply for num_proj projections that share X, the shapes and the
 // segments.  Projection i uses the workspace slice [i*stride, i*stride + need).
+// clear_counters: zero the two-launch route's counters with a fill kernel
+// before its shrink (a workspace whose counter area may not be zero).
 sgmv_status_t apply(const sgmv_problem_t& p, const void* X, const sgmv_projection_t* pj, int np,
                     const int32_t* seg_indptr, const int32_t* lora_idx, const int32_t* row_idx, char* ws,
-                    size_t stride, hipStream_t s) {
+                    size_t stride, hipStream_t s, bool clear_counters = false) {
   bool het = false;
   for (int i = 0; i < np; ++i) het = het || pj[i].ranks || pj[i].scales;
   const int variant = decode_variant(p, row_idx != nullptr, het);
@@ -194,8 +196,8 @@ sgmv_status_t apply(const sgmv_problem_t& p, const void* X, const sgmv_projectio
     // run in one launch when all of them fit on the device at once.
     if (np > 1 && d.grid * np > decode_capacity(p.dtype, p.rank, d.rb, variant)) {
       for (int i = 0; i < np; ++i) {
-        const sgmv_status_t st =
-            apply(p, X, pj + i, 1, seg_indptr, lora_idx, row_idx, ws + (size_t)i * stride, stride, s);
+        const sgmv_status_t st = apply(p, X, pj + i, 1, seg_indptr, lora_idx, row_idx, ws + (size_t)i * stride,
+                                       stride, s, clear_counters);
         if (st != SGMV_OK) return st;
       }
       return SGMV_OK;
@@ -261,12 +263,39 @@ sgmv_status_t apply(const sgmv_problem_t& p, const void* X, const sgmv_projectio
     q.ranks = pj[i].ranks;
     q.scales = pj[i].scales;
     q.V = reinterpret_cast<float*>(wsi + need);
-    hipError_t e = sgmv::launch_vec(p.dtype, p.rank, v.rb, sgmv::kModeShrink, q, s);
+    hipError_t e = hipSuccess;
+    if (clear_counters) e = sgmv::launch_clear_u32(q.counters, 2 * v.num_units, s);
+    if (e != hipSuccess) return SGMV_ERR_HIP;
+    e = sgmv::launch_vec(p.dtype, p.rank, v.rb, sgmv::kModeShrink, q, s);
     if (e != hipSuccess) return SGMV_ERR_HIP;
     e = sgmv::launch_vec(p.dtype, p.rank, v.rb, sgmv::kModeExpand, q, s);
     if (e != hipSuccess) return SGMV_ERR_HIP;
   }
   return SGMV_OK;
+}
+
+// Static scratch of sgmv_lora_apply_noalloc: device memory of the library,
+// one copy on every GPU it runs on, held until the process ends.  In host code
+// the array's name is not a device address; the address of each device's copy
+// comes from hipGetSymbolAddress, once per device.
+__device__ __align__(256) unsigned char scratch[SGMV_NOALLOC_MAX_WORKSPACE];
+
+hipError_t scratch_address(char** out) {
+  static std::mutex mu;
+  static char* addr[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    char* ptr = nullptr;
+    e = hipGetSymbolAddress(reinterpret_cast<void**>(&ptr), HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = ptr;
+  }
+  *out = addr[dev];
+  return hipSuccess;
 }
 
 }  // namespace
@@ -393,6 +422,26 @@ sgmv_status_t sgmv_lora_apply(const sgmv_problem_t* p, const void* X, const void
                               const int32_t* lora_idx, void* ws, size_t ws_bytes, void* stream) {
   const sgmv_projection_t one{A_ptrs, B_ptrs, Y, nullptr, nullptr};
   return sgmv_lora_apply_batched(p, X, &one, 1, seg_indptr, lora_idx, nullptr, ws, ws_bytes, stream);
+}
+
+sgmv_status_t sgmv_lora_apply_noalloc(const sgmv_problem_t* p, const void* X, const void* const* A_ptrs,
+                                      const void* const* B_ptrs, void* Y, const int32_t* seg_indptr,
+                                      const int32_t* lora_idx, void* stream) {
+  sgmv_status_t st = sgmv_check_problem(p);
+  if (st != SGMV_OK) return st;
+  if (nothing_to_do(*p)) return SGMV_OK;
+  if (!X || !A_ptrs || !B_ptrs || !Y || !seg_indptr || !lora_idx) return SGMV_ERR_INVALID_ARG;
+  if (!aligned16(X) || !aligned16(Y) || !aligned8(A_ptrs) || !aligned8(B_ptrs)) return SGMV_ERR_UNSUPPORTED;
+  const size_t need = apply_ws_layout(*p).total;
+  if (need > (size_t)SGMV_NOALLOC_MAX_WORKSPACE) return SGMV_ERR_WORKSPACE;
+  char* ws = nullptr;
+  if (scratch_address(&ws) != hipSuccess) return SGMV_ERR_HIP;
+  const sgmv_projection_t one{A_ptrs, B_ptrs, Y, nullptr, nullptr};
+  // The scratch keeps the last call's contents: the two-launch route clears
+  // its counters itself; the decode route's tagged slots and the matrix-core
+  // route's planes need no initial value.
+  return apply(*p, X, &one, 1, seg_indptr, lora_idx, nullptr, ws, (size_t)round_up((int64_t)need, 256),
+               static_cast<hipStream_t>(stream), /*clear_counters=*/true);
 }
 
 sgmv_status_t sgmv_lora_apply_batched(const sgmv_problem_t* p, const void* X,

@@ -40,6 +40,8 @@ struct VecParams {
 
 // Launch one vector kernel; returns the HIP error of the launch.
 hipError_t launch_vec(int dtype, int rank, int rb, int mode, const VecParams& p, hipStream_t stream);
+// Zero n 32-bit words with a fill kernel on `stream` (graph-capturable).
+hipError_t launch_clear_u32(uint32_t* p, int64_t n, hipStream_t stream);
 
 // One projection of a batched call (its own LoRA tables and output); the
 // projection of a workgroup is blockIdx.y.

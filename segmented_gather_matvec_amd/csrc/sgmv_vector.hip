@@ -415,4 +415,18 @@ hipError_t launch_vec(int dtype, int rank, int rb, int mode, const VecParams& p,
                     : launch_rank<F16>(rank, rb, mode, p, stream);
 }
 
+namespace {
+__global__ __launch_bounds__(kThreads) void clear_u32_kernel(uint32_t* p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+}  // namespace
+
+hipError_t launch_clear_u32(uint32_t* p, int64_t n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = (n + kThreads - 1) / kThreads;
+  hipLaunchKernelGGL(clear_u32_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p, n);
+  return hipGetLastError();
+}
+
 }  // namespace sgmv
