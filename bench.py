@@ -145,6 +145,12 @@ HET_WORKLOADS = ["decode_mixedrank_h4096_r64_b32"]
 BASE_WORKLOADS = ["base_decode_distinct_h4096_r16_b32", "base_decode_distinct_h4096_r16_b8",
                   "base_decode_distinct_h4096_r16_b64", "base_decode_distinct_h11008to4096_r16_b32"]
 BASE_WORKLOADS += [w.replace("base_", "base_packed_", 1) for w in BASE_WORKLOADS]
+# One GPU's shard of a tensor-parallel layer over 8 GPUs (H = 4096): the
+# column-parallel shard (W[:, slice], B_k[:, slice]: 4096 -> 512, the ordinary
+# call) and the row-parallel shard (W[slice, :], A_k[slice, :]: 512 -> 4096,
+# sgmv_base_lora_apply_partial, fp32 partial output for the layer's all-reduce).
+BASE_WORKLOADS += ["base_decode_distinct_h4096to512_r16_b32", "base_partial_decode_distinct_h512to4096_r16_b32",
+                   "base_packed_decode_distinct_h4096to512_r16_b32"]
 
 
 class SingleCallBench:
@@ -715,6 +721,101 @@ def latency_curve(batches=(1, 2, 4, 8, 16, 32, 64), steps=200, warmup=20):
             "curve": curve}
 
 
+def base_rows_curve(batches=(8, 16, 32, 64, 128, 256, 512, 1024), steps=160):
+    """The base projection with the LoRA term, Y = X @ W + (X @ A_k) @ B_k, against
+    the number of rows (Punica README, page "Punica：多 LoRA 模型统一服务框架",
+    LoRA and multi-LoRA paragraphs).  H1 = H2 = 4096, r = 16, fp16, Distinct
+    LoRAs (every row its own).  Per batch size n, device time per call from 16
+    calls replayed out of a captured HIP graph (weights rotate through >= 1 GiB):
+      torch_gemm_us            torch.matmul(X, W) written to Y (the base layer alone)
+      torch_gemm_plus_sgmv_us  that GEMM, then sgmv_lora_apply adding the LoRA term
+      fused_us                 sgmv_base_lora_apply (n <= 64 only), one rounding
+      fused_packed_us          sgmv_base_lora_apply_packed on W packed beforehand
+    with the HBM floor of streaming W once (w_floor_us, 8 TB/s) and the matrix-core
+    floor of the GEMM's flops (gemm_flop_floor_us, 2.5 PFLOP/s fp16)."""
+    import torch
+    import segmented_gather_matvec_amd as sg
+    import workloads as wl
+
+    H, r = 4096, 16
+    Ws = wl.device_normal((16, H, H), H ** -0.5, "f16", 7301)
+    Wps = [sg.pack_base_weight(Ws[i]) for i in range(16)]
+    lib = sg.load_library()
+    sid = lambda: torch.cuda.current_stream().cuda_stream  # noqa: E731
+    curve = []
+    for n in batches:
+        P = max(n, 64) * 4
+        A = wl.device_normal((P, H, r), H ** -0.5, "f16", 7400 + n)
+        B = wl.device_normal((P, r, H), r ** -0.5, "f16", 7500 + n)
+        X = wl.device_normal((16, n, H), 1.0, "f16", 7600 + n)
+        Y = torch.zeros((16, n, H), dtype=torch.float16, device="cuda")
+        tables = P // n
+        phys = torch.arange(tables * n, device="cuda", dtype=torch.int64).view(tables, n)
+        A_tab = (A.data_ptr() + phys * (H * r * 2)).contiguous()
+        B_tab = (B.data_ptr() + phys * (r * H * 2)).contiguous()
+        seg = torch.arange(n + 1, dtype=torch.int32, device="cuda")
+        lidx = torch.arange(n, dtype=torch.int32, device="cuda")
+        prob = sg.make_problem("f16", n, H, H, r, n, n, 1)
+        ws = sg.new_workspace(prob)
+        bws = sg.new_base_workspace(prob) if n <= 64 else None
+        pb = ctypes.byref(prob)
+
+        def gemm(c):
+            torch.matmul(X[c % 16], Ws[c % 16], out=Y[c % 16])
+
+        def gemm_sgmv(c):
+            gemm(c)
+            st = lib.sgmv_lora_apply(pb, X[c % 16].data_ptr(), A_tab[c % tables].data_ptr(),
+                                     B_tab[c % tables].data_ptr(), Y[c % 16].data_ptr(), seg.data_ptr(),
+                                     lidx.data_ptr(), ws.data_ptr(), ws.numel(), sid())
+            if st != 0:
+                raise RuntimeError(sg.sgmv_status_str(st))
+
+        def fused_with(fn, W):
+            def run(c):
+                st = fn(pb, X[c % 16].data_ptr(), W[c % 16].data_ptr(), A_tab[c % tables].data_ptr(),
+                        B_tab[c % tables].data_ptr(), Y[c % 16].data_ptr(), seg.data_ptr(), lidx.data_ptr(),
+                        bws.data_ptr(), bws.numel(), sid())
+                if st != 0:
+                    raise RuntimeError(sg.sgmv_status_str(st))
+            return run
+
+        methods = {"torch_gemm": gemm, "torch_gemm_plus_sgmv": gemm_sgmv}
+        if n <= 64:
+            methods["fused"] = fused_with(lib.sgmv_base_lora_apply, Ws)
+            methods["fused_packed"] = fused_with(lib.sgmv_base_lora_apply_packed, Wps)
+        row = {"rows": n, "w_floor_us": round(2 * H * H / 8e12 * 1e6, 3),
+               "gemm_flop_floor_us": round(2 * n * H * H / 2.5e15 * 1e6, 3)}
+        for name, fn in methods.items():
+            for c in range(16):
+                fn(c)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for c in range(16):
+                    fn(c)
+            g.replay()
+            torch.cuda.synchronize()
+            reps = max(1, steps // 16)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            row[name + "_us"] = round(e0.elapsed_time(e1) * 1e3 / (reps * 16), 3)
+            del g
+        for name in ("fused", "fused_packed"):
+            row.setdefault(name + "_us", None)
+        curve.append(row)
+        print(json.dumps(row), file=sys.stderr, flush=True)
+        del A, B, X, Y, A_tab, B_tab, ws, bws
+    return {"metric": "base projection with the LoRA term: fused call vs torch GEMM + SGMV, device time per call",
+            "unit": "us", "higher_is_better": False, "dtype": "f16", "data": "synthetic",
+            "config": {"workload": "base_rows_curve_h4096_r16_distinct", "h_in": H, "h_out": H, "rank": r,
+                       "steps": steps},
+            "curve": curve}
+
+
 def cpu_baseline(seconds=10.0, threads=0):
     """The oracle as it stands, on a host copy of the headline workload's shape
     (threads: 0 = every host core OpenMP offers)."""
@@ -740,7 +841,9 @@ def cpu_baseline(seconds=10.0, threads=0):
 
 class BaseBench:
     """One sgmv_base_lora_apply call per step: Y = X @ W + (X @ A_k) @ B_k for a
-    Distinct decode batch (row i -> LoRA i), fp16.  W rotates through >= 1 GiB of
+    Distinct decode batch (row i -> LoRA i), fp16.  "base_partial_" workloads
+    run sgmv_base_lora_apply_partial instead: the same product written as an
+    unrounded fp32 partial, one shard of a row-parallel layer.  W rotates through >= 1 GiB of
     copies, the LoRAs through a >= 1 GiB pool and X / Y through 64 copies, so no
     step finds its weights in the 256 MB Infinity Cache.  For context the config
     also carries the unfused composition on the same buffers: torch's X @ W
@@ -753,10 +856,11 @@ class BaseBench:
         import segmented_gather_matvec_amd as sg
         import workloads as wl
 
-        m = re.fullmatch(r"base_(packed_)?decode_distinct_h(\d+)(?:to(\d+))?_r(\d+)_b(\d+)", name)
+        m = re.fullmatch(r"base_(packed_|partial_)?decode_distinct_h(\d+)(?:to(\d+))?_r(\d+)_b(\d+)", name)
         if not m:
             raise SystemExit(f"unknown workload {name}")
-        self.packed = m.group(1) is not None
+        self.packed = m.group(1) == "packed_"
+        self.partial = m.group(1) == "partial_"
         self.name, self.sg, self.torch = name, sg, torch
         self.dtype = "f16"
         self.h_in = int(m.group(2))
@@ -775,7 +879,8 @@ class BaseBench:
         self.B = wl.device_normal((self.tables * self.n, self.rank, self.h_out), self.rank ** -0.5, self.dtype,
                                   s0 + 2)
         self.X = wl.device_normal((self.copies, self.n, self.h_in), 1.0, self.dtype, s0 + 3)
-        self.Y = torch.zeros((self.copies, self.n, self.h_out), dtype=self.X.dtype, device="cuda")
+        self.Y = torch.zeros((self.copies, self.n, self.h_out), dtype=torch.float32 if self.partial else self.X.dtype,
+                             device="cuda")
         idx = torch.arange(self.tables * self.n, dtype=torch.int64, device="cuda").view(self.tables, self.n)
         self.A_tab = (self.A.data_ptr() + idx * (self.h_in * self.rank * e)).contiguous()
         self.B_tab = (self.B.data_ptr() + idx * (self.rank * self.h_out * e)).contiguous()
@@ -785,12 +890,14 @@ class BaseBench:
         self.lidx = torch.from_numpy(self.lidx_h).cuda()
         self.problem = sg.make_problem(self.dtype, self.n, self.h_in, self.h_out, self.rank, self.n, self.n, 1)
         self.ws = sg.new_base_workspace(self.problem)
-        self.bytes = e * (self.h_in * self.h_out + self.n * (self.h_in + self.h_out) * self.rank
-                          + self.n * self.h_in + self.n * self.h_out)
+        self.bytes = (e * (self.h_in * self.h_out + self.n * (self.h_in + self.h_out) * self.rank + self.n * self.h_in)
+                      + (4 if self.partial else e) * self.n * self.h_out)
         self.rows_per_step = self.n
         self.calls_per_step = 1
         self.fn = sg.load_library().sgmv_base_lora_apply
         Wsrc = self.W
+        if self.partial:
+            self.fn = sg.load_library().sgmv_base_lora_apply_partial
         if self.packed:
             self.fn = sg.load_library().sgmv_base_lora_apply_packed
             Wsrc = torch.stack([sg.pack_base_weight(self.W[w]) for w in range(self.wcopies)])
@@ -799,10 +906,11 @@ class BaseBench:
         self.args = []
         for c in range(max(self.wcopies, self.tables, self.copies)):
             w, t, x = c % self.wcopies, c % self.tables, c % self.copies
-            self.args.append((pb, self.X[x].data_ptr(), Wsrc[w].data_ptr(), self.A_tab[t].data_ptr(),
-                              self.B_tab[t].data_ptr(), self.Y[x].data_ptr(), self.seg.data_ptr(),
-                              self.lidx.data_ptr(), self.ws.data_ptr(), self.ws.numel()))
-        self.unfused = self.time_unfused()
+            head = (pb, self.X[x].data_ptr(), Wsrc[w].data_ptr()) + ((0,) if self.partial else ())
+            self.args.append(head + (self.A_tab[t].data_ptr(), self.B_tab[t].data_ptr(), self.Y[x].data_ptr(),
+                                     self.seg.data_ptr(), self.lidx.data_ptr(), self.ws.data_ptr(), self.ws.numel()))
+        # (a shard's fp32 partial has no torch counterpart of the same semantics)
+        self.unfused = None if self.partial else self.time_unfused()
         torch.cuda.synchronize()
 
     def step(self, c, stream):
@@ -851,7 +959,8 @@ class BaseBench:
             self.Y[x].fill_(float("nan"))
             self.step(c, sid)
             torch.cuda.synchronize()
-            got = oracle.decode(_bits(self.Y[x]), self.dtype)
+            got = (self.Y[x].cpu().numpy().astype(np.float64) if self.partial
+                   else oracle.decode(_bits(self.Y[x]), self.dtype))
             ref = oracle.sgmv_base_apply(self.dtype, _bits(self.X[x]), _bits(self.W[w]), A, B, self.seg_h,
                                          self.lidx_h)
             worst = max(worst, float((np.abs(got - ref) / (1e-3 + 1e-2 * np.abs(ref))).max()))
@@ -863,9 +972,10 @@ class BaseBench:
         return {"workload": self.name, "h_in": self.h_in, "h_out": self.h_out, "rank": self.rank,
                 "batch_rows": self.n, "segments": self.n, "distinct_loras": self.n, "w_copies": self.wcopies,
                 "lora_tables": self.tables, "xy_copies": self.copies, "algorithmic_bytes_per_step": self.bytes,
-                "output": "Y = X @ W + LoRA term (written, one rounding)",
+                "output": ("fp32 partial X_g @ W_g + LoRA term of one row-parallel shard (written, unrounded)"
+                           if self.partial else "Y = X @ W + LoRA term (written, one rounding)"),
                 "weight_layout": "packed once before timing" if self.packed else "row-major",
-                "unfused_torch_matmul_plus_sgmv_us_per_call": round(self.unfused, 3)}
+                "unfused_torch_matmul_plus_sgmv_us_per_call": None if self.unfused is None else round(self.unfused, 3)}
 
 
 def main():
@@ -886,6 +996,9 @@ def main():
     ap.add_argument("--curve", action="store_true",
                     help="instead of one workload: the LoRA addend's latency against batch size for "
                          "SGMV and two naive LoRA implementations (one JSON line)")
+    ap.add_argument("--base-rows-curve", action="store_true",
+                    help="instead of one workload: the base projection with the LoRA term against the "
+                         "number of rows, fused call vs torch GEMM + SGMV (one JSON line)")
     ap.add_argument("--graph", action="store_true",
                     help="replay the timed steps from a captured HIP graph instead of eager launches")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -915,6 +1028,9 @@ def main():
         torch.cuda.empty_cache()
     if args.curve:
         print(json.dumps(latency_curve()), flush=True)
+        return
+    if args.base_rows_curve:
+        print(json.dumps(base_rows_curve()), flush=True)
         return
     variant = {"auto": 0, "vector": 1, "fused": 2, "mfma": 3}[args.variant]
     model = args.workload in MODEL_WORKLOADS

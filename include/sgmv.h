@@ -386,6 +386,32 @@ sgmv_status_t sgmv_base_lora_apply_packed(const sgmv_problem_t* problem, const v
                                           const int32_t* seg_indptr, const int32_t* lora_idx, void* ws,
                                           size_t ws_bytes, void* stream);
 
+/* One shard of a row-parallel (H1-split) base layer: the same product written
+ * as an unrounded fp32 partial.  The LoRA paragraph's output x@W + x@A@B is
+ * linear in x over any split of H1 into slices g: x@W = sum_g x_g@W_g and
+ * x@A@B = (sum_g x_g@A_g)@B = sum_g (x_g@A_g)@B.  A device holding slice g of a
+ * layer whose input is split along H1 computes
+ *     Yp[i, :] = X_g[i, :] @ W_g + (X_g[i, :] @ A_{k,g}) @ B_k      (fp32, written)
+ * for every row i (rows no segment covers get X_g[i, :] @ W_g), and the layer's
+ * existing all-reduce sums the shards' Yp; rounding the sum once to the input
+ * format gives the one-rounding output of sgmv_base_lora_apply.
+ *   problem   h_in = the slice's width, h_out = the full H2; other fields as for
+ *             sgmv_base_lora_apply (n_rows <= 64).
+ *   X, W      device X_g [n_rows, h_in] and W_g [h_in, h_out] (rows of W in the
+ *             slice), row-major, or W_g in the packed layout of
+ *             sgmv_base_pack_weight when w_packed = 1 (0: row-major).
+ *   A_ptrs    [num_loras] device pointers to A_{k,g}, the slice's rows of A_k:
+ *             [h_in, rank] row-major (A_k's own storage at row offset g * h_in).
+ *   B_ptrs    [num_loras] device pointers to the whole B_k [rank, h_out].
+ *   Yp        device fp32 [n_rows, h_out], 16-byte aligned, written.
+ *   ws        as for sgmv_base_lora_apply (sgmv_base_workspace_bytes).
+ * Errors as for sgmv_base_lora_apply; SGMV_ERR_INVALID_ARG for w_packed other
+ * than 0 or 1. */
+sgmv_status_t sgmv_base_lora_apply_partial(const sgmv_problem_t* problem, const void* X, const void* W,
+                                           int32_t w_packed, const void* const* A_ptrs,
+                                           const void* const* B_ptrs, float* Yp, const int32_t* seg_indptr,
+                                           const int32_t* lora_idx, void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

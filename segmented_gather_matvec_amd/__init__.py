@@ -35,7 +35,7 @@ ENTRY_POINTS = ("sgmv_status_str", "sgmv_build_segments", "sgmv_check_problem",
                 "sgmv_expand", "sgmv_lora_apply", "sgmv_lora_apply_batched", "sgmv_base_workspace_bytes",
                 "sgmv_base_lora_apply", "sgmv_base_packed_weight_bytes", "sgmv_base_pack_weight",
                 "sgmv_base_lora_apply_packed", "sgmv_set_wait_limit", "sgmv_take_device_errors",
-                "sgmv_lora_apply_noalloc")
+                "sgmv_lora_apply_noalloc", "sgmv_base_lora_apply_partial")
 SGMV_DEVICE_ERR_WAIT_TIMEOUT = 1
 SGMV_NOALLOC_MAX_WORKSPACE = 16 << 20
 
@@ -110,6 +110,7 @@ def load_library(path: str = LIB_PATH):
     lib.sgmv_set_wait_limit.argtypes = [ctypes.c_int64]
     lib.sgmv_take_device_errors.argtypes = [ctypes.POINTER(ctypes.c_uint32)]
     lib.sgmv_lora_apply_noalloc.argtypes = [prob, P, P, P, P, P, P, P]
+    lib.sgmv_base_lora_apply_partial.argtypes = [prob, P, P, I32, P, P, P, P, P, P, SZ, P]
     for name in ENTRY_POINTS[1:]:
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -343,6 +344,23 @@ def sgmv_base_lora_apply(problem, X, W, A_ptrs, B_ptrs, Y, seg_indptr, lora_idx,
     """Y[i] = X[i] @ W + (X[i] @ A_k) @ B_k on the device (Y written, rounded once); asynchronous.
     Rows no segment covers get X[i] @ W.  At most 64 rows."""
     _base_apply("sgmv_base_lora_apply", problem, X, W, A_ptrs, B_ptrs, Y, seg_indptr, lora_idx, ws, stream)
+
+
+def sgmv_base_lora_apply_partial(problem, X, W, A_ptrs, B_ptrs, Yp, seg_indptr, lora_idx, ws, w_packed=False,
+                                 stream=None):
+    """One shard of a row-parallel base layer: Yp[i] = X_g[i] @ W_g + (X_g[i] @ A_{k,g}) @ B_k in
+    fp32, unrounded (Yp float32 [n_rows, h_out]); W_g row-major or packed (w_packed)."""
+    import torch
+    dt = _torch_dtype(problem)
+    _need(X, "X", dt); _need(W, "W", dt); _need(Yp, "Yp", torch.float32)
+    _need(A_ptrs, "A_ptrs", torch.int64); _need(B_ptrs, "B_ptrs", torch.int64)
+    _need(seg_indptr, "seg_indptr", torch.int32); _need(lora_idx, "lora_idx", torch.int32)
+    _need(ws, "ws")
+    st = load_library().sgmv_base_lora_apply_partial(
+        ctypes.byref(problem), _ptr(X), _ptr(W), 1 if w_packed else 0, _ptr(A_ptrs), _ptr(B_ptrs), _ptr(Yp),
+        _ptr(seg_indptr), _ptr(lora_idx), _ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0,
+        _stream(stream))
+    _check(st, "sgmv_base_lora_apply_partial")
 
 
 def sgmv_base_packed_weight_bytes(h_in: int, h_out: int) -> int:

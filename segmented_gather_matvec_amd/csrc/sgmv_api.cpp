@@ -74,35 +74,31 @@ int decode_capacity(int dtype, int rank, int rb, int variant) {
   return cache[dev][dtype][ri][bi][variant];
 }
 
-// Passes (launches) of the decode kernel over the units beyond which the
-// two-launch route is taken instead (Distinct batches, H = 4096, r = 16: 256
-// rows in 2 passes 20.0 us against 27.4 us; 512 rows in 4 passes 40.2 against
-// 43.2 us).
-constexpr int64_t kMaxDecodeRounds = 4;
-
 // The first candidate whose grid is co-resident on the current device (the
 // kernel's workgroups wait for each other; the capacity is the launched
 // variant's, see decode_variant).  When none is, the smallest row block runs
 // in passes: launches of the largest co-resident grid, each over the next
 // round_units units, up to kMaxDecodeRounds; else unsupported.
+// (kMaxDecodeRounds: Distinct batches, H = 4096, r = 16, took 512 rows in 4
+// passes in 40.2 us against 43.2 us on the two-launch route.)
 DecodePlan plan_decode(const sgmv_problem_t& p, int variant) {
   DecodePlan c[3];
   const int n = decode_candidates(p, c);
   for (int i = 0; i < n; ++i) {
     const int cap = decode_capacity(p.dtype, p.rank, c[i].rb, variant);
-    if (cap > 0 && c[i].grid <= cap) return c[i];
+    if (cap > 0 && c[i].grid <= cap && c[i].grid <= kMaxResidentGrid) return c[i];
   }
   // (Batches with long segments go to the matrix-core kernels instead.)
   if (n > 0 && !stage_uses_mfma(p)) {
     DecodePlan d = c[0];
     const int64_t cap = decode_capacity(p.dtype, p.rank, d.rb, variant);
     const int64_t step = d.split_major ? 1 : 8;  // the XCD mapping covers units 8 at a time
-    const int64_t ru = cap / d.splits / step * step;
+    const int64_t ru = std::min(cap, kMaxResidentGrid) / d.splits / step * step;
     if (ru >= step) {
       d.round_units = ru;
       d.grid = ru * d.splits;
       d.rounds = ceil_div(d.num_units, ru);
-      if (d.rounds <= kMaxDecodeRounds) return d;
+      if (d.rounds <= kMaxDecodeRounds && d.num_units * d.splits <= kMaxDecodeRounds * kMaxResidentGrid) return d;
     }
   }
   return DecodePlan{};
@@ -244,6 +240,7 @@ sgmv_status_t apply(const sgmv_problem_t& p, const void* X, const sgmv_projectio
     q.partials = reinterpret_cast<float*>(ws + SGMV_WS_COUNTER_BYTES);
     q.V = reinterpret_cast<float*>(ws + SGMV_WS_COUNTER_BYTES + m.partial_bytes);
     q.proj_stride = (int64_t)(stride / sizeof(float));
+    q.fold_planes = m.fold;
     hipError_t e = sgmv::launch_mfma_shrink(p.dtype, p.rank, q, np, s);
     if (e != hipSuccess) return SGMV_ERR_HIP;
     return hip_status(sgmv::launch_mfma_expand(p.dtype, p.rank, q, np, s));
@@ -375,7 +372,7 @@ sgmv_status_t sgmv_query_plan(const sgmv_problem_t* p, sgmv_plan_info_t* info) {
       break;
     case SGMV_ROUTE_MFMA: {
       const MfmaPlan m = plan_mfma(*p);
-      info->launches = 3;
+      info->launches = m.fold ? 2 : 3;
       info->rows_per_unit = sgmv::kMfmaRowsPerTile;
       info->units = (int32_t)m.units64;
       info->splits = m.ksplit;
@@ -474,18 +471,20 @@ sgmv_status_t sgmv_lora_apply_batched(const sgmv_problem_t* p, const void* X,
 
 namespace {
 
+// Yf (non-null): write the fp32 sum unrounded into Yf instead of rounding it into Y.
 sgmv_status_t base_apply(const sgmv_problem_t* p, const void* X, const void* W, bool packed,
                          const void* const* A_ptrs, const void* const* B_ptrs, void* Y,
                          const int32_t* seg_indptr, const int32_t* lora_idx, void* ws, size_t ws_bytes,
-                         void* stream) {
+                         void* stream, float* Yf = nullptr) {
   sgmv_status_t st = sgmv_check_problem(p);
   if (st != SGMV_OK) return st;
   if (p->n_rows > sgmv::kBaseMaxRows) return SGMV_ERR_UNSUPPORTED;
   if (p->n_rows == 0) return SGMV_OK;
-  if (!X || !W || !Y) return SGMV_ERR_INVALID_ARG;
+  if (!X || !W || (!Y && !Yf)) return SGMV_ERR_INVALID_ARG;
   const bool lora = !nothing_to_do(*p);
   if (lora && (!A_ptrs || !B_ptrs || !seg_indptr || !lora_idx)) return SGMV_ERR_INVALID_ARG;
-  if (!aligned16(X) || !aligned16(W) || !aligned16(Y)) return SGMV_ERR_UNSUPPORTED;
+  if (!aligned16(X) || !aligned16(W) || !aligned16(Yf ? static_cast<const void*>(Yf) : Y))
+    return SGMV_ERR_UNSUPPORTED;
   if (lora && (!aligned8(A_ptrs) || !aligned8(B_ptrs))) return SGMV_ERR_UNSUPPORTED;
   const BasePlan b = plan_base(*p, packed);
   if (!ws || ws_bytes < b.total) return SGMV_ERR_WORKSPACE;
@@ -515,7 +514,8 @@ sgmv_status_t base_apply(const sgmv_problem_t* p, const void* X, const void* W, 
   q.vpartials = lora ? reinterpret_cast<float*>(w + b.v_off) : nullptr;
   q.row_b = lora ? reinterpret_cast<uint64_t*>(w + b.b_off) : nullptr;
   q.partials = reinterpret_cast<float*>(w + b.p_off);
-  q.Y = static_cast<uint16_t*>(Y);
+  q.Y = Yf ? nullptr : static_cast<uint16_t*>(Y);
+  q.Yf = Yf;
   return hip_status(sgmv::launch_base(p->dtype, p->rank, q, s));
 }
 
@@ -537,6 +537,16 @@ sgmv_status_t sgmv_base_pack_weight(const void* W, int32_t h_in, int32_t h_out, 
   if (!aligned2(W) || !aligned16(Wp)) return SGMV_ERR_UNSUPPORTED;
   return hip_status(sgmv::launch_base_pack(static_cast<const uint16_t*>(W), h_in, h_out,
                                            static_cast<uint16_t*>(Wp), static_cast<hipStream_t>(stream)));
+}
+
+sgmv_status_t sgmv_base_lora_apply_partial(const sgmv_problem_t* p, const void* X, const void* W,
+                                           int32_t w_packed, const void* const* A_ptrs,
+                                           const void* const* B_ptrs, float* Yp, const int32_t* seg_indptr,
+                                           const int32_t* lora_idx, void* ws, size_t ws_bytes, void* stream) {
+  if (w_packed != 0 && w_packed != 1) return SGMV_ERR_INVALID_ARG;
+  if (!Yp) return SGMV_ERR_INVALID_ARG;
+  return base_apply(p, X, W, w_packed == 1, A_ptrs, B_ptrs, nullptr, seg_indptr, lora_idx, ws, ws_bytes, stream,
+                    Yp);
 }
 
 sgmv_status_t sgmv_base_lora_apply_packed(const sgmv_problem_t* p, const void* X, const void* Wp,

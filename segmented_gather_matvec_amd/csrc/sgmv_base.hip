@@ -444,7 +444,7 @@ __global__ __launch_bounds__(64) void sgmv_base_epilogue_kernel(BaseParams p) {
   const int i = blockIdx.y;
   const bool bad = (p.n_rows | p.h_out | p.num_segs | p.num_loras | (p.ksplit - 1) |
                     (int32_t)(p.plane_stride >> 32)) < 0;
-  const bool bad_ptr = (p.partials == nullptr) | (p.Y == nullptr);
+  const bool bad_ptr = (p.partials == nullptr) | (p.Y == nullptr && p.Yf == nullptr);
   if (bad | bad_ptr || i >= p.n_rows) return;
   const int c = blockIdx.x * 512 + lane * 8;
   const bool col_ok = c < p.h_out;
@@ -542,7 +542,16 @@ __global__ __launch_bounds__(64) void sgmv_base_epilogue_kernel(BaseParams p) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) y[e] += s[e];
   }
-  if (col_ok) store_vec(p.Y + (int64_t)i * p.h_out + c, pack8<T>(y));
+  if (!col_ok) return;
+  if (p.Yf != nullptr) {
+    // A shard's partial output: fp32, unrounded (summed across shards, then
+    // rounded once, by the caller).
+    float* yf = p.Yf + (int64_t)i * p.h_out + c;
+    *reinterpret_cast<f32x4*>(yf) = f32x4{y[0], y[1], y[2], y[3]};
+    *reinterpret_cast<f32x4*>(yf + 4) = f32x4{y[4], y[5], y[6], y[7]};
+  } else {
+    store_vec(p.Y + (int64_t)i * p.h_out + c, pack8<T>(y));
+  }
 }
 
 // Grid: shrink_grid shrink workgroups (n_rows * ksplit rounded up to a

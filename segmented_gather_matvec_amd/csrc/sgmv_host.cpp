@@ -99,8 +99,13 @@ int decode_candidates(const sgmv_problem_t& p, DecodePlan out[3]) {
 size_t decode_slot_bytes(const sgmv_problem_t& p) {
   DecodePlan c[3];
   const int n = decode_candidates(p, c);
+  // With long segments the decode route is taken only when one launch holds
+  // every unit; otherwise the smallest row block may run in passes.
+  const int64_t limit = stage_uses_mfma(p) ? kMaxResidentGrid : kMaxDecodeRounds * kMaxResidentGrid;
   size_t b = 0;
-  for (int i = 0; i < n; ++i) b = std::max(b, c[i].slot_bytes);
+  for (int i = 0; i < n; ++i)
+    if (c[i].grid <= limit || (i == 0 && !stage_uses_mfma(p) && c[i].num_units * c[i].splits <= limit))
+      b = std::max(b, c[i].slot_bytes);
   return b;
 }
 
@@ -122,6 +127,9 @@ constexpr int kMfmaExpandTarget = 1024;
 constexpr int kMfmaShortTileRows = 32;   // mean rows per 64-row tile below which tiles count as short
 constexpr int kMfmaShortExpandRows = 16; // expand tile rows for short tiles
 constexpr int kMfmaShortChunksPerWg = 3;
+// Up to this many partial planes the expand sums them itself and the reduce
+// launch is skipped.
+constexpr int kMfmaFoldPlanes = 8;
 
 MfmaPlan plan_mfma(const sgmv_problem_t& p) {
   MfmaPlan m;
@@ -154,6 +162,7 @@ MfmaPlan plan_mfma(const sgmv_problem_t& p) {
     m.chunks_per_wg = (int)ceil_div(nchunks, groups);
   }
   m.partial_bytes = (size_t)m.ksplit * (size_t)p.n_rows * p.rank * sizeof(float);
+  m.fold = m.ksplit <= kMfmaFoldPlanes ? 1 : 0;
   return m;
 }
 

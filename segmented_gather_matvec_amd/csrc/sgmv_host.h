@@ -65,7 +65,15 @@ struct DecodePlan {
 DecodePlan plan_decode_rb(const sgmv_problem_t& p, int rb, int split_major);
 // Candidate decode plans, smallest row block first; returns how many.
 int decode_candidates(const sgmv_problem_t& p, DecodePlan out[3]);
-// Slot bytes of the largest candidate.
+// Passes (launches) of the decode kernel over the units beyond which the
+// two-launch route is taken instead.
+constexpr int64_t kMaxDecodeRounds = 4;
+// Upper bound on the workgroups any supported device holds at once (8 per CU
+// on 1024 CUs; an MI355X holds at most 2048): a decode plan whose launch
+// exceeds it is never taken.
+constexpr int64_t kMaxResidentGrid = 8192;
+// Slot bytes of the largest candidate the decode route can take (on any
+// device): the workspace is sized for it.
 size_t decode_slot_bytes(const sgmv_problem_t& p);
 
 // The matrix-core kernels take a stage when AUTO sees a segment longer than
@@ -83,6 +91,7 @@ struct MfmaPlan {
   int64_t units_x = 0;                        // expand units of <= expand_rows rows
   int direct_x = 1;
   size_t partial_bytes = 0;  // split partials of V, fp32 [ksplit][n_rows][rank]
+  int fold = 0;              // 1: the expand sums the partial planes (no reduce launch)
 };
 MfmaPlan plan_mfma(const sgmv_problem_t& p);
 

@@ -283,9 +283,11 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_expand_kernel(MfmaParams p
   const Projection pj = p.proj[blockIdx.y];
   // Malformed launch test; it also batches the argument loads (as in the shrink).
   const bool bad_size = (p.n_rows | p.h_out | p.num_segs | p.num_loras | p.num_units_x | p.direct_units_x |
-                         (p.chunks_per_wg - 1) | (int32_t)(p.proj_stride >> 32)) < 0;
-  const bool bad_ptr = (p.seg_indptr == nullptr) | (p.lora_idx == nullptr) | (p.V == nullptr) |
-                       (pj.B_ptrs == nullptr) | (pj.Y == nullptr);
+                         (p.chunks_per_wg - 1) | (int32_t)(p.proj_stride >> 32) | (p.ksplit - 1) |
+                         (int32_t)(p.partial_stride >> 32)) < 0;
+  const bool bad_ptr = (p.seg_indptr == nullptr) | (p.lora_idx == nullptr) |
+                       (p.fold_planes ? p.partials == nullptr : p.V == nullptr) | (pj.B_ptrs == nullptr) |
+                       (pj.Y == nullptr);
   if (bad_size | bad_ptr) return;
   const int nchunks = (p.h_out + kCW - 1) / kCW;
   const int ngroups = (nchunks + p.chunks_per_wg - 1) / p.chunks_per_wg;
@@ -350,11 +352,41 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_expand_kernel(MfmaParams p
   constexpr int NVF = MT * R / 4;                       // float4 of V in the tile
   constexpr int NV4 = (NVF + kThreads - 1) / kThreads;  // ... per thread
   f32x4 vv[NV4];
+  if (p.fold_planes) {
+    // V = the sum of the shrink's partial planes, added in plane order from
+    // zero as the reduce launch would (same bits), kBatch planes in flight.
+    constexpr int kBatch = 4;
+    const float* Pp = p.partials + (int64_t)blockIdx.y * p.proj_stride;
 #pragma unroll
-  for (int m = 0; m < NV4; ++m) {
-    const int o = (t + kThreads * m) * 4;
-    const int rr = o / R;
-    vv[m] = *reinterpret_cast<const f32x4*>(Vp + (int64_t)(r0 + (rr < L ? rr : 0)) * R + o % R);
+    for (int m = 0; m < NV4; ++m) vv[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < p.ksplit; k0 += kBatch) {
+      f32x4 pv[kBatch][NV4];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int64_t k = k0 + u < p.ksplit ? k0 + u : p.ksplit - 1;
+#pragma unroll
+        for (int m = 0; m < NV4; ++m) {
+          const int o = (t + kThreads * m) * 4;
+          const int rr = o / R;
+          pv[u][m] = *reinterpret_cast<const f32x4*>(Pp + k * p.partial_stride +
+                                                     (int64_t)(r0 + (rr < L ? rr : 0)) * R + o % R);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+#pragma unroll
+        for (int m = 0; m < NV4; ++m) {
+          const f32x4 a = vv[m] + pv[u][m];
+          vv[m] = k0 + u < p.ksplit ? a : vv[m];
+        }
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < NV4; ++m) {
+      const int o = (t + kThreads * m) * 4;
+      const int rr = o / R;
+      vv[m] = *reinterpret_cast<const f32x4*>(Vp + (int64_t)(r0 + (rr < L ? rr : 0)) * R + o % R);
+    }
   }
   u32x4 bvA[NBP][2], yvA[NYV], bvB[NBP][2], yvB[NYV];
   issue(ch0, bvA, yvA);
@@ -498,7 +530,7 @@ hipError_t launch_stage(int dtype, int rank, int stage, const MfmaParams& p, int
 
 hipError_t launch_mfma_shrink(int dtype, int rank, const MfmaParams& p, int num_proj, hipStream_t stream) {
   hipError_t e = launch_stage(dtype, rank, 0, p, num_proj, stream);
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || p.fold_planes) return e;
   return launch_stage(dtype, rank, 1, p, num_proj, stream);
 }
 

@@ -103,7 +103,10 @@ struct MfmaParams {
   int32_t num_units64, direct_units64;  // units of <= 64 rows of one segment
   int32_t ksplit, kc, chunks_per_wg;
   // Expand tiles of expand_rows (16 or 64) rows of one segment: num_units_x of them.
-  int32_t expand_rows, num_units_x, direct_units_x, pad_;
+  int32_t expand_rows, num_units_x, direct_units_x;
+  // 1: no reduce launch; the expand sums the ksplit partial planes of its rows
+  // itself (in plane order, the reduce's order) instead of reading V.
+  int32_t fold_planes;
   const int32_t* seg_indptr;
   const int32_t* lora_idx;
   const int32_t* row_idx;  // null, or row of X / Y of each sorted row
@@ -115,7 +118,8 @@ struct MfmaParams {
   Projection proj[kMaxProjections];
 };
 
-// Shrink into the partial planes, then reduce them into V (two launches).
+// Shrink into the partial planes, then (unless p.fold_planes) reduce them into
+// V: one or two launches.
 hipError_t launch_mfma_shrink(int dtype, int rank, const MfmaParams& p, int num_proj, hipStream_t stream);
 hipError_t launch_mfma_expand(int dtype, int rank, const MfmaParams& p, int num_proj, hipStream_t stream);
 
@@ -142,7 +146,8 @@ struct BaseParams {
   float* vpartials;        // [ksplit][n_rows][rank] (null: no LoRA term)
   uint64_t* row_b;         // [n_rows] B_k of each row, 0 without a LoRA term (written by the shrink)
   float* partials;         // [ksplit][n_rows][h_out]
-  uint16_t* Y;             // [n_rows, h_out], written
+  uint16_t* Y;             // [n_rows, h_out], written rounded (when Yf is null)
+  float* Yf;               // null, or [n_rows, h_out] fp32, written unrounded instead of Y
 };
 
 // Partials then epilogue (two launches).

@@ -73,7 +73,7 @@ def test_query_plan_routes(kw, routes):
     if info.route == sg.SGMV_ROUTE_NONE:
         assert info.launches == 0 and info.grid == 0
     else:
-        assert info.launches == {1: 1, 2: 3, 3: 2}[info.route]
+        assert info.launches in {1: (1,), 2: (2, 3), 3: (2,)}[info.route]
         assert info.units >= 1 and info.splits >= 1 and info.grid >= 1
     with pytest.raises(sg.SgmvError):
         sg.sgmv_query_plan(good(rank=7))

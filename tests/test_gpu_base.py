@@ -5,14 +5,17 @@ Cases cover: one row per LoRA (the decode batch of the headline shape, full
 size), repeated LoRAs, rows no segment covers, no segments at all (Y = X @ W),
 a single row, 64 rows, ragged K (h_in not a multiple of the 128-row stage) and
 ragged column strips (h_out not a multiple of 128), both formats, every rank,
-and integer-valued inputs whose result is exact (compared bit for bit)."""
+and integer-valued inputs whose result is exact (compared bit for bit).  The
+row-parallel shard entry point (sgmv_base_lora_apply_partial) is checked shard by
+shard against the oracle on each H1 slice, summed against the whole product,
+and, with one slice, rounded against sgmv_base_lora_apply bit for bit."""
 import numpy as np
 import pytest
 
 import oracle
 import segmented_gather_matvec_amd as sg
 import workloads
-from tests.gpu_cases import assert_close, i32, to_bits, to_device
+from tests.gpu_cases import assert_close, assert_close_f32, i32, to_bits, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -161,3 +164,88 @@ def test_base_apply_repeated_calls_and_shared_workspace():
                             i32(lidx2a), ws)
     torch.cuda.synchronize()
     assert_close(to_bits(Y), oracle.sgmv_base_apply(dtype, X2, W2, A2, B2, seg2, lidx2), dtype, what="second")
+
+
+# ------------------------------------------------------------ row-parallel shards
+
+def run_partial(dtype, X, W, A_dev, lo, hi, B, seg, lidx, packed=False):
+    """sgmv_base_lora_apply_partial on the K slice [lo, hi) of X, W and every A_k
+    (A_dev: the whole stacked A on the device, [P, h_in, rank]); fp32 Yp as float64."""
+    import torch
+    n, h_in = X.shape
+    P, _, rank = A_dev.shape
+    h_out = W.shape[1]
+    seg = np.asarray(seg, np.int32)
+    lidx = np.asarray(lidx, np.int32)
+    mx = int(np.diff(seg).max()) if len(seg) > 1 else 0
+    prob = sg.make_problem(dtype, n, hi - lo, h_out, rank, P, len(lidx), mx)
+    Xg = to_device(np.ascontiguousarray(X[:, lo:hi]), dtype)
+    Wg = to_device(np.ascontiguousarray(W[lo:hi]), dtype)
+    if packed:
+        Wg = sg.pack_base_weight(Wg)
+    # A_{k,g}: rows lo..hi-1 of A_k, addressed inside A_k's own storage
+    A_tab = (A_dev.data_ptr() + (torch.arange(P, device="cuda", dtype=torch.int64) * h_in + lo) * rank * 2).contiguous()
+    Bd = to_device(B, dtype)
+    Yp = torch.full((n, h_out), float("nan"), dtype=torch.float32, device="cuda")
+    ws = torch.full((sg.sgmv_base_workspace_bytes(prob),), 0x5A, dtype=torch.uint8, device="cuda")
+    sg.sgmv_base_lora_apply_partial(prob, Xg, Wg, A_tab, sg.pointer_table(Bd), Yp, i32(seg if seg.size else [0]),
+                                    i32(lidx if lidx.size else [0]), ws, w_packed=packed)
+    torch.cuda.synchronize()
+    return Yp.cpu().numpy().astype(np.float64)
+
+
+SHARD_CASES = ["distinct_b32_h4096_r16", "skewed_b64_bf16_r64", "tail_uncovered_ragged", "no_segments_bf16"]
+
+
+@pytest.mark.parametrize("packed", [False, True])
+@pytest.mark.parametrize("name", SHARD_CASES)
+def test_row_parallel_shards_sum_to_the_whole_product(name, packed):
+    """Two H1 slices of the inputs (as two devices of a row-parallel layer hold
+    them): each shard's fp32 partial equals the oracle on that slice, and the
+    shards sum to the oracle's whole product (X @ W + per-row LoRA term)."""
+    seed, dtype, n, h_in, h_out, rank, P, layout = CASES[name]
+    X, W, A, B, seg, lidx = make_case(seed, dtype, n, h_in, h_out, rank, P, layout)
+    A_dev = to_device(A, dtype)
+    cut = (h_in // 2 + 7) // 8 * 8
+    total = np.zeros((n, h_out))
+    for lo, hi in ((0, cut), (cut, h_in)):
+        Yp = run_partial(dtype, X, W, A_dev, lo, hi, B, seg, lidx, packed=packed)
+        ref = oracle.sgmv_base_apply(dtype, np.ascontiguousarray(X[:, lo:hi]), np.ascontiguousarray(W[lo:hi]),
+                                     np.ascontiguousarray(A[:, lo:hi, :]), B, seg, lidx)
+        assert_close_f32(Yp, ref, what=f"{name} shard [{lo}, {hi})")
+        total += Yp
+    assert_close_f32(total, oracle.sgmv_base_apply(dtype, X, W, A, B, seg, lidx), what=f"{name} sum")
+
+
+@pytest.mark.parametrize("packed", [False, True])
+def test_one_shard_rounded_equals_the_rounded_call(packed):
+    """With the whole H1 as its one slice, the shard's fp32 output rounded once
+    (nearest even) is bit for bit the output of sgmv_base_lora_apply: the same
+    partial planes, summed in the same order, before the one rounding."""
+    import torch
+    name = "skewed_b64_bf16_r64"
+    seed, dtype, n, h_in, h_out, rank, P, layout = CASES[name]
+    X, W, A, B, seg, lidx = make_case(seed, dtype, n, h_in, h_out, rank, P, layout)
+    Yp = run_partial(dtype, X, W, to_device(A, dtype), 0, h_in, B, seg, lidx, packed=packed)
+    rounded = to_bits(torch.from_numpy(Yp.astype(np.float32)).to(torch.bfloat16))
+    got, _, _ = run_base(dtype, X, W, A, B, seg, lidx, packed=packed)
+    assert np.array_equal(rounded, got)
+
+
+def test_shards_of_integer_inputs_sum_exactly():
+    """Integer-valued inputs: every shard is exact in fp32 and the shards sum to
+    the oracle's whole product bit for bit."""
+    rng = np.random.default_rng(12)
+    n, h_in, h_out, rank, P = 24, 768, 392, 16, 5
+    X, A, B, _ = workloads.integer_exact(rng, n, h_in, h_out, rank, P, "f16", nnz_per_col=8, y0_bound=0)
+    Wf = np.zeros((h_in, h_out), np.float32)
+    for c in range(h_out):
+        rows = rng.choice(h_in, size=12, replace=False)
+        Wf[rows, c] = rng.choice([-1.0, 1.0], size=12)
+    W = workloads.to_bits(Wf, "f16")
+    seg, lidx = [0, 5, 6, 14, 20], [4, 0, 4, 2]
+    A_dev = to_device(A, "f16")
+    total = np.zeros((n, h_out))
+    for lo, hi in ((0, 256), (256, 512), (512, 768)):
+        total += run_partial("f16", X, W, A_dev, lo, hi, B, seg, lidx)
+    assert np.array_equal(total, oracle.sgmv_base_apply("f16", X, W, A, B, seg, lidx))
