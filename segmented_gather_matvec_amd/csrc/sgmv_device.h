@@ -14,6 +14,7 @@ constexpr int kWaves = kThreads / 64;
 // Element formats.  Values travel as raw 16-bit patterns and are widened to
 // fp32 for arithmetic.
 struct F16 {
+  static constexpr float kMaxFinite = 65504.f;
   __device__ static inline float lo(uint32_t w) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
   }
@@ -28,6 +29,7 @@ struct F16 {
 };
 
 struct BF16 {
+  static constexpr float kMaxFinite = 3.3895314e38f;
   __device__ static inline float lo(uint32_t w) { return __uint_as_float(w << 16); }
   __device__ static inline float hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
   __device__ static inline float one(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }

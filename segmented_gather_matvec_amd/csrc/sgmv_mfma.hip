@@ -272,6 +272,11 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_expand_kernel(MfmaParams p
   __shared__ __attribute__((aligned(16))) uint16_t lds_bt[kCW * BST];
   __shared__ __attribute__((aligned(16))) uint16_t lds_v[MT * VST];
   __shared__ __attribute__((aligned(16))) float lds_o[kWaves * 16 * OST];
+  // fp16 holds V's hi and lo halves only below 65504: a tile row whose V is
+  // larger is scaled down by a power of two before the split and its product
+  // scaled back in fp32 (both exact).  bf16 has fp32's range: no scaling.
+  constexpr bool kRowScale = T::kMaxFinite < 1e5f;
+  __shared__ float lds_rs[MT];
 
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -395,11 +400,25 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_expand_kernel(MfmaParams p
     const int o = (t + kThreads * m) * 4;
     if (o < NVF * 4) {
       const int rr = o / R, j = o % R;
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = rr < L ? vv[m][e] * sk : 0.f;
+      if constexpr (kRowScale) {
+        // The R / 4 lanes of one row (consecutive lanes) agree on its largest
+        // magnitude; rows under 2^15 keep the factor 1 (the same bits as
+        // without scaling).
+        float mx = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+#pragma unroll
+        for (int d = 1; d < R / 4; d <<= 1) mx = fmaxf(mx, shfl_xor(mx, d));
+        const int k = isfinite(mx) && mx >= 32768.f ? ilogbf(mx) - 14 : 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = ldexpf(v[e], -k);
+        if (j == 0) lds_rs[rr] = ldexpf(1.f, k);
+      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float v = rr < L ? vv[m][e] * sk : 0.f;
-        const uint16_t hi = T::round(v);
-        const uint16_t lo = T::round(v - T::one(hi));
+        const uint16_t hi = T::round(v[e]);
+        const uint16_t lo = T::round(v[e] - T::one(hi));
         lds_v[rr * VST + j + e] = hi;
         lds_v[rr * VST + R + j + e] = lo;
       }
@@ -455,8 +474,14 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_expand_kernel(MfmaParams p
       if (rr < L && ch < ch1 && c < p.h_out) {
         float yf[8];
         unpack8<T>(yv[u], yf);
+        if constexpr (kRowScale) {
+          const float rs = lds_rs[rr];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) yf[e] += out[rl * OST + cl + e];
+          for (int e = 0; e < 8; ++e) yf[e] += out[rl * OST + cl + e] * rs;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) yf[e] += out[rl * OST + cl + e];
+        }
         store_vec(Ybase + (int64_t)yrow[u] * p.h_out + c, pack8<T>(yf));
       }
     }

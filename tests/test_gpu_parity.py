@@ -493,3 +493,24 @@ def test_llama13b_layer_sampled(row_layout):
             got = to_bits(Y)[order]
             assert_close(got, ref, "bf16", rows=mask.astype(bool), what=f"{row_layout} {name}")
             assert np.isfinite(oracle.decode(to_bits(Y), "bf16")).all()
+
+
+@pytest.mark.parametrize("variant", [sg.SGMV_VARIANT_MFMA, sg.SGMV_VARIANT_VECTOR, sg.SGMV_VARIANT_AUTO])
+def test_f16_large_intermediate(variant):
+    """fp16 inputs whose intermediate V = x @ A_k exceeds fp16's range (|V| up to
+    ~1e5, the term itself and Y in range): every route keeps V in fp32 or, on the
+    matrix cores, splits a power-of-two scaled copy of it, so every route meets
+    the oracle bound; rows with small V share the tiles."""
+    rng = np.random.default_rng(55)
+    n, h_in, h_out, rank, P = 48, 512, 256, 16, 3
+    Xf = rng.standard_normal((n, h_in)).astype(np.float32)
+    Xf[24:] *= 1e-3                                  # small-V rows beside the large ones
+    Af = (rng.standard_normal((P, h_in, rank)) * 4000.0).astype(np.float32)
+    Bf = (rng.standard_normal((P, rank, h_out)) * 1e-3).astype(np.float32)
+    Y0f = rng.standard_normal((n, h_out)).astype(np.float32)
+    X, A, B, Y0 = (workloads.to_bits(a, "f16") for a in (Xf, Af, Bf, Y0f))
+    seg, lidx = [0, 20, 21, 48], [2, 0, 1]
+    call = DeviceCall("f16", X, A, B, Y0, seg, lidx, variant=variant)
+    _, V = oracle.sgmv_apply("f16", X, A, B, seg, lidx, Y0, want_v=True)
+    assert np.nanmax(np.abs(V)) > 65504.0
+    assert_close(to_bits(call.apply()), call.oracle_apply(), "f16")
