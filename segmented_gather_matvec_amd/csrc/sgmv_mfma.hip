@@ -8,7 +8,7 @@
 // sustain against HBM, so both run on v_mfma_f32_16x16x32_{f16,bf16}
 // (lane l holds A[l%16][8(l/16)+e], B[8(l/16)+e][l%16], D[4(l/16)+i][l%16]).
 //
-// Three launches:
+// Three launches (two when the expand sums the partial planes itself):
 //  1. shrink: a workgroup (4 waves, 16 rows each) takes up to 64 rows of one
 //     segment and one chunk of H1, streamed in stages of 128 H1 rows that are
 //     pipelined two deep: the X fragments (registers, straight from HBM) and
@@ -18,7 +18,9 @@
 //     read.  Each H1 chunk writes its own fp32 partial plane of V; workgroups
 //     that read the same chunk of A_k run on one XCD.
 //  2. reduce: V = sum of the partial planes, in chunk order (reproducible);
-//     the LoRA's scale, if any, is applied to V by the expand.
+//     the LoRA's scale, if any, is applied to V by the expand.  Up to 8
+//     planes the expand adds them itself, in the same order (same bits), and
+//     this launch is skipped.
 //  3. expand: a workgroup takes 64 rows (16 when the segments are short) and a
 //     group of 128-column chunks.  V is split into V_hi + V_lo (both in the
 //     input format), consumed as a K of 2r against [B_k; B_k], which keeps
@@ -64,13 +66,33 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_shrink_kernel(MfmaParams p
   constexpr int PAIRS = kKStage / 2 * JG;   // (h, h+1) vector pairs of A_k per stage
   constexpr int NPAIR = (PAIRS + kThreads - 1) / kThreads;
   constexpr int MS = kKStage / 32;          // MFMA k-steps per stage
-  constexpr int AST = kKStage + 8;          // LDS row stride (halves) of transposed A_k
+  // LDS row stride (halves) of transposed A_k: 72 dwords, which the 16 rank
+  // rows of one 128-bit MFMA operand read cover without bank conflicts (a
+  // stride of 68 dwords costs a second pass).
+  constexpr int AST = kKStage + 16;
   // Within a rank row, the stage's h sit in groups of 8 (one 128-bit MFMA
-  // operand read); group g of rank row r is stored at group g ^ swz(r), which
-  // spreads a wave's transposed stores over the LDS banks at ranks 32 and 64
-  // (rank 16 is conflict-free as is) while the operand reads stay
-  // conflict-free.
-  auto swz = [](int r) { return (r >> 4) << (R == 64 ? 1 : 2); };
+  // operand read); group g of rank row r is stored at group g ^ swz(r).  The
+  // xor changes every 4 rank rows, which the operand reads take without
+  // conflicts, and it spreads the transposed stores of each half-wave (the
+  // pair map below) over all banks.
+  auto swz = [](int r) { return (r >> 2) & (kKStage / 8 - 1); };
+  // (h-pair, rank group) item pr of a stage -> its h pair hp and its rank
+  // group jg.  Each half-wave's 32 items are 4 rank groups x 8 h pairs
+  // (r = 64, 32), or one rank group x 32 h pairs (r = 16): with the xor above
+  // the transposed stores of a half-wave then meet every LDS bank once, and a
+  // wave's loads still read whole rows of A_k.
+  auto pair_of = [](int pr, int& hp, int& jg) {
+    if constexpr (R == 64) {
+      jg = (pr & 3) | (((pr >> 5) & 1) << 2);
+      hp = ((pr >> 2) & 7) | ((pr >> 6) << 3);
+    } else if constexpr (R == 32) {
+      jg = pr & 3;
+      hp = pr >> 2;
+    } else {
+      jg = (pr >> 5) & 1;
+      hp = (pr & 31) | ((pr >> 6) << 5);
+    }
+  };
   static_assert(kMfmaKChunk % (2 * kKStage) == 0, "H1 chunks hold whole stage pairs");
   __shared__ __attribute__((aligned(16))) uint16_t lds_at[R * AST];
 
@@ -120,7 +142,9 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_shrink_kernel(MfmaParams p
 #pragma unroll
     for (int m = 0; m < NPAIR; ++m) {
       const int pr = t + kThreads * m;
-      const int h = kk + (pr / JG) * 2, jg = pr % JG;
+      int hp, jg;
+      pair_of(pr, hp, jg);
+      const int h = kk + hp * 2;
       const bool ok = pr < PAIRS && (!EXT || jg * 8 < rk);
       a[m][0] = load_stream(Ak + (ok && h < k1 ? (int64_t)h * a_stride + jg * 8 : 0));
       a[m][1] = load_stream(Ak + (ok && h + 1 < k1 ? (int64_t)(h + 1) * a_stride + jg * 8 : 0));
@@ -145,11 +169,15 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_shrink_kernel(MfmaParams p
     for (int m = 0; m < NPAIR; ++m) {
       const int pr = t + kThreads * m;
       if (pr < PAIRS) {
-        const int h = (pr / JG) * 2, jg = pr % JG;
+        int hp, jg;
+        pair_of(pr, hp, jg);
+        const int h = hp * 2;
         const bool live = !EXT || jg * 8 < rk;
-        const int hs = (((h >> 3) ^ swz(jg * 8)) << 3) | (h & 7);  // rows jg*8..+7 share swz
-        store_pair_transposed(&lds_at[(jg * 8) * AST + hs], AST, live && kk + h < k1 ? a[m][0] : z,
-                              live && kk + h + 1 < k1 ? a[m][1] : z);
+        // rank rows jg*8..+3 share one swz, rows jg*8+4..+7 the next
+        const int hs0 = (((h >> 3) ^ swz(jg * 8)) << 3) | (h & 7);
+        const int hs1 = (((h >> 3) ^ swz(jg * 8 + 4)) << 3) | (h & 7);
+        store_pair_transposed_split(&lds_at[(jg * 8) * AST + hs0], &lds_at[(jg * 8 + 4) * AST + hs1], AST,
+                                    live && kk + h < k1 ? a[m][0] : z, live && kk + h + 1 < k1 ? a[m][1] : z);
       }
     }
     __syncthreads();
@@ -159,7 +187,7 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_shrink_kernel(MfmaParams p
       const u32x4 xa = kk + s * 32 + q * 8 < k1 ? x[s] : z;  // ragged tail of H1
 #pragma unroll
       for (int n = 0; n < NT; ++n)
-        acc[n] = mfma<T>(xa, load_vec(&lds_at[(n * 16 + ml) * AST + (((4 * s + q) ^ swz(n * 16)) << 3)]), acc[n]);
+        acc[n] = mfma<T>(xa, load_vec(&lds_at[(n * 16 + ml) * AST + (((4 * s + q) ^ swz(n * 16 + ml)) << 3)]), acc[n]);
     }
   };
 
@@ -257,14 +285,33 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_expand_kernel(MfmaParams p
   constexpr int NTW = NTC / WC;        // column tiles per wave
   constexpr int CV = kCW / 8;          // 128-bit column vectors per chunk row
   constexpr int CVW = CV / WC;         // ... of one wave's columns
-  constexpr int BST = R + 8;           // LDS stride (halves) of transposed B_k, per column
+  // LDS stride (halves) of transposed B_k, per column: 40 dwords at r = 64 and
+  // 24 at r = 16, which the 16 columns of one 128-bit MFMA operand read cover
+  // without bank conflicts (r + 8 halves costs a second pass).  At r = 32 the
+  // conflict-free 24 dwords would leave room for only two 64-row workgroups
+  // per CU instead of three; it keeps r + 8.
+  constexpr int BST = R + (R == 64 ? 16 : R == 32 ? 8 : 32);
   // Within a column, B_k's ranks sit in groups of 8 (one 128-bit MFMA operand
-  // read); group g of column c is stored at group g ^ swz(c).  The transposed
-  // stores of a wave then spread over the LDS banks (without the swizzle the
-  // 16 lanes that write one rank pair of 16 column groups hit 2 banks), and
-  // the operand reads stay conflict-free.
+  // read); group g of column c is stored at group g ^ swz(c), constant over a
+  // 16-column MFMA tile (the operand reads stay conflict-free).  At r = 64 the
+  // xor takes the even groups, so that with the pair map below the transposed
+  // stores of a half-wave (8 rank pairs of 4 tiles) meet every bank once.
   constexpr int GMASK = R / 8 - 1;
-  auto swz = [](int c) { return (c >> 4) & GMASK; };
+  auto swz = [](int c) { return (R == 64 ? 2 * (c >> 4) : c >> 4) & GMASK; };
+  // (rank pair, 8-column group) item pr of a chunk -> first rank j and first
+  // chunk column cl.  At r = 64 a half-wave takes rank pairs 0..7 of every
+  // other column group (4 tiles) and a wave 8 whole column groups, so its
+  // loads still read 128 contiguous bytes of each B_k row.
+  auto item_of = [](int pr, int& j, int& cl) {
+    if constexpr (R == 64) {
+      const int rest = pr >> 6;
+      j = 2 * (((pr >> 2) & 7) + 8 * (rest >> 1));
+      cl = 8 * ((((pr & 3) << 1) | ((pr >> 5) & 1)) + 8 * (rest & 1));
+    } else {
+      j = (pr / (kCW / 8)) * 2;
+      cl = (pr % (kCW / 8)) * 8;
+    }
+  };
   constexpr int VST = K2 + 8;          // LDS stride (halves) of [V_hi | V_lo], per row
   constexpr int OST = kCW / WC + 4;    // LDS stride (floats) of a wave's result tile
   constexpr int NBP = (R / 2 * CV + kThreads - 1) / kThreads;  // (j, j+1) B_k vector pairs per thread
@@ -337,7 +384,9 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_expand_kernel(MfmaParams p
 #pragma unroll
     for (int m = 0; m < NBP; ++m) {
       const int pv = t + kThreads * m;
-      const int j = (pv / CV) * 2, c = c0 + (pv % CV) * 8;
+      int j, cl;
+      item_of(pv, j, cl);
+      const int c = c0 + cl;
       const bool ok = pv < R / 2 * CV && ch < ch1 && c < p.h_out && (!EXT || j < rk);
       bv[m][0] = load_stream(Bk + (ok ? (int64_t)j * p.h_out + c : 0));
       bv[m][1] = load_stream(Bk + (ok ? (int64_t)(j + 1) * p.h_out + c : 0));
@@ -437,7 +486,8 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_expand_kernel(MfmaParams p
     for (int m = 0; m < NBP; ++m) {
       const int pr = t + kThreads * m;
       if (pr < R / 2 * CV) {
-        const int j = (pr / CV) * 2, cl = (pr % CV) * 8;
+        int j, cl;
+        item_of(pr, j, cl);
         const u32x4 z = {0u, 0u, 0u, 0u};
         const bool live = !EXT || j < rk;  // rk is even, so j < rk covers row j + 1 too
         const int js = (((j >> 3) ^ swz(cl)) << 3) | (j & 7);  // columns cl..cl+7 share swz(cl)

@@ -40,4 +40,18 @@ __device__ inline void store_pair_transposed(uint16_t* dst, int stride, const u3
   }
 }
 
+// The same pair, with the pair's rows 0..3 at dst_lo + k * stride and rows
+// 4..7 at dst_hi + (k - 4) * stride.
+__device__ inline void store_pair_transposed_split(uint16_t* dst_lo, uint16_t* dst_hi, int stride, const u32x4& u,
+                                                   const u32x4& v) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    uint16_t* d = w < 2 ? dst_lo + (2 * w) * stride : dst_hi + (2 * w - 4) * stride;
+    const uint32_t lo = (u[w] & 0xffffu) | (v[w] << 16);
+    const uint32_t hi = (u[w] >> 16) | (v[w] & 0xffff0000u);
+    *reinterpret_cast<uint32_t*>(d) = lo;
+    *reinterpret_cast<uint32_t*>(d + stride) = hi;
+  }
+}
+
 }  // namespace sgmv

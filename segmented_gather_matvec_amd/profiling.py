@@ -4,9 +4,17 @@
     python -m segmented_gather_matvec_amd.profiling traffic --fetch DIR --write DIR --kernel REGEX \
         --copy REGEX --copy-bytes N --algorithmic-bytes B --source-hash H --out FILE.json \
         --summary FILE.txt --command-fetch "..." --command-write "..."
+    python -m segmented_gather_matvec_amd.profiling counters --pmc DIR [DIR ...] --kernel REGEX \
+        --simds N --out FILE.txt --command "..." [--command "..."]
 
 `stats` reads the kernel-trace CSVs of a `rocprofv3 --kernel-trace -f csv` run
-and writes per-kernel launch counts and durations.  `traffic` reads two
+and writes per-kernel launch counts and durations.  `counters` reads
+`rocprofv3 --pmc ... -f csv` runs and writes, per matched kernel, the mean of
+every counter per dispatch (summed over the device's XCDs / SEs) and the ratios
+derived from them: matrix-core busy fraction (SQ_VALU_MFMA_BUSY_CYCLES over
+SIMDs x GPU-busy cycles per XCD), LDS bank-conflict fraction of active LDS
+cycles, L2 hit rate, mean L1->L2 read latency, and the share of wave time spent
+waiting.  `traffic` reads two
 `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs (KiB per dispatch),
 scales each counter by what it reads for a plain device copy of known size in
 the same run, and writes the HBM bytes per launch of the matched kernel.
@@ -105,6 +113,57 @@ def cmd_stats(a):
     print(text)
 
 
+def pmc_dispatch_totals(dirs: List[str]) -> Dict[str, Dict[str, List[float]]]:
+    """kernel -> counter -> per-dispatch totals (summed over the rows a
+    dispatch has per XCD / SE / instance)."""
+    acc: Dict[str, Dict[str, Dict[str, float]]] = {}
+    for d in dirs:
+        for r in _rows(d, "counter_collection.csv"):
+            k = short_name(r["Kernel_Name"])
+            c = acc.setdefault(k, {}).setdefault(r["Counter_Name"], {})
+            key = f"{d}:{r['Dispatch_Id']}"
+            c[key] = c.get(key, 0.0) + float(r["Counter_Value"])
+    return {k: {c: list(v.values()) for c, v in cs.items()} for k, cs in acc.items()}
+
+
+def cmd_counters(a):
+    tot = pmc_dispatch_totals(a.pmc)
+    keys = sorted(k for k in tot if re.search(a.kernel, k))
+    if not keys:
+        raise SystemExit(f"no kernel matches {a.kernel!r}; kernels: {sorted(tot)}")
+    lines = ["# rocprofv3 counters per dispatch (mean over dispatches; each summed over the device)"]
+    lines += [f"# command: {c}" for c in a.command]
+    lines += [f"# derived ratios assume {a.simds} SIMDs and {a.xcds} XCDs", ""]
+    for k in keys:
+        m = {c: st.mean(v) for c, v in tot[k].items()}
+        n = max(len(v) for v in tot[k].values())
+        lines.append(f"kernel: {k}  ({n} dispatches)")
+        for c in sorted(m):
+            lines.append(f"  {c:36s} {m[c]:18,.1f}")
+        der = []
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in m and "GRBM_GUI_ACTIVE" in m:
+            der.append(("matrix-core busy fraction",
+                        m["SQ_VALU_MFMA_BUSY_CYCLES"] / (m["GRBM_GUI_ACTIVE"] / a.xcds * a.simds)))
+        if "SQ_LDS_BANK_CONFLICT" in m and m.get("SQ_LDS_IDX_ACTIVE"):
+            der.append(("LDS bank-conflict share of active LDS cycles", m["SQ_LDS_BANK_CONFLICT"] / m["SQ_LDS_IDX_ACTIVE"]))
+        if "TCC_HIT_sum" in m and "TCC_MISS_sum" in m and m["TCC_HIT_sum"] + m["TCC_MISS_sum"] > 0:
+            der.append(("L2 hit rate", m["TCC_HIT_sum"] / (m["TCC_HIT_sum"] + m["TCC_MISS_sum"])))
+        if m.get("TCP_TCC_READ_REQ_sum"):
+            der.append(("mean L1->L2 read latency (cycles)", m["TCP_TCC_READ_REQ_LATENCY_sum"] / m["TCP_TCC_READ_REQ_sum"]))
+        if m.get("SQ_WAVE_CYCLES") and "SQ_WAIT_INST_ANY" in m:
+            der.append(("share of wave cycles waiting on a dependency", m["SQ_WAIT_INST_ANY"] / m["SQ_WAVE_CYCLES"]))
+        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in m or "SQ_INSTS_VALU_MFMA_MOPS_F16" in m:
+            mops = m.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) + m.get("SQ_INSTS_VALU_MFMA_MOPS_F16", 0.0)
+            der.append(("matrix-core flops per dispatch (MOPS x 512)", mops * 512))
+        for name, v in der:
+            lines.append(f"  = {name:46s} {v:14.4f}" if v < 1e6 else f"  = {name:46s} {v:14,.0f}")
+        lines.append("")
+    text = "\n".join(lines) + "\n"
+    with open(a.out, "w") as f:
+        f.write(text)
+    print(text)
+
+
 def cmd_traffic(a):
     fetch = counter_means(a.fetch, "FETCH_SIZE")
     write = counter_means(a.write, "WRITE_SIZE")
@@ -159,8 +218,15 @@ def main():
     t.add_argument("--summary", required=True)
     t.add_argument("--command-fetch", default="")
     t.add_argument("--command-write", default="")
+    c = sub.add_parser("counters")
+    c.add_argument("--pmc", nargs="+", required=True)
+    c.add_argument("--kernel", required=True)
+    c.add_argument("--simds", type=int, default=1024)
+    c.add_argument("--xcds", type=int, default=8)
+    c.add_argument("--out", required=True)
+    c.add_argument("--command", action="append", default=[])
     a = ap.parse_args()
-    {"stats": cmd_stats, "traffic": cmd_traffic}[a.cmd](a)
+    {"stats": cmd_stats, "traffic": cmd_traffic, "counters": cmd_counters}[a.cmd](a)
 
 
 if __name__ == "__main__":
