@@ -192,17 +192,22 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_shrink_kernel(MfmaParams p
   };
 
   // Ping-pong over stage pairs: each buffer is waited for only where it is
-  // consumed.  A stage past k1 loads clamped addresses and contributes zeros;
-  // no loads are issued past the last stage pair (the stores below would
-  // wait for them).
+  // consumed.  A stage past k1 loads clamped addresses and contributes zeros.
+  // The loop body issues its loads unconditionally (a load under a branch
+  // makes the compiler wait for every load in flight at the loop head); the
+  // last stage pair, which issues no loads beyond itself, is peeled.
   u32x4 xA[MS], aA[NPAIR][2], xB[MS], aB[NPAIR][2];
   issue(k0, xA, aA);
-  for (int kk = k0; kk < k1; kk += 2 * kKStage) {
+  int kk = k0;
+  for (; kk + 2 * kKStage < k1; kk += 2 * kKStage) {
     issue(kk + kKStage, xB, aB);
     compute(kk, xA, aA);
-    if (kk + 2 * kKStage < k1) issue(kk + 2 * kKStage, xA, aA);
+    issue(kk + 2 * kKStage, xA, aA);
     compute(kk + kKStage, xB, aB);
   }
+  issue(kk + kKStage, xB, aB);
+  compute(kk, xA, aA);
+  compute(kk + kKStage, xB, aB);
 
   // D[4q+i][ml] of rank tile n: row wave*16 + 4q + i, rank n*16 + ml.
   float* dst = p.partials + (int64_t)blockIdx.y * p.proj_stride + (int64_t)g * p.partial_stride;

@@ -13,8 +13,9 @@ and writes per-kernel launch counts and durations.  `counters` reads
 every counter per dispatch (summed over the device's XCDs / SEs) and the ratios
 derived from them: matrix-core busy fraction (SQ_VALU_MFMA_BUSY_CYCLES over
 SIMDs x GPU-busy cycles per XCD), LDS bank-conflict fraction of active LDS
-cycles, L2 hit rate, mean L1->L2 read latency, and the share of wave time spent
-waiting.  `traffic` reads two
+cycles, L2 hit rate, mean L1->L2 read latency and reads in flight, the share of
+L1 cycles stalled with its table of pending L2 reads full, and the share of
+wave time spent waiting.  `traffic` reads two
 `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs (KiB per dispatch),
 scales each counter by what it reads for a plain device copy of known size in
 the same run, and writes the HBM bytes per launch of the matched kernel.
@@ -133,7 +134,7 @@ def cmd_counters(a):
         raise SystemExit(f"no kernel matches {a.kernel!r}; kernels: {sorted(tot)}")
     lines = ["# rocprofv3 counters per dispatch (mean over dispatches; each summed over the device)"]
     lines += [f"# command: {c}" for c in a.command]
-    lines += [f"# derived ratios assume {a.simds} SIMDs and {a.xcds} XCDs", ""]
+    lines += [f"# derived ratios assume {a.simds} SIMDs, {a.cus} CUs and {a.xcds} XCDs", ""]
     for k in keys:
         m = {c: st.mean(v) for c, v in tot[k].items()}
         n = max(len(v) for v in tot[k].values())
@@ -150,6 +151,12 @@ def cmd_counters(a):
             der.append(("L2 hit rate", m["TCC_HIT_sum"] / (m["TCC_HIT_sum"] + m["TCC_MISS_sum"])))
         if m.get("TCP_TCC_READ_REQ_sum"):
             der.append(("mean L1->L2 read latency (cycles)", m["TCP_TCC_READ_REQ_LATENCY_sum"] / m["TCP_TCC_READ_REQ_sum"]))
+        if m.get("TCP_TCC_READ_REQ_LATENCY_sum") and m.get("GRBM_GUI_ACTIVE"):
+            der.append(("mean L1->L2 reads in flight (device)",
+                        m["TCP_TCC_READ_REQ_LATENCY_sum"] / (m["GRBM_GUI_ACTIVE"] / a.xcds)))
+        if "TCP_PENDING_STALL_CYCLES" in m and m.get("GRBM_GUI_ACTIVE"):
+            der.append(("share of L1 cycles stalled on pending L2 data",
+                        m["TCP_PENDING_STALL_CYCLES"] / (m["GRBM_GUI_ACTIVE"] / a.xcds * a.cus)))
         if m.get("SQ_WAVE_CYCLES") and "SQ_WAIT_INST_ANY" in m:
             der.append(("share of wave cycles waiting on a dependency", m["SQ_WAIT_INST_ANY"] / m["SQ_WAVE_CYCLES"]))
         if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in m or "SQ_INSTS_VALU_MFMA_MOPS_F16" in m:
@@ -223,6 +230,7 @@ def main():
     c.add_argument("--kernel", required=True)
     c.add_argument("--simds", type=int, default=1024)
     c.add_argument("--xcds", type=int, default=8)
+    c.add_argument("--cus", type=int, default=256)
     c.add_argument("--out", required=True)
     c.add_argument("--command", action="append", default=[])
     a = ap.parse_args()
