@@ -183,21 +183,22 @@ WsLayout apply_ws_layout(const sgmv_problem_t& p) {
 // 32-row batches (H = 4096 and 11008 -> 4096) found 128 x 256 best: more
 // splits write (and the epilogue reads) more partial planes.  Narrow outputs
 // (a column shard of a tensor-parallel layer, 4096 -> 512) would take 32
-// splits for 256 workgroups; capped at 16 (row-major W) or 8 (packed W) the
-// call took 11.2 / 11.9 us instead of 16.5 / 17.0 us (the epilogue sums fewer
-// planes).  Full-width outputs already stay below the caps.
+// splits for 256 workgroups; capped at 8 the row-major and packed calls took
+// 11.6 / 11.9 us instead of 16.5 / 17.0 us (the epilogue sums fewer planes;
+// caps of 4 and 16 were slower for one layout or the other).  Both layouts
+// share the cap, so they keep splitting K alike.  Full-width outputs already
+// stay below it.
 constexpr int kBaseStripCols = 128;
 constexpr int kBaseTarget = 256;
-constexpr int kBaseMaxSplitRowMajor = 16;
-constexpr int kBaseMaxSplitPacked = 8;
+constexpr int kBaseMaxSplit = 8;
 
 BasePlan plan_base(const sgmv_problem_t& p, bool packed) {
   BasePlan b;
   b.strip_cols = kBaseStripCols;
   b.strips = (int)ceil_div(p.h_out, b.strip_cols);
   const int64_t max_split = ceil_div(p.h_in, sgmv::kBaseStageRows);
-  const int64_t split_cap = packed ? kBaseMaxSplitPacked : kBaseMaxSplitRowMajor;
-  const int64_t ks = std::max<int64_t>(1, std::min<int64_t>({ceil_div(kBaseTarget, b.strips), max_split, split_cap}));
+  const int64_t ks = std::max<int64_t>(1, std::min<int64_t>({ceil_div(kBaseTarget, b.strips), max_split,
+                                                             (int64_t)kBaseMaxSplit}));
   b.kc = (int)round_up(ceil_div(p.h_in, ks), sgmv::kBaseStageRows);
   if (packed && p.n_rows > 32) {
     // The packed-W kernel stages the X chunk of its four row tiles (64 x kc) in LDS.
