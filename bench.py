@@ -143,7 +143,8 @@ HET_WORKLOADS = ["decode_mixedrank_h4096_r64_b32"]
 # The base_packed_ lines run sgmv_base_lora_apply_packed on W packed once
 # beforehand (the packing is not timed: a server packs its weights at load).
 BASE_WORKLOADS = ["base_decode_distinct_h4096_r16_b32", "base_decode_distinct_h4096_r16_b8",
-                  "base_decode_distinct_h4096_r16_b64", "base_decode_distinct_h11008to4096_r16_b32"]
+                  "base_decode_distinct_h4096_r16_b64", "base_decode_distinct_h11008to4096_r16_b32",
+                  "base_decode_distinct_h4096_r16_b128"]
 BASE_WORKLOADS += [w.replace("base_", "base_packed_", 1) for w in BASE_WORKLOADS]
 # One GPU's shard of a tensor-parallel layer over 8 GPUs (H = 4096): the
 # column-parallel shard (W[:, slice], B_k[:, slice]: 4096 -> 512, the ordinary
@@ -729,7 +730,7 @@ def base_rows_curve(batches=(8, 16, 32, 64, 128, 256, 512, 1024), steps=160):
     calls replayed out of a captured HIP graph (weights rotate through >= 1 GiB):
       torch_gemm_us            torch.matmul(X, W) written to Y (the base layer alone)
       torch_gemm_plus_sgmv_us  that GEMM, then sgmv_lora_apply adding the LoRA term
-      fused_us                 sgmv_base_lora_apply (n <= 64 only), one rounding
+      fused_us                 sgmv_base_lora_apply (n <= SGMV_BASE_MAX_ROWS only), one rounding
       fused_packed_us          sgmv_base_lora_apply_packed on W packed beforehand
     with the HBM floor of streaming W once (w_floor_us, 8 TB/s) and the matrix-core
     floor of the GEMM's flops (gemm_flop_floor_us, 2.5 PFLOP/s fp16)."""
@@ -757,7 +758,7 @@ def base_rows_curve(batches=(8, 16, 32, 64, 128, 256, 512, 1024), steps=160):
         lidx = torch.arange(n, dtype=torch.int32, device="cuda")
         prob = sg.make_problem("f16", n, H, H, r, n, n, 1)
         ws = sg.new_workspace(prob)
-        bws = sg.new_base_workspace(prob) if n <= 64 else None
+        bws = sg.new_base_workspace(prob) if n <= sg.SGMV_BASE_MAX_ROWS else None
         pb = ctypes.byref(prob)
 
         def gemm(c):
@@ -781,7 +782,7 @@ def base_rows_curve(batches=(8, 16, 32, 64, 128, 256, 512, 1024), steps=160):
             return run
 
         methods = {"torch_gemm": gemm, "torch_gemm_plus_sgmv": gemm_sgmv}
-        if n <= 64:
+        if n <= sg.SGMV_BASE_MAX_ROWS:
             methods["fused"] = fused_with(lib.sgmv_base_lora_apply, Ws)
             methods["fused_packed"] = fused_with(lib.sgmv_base_lora_apply_packed, Wps)
         row = {"rows": n, "w_floor_us": round(2 * H * H / 8e12 * 1e6, 3),

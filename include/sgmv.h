@@ -340,13 +340,17 @@ sgmv_status_t sgmv_lora_apply_batched(const sgmv_problem_t* problem, const void*
  *           when num_segs == 0 or max_seg_len == 0: then Y = X @ W).
  *   ws      device workspace of sgmv_base_workspace_bytes bytes (any contents;
  *           it holds the fp32 partial planes of V and of X @ W).
- * Supported: n_rows <= 64 (SGMV_ERR_UNSUPPORTED above; a prefill-sized base
- * projection is a dense GEMM for a GEMM library, followed by sgmv_lora_apply);
+ * Supported: n_rows <= SGMV_BASE_MAX_ROWS (SGMV_ERR_UNSUPPORTED above; a
+ * prefill-sized base projection is a dense GEMM for a GEMM library, followed by
+ * sgmv_lora_apply);
  * ranks, formats and alignment as for sgmv_lora_apply.  Two launches (split-K
  * partial products of X @ W on the matrix cores together with the partial
  * planes of V = X @ A_k; an epilogue that sums them, adds V @ B_k and rounds);
  * asynchronous on `stream`.  Same metadata preconditions and error
  * conventions as sgmv_lora_apply. */
+/* Largest batch (rows) the base projection entry points take. */
+#define SGMV_BASE_MAX_ROWS 128
+
 sgmv_status_t sgmv_base_workspace_bytes(const sgmv_problem_t* problem, size_t* bytes);
 sgmv_status_t sgmv_base_lora_apply(const sgmv_problem_t* problem, const void* X, const void* W,
                                    const void* const* A_ptrs, const void* const* B_ptrs, void* Y,
@@ -396,7 +400,7 @@ sgmv_status_t sgmv_base_lora_apply_packed(const sgmv_problem_t* problem, const v
  * existing all-reduce sums the shards' Yp; rounding the sum once to the input
  * format gives the one-rounding output of sgmv_base_lora_apply.
  *   problem   h_in = the slice's width, h_out = the full H2; other fields as for
- *             sgmv_base_lora_apply (n_rows <= 64).
+ *             sgmv_base_lora_apply (n_rows <= SGMV_BASE_MAX_ROWS).
  *   X, W      device X_g [n_rows, h_in] and W_g [h_in, h_out] (rows of W in the
  *             slice), row-major, or W_g in the packed layout of
  *             sgmv_base_pack_weight when w_packed = 1 (0: row-major).

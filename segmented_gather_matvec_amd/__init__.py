@@ -38,6 +38,7 @@ ENTRY_POINTS = ("sgmv_status_str", "sgmv_build_segments", "sgmv_check_problem",
                 "sgmv_lora_apply_noalloc", "sgmv_base_lora_apply_partial")
 SGMV_DEVICE_ERR_WAIT_TIMEOUT = 1
 SGMV_NOALLOC_MAX_WORKSPACE = 16 << 20
+SGMV_BASE_MAX_ROWS = 128
 
 
 class SgmvError(RuntimeError):
@@ -313,7 +314,7 @@ def sgmv_lora_apply_batched(problem, X, projections, seg_indptr, lora_idx, ws, r
 # ----------------------------------------------------------------- helpers
 
 def sgmv_base_workspace_bytes(problem: sgmv_problem_t) -> int:
-    """Workspace bytes of sgmv_base_lora_apply (n_rows <= 64)."""
+    """Workspace bytes of sgmv_base_lora_apply (n_rows <= SGMV_BASE_MAX_ROWS)."""
     out = ctypes.c_size_t(0)
     _check(load_library().sgmv_base_workspace_bytes(ctypes.byref(problem), ctypes.byref(out)),
            "sgmv_base_workspace_bytes")
@@ -342,7 +343,7 @@ def _base_apply(name, problem, X, W, A_ptrs, B_ptrs, Y, seg_indptr, lora_idx, ws
 
 def sgmv_base_lora_apply(problem, X, W, A_ptrs, B_ptrs, Y, seg_indptr, lora_idx, ws, stream=None):
     """Y[i] = X[i] @ W + (X[i] @ A_k) @ B_k on the device (Y written, rounded once); asynchronous.
-    Rows no segment covers get X[i] @ W.  At most 64 rows."""
+    Rows no segment covers get X[i] @ W.  At most SGMV_BASE_MAX_ROWS rows."""
     _base_apply("sgmv_base_lora_apply", problem, X, W, A_ptrs, B_ptrs, Y, seg_indptr, lora_idx, ws, stream)
 
 

@@ -4,7 +4,7 @@
 // The LoRA paragraph of the Punica README (page "Punica：多 LoRA 模型统一服务框架")
 // gives a row vector x the output x@W + x@A@B; the multi-LoRA paragraph runs
 // X@W once for the whole batch and adds every row's own LoRA term.  For at
-// most 64 rows this file computes
+// most 128 rows this file computes
 //     Y[i, :] = X[i, :] @ W + V[i, :] @ B_k      (k: LoRA of row i's segment)
 // with V = X @ A_k, the sum kept in fp32 and rounded once.  Rows no segment covers get X @ W.
 //
@@ -286,8 +286,8 @@ __global__ __launch_bounds__(64) void sgmv_base_pack_kernel(const uint16_t* __re
 // k-steps: S - 1 sets are in flight while one is multiplied.  X operands:
 //  - up to two row tiles: each wave loads them from L2 with its W (no LDS,
 //    no barrier);
-//  - four row tiles (XL): the workgroup's X chunk ([64 rows][kc], at most
-//    64 KiB) is staged in LDS once, behind one barrier, its 16-byte groups at
+//  - four or eight row tiles (XL): the workgroup's X chunk ([64 or 128
+//    rows][kc], at most 64 or 128 KiB) is staged in LDS once, behind one barrier, its 16-byte groups at
 //    group ^ (row & 7) within a row so that the 16 rows of one operand read
 //    fall on different banks.  Four operand loads per k-step from L2 would
 //    outnumber the two of W.
@@ -297,7 +297,8 @@ __global__ __launch_bounds__(kThreads) void sgmv_base_packed_kernel(BaseParams p
   constexpr int S = 2;  // register sets (three measured slower)
   constexpr bool XL = NRT > 2;
   constexpr int NX = XL ? 0 : NRT;  // X operands per k-step held in the ring
-  __shared__ __attribute__((aligned(16))) uint16_t lds_x[XL ? kBasePackedXElems : kWaves * 128];
+  constexpr int XE = base_packed_x_elems(NRT * 16);
+  __shared__ __attribute__((aligned(16))) uint16_t lds_x[XL ? XE : kWaves * 128];
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = t >> 6;
@@ -305,7 +306,7 @@ __global__ __launch_bounds__(kThreads) void sgmv_base_packed_kernel(BaseParams p
   const int ml = lane & 15;
   const int kst = p.packed_ksteps;
   const bool bad = ((p.n_rows - 1) | p.h_in | p.h_out | (p.kc - 1) | (p.strips - 1) | (p.ksplit - 1) |
-                    (kst - 1) | (NRT * 16 - p.n_rows) | (XL ? kBasePackedXElems - NRT * 16 * p.kc : 0) |
+                    (kst - 1) | (NRT * 16 - p.n_rows) | (XL ? XE - NRT * 16 * p.kc : 0) |
                     (int32_t)(p.plane_stride >> 32)) < 0;
   const bool bad_ptr = (p.X == nullptr) | (p.W == nullptr) | (p.partials == nullptr);
   if (bad | bad_ptr) return;
@@ -564,8 +565,10 @@ hipError_t launch_partial(const BaseParams& p, hipStream_t s) {
     hipLaunchKernelGGL((sgmv_base_partial_kernel<T, R, SC, 1>), grid, dim3(kThreads), 0, s, p);
   else if (p.n_rows <= 32)
     hipLaunchKernelGGL((sgmv_base_partial_kernel<T, R, SC, 2>), grid, dim3(kThreads), 0, s, p);
-  else
+  else if (p.n_rows <= 64)
     hipLaunchKernelGGL((sgmv_base_partial_kernel<T, R, SC, 4>), grid, dim3(kThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL((sgmv_base_partial_kernel<T, R, SC, 8>), grid, dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 
@@ -576,8 +579,10 @@ hipError_t launch_packed(const BaseParams& p, hipStream_t s) {
     hipLaunchKernelGGL((sgmv_base_packed_kernel<T, R, 1>), grid, dim3(kThreads), 0, s, p);
   else if (p.n_rows <= 32)
     hipLaunchKernelGGL((sgmv_base_packed_kernel<T, R, 2>), grid, dim3(kThreads), 0, s, p);
-  else
+  else if (p.n_rows <= 64)
     hipLaunchKernelGGL((sgmv_base_packed_kernel<T, R, 4>), grid, dim3(kThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL((sgmv_base_packed_kernel<T, R, 8>), grid, dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 

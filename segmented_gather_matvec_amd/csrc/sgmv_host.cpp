@@ -192,6 +192,8 @@ constexpr int kBaseStripCols = 128;
 constexpr int kBaseTarget = 256;
 constexpr int kBaseMaxSplit = 8;
 
+static_assert(sgmv::kBaseMaxRows == SGMV_BASE_MAX_ROWS, "one row limit for the base projection");
+
 BasePlan plan_base(const sgmv_problem_t& p, bool packed) {
   BasePlan b;
   b.strip_cols = kBaseStripCols;
@@ -201,8 +203,10 @@ BasePlan plan_base(const sgmv_problem_t& p, bool packed) {
                                                              (int64_t)kBaseMaxSplit}));
   b.kc = (int)round_up(ceil_div(p.h_in, ks), sgmv::kBaseStageRows);
   if (packed && p.n_rows > 32) {
-    // The packed-W kernel stages the X chunk of its four row tiles (64 x kc) in LDS.
-    const int64_t cap = sgmv::kBasePackedXElems / 64 / sgmv::kBaseStageRows * sgmv::kBaseStageRows;
+    // The packed-W kernel stages the X chunk of its four or eight row tiles
+    // (64 or 128 rows x kc) in LDS.
+    const int64_t rows = p.n_rows > 64 ? 128 : 64;
+    const int64_t cap = sgmv::base_packed_x_elems((int)rows) / rows / sgmv::kBaseStageRows * sgmv::kBaseStageRows;
     b.kc = (int)std::min<int64_t>(b.kc, cap);
   }
   b.ksplit = (int)ceil_div(p.h_in, b.kc);

@@ -88,6 +88,8 @@ def test_projection_struct_layout_matches_header():
     assert fields == [n for n, _ in sg.sgmv_projection_t._fields_]
     assert ctypes.sizeof(sg.sgmv_projection_t) == 8 * len(fields)
     assert re.search(r"#define SGMV_MAX_PROJECTIONS 4\b", src) and sg.SGMV_MAX_PROJECTIONS == 4
+    m = re.search(r"#define SGMV_BASE_MAX_ROWS (\d+)\b", src)
+    assert m and int(m.group(1)) == sg.SGMV_BASE_MAX_ROWS
 
 
 def test_batched_apply_fails_fast_on_bad_arguments():
@@ -292,8 +294,8 @@ def test_base_apply_fails_fast_on_bad_arguments():
     assert call(p, fake, odd, fake, fake, need) == sg.SGMV_ERR_UNSUPPORTED
     assert call(p, fake, fake, fake, None, 0) == sg.SGMV_ERR_WORKSPACE
     assert call(p, fake, fake, fake, fake, need - 1) == sg.SGMV_ERR_WORKSPACE
-    # more than 64 rows: a dense GEMM, not this entry point
-    big = good(n_rows=65, num_segs=65)
+    # more than SGMV_BASE_MAX_ROWS rows: a dense GEMM, not this entry point
+    big = good(n_rows=sg.SGMV_BASE_MAX_ROWS + 1, num_segs=sg.SGMV_BASE_MAX_ROWS + 1)
     assert call(big, fake, fake, fake, fake, need) == sg.SGMV_ERR_UNSUPPORTED
     with pytest.raises(sg.SgmvError) as e:
         sg.sgmv_base_workspace_bytes(big)
@@ -326,7 +328,8 @@ def test_packed_base_entry_points_fail_fast():
     assert call(p, fake, None, fake, ws) == sg.SGMV_ERR_INVALID_ARG
     assert call(p, fake, ctypes.c_void_p(0x10008), fake, ws) == sg.SGMV_ERR_UNSUPPORTED
     assert call(p, fake, fake, fake, ws - 1) == sg.SGMV_ERR_WORKSPACE
-    assert call(good(n_rows=65, num_segs=65), fake, fake, fake, ws) == sg.SGMV_ERR_UNSUPPORTED
+    assert call(good(n_rows=sg.SGMV_BASE_MAX_ROWS + 1, num_segs=sg.SGMV_BASE_MAX_ROWS + 1), fake, fake, fake,
+                ws) == sg.SGMV_ERR_UNSUPPORTED
 
 
 @pytest.mark.parametrize("h_in,h_out,blocks,ksteps", [(4096, 4096, 256, 128), (520, 264, 18, 20),
@@ -337,7 +340,8 @@ def test_packed_weight_size(h_in, h_out, blocks, ksteps):
 
 
 @pytest.mark.parametrize("kw", [{}, {"h_out": 11008}, {"h_in": 13824, "h_out": 5120, "rank": 64},
-                                {"n_rows": 1, "num_segs": 1}, {"n_rows": 64, "num_segs": 64}])
+                                {"n_rows": 1, "num_segs": 1}, {"n_rows": 64, "num_segs": 64},
+                                {"n_rows": 128, "num_segs": 128}])
 def test_base_workspace_covers_its_parts(kw):
     """The base workspace holds one fp32 partial plane of V and of Y per K split."""
     p = good(**kw)

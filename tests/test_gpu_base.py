@@ -3,7 +3,7 @@ against the fp64 oracle, through the C ABI.
 
 Cases cover: one row per LoRA (the decode batch of the headline shape, full
 size), repeated LoRAs, rows no segment covers, no segments at all (Y = X @ W),
-a single row, 64 rows, ragged K (h_in not a multiple of the 128-row stage) and
+a single row, 64, 96 and 128 rows, ragged K (h_in not a multiple of the 128-row stage) and
 ragged column strips (h_out not a multiple of 128), both formats, every rank,
 and integer-valued inputs whose result is exact (compared bit for bit).  The
 row-parallel shard entry point (sgmv_base_lora_apply_partial) is checked shard by
@@ -86,6 +86,10 @@ CASES = {
     # 40 rows (four row tiles) over many strips: the packed kernel's LDS cap on
     # the X chunk (512 k) cuts the K chunk below the row-major call's 640
     "capped_chunk_b40_bf16_r32": (9, "bf16", 40, 2560, 8200, 32, 6, "skewed"),
+    # eight row tiles (65..128 rows): the packed kernel stages 128 rows of X
+    # (K chunk up to 512, the row-major call's chunk here)
+    "distinct_b128_f16_r16": (10, "f16", 128, 4096, 4096, 16, 128, "distinct"),
+    "skewed_b96_bf16_r64": (11, "bf16", 96, 1536, 1032, 64, 24, "skewed"),
 }
 
 
