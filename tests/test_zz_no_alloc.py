@@ -65,3 +65,41 @@ def test_noalloc_rejects_problems_beyond_its_scratch():
     fake = ctypes.c_void_p(0x10000)
     assert lib.sgmv_lora_apply_noalloc(ctypes.byref(p), fake, fake, fake, fake, fake, fake,
                                        None) == sg.SGMV_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("route", sorted(CASES))
+def test_noalloc_call_captured_in_a_graph_replays_exactly(route):
+    """The callers this entry point is for capture it in a HIP graph.  A reset of
+    Y plus one no-alloc call is captured and replayed several times, with eager
+    no-alloc calls in between that use the same static scratch; every replay and
+    every eager call must equal the workspace entry point bit for bit."""
+    import torch
+    from tests.gpu_cases import to_device
+    _, small, variant = CASES[route]
+    call = _pair(small(), variant)
+    ref = to_bits(call.apply()).copy()
+    side = _pair(small(), variant)
+    Y0d = to_device(call.Y0h, call.dtype)
+    call.reset_y()
+    sg.sgmv_lora_apply_noalloc(call.problem, call.X, call.A_ptrs, call.B_ptrs, call.Y, call.seg_d, call.lidx_d)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_bits(call.Y), ref)
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            call.Y.copy_(Y0d)
+            sg.sgmv_lora_apply_noalloc(call.problem, call.X, call.A_ptrs, call.B_ptrs, call.Y, call.seg_d,
+                                       call.lidx_d, stream=stream)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(to_bits(call.Y), ref), f"{route}: replay {rep} differs"
+        side.reset_y()
+        sg.sgmv_lora_apply_noalloc(side.problem, side.X, side.A_ptrs, side.B_ptrs, side.Y, side.seg_d,
+                                   side.lidx_d)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_bits(side.Y), ref), f"{route}: eager no-alloc call after replay {rep} differs"
+    assert sg.sgmv_take_device_errors() == 0
