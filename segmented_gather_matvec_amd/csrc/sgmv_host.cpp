@@ -126,6 +126,7 @@ constexpr int kMfmaShrinkTarget = 1024;
 constexpr int kMfmaExpandTarget = 1024;
 constexpr int kMfmaShortTileRows = 32;   // mean rows per 64-row tile below which tiles count as short
 constexpr int kMfmaShortExpandRows = 16; // expand tile rows for short tiles
+constexpr int kMfmaLowRankExpandRows = 32;  // expand tile rows for full tiles at rank <= 16
 constexpr int kMfmaShortChunksPerWg = 3;
 // Up to this many partial planes the expand sums them itself and the reduce
 // launch is skipped.
@@ -158,7 +159,17 @@ MfmaPlan plan_mfma(const sgmv_problem_t& p) {
     m.direct_x = direct;
     m.chunks_per_wg = (int)std::min<int64_t>(nchunks, kMfmaShortChunksPerWg);
   } else {
-    const int64_t groups = std::max<int64_t>(1, std::min<int64_t>(nchunks, kMfmaExpandTarget / units));
+    // Full tiles: each tile re-reads its B_k slice, r x 2 bytes per output per
+    // tile row.  At rank <= 16 that is cheap, and 32-row tiles (twice the
+    // workgroups) won: 78.9 -> 72.7 us on the mixed r = 16 4096 -> 11008 batch,
+    // equal at 11008 -> 4096; at rank 64 they lost 4-10%.
+    if (p.rank <= 16) {
+      m.expand_rows = kMfmaLowRankExpandRows;
+      m.units_x = units_for(p, kMfmaLowRankExpandRows, &direct);
+      m.direct_x = direct;
+    }
+    const int64_t ux = std::max<int64_t>(m.units_x, 1);
+    const int64_t groups = std::max<int64_t>(1, std::min<int64_t>(nchunks, kMfmaExpandTarget / ux));
     m.chunks_per_wg = (int)ceil_div(nchunks, groups);
   }
   m.partial_bytes = (size_t)m.ksplit * (size_t)p.n_rows * p.rank * sizeof(float);

@@ -87,7 +87,7 @@ struct MfmaPlan {
   int ksplit = 1;
   int kc = 0;
   int chunks_per_wg = 1;
-  int expand_rows = sgmv::kMfmaRowsPerTile;  // rows of one expand tile (16 for short tiles)
+  int expand_rows = sgmv::kMfmaRowsPerTile;  // rows of one expand tile (16 for short tiles, 32 at rank <= 16)
   int64_t units_x = 0;                        // expand units of <= expand_rows rows
   int direct_x = 1;
   size_t partial_bytes = 0;  // split partials of V, fp32 [ksplit][n_rows][rank]

@@ -285,7 +285,7 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_expand_kernel(MfmaParams p
   constexpr int KSTEPS = K2 / 32;
   constexpr int WR = MT / 16;          // 16-row groups of the tile
   constexpr int WC = kWaves / WR;      // waves that share a row group, each on its own columns
-  static_assert(WR * WC == kWaves, "tile rows are 16 or 64");
+  static_assert(WR * WC == kWaves, "tile rows are 16, 32 or 64");
   constexpr int NTC = kCW / 16;        // 16-wide column tiles per chunk
   constexpr int NTW = NTC / WC;        // column tiles per wave
   constexpr int CV = kCW / 8;          // 128-bit column vectors per chunk row
@@ -576,16 +576,18 @@ hipError_t launch_t(int stage, const MfmaParams& p, int np, hipStream_t s) {
     grid = ((unsigned)p.n_rows + rows - 1) / rows;
     if (grid && np > 0) hipLaunchKernelGGL((sgmv_mfma_reduce_kernel<R>), dim3(grid, np), dim3(kThreads), 0, s, p);
   } else {
-    if (p.expand_rows != 16 && p.expand_rows != kMT) return hipErrorInvalidValue;
+    if (p.expand_rows != 16 && p.expand_rows != 32 && p.expand_rows != kMT) return hipErrorInvalidValue;
     const int nchunks = (p.h_out + kCW - 1) / kCW;
     grid = xcd_grid((unsigned)p.num_units_x * (unsigned)((nchunks + p.chunks_per_wg - 1) / p.chunks_per_wg));
     if (grid && np > 0) {
       using K = void (*)(MfmaParams);
-      // [short tiles][ext]
-      static constexpr K kernels[2][2] = {
+      // [tile rows 64, 32, 16][ext]
+      static constexpr K kernels[3][2] = {
           {sgmv_mfma_expand_kernel<T, R, false, kMT>, sgmv_mfma_expand_kernel<T, R, true, kMT>},
+          {sgmv_mfma_expand_kernel<T, R, false, 32>, sgmv_mfma_expand_kernel<T, R, true, 32>},
           {sgmv_mfma_expand_kernel<T, R, false, 16>, sgmv_mfma_expand_kernel<T, R, true, 16>}};
-      hipLaunchKernelGGL(kernels[p.expand_rows == 16][ext], dim3(grid, np), dim3(kThreads), 0, s, p);
+      const int which = p.expand_rows == kMT ? 0 : p.expand_rows == 32 ? 1 : 2;
+      hipLaunchKernelGGL(kernels[which][ext], dim3(grid, np), dim3(kThreads), 0, s, p);
     }
   }
   return grid && np > 0 ? hipGetLastError() : hipSuccess;

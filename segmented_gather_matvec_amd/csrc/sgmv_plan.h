@@ -102,7 +102,7 @@ struct MfmaParams {
   int32_t n_rows, h_in, h_out, num_segs, num_loras;
   int32_t num_units64, direct_units64;  // units of <= 64 rows of one segment
   int32_t ksplit, kc, chunks_per_wg;
-  // Expand tiles of expand_rows (16 or 64) rows of one segment: num_units_x of them.
+  // Expand tiles of expand_rows (16, 32 or 64) rows of one segment: num_units_x of them.
   int32_t expand_rows, num_units_x, direct_units_x;
   // 1: no reduce launch; the expand sums the ksplit partial planes of its rows
   // itself (in plane order, the reduce's order) instead of reading V.

@@ -162,7 +162,8 @@ static void problems(std::mt19937_64& rng) {
       const MfmaPlan m = plan_mfma(p);
       CHECK(m.ksplit >= 1 && m.kc % sgmv::kMfmaKChunk == 0);
       CHECK((int64_t)m.ksplit * m.kc >= p.h_in && (int64_t)(m.ksplit - 1) * m.kc < p.h_in);
-      CHECK(m.chunks_per_wg >= 1 && (m.expand_rows == 16 || m.expand_rows == 64));
+      CHECK(m.chunks_per_wg >= 1 && (m.expand_rows == 16 || m.expand_rows == 32 || m.expand_rows == 64));
+      CHECK(m.expand_rows != 32 || p.rank <= 16);
     }
     // the decode slots sit after every other route's area
     const WsLayout w = apply_ws_layout(p);
