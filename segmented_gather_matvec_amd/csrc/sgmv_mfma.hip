@@ -149,10 +149,20 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_shrink_kernel(MfmaParams p
       a[m][0] = load_stream(Ak + (ok && h < k1 ? (int64_t)h * a_stride + jg * 8 : 0));
       a[m][1] = load_stream(Ak + (ok && h + 1 < k1 ? (int64_t)(h + 1) * a_stride + jg * 8 : 0));
     }
+    // A wave's X load covers 64 of the 128 bytes of 16 row lines; the next
+    // k-step's load covers the other half.  At rank <= 16 (a small A_k stage)
+    // X goes through the L1, so the second half hits there instead of asking
+    // L2 again (mixed r = 16 batches: 11008 -> 4096 67.7 -> 58.8 us,
+    // 4096 -> 11008 76.4 -> 70.8 us); at rank 64 the cached X costs the A_k
+    // stages their L2 reuse (4096 -> 11008: 89.3 -> 92.7 us) and stays
+    // streaming.
 #pragma unroll
     for (int s = 0; s < MS; ++s) {
       const int h = kk + s * 32 + q * 8;
-      x[s] = load_stream(xrow + (h < k1 ? h : 0));
+      if constexpr (R <= 16)
+        x[s] = load_vec(xrow + (h < k1 ? h : 0));
+      else
+        x[s] = load_stream(xrow + (h < k1 ? h : 0));
     }
   };
 
