@@ -19,10 +19,15 @@ LoRA assignment), where one step is the whole forward.
 
 Prints one JSON line.  The timed region is K back-to-back steps on one stream,
 with HIP events recorded on that stream at both ends and a device
-synchronisation before and after.  value = whole-job algorithmic GB/s over the
-device time between the two events (ms_per_step and tokens_per_s come from the
-same device time); the host wall clock around the region, which adds the fixed
-cost of the synchronisations and of the first launch, is reported beside it
+synchronisation before and after.  A bounded sleep kernel (about 200 us, timed
+and reported as preroll_us) is queued ahead of the first event, so the host has
+already enqueued the first steps when the device clock starts and the events
+time the K steps running back to back, not the host-to-device latency of the
+first launch (about 15 us, a sixth of a 20-step region of 5 us calls).  value =
+whole-job algorithmic GB/s over the device time between the two events
+(ms_per_step and tokens_per_s come from the same device time); the host wall
+clock around the region less the pre-roll, which adds the fixed cost of the
+synchronisations and of the first launch, is reported beside it
 (wall_ms_per_step, wall_value).  roofline.achieved = algorithmic bytes per
 launch / mean launch duration from the same events; roofline.traffic = HBM
 bytes per launch from the committed counter runs (FETCH_SIZE + WRITE_SIZE
@@ -817,6 +822,24 @@ def base_rows_curve(batches=(8, 16, 32, 64, 128, 256, 512, 1024), steps=160):
             "curve": curve}
 
 
+def preroll_cycles(stream, target_us=200.0):
+    """Cycle count for torch's sleep kernel that keeps the stream busy for
+    about target_us, from one timed calibration launch after an untimed one
+    (the first launch also loads the kernel's code, about 1 ms); bounded so a
+    clock that reads slower than expected still gives a finite pre-roll."""
+    import torch
+    probe = 100000
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(probe)
+    torch.cuda.synchronize()
+    a.record(stream)
+    torch.cuda._sleep(probe)
+    b.record(stream)
+    torch.cuda.synchronize()
+    us = max(a.elapsed_time(b) * 1e3, 1.0)
+    return int(min(probe * target_us / us, 20 * probe))
+
+
 def cpu_baseline(seconds=10.0, threads=0):
     """The oracle as it stands, on a host copy of the headline workload's shape
     (threads: 0 = every host core OpenMP offers)."""
@@ -1066,10 +1089,13 @@ def main():
         torch.cuda.synchronize()
 
     # Timed region: K steps between two device synchronisations, with HIP
-    # events recorded on the launch stream at both ends.
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # events recorded on the launch stream at both ends, behind the pre-roll.
+    cycles = preroll_cycles(stream)
+    ep, e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ep.record(stream)
+    torch.cuda._sleep(cycles)
     e0.record(stream)
     if graph is not None:
         graph.replay()
@@ -1078,7 +1104,8 @@ def main():
             bench.step(c, sid)
     e1.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    preroll_s = ep.elapsed_time(e0) * 1e-3
+    wall = time.perf_counter() - t0 - preroll_s
     ev_s = e0.elapsed_time(e1) * 1e-3
     ms_per_step = ev_s / K * 1e3
     launch_s = ev_s / (K * bench.calls_per_step)
@@ -1108,6 +1135,7 @@ def main():
         "launch_us_mean_events": round(launch_s * 1e6, 3),
         "wall_ms_per_step": round(wall / K * 1e3, 6),
         "wall_value": round(bench.bytes * K / wall / 1e9, 2),
+        "preroll_us": round(preroll_s * 1e6, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic},
