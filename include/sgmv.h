@@ -169,7 +169,7 @@ sgmv_status_t sgmv_workspace_bytes(const sgmv_problem_t* problem, size_t* bytes)
 typedef enum sgmv_route {
   SGMV_ROUTE_NONE = 0,    /* nothing to do (no rows or segments) */
   SGMV_ROUTE_DECODE = 1,  /* one launch: shrink, on-chip exchange, expand */
-  SGMV_ROUTE_MFMA = 2,    /* matrix-core shrink, split reduce (summed by the expand up to 8 splits), matrix-core expand */
+  SGMV_ROUTE_MFMA = 2,    /* matrix-core shrink, split reduce (summed by the expand up to 8 splits, 32 at rank <= 16), matrix-core expand */
   SGMV_ROUTE_VECTOR = 3   /* split-K vector shrink, then vector expand */
 } sgmv_route_t;
 

@@ -129,8 +129,13 @@ constexpr int kMfmaShortExpandRows = 16; // expand tile rows for short tiles
 constexpr int kMfmaLowRankExpandRows = 32;  // expand tile rows for full tiles at rank <= 16
 constexpr int kMfmaShortChunksPerWg = 3;
 // Up to this many partial planes the expand sums them itself and the reduce
-// launch is skipped.
+// launch is skipped.  At rank <= 16 a plane is a quarter of rank 64's, and
+// full tiles fold up to 32 of them (mixed r = 16 11008 -> 4096, 9 planes:
+// 58.5 -> 56.4 us per call).  Short tiles re-read the planes for every column
+// group and keep the launch beyond 8 (folding 20 planes cost the 13B forward),
+// as do full tiles at rank 64 (9 planes at 11008 -> 4096 were 9% slower).
 constexpr int kMfmaFoldPlanes = 8;
+constexpr int kMfmaLowRankFoldPlanes = 32;
 
 MfmaPlan plan_mfma(const sgmv_problem_t& p) {
   MfmaPlan m;
@@ -173,7 +178,8 @@ MfmaPlan plan_mfma(const sgmv_problem_t& p) {
     m.chunks_per_wg = (int)ceil_div(nchunks, groups);
   }
   m.partial_bytes = (size_t)m.ksplit * (size_t)p.n_rows * p.rank * sizeof(float);
-  m.fold = m.ksplit <= kMfmaFoldPlanes ? 1 : 0;
+  const bool low_rank_full = p.rank <= 16 && m.expand_rows != kMfmaShortExpandRows;
+  m.fold = m.ksplit <= (low_rank_full ? kMfmaLowRankFoldPlanes : kMfmaFoldPlanes) ? 1 : 0;
   return m;
 }
 

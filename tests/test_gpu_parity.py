@@ -295,6 +295,22 @@ def test_integer_exact_shrink_bitwise(variant):
     assert np.array_equal(V, oracle.sgmv_shrink("bf16", X, A, seg, lidx))
 
 
+@pytest.mark.parametrize("rank,h_in,launches", [(16, 4096, 2), (64, 8192, 3)])
+def test_integer_exact_many_planes_bitwise(rank, h_in, launches):
+    """A long H1 on full 64-row tiles: 16 partial planes summed by the expand
+    itself at rank 16, 11 planes and a reduce launch at rank 64.  Integer inputs
+    make every result exact, so both ways of summing the planes must give the
+    oracle's bits."""
+    rng = np.random.default_rng(5000 + rank)
+    m, c = INT_EXACT[("bf16", rank)]
+    X, A, B, Y0 = workloads.integer_exact(rng, 256, h_in, 256, rank, 3, "bf16", m, c)
+    call = DeviceCall("bf16", X, A, B, Y0, [0, 128, 256], [2, 0], variant=sg.SGMV_VARIANT_MFMA)
+    info = sg.sgmv_query_plan(call.problem)
+    assert (info.route, info.launches) == (sg.SGMV_ROUTE_MFMA, launches), info.as_dict()
+    assert info.splits > 8, info.as_dict()
+    assert np.array_equal(oracle.decode(to_bits(call.apply()), "bf16"), call.oracle_apply())
+
+
 # ------------------------------------------------------------ edge cases
 
 def rand_inputs(seed, n, h_in, h_out, rank, P, dtype="f16"):
