@@ -231,15 +231,22 @@ __global__ __launch_bounds__(kThreads) void sgmv_base_partial_kernel(BaseParams 
   };
 
   // Ping-pong over stage pairs; a stage past k1 loads clamped addresses and
-  // contributes zeros.
+  // contributes zeros.  The loop body issues its loads unconditionally (a
+  // load under a branch makes the compiler wait for every load in flight,
+  // the next stage's included, before the current stage is used); the last
+  // stage pair, which issues nothing beyond itself, is peeled.
   u32x4 wA[NWP][2], xA[NXV], wB[NWP][2], xB[NXV];
   issue(k0, wA, xA);
-  for (int kk = k0; kk < k1; kk += 2 * KS) {
+  int kk = k0;
+  for (; kk + 2 * KS < k1; kk += 2 * KS) {
     issue(kk + KS, wB, xB);
     compute(kk, wA, xA);
-    if (kk + 2 * KS < k1) issue(kk + 2 * KS, wA, xA);
+    issue(kk + 2 * KS, wA, xA);
     compute(kk + KS, wB, xB);
   }
+  issue(kk + KS, wB, xB);
+  compute(kk, wA, xA);
+  compute(kk + KS, wB, xB);
 
   // D[4q+i][ml] of tile (rt, j): row rt*16 + 4q + i, column c0 + (wave*NTW + j)*16 + ml.
   float* dst = p.partials + (int64_t)g * p.plane_stride;
