@@ -421,15 +421,16 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_expand_kernel(MfmaParams p
   constexpr int NVF = MT * R / 4;                       // float4 of V in the tile
   constexpr int NV4 = (NVF + kThreads - 1) / kThreads;  // ... per thread
   f32x4 vv[NV4];
+  u32x4 bvA[NBP][2], yvA[NYV], bvB[NBP][2], yvB[NYV];
   if (p.fold_planes) {
     // V = the sum of the shrink's partial planes, added in plane order from
     // zero as the reduce launch would (same bits), kBatch planes in flight.
+    // The first batch is loaded before the first chunk's B_k and Y, so that
+    // its sum waits for the planes but not for the chunk.
     constexpr int kBatch = 4;
     const float* Pp = p.partials + (int64_t)blockIdx.y * p.proj_stride;
-#pragma unroll
-    for (int m = 0; m < NV4; ++m) vv[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int k0 = 0; k0 < p.ksplit; k0 += kBatch) {
-      f32x4 pv[kBatch][NV4];
+    f32x4 pv[kBatch][NV4];
+    auto load_planes = [&](int k0) {
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
         const int64_t k = k0 + u < p.ksplit ? k0 + u : p.ksplit - 1;
@@ -441,6 +442,8 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_expand_kernel(MfmaParams p
                                                      (int64_t)(r0 + (rr < L ? rr : 0)) * R + o % R);
         }
       }
+    };
+    auto add_planes = [&](int k0) {
 #pragma unroll
       for (int u = 0; u < kBatch; ++u)
 #pragma unroll
@@ -448,6 +451,15 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_expand_kernel(MfmaParams p
           const f32x4 a = vv[m] + pv[u][m];
           vv[m] = k0 + u < p.ksplit ? a : vv[m];
         }
+    };
+#pragma unroll
+    for (int m = 0; m < NV4; ++m) vv[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    load_planes(0);
+    issue(ch0, bvA, yvA);
+    add_planes(0);
+    for (int k0 = kBatch; k0 < p.ksplit; k0 += kBatch) {
+      load_planes(k0);
+      add_planes(k0);
     }
   } else {
 #pragma unroll
@@ -456,9 +468,8 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_expand_kernel(MfmaParams p
       const int rr = o / R;
       vv[m] = *reinterpret_cast<const f32x4*>(Vp + (int64_t)(r0 + (rr < L ? rr : 0)) * R + o % R);
     }
+    issue(ch0, bvA, yvA);
   }
-  u32x4 bvA[NBP][2], yvA[NYV], bvB[NBP][2], yvB[NYV];
-  issue(ch0, bvA, yvA);
 #pragma unroll
   for (int m = 0; m < NV4; ++m) {
     const int o = (t + kThreads * m) * 4;
