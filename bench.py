@@ -1090,12 +1090,14 @@ def main():
 
     # Timed region: K steps between two device synchronisations, with HIP
     # events recorded on the launch stream at both ends, behind the pre-roll.
-    cycles = preroll_cycles(stream)
+    sleep = getattr(torch.cuda, "_sleep", None)  # torch's internal spin kernel; absent: no pre-roll
+    cycles = preroll_cycles(stream) if sleep is not None else 0
     ep, e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ep.record(stream)
-    torch.cuda._sleep(cycles)
+    if cycles:
+        sleep(cycles)
     e0.record(stream)
     if graph is not None:
         graph.replay()
