@@ -328,7 +328,8 @@ class SingleCallBench:
                 "lora_pool": self.lpool, "physical_lora_pool": self.ppool, "xy_copies": self.copies,
                 "row_layout": {"none": "segment order", "kernel": "request order, kernel row map",
                                "torch": "request order, torch gather/scatter"}[self.row_map],
-                "algorithmic_bytes_per_step": self.bytes}
+                "algorithmic_bytes_per_step": self.bytes,
+                "plan": self.sg.sgmv_query_plan(self.problem).as_dict()}
 
 
 class MixedRankBench:
@@ -602,7 +603,8 @@ class ModelForwardBench:
                 "calls_per_step": len(self.batched), "calls_per_layer": self.group_names,
                 "row_layout": {"none": "segment order", "kernel": "request order, kernel row map",
                                "torch": "request order, torch gather/scatter"}[self.row_map],
-                "algorithmic_bytes_per_step": self.bytes}
+                "algorithmic_bytes_per_step": self.bytes,
+                "plan": self.sg.sgmv_query_plan(self.problem).as_dict()}
 
 
 def latency_curve(batches=(1, 2, 4, 8, 16, 32, 64), steps=200, warmup=20):

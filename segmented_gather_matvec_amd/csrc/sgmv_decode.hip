@@ -356,9 +356,10 @@ __global__ __launch_bounds__(kThreads) void sgmv_decode_kernel(DecodeParams p) {
   const int parts = G * PW;                   // partials per output
   const int per_round = kStage / n_out;       // partials staged per round (>= 1)
   float vsum = 0.f;
-  // The wait ends at a deadline on the constant-rate real-time counter.  A
-  // limit of 0 (the host's test hook) waits for a tag no partial carries, so
-  // every workgroup gives up at its first check.
+  // The wait ends at a deadline on the constant-rate real-time counter, read
+  // right after each round of polls is issued so that its latency overlaps
+  // theirs.  A limit of 0 (the host's test hook) waits for a tag no partial
+  // carries, so every workgroup gives up after one round of polls.
   const uint64_t deadline = __builtin_amdgcn_s_memrealtime() + p.wait_ticks;
   const uint32_t want = p.wait_ticks != 0 ? tag : ~tag;
   for (int p0 = 0; p0 < parts; p0 += per_round) {
@@ -376,16 +377,18 @@ __global__ __launch_bounds__(kThreads) void sgmv_decode_kernel(DecodeParams p) {
       w[m] = it < items ? fetch_tagged(src[m]) : 0;
     }
     bool done;
+    uint64_t now = 0;  // read beside each round of polls, checked at the next
     for (;;) {
       done = true;
 #pragma unroll
       for (int m = 0; m < kPollPerThread; ++m)
         if (t + kThreads * m < items && (uint32_t)(w[m] >> 32) != want) done = false;
-      if (done || __builtin_amdgcn_s_memrealtime() > deadline) break;
+      if (done || now > deadline) break;
       __builtin_amdgcn_s_sleep(1);
 #pragma unroll
       for (int m = 0; m < kPollPerThread; ++m)
         if (t + kThreads * m < items && (uint32_t)(w[m] >> 32) != want) w[m] = fetch_tagged(src[m]);
+      now = __builtin_amdgcn_s_memrealtime();
     }
 #pragma unroll
     for (int m = 0; m < kPollPerThread; ++m) {
