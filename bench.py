@@ -165,7 +165,7 @@ class SingleCallBench:
     value projections, each with its own LoRA pool and output) as one
     sgmv_lora_apply_batched call per step."""
 
-    def __init__(self, name, variant=0, splits=0, row_map="none"):
+    def __init__(self, name, variant=0, splits=0, row_map="none", host_meta=False):
         import numpy as np
         import torch
         import segmented_gather_matvec_amd as sg
@@ -173,9 +173,12 @@ class SingleCallBench:
 
         self.name, self.sg, self.torch = name, sg, torch
         self.row_map = row_map
+        self.host_meta = host_meta
         self.nproj = 3 if "_qkv_" in name else 1
         if self.nproj > 1 and row_map != "none":
             raise SystemExit("the projection-batched workloads take rows in segment order only")
+        if host_meta and (self.nproj > 1 or row_map != "none"):
+            raise SystemExit("--host-meta runs one projection with rows in segment order")
         (self.dtype, self.h_in, self.h_out, self.rank, self.n, seg, lidx, self.lpool,
          seed) = workload_layout(name)
         seg, lidx = np.asarray(seg, np.int32), np.asarray(lidx, np.int32)
@@ -234,6 +237,13 @@ class SingleCallBench:
         self.perm64 = self.perm.to(torch.int64)
         lib = sg.load_library()
         self.fn, self.fn_batched = lib.sgmv_lora_apply, lib.sgmv_lora_apply_batched
+        if host_meta:
+            # sgmv_lora_apply_host_meta: metadata and pointer tables from host memory
+            self.fn = lib.sgmv_lora_apply_host_meta
+            self.A_tab_h = [np.ascontiguousarray(tab.cpu().numpy().astype(np.uint64)) for tab in self.A_tab]
+            self.B_tab_h = [np.ascontiguousarray(tab.cpu().numpy().astype(np.uint64)) for tab in self.B_tab]
+            self.seg_hc = np.ascontiguousarray(seg, np.int32)
+            self.lidx_hc = np.ascontiguousarray(lidx if lidx.size else np.zeros(1, np.int32), np.int32)
         if row_map == "torch":
             self.Xs = torch.empty_like(self.X[0])
             self.Ys = torch.empty_like(self.Y[0])
@@ -264,6 +274,10 @@ class SingleCallBench:
                 self.args.append((pb, self.Xs.data_ptr(), self.A_tab[t].data_ptr(), self.B_tab[t].data_ptr(),
                                   self.Ys.data_ptr(), self.seg.data_ptr(), self.lidx.data_ptr(),
                                   self.ws.data_ptr(), wsn))
+            elif self.host_meta:
+                self.args.append((pb, self.X[x].data_ptr(), self.A_tab_h[t].ctypes.data,
+                                  self.B_tab_h[t].ctypes.data, self.Y[x].data_ptr(), self.seg_hc.ctypes.data,
+                                  self.lidx_hc.ctypes.data, self.ws.data_ptr(), wsn))
             else:
                 self.args.append((pb, self.X[x].data_ptr(), self.A_tab[t].data_ptr(), self.B_tab[t].data_ptr(),
                                   self.Y[x].data_ptr(), self.seg.data_ptr(), self.lidx.data_ptr(),
@@ -329,6 +343,9 @@ class SingleCallBench:
                 "row_layout": {"none": "segment order", "kernel": "request order, kernel row map",
                                "torch": "request order, torch gather/scatter"}[self.row_map],
                 "algorithmic_bytes_per_step": self.bytes,
+                "entry_point": "sgmv_lora_apply_host_meta" if self.host_meta else
+                               ("sgmv_lora_apply_batched" if self.nproj > 1 or self.row_map == "kernel"
+                                else "sgmv_lora_apply"),
                 "plan": self.sg.sgmv_query_plan(self.problem).as_dict()}
 
 
@@ -604,7 +621,8 @@ class ModelForwardBench:
                 "row_layout": {"none": "segment order", "kernel": "request order, kernel row map",
                                "torch": "request order, torch gather/scatter"}[self.row_map],
                 "algorithmic_bytes_per_step": self.bytes,
-                "plan": self.sg.sgmv_query_plan(self.problem).as_dict()}
+                "plans": {f"{h_in}to{h_out}": self.sg.sgmv_query_plan(prob).as_dict()
+                          for (h_in, h_out), prob in self.probs.items()}}
 
 
 def latency_curve(batches=(1, 2, 4, 8, 16, 32, 64), steps=200, warmup=20):
@@ -1019,6 +1037,9 @@ def main():
     ap.add_argument("--row-map", choices=["none", "kernel", "torch"], default="none",
                     help="rows of X and Y in segment order (none), or in request order gathered and "
                          "scattered by the kernels' row map (kernel) or by torch around each call (torch)")
+    ap.add_argument("--host-meta", action="store_true",
+                    help="single-projection workloads: call sgmv_lora_apply_host_meta (segment bounds and "
+                         "LoRA pointer tables from host memory, passed in the kernel's arguments)")
     ap.add_argument("--curve", action="store_true",
                     help="instead of one workload: the LoRA addend's latency against batch size for "
                          "SGMV and two naive LoRA implementations (one JSON line)")
@@ -1070,7 +1091,8 @@ def main():
         bench = ModelForwardBench(args.workload, variant=variant, splits=args.splits,
                                   batch_projections=not args.no_batch, row_map=args.row_map)
     else:
-        bench = SingleCallBench(args.workload, variant=variant, splits=args.splits, row_map=args.row_map)
+        bench = SingleCallBench(args.workload, variant=variant, splits=args.splits, row_map=args.row_map,
+                                host_meta=args.host_meta)
     worst = None if args.no_check else bench.check_sample()
 
     stream = torch.cuda.current_stream()

@@ -228,6 +228,32 @@ sgmv_status_t sgmv_lora_apply(const sgmv_problem_t* problem, const void* X,
                               const int32_t* seg_indptr, const int32_t* lora_idx, void* ws,
                               size_t ws_bytes, void* stream);
 
+/* Fused apply with the segment metadata and the LoRA pointer tables on the
+ * host: the segments the host builder produced for a batch (Punica README,
+ * SGMV paragraph: a batch grouped into segments, each gathering its own
+ * LoRA's weights) need not be copied to the device first.  Same result, bit
+ * for bit, as sgmv_lora_apply on device copies of the same arrays.  The
+ * library gathers each segment's A_k and B_k pointers on the host and passes
+ * them with the segment bounds in the kernel's arguments, so the kernel reads
+ * no metadata from device memory before its first weight load (one dependent
+ * memory trip fewer than sgmv_lora_apply).
+ *   A_ptrs_host, B_ptrs_host  [num_loras]     host arrays of device pointers
+ *   seg_indptr_host           [num_segs + 1]  host arrays, checked as by
+ *   lora_idx_host             [num_segs]      sgmv_check_segments
+ * The host arrays are read during the call only.  Only for calls that the
+ * one-launch decode route takes (decode-shaped batches) with at most
+ * SGMV_HOST_META_MAX_SEGS segments; otherwise SGMV_ERR_UNSUPPORTED and nothing
+ * is launched (use sgmv_lora_apply).  A null A_k or B_k of a segment gives
+ * SGMV_ERR_INVALID_ARG, one not 16-byte aligned SGMV_ERR_UNSUPPORTED.
+ * Workspace (sgmv_workspace_bytes), stream and device-sharing rules as for
+ * sgmv_lora_apply. */
+#define SGMV_HOST_META_MAX_SEGS 64
+sgmv_status_t sgmv_lora_apply_host_meta(const sgmv_problem_t* problem, const void* X,
+                                        const void* const* A_ptrs_host, const void* const* B_ptrs_host,
+                                        void* Y, const int32_t* seg_indptr_host,
+                                        const int32_t* lora_idx_host, void* ws, size_t ws_bytes,
+                                        void* stream);
+
 /* Bound on how long a workgroup of the one-launch decode route waits for the
  * partial sums of the other workgroups of its unit, in microseconds (process
  * wide, applies to later calls; default 1000000).  0 makes every such wait

@@ -35,10 +35,11 @@ ENTRY_POINTS = ("sgmv_status_str", "sgmv_build_segments", "sgmv_check_problem",
                 "sgmv_expand", "sgmv_lora_apply", "sgmv_lora_apply_batched", "sgmv_base_workspace_bytes",
                 "sgmv_base_lora_apply", "sgmv_base_packed_weight_bytes", "sgmv_base_pack_weight",
                 "sgmv_base_lora_apply_packed", "sgmv_set_wait_limit", "sgmv_take_device_errors",
-                "sgmv_lora_apply_noalloc", "sgmv_base_lora_apply_partial")
+                "sgmv_lora_apply_noalloc", "sgmv_base_lora_apply_partial", "sgmv_lora_apply_host_meta")
 SGMV_DEVICE_ERR_WAIT_TIMEOUT = 1
 SGMV_NOALLOC_MAX_WORKSPACE = 16 << 20
 SGMV_BASE_MAX_ROWS = 128
+SGMV_HOST_META_MAX_SEGS = 64
 
 
 class SgmvError(RuntimeError):
@@ -112,6 +113,7 @@ def load_library(path: str = LIB_PATH):
     lib.sgmv_take_device_errors.argtypes = [ctypes.POINTER(ctypes.c_uint32)]
     lib.sgmv_lora_apply_noalloc.argtypes = [prob, P, P, P, P, P, P, P]
     lib.sgmv_base_lora_apply_partial.argtypes = [prob, P, P, I32, P, P, P, P, P, P, SZ, P]
+    lib.sgmv_lora_apply_host_meta.argtypes = [prob, P, P, P, P, P, P, P, SZ, P]
     for name in ENTRY_POINTS[1:]:
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -266,6 +268,29 @@ def sgmv_lora_apply(problem, X, A_ptrs, B_ptrs, Y, seg_indptr, lora_idx, ws, str
                                         ws.numel() * ws.element_size() if ws is not None else 0,
                                         _stream(stream))
     _check(st, "sgmv_lora_apply")
+
+
+def sgmv_lora_apply_host_meta(problem, X, A_ptrs_host, B_ptrs_host, Y, seg_indptr_host, lora_idx_host, ws,
+                              stream=None):
+    """sgmv_lora_apply with the segment metadata and the LoRA pointer tables on the host
+    (numpy int32 seg_indptr / lora_idx, uint64 or int64 arrays of device pointers),
+    carried in the kernel's arguments; decode-shaped calls of at most
+    SGMV_HOST_META_MAX_SEGS segments only.  Asynchronous."""
+    import numpy as np
+    dt = _torch_dtype(problem)
+    _need(X, "X", dt); _need(Y, "Y", dt)
+    _need(ws, "ws")
+    a = np.ascontiguousarray(A_ptrs_host, dtype=np.uint64)
+    b = np.ascontiguousarray(B_ptrs_host, dtype=np.uint64)
+    seg = np.ascontiguousarray(seg_indptr_host, dtype=np.int32)
+    lidx = np.ascontiguousarray(lora_idx_host, dtype=np.int32)
+    if lidx.size == 0:
+        lidx = np.zeros(1, np.int32)
+    st = load_library().sgmv_lora_apply_host_meta(ctypes.byref(problem), _ptr(X), a.ctypes.data, b.ctypes.data,
+                                                  _ptr(Y), seg.ctypes.data, lidx.ctypes.data, _ptr(ws),
+                                                  ws.numel() * ws.element_size() if ws is not None else 0,
+                                                  _stream(stream))
+    _check(st, "sgmv_lora_apply_host_meta")
 
 
 def sgmv_lora_apply_noalloc(problem, X, A_ptrs, B_ptrs, Y, seg_indptr, lora_idx, stream=None):

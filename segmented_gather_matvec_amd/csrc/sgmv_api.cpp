@@ -22,6 +22,7 @@ using sgmv::VecParams;
 constexpr int kMaxDevices = 64;
 
 static_assert(sgmv::kDecodeErrWaitTimeout == SGMV_DEVICE_ERR_WAIT_TIMEOUT, "error bits of the ABI");
+static_assert(sgmv::kInlineSegs == SGMV_HOST_META_MAX_SEGS, "segments carried in the kernel arguments");
 
 // Longest wait of a decode-route workgroup for its unit's other partials
 // (sgmv_set_wait_limit).  A legitimate wait lasts microseconds; the bound is
@@ -58,17 +59,16 @@ int decode_variant(const sgmv_problem_t& p, bool map, bool het) {
 
 int decode_capacity(int dtype, int rank, int rb, int variant) {
   static std::mutex mu;
-  static int cache[kMaxDevices][2][4][3][8];
-  static bool init[kMaxDevices][2][4][3][8];
+  static int cache[kMaxDevices][2][4][3][sgmv::kDecodeInlineVariant + 1];
+  static bool init[kMaxDevices][2][4][3][sgmv::kDecodeInlineVariant + 1];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
-  if (variant < 0 || variant > 7) return 0;
+  if (variant < 0 || variant > sgmv::kDecodeInlineVariant) return 0;
   const int ri = rank == 8 ? 0 : rank == 16 ? 1 : rank == 32 ? 2 : 3;
   const int bi = rb == 1 ? 0 : rb == 4 ? 1 : 2;
   std::lock_guard<std::mutex> lock(mu);
   if (!init[dev][dtype][ri][bi][variant]) {
-    cache[dev][dtype][ri][bi][variant] = sgmv::decode_resident_capacity(
-        dtype, rank, rb, (variant & 1) != 0, (variant & 2) != 0, (variant & 4) != 0);
+    cache[dev][dtype][ri][bi][variant] = sgmv::decode_resident_capacity(dtype, rank, rb, variant);
     init[dev][dtype][ri][bi][variant] = true;
   }
   return cache[dev][dtype][ri][bi][variant];
@@ -175,6 +175,38 @@ sgmv::Projection kernel_projection(const sgmv_projection_t& pj) {
   return k;
 }
 
+// Arguments of the decode kernel for plan d; ws is projection 0's workspace
+// slice, stride the bytes between slices.
+hipError_t decode_params(const sgmv_problem_t& p, const DecodePlan& d, const void* X, const sgmv_projection_t* pj,
+                         int np, const int32_t* seg_indptr, const int32_t* lora_idx, const int32_t* row_idx,
+                         char* ws, size_t stride, sgmv::DecodeParams* out) {
+  sgmv::DecodeParams& q = *out;
+  q = sgmv::DecodeParams{};
+  const hipError_t e = sgmv::decode_error_word(&q.errors);
+  if (e != hipSuccess) return e;
+  q.wait_ticks = wait_ticks();
+  q.X = static_cast<const uint16_t*>(X);
+  for (int i = 0; i < np; ++i) q.proj[i] = kernel_projection(pj[i]);
+  q.seg_indptr = seg_indptr;
+  q.lora_idx = lora_idx;
+  q.row_idx = row_idx;
+  q.slots = reinterpret_cast<uint64_t*>(ws + apply_ws_layout(p).decode_off);
+  q.slot_stride = (int64_t)(stride / sizeof(uint64_t));
+  q.n_rows = p.n_rows;
+  q.h_in = p.h_in;
+  q.h_out = p.h_out;
+  q.num_segs = p.num_segs;
+  q.num_loras = p.num_loras;
+  q.num_units = (int32_t)d.num_units;
+  q.splits = d.splits;
+  q.kc = d.kc;
+  q.cw = d.cw;
+  q.direct_units = d.direct;
+  q.split_major = d.split_major;
+  q.round_units = (int32_t)d.round_units;
+  return hipSuccess;
+}
+
 // sgmv_lora_apply for num_proj projections that share X, the shapes and the
 // segments.  Projection i uses the workspace slice [i*stride, i*stride + need).
 // clear_counters: zero the two-launch route's counters with a fill kernel
@@ -199,27 +231,8 @@ sgmv_status_t apply(const sgmv_problem_t& p, const void* X, const sgmv_projectio
       return SGMV_OK;
     }
     sgmv::DecodeParams q{};
-    if (sgmv::decode_error_word(&q.errors) != hipSuccess) return SGMV_ERR_HIP;
-    q.wait_ticks = wait_ticks();
-    q.X = static_cast<const uint16_t*>(X);
-    for (int i = 0; i < np; ++i) q.proj[i] = kernel_projection(pj[i]);
-    q.seg_indptr = seg_indptr;
-    q.lora_idx = lora_idx;
-    q.row_idx = row_idx;
-    q.slots = reinterpret_cast<uint64_t*>(ws + apply_ws_layout(p).decode_off);
-    q.slot_stride = (int64_t)(stride / sizeof(uint64_t));
-    q.n_rows = p.n_rows;
-    q.h_in = p.h_in;
-    q.h_out = p.h_out;
-    q.num_segs = p.num_segs;
-    q.num_loras = p.num_loras;
-    q.num_units = (int32_t)d.num_units;
-    q.splits = d.splits;
-    q.kc = d.kc;
-    q.cw = d.cw;
-    q.direct_units = d.direct;
-    q.split_major = d.split_major;
-    q.round_units = (int32_t)d.round_units;
+    if (decode_params(p, d, X, pj, np, seg_indptr, lora_idx, row_idx, ws, stride, &q) != hipSuccess)
+      return SGMV_ERR_HIP;
     // One launch per pass of round_units units (a single one when they all
     // fit on the device at once); each launch's workgroups are co-resident.
     for (int64_t pass = 0; pass < d.rounds; ++pass) {
@@ -465,6 +478,44 @@ sgmv_status_t sgmv_lora_apply_batched(const sgmv_problem_t* p, const void* X,
   if (ws_bytes < stride * (size_t)(num_projections - 1) + need) return SGMV_ERR_WORKSPACE;
   return apply(*p, X, projections, num_projections, seg_indptr, lora_idx, row_idx, static_cast<char*>(ws),
                stride, static_cast<hipStream_t>(stream));
+}
+
+sgmv_status_t sgmv_lora_apply_host_meta(const sgmv_problem_t* p, const void* X, const void* const* A_ptrs_host,
+                                        const void* const* B_ptrs_host, void* Y, const int32_t* seg_indptr_host,
+                                        const int32_t* lora_idx_host, void* ws, size_t ws_bytes, void* stream) {
+  sgmv_status_t st = sgmv_check_problem(p);
+  if (st != SGMV_OK) return st;
+  if (nothing_to_do(*p)) return SGMV_OK;
+  if (!X || !A_ptrs_host || !B_ptrs_host || !Y || !seg_indptr_host || !lora_idx_host) return SGMV_ERR_INVALID_ARG;
+  if (!aligned16(X) || !aligned16(Y)) return SGMV_ERR_UNSUPPORTED;
+  st = sgmv_check_segments(p, seg_indptr_host, lora_idx_host);
+  if (st != SGMV_OK) return st;
+  if (p->num_segs > sgmv::kInlineSegs) return SGMV_ERR_UNSUPPORTED;
+  // Each segment's A_k and B_k, gathered here on the host.
+  sgmv::InlineMeta m{};
+  for (int32_t s = 0; s <= p->num_segs; ++s) m.seg[s] = seg_indptr_host[s];
+  for (int32_t s = 0; s < p->num_segs; ++s) {
+    m.a[s] = reinterpret_cast<uint64_t>(A_ptrs_host[lora_idx_host[s]]);
+    m.b[s] = reinterpret_cast<uint64_t>(B_ptrs_host[lora_idx_host[s]]);
+    if (m.a[s] == 0 || m.b[s] == 0) return SGMV_ERR_INVALID_ARG;
+    if ((m.a[s] | m.b[s]) % 16 != 0) return SGMV_ERR_UNSUPPORTED;
+  }
+  if (!ws) return SGMV_ERR_WORKSPACE;
+  if (!aligned16(ws)) return SGMV_ERR_UNSUPPORTED;
+  if (ws_bytes < apply_ws_layout(*p).total) return SGMV_ERR_WORKSPACE;
+  const DecodePlan d = plan_decode(*p, sgmv::kDecodeInlineVariant);
+  if (apply_route(*p, d) != SGMV_ROUTE_DECODE) return SGMV_ERR_UNSUPPORTED;
+  const sgmv_projection_t one{nullptr, nullptr, Y, nullptr, nullptr};
+  sgmv::DecodeParams q{};
+  const size_t stride = (size_t)round_up((int64_t)apply_ws_layout(*p).total, 256);
+  if (decode_params(*p, d, X, &one, 1, nullptr, nullptr, nullptr, static_cast<char*>(ws), stride, &q) != hipSuccess)
+    return SGMV_ERR_HIP;
+  for (int64_t pass = 0; pass < d.rounds; ++pass) {
+    q.unit_base = (int32_t)(pass * d.round_units);
+    if (sgmv::launch_decode_inline(p->dtype, p->rank, d.rb, q, m, static_cast<hipStream_t>(stream)) != hipSuccess)
+      return SGMV_ERR_HIP;
+  }
+  return SGMV_OK;
 }
 
 }  // extern "C"

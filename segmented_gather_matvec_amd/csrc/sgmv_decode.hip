@@ -107,9 +107,12 @@ constexpr int log2_groups() {
 // MAP: rows of X / Y are looked up in a row map.
 // HET: per-LoRA ranks (compact A_k [h_in, r_k], B_k [r_k, h_out]; ranks
 // r_k..R-1 are zero) and / or per-LoRA scales may be given.
+// INL: the segment bounds and each segment's A_k / B_k come in the kernel
+// arguments (m) instead of device tables, so they arrive with the other
+// arguments rather than one dependent memory trip later.
 // Each feature is a template flag, so a call pays only for what it uses.
-template <class T, int R, int RB, bool SMALL, bool MAP, bool HET>
-__global__ __launch_bounds__(kThreads) void sgmv_decode_kernel(DecodeParams p) {
+template <class T, int R, int RB, bool SMALL, bool MAP, bool HET, bool INL>
+__device__ __forceinline__ void decode_body(const DecodeParams& p, const InlineMeta* m) {
   constexpr int JG = R / 8;                  // 128-bit vectors per row of A_k
   constexpr int B0 = log2_groups<R>();
   constexpr int HS = kThreads / JG;          // A_k rows covered by one sweep of the workgroup
@@ -133,8 +136,32 @@ __global__ __launch_bounds__(kThreads) void sgmv_decode_kernel(DecodeParams p) {
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = t >> 6;
+  // INL: lane l fetches segment l's bounds and pointers from the kernel
+  // arguments before anything else (entries past num_segs are not used), so
+  // these loads depend on nothing and go out with the first argument loads.
+  int lo_l = 0, hi_l = 0;
+  uint64_t a_lane = 0, b_lane = 0;
+  if constexpr (INL) {
+    lo_l = m->seg[lane];
+    hi_l = m->seg[lane + 1];
+    a_lane = m->a[lane];
+    b_lane = m->b[lane];
+    // Consumed here, the loads stay ahead of the first branch and overlap the
+    // argument loads; otherwise the compiler sinks them past the argument
+    // checks, one memory trip later.
+    asm volatile("" ::"v"(lo_l), "v"(hi_l), "v"(a_lane), "v"(b_lane));
+  }
   const int G = p.splits;
-  const Projection pr = p.proj[blockIdx.y];
+  // Every projection's entry is loaded at a constant offset and blockIdx.y
+  // selects one: loads at an offset computed from blockIdx.y were issued only
+  // after the first argument loads had returned, a second trip before the
+  // first metadata load.
+  Projection pr = p.proj[0];
+  if constexpr (!INL) {  // (INL launches one projection)
+#pragma unroll
+    for (int i = 1; i < kMaxProjections; ++i)
+      if ((int)blockIdx.y == i) pr = p.proj[i];
+  }
   // A negative size or a null table is a malformed launch (the host rejects
   // both).  Testing every uniform argument here also makes the compiler fetch
   // them all in the first batch of loads instead of one round trip per
@@ -142,9 +169,10 @@ __global__ __launch_bounds__(kThreads) void sgmv_decode_kernel(DecodeParams p) {
   const bool bad_size = (p.num_units | p.splits | p.kc | p.cw | p.direct_units | p.split_major | p.n_rows |
                          p.h_in | p.h_out | p.num_segs | p.num_loras | p.unit_base | (p.round_units - 1) |
                          (int32_t)(p.slot_stride >> 32)) < 0;
-  bool bad_ptr = (p.seg_indptr == nullptr) | (p.lora_idx == nullptr) | (p.X == nullptr) |
-                 (p.slots == nullptr) | (pr.A_ptrs == nullptr) | (pr.B_ptrs == nullptr) | (pr.Y == nullptr) |
-                 (p.errors == nullptr);
+  bool bad_ptr = (p.X == nullptr) | (p.slots == nullptr) | (pr.Y == nullptr) | (p.errors == nullptr);
+  if constexpr (!INL)
+    bad_ptr |= (p.seg_indptr == nullptr) | (p.lora_idx == nullptr) | (pr.A_ptrs == nullptr) |
+               (pr.B_ptrs == nullptr);
   // The optional int32 / fp32 tables are 4-byte aligned (the rank and scale
   // tables are nullable).
   if constexpr (MAP) bad_ptr |= (reinterpret_cast<uintptr_t>(p.row_idx) & 3) != 0 || p.row_idx == nullptr;
@@ -172,10 +200,9 @@ __global__ __launch_bounds__(kThreads) void sgmv_decode_kernel(DecodeParams p) {
   // With at most 64 LoRAs, fetch both pointer tables (one entry per lane) in
   // parallel with the segment metadata instead of after it: the LoRA id then
   // selects its pointers from registers, saving one dependent memory trip.
-  uint64_t a_lane = 0, b_lane = 0;
   int rk_lane = R;
   float sk_lane = 1.f;
-  if (SMALL && lane < p.num_loras) {
+  if (SMALL && !INL && lane < p.num_loras) {
     a_lane = pr.A_ptrs[lane];
     b_lane = pr.B_ptrs[lane];
     if constexpr (HET) {
@@ -183,8 +210,11 @@ __global__ __launch_bounds__(kThreads) void sgmv_decode_kernel(DecodeParams p) {
       if (pr.scales) sk_lane = pr.scales[lane];
     }
   }
-  const Unit un = resolve_unit<RB>(p.seg_indptr, p.lora_idx, p.num_segs, p.num_loras, p.n_rows,
-                                   p.direct_units, unit);
+  Unit un;
+  if constexpr (INL)  // the unit's k is its segment
+    un = resolve_unit_lanes<RB>(lo_l, hi_l, p.num_segs, p.n_rows, p.direct_units, unit);
+  else
+    un = resolve_unit<RB>(p.seg_indptr, p.lora_idx, p.num_segs, p.num_loras, p.n_rows, p.direct_units, unit);
   if (un.L <= 0) return;  // uniform over the workgroup (and over the unit)
   const int L = un.L;
   const int r0 = un.r0;
@@ -194,7 +224,10 @@ __global__ __launch_bounds__(kThreads) void sgmv_decode_kernel(DecodeParams p) {
   const uint16_t* Bk;
   int rk = R;      // rank of this unit's LoRA (row stride of A_k)
   float sk = 1.f;  // scale of its term
-  if constexpr (SMALL) {
+  if constexpr (INL) {
+    Ak = reinterpret_cast<const uint16_t*>(readlane_u64(a_lane, un.k));
+    Bk = reinterpret_cast<const uint16_t*>(readlane_u64(b_lane, un.k));
+  } else if constexpr (SMALL) {
     Ak = reinterpret_cast<const uint16_t*>(readlane_u64(a_lane, un.k));
     Bk = reinterpret_cast<const uint16_t*>(readlane_u64(b_lane, un.k));
     if constexpr (HET) {
@@ -445,6 +478,17 @@ __global__ __launch_bounds__(kThreads) void sgmv_decode_kernel(DecodeParams p) {
   }
 }
 
+template <class T, int R, int RB, bool SMALL, bool MAP, bool HET>
+__global__ __launch_bounds__(kThreads) void sgmv_decode_kernel(DecodeParams p) {
+  decode_body<T, R, RB, SMALL, MAP, HET, false>(p, nullptr);
+}
+
+// One projection, no row map, no rank or scale tables; the metadata in m.
+template <class T, int R, int RB>
+__global__ __launch_bounds__(kThreads) void sgmv_decode_inline_kernel(DecodeParams p, InlineMeta m) {
+  decode_body<T, R, RB, false, false, false, true>(p, &m);
+}
+
 template <class T, int R, int RB>
 hipError_t launch_t(const DecodeParams& p, int num_proj, hipStream_t stream) {
   const unsigned grid = (unsigned)p.round_units * (unsigned)p.splits;
@@ -475,33 +519,54 @@ int per_cu_t() {
   return n;
 }
 
+template <class T, int R, int RB>
+int per_cu_inline_t() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &n, reinterpret_cast<const void*>(&sgmv_decode_inline_kernel<T, R, RB>), kThreads, 0) != hipSuccess)
+    return 0;
+  return n;
+}
+
 // Workgroups of one variant that fit on the device at once.  `variant` holds
-// the pointer-pool, row-map and rank/scale flags as bits 0, 1, 2.
+// the pointer-pool, row-map and rank/scale flags as bits 0, 1, 2, or is
+// kDecodeInlineVariant for the kernel with the metadata in its arguments.
 template <class T, int R, int RB>
 int capacity_t(int variant) {
   using F = int (*)();
-  static constexpr F per_cu[8] = {
+  static constexpr F per_cu[9] = {
       per_cu_t<T, R, RB, false, false, false>, per_cu_t<T, R, RB, true, false, false>,
       per_cu_t<T, R, RB, false, true, false>,  per_cu_t<T, R, RB, true, true, false>,
       per_cu_t<T, R, RB, false, false, true>,  per_cu_t<T, R, RB, true, false, true>,
-      per_cu_t<T, R, RB, false, true, true>,   per_cu_t<T, R, RB, true, true, true>};
+      per_cu_t<T, R, RB, false, true, true>,   per_cu_t<T, R, RB, true, true, true>,
+      per_cu_inline_t<T, R, RB>};
   int dev = 0, cus = 0;
-  if (variant < 0 || variant > 7) return 0;
+  if (variant < 0 || variant > kDecodeInlineVariant) return 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
   return per_cu[variant]() * cus;
 }
 
 // Instantiated (rank, rows per unit) pairs: rank * RB <= 256.
+template <class T, int R, int RB>
+hipError_t launch_inline_t(const DecodeParams& p, const InlineMeta& m, hipStream_t stream) {
+  const unsigned grid = (unsigned)p.round_units * (unsigned)p.splits;
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL((sgmv_decode_inline_kernel<T, R, RB>), dim3(grid, 1), dim3(kThreads), 0, stream, p, m);
+  return hipGetLastError();
+}
+
+// m: launch the kernel with the metadata in its arguments (one projection).
 template <class T>
 hipError_t dispatch(int rank, int rb, const DecodeParams& p, int num_proj, hipStream_t s, int* cap,
-                    int variant) {
+                    int variant, const InlineMeta* m = nullptr) {
 #define SGMV_DECODE_CASE(R_, RB_)                          \
   if (rank == R_ && rb == RB_) {                           \
     if (cap) {                                             \
       *cap = capacity_t<T, R_, RB_>(variant);              \
       return hipSuccess;                                   \
     }                                                      \
+    if (m) return launch_inline_t<T, R_, RB_>(p, *m, s);   \
     return launch_t<T, R_, RB_>(p, num_proj, s);           \
   }
   SGMV_DECODE_CASE(8, 1) SGMV_DECODE_CASE(8, 4) SGMV_DECODE_CASE(8, 16)
@@ -538,8 +603,13 @@ hipError_t launch_decode(int dtype, int rank, int rb, const DecodeParams& p, int
                     : dispatch<F16>(rank, rb, p, num_proj, stream, nullptr, 0);
 }
 
-int decode_resident_capacity(int dtype, int rank, int rb, bool small, bool map, bool het) {
-  const int variant = (small ? 1 : 0) | (map ? 2 : 0) | (het ? 4 : 0);
+hipError_t launch_decode_inline(int dtype, int rank, int rb, const DecodeParams& p, const InlineMeta& m,
+                                hipStream_t stream) {
+  return dtype == 1 ? dispatch<BF16>(rank, rb, p, 1, stream, nullptr, 0, &m)
+                    : dispatch<F16>(rank, rb, p, 1, stream, nullptr, 0, &m);
+}
+
+int decode_resident_capacity(int dtype, int rank, int rb, int variant) {
   int cap = 0;
   if (dtype == 1)
     (void)dispatch<BF16>(rank, rb, DecodeParams{}, 0, nullptr, &cap, variant);

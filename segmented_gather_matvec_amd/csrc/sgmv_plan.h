@@ -90,10 +90,27 @@ constexpr uint32_t kDecodeErrWaitTimeout = 1u;
 hipError_t decode_error_word(uint32_t** word);
 // Launches num_proj projections (blockIdx.y).
 hipError_t launch_decode(int dtype, int rank, int rb, const DecodeParams& p, int num_proj, hipStream_t stream);
+
+// Segment metadata passed in the decode kernel's arguments (calls whose segment
+// bounds and LoRA pointer tables are on the host): the bounds of at most
+// kInlineSegs segments and the A_k / B_k of each segment.
+constexpr int kInlineSegs = 64;
+struct InlineMeta {
+  int32_t seg[kInlineSegs + 1];
+  uint64_t a[kInlineSegs];
+  uint64_t b[kInlineSegs];
+};
+// One projection, no row map, no rank or scale tables; p's table pointers are
+// not used.
+hipError_t launch_decode_inline(int dtype, int rank, int rb, const DecodeParams& p, const InlineMeta& m,
+                                hipStream_t stream);
+
 // Workgroups of the decode kernel variant that fit on the device at once (0 if
-// unknown).
-// small: at most 64 LoRAs; map: a row map; het: rank or scale tables.
-int decode_resident_capacity(int dtype, int rank, int rb, bool small, bool map, bool het);
+// unknown).  variant: bit 0 at most 64 LoRAs, bit 1 a row map, bit 2 rank or
+// scale tables; or kDecodeInlineVariant, the kernel with the metadata in its
+// arguments.
+constexpr int kDecodeInlineVariant = 8;
+int decode_resident_capacity(int dtype, int rank, int rb, int variant);
 
 // Matrix-core kernels for long segments: shrink (+ reduce of the H1 split),
 // then expand.

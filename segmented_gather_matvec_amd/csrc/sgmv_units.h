@@ -77,6 +77,53 @@ __device__ inline Unit resolve_unit(const int32_t* seg_indptr, const int32_t* lo
   return out;
 }
 
+// resolve_unit for at most 64 segments whose bounds are already in registers:
+// lane l holds lo_l = seg_indptr[l] and hi_l = seg_indptr[l + 1] (lanes at or
+// past num_segs hold anything).  The returned k is the unit's segment.
+template <int RB>
+__device__ inline Unit resolve_unit_lanes(int lo_l, int hi_l, int num_segs, int n_rows, int direct_units,
+                                          int u) {
+  Unit out{0, 0, 0};
+  const int lane = threadIdx.x & 63;
+  int s = -1, rb = 0;
+  if (direct_units) {
+    if (u < num_segs) s = u;
+  } else {
+    int units = 0;
+    if (lane < num_segs) {
+      const int len = hi_l - lo_l > 0 ? hi_l - lo_l : 0;
+      units = (len + RB - 1) / RB;
+    }
+    int incl = units;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int up = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += up;
+    }
+    const int excl = incl - units;
+    const bool hit = lane < num_segs && u >= excl && u < incl;
+    const unsigned long long m = __ballot(hit);
+    if (m) {
+      const int l = __builtin_ctzll(m);
+      s = l;
+      rb = u - __shfl(excl, l, 64);
+    }
+  }
+  s = __builtin_amdgcn_readfirstlane(s);
+  rb = __builtin_amdgcn_readfirstlane(rb);
+  if (s < 0 || s >= 64) return out;
+  const int lo = __builtin_amdgcn_readlane(lo_l, s);
+  const int hi = __builtin_amdgcn_readlane(hi_l, s);
+  const int r0 = lo + rb * RB;
+  int r1 = hi < r0 + RB ? hi : r0 + RB;
+  r1 = r1 < n_rows ? r1 : n_rows;
+  if ((r0 < 0) | (r1 <= r0)) return out;
+  out.r0 = r0;
+  out.L = r1 - r0;
+  out.k = s;
+  return out;
+}
+
 // Rank of a LoRA as used by the kernels: the stored value clamped to [0, R]
 // and rounded down to a multiple of 8 (one 128-bit vector of A_k per 8 ranks).
 template <int R>

@@ -246,6 +246,49 @@ def test_workspace_bytes_degenerate_and_extreme_problems(kw, rank):
     assert nbytes >= sg.SGMV_WS_COUNTER_BYTES
 
 
+def test_host_meta_entry_point_fails_fast_on_bad_host_metadata():
+    """sgmv_lora_apply_host_meta checks its host arrays before any HIP call: null
+    or misaligned arguments, metadata that breaks the segment preconditions, more
+    segments than its kernel arguments carry, a null or misaligned A_k / B_k of a
+    used LoRA, a missing or short workspace."""
+    import numpy as np
+    lib = sg.load_library()
+    fake = ctypes.c_void_p(0x10000)    # aligned, never dereferenced on these paths
+    odd = ctypes.c_void_p(0x10002)
+    P = 4
+    good_ptrs = [0x100000 * (k + 1) for k in range(P)]
+
+    def run(p, seg, lidx, A=good_ptrs, B=good_ptrs, X=fake, Y=fake, ws=fake, nbytes=1 << 30):
+        seg_a = None if seg is None else np.ascontiguousarray(seg, np.int32)
+        lidx_a = np.ascontiguousarray(lidx if len(lidx) else [0], np.int32)
+        A_a, B_a = np.ascontiguousarray(A, np.uint64), np.ascontiguousarray(B, np.uint64)
+        return lib.sgmv_lora_apply_host_meta(ctypes.byref(p), X, A_a.ctypes.data, B_a.ctypes.data, Y,
+                                             None if seg_a is None else seg_a.ctypes.data, lidx_a.ctypes.data,
+                                             ws, nbytes, None)
+
+    p = sg.make_problem("f16", 8, 256, 256, 16, P, 3, 4)
+    seg, lidx = [0, 2, 6, 8], [3, 0, 1]
+    assert run(p, seg, lidx, X=None) == sg.SGMV_ERR_INVALID_ARG
+    assert run(p, seg, lidx, Y=None) == sg.SGMV_ERR_INVALID_ARG
+    assert run(p, None, lidx) == sg.SGMV_ERR_INVALID_ARG
+    assert run(p, seg, lidx, X=odd) == sg.SGMV_ERR_UNSUPPORTED
+    assert run(p, seg, [3, 0, 4]) == sg.SGMV_ERR_INVALID_ARG          # LoRA id out of range
+    assert run(p, [0, 2, 7, 8], lidx) == sg.SGMV_ERR_INVALID_ARG      # a segment longer than max_seg_len
+    assert run(p, [0, 2, 6, 9], lidx) == sg.SGMV_ERR_INVALID_ARG      # past n_rows
+    null_a = list(good_ptrs); null_a[0] = 0                            # LoRA 0 is used by segment 1
+    assert run(p, seg, lidx, A=null_a) == sg.SGMV_ERR_INVALID_ARG
+    odd_b = list(good_ptrs); odd_b[3] += 8                             # LoRA 3 is used by segment 0
+    assert run(p, seg, lidx, B=odd_b) == sg.SGMV_ERR_UNSUPPORTED
+    assert run(p, seg, lidx, ws=None, nbytes=0) == sg.SGMV_ERR_WORKSPACE
+    assert run(p, seg, lidx, nbytes=sg.SGMV_WS_COUNTER_BYTES - 1) == sg.SGMV_ERR_WORKSPACE
+    many = sg.SGMV_HOST_META_MAX_SEGS + 1
+    pm = sg.make_problem("f16", many, 256, 256, 16, P, many, 1)
+    assert run(pm, list(range(many + 1)), [0] * many) == sg.SGMV_ERR_UNSUPPORTED
+    empty = sg.make_problem("f16", 8, 256, 256, 16, P, 0, 0)
+    assert lib.sgmv_lora_apply_host_meta(ctypes.byref(empty), None, None, None, None, None, None, None, 0,
+                                         None) == sg.SGMV_OK
+
+
 def test_device_entry_points_fail_fast_on_bad_arguments():
     """Every status below is returned by host checks before any HIP call."""
     lib = sg.load_library()
