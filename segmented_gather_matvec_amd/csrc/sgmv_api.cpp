@@ -123,6 +123,7 @@ sgmv::MfmaParams mfma_params(const sgmv_problem_t& p, const MfmaPlan& m, const i
   q.expand_rows = m.expand_rows;
   q.num_units_x = (int32_t)m.units_x;
   q.direct_units_x = m.direct_x;
+  q.x_lds = m.x_lds;
   return q;
 }
 

@@ -164,6 +164,12 @@ MfmaPlan plan_mfma(const sgmv_problem_t& p) {
     m.direct_x = direct;
     m.chunks_per_wg = (int)std::min<int64_t>(nchunks, kMfmaShortChunksPerWg);
   } else {
+    // Full tiles: the shrink stages X through LDS, whole row pieces per load
+    // (mixed r = 64 batches, shrink: 11008 -> 4096 50.2 -> 43.3 us, 4096 ->
+    // 11008 21.9 -> 18.1 us).  Short tiles keep X in registers: the LDS stage
+    // adds latency to every stage of their few-stage workgroups (13B shapes,
+    // 13824 -> 5120 shrink: 17.0 -> 18.4 us through LDS).
+    m.x_lds = 1;
     // Full tiles: each tile re-reads its B_k slice, r x 2 bytes per output per
     // tile row.  At rank <= 16 that is cheap, and 32-row tiles (twice the
     // workgroups) won: 78.9 -> 72.7 us on the mixed r = 16 4096 -> 11008 batch,

@@ -92,6 +92,7 @@ struct MfmaPlan {
   int direct_x = 1;
   size_t partial_bytes = 0;  // split partials of V, fp32 [ksplit][n_rows][rank]
   int fold = 0;              // 1: the expand sums the partial planes (no reduce launch)
+  int x_lds = 0;             // 1: the shrink stages X through LDS (full row tiles)
 };
 MfmaPlan plan_mfma(const sgmv_problem_t& p);
 

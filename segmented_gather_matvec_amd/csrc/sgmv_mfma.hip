@@ -11,11 +11,11 @@
 // Three launches (two when the expand sums the partial planes itself):
 //  1. shrink: a workgroup (4 waves, 16 rows each) takes up to 64 rows of one
 //     segment and one chunk of H1, streamed in stages of 128 H1 rows that are
-//     pipelined two deep: the X fragments (registers, straight from HBM) and
-//     A_k rows of the next stage are in flight while the current one is
-//     multiplied.  Each stage of A_k is staged in LDS, transposed to [r][h] so
-//     that a lane reads the 8 consecutive h of one rank with one 128-bit LDS
-//     read.  Each H1 chunk writes its own fp32 partial plane of V; workgroups
+//     pipelined two deep: the X rows and A_k rows of the next stage are in
+//     flight (registers) while the current one is multiplied.  Both are
+//     staged in LDS: X as loaded (whole rows per load instruction), A_k
+//     transposed to [r][h] so that a lane reads the 8 consecutive h of one
+//     rank with one 128-bit LDS read.  Each H1 chunk writes its own fp32 partial plane of V; workgroups
 //     that read the same chunk of A_k run on one XCD.
 //  2. reduce: V = sum of the partial planes, in chunk order (reproducible);
 //     the LoRA's scale, if any, is applied to V by the expand.  Up to 8
@@ -59,7 +59,9 @@ constexpr int kKStage = 128;
 
 // EXT: the extended arguments may be set (row map, per-LoRA ranks and scales;
 // see the decode kernel).  Without EXT the kernel carries none of it.
-template <class T, int R, bool EXT>
+// XL: X goes through LDS (below); else straight into the MFMA operand
+// registers, which costs each stage less latency and suits short row tiles.
+template <class T, int R, bool EXT, bool XL>
 __global__ __launch_bounds__(kThreads) void sgmv_mfma_shrink_kernel(MfmaParams p) {
   constexpr int NT = R / 16;                // 16-wide rank tiles
   constexpr int JG = R / 8;                 // 128-bit vectors per row of A_k
@@ -94,7 +96,18 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_shrink_kernel(MfmaParams p
     }
   };
   static_assert(kMfmaKChunk % (2 * kKStage) == 0, "H1 chunks hold whole stage pairs");
+  // XL: the X tile of a stage (64 rows x kKStage h, 128-bit vectors) is loaded
+  // with whole rows per instruction (4 rows x 256 contiguous bytes), then
+  // staged in LDS for the MFMA A operand, whose own layout (16 rows x 64 bytes
+  // per instruction) asks L2 twice for every 128-byte line: streamed that way,
+  // X arrives at about 3.2 TB/s.  Row stride 72 dwords: the operand reads
+  // (16 rows x 4 k-groups) meet no bank twice.
+  constexpr int XV = kKStage / 8;                  // 128-bit vectors per X row of a stage
+  constexpr int NXV = XL ? kMT * XV / kThreads : MS;  // X vectors per thread and stage
+  constexpr int XST = kKStage + 16;
+  static_assert(!XL || NXV * kThreads == kMT * XV, "whole X tiles per stage");
   __shared__ __attribute__((aligned(16))) uint16_t lds_at[R * AST];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_x[XL ? kMT * XST : 8];
 
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -130,15 +143,30 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_shrink_kernel(MfmaParams p
   const int a_stride = EXT ? rk : R;
   const int k0 = g * p.kc;
   const int k1 = p.h_in < k0 + p.kc ? p.h_in : k0 + p.kc;
-  // Row this lane feeds into the MFMA A operand (rows past the segment re-read
-  // its last row and are never stored).
-  const int row = wave * 16 + ml;
-  const int srow = r0 + (row < L ? row : L - 1);
-  const uint16_t* xrow = p.X + (EXT && p.row_idx ? (int64_t)p.row_idx[srow] : (int64_t)srow) * p.h_in;
+  // X rows of this thread.  XL: rows xr0 + 16m (m < NXV), h block xc of each
+  // stage; otherwise the row the lane feeds into the MFMA A operand.  Rows
+  // past the segment re-read its last row; they feed MFMA rows that are never
+  // stored.
+  const int xr0 = XL ? t / XV : wave * 16 + ml;
+  const int xc = t % XV;
+  constexpr int NXR = XL ? NXV : 1;
+  const uint16_t* xrow[NXR];
+#pragma unroll
+  for (int m = 0; m < NXR; ++m) {
+    const int rr = xr0 + m * (kThreads / XV);
+    const int srow = r0 + (rr < L ? rr : L - 1);
+    xrow[m] = p.X + (EXT && p.row_idx ? (int64_t)p.row_idx[srow] : (int64_t)srow) * p.h_in;
+  }
+  // X through the L1 at rank <= 16: with the direct layout, the next k-step's
+  // load hits the other half of each line there; with either layout the
+  // expand that follows ran faster (mixed r = 16, 4096 -> 11008: 60.5 -> 56.4
+  // us) than after streaming X.  At rank 64 cached X costs the A_k stages
+  // their L2 reuse (4096 -> 11008: 89.3 -> 92.7 us per call) and streams.
+  auto load_x = [](const uint16_t* a) { return R <= 16 ? load_vec(a) : load_stream(a); };
 
   // All loads of one stage, at clamped (valid) addresses; values past k1 are
   // zeroed where they are consumed.
-  auto issue = [&](int kk, u32x4 (&x)[MS], u32x4 (&a)[NPAIR][2]) {
+  auto issue = [&](int kk, u32x4 (&x)[NXV], u32x4 (&a)[NPAIR][2]) {
 #pragma unroll
     for (int m = 0; m < NPAIR; ++m) {
       const int pr = t + kThreads * m;
@@ -149,20 +177,16 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_shrink_kernel(MfmaParams p
       a[m][0] = load_stream(Ak + (ok && h < k1 ? (int64_t)h * a_stride + jg * 8 : 0));
       a[m][1] = load_stream(Ak + (ok && h + 1 < k1 ? (int64_t)(h + 1) * a_stride + jg * 8 : 0));
     }
-    // A wave's X load covers 64 of the 128 bytes of 16 row lines; the next
-    // k-step's load covers the other half.  At rank <= 16 (a small A_k stage)
-    // X goes through the L1, so the second half hits there instead of asking
-    // L2 again (mixed r = 16 batches: 11008 -> 4096 67.7 -> 58.8 us,
-    // 4096 -> 11008 76.4 -> 70.8 us); at rank 64 the cached X costs the A_k
-    // stages their L2 reuse (4096 -> 11008: 89.3 -> 92.7 us) and stays
-    // streaming.
+    if constexpr (XL) {
+      const int h = kk + xc * 8;
 #pragma unroll
-    for (int s = 0; s < MS; ++s) {
-      const int h = kk + s * 32 + q * 8;
-      if constexpr (R <= 16)
-        x[s] = load_vec(xrow + (h < k1 ? h : 0));
-      else
-        x[s] = load_stream(xrow + (h < k1 ? h : 0));
+      for (int m = 0; m < NXV; ++m) x[m] = load_x(xrow[m] + (h < k1 ? h : 0));
+    } else {
+#pragma unroll
+      for (int s = 0; s < MS; ++s) {
+        const int h = kk + s * 32 + q * 8;
+        x[s] = load_x(xrow[0] + (h < k1 ? h : 0));
+      }
     }
   };
 
@@ -172,7 +196,7 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_shrink_kernel(MfmaParams p
 
   // Stage the A_k rows transposed ([r][h]) so that a lane reads the 8
   // consecutive h of one rank with one 128-bit LDS read, then multiply.
-  auto compute = [&](int kk, const u32x4 (&x)[MS], const u32x4 (&a)[NPAIR][2]) {
+  auto compute = [&](int kk, const u32x4 (&x)[NXV], const u32x4 (&a)[NPAIR][2]) {
     const u32x4 z = {0u, 0u, 0u, 0u};
     __syncthreads();  // the previous stage is done with lds_at
 #pragma unroll
@@ -190,11 +214,21 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_shrink_kernel(MfmaParams p
                                     live && kk + h < k1 ? a[m][0] : z, live && kk + h + 1 < k1 ? a[m][1] : z);
       }
     }
+    if constexpr (XL) {
+      const bool xlive = kk + xc * 8 < k1;  // ragged tail of H1: zeros
+#pragma unroll
+      for (int m = 0; m < NXV; ++m)
+        store_vec(&lds_x[(xr0 + m * (kThreads / XV)) * XST + xc * 8], xlive ? x[m] : z);
+    }
     __syncthreads();
     if (wave * 16 >= L) return;  // this wave's rows are all past the segment
 #pragma unroll
     for (int s = 0; s < MS; ++s) {
-      const u32x4 xa = kk + s * 32 + q * 8 < k1 ? x[s] : z;  // ragged tail of H1
+      u32x4 xa;
+      if constexpr (XL)
+        xa = load_vec(&lds_x[(wave * 16 + ml) * XST + s * 32 + q * 8]);
+      else
+        xa = kk + s * 32 + q * 8 < k1 ? x[s] : z;  // ragged tail of H1
 #pragma unroll
       for (int n = 0; n < NT; ++n)
         acc[n] = mfma<T>(xa, load_vec(&lds_at[(n * 16 + ml) * AST + (((4 * s + q) ^ swz(n * 16 + ml)) << 3)]), acc[n]);
@@ -206,7 +240,7 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_shrink_kernel(MfmaParams p
   // The loop body issues its loads unconditionally (a load under a branch
   // makes the compiler wait for every load in flight at the loop head); the
   // last stage pair, which issues no loads beyond itself, is peeled.
-  u32x4 xA[MS], aA[NPAIR][2], xB[MS], aB[NPAIR][2];
+  u32x4 xA[NXV], aA[NPAIR][2], xB[NXV], aB[NPAIR][2];
   issue(k0, xA, aA);
   int kk = k0;
   for (; kk + 2 * kKStage < k1; kk += 2 * kKStage) {
@@ -587,10 +621,12 @@ hipError_t launch_t(int stage, const MfmaParams& p, int np, hipStream_t s) {
   if (stage == 0) {
     grid = xcd_grid((unsigned)p.num_units64 * (unsigned)p.ksplit);
     if (grid && np > 0) {
-      if (ext)
-        hipLaunchKernelGGL((sgmv_mfma_shrink_kernel<T, R, true>), dim3(grid, np), dim3(kThreads), 0, s, p);
-      else
-        hipLaunchKernelGGL((sgmv_mfma_shrink_kernel<T, R, false>), dim3(grid, np), dim3(kThreads), 0, s, p);
+      using K = void (*)(MfmaParams);
+      // [x through LDS][ext]
+      static constexpr K kernels[2][2] = {
+          {sgmv_mfma_shrink_kernel<T, R, false, false>, sgmv_mfma_shrink_kernel<T, R, true, false>},
+          {sgmv_mfma_shrink_kernel<T, R, false, true>, sgmv_mfma_shrink_kernel<T, R, true, true>}};
+      hipLaunchKernelGGL(kernels[p.x_lds ? 1 : 0][ext], dim3(grid, np), dim3(kThreads), 0, s, p);
     }
   } else if (stage == 1) {
     constexpr unsigned rows = kThreads / (R / 4);

@@ -124,6 +124,9 @@ struct MfmaParams {
   // 1: no reduce launch; the expand sums the ksplit partial planes of its rows
   // itself (in plane order, the reduce's order) instead of reading V.
   int32_t fold_planes;
+  // 1: the shrink stages X through LDS, loaded a whole row piece per
+  // instruction (full row tiles); 0: X straight into the operand registers.
+  int32_t x_lds;
   const int32_t* seg_indptr;
   const int32_t* lora_idx;
   const int32_t* row_idx;  // null, or row of X / Y of each sorted row

@@ -350,6 +350,42 @@ def test_ragged_hidden_sizes(h_in, h_out, variant):
     assert_close(to_bits(call.apply()), call.oracle_apply(), "bf16")
 
 
+@pytest.mark.parametrize("row_map", [False, True])
+@pytest.mark.parametrize("rank", [16, 32, 64])
+@pytest.mark.parametrize("h_in,dtype", [(40, "bf16"), (4104, "f16"), (4104, "bf16")])
+def test_full_row_tiles(h_in, dtype, rank, row_map):
+    """Segments long enough for full 64-row tiles (at least 32 rows per tile on
+    average, where the matrix-core shrink stages X through LDS), with a ragged
+    H1 (40 = a stage of 128 holding 5 vectors; 4104 = 32 stages plus 8), every
+    rank, in segment order and through a row map among spare rows."""
+    import torch
+    n, h_out, P = 200, 264, 3
+    seg, lidx = [0, 130, 131, 200], [2, 0, 1]
+    tiles = sum(-(-(b - a) // 64) for a, b in zip(seg, seg[1:]))
+    assert n >= 32 * tiles
+    Xs, A, B, Y0s = rand_inputs(11 + rank, n, h_in, h_out, rank, P, dtype)
+    if row_map:
+        perm = np.random.default_rng(rank).permutation(n + 5)[:n].astype(np.int32)
+        X = np.zeros((n + 5, h_in), np.uint16); X[perm] = Xs
+        Y0 = workloads.to_bits(np.random.default_rng(9).standard_normal((n + 5, h_out)).astype(np.float32), dtype)
+        Y0[perm] = Y0s
+    else:
+        X, Y0 = Xs, Y0s
+    call = DeviceCall(dtype, X, A, B, Y0, seg, lidx, variant=sg.SGMV_VARIANT_MFMA)
+    assert sg.sgmv_query_plan(call.problem).route == sg.SGMV_ROUTE_MFMA
+    row_idx = torch.from_numpy(perm).cuda() if row_map else None
+    sg.sgmv_lora_apply_batched(call.problem, call.X, [(call.A_ptrs, call.B_ptrs, call.Y)], call.seg_d,
+                               call.lidx_d, call.ws, row_idx=row_idx)
+    torch.cuda.synchronize()
+    ref_sorted = oracle.sgmv_apply(dtype, Xs, A, B, np.asarray(seg, np.int32), np.asarray(lidx, np.int32), Y0s)
+    if row_map:
+        ref = oracle.decode(Y0, dtype)
+        ref[perm] = ref_sorted
+    else:
+        ref = ref_sorted
+    assert_close(to_bits(call.Y), ref, dtype, what=f"h_in {h_in} rank {rank}")
+
+
 @pytest.mark.parametrize("variant", APPLY_VARIANTS)
 @pytest.mark.parametrize("rank", [8, 32, 64])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
