@@ -169,7 +169,8 @@ sgmv_status_t sgmv_workspace_bytes(const sgmv_problem_t* problem, size_t* bytes)
 typedef enum sgmv_route {
   SGMV_ROUTE_NONE = 0,    /* nothing to do (no rows or segments) */
   SGMV_ROUTE_DECODE = 1,  /* one launch: shrink, on-chip exchange, expand */
-  SGMV_ROUTE_MFMA = 2,    /* matrix-core shrink, split reduce (summed by the expand up to 8 splits, 32 at rank <= 16), matrix-core expand */
+  SGMV_ROUTE_MFMA = 2,    /* matrix-core shrink, then matrix-core expand, whose launch also sums the shrink's split partials
+                             (each expand workgroup up to 8 splits, 32 at rank <= 16; beyond, lead workgroups of the launch) */
   SGMV_ROUTE_VECTOR = 3   /* split-K vector shrink, then vector expand */
 } sgmv_route_t;
 
@@ -222,7 +223,11 @@ sgmv_status_t sgmv_expand(const sgmv_problem_t* problem, const float* V, const v
  * (sgmv_set_wait_limit, default 1 s), leaves its part of Y untouched and sets
  * SGMV_DEVICE_ERR_WAIT_TIMEOUT in the device error word
  * (sgmv_take_device_errors): the kernel always ends, and the error is
- * reported instead of a hang.  Calls on one workspace must not overlap. */
+ * reported instead of a hang.  On the matrix-core route with more split
+ * partials than its expand workgroups sum themselves, the expand launch's
+ * first workgroups (lowest ids, dispatched first; they wait for nothing) sum
+ * them, and the other workgroups wait for their rows' sums under the same
+ * bound and error word.  Calls on one workspace must not overlap. */
 sgmv_status_t sgmv_lora_apply(const sgmv_problem_t* problem, const void* X,
                               const void* const* A_ptrs, const void* const* B_ptrs, void* Y,
                               const int32_t* seg_indptr, const int32_t* lora_idx, void* ws,
@@ -254,16 +259,18 @@ sgmv_status_t sgmv_lora_apply_host_meta(const sgmv_problem_t* problem, const voi
                                         const int32_t* lora_idx_host, void* ws, size_t ws_bytes,
                                         void* stream);
 
-/* Bound on how long a workgroup of the one-launch decode route waits for the
- * partial sums of the other workgroups of its unit, in microseconds (process
- * wide, applies to later calls; default 1000000).  0 makes every such wait
- * give up at once: the decode kernels then exit without updating Y and set
- * SGMV_DEVICE_ERR_WAIT_TIMEOUT (a test hook for the give-up path).
+/* Bound on how long a workgroup waits for partial sums made by other
+ * workgroups of the same launch (the one-launch decode route, and the
+ * matrix-core expand when its lead workgroups sum the split partials), in
+ * microseconds (process wide, applies to later calls; default 1000000).  0
+ * makes every such wait give up at once: those workgroups then exit without
+ * updating Y and set SGMV_DEVICE_ERR_WAIT_TIMEOUT (a test hook for the
+ * give-up path).
  * SGMV_ERR_INVALID_ARG for a negative value.  Host only. */
 sgmv_status_t sgmv_set_wait_limit(int64_t microseconds);
 
 /* Device error bits of the current HIP device. */
-#define SGMV_DEVICE_ERR_WAIT_TIMEOUT 1u  /* a decode-route wait gave up: Y of that call is unspecified */
+#define SGMV_DEVICE_ERR_WAIT_TIMEOUT 1u  /* a wait for another workgroup's partial sums gave up: Y of that call is unspecified */
 
 /* Synchronises the current device (hipDeviceSynchronize), then reads and
  * clears its device error word: *flags gets the SGMV_DEVICE_ERR_* bits set by

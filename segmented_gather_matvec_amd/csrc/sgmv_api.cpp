@@ -255,6 +255,17 @@ sgmv_status_t apply(const sgmv_problem_t& p, const void* X, const sgmv_projectio
     q.V = reinterpret_cast<float*>(ws + SGMV_WS_COUNTER_BYTES + m.partial_bytes);
     q.proj_stride = (int64_t)(stride / sizeof(float));
     q.fold_planes = m.fold;
+    if (m.lead) {
+      // Lead workgroups of the expand launch sum the planes; their flags
+      // follow V in each projection's slice of the workspace.
+      if (sgmv::decode_error_word(&q.errors) != hipSuccess) return SGMV_ERR_HIP;
+      q.lead_reduce = 1;
+      q.lead_blocks = m.lead_blocks;
+      q.lead_rows = m.lead_rows;
+      q.lead_proj = np;
+      q.wait_ticks = wait_ticks();
+      q.flags = reinterpret_cast<uint32_t*>(ws + SGMV_WS_COUNTER_BYTES + m.partial_bytes + v_area_bytes(p));
+    }
     hipError_t e = sgmv::launch_mfma_shrink(p.dtype, p.rank, q, np, s);
     if (e != hipSuccess) return SGMV_ERR_HIP;
     return hip_status(sgmv::launch_mfma_expand(p.dtype, p.rank, q, np, s));
@@ -386,7 +397,7 @@ sgmv_status_t sgmv_query_plan(const sgmv_problem_t* p, sgmv_plan_info_t* info) {
       break;
     case SGMV_ROUTE_MFMA: {
       const MfmaPlan m = plan_mfma(*p);
-      info->launches = m.fold ? 2 : 3;
+      info->launches = 2;  // the planes are summed by the expand launch (folded or by its lead workgroups)
       info->rows_per_unit = sgmv::kMfmaRowsPerTile;
       info->units = (int32_t)m.units64;
       info->splits = m.ksplit;

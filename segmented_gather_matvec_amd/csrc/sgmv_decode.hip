@@ -36,10 +36,6 @@
 #include "sgmv_plan.h"
 #include "sgmv_units.h"
 
-// The packet id of the current kernel dispatch (LLVM intrinsic; it makes the
-// runtime pass the id in user SGPRs).
-extern "C" __device__ unsigned long long sgmv_llvm_dispatch_id() __asm("llvm.amdgcn.dispatch.id");
-
 namespace sgmv {
 
 // Sticky error bits of the decode route on this device (SGMV_DEVICE_ERR_*),
@@ -55,13 +51,6 @@ constexpr int kXcds = 8;
 // more of the register budget to the streamed A_k and B_k.
 constexpr int poll_per_thread(int rb, int r) {
   return rb * r * 16 / kThreads < 1 ? 1 : rb * r * 16 / kThreads > 4 ? 4 : rb * r * 16 / kThreads;
-}
-
-__device__ inline uint32_t launch_tag() {
-  const uint64_t did = sgmv_llvm_dispatch_id();
-  const uint64_t q = reinterpret_cast<uint64_t>(__builtin_amdgcn_queue_ptr());
-  const uint32_t qh = (uint32_t)(q >> 12) * 0x9E3779B1u;
-  return (((uint32_t)did ^ qh) << 1) | 1u;
 }
 
 __device__ inline void publish_tagged(uint64_t* slot, float v, uint32_t tag) {

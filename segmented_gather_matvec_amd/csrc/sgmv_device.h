@@ -4,6 +4,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+// The packet id of the current kernel dispatch (LLVM intrinsic; it makes the
+// runtime pass the id in user SGPRs).
+extern "C" __device__ unsigned long long sgmv_llvm_dispatch_id() __asm("llvm.amdgcn.dispatch.id");
+
 namespace sgmv {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -85,6 +89,21 @@ __device__ inline void publish_f32(float* p, float v) {
 }
 __device__ inline float fetch_published_f32(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline uint64_t fetch_published_u64(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void publish_u64(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// A tag that differs on every launch, replays of a captured graph included:
+// the dispatch packet id mixed with the queue address.  Always odd, so a
+// zero-filled word never matches.
+__device__ inline uint32_t launch_tag() {
+  const uint64_t did = sgmv_llvm_dispatch_id();
+  const uint64_t q = reinterpret_cast<uint64_t>(__builtin_amdgcn_queue_ptr());
+  const uint32_t qh = (uint32_t)(q >> 12) * 0x9E3779B1u;
+  return (((uint32_t)did ^ qh) << 1) | 1u;
 }
 // Wait until every memory operation this thread issued has completed.
 __device__ inline void wait_memory_ops() {

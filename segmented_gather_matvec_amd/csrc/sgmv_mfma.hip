@@ -8,7 +8,7 @@
 // sustain against HBM, so both run on v_mfma_f32_16x16x32_{f16,bf16}
 // (lane l holds A[l%16][8(l/16)+e], B[8(l/16)+e][l%16], D[4(l/16)+i][l%16]).
 //
-// Three launches (two when the expand sums the partial planes itself):
+// Two launches (three for the standalone shrink, whose reduce writes V):
 //  1. shrink: a workgroup (4 waves, 16 rows each) takes up to 64 rows of one
 //     segment and one chunk of H1, streamed in stages of 128 H1 rows that are
 //     pipelined two deep: the X rows and A_k rows of the next stage are in
@@ -17,10 +17,13 @@
 //     transposed to [r][h] so that a lane reads the 8 consecutive h of one
 //     rank with one 128-bit LDS read.  Each H1 chunk writes its own fp32 partial plane of V; workgroups
 //     that read the same chunk of A_k run on one XCD.
-//  2. reduce: V = sum of the partial planes, in chunk order (reproducible);
-//     the LoRA's scale, if any, is applied to V by the expand.  Up to 8
-//     planes the expand adds them itself, in the same order (same bits), and
-//     this launch is skipped.
+//  2. V = sum of the partial planes, in chunk order (reproducible); the
+//     LoRA's scale, if any, is applied to V by the expand.  Up to 8 planes
+//     (32 at rank <= 16 on full tiles) each expand workgroup adds those of its
+//     rows itself.  Beyond, the expand launch begins with lead workgroups that
+//     sum them for blocks of rows and flag each block with the launch's tag;
+//     the expand workgroups issue their first loads, then wait for the flags
+//     of their rows.  The separate reduce launch serves the standalone shrink.
 //  3. expand: a workgroup takes 64 rows (16 when the segments are short) and a
 //     group of 128-column chunks.  V is split into V_hi + V_lo (both in the
 //     input format), consumed as a K of 2r against [B_k; B_k], which keeps
@@ -46,9 +49,11 @@ constexpr int kXcds = 8;
 // b % 8), each with its own L2.  Give every XCD a contiguous run of the linear
 // work order (grid = 8 * per_xcd), so that items adjacent in that order, which
 // read the same weight slice, run on one XCD and share its L2.
-__device__ inline int xcd_linear_index() {
-  const int per_xcd = gridDim.x / kXcds;
-  return (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+// The first `skip` workgroups (a multiple of 8) are left out of the order.
+__device__ inline int xcd_linear_index(int skip = 0) {
+  const int per_xcd = (gridDim.x - skip) / kXcds;
+  const int b = blockIdx.x - skip;
+  return (b % kXcds) * per_xcd + b / kXcds;
 }
 
 
@@ -317,13 +322,73 @@ void sgmv_mfma_reduce_kernel(MfmaParams p) {
   if (row < end) *reinterpret_cast<f32x4*>(V + off) = s;
 }
 
+// ---------------------------------------------------------------- lead reduce
+// Lead workgroup b of projection y: V of rows [b * lead_rows, (b + 1) *
+// lead_rows) = the sum of the partial planes in plane order from zero (the
+// reduce launch's order and bits), written through to the device-coherent
+// level, then flags[b] = tag once every thread's stores have completed.  Lead
+// workgroups never wait, and they have the lowest workgroup ids of the launch,
+// so they are dispatched ahead of every workgroup that waits for them.  Up to
+// 16 planes a thread sums one float4 of a row (1024 / R rows per workgroup);
+// beyond, one float2 (512 / R rows), so that every plane load of a thread is in
+// flight at once up to 32 planes at the same register count (more would cost
+// the expand occupancy).
+template <int R, int W>
+__device__ inline void lead_sum(const MfmaParams& p, int y, int b, uint32_t tag) {
+  using VT = __attribute__((ext_vector_type(W))) float;
+  constexpr int VW = R / W;               // vectors per row of V
+  constexpr int ROWS = kThreads / VW;
+  constexpr int kBatch = 64 / W;          // plane loads in flight per thread
+  const int t = threadIdx.x;
+  const int row = b * ROWS + t / VW;
+  const float* partials = p.partials + (int64_t)y * p.proj_stride;
+  float* V = p.V + (int64_t)y * p.proj_stride;
+  int end = p.seg_indptr[p.num_segs];
+  end = end < p.n_rows ? end : p.n_rows;
+  const int64_t off = (int64_t)(row < p.n_rows ? row : p.n_rows - 1) * R + (t % VW) * W;
+  VT s = {};
+  for (int k0 = 0; k0 < p.ksplit; k0 += kBatch) {
+    VT v[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int64_t k = k0 + u < p.ksplit ? k0 + u : p.ksplit - 1;
+      v[u] = *reinterpret_cast<const VT*>(partials + k * p.partial_stride + off);
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const VT a = s + v[u];
+      s = k0 + u < p.ksplit ? a : s;
+    }
+  }
+  if (row < end) {
+    uint64_t* dst = reinterpret_cast<uint64_t*>(V + off);
+#pragma unroll
+    for (int e = 0; e < W / 2; ++e)
+      publish_u64(dst + e, ((uint64_t)__float_as_uint(s[2 * e + 1]) << 32) | __float_as_uint(s[2 * e]));
+  }
+  wait_memory_ops();
+  __syncthreads();
+  if (t == 0)
+    __hip_atomic_store(p.flags + (int64_t)y * p.proj_stride + b, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int R>
+__device__ inline void lead_reduce_rows(const MfmaParams& p, int y, int b, uint32_t tag) {
+  if (p.lead_rows == kThreads * 4 / R)
+    lead_sum<R, 4>(p, y, b, tag);
+  else
+    lead_sum<R, 2>(p, y, b, tag);
+}
+
 // ---------------------------------------------------------------- expand
 // MT rows per tile.  MT = 64: wave w computes rows 16w..16w+15 over the whole
 // chunk.  MT = 16 (short segments, e.g. decode batches with a few rows per
 // LoRA): the four waves share the 16 rows and each computes a quarter of the
 // chunk's columns, so no wave idles and the smaller LDS footprint lets more
 // workgroups stream B_k at once.
-template <class T, int R, bool EXT, int MT>
+// LEAD: the launch carries lead workgroups (p.lead_reduce); a template flag so
+// that the kernels without them keep their register count (occupancy).
+template <class T, int R, bool EXT, int MT, bool LEAD>
 __global__ __launch_bounds__(kThreads) void sgmv_mfma_expand_kernel(MfmaParams p) {
   constexpr int K2 = 2 * R;            // virtual K: [V_hi | V_lo] against [B_k; B_k]
   constexpr int KSTEPS = K2 / 32;
@@ -390,11 +455,20 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_expand_kernel(MfmaParams p
                        (p.fold_planes ? p.partials == nullptr : p.V == nullptr) | (pj.B_ptrs == nullptr) |
                        (pj.Y == nullptr);
   if (bad_size | bad_ptr) return;
+  const int lead = LEAD ? p.lead_blocks * p.lead_proj : 0;
+  if (LEAD && (p.partials == nullptr) | (p.flags == nullptr) | (p.errors == nullptr) |
+      ((p.lead_blocks | (p.lead_proj - 1) | (p.lead_rows - 1)) < 0))
+    return;
+  const uint32_t tag = LEAD ? launch_tag() : 0u;
+  if (LEAD && (int)blockIdx.x < lead) {
+    if (blockIdx.y == 0) lead_reduce_rows<R>(p, blockIdx.x / p.lead_blocks, blockIdx.x % p.lead_blocks, tag);
+    return;
+  }
   const int nchunks = (p.h_out + kCW - 1) / kCW;
   const int ngroups = (nchunks + p.chunks_per_wg - 1) / p.chunks_per_wg;
   // Linear order: column group major, so the row units that read one slice of
   // B_k share an XCD.
-  const int idx = xcd_linear_index();
+  const int idx = xcd_linear_index(lead);
   if (idx >= p.num_units_x * ngroups) return;
   const int grp = idx / p.num_units_x;
   const int unit = idx - grp * p.num_units_x;
@@ -494,6 +568,46 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_expand_kernel(MfmaParams p
     for (int k0 = kBatch; k0 < p.ksplit; k0 += kBatch) {
       load_planes(k0);
       add_planes(k0);
+    }
+  } else if (LEAD) {
+    // V of these rows is summed by lead workgroups of this launch: the first
+    // chunk's loads go out, then the wait for the flags of the tile's row
+    // blocks (one lane each), then V through device-coherent loads.
+    issue(ch0, bvA, yvA);
+    __shared__ uint32_t lds_ok;
+    if (wave == 0) {
+      const int b0 = r0 / p.lead_rows, nb = (r0 + L - 1) / p.lead_rows - b0 + 1;
+      const uint32_t* fl = p.flags + (int64_t)blockIdx.y * p.proj_stride + b0;
+      // A limit of 0 (the host's test hook) waits for a tag no flag carries.
+      const uint32_t want = p.wait_ticks != 0 ? tag : ~tag;
+      bool ok = true;
+      if (lane < nb) {
+        const uint64_t deadline = __builtin_amdgcn_s_memrealtime() + p.wait_ticks;
+        uint32_t f = __hip_atomic_load(fl + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        uint64_t now = 0;
+        while (f != want && now <= deadline) {
+          __builtin_amdgcn_s_sleep(1);
+          f = __hip_atomic_load(fl + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          now = __builtin_amdgcn_s_memrealtime();
+        }
+        ok = f == want;
+      }
+      const bool all_ok = __all(ok);
+      if (lane == 0) lds_ok = all_ok;
+    }
+    __syncthreads();
+    if (!lds_ok) {
+      if (t == 0) __hip_atomic_fetch_or(p.errors, kDecodeErrWaitTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;  // Y untouched
+    }
+#pragma unroll
+    for (int m = 0; m < NV4; ++m) {
+      const int o = (t + kThreads * m) * 4;
+      const int rr = o / R;
+      const uint64_t* src = reinterpret_cast<const uint64_t*>(Vp + (int64_t)(r0 + (rr < L ? rr : 0)) * R + o % R);
+      const uint64_t lo = fetch_published_u64(src), hi = fetch_published_u64(src + 1);
+      vv[m] = f32x4{__uint_as_float((uint32_t)lo), __uint_as_float((uint32_t)(lo >> 32)),
+                    __uint_as_float((uint32_t)hi), __uint_as_float((uint32_t)(hi >> 32))};
     }
   } else {
 #pragma unroll
@@ -636,15 +750,25 @@ hipError_t launch_t(int stage, const MfmaParams& p, int np, hipStream_t s) {
     if (p.expand_rows != 16 && p.expand_rows != 32 && p.expand_rows != kMT) return hipErrorInvalidValue;
     const int nchunks = (p.h_out + kCW - 1) / kCW;
     grid = xcd_grid((unsigned)p.num_units_x * (unsigned)((nchunks + p.chunks_per_wg - 1) / p.chunks_per_wg));
+    if (p.lead_reduce) {
+      if (p.lead_blocks % kXcds != 0 || p.lead_proj != np ||
+          (p.lead_rows != kThreads * 4 / R && p.lead_rows != kThreads * 2 / R) ||
+          (int64_t)p.lead_blocks * p.lead_rows < (int64_t)p.n_rows)
+        return hipErrorInvalidValue;
+      if (grid) grid += (unsigned)(p.lead_blocks * np);
+    }
     if (grid && np > 0) {
       using K = void (*)(MfmaParams);
-      // [tile rows 64, 32, 16][ext]
-      static constexpr K kernels[3][2] = {
-          {sgmv_mfma_expand_kernel<T, R, false, kMT>, sgmv_mfma_expand_kernel<T, R, true, kMT>},
-          {sgmv_mfma_expand_kernel<T, R, false, 32>, sgmv_mfma_expand_kernel<T, R, true, 32>},
-          {sgmv_mfma_expand_kernel<T, R, false, 16>, sgmv_mfma_expand_kernel<T, R, true, 16>}};
+      // [lead workgroups][tile rows 64, 32, 16][ext]
+      static constexpr K kernels[2][3][2] = {
+          {{sgmv_mfma_expand_kernel<T, R, false, kMT, false>, sgmv_mfma_expand_kernel<T, R, true, kMT, false>},
+           {sgmv_mfma_expand_kernel<T, R, false, 32, false>, sgmv_mfma_expand_kernel<T, R, true, 32, false>},
+           {sgmv_mfma_expand_kernel<T, R, false, 16, false>, sgmv_mfma_expand_kernel<T, R, true, 16, false>}},
+          {{sgmv_mfma_expand_kernel<T, R, false, kMT, true>, sgmv_mfma_expand_kernel<T, R, true, kMT, true>},
+           {sgmv_mfma_expand_kernel<T, R, false, 32, true>, sgmv_mfma_expand_kernel<T, R, true, 32, true>},
+           {sgmv_mfma_expand_kernel<T, R, false, 16, true>, sgmv_mfma_expand_kernel<T, R, true, 16, true>}}};
       const int which = p.expand_rows == kMT ? 0 : p.expand_rows == 32 ? 1 : 2;
-      hipLaunchKernelGGL(kernels[which][ext], dim3(grid, np), dim3(kThreads), 0, s, p);
+      hipLaunchKernelGGL(kernels[p.lead_reduce ? 1 : 0][which][ext], dim3(grid, np), dim3(kThreads), 0, s, p);
     }
   }
   return grid && np > 0 ? hipGetLastError() : hipSuccess;
@@ -669,7 +793,7 @@ hipError_t launch_stage(int dtype, int rank, int stage, const MfmaParams& p, int
 
 hipError_t launch_mfma_shrink(int dtype, int rank, const MfmaParams& p, int num_proj, hipStream_t stream) {
   hipError_t e = launch_stage(dtype, rank, 0, p, num_proj, stream);
-  if (e != hipSuccess || p.fold_planes) return e;
+  if (e != hipSuccess || p.fold_planes || p.lead_reduce) return e;
   return launch_stage(dtype, rank, 1, p, num_proj, stream);
 }
 

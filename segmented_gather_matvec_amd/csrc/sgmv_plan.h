@@ -127,6 +127,19 @@ struct MfmaParams {
   // 1: the shrink stages X through LDS, loaded a whole row piece per
   // instruction (full row tiles); 0: X straight into the operand registers.
   int32_t x_lds;
+  // 1 (with fold_planes 0): no reduce launch; lead workgroups of the expand
+  // launch sum the partial planes of their row blocks (lead_rows rows each,
+  // lead_blocks blocks per projection, in plane order: the reduce's bits) into
+  // V and publish flags[block] = the launch tag; the other workgroups wait for
+  // the flags of their rows, at most wait_ticks of the real-time counter (0:
+  // give up at once), before reading V.  Every grid row starts with
+  // lead_blocks * lead_proj workgroups: those of row 0 do the lead work of all
+  // lead_proj projections, so that it is dispatched ahead of every waiting
+  // workgroup; those of the other rows exit at once.
+  int32_t lead_reduce, lead_blocks, lead_rows, lead_proj;
+  uint32_t wait_ticks;
+  uint32_t* flags;         // projection 0; projection y at flags + y * proj_stride
+  uint32_t* errors;        // device error word (a wait that gave up sets bit 0)
   const int32_t* seg_indptr;
   const int32_t* lora_idx;
   const int32_t* row_idx;  // null, or row of X / Y of each sorted row

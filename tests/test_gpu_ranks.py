@@ -74,6 +74,9 @@ CASES = {
                    [0, 8, 16], sg.SGMV_VARIANT_FUSED, 64),
     "mfma_r64": (5, "bf16", 300, 1024, 1376, 64, 6, ([0, 120, 121, 250, 251, 300], [3, 0, 5, 1, 2]),
                  [0, 16, 32, 48, 64], sg.SGMV_VARIANT_MFMA, 0),
+    # short row tiles and 20 H1 planes: summed by the lead workgroups of the expand launch
+    "mfma_r64_lead": (11, "bf16", 200, 5120, 1024, 64, 24, (list(range(0, 201, 10)), [(7 * i) % 24 for i in range(20)]),
+                      [0, 16, 32, 64], sg.SGMV_VARIANT_MFMA, 0),
     "mfma_r16": (8, "f16", 160, 2048, 512, 16, 4, ([0, 70, 71, 160], [1, 2, 3]), [0, 8, 16],
                  sg.SGMV_VARIANT_MFMA, 0),
     "vector_r32": (7, "f16", 40, 1024, 1000, 32, 10, ([0, 5, 6, 20, 21, 40], [9, 0, 4, 7, 2]),

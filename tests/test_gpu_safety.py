@@ -75,6 +75,31 @@ def test_multi_pass_decode_gives_up_in_every_pass():
     assert sg.sgmv_take_device_errors() == 0
 
 
+def test_matrix_core_lead_wait_gives_up_under_the_test_hook_and_recovers():
+    """Beyond the planes the expand folds itself, the first workgroups of the
+    expand launch sum them and flag each row block; the others wait for those
+    flags under the same bound as the decode route.  Under the test hook every
+    such wait gives up: Y is untouched and the error word reports it."""
+    import torch
+    rng = np.random.default_rng(4242)
+    X, A, B, Y0 = workloads.integer_exact(rng, 256, 8192, 256, 64, 3, "bf16", 2, 64)
+    call = DeviceCall("bf16", X, A, B, Y0, [0, 100, 256], [2, 0], variant=sg.SGMV_VARIANT_MFMA)
+    info = sg.sgmv_query_plan(call.problem)
+    assert info.route == sg.SGMV_ROUTE_MFMA and info.splits > 8 and info.launches == 2, info.as_dict()
+    assert sg.sgmv_take_device_errors() == 0
+    try:
+        sg.sgmv_set_wait_limit(0)
+        call.apply()
+        torch.cuda.synchronize()
+        assert sg.sgmv_take_device_errors() == sg.SGMV_DEVICE_ERR_WAIT_TIMEOUT
+        assert np.array_equal(to_bits(call.Y), call.Y0h)
+    finally:
+        sg.sgmv_set_wait_limit(DEFAULT_WAIT_US)
+    call.reset_y()
+    assert np.array_equal(oracle.decode(to_bits(call.apply()), "bf16"), call.oracle_apply())
+    assert sg.sgmv_take_device_errors() == 0
+
+
 def test_decode_slots_untouched_by_other_routes():
     """One workspace serves the matrix-core route, the two-launch route and the
     decode route in turn; the decode route's result is the oracle's."""
