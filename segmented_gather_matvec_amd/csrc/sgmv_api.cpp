@@ -256,15 +256,16 @@ sgmv_status_t apply(const sgmv_problem_t& p, const void* X, const sgmv_projectio
     q.proj_stride = (int64_t)(stride / sizeof(float));
     q.fold_planes = m.fold;
     if (m.lead) {
-      // Lead workgroups of the expand launch sum the planes; their flags
-      // follow V in each projection's slice of the workspace.
+      // Lead workgroups of the expand launch sum the planes; their tagged V
+      // words or row-block flags follow V in each projection's slice of the
+      // workspace.
       if (sgmv::decode_error_word(&q.errors) != hipSuccess) return SGMV_ERR_HIP;
       q.lead_reduce = 1;
       q.lead_blocks = m.lead_blocks;
       q.lead_rows = m.lead_rows;
       q.lead_proj = np;
       q.wait_ticks = wait_ticks();
-      q.flags = reinterpret_cast<uint32_t*>(ws + SGMV_WS_COUNTER_BYTES + m.partial_bytes + v_area_bytes(p));
+      q.lead_area = ws + SGMV_WS_COUNTER_BYTES + m.partial_bytes + v_area_bytes(p);
     }
     hipError_t e = sgmv::launch_mfma_shrink(p.dtype, p.rank, q, np, s);
     if (e != hipSuccess) return SGMV_ERR_HIP;

@@ -53,13 +53,6 @@ constexpr int poll_per_thread(int rb, int r) {
   return rb * r * 16 / kThreads < 1 ? 1 : rb * r * 16 / kThreads > 4 ? 4 : rb * r * 16 / kThreads;
 }
 
-__device__ inline void publish_tagged(uint64_t* slot, float v, uint32_t tag) {
-  const uint64_t w = ((uint64_t)tag << 32) | __float_as_uint(v);
-  __hip_atomic_store(slot, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline uint64_t fetch_tagged(const uint64_t* slot) {
-  return __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 // Value of a 64-bit lane variable in lane `l` (l uniform over the wave).
 __device__ inline uint64_t readlane_u64(uint64_t v, int l) {

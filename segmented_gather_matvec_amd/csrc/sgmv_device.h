@@ -90,12 +90,6 @@ __device__ inline void publish_f32(float* p, float v) {
 __device__ inline float fetch_published_f32(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ inline uint64_t fetch_published_u64(const uint64_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline void publish_u64(uint64_t* p, uint64_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 // A tag that differs on every launch, replays of a captured graph included:
 // the dispatch packet id mixed with the queue address.  Always odd, so a
 // zero-filled word never matches.
@@ -104,6 +98,21 @@ __device__ inline uint32_t launch_tag() {
   const uint64_t q = reinterpret_cast<uint64_t>(__builtin_amdgcn_queue_ptr());
   const uint32_t qh = (uint32_t)(q >> 12) * 0x9E3779B1u;
   return (((uint32_t)did ^ qh) << 1) | 1u;
+}
+__device__ inline uint64_t fetch_published_u64(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void publish_u64(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// A value and its validity in one device-coherent 64-bit word {fp32, tag}:
+// no counter, fence or flag is needed to hand it to another workgroup.
+__device__ inline void publish_tagged(uint64_t* slot, float v, uint32_t tag) {
+  const uint64_t w = ((uint64_t)tag << 32) | __float_as_uint(v);
+  __hip_atomic_store(slot, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline uint64_t fetch_tagged(const uint64_t* slot) {
+  return __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 // Wait until every memory operation this thread issued has completed.
 __device__ inline void wait_memory_ops() {

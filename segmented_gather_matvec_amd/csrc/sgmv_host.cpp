@@ -187,13 +187,12 @@ MfmaPlan plan_mfma(const sgmv_problem_t& p) {
   const bool low_rank_full = p.rank <= 16 && m.expand_rows != kMfmaShortExpandRows;
   m.fold = m.ksplit <= (low_rank_full ? kMfmaLowRankFoldPlanes : kMfmaFoldPlanes) ? 1 : 0;
   // Beyond the fold limit the first workgroups of the expand launch sum the
-  // planes (1024 / rank rows each, 512 / rank beyond 16 planes) and flag each
-  // row block with the launch's tag; the reduce launch remains for the
-  // standalone shrink.
+  // planes (1024 / rank rows each, 512 / rank beyond 16 planes) into tagged V
+  // words; the reduce launch remains for the standalone shrink.
   m.lead = m.fold ? 0 : 1;
   m.lead_rows = m.ksplit > 16 ? 512 / p.rank : 1024 / p.rank;
   m.lead_blocks = (int)round_up(ceil_div(p.n_rows, m.lead_rows), 8);
-  m.flag_bytes = (size_t)round_up((int64_t)m.lead_blocks * (int64_t)sizeof(uint32_t), 256);
+  m.vt_bytes = m.lead ? (size_t)round_up((int64_t)p.n_rows * p.rank * (int64_t)sizeof(uint64_t), 256) : 0;
   return m;
 }
 
@@ -202,7 +201,7 @@ WsLayout apply_ws_layout(const sgmv_problem_t& p) {
   const size_t two_launch = vec_ws_bytes(v, p.rank) + v_area_bytes(p);
   const size_t matrix =
       sgmv::mfma_supported(p.rank)
-          ? SGMV_WS_COUNTER_BYTES + plan_mfma(p).partial_bytes + v_area_bytes(p) + plan_mfma(p).flag_bytes
+          ? SGMV_WS_COUNTER_BYTES + plan_mfma(p).partial_bytes + v_area_bytes(p) + plan_mfma(p).vt_bytes
           : 0;
   WsLayout w;
   w.decode_off = (size_t)round_up((int64_t)std::max(two_launch, matrix), 256);

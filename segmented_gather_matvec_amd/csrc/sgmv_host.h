@@ -95,7 +95,7 @@ struct MfmaPlan {
   int lead = 0;              // 1: lead workgroups of the expand launch sum them (no reduce launch)
   int lead_blocks = 0;       // ... that many per projection (a multiple of 8)
   int lead_rows = 0;         // ... of that many rows each
-  size_t flag_bytes = 0;     // their flags, after V in the workspace
+  size_t vt_bytes = 0;       // their tagged V words or flags, after V in the workspace
   int x_lds = 0;             // 1: the shrink stages X through LDS (full row tiles)
 };
 MfmaPlan plan_mfma(const sgmv_problem_t& p);

@@ -21,9 +21,10 @@
 //     LoRA's scale, if any, is applied to V by the expand.  Up to 8 planes
 //     (32 at rank <= 16 on full tiles) each expand workgroup adds those of its
 //     rows itself.  Beyond, the expand launch begins with lead workgroups that
-//     sum them for blocks of rows and flag each block with the launch's tag;
-//     the expand workgroups issue their first loads, then wait for the flags
-//     of their rows.  The separate reduce launch serves the standalone shrink.
+//     sum them for blocks of rows and publish V as words {fp32, launch tag}
+//     (16-row expand tiles), or write V and flag each row block with the
+//     launch's tag (larger tiles); the expand workgroups issue their first
+//     loads, then poll the words or flags of their rows.  The separate reduce launch serves the standalone shrink.
 //  3. expand: a workgroup takes 64 rows (16 when the segments are short) and a
 //     group of 128-column chunks.  V is split into V_hi + V_lo (both in the
 //     input format), consumed as a K of 2r against [B_k; B_k], which keeps
@@ -325,15 +326,16 @@ void sgmv_mfma_reduce_kernel(MfmaParams p) {
 // ---------------------------------------------------------------- lead reduce
 // Lead workgroup b of projection y: V of rows [b * lead_rows, (b + 1) *
 // lead_rows) = the sum of the partial planes in plane order from zero (the
-// reduce launch's order and bits), written through to the device-coherent
-// level, then flags[b] = tag once every thread's stores have completed.  Lead
-// workgroups never wait, and they have the lowest workgroup ids of the launch,
-// so they are dispatched ahead of every workgroup that waits for them.  Up to
-// 16 planes a thread sums one float4 of a row (1024 / R rows per workgroup);
-// beyond, one float2 (512 / R rows), so that every plane load of a thread is in
-// flight at once up to 32 planes at the same register count (more would cost
-// the expand occupancy).
-template <int R, int W>
+// reduce launch's order and bits).  TAGGED: published as words {fp32, launch
+// tag}; otherwise V is written through to the device-coherent level and, once
+// every thread's stores have completed, flags[b] = tag.  Lead workgroups never
+// wait, and they have the lowest workgroup ids of the launch, so they are
+// dispatched ahead of every workgroup that waits for them.  Up to 16 planes a
+// thread sums one float4 of a row (1024 / R rows per workgroup); beyond, one
+// float2 (512 / R rows), so that every plane load of a thread is in flight at
+// once up to 32 planes at the same register count (more would cost the expand
+// occupancy).
+template <int R, int W, bool TAGGED>
 __device__ inline void lead_sum(const MfmaParams& p, int y, int b, uint32_t tag) {
   using VT = __attribute__((ext_vector_type(W))) float;
   constexpr int VW = R / W;               // vectors per row of V
@@ -342,7 +344,7 @@ __device__ inline void lead_sum(const MfmaParams& p, int y, int b, uint32_t tag)
   const int t = threadIdx.x;
   const int row = b * ROWS + t / VW;
   const float* partials = p.partials + (int64_t)y * p.proj_stride;
-  float* V = p.V + (int64_t)y * p.proj_stride;
+  char* area = static_cast<char*>(p.lead_area) + (int64_t)y * p.proj_stride * 4;
   int end = p.seg_indptr[p.num_segs];
   end = end < p.n_rows ? end : p.n_rows;
   const int64_t off = (int64_t)(row < p.n_rows ? row : p.n_rows - 1) * R + (t % VW) * W;
@@ -360,24 +362,32 @@ __device__ inline void lead_sum(const MfmaParams& p, int y, int b, uint32_t tag)
       s = k0 + u < p.ksplit ? a : s;
     }
   }
-  if (row < end) {
-    uint64_t* dst = reinterpret_cast<uint64_t*>(V + off);
+  if constexpr (TAGGED) {
+    if (row < end) {
+      uint64_t* dst = reinterpret_cast<uint64_t*>(area) + off;
 #pragma unroll
-    for (int e = 0; e < W / 2; ++e)
-      publish_u64(dst + e, ((uint64_t)__float_as_uint(s[2 * e + 1]) << 32) | __float_as_uint(s[2 * e]));
+      for (int e = 0; e < W; ++e) publish_tagged(dst + e, s[e], tag);
+    }
+  } else {
+    if (row < end) {
+      uint64_t* dst = reinterpret_cast<uint64_t*>(p.V + (int64_t)y * p.proj_stride + off);
+#pragma unroll
+      for (int e = 0; e < W / 2; ++e)
+        publish_u64(dst + e, ((uint64_t)__float_as_uint(s[2 * e + 1]) << 32) | __float_as_uint(s[2 * e]));
+    }
+    wait_memory_ops();
+    __syncthreads();
+    if (t == 0)
+      __hip_atomic_store(reinterpret_cast<uint32_t*>(area) + b, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  wait_memory_ops();
-  __syncthreads();
-  if (t == 0)
-    __hip_atomic_store(p.flags + (int64_t)y * p.proj_stride + b, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int R>
+template <int R, bool TAGGED>
 __device__ inline void lead_reduce_rows(const MfmaParams& p, int y, int b, uint32_t tag) {
   if (p.lead_rows == kThreads * 4 / R)
-    lead_sum<R, 4>(p, y, b, tag);
+    lead_sum<R, 4, TAGGED>(p, y, b, tag);
   else
-    lead_sum<R, 2>(p, y, b, tag);
+    lead_sum<R, 2, TAGGED>(p, y, b, tag);
 }
 
 // ---------------------------------------------------------------- expand
@@ -455,13 +465,17 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_expand_kernel(MfmaParams p
                        (p.fold_planes ? p.partials == nullptr : p.V == nullptr) | (pj.B_ptrs == nullptr) |
                        (pj.Y == nullptr);
   if (bad_size | bad_ptr) return;
+  // 16-row tiles read V as tagged words (a tile's V is small); larger tiles,
+  // each reading 4 KiB of V per 16 rows from every column group, wait for one
+  // flag per row block and read V itself (half the device-coherent bytes).
+  constexpr bool kTaggedV = MT == 16;
   const int lead = LEAD ? p.lead_blocks * p.lead_proj : 0;
-  if (LEAD && (p.partials == nullptr) | (p.flags == nullptr) | (p.errors == nullptr) |
+  if (LEAD && (p.partials == nullptr) | (p.lead_area == nullptr) | (p.errors == nullptr) |
       ((p.lead_blocks | (p.lead_proj - 1) | (p.lead_rows - 1)) < 0))
     return;
   const uint32_t tag = LEAD ? launch_tag() : 0u;
   if (LEAD && (int)blockIdx.x < lead) {
-    if (blockIdx.y == 0) lead_reduce_rows<R>(p, blockIdx.x / p.lead_blocks, blockIdx.x % p.lead_blocks, tag);
+    if (blockIdx.y == 0) lead_reduce_rows<R, kTaggedV>(p, blockIdx.x / p.lead_blocks, blockIdx.x % p.lead_blocks, tag);
     return;
   }
   const int nchunks = (p.h_out + kCW - 1) / kCW;
@@ -571,43 +585,86 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_expand_kernel(MfmaParams p
     }
   } else if (LEAD) {
     // V of these rows is summed by lead workgroups of this launch: the first
-    // chunk's loads go out, then the wait for the flags of the tile's row
-    // blocks (one lane each), then V through device-coherent loads.
+    // chunk's loads go out, then the wait (bounded; a limit of 0, the host's
+    // test hook, waits for a tag no word carries).
     issue(ch0, bvA, yvA);
-    __shared__ uint32_t lds_ok;
-    if (wave == 0) {
-      const int b0 = r0 / p.lead_rows, nb = (r0 + L - 1) / p.lead_rows - b0 + 1;
-      const uint32_t* fl = p.flags + (int64_t)blockIdx.y * p.proj_stride + b0;
-      // A limit of 0 (the host's test hook) waits for a tag no flag carries.
-      const uint32_t want = p.wait_ticks != 0 ? tag : ~tag;
-      bool ok = true;
-      if (lane < nb) {
-        const uint64_t deadline = __builtin_amdgcn_s_memrealtime() + p.wait_ticks;
-        uint32_t f = __hip_atomic_load(fl + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        uint64_t now = 0;
-        while (f != want && now <= deadline) {
-          __builtin_amdgcn_s_sleep(1);
-          f = __hip_atomic_load(fl + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          now = __builtin_amdgcn_s_memrealtime();
-        }
-        ok = f == want;
-      }
-      const bool all_ok = __all(ok);
-      if (lane == 0) lds_ok = all_ok;
-    }
+    __shared__ uint32_t lds_gave_up;
+    if (t == 0) lds_gave_up = 0;
     __syncthreads();
-    if (!lds_ok) {
+    const uint32_t want = p.wait_ticks != 0 ? tag : ~tag;
+    const char* area = static_cast<const char*>(p.lead_area) + (int64_t)blockIdx.y * p.proj_stride * 4;
+    const uint64_t deadline = __builtin_amdgcn_s_memrealtime() + p.wait_ticks;
+    uint64_t now = 0;  // read beside each round of polls, checked at the next
+    bool done;
+    if constexpr (kTaggedV) {
+      // Every thread polls the tagged words of its V values.
+      const uint64_t* vt = reinterpret_cast<const uint64_t*>(area);
+      uint64_t w[NV4][4];
+#pragma unroll
+      for (int m = 0; m < NV4; ++m) {
+        const int o = (t + kThreads * m) * 4;
+        const int rr = o / R;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[m][e] = fetch_tagged(vt + (int64_t)(r0 + (rr < L ? rr : 0)) * R + o % R + e);
+      }
+      for (;;) {
+        done = true;
+#pragma unroll
+        for (int m = 0; m < NV4; ++m)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if ((uint32_t)(w[m][e] >> 32) != want) done = false;
+        if (done || now > deadline) break;
+        __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+        for (int m = 0; m < NV4; ++m) {
+          const int o = (t + kThreads * m) * 4;
+          const int rr = o / R;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if ((uint32_t)(w[m][e] >> 32) != want)
+              w[m][e] = fetch_tagged(vt + (int64_t)(r0 + (rr < L ? rr : 0)) * R + o % R + e);
+        }
+        now = __builtin_amdgcn_s_memrealtime();
+      }
+#pragma unroll
+      for (int m = 0; m < NV4; ++m)
+        vv[m] = f32x4{__uint_as_float((uint32_t)w[m][0]), __uint_as_float((uint32_t)w[m][1]),
+                      __uint_as_float((uint32_t)w[m][2]), __uint_as_float((uint32_t)w[m][3])};
+    } else {
+      // One lane per row block of the tile polls its flag.
+      done = true;
+      if (t < 64) {
+        const int b0 = r0 / p.lead_rows, nb = (r0 + L - 1) / p.lead_rows - b0 + 1;
+        const uint32_t* fl = reinterpret_cast<const uint32_t*>(area) + b0;
+        if (lane < nb) {
+          uint32_t f = __hip_atomic_load(fl + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          while (f != want && now <= deadline) {
+            __builtin_amdgcn_s_sleep(1);
+            f = __hip_atomic_load(fl + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            now = __builtin_amdgcn_s_memrealtime();
+          }
+          done = f == want;
+        }
+      }
+    }
+    if (!done) lds_gave_up = 1;
+    __syncthreads();
+    if (lds_gave_up) {
       if (t == 0) __hip_atomic_fetch_or(p.errors, kDecodeErrWaitTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       return;  // Y untouched
     }
+    if constexpr (!kTaggedV) {
 #pragma unroll
-    for (int m = 0; m < NV4; ++m) {
-      const int o = (t + kThreads * m) * 4;
-      const int rr = o / R;
-      const uint64_t* src = reinterpret_cast<const uint64_t*>(Vp + (int64_t)(r0 + (rr < L ? rr : 0)) * R + o % R);
-      const uint64_t lo = fetch_published_u64(src), hi = fetch_published_u64(src + 1);
-      vv[m] = f32x4{__uint_as_float((uint32_t)lo), __uint_as_float((uint32_t)(lo >> 32)),
-                    __uint_as_float((uint32_t)hi), __uint_as_float((uint32_t)(hi >> 32))};
+      for (int m = 0; m < NV4; ++m) {
+        const int o = (t + kThreads * m) * 4;
+        const int rr = o / R;
+        const uint64_t* src =
+            reinterpret_cast<const uint64_t*>(Vp + (int64_t)(r0 + (rr < L ? rr : 0)) * R + o % R);
+        const uint64_t lo = fetch_published_u64(src), hi = fetch_published_u64(src + 1);
+        vv[m] = f32x4{__uint_as_float((uint32_t)lo), __uint_as_float((uint32_t)(lo >> 32)),
+                      __uint_as_float((uint32_t)hi), __uint_as_float((uint32_t)(hi >> 32))};
+      }
     }
   } else {
 #pragma unroll

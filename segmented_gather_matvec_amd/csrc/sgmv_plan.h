@@ -129,16 +129,22 @@ struct MfmaParams {
   int32_t x_lds;
   // 1 (with fold_planes 0): no reduce launch; lead workgroups of the expand
   // launch sum the partial planes of their row blocks (lead_rows rows each,
-  // lead_blocks blocks per projection, in plane order: the reduce's bits) into
-  // V and publish flags[block] = the launch tag; the other workgroups wait for
-  // the flags of their rows, at most wait_ticks of the real-time counter (0:
-  // give up at once), before reading V.  Every grid row starts with
-  // lead_blocks * lead_proj workgroups: those of row 0 do the lead work of all
-  // lead_proj projections, so that it is dispatched ahead of every waiting
-  // workgroup; those of the other rows exit at once.
+  // lead_blocks blocks per projection, in plane order: the reduce's bits).
+  // With 16-row expand tiles they publish V as tagged words {fp32, launch tag}
+  // in the lead area, and the other workgroups poll the words of their rows
+  // until every tag is the launch's; with larger tiles (each reading more of
+  // V) they write V and then flags[block] = the launch tag in the lead area,
+  // and the others wait for the flags of their rows, then read V.  Every wait
+  // lasts at most wait_ticks of the real-time counter (0: give up at once).
+  // Every grid row starts with lead_blocks * lead_proj workgroups: those of
+  // row 0 do the lead work of all lead_proj projections, so that it is
+  // dispatched ahead of every waiting workgroup; those of the other rows exit
+  // at once.
   int32_t lead_reduce, lead_blocks, lead_rows, lead_proj;
   uint32_t wait_ticks;
-  uint32_t* flags;         // projection 0; projection y at flags + y * proj_stride
+  // Projection 0's lead area: [n_rows][rank] tagged words, or [lead_blocks]
+  // flags; projection y's at lead_area + y * proj_stride * 4 bytes.
+  void* lead_area;
   uint32_t* errors;        // device error word (a wait that gave up sets bit 0)
   const int32_t* seg_indptr;
   const int32_t* lora_idx;

@@ -111,7 +111,7 @@ def test_ranks_without_scales(case):
     assert_close(to_bits(call.Y), call.oracle(), dtype, what=case)
 
 
-@pytest.mark.parametrize("case", ["decode_r64_b32", "mfma_r16", "vector_r32"])
+@pytest.mark.parametrize("case", ["decode_r64_b32", "mfma_r16", "mfma_r64_lead", "vector_r32"])
 def test_ranks_scales_with_row_map(case):
     """Request-order rows (row map) together with ranks and scales."""
     import torch
@@ -125,7 +125,7 @@ def test_ranks_scales_with_row_map(case):
     assert_close(to_bits(call.Y), ref, dtype, what=case)
 
 
-@pytest.mark.parametrize("case", ["decode_r16_b32", "mfma_r64"])
+@pytest.mark.parametrize("case", ["decode_r16_b32", "mfma_r64", "mfma_r64_lead"])
 def test_batched_projections_with_their_own_ranks(case):
     """Two projections in one call, each with its own rank table and scales."""
     seed, dtype, n, h_in, h_out, R, P, (seg, lidx), choices, variant, splits = CASES[case]

@@ -75,15 +75,19 @@ def test_multi_pass_decode_gives_up_in_every_pass():
     assert sg.sgmv_take_device_errors() == 0
 
 
-def test_matrix_core_lead_wait_gives_up_under_the_test_hook_and_recovers():
+@pytest.mark.parametrize("seg,lidx", [([0, 100, 256], [2, 0]),
+                                      (list(range(0, 257, 16)), [i % 3 for i in range(16)])],
+                         ids=["full_tiles_flags", "short_tiles_tagged_words"])
+def test_matrix_core_lead_wait_gives_up_under_the_test_hook_and_recovers(seg, lidx):
     """Beyond the planes the expand folds itself, the first workgroups of the
-    expand launch sum them and flag each row block; the others wait for those
-    flags under the same bound as the decode route.  Under the test hook every
-    such wait gives up: Y is untouched and the error word reports it."""
+    expand launch sum them: for full row tiles (12 planes) they flag each row
+    block, for short tiles (32 planes) they publish V as tagged words; the
+    others wait under the same bound as the decode route.  Under the test hook
+    every such wait gives up: Y is untouched and the error word reports it."""
     import torch
     rng = np.random.default_rng(4242)
     X, A, B, Y0 = workloads.integer_exact(rng, 256, 8192, 256, 64, 3, "bf16", 2, 64)
-    call = DeviceCall("bf16", X, A, B, Y0, [0, 100, 256], [2, 0], variant=sg.SGMV_VARIANT_MFMA)
+    call = DeviceCall("bf16", X, A, B, Y0, seg, lidx, variant=sg.SGMV_VARIANT_MFMA)
     info = sg.sgmv_query_plan(call.problem)
     assert info.route == sg.SGMV_ROUTE_MFMA and info.splits > 8 and info.launches == 2, info.as_dict()
     assert sg.sgmv_take_device_errors() == 0
