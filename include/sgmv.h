@@ -170,7 +170,7 @@ typedef enum sgmv_route {
   SGMV_ROUTE_NONE = 0,    /* nothing to do (no rows or segments) */
   SGMV_ROUTE_DECODE = 1,  /* one launch: shrink, on-chip exchange, expand */
   SGMV_ROUTE_MFMA = 2,    /* matrix-core shrink, then matrix-core expand, whose launch also sums the shrink's split partials
-                             (each expand workgroup up to 8 splits, 32 at rank <= 16; beyond, lead workgroups of the launch) */
+                             (in its first, lead workgroups) */
   SGMV_ROUTE_VECTOR = 3   /* split-K vector shrink, then vector expand */
 } sgmv_route_t;
 
@@ -223,11 +223,11 @@ sgmv_status_t sgmv_expand(const sgmv_problem_t* problem, const float* V, const v
  * (sgmv_set_wait_limit, default 1 s), leaves its part of Y untouched and sets
  * SGMV_DEVICE_ERR_WAIT_TIMEOUT in the device error word
  * (sgmv_take_device_errors): the kernel always ends, and the error is
- * reported instead of a hang.  On the matrix-core route with more split
- * partials than its expand workgroups sum themselves, the expand launch's
- * first workgroups (lowest ids, dispatched first; they wait for nothing) sum
- * them, and the other workgroups wait for their rows' sums under the same
- * bound and error word.  Calls on one workspace must not overlap. */
+ * reported instead of a hang.  On the matrix-core route with more than one
+ * split partial per row, the expand launch's first workgroups (lowest ids,
+ * dispatched first; they wait for nothing) sum them, and the other workgroups
+ * wait for their rows' sums under the same bound and error word.  Calls on
+ * one workspace must not overlap. */
 sgmv_status_t sgmv_lora_apply(const sgmv_problem_t* problem, const void* X,
                               const void* const* A_ptrs, const void* const* B_ptrs, void* Y,
                               const int32_t* seg_indptr, const int32_t* lora_idx, void* ws,

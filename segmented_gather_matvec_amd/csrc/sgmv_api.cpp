@@ -254,7 +254,7 @@ sgmv_status_t apply(const sgmv_problem_t& p, const void* X, const sgmv_projectio
     q.partials = reinterpret_cast<float*>(ws + SGMV_WS_COUNTER_BYTES);
     q.V = reinterpret_cast<float*>(ws + SGMV_WS_COUNTER_BYTES + m.partial_bytes);
     q.proj_stride = (int64_t)(stride / sizeof(float));
-    q.fold_planes = m.fold;
+    if (!m.lead) q.V = q.partials;  // a single plane is V itself
     if (m.lead) {
       // Lead workgroups of the expand launch sum the planes; their tagged V
       // words or row-block flags follow V in each projection's slice of the
@@ -398,7 +398,7 @@ sgmv_status_t sgmv_query_plan(const sgmv_problem_t* p, sgmv_plan_info_t* info) {
       break;
     case SGMV_ROUTE_MFMA: {
       const MfmaPlan m = plan_mfma(*p);
-      info->launches = 2;  // the planes are summed by the expand launch (folded or by its lead workgroups)
+      info->launches = 2;  // the planes are summed by the expand launch's lead workgroups
       info->rows_per_unit = sgmv::kMfmaRowsPerTile;
       info->units = (int32_t)m.units64;
       info->splits = m.ksplit;

@@ -128,14 +128,6 @@ constexpr int kMfmaShortTileRows = 32;   // mean rows per 64-row tile below whic
 constexpr int kMfmaShortExpandRows = 16; // expand tile rows for short tiles
 constexpr int kMfmaLowRankExpandRows = 32;  // expand tile rows for full tiles at rank <= 16
 constexpr int kMfmaShortChunksPerWg = 3;
-// Up to this many partial planes the expand sums them itself and the reduce
-// launch is skipped.  At rank <= 16 a plane is a quarter of rank 64's, and
-// full tiles fold up to 32 of them (mixed r = 16 11008 -> 4096, 9 planes:
-// 58.5 -> 56.4 us per call).  Short tiles re-read the planes for every column
-// group and keep the launch beyond 8 (folding 20 planes cost the 13B forward),
-// as do full tiles at rank 64 (9 planes at 11008 -> 4096 were 9% slower).
-constexpr int kMfmaFoldPlanes = 8;
-constexpr int kMfmaLowRankFoldPlanes = 32;
 
 MfmaPlan plan_mfma(const sgmv_problem_t& p) {
   MfmaPlan m;
@@ -184,12 +176,13 @@ MfmaPlan plan_mfma(const sgmv_problem_t& p) {
     m.chunks_per_wg = (int)ceil_div(nchunks, groups);
   }
   m.partial_bytes = (size_t)m.ksplit * (size_t)p.n_rows * p.rank * sizeof(float);
-  const bool low_rank_full = p.rank <= 16 && m.expand_rows != kMfmaShortExpandRows;
-  m.fold = m.ksplit <= (low_rank_full ? kMfmaLowRankFoldPlanes : kMfmaFoldPlanes) ? 1 : 0;
-  // Beyond the fold limit the first workgroups of the expand launch sum the
-  // planes (1024 / rank rows each, 512 / rank beyond 16 planes) into tagged V
-  // words; the reduce launch remains for the standalone shrink.
-  m.lead = m.fold ? 0 : 1;
+  // The first workgroups of the expand launch sum the planes (1024 / rank rows
+  // each, 512 / rank beyond 16 planes); the reduce launch remains for the
+  // standalone shrink.  This beat each expand workgroup summing the planes of
+  // its own rows (which re-reads them once per column group) at every split:
+  // mixed r = 64, 4096 -> 11008 (4 planes) 85.3 -> 83.0 us per call, r = 16
+  // 11008 -> 4096 (9 planes) 53.9 -> 53.4 us, the other shapes equal.
+  m.lead = m.ksplit > 1 ? 1 : 0;
   m.lead_rows = m.ksplit > 16 ? 512 / p.rank : 1024 / p.rank;
   m.lead_blocks = (int)round_up(ceil_div(p.n_rows, m.lead_rows), 8);
   m.vt_bytes = m.lead ? (size_t)round_up((int64_t)p.n_rows * p.rank * (int64_t)sizeof(uint64_t), 256) : 0;

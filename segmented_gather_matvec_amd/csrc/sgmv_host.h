@@ -91,8 +91,7 @@ struct MfmaPlan {
   int64_t units_x = 0;                        // expand units of <= expand_rows rows
   int direct_x = 1;
   size_t partial_bytes = 0;  // split partials of V, fp32 [ksplit][n_rows][rank]
-  int fold = 0;              // 1: the expand sums the partial planes (no reduce launch)
-  int lead = 0;              // 1: lead workgroups of the expand launch sum them (no reduce launch)
+  int lead = 0;              // 1: lead workgroups of the expand launch sum the planes (ksplit > 1)
   int lead_blocks = 0;       // ... that many per projection (a multiple of 8)
   int lead_rows = 0;         // ... of that many rows each
   size_t vt_bytes = 0;       // their tagged V words or flags, after V in the workspace

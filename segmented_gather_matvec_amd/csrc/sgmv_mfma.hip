@@ -18,13 +18,14 @@
 //     rank with one 128-bit LDS read.  Each H1 chunk writes its own fp32 partial plane of V; workgroups
 //     that read the same chunk of A_k run on one XCD.
 //  2. V = sum of the partial planes, in chunk order (reproducible); the
-//     LoRA's scale, if any, is applied to V by the expand.  Up to 8 planes
-//     (32 at rank <= 16 on full tiles) each expand workgroup adds those of its
-//     rows itself.  Beyond, the expand launch begins with lead workgroups that
-//     sum them for blocks of rows and publish V as words {fp32, launch tag}
+//     LoRA's scale, if any, is applied to V by the expand.  With more than one
+//     plane the expand launch begins with lead workgroups that sum them for
+//     blocks of rows and publish V as words {fp32, launch tag}
 //     (16-row expand tiles), or write V and flag each row block with the
 //     launch's tag (larger tiles); the expand workgroups issue their first
-//     loads, then poll the words or flags of their rows.  The separate reduce launch serves the standalone shrink.
+//     loads, then poll the words or flags of their rows.  With one plane the
+//     expand reads it as V.  The separate reduce launch serves the standalone
+//     shrink.
 //  3. expand: a workgroup takes 64 rows (16 when the segments are short) and a
 //     group of 128-column chunks.  V is split into V_hi + V_lo (both in the
 //     input format), consumed as a K of 2r against [B_k; B_k], which keeps
@@ -462,7 +463,7 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_expand_kernel(MfmaParams p
                          (p.chunks_per_wg - 1) | (int32_t)(p.proj_stride >> 32) | (p.ksplit - 1) |
                          (int32_t)(p.partial_stride >> 32)) < 0;
   const bool bad_ptr = (p.seg_indptr == nullptr) | (p.lora_idx == nullptr) |
-                       (p.fold_planes ? p.partials == nullptr : p.V == nullptr) | (pj.B_ptrs == nullptr) |
+                       (p.V == nullptr) | (pj.B_ptrs == nullptr) |
                        (pj.Y == nullptr);
   if (bad_size | bad_ptr) return;
   // 16-row tiles read V as tagged words (a tile's V is small); larger tiles,
@@ -544,46 +545,7 @@ __global__ __launch_bounds__(kThreads) void sgmv_mfma_expand_kernel(MfmaParams p
   constexpr int NV4 = (NVF + kThreads - 1) / kThreads;  // ... per thread
   f32x4 vv[NV4];
   u32x4 bvA[NBP][2], yvA[NYV], bvB[NBP][2], yvB[NYV];
-  if (p.fold_planes) {
-    // V = the sum of the shrink's partial planes, added in plane order from
-    // zero as the reduce launch would (same bits), kBatch planes in flight.
-    // The first batch is loaded before the first chunk's B_k and Y, so that
-    // its sum waits for the planes but not for the chunk.
-    constexpr int kBatch = 4;
-    const float* Pp = p.partials + (int64_t)blockIdx.y * p.proj_stride;
-    f32x4 pv[kBatch][NV4];
-    auto load_planes = [&](int k0) {
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const int64_t k = k0 + u < p.ksplit ? k0 + u : p.ksplit - 1;
-#pragma unroll
-        for (int m = 0; m < NV4; ++m) {
-          const int o = (t + kThreads * m) * 4;
-          const int rr = o / R;
-          pv[u][m] = *reinterpret_cast<const f32x4*>(Pp + k * p.partial_stride +
-                                                     (int64_t)(r0 + (rr < L ? rr : 0)) * R + o % R);
-        }
-      }
-    };
-    auto add_planes = [&](int k0) {
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u)
-#pragma unroll
-        for (int m = 0; m < NV4; ++m) {
-          const f32x4 a = vv[m] + pv[u][m];
-          vv[m] = k0 + u < p.ksplit ? a : vv[m];
-        }
-    };
-#pragma unroll
-    for (int m = 0; m < NV4; ++m) vv[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-    load_planes(0);
-    issue(ch0, bvA, yvA);
-    add_planes(0);
-    for (int k0 = kBatch; k0 < p.ksplit; k0 += kBatch) {
-      load_planes(k0);
-      add_planes(k0);
-    }
-  } else if (LEAD) {
+  if (LEAD) {
     // V of these rows is summed by lead workgroups of this launch: the first
     // chunk's loads go out, then the wait (bounded; a limit of 0, the host's
     // test hook, waits for a tag no word carries).
@@ -850,7 +812,9 @@ hipError_t launch_stage(int dtype, int rank, int stage, const MfmaParams& p, int
 
 hipError_t launch_mfma_shrink(int dtype, int rank, const MfmaParams& p, int num_proj, hipStream_t stream) {
   hipError_t e = launch_stage(dtype, rank, 0, p, num_proj, stream);
-  if (e != hipSuccess || p.fold_planes || p.lead_reduce) return e;
+  // Nothing to reduce when the expand launch sums the planes (lead
+  // workgroups) or when V is the single plane itself.
+  if (e != hipSuccess || p.lead_reduce || p.V == p.partials) return e;
   return launch_stage(dtype, rank, 1, p, num_proj, stream);
 }
 

@@ -121,13 +121,10 @@ struct MfmaParams {
   int32_t ksplit, kc, chunks_per_wg;
   // Expand tiles of expand_rows (16, 32 or 64) rows of one segment: num_units_x of them.
   int32_t expand_rows, num_units_x, direct_units_x;
-  // 1: no reduce launch; the expand sums the ksplit partial planes of its rows
-  // itself (in plane order, the reduce's order) instead of reading V.
-  int32_t fold_planes;
   // 1: the shrink stages X through LDS, loaded a whole row piece per
   // instruction (full row tiles); 0: X straight into the operand registers.
   int32_t x_lds;
-  // 1 (with fold_planes 0): no reduce launch; lead workgroups of the expand
+  // 1 (ksplit > 1): no reduce launch; lead workgroups of the expand
   // launch sum the partial planes of their row blocks (lead_rows rows each,
   // lead_blocks blocks per projection, in plane order: the reduce's bits).
   // With 16-row expand tiles they publish V as tagged words {fp32, launch tag}
@@ -157,8 +154,8 @@ struct MfmaParams {
   Projection proj[kMaxProjections];
 };
 
-// Shrink into the partial planes, then (unless p.fold_planes) reduce them into
-// V: one or two launches.
+// Shrink into the partial planes, then (unless the expand launch sums them, or
+// V is the single plane itself) reduce them into V: one or two launches.
 hipError_t launch_mfma_shrink(int dtype, int rank, const MfmaParams& p, int num_proj, hipStream_t stream);
 hipError_t launch_mfma_expand(int dtype, int rank, const MfmaParams& p, int num_proj, hipStream_t stream);
 

@@ -297,11 +297,11 @@ def test_integer_exact_shrink_bitwise(variant):
 
 @pytest.mark.parametrize("rank,h_in,launches", [(16, 4096, 2), (64, 8192, 2)])
 def test_integer_exact_many_planes_bitwise(rank, h_in, launches):
-    """A long H1 on full 64-row tiles: 16 partial planes summed by each expand
-    workgroup itself at rank 16, 11 planes summed by the lead workgroups of the
-    expand launch at rank 64 (the standalone shrink's reduce launch is checked
-    against the same planes).  Integer inputs make every result exact, so every
-    way of summing the planes must give the oracle's bits."""
+    """A long H1 on full 64-row tiles: 16 partial planes at rank 16 and 11 at
+    rank 64, summed by the lead workgroups of the expand launch (row-block
+    flags); the standalone shrink's reduce launch is checked on the same
+    planes.  Integer inputs make every result exact, so every way of summing
+    the planes must give the oracle's bits."""
     rng = np.random.default_rng(5000 + rank)
     m, c = INT_EXACT[("bf16", rank)]
     X, A, B, Y0 = workloads.integer_exact(rng, 256, h_in, 256, rank, 3, "bf16", m, c)

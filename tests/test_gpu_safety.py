@@ -79,11 +79,11 @@ def test_multi_pass_decode_gives_up_in_every_pass():
                                       (list(range(0, 257, 16)), [i % 3 for i in range(16)])],
                          ids=["full_tiles_flags", "short_tiles_tagged_words"])
 def test_matrix_core_lead_wait_gives_up_under_the_test_hook_and_recovers(seg, lidx):
-    """Beyond the planes the expand folds itself, the first workgroups of the
-    expand launch sum them: for full row tiles (12 planes) they flag each row
-    block, for short tiles (32 planes) they publish V as tagged words; the
-    others wait under the same bound as the decode route.  Under the test hook
-    every such wait gives up: Y is untouched and the error word reports it."""
+    """The first workgroups of the expand launch sum the shrink's partial
+    planes: for full row tiles (12 planes) they flag each row block, for short
+    tiles (32 planes) they publish V as tagged words; the others wait under the
+    same bound as the decode route.  Under the test hook every such wait gives
+    up: Y is untouched and the error word reports it."""
     import torch
     rng = np.random.default_rng(4242)
     X, A, B, Y0 = workloads.integer_exact(rng, 256, 8192, 256, 64, 3, "bf16", 2, 64)
