@@ -336,6 +336,32 @@ def test_empty_unsorted_repeated_segments_and_uncovered_rows(variant):
     assert call.counters_clear()
 
 
+@pytest.mark.parametrize("layout", ["full_tiles", "short_tiles"])
+def test_split_sum_in_the_expand_launch_with_empty_unsorted_segments_and_uncovered_rows(layout):
+    """The matrix-core route with several H1 planes (their sum done by lead
+    workgroups of the expand launch: row-block flags for full tiles, tagged V
+    words for short ones, one float4 or one float2 per thread), on a batch with
+    empty, repeated and unsorted segments, rows that no segment covers (left
+    untouched), and H1 / H2 that are not multiples of the tile sizes."""
+    if layout == "full_tiles":
+        n, h_in, seg, lidx = 150, 4104, [0, 0, 70, 70, 71, 130], [4, 2, 2, 0, 3]
+    else:
+        n, h_in = 90, 8200
+        seg = [0, 3, 3, 10, 17, 20, 20, 31, 35, 44, 50, 61, 62, 75, 80]
+        lidx = [1, 4, 0, 2, 3, 3, 0, 1, 4, 2, 2, 0, 1, 3]
+    X, A, B, Y0 = rand_inputs(30 + len(seg), n, h_in, 1000, 64, 5, "bf16")
+    call = DeviceCall("bf16", X, A, B, Y0, seg, lidx, variant=sg.SGMV_VARIANT_MFMA)
+    info = sg.sgmv_query_plan(call.problem)
+    assert info.route == sg.SGMV_ROUTE_MFMA and info.splits > 1 and info.launches == 2, info.as_dict()
+    end = seg[-1]
+    for _ in range(2):  # the second call finds the first call's V words and flags in the workspace
+        call.reset_y()
+        got = to_bits(call.apply())
+        assert_close(got, call.oracle_apply(), "bf16")
+        assert np.array_equal(got[end:], Y0[end:])
+    assert sg.sgmv_take_device_errors() == 0
+
+
 @pytest.mark.parametrize("variant", APPLY_VARIANTS)
 def test_no_segments_is_a_no_op(variant):
     X, A, B, Y0 = rand_inputs(2, 8, 64, 64, 16, 2)
