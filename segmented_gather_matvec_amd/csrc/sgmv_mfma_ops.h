@@ -14,6 +14,13 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// 128-bit store with the non-temporal hint (streamed output that should not
+// displace reused data from the caches).
+typedef __attribute__((address_space(1))) u32x4* global_u32x4_wptr;
+__device__ inline void store_stream(void* p, const u32x4& v) {
+  __builtin_nontemporal_store(v, (global_u32x4_wptr)p);
+}
+
 template <class T>
 __device__ inline f32x4 mfma(const u32x4& a, const u32x4& b, f32x4 c);
 template <>
