@@ -104,6 +104,37 @@ def test_matrix_core_lead_wait_gives_up_under_the_test_hook_and_recovers(seg, li
     assert sg.sgmv_take_device_errors() == 0
 
 
+def test_matrix_core_lead_calls_on_two_streams():
+    """Two matrix-core calls whose expand launches carry lead workgroups (one
+    with short tiles and tagged V words, one with full tiles and flags) run at
+    the same time on two streams, each with its own workspace.  Lead workgroups
+    wait for nothing and every wait is for lead workgroups of its own launch,
+    dispatched ahead of it, so the calls need no device to themselves: both
+    give the oracle's bits (integer-exact inputs) and no wait gives up."""
+    import torch
+    rng = np.random.default_rng(777)
+    calls = []
+    for seg, lidx in ((list(range(0, 257, 16)), [i % 3 for i in range(16)]), ([0, 100, 256], [2, 0])):
+        X, A, B, Y0 = workloads.integer_exact(rng, 256, 8192, 2048, 64, 3, "bf16", 2, 64)
+        c = DeviceCall("bf16", X, A, B, Y0, seg, lidx, variant=sg.SGMV_VARIANT_MFMA)
+        info = sg.sgmv_query_plan(c.problem)
+        assert info.route == sg.SGMV_ROUTE_MFMA and info.splits > 1, info.as_dict()
+        calls.append(c)
+    refs = [c.oracle_apply() for c in calls]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]  # default priority
+    assert sg.sgmv_take_device_errors() == 0
+    for _ in range(4):
+        for c in calls:
+            c.reset_y()
+        torch.cuda.synchronize()
+        for c, st in zip(calls, streams):
+            sg.sgmv_lora_apply(c.problem, c.X, c.A_ptrs, c.B_ptrs, c.Y, c.seg_d, c.lidx_d, c.ws, stream=st)
+        torch.cuda.synchronize()
+        for c, ref in zip(calls, refs):
+            assert np.array_equal(oracle.decode(to_bits(c.Y), "bf16"), ref)
+    assert sg.sgmv_take_device_errors() == 0
+
+
 def test_decode_slots_untouched_by_other_routes():
     """One workspace serves the matrix-core route, the two-launch route and the
     decode route in turn; the decode route's result is the oracle's."""
