@@ -118,12 +118,15 @@ typedef struct sgmv_problem {
  *                               stale word there is always a tag of an
  *                               earlier decode launch, never another route's
  *                               data.
+ *   then                        the matrix-core expand's lead area (V as tagged
+ *                               words, or one flag per row block), for the same
+ *                               reason also written by no other route.
  * Only the counter area must be zero before first use; the rest may hold
  * anything.  A call that does not complete (a kernel killed part way, a
  * device reset) can leave counters non-zero, after which two-launch calls on
  * that workspace give unspecified results: zero the counter area again before
- * reusing a workspace after such a failure.  The decode route needs no reset:
- * its slots carry a per-launch tag. */
+ * reusing a workspace after such a failure.  The decode route and the
+ * matrix-core route need no reset: their hand-offs carry a per-launch tag. */
 #define SGMV_WS_COUNTER_BYTES ((size_t)1 << 20)
 
 /* Human-readable name of a status code (static string, never NULL). */

@@ -257,15 +257,15 @@ sgmv_status_t apply(const sgmv_problem_t& p, const void* X, const sgmv_projectio
     if (!m.lead) q.V = q.partials;  // a single plane is V itself
     if (m.lead) {
       // Lead workgroups of the expand launch sum the planes; their tagged V
-      // words or row-block flags follow V in each projection's slice of the
-      // workspace.
+      // words or row-block flags have an area of their own in each
+      // projection's slice of the workspace.
       if (sgmv::decode_error_word(&q.errors) != hipSuccess) return SGMV_ERR_HIP;
       q.lead_reduce = 1;
       q.lead_blocks = m.lead_blocks;
       q.lead_rows = m.lead_rows;
       q.lead_proj = np;
       q.wait_ticks = wait_ticks();
-      q.lead_area = ws + SGMV_WS_COUNTER_BYTES + m.partial_bytes + v_area_bytes(p);
+      q.lead_area = ws + apply_ws_layout(p).lead_off;
     }
     hipError_t e = sgmv::launch_mfma_shrink(p.dtype, p.rank, q, np, s);
     if (e != hipSuccess) return SGMV_ERR_HIP;

@@ -193,12 +193,13 @@ WsLayout apply_ws_layout(const sgmv_problem_t& p) {
   const VecPlan v = plan_vec(p, kTargetWorkgroups);
   const size_t two_launch = vec_ws_bytes(v, p.rank) + v_area_bytes(p);
   const size_t matrix =
-      sgmv::mfma_supported(p.rank)
-          ? SGMV_WS_COUNTER_BYTES + plan_mfma(p).partial_bytes + v_area_bytes(p) + plan_mfma(p).vt_bytes
-          : 0;
+      sgmv::mfma_supported(p.rank) ? SGMV_WS_COUNTER_BYTES + plan_mfma(p).partial_bytes + v_area_bytes(p) : 0;
   WsLayout w;
   w.decode_off = (size_t)round_up((int64_t)std::max(two_launch, matrix), 256);
-  w.total = w.decode_off + decode_slot_bytes(p);
+  // Tagged words only in areas of their own: a stale word there is a tag of
+  // an earlier launch, never another route's fp32 data posing as one.
+  w.lead_off = (size_t)round_up((int64_t)(w.decode_off + decode_slot_bytes(p)), 256);
+  w.total = w.lead_off + (sgmv::mfma_supported(p.rank) ? plan_mfma(p).vt_bytes : 0);
   return w;
 }
 

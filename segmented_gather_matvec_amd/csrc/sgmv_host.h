@@ -104,10 +104,14 @@ MfmaPlan plan_mfma(const sgmv_problem_t& p);
 //   [SGMV_WS_COUNTER_BYTES, decode_off)
 //                                the vector shrink's split partials then V, or
 //                                the matrix-core partial planes then V
-//   [decode_off, total)          the decode kernel's tagged slots, which no other
+//   [decode_off, lead_off)       the decode kernel's tagged slots, which no other
 //                                route writes
+//   [lead_off, total)            the matrix-core expand's lead area (tagged V
+//                                words or row-block flags), which no other route
+//                                writes either
 struct WsLayout {
   size_t decode_off = 0;
+  size_t lead_off = 0;  // the matrix-core expand's lead area (tagged V words or row-block flags)
   size_t total = 0;
 };
 WsLayout apply_ws_layout(const sgmv_problem_t& p);

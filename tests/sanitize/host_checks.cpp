@@ -165,14 +165,19 @@ static void problems(std::mt19937_64& rng) {
       CHECK(m.chunks_per_wg >= 1 && (m.expand_rows == 16 || m.expand_rows == 32 || m.expand_rows == 64));
       CHECK(m.expand_rows != 32 || p.rank <= 16);
     }
-    // the decode slots sit after every other route's area
+    // the decode slots, then the matrix-core lead area, sit after every other
+    // route's area and do not overlap
     const WsLayout w = apply_ws_layout(p);
     CHECK(w.total == bytes);
-    CHECK(w.decode_off % 256 == 0);
+    CHECK(w.decode_off % 256 == 0 && w.lead_off % 256 == 0);
     CHECK(w.decode_off >= vec_ws_bytes(v, p.rank) + v_area_bytes(p));
     if (sgmv::mfma_supported(p.rank))
       CHECK(w.decode_off >= SGMV_WS_COUNTER_BYTES + plan_mfma(p).partial_bytes + v_area_bytes(p));
-    CHECK(w.total == w.decode_off + decode_slot_bytes(p));
+    CHECK(w.lead_off >= w.decode_off + decode_slot_bytes(p));
+    CHECK(w.total == w.lead_off + (sgmv::mfma_supported(p.rank) ? plan_mfma(p).vt_bytes : 0));
+    if (sgmv::mfma_supported(p.rank) && plan_mfma(p).lead)
+      CHECK(plan_mfma(p).vt_bytes >= (size_t)p.n_rows * p.rank * 8 &&
+            plan_mfma(p).vt_bytes >= (size_t)plan_mfma(p).lead_blocks * 4);
     // base projection
     if (p.n_rows > sgmv::kBaseMaxRows) {
       CHECK(bst == SGMV_ERR_UNSUPPORTED);
