@@ -138,11 +138,26 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, const InlineM
   // selects one: loads at an offset computed from blockIdx.y were issued only
   // after the first argument loads had returned, a second trip before the
   // first metadata load.
+  // With the rank and scale tables, the whole-struct copy under a condition
+  // went through a stack copy of all entries (private memory on the critical
+  // path: mixed-rank batch 13.9 us instead of 9.2 us), so those kernels select
+  // field by field; the others keep the struct copy, which the compiler turns
+  // into one load at a selected offset (0.2 us faster than selecting fields).
   Projection pr = p.proj[0];
   if constexpr (!INL) {  // (INL launches one projection)
 #pragma unroll
-    for (int i = 1; i < kMaxProjections; ++i)
-      if ((int)blockIdx.y == i) pr = p.proj[i];
+    for (int i = 1; i < kMaxProjections; ++i) {
+      if constexpr (HET) {
+        const bool s = (int)blockIdx.y == i;
+        pr.A_ptrs = s ? p.proj[i].A_ptrs : pr.A_ptrs;
+        pr.B_ptrs = s ? p.proj[i].B_ptrs : pr.B_ptrs;
+        pr.Y = s ? p.proj[i].Y : pr.Y;
+        pr.ranks = s ? p.proj[i].ranks : pr.ranks;
+        pr.scales = s ? p.proj[i].scales : pr.scales;
+      } else if ((int)blockIdx.y == i) {
+        pr = p.proj[i];
+      }
+    }
   }
   // A negative size or a null table is a malformed launch (the host rejects
   // both).  Testing every uniform argument here also makes the compiler fetch
