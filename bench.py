@@ -245,8 +245,9 @@ class SingleCallBench:
             self.seg_hc = np.ascontiguousarray(seg, np.int32)
             self.lidx_hc = np.ascontiguousarray(lidx if lidx.size else np.zeros(1, np.int32), np.int32)
         if row_map == "torch":
-            self.Xs = torch.empty_like(self.X[0])
-            self.Ys = torch.empty_like(self.Y[0])
+            # X and Y gathered into segment order around each call
+            self.X_sorted = torch.empty_like(self.X[0])
+            self.Y_sorted = torch.empty_like(self.Y[0])
         self.marshal()
         torch.cuda.synchronize()
 
@@ -271,8 +272,8 @@ class SingleCallBench:
                 self.args.append((pb, self.X[x].data_ptr(), pj, 1, self.seg.data_ptr(), self.lidx.data_ptr(),
                                   self.perm.data_ptr(), self.ws.data_ptr(), wsn))
             elif self.row_map == "torch":
-                self.args.append((pb, self.Xs.data_ptr(), self.A_tab[t].data_ptr(), self.B_tab[t].data_ptr(),
-                                  self.Ys.data_ptr(), self.seg.data_ptr(), self.lidx.data_ptr(),
+                self.args.append((pb, self.X_sorted.data_ptr(), self.A_tab[t].data_ptr(), self.B_tab[t].data_ptr(),
+                                  self.Y_sorted.data_ptr(), self.seg.data_ptr(), self.lidx.data_ptr(),
                                   self.ws.data_ptr(), wsn))
             elif self.host_meta:
                 self.args.append((pb, self.X[x].data_ptr(), self.A_tab_h[t].ctypes.data,
@@ -292,10 +293,10 @@ class SingleCallBench:
             # segment order, apply, scatter Y back (torch ops on the same stream).
             x = i % self.copies
             torch = self.torch
-            torch.index_select(self.X[x], 0, self.perm64, out=self.Xs)
-            torch.index_select(self.Y[x], 0, self.perm64, out=self.Ys)
+            torch.index_select(self.X[x], 0, self.perm64, out=self.X_sorted)
+            torch.index_select(self.Y[x], 0, self.perm64, out=self.Y_sorted)
             st = self.fn(*self.args[i], stream)
-            self.Y[x].index_copy_(0, self.perm64, self.Ys)
+            self.Y[x].index_copy_(0, self.perm64, self.Y_sorted)
         else:
             st = self.fn(*self.args[i], stream)
         if st != 0:
