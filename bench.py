@@ -92,6 +92,15 @@ def recorded_traffic(src_hash, workload):
     return rec.get("bytes_per_launch")
 
 
+def traffic_applies(args) -> bool:
+    """The committed counter run was taken on the headline workload's default
+    launch (automatic variant and split count, device metadata, rows in segment
+    order); other launches run other kernels or plans.  Graph replay launches
+    the same kernel."""
+    return (args.workload == DEFAULT_WORKLOAD and args.variant == "auto" and args.splits == 0
+            and not args.host_meta and args.row_map == "none")
+
+
 def _bits(t):
     import numpy as np
     import torch
@@ -1140,7 +1149,7 @@ def main():
     value = bench.bytes * K / ev_s / 1e9
     achieved = bench.bytes / bench.calls_per_step / launch_s / 1e9
     src_hash = kernel_source_hash()
-    traffic = recorded_traffic(src_hash, args.workload)
+    traffic = recorded_traffic(src_hash, args.workload) if traffic_applies(args) else None
     line = {
         "metric": METRIC,
         "value": round(value, 2),

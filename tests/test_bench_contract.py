@@ -87,3 +87,15 @@ def test_cpu_baseline_times_the_oracle():
     assert cb["kind"] == "oracle" and cb["unit"] == "GB/s" and cb["cores"] == 1
     assert cb["value"] > 0
     assert "oracle calls on one decode batch" in cb["sample"]
+
+
+def test_traffic_record_only_for_the_default_launch():
+    """The counter run behind roofline.traffic was taken on the headline's
+    default launch; a forced variant, split count, host metadata or row layout
+    runs other kernels and reports no traffic."""
+    import argparse
+    base = dict(workload=bench.DEFAULT_WORKLOAD, variant="auto", splits=0, host_meta=False, row_map="none")
+    assert bench.traffic_applies(argparse.Namespace(**base))
+    for k, v in (("variant", "vector"), ("variant", "mfma"), ("splits", 16), ("host_meta", True),
+                 ("row_map", "kernel"), ("workload", "skewed_b32")):
+        assert not bench.traffic_applies(argparse.Namespace(**dict(base, **{k: v}))), (k, v)
